@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD scan on one MI355X.
+
+One step = one ssd_chunk_scan over one batch of the Mamba2-130m-shaped
+workload (batch 8, seqlen 2048, 24 heads, head_dim 64, state_dim 128,
+1 group, chunk 256, bf16 io, fp32 state), inputs resident in HBM.  Steps
+cycle through several independently drawn input/output sets so that the
+working set exceeds the 256 MB Infinity Cache.  Printed: one JSON line with
+tokens/s (value), the dominant kernel's roofline (HIP-event durations of
+that kernel on its launch stream), the whole scan against its HBM roofline,
+the decode step rate (ssd_step at batch 256, 80 heads, state from a
+1024-token prefill), and the oracle timed on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD scan tokens/sec at 1 GPU; % of MFMA/HBM roofline; decode steps/sec"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_IDS = ("dt_cumsum", "state_pass", "seg_combine", "chunk_out")
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan.hpp",
+                  "mamba_ssd_chunked_chunk_amd/csrc/ssd_device.hpp",
+                  "mamba_ssd_chunked_chunk_amd/csrc/ssd_plan.hpp")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------- byte counts ---
+def plan_sizes(b, l, h, p, n, g, Q, T=64, target_chains=2048):
+    nc = -(-l // Q)
+    nsplit = max(1, n // 32)
+    chains = b * h * nsplit
+    nseg = min(max(1, -(-target_chains // chains)), nc)
+    cps = -(-nc // nseg)
+    nseg = -(-nc // cps)
+    lp = nc * (-(-Q // T) * T)
+    return nc, nseg, lp
+
+
+def bytes_scan_alg(b, l, h, p, n, g, Q, s, init=False, final=False):
+    """Algorithmic bytes of the whole scan: inputs and outputs once plus one
+    write and one read of the fp32 chunk-boundary-state tensor."""
+    th = b * l * h
+    per = 2 * p * s + 2 * n * s * g / h + s + 8.0 * n * p / Q
+    extra = (4 * n * p * b * h) * (int(init) + int(final))
+    return th * per + extra
+
+
+def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
+    th = b * l * h
+    return th * (2 * p * s + 2 * n * s * g / h + s) + 4 * n * p * b * h * (int(init) + int(final))
+
+
+def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
+    """Algorithmic bytes one launch of a kernel moves (each operand once)."""
+    nc, nseg, lp = plan_sizes(b, l, h, p, n, g, Q)
+    th = b * l * h
+    x = th * p * s
+    BC = b * l * g * n * s
+    rows = b * h * lp * 4              # lcs or dtp
+    hb = b * nc * h * n * p * 4        # boundary states
+    seg = b * nseg * h * n * p * 4 if nseg > 1 else 0
+    st = b * h * n * p * 4
+    if name == "dt_cumsum":
+        return th * s + 2 * rows
+    if name == "state_pass":
+        return x + BC + 2 * rows + hb + seg + (st if final and nseg == 1 else 0)
+    if name == "seg_combine":
+        return 2 * seg + (st if final else 0)
+    if name == "chunk_out":
+        return x + 2 * BC + 2 * rows + hb + seg + x   # x read, y written
+    raise KeyError(name)
+
+
+def bytes_step(b, h, p, n, g, s):
+    return b * h * (8 * n * p + 2 * p * s + s) + 2 * b * g * n * s + 12 * h
+
+
+# --------------------------------------------------------------- traffic ---
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel sources changed since."""
+    path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_digest") != source_digest():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ main ---
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=4, help="input/output sets cycled through")
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=0, help="oracle sample size (0: all)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a few scans and a plain copy of known size, for counter runs")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the scan is built and measured on a single "
+              "MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mamba_ssd_chunked_chunk_amd as ssd
+    import ssd_synth as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = syn.WORKLOADS["mamba2_130m"]
+    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
+    s = 2
+
+    def t(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    log("generating %d input sets of %s" % (args.sets, w))
+    sets = []
+    host0 = None
+    for k in range(args.sets):
+        inp = syn.make_inputs(w.replace(seed=w.seed + 1000 * k))
+        if k == 0:
+            host0 = inp
+        sets.append(dict(x=t(inp["x"]), dt=t(inp["dt"]), A=t(inp["A"]), B=t(inp["B"]),
+                         C=t(inp["C"]), D=t(inp["D"]), bias=t(inp["dt_bias"]),
+                         y=torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev)))
+    wsb = ssd.workspace_bytes(b, l, h, p, n, g, Q)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def run(i):
+        S = sets[i % len(sets)]
+        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
+                       dt_bias=S["bias"], out=S["y"], workspace=ws)
+
+    log("warmup", args.warmup)
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    if args.traffic_probe:
+        for i in range(3):
+            run(i)
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel()}))
+        return
+
+    log("timed", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    value = b * l * args.steps / (t1 - t0)
+    log("scan: %.3f ms/step, %.4g tokens/s" % (ms_step, value))
+
+    # per-kernel durations: HIP events recorded by the library on the launch stream
+    ssd.trace_enable(True)
+    for name in KERNEL_IDS:
+        ssd.trace_read(name)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        run(i)
+    torch.cuda.synchronize()
+    ssd.trace_enable(False)
+    kern = {}
+    for name in KERNEL_IDS:
+        tot, cnt = ssd.trace_read(name)
+        if cnt:
+            kern[name] = dict(avg_us=1e3 * tot / cnt, launches=cnt,
+                              alg_bytes=bytes_kernel(name, b, l, h, p, n, g, Q, s))
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    dk = kern[dom]
+    achieved = dk["alg_bytes"] / (dk["avg_us"] * 1e-6) / 1e9
+    for name, v in kern.items():
+        v["GBs"] = round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1)
+        v["avg_us"] = round(v["avg_us"], 2)
+    log("kernels:", json.dumps(kern))
+    traffic = measured_traffic("k_" + dom, w.name)
+    roofline = {"kernel": "k_" + dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "alg_bytes_per_launch": dk["alg_bytes"],
+                "avg_launch_us": dk["avg_us"]}
+    balg = bytes_scan_alg(b, l, h, p, n, g, Q, s)
+    bmin = bytes_scan_min(b, l, h, p, n, g, Q, s)
+    t_roof = balg / (HBM_PEAK_GBS * 1e9)
+    scan_roof = {"bound": "hbm", "alg_bytes": balg, "min_bytes": bmin,
+                 "t_roof_us": round(t_roof * 1e6, 2), "t_step_us": round(ms_step * 1e3, 2),
+                 "frac_alg": round(t_roof / (ms_step * 1e-3), 4),
+                 "frac_min": round(bmin / (HBM_PEAK_GBS * 1e9) / (ms_step * 1e-3), 4),
+                 "kernels": kern}
+
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(args, torch, ssd, syn, dev)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args, host0, w)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) x/B/C/dt, A=-exp(U[0,ln16]), "
+                "dt_bias=softplus^-1(loguniform[1e-3,0.1]), D=1, zero initial state)",
+        "config": {"workload": "mamba2_130m", "batch": b, "seqlen": l, "heads": h,
+                   "head_dim": p, "state_dim": n, "groups": g, "chunk": Q, "io": "bf16",
+                   "state": "fp32", "input_sets": args.sets},
+        "roofline": roofline,
+        "scan_roofline": scan_roof,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def bench_decode(args, torch, ssd, syn, dev):
+    """Decode steps/s: batch 256, 80 heads, head_dim 64, state 128, bf16 io,
+    fp32 state initialised by a 1024-token chunk-scan prefill."""
+    w = syn.WORKLOADS["decode_2p7b"]
+    b, l, h, p, n, g = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups
+    head = syn.make_inputs(w.replace(seqlen=1), batch=1)
+    A = torch.from_numpy(head["A"]).to(dev)
+    D = torch.from_numpy(head["D"]).to(dev)
+    bias = torch.from_numpy(head["dt_bias"]).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).bfloat16()
+
+    log("decode prefill", b, "x", l)
+    x, dt, B, C = rnd(b, l, h, p), rnd(b, l, h), rnd(b, l, g, n), rnd(b, l, g, n)
+    _, st = ssd.chunk_scan(x, dt, A, B, C, D, chunk_size=w.chunk, dt_bias=bias,
+                           return_final_state=True)
+    del x, dt, B, C
+    K = args.decode_steps
+    xs, dts, Bs, Cs = rnd(K, b, h, p), rnd(K, b, h), rnd(K, b, g, n), rnd(K, b, g, n)
+    y = torch.empty((b, h, p), dtype=torch.bfloat16, device=dev)
+    for k in range(3):
+        ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rate = K / (t1 - t0)
+    ssd.trace_enable(True)
+    ssd.trace_read("step")
+    for k in range(K):
+        ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
+    torch.cuda.synchronize()
+    ssd.trace_enable(False)
+    tot, cnt = ssd.trace_read("step")
+    avg_us = 1e3 * tot / cnt
+    alg = bytes_step(b, h, p, n, g, 2)
+    achieved = alg / (avg_us * 1e-6) / 1e9
+    log("decode: %.1f steps/s, kernel %.2f us, %.0f GB/s" % (rate, avg_us, achieved))
+    return {"metric": "decode steps/s", "value": round(rate, 1), "unit": "steps/s",
+            "tokens_per_s": round(rate * b, 1), "steps": K,
+            "config": {"workload": "decode_2p7b", "batch": b, "heads": h, "head_dim": p,
+                       "state_dim": n, "groups": g, "io": "bf16", "state": "fp32",
+                       "prefill_tokens": l},
+            "roofline": {"kernel": "k_step", "bound": "hbm", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("k_step", "decode_2p7b"),
+                         "alg_bytes_per_launch": alg, "avg_launch_us": round(avg_us, 2)}}
+
+
+def cpu_baseline(args, inp, w):
+    """The fp64 oracle on the host cores, on a sample of (batch, head) pairs of
+    the same workload (all 2048 tokens of each), reported in tokens/s (a token
+    being one position across all heads)."""
+    import oracle
+    oracle.build()
+    pairs_all = [(bb, hh) for bb in range(w.batch) for hh in range(w.heads)]
+    k = args.cpu_pairs or len(pairs_all)
+    pairs = pairs_all[:k]
+    cores = oracle.default_threads()
+    log("oracle on %d pairs, %d threads" % (len(pairs), cores))
+    t0 = time.perf_counter()
+    oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["dt_bias"],
+                io=inp["io"], pairs=pairs, nthreads=cores)
+    dt_s = time.perf_counter() - t0
+    tok = len(pairs) * w.seqlen / w.heads
+    log("oracle: %.2f s" % dt_s)
+    return {"value": round(tok / dt_s, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d (batch, head) pairs x %d tokens of the mamba2_130m workload "
+                      "(%.1f s wall)" % (len(pairs), len(pairs_all), w.seqlen, dt_s)}
+
+
+if __name__ == "__main__":
+    main()

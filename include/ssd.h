@@ -1,0 +1,168 @@
+/*
+ * ssd.h -- C ABI of libssd.so: the Mamba-2 SSD selective-state-space scan on
+ * AMD MI355X (gfx950).
+ *
+ * The scan (nnterp guide, "Mamba-2" page, opening section): per head the
+ * state h is a state_dim x head_dim matrix, and every token t does
+ *
+ *     h = exp(A d_t) h + d_t B_t x_t^T          (decay, then write)
+ *     y_t = C_t^T h + D x_t                      (read after the write)
+ *
+ * where d_t is the processed time step of section "The values":
+ * d_t = clamp(softplus(dt_t + dt_bias), dt_min, dt_max) (softplus optional).
+ * The heads of a group share B and C; head hh uses group hh / (heads/groups).
+ *
+ * Layouts (section "The values"; all row-major and contiguous):
+ *   x   [batch, seqlen, heads, head_dim]        io dtype
+ *   dt  [batch, seqlen, heads]                  io dtype (raw, before bias)
+ *   B,C [batch, seqlen, groups, state_dim]      io dtype
+ *   A, D, dt_bias [heads]                       fp32
+ *   states [batch, heads, state_dim, head_dim]  fp32 (state_dim first)
+ *   y   [batch, seqlen, heads, head_dim]        io dtype
+ * A decode step drops the seqlen axis (section "The state between steps").
+ *
+ * Every pointer argument except the stream is a device pointer.  The caller
+ * owns every buffer; the library allocates nothing.  Calls are asynchronous
+ * on the given HIP stream (NULL = the null stream) and never synchronise.
+ * Arguments are validated before anything is launched: a call that returns
+ * an error has launched nothing and left every output untouched.  A device
+ * fault surfaces at the caller's next synchronisation.  No C++ exception
+ * crosses this interface.
+ *
+ * Preconditions not checked on the device: A <= 0 (decays are non-positive,
+ * section "The values"), inputs finite, y not overlapping any input.
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+/* io dtype of x, dt, B, C and y */
+enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
+
+enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = -2,       /* a size < 0 (or <= 0 where a size of 0 is meaningless),
+                                 heads % groups != 0, chunk <= 0 */
+    SSD_ERR_UNSUPPORTED = -3, /* head_dim / state_dim outside the compiled set, or
+                                 an io dtype other than SSD_F32 / SSD_BF16 */
+    SSD_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the query returns */
+    SSD_ERR_ALIGN = -5,       /* a pointer is not aligned as documented */
+    SSD_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * ssd_chunk_scan -- the prompt / forward scan over a whole sequence.
+ *
+ * Computes the recurrence above for every (batch, head) from init_state (or
+ * from zero) in the chunked two-stage form (kongchang "Mamba2" page,
+ * chunk-scan entry: parallel inside a chunk, serial across chunks).  The
+ * state at every chunk boundary is kept in the workspace as one tensor
+ * (nnterp, "The state after every token": the chunk scan holds the state at
+ * each chunk boundary, each a cumulative function of the initial state).
+ * The result equals the token-by-token recurrence up to rounding order.
+ *
+ *   x, dt, B, C   inputs in io_dtype (layouts above); x, B, C 16-byte aligned
+ *   A             [heads] fp32, required
+ *   D             [heads] fp32, NULL -> no skip term
+ *   dt_bias       [heads] fp32, NULL -> zero bias
+ *   dt_softplus   nonzero -> d = softplus(dt + dt_bias), else d = dt + dt_bias
+ *   dt_min,dt_max time-step limit applied after the softplus (use 0, +INF
+ *                 for none)
+ *   init_state    [batch, heads, state_dim, head_dim] fp32 or NULL (zeros);
+ *                 16-byte aligned
+ *   y             output, io dtype, written for every token; 16-byte aligned
+ *   final_state   output [batch, heads, state_dim, head_dim] fp32 or NULL (not
+ *                 written); may equal init_state (in-place continuation);
+ *                 16-byte aligned
+ *   chunk         chunk length (any value >= 1; boundary states every chunk
+ *                 tokens; the last chunk may be shorter)
+ *   workspace     device scratch of at least ssd_chunk_scan_workspace_bytes
+ *                 (...) bytes, 256-byte aligned; contents on entry ignored
+ *   hip_stream    hipStream_t to launch on
+ *
+ * Supported: head_dim in {16, 32, 64, 128}, state_dim in {32, 64, 128}.
+ * batch == 0 or seqlen == 0 is valid: nothing is computed except that
+ * final_state (if given) receives init_state, or zeros.
+ */
+int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *dt_bias,
+                       int32_t dt_softplus, float dt_min, float dt_max,
+                       const float *init_state, void *y, float *final_state,
+                       int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
+                       int64_t state_dim, int64_t groups, int64_t chunk, int32_t io_dtype,
+                       void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Bytes of workspace ssd_chunk_scan needs for these sizes (a pure function
+ * of its arguments; 0 for invalid sizes).  Layout, in order, each part
+ * 256-byte aligned: per-row cumulative log2 decay and processed time step
+ * [batch, heads, padded seqlen] fp32 each; chunk-boundary states
+ * [batch, chunks, heads, state_dim, head_dim] fp32; then, when the sequence
+ * is cut into several segments, segment states [batch, segments, heads,
+ * state_dim, head_dim] fp32 and per-chunk / per-segment log2 decays.
+ */
+size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                                      int64_t head_dim, int64_t state_dim,
+                                      int64_t groups, int64_t chunk);
+
+/*
+ * ssd_step -- one decode step: no sequence axis, the state updated in place,
+ * only y returned (nnterp, "The state between steps").  Exactly one
+ * iteration of the recurrence above, with the same time-step processing as
+ * ssd_chunk_scan, so a prompt scan followed by steps continues it.
+ *
+ *   state   [batch, heads, state_dim, head_dim] fp32, read and overwritten;
+ *           16-byte aligned
+ *   x       [batch, heads, head_dim] io dtype; dt [batch, heads] io dtype
+ *   B, C    [batch, groups, state_dim] io dtype
+ *   A, D, dt_bias, dt_softplus, dt_min, dt_max: as for ssd_chunk_scan
+ *   y       [batch, heads, head_dim] io dtype, written
+ *
+ * With d = 0 (dt_softplus = 0, dt + dt_bias = 0) the state is left exactly
+ * unchanged (exp(0) = 1 and nothing is written).
+ */
+int32_t ssd_step(float *state, const void *x, const void *dt, const float *A,
+                 const void *B, const void *C, const float *D, const float *dt_bias,
+                 int32_t dt_softplus, float dt_min, float dt_max, void *y, int64_t batch,
+                 int64_t heads, int64_t head_dim, int64_t state_dim, int64_t groups,
+                 int32_t io_dtype, void *hip_stream);
+
+/* Static text for a status code (never NULL). */
+const char *ssd_status_string(int32_t status);
+
+/* SSD_ABI_VERSION of the built library. */
+int32_t ssd_abi_version(void);
+
+/*
+ * Kernel timing for measurement.  While enabled, every kernel the two calls
+ * launch is bracketed by a pair of HIP events recorded on the launch stream
+ * (at most 65536 pairs are kept; later launches are not timed).
+ * ssd_trace_read synchronises those events and returns, for kernel id
+ * `kernel` (SSD_K_*), the summed milliseconds and the launch count, then
+ * clears that kernel's record.  Not thread-safe with concurrent scan calls.
+ */
+enum ssd_kernel_id {
+    SSD_K_DT_CUMSUM = 0,   /* time step, log decay and per-block cumulative sum */
+    SSD_K_STATE_PASS = 1,  /* chunk states and serial state passing */
+    SSD_K_SEG_COMBINE = 2, /* combination of segment states (long sequences) */
+    SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */
+    SSD_K_STEP = 4,        /* decode step */
+    SSD_K_COUNT = 5
+};
+int32_t ssd_trace_enable(int32_t on);
+int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

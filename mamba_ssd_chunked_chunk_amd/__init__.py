@@ -1,0 +1,172 @@
+"""Mamba-2 SSD selective-state-space scan on AMD MI355X (gfx950).
+
+Thin Python binding over libssd.so (include/ssd.h).  Every step of the scan
+runs in the library's HIP kernels; this module only checks and marshals
+arguments.  torch supplies device memory and the current HIP stream.
+
+    y = chunk_scan(x, dt, A, B, C, D, chunk_size=256)
+    y, final = chunk_scan(..., initial_state=h0, return_final_state=True)
+    y = step(state, x_t, dt_t, A, B_t, C_t, D)        # state updated in place
+
+Tensor contract (nnterp guide, "Mamba-2" page, section "The values"):
+x [b, l, h, p], dt [b, l, h], B and C [b, l, g, n], states [b, h, n, p]
+(fp32), A, D, dt_bias [h] (fp32).  x, dt, B, C share one io dtype
+(torch.float32 or torch.bfloat16); y has that dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+from . import _lib
+from ._lib import LibraryMissing, load, status_string  # noqa: F401
+
+__all__ = ["chunk_scan", "step", "workspace_bytes", "abi_version", "trace_enable",
+           "trace_read", "LibraryMissing", "SsdError"]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(code), code))
+        self.code = code
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float32:
+        return _lib.SSD_F32
+    if dtype == torch.bfloat16:
+        return _lib.SSD_BF16
+    raise ValueError("io dtype must be torch.float32 or torch.bfloat16, got %s" % (dtype,))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(name, t, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def abi_version() -> int:
+    return int(load().ssd_abi_version())
+
+
+def workspace_bytes(batch, seqlen, heads, head_dim, state_dim, groups, chunk) -> int:
+    return int(load().ssd_chunk_scan_workspace_bytes(batch, seqlen, heads, head_dim,
+                                                     state_dim, groups, chunk))
+
+
+def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
+               dt_softplus: bool = True, dt_limit: Tuple[float, float] = (0.0, math.inf),
+               initial_state=None, return_final_state: bool = False, out=None,
+               final_out=None, workspace=None):
+    """The chunked SSD scan of a whole sequence (ssd_chunk_scan).
+
+    Returns y, or (y, final_state) when return_final_state.  `out`,
+    `final_out` and `workspace` (uint8, at least workspace_bytes(...)) may be
+    given to avoid allocations; final_out may alias initial_state.
+    """
+    torch = _torch()
+    lib = load()
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, heads, head_dim]")
+    b, l, h, p = x.shape
+    if B.dim() != 4:
+        raise ValueError("B must be [batch, seqlen, groups, state_dim]")
+    g, n = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = x.dtype
+    _io_code(io)
+    _check("x", x, io)
+    _check("dt", dt, io, (b, l, h), dev)
+    _check("B", B, io, (b, l, g, n), dev)
+    _check("C", C, io, (b, l, g, n), dev)
+    _check("A", A, torch.float32, (h,), dev)
+    _check("D", D, torch.float32, (h,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (h,), dev)
+    _check("initial_state", initial_state, torch.float32, (b, h, n, p), dev)
+    y = torch.empty_like(x) if out is None else out
+    _check("out", y, io, (b, l, h, p), dev)
+    fin = None
+    if return_final_state:
+        fin = torch.empty((b, h, n, p), dtype=torch.float32, device=dev) \
+            if final_out is None else final_out
+        _check("final_out", fin, torch.float32, (b, h, n, p), dev)
+    wsb = int(lib.ssd_chunk_scan_workspace_bytes(b, l, h, p, n, g, int(chunk_size)))
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_chunk_scan(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+        int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
+        _ptr(initial_state), _ptr(y), _ptr(fin), b, l, h, p, n, g, int(chunk_size),
+        _io_code(io), _ptr(ws), ws.numel() * ws.element_size(), stream)
+    if rc != 0:
+        raise SsdError("ssd_chunk_scan", rc)
+    return (y, fin) if return_final_state else y
+
+
+def step(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softplus: bool = True,
+         dt_limit: Tuple[float, float] = (0.0, math.inf), out=None):
+    """One decode step (ssd_step): updates `state` [b,h,n,p] in place, returns y."""
+    torch = _torch()
+    lib = load()
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, heads, head_dim]")
+    b, h, p = x.shape
+    g, n = B.shape[1], B.shape[2]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = x.dtype
+    _io_code(io)
+    _check("state", state, torch.float32, (b, h, n, p), dev)
+    _check("x", x, io)
+    _check("dt", dt, io, (b, h), dev)
+    _check("B", B, io, (b, g, n), dev)
+    _check("C", C, io, (b, g, n), dev)
+    _check("A", A, torch.float32, (h,), dev)
+    _check("D", D, torch.float32, (h,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (h,), dev)
+    y = torch.empty_like(x) if out is None else out
+    _check("out", y, io, (b, h, p), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                      _ptr(dt_bias), int(bool(dt_softplus)), float(dt_limit[0]),
+                      float(dt_limit[1]), _ptr(y), b, h, p, n, g, _io_code(io), stream)
+    if rc != 0:
+        raise SsdError("ssd_step", rc)
+    return y
+
+
+def trace_enable(on: bool = True) -> None:
+    load().ssd_trace_enable(1 if on else 0)
+
+
+def trace_read(kernel: str):
+    """(total milliseconds, launches) recorded for `kernel` since the last read."""
+    ms = ctypes.c_double()
+    cnt = ctypes.c_int64()
+    rc = load().ssd_trace_read(_lib.KERNELS[kernel], ctypes.byref(ms), ctypes.byref(cnt))
+    if rc != 0:
+        raise SsdError("ssd_trace_read", rc)
+    return ms.value, cnt.value

@@ -1,0 +1,67 @@
+"""ctypes view of libssd.so (the C ABI declared in include/ssd.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libssd.so")
+
+SSD_F32 = 0
+SSD_BF16 = 1
+SSD_OK = 0
+SSD_ERR_NULL = -1
+SSD_ERR_SHAPE = -2
+SSD_ERR_UNSUPPORTED = -3
+SSD_ERR_WORKSPACE = -4
+SSD_ERR_ALIGN = -5
+SSD_ERR_HIP = -6
+
+KERNELS = {"dt_cumsum": 0, "state_pass": 1, "seg_combine": 2, "chunk_out": 3, "step": 4}
+
+# every symbol include/ssd.h declares
+EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_workspace_bytes", "ssd_step",
+           "ssd_status_string", "ssd_abi_version", "ssd_trace_enable", "ssd_trace_read")
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libssd.so from the package directory (never a fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            "libssd.so is not built (%s); run `python -m mamba_ssd_chunked_chunk_amd.build`"
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.ssd_chunk_scan.restype = I32
+    lib.ssd_chunk_scan.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P,
+                                   I64, I64, I64, I64, I64, I64, I64, I32,
+                                   P, ctypes.c_size_t, P]
+    lib.ssd_chunk_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_workspace_bytes.argtypes = [I64] * 7
+    lib.ssd_step.restype = I32
+    lib.ssd_step.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, P,
+                             I64, I64, I64, I64, I64, I32, P]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [I32]
+    lib.ssd_abi_version.restype = I32
+    lib.ssd_abi_version.argtypes = []
+    lib.ssd_trace_enable.restype = I32
+    lib.ssd_trace_enable.argtypes = [I32]
+    lib.ssd_trace_read.restype = I32
+    lib.ssd_trace_read.argtypes = [I32, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_int64)]
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().ssd_status_string(int(code)).decode()

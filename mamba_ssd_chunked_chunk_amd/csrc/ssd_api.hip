@@ -1,0 +1,259 @@
+// libssd.so host side: argument validation, launch planning, dispatch over
+// the compiled (head_dim, state_dim) set, and the optional kernel timing.
+// Nothing here allocates device memory: the caller passes every buffer.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/ssd.h"
+#include "ssd_device.hpp"
+#include "ssd_plan.hpp"
+
+namespace ssd {
+
+// ------------------------------------------------------------ timing hooks --
+namespace {
+struct TraceRec {
+    int kernel;
+    hipEvent_t start, end;
+};
+struct Trace {
+    std::mutex mu;
+    bool on = false;
+    std::vector<TraceRec> recs;
+    std::vector<hipEvent_t> pool;
+    int open = -1;  // index of the record whose end is pending
+};
+Trace &tr() {
+    static Trace *t = new Trace();  // never destroyed: events outlive static teardown
+    return *t;
+}
+constexpr size_t kMaxRecs = 65536;
+
+hipEvent_t take_event(Trace &t) {
+    if (!t.pool.empty()) {
+        hipEvent_t e = t.pool.back();
+        t.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+void trace_begin(int kernel, hipStream_t s) {
+    Trace &t = tr();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.open = -1;
+    if (!t.on || t.recs.size() >= kMaxRecs) return;
+    TraceRec r{kernel, take_event(t), take_event(t)};
+    if (!r.start || !r.end) return;
+    if (hipEventRecord(r.start, s) != hipSuccess) return;
+    t.recs.push_back(r);
+    t.open = (int)t.recs.size() - 1;
+}
+
+void trace_end(int kernel, hipStream_t s) {
+    Trace &t = tr();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (t.open < 0 || t.recs[t.open].kernel != kernel) return;
+    (void)hipEventRecord(t.recs[t.open].end, s);
+    t.open = -1;
+}
+
+// -------------------------------------------------------------- dispatch ---
+template <typename IO>
+static hipError_t dispatch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
+#define SSD_CASE(PP, NN) \
+    if (pl.p == PP && pl.n == NN) return launch_scan<IO, PP, NN>(pl, a, s);
+#define SSD_ROW(PP) SSD_CASE(PP, 32) SSD_CASE(PP, 64) SSD_CASE(PP, 128)
+    SSD_ROW(16) SSD_ROW(32) SSD_ROW(64) SSD_ROW(128)
+#undef SSD_ROW
+#undef SSD_CASE
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+static hipError_t dispatch_step(const StepArgs &a, hipStream_t s) {
+#define SSD_CASE(PP, NN) \
+    if (a.p == PP && a.n == NN) return launch_step<IO, PP, NN>(a, s);
+#define SSD_ROW(PP) SSD_CASE(PP, 32) SSD_CASE(PP, 64) SSD_CASE(PP, 128)
+    SSD_ROW(16) SSD_ROW(32) SSD_ROW(64) SSD_ROW(128)
+#undef SSD_ROW
+#undef SSD_CASE
+    return hipErrorInvalidValue;
+}
+
+// final_state <- init_state (or zeros), for calls with nothing to scan.
+__global__ void k_fill_state(float *__restrict__ dst, const float *__restrict__ src, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+static bool supported_dims(int64_t p, int64_t n) {
+    return (p == 16 || p == 32 || p == 64 || p == 128) && (n == 32 || n == 64 || n == 128);
+}
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+static bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= lim / a; }
+
+}  // namespace ssd
+
+using namespace ssd;
+
+extern "C" {
+
+int32_t ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char *ssd_status_string(int32_t status) {
+    switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_NULL: return "a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "invalid sizes (negative or zero size, heads % groups != 0, "
+                               "or chunk <= 0)";
+    case SSD_ERR_UNSUPPORTED: return "unsupported head_dim / state_dim / io dtype or sizes "
+                                     "beyond the launch limits";
+    case SSD_ERR_WORKSPACE: return "workspace missing or smaller than "
+                                   "ssd_chunk_scan_workspace_bytes()";
+    case SSD_ERR_ALIGN: return "a pointer is not aligned as documented";
+    case SSD_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+    }
+}
+
+size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                                      int64_t head_dim, int64_t state_dim, int64_t groups,
+                                      int64_t chunk) {
+    ScanPlan pl;
+    // the larger of the two io layouts (fp32 pads rows to 32, bf16 to 64)
+    size_t best = 0;
+    for (int io = 0; io < 2; ++io) {
+        if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io))
+            return 0;
+        if (pl.total > best) best = pl.total;
+    }
+    return best;
+}
+
+int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *dt_bias,
+                       int32_t dt_softplus, float dt_min, float dt_max,
+                       const float *init_state, void *y, float *final_state, int64_t batch,
+                       int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
+                       int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
+                       size_t workspace_bytes, void *hip_stream) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
+        groups <= 0 || chunk <= 0 || heads % groups != 0)
+        return SSD_ERR_SHAPE;
+    if (!supported_dims(head_dim, state_dim)) return SSD_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 62;
+    if (!mul_ok(batch, seqlen, lim) || !mul_ok(batch * seqlen, heads, lim) ||
+        !mul_ok(batch * seqlen * heads, 128 * 128, lim))
+        return SSD_ERR_UNSUPPORTED;
+    const bool work = batch > 0 && seqlen > 0;
+    if (!A) return SSD_ERR_NULL;
+    if (work && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL;
+    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) ||
+        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256))
+        return SSD_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+    if (!work) {
+        if (final_state && batch > 0) {
+            const int64_t cnt = batch * heads * head_dim * state_dim;
+            hipLaunchKernelGGL(k_fill_state, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
+                               final_state, init_state, cnt);
+            if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
+        }
+        return SSD_OK;
+    }
+
+    ScanPlan pl;
+    if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io_dtype))
+        return SSD_ERR_SHAPE;
+    // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
+    const int64_t gmax = ((int64_t)1 << 31) - 1;
+    if (pl.nc > gmax || batch > 65535 || (heads + 3) / 4 > 65535 ||
+        pl.b * pl.nc * pl.h > gmax || pl.b * pl.nseg * pl.h * (state_dim / 32) > gmax)
+        return SSD_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < ssd_chunk_scan_workspace_bytes(
+                                            batch, seqlen, heads, head_dim, state_dim, groups,
+                                            chunk))
+        return SSD_ERR_WORKSPACE;
+
+    ScanArgs a{x, dt, B, C, A, D, dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max,
+               init_state, y, final_state, static_cast<char *>(workspace)};
+    hipError_t e = io_dtype == SSD_BF16 ? dispatch_scan<bf16>(pl, a, s)
+                                        : dispatch_scan<float>(pl, a, s);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+int32_t ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,
+                 const void *C, const float *D, const float *dt_bias, int32_t dt_softplus,
+                 float dt_min, float dt_max, void *y, int64_t batch, int64_t heads,
+                 int64_t head_dim, int64_t state_dim, int64_t groups, int32_t io_dtype,
+                 void *hip_stream) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 || groups <= 0 ||
+        heads % groups != 0)
+        return SSD_ERR_SHAPE;
+    if (!supported_dims(head_dim, state_dim)) return SSD_ERR_UNSUPPORTED;
+    if (batch == 0) return SSD_OK;
+    if (!mul_ok(batch, heads, (int64_t)1 << 40)) return SSD_ERR_UNSUPPORTED;
+    if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(state, 16) || !aligned(x, 8) || !aligned(y, 8) || !aligned(dt, es) ||
+        !aligned(B, es) || !aligned(C, es) || !aligned(A, 4) || !aligned(D, 4) ||
+        !aligned(dt_bias, 4))
+        return SSD_ERR_ALIGN;
+    StepArgs a{state, x, dt, B, C, A, D, dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max, y,
+               batch, heads, head_dim, state_dim, groups, io_dtype};
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = io_dtype == SSD_BF16 ? dispatch_step<bf16>(a, s) : dispatch_step<float>(a, s);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+int32_t ssd_trace_enable(int32_t on) {
+    Trace &t = tr();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.on = on != 0;
+    return SSD_OK;
+}
+
+int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches) {
+    if (!total_ms || !launches) return SSD_ERR_NULL;
+    if (kernel < 0 || kernel >= SSD_K_COUNT) return SSD_ERR_SHAPE;
+    Trace &t = tr();
+    std::lock_guard<std::mutex> g(t.mu);
+    double sum = 0.0;
+    int64_t cnt = 0;
+    std::vector<TraceRec> keep;
+    keep.reserve(t.recs.size());
+    for (const TraceRec &r : t.recs) {
+        if (r.kernel != kernel) {
+            keep.push_back(r);
+            continue;
+        }
+        float ms = 0.f;
+        if (hipEventSynchronize(r.end) == hipSuccess &&
+            hipEventElapsedTime(&ms, r.start, r.end) == hipSuccess) {
+            sum += ms;
+            ++cnt;
+        }
+        t.pool.push_back(r.start);
+        t.pool.push_back(r.end);
+    }
+    t.recs.swap(keep);
+    t.open = -1;
+    *total_ms = sum;
+    *launches = cnt;
+    return SSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Host-side launch plan of one ssd_chunk_scan call: sizes, the padded row
+// space, the segment split of the serial chunk pass and the workspace map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Rows are processed in blocks of T rows (T = 64 for bf16 operands, 32 for
+// fp32).  A block never straddles a chunk boundary: chunk c owns padded rows
+// [c * Qp, (c + 1) * Qp) with Qp = ceil(Q / T) * T; padded rows past the end
+// of a chunk or of the sequence carry d = 0 (no write, no decay).
+struct ScanPlan {
+    int64_t b, l, h, p, n, g, Q;
+    int io;
+    int T;        // rows per block
+    int64_t nc;   // chunks
+    int64_t nsb;  // blocks per chunk (Qp / T)
+    int64_t Qp;   // padded rows per chunk
+    int64_t lp;   // padded rows per sequence (nc * Qp)
+    int nsplit;   // workgroups sharing one state (state_dim split)
+    int64_t nseg; // segments of the serial chunk pass
+    int64_t cps;  // chunks per segment
+    // workspace offsets (bytes)
+    size_t off_lcs, off_dtp, off_hb, off_seg, off_dlog, off_lseg, total;
+};
+
+constexpr int64_t kTargetChains = 2048;  // independent serial chains wanted
+
+inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Fills the plan from the sizes; returns false if they are invalid.
+inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, int64_t n,
+                      int64_t g, int64_t Q, int io) {
+    if (b < 0 || l < 0 || h <= 0 || p <= 0 || n <= 0 || g <= 0 || Q <= 0) return false;
+    if (h % g != 0) return false;
+    P.b = b; P.l = l; P.h = h; P.p = p; P.n = n; P.g = g; P.Q = Q; P.io = io;
+    P.T = (io == 1) ? 64 : 32;
+    P.nc = (l + Q - 1) / Q;
+    P.nsb = (Q + P.T - 1) / P.T;
+    P.Qp = P.nsb * P.T;
+    P.lp = P.nc * P.Qp;
+    P.nsplit = n >= 32 ? (int)(n / 32) : 1;
+    const int64_t chains = b * h * P.nsplit;
+    int64_t nseg = chains > 0 ? (kTargetChains + chains - 1) / chains : 1;
+    if (nseg < 1) nseg = 1;
+    if (nseg > P.nc) nseg = P.nc > 0 ? P.nc : 1;
+    P.cps = P.nc > 0 ? (P.nc + nseg - 1) / nseg : 1;
+    P.nseg = P.nc > 0 ? (P.nc + P.cps - 1) / P.cps : 1;
+    const int64_t st = n * p * 4;  // one fp32 state
+    size_t o = 0;
+    P.off_lcs = o;  o += align256(b * h * P.lp * 4);
+    P.off_dtp = o;  o += align256(b * h * P.lp * 4);
+    P.off_hb = o;   o += align256(b * P.nc * h * st);
+    if (P.nseg > 1) {
+        P.off_seg = o;  o += align256(b * P.nseg * h * st);
+        P.off_dlog = o; o += align256(b * h * P.nc * 4);
+        P.off_lseg = o; o += align256(b * h * P.nseg * 4);
+    } else {
+        P.off_seg = P.off_dlog = P.off_lseg = o;
+    }
+    P.total = o;
+    return true;
+}
+
+struct ScanArgs {
+    const void *x, *dt, *B, *C;
+    const float *A, *D, *dt_bias;
+    int softplus;
+    float dt_min, dt_max;
+    const float *init;
+    void *y;
+    float *final_state;
+    char *ws;
+};
+
+struct StepArgs {
+    float *state;
+    const void *x, *dt, *B, *C;
+    const float *A, *D, *dt_bias;
+    int softplus;
+    float dt_min, dt_max;
+    void *y;
+    int64_t b, h, p, n, g;
+    int io;
+};
+
+// Kernel-timing hooks (ssd_trace_*): called around every launch.
+void trace_begin(int kernel, hipStream_t s);
+void trace_end(int kernel, hipStream_t s);
+
+// Launchers, one per (io, head_dim, state_dim) instantiation.
+template <typename IO, int P, int N>
+hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &a, hipStream_t s);
+template <typename IO, int P, int N>
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
+}  // namespace ssd

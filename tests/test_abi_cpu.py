@@ -1,0 +1,153 @@
+"""Host-side checks of libssd.so that need no GPU.
+
+The library loads, exports every function include/ssd.h declares, and
+rejects invalid arguments with the documented status before touching the
+HIP runtime (so these calls are safe on a machine without a GPU: only
+argument checking runs).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def _lib():
+    from mamba_ssd_chunked_chunk_amd import _lib
+    try:
+        return _lib.load()
+    except _lib.LibraryMissing:
+        from mamba_ssd_chunked_chunk_amd import build
+        build.build(verbose=False)
+        return _lib.load()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+    declared = _declared_functions()
+    assert set(declared) == set(L.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+SSD_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.ssd_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in range(0, -7, -1):
+        s = lib.ssd_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.ssd_status_string(12345) == b"unknown status"
+
+
+def test_workspace_query_is_pure_and_validating(lib):
+    ws = lib.ssd_chunk_scan_workspace_bytes
+    a = ws(8, 2048, 24, 64, 128, 1, 256)
+    assert a == ws(8, 2048, 24, 64, 128, 1, 256) and a > 0
+    # boundary states alone: b * chunks * h * n * p * 4 bytes
+    assert a >= 8 * 8 * 24 * 128 * 64 * 4
+    assert ws(8, 2048, 24, 64, 128, 5, 256) == 0      # heads % groups
+    assert ws(8, 2048, 24, 64, 128, 1, 0) == 0        # chunk
+    assert ws(-1, 2048, 24, 64, 128, 1, 256) == 0
+    assert ws(0, 2048, 24, 64, 128, 1, 256) >= 0
+    assert ws(8, 4096, 24, 64, 128, 1, 256) > a       # grows with length
+
+
+FAKE = 0x10000  # 256-byte aligned, never dereferenced: every call below fails validation
+
+
+def _scan(lib, **over):
+    kw = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, dt_bias=None, sp=1,
+              lo=0.0, hi=math.inf, init=None, y=FAKE, fin=None, b=2, l=64, h=4, p=64, n=128,
+              g=1, Q=64, io=1, ws=FAKE, wsb=1 << 30, stream=None)
+    kw.update(over)
+    return lib.ssd_chunk_scan(kw["x"], kw["dt"], kw["A"], kw["B"], kw["C"], kw["D"],
+                              kw["dt_bias"], kw["sp"], kw["lo"], kw["hi"], kw["init"], kw["y"],
+                              kw["fin"], kw["b"], kw["l"], kw["h"], kw["p"], kw["n"], kw["g"],
+                              kw["Q"], kw["io"], kw["ws"], kw["wsb"], kw["stream"])
+
+
+def test_chunk_scan_rejects_bad_arguments(lib):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+    assert _scan(lib, io=7) == L.SSD_ERR_UNSUPPORTED
+    assert _scan(lib, b=-1) == L.SSD_ERR_SHAPE
+    assert _scan(lib, l=-3) == L.SSD_ERR_SHAPE
+    assert _scan(lib, h=0) == L.SSD_ERR_SHAPE
+    assert _scan(lib, Q=0) == L.SSD_ERR_SHAPE
+    assert _scan(lib, h=6, g=4) == L.SSD_ERR_SHAPE
+    assert _scan(lib, p=48) == L.SSD_ERR_UNSUPPORTED
+    assert _scan(lib, n=256) == L.SSD_ERR_UNSUPPORTED
+    assert _scan(lib, x=None) == L.SSD_ERR_NULL
+    assert _scan(lib, A=None) == L.SSD_ERR_NULL
+    assert _scan(lib, y=None) == L.SSD_ERR_NULL
+    assert _scan(lib, x=FAKE + 8) == L.SSD_ERR_ALIGN
+    assert _scan(lib, dt=FAKE + 1) == L.SSD_ERR_ALIGN
+    assert _scan(lib, init=FAKE + 4) == L.SSD_ERR_ALIGN
+    assert _scan(lib, ws=FAKE + 16) == L.SSD_ERR_ALIGN
+    assert _scan(lib, ws=None) == L.SSD_ERR_WORKSPACE
+    assert _scan(lib, wsb=1024) == L.SSD_ERR_WORKSPACE
+
+
+def test_step_rejects_bad_arguments(lib):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+
+    def step(**over):
+        kw = dict(state=FAKE, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, bias=None,
+                  sp=1, lo=0.0, hi=math.inf, y=FAKE, b=4, h=8, p=64, n=128, g=2, io=1,
+                  stream=None)
+        kw.update(over)
+        return lib.ssd_step(kw["state"], kw["x"], kw["dt"], kw["A"], kw["B"], kw["C"], kw["D"],
+                            kw["bias"], kw["sp"], kw["lo"], kw["hi"], kw["y"], kw["b"], kw["h"],
+                            kw["p"], kw["n"], kw["g"], kw["io"], kw["stream"])
+    assert step(io=2) == L.SSD_ERR_UNSUPPORTED
+    assert step(h=8, g=3) == L.SSD_ERR_SHAPE
+    assert step(b=-1) == L.SSD_ERR_SHAPE
+    assert step(p=24) == L.SSD_ERR_UNSUPPORTED
+    assert step(state=None) == L.SSD_ERR_NULL
+    assert step(C=None) == L.SSD_ERR_NULL
+    assert step(state=FAKE + 4) == L.SSD_ERR_ALIGN
+    assert step(b=0) == L.SSD_OK     # nothing to do, nothing launched
+
+
+def test_trace_read_validates(lib):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    assert lib.ssd_trace_read(99, ctypes.byref(ms), ctypes.byref(n)) != 0
+    assert lib.ssd_trace_read(0, None, None) != 0
+    assert lib.ssd_trace_read(0, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(L.LibraryMissing):
+        L.load()
+
+
+def test_oracle_is_not_on_the_product_path():
+    """The package never imports, loads or names the oracle."""
+    pkg = os.path.join(ROOT, "mamba_ssd_chunked_chunk_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), os.path.join(dirpath, f)

@@ -1,0 +1,257 @@
+"""GPU parity of ssd_chunk_scan against the fp64 oracle (through the C ABI).
+
+Small cases compare every output element; they span several row blocks and
+chunks, ragged last chunks, chunk lengths below / not a multiple of the row
+block, grouped B/C, initial states and both io dtypes.  Workload-sized
+cases are in test_gpu_workloads.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import ssd_synth as syn
+from gpu_util import (check_close, gpu_inputs, log, oracle_kw, run_scan, to_f64, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+# (batch, seqlen, heads, head_dim, state_dim, groups, chunk, init_std)
+SMALL = [
+    (1, 256, 24, 64, 128, 1, 64, 0.0),    # the tiny fp32 workload's shape
+    (2, 77, 4, 64, 128, 2, 64, 0.1),      # ragged last chunk, groups
+    (1, 10, 8, 16, 64, 1, 16, 0.0),       # head_dim 16, state 64, chunk 16, 10 tokens
+    (2, 300, 6, 32, 64, 3, 100, 0.5),     # chunk not a multiple of the row block
+    (1, 129, 2, 128, 128, 1, 256, 0.1),   # sequence shorter than a chunk, head_dim 128
+    (3, 40, 4, 64, 32, 4, 1, 0.2),        # one token per chunk
+    (2, 1, 4, 64, 128, 1, 64, 0.3),       # a single token
+    (16, 100, 32, 16, 128, 1, 32, 0.1),   # many heads: one segment in the serial pass
+    (1, 1000, 2, 64, 64, 2, 64, 0.0),     # long, few heads: many segments
+]
+
+
+def _id(c):
+    return "b%d_l%d_h%d_p%d_n%d_g%d_Q%d" % c[:7]
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    log("start", request.node.nodeid)
+    yield
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build()
+    return oracle
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("case", SMALL, ids=_id)
+def test_small_parity(orc, case, io):
+    b, l, h, p, n, g, Q, init = case
+    inp = syn.random_case(1000 + sum(case[:7]), b, l, h, p, n, g, io=io, init_std=init)
+    y, fin = run_scan(inp, Q)
+    yo, fo = orc.scan(**oracle_kw(inp))
+    s1 = check_close(to_f64(y), yo, io, "y")
+    s2 = check_close(to_f64(fin), fo, io, "final_state")
+    log("y max_abs %.3g max_rel %.3g | final max_abs %.3g" % (s1[0], s1[1], s2[0]))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_no_skip_no_bias_clamped(orc, io):
+    inp = syn.random_case(7, 2, 150, 4, 64, 64, 2, io=io, init_std=0.2)
+    inp["D"] = None
+    inp["dt_bias"] = None
+    y, fin = run_scan(inp, 64, dt_limit=(0.05, 0.5))
+    yo, fo = orc.scan(**oracle_kw(inp, dt_limit=(0.05, 0.5)))
+    check_close(to_f64(y), yo, io, "y")
+    check_close(to_f64(fin), fo, io, "final_state")
+
+
+def test_raw_time_step_without_softplus(orc):
+    inp = syn.random_case(8, 2, 90, 4, 32, 64, 1, io="f32")
+    inp["dt"] = np.abs(inp["dt"]) * np.float32(0.1)
+    inp["dt_bias"] = None
+    y, fin = run_scan(inp, 32, dt_softplus=False)
+    yo, fo = orc.scan(**oracle_kw(inp, dt_softplus=False))
+    check_close(to_f64(y), yo, "f32", "y")
+    check_close(to_f64(fin), fo, "f32", "final_state")
+
+
+def test_deterministic_bitwise():
+    """Two runs on the same inputs give identical bits (no float atomics,
+    fixed reduction order); nondeterminism is the complaint of the mirror of
+    state-spaces/mamba issue 1024."""
+    torch = torch_mod()
+    inp = syn.random_case(9, 4, 700, 8, 64, 128, 2, io="bf16", init_std=0.1)
+    g = gpu_inputs(inp)
+    y1, f1 = run_scan(inp, 256, g=g)
+    y2, f2 = run_scan(inp, 256, g=g)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(f1.view(torch.int32), f2.view(torch.int32))
+
+
+def test_extreme_decays_stay_finite(orc):
+    """A = -16 with large time steps (cumulative log decay far below -1e4):
+    every output finite (kongchang "Mamba2": a NaN from a chunk-scan kernel
+    was a numerical-stability defect) and equal to the oracle."""
+    inp = syn.random_case(10, 2, 600, 4, 64, 128, 1, io="bf16", init_std=1.0)
+    inp["A"] = np.full_like(inp["A"], -16.0)
+    inp["dt"] = syn.bf16_round(np.abs(syn.bf16_to_f32(inp["dt"])) + np.float32(10.0))
+    y, fin = run_scan(inp, 256)
+    assert torch_mod().isfinite(y.float()).all() and torch_mod().isfinite(fin).all()
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(to_f64(y), yo, "bf16", "y")
+    check_close(to_f64(fin), fo, "bf16", "final_state")
+
+
+def test_literal_dt_bias_reading_stress(orc):
+    """The literal reading of 'dt_bias loguniform[1e-3, 0.1]' (no inverse
+    softplus): larger time steps and decays."""
+    inp = syn.random_case(11, 1, 2048, 16, 64, 128, 8, io="bf16", literal=True)
+    y, fin = run_scan(inp, 256)
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(to_f64(y), yo, "bf16", "y")
+    check_close(to_f64(fin), fo, "bf16", "final_state")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_split_forward_equals_one_forward(orc, io):
+    """scan(l1) -> final as init -> scan(l2) equals scan(l1 + l2): the
+    boundary state is a function of the initial state (nnterp, "The state
+    after every token"), so a prompt can be resumed."""
+    inp = syn.random_case(12, 2, 333, 4, 64, 128, 1, io=io, init_std=0.1)
+    l1 = 140
+    first = {k: (v[:, :l1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    second = {k: (v[:, l1:] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    y1, f1 = run_scan(first, 64)
+    g2 = gpu_inputs(second)
+    g2["init"] = f1
+    y2, f2 = run_scan(second, 64, g=g2)
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(np.concatenate([to_f64(y1), to_f64(y2)], axis=1), yo, io, "y")
+    check_close(to_f64(f2), fo, io, "final_state")
+
+
+def test_final_state_may_alias_initial_state(orc):
+    import mamba_ssd_chunked_chunk_amd as ssd
+    inp = syn.random_case(13, 2, 200, 4, 64, 128, 1, io="bf16", init_std=0.3)
+    g = gpu_inputs(inp)
+    st = g["init"].clone()
+    y, fin = ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk_size=64,
+                            dt_bias=g["dt_bias"], initial_state=st, return_final_state=True,
+                            final_out=st)
+    torch_mod().cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(to_f64(y), yo, "bf16", "y")
+    check_close(to_f64(st), fo, "bf16", "final_state")
+
+
+def test_group_expansion():
+    """g groups equal h groups with B, C repeated over each group's contiguous
+    heads (the head -> group map hh // (heads // groups))."""
+    torch = torch_mod()
+    inp = syn.random_case(14, 2, 300, 8, 64, 128, 2, io="f32", init_std=0.1)
+    y, fin = run_scan(inp, 64)
+    rep = dict(inp, B=np.repeat(inp["B"], 4, axis=2), C=np.repeat(inp["C"], 4, axis=2))
+    yr, fr = run_scan(rep, 64)
+    assert torch.allclose(y, yr, rtol=1e-5, atol=1e-5)
+    assert torch.allclose(fin, fr, rtol=1e-5, atol=1e-5)
+
+
+def test_nan_stays_in_its_head():
+    """A NaN in one (batch, head)'s x reaches only that (batch, head)."""
+    torch = torch_mod()
+    inp = syn.random_case(15, 2, 300, 4, 64, 128, 1, io="f32")
+    inp["x"] = inp["x"].copy()
+    inp["x"][1, 77, 2, 5] = np.nan
+    y, fin = run_scan(inp, 64)
+    bad = ~torch.isfinite(y)
+    assert bad[1, 77:, 2].any()
+    bad[1, :, 2] = False
+    assert not bad.any()
+    fb = ~torch.isfinite(fin)
+    fb[1, 2] = False
+    assert not fb.any()
+
+
+def test_empty_sequence_and_batch():
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    inp = syn.random_case(16, 3, 5, 4, 64, 128, 1, io="bf16", init_std=0.5)
+    g = gpu_inputs(inp)
+    empty = {k: (v[:, :0].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in g.items()}
+    y, fin = ssd.chunk_scan(empty["x"], empty["dt"], g["A"], empty["B"], empty["C"], g["D"],
+                            chunk_size=64, dt_bias=g["dt_bias"], initial_state=g["init"],
+                            return_final_state=True)
+    torch.cuda.synchronize()
+    assert y.shape == (3, 0, 4, 64)
+    assert torch.equal(fin, g["init"])
+    y, fin = ssd.chunk_scan(empty["x"], empty["dt"], g["A"], empty["B"], empty["C"], g["D"],
+                            chunk_size=64, return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fin) == 0
+    z = {k: (v[:0].contiguous() if k in ("x", "dt", "B", "C") else v) for k, v in g.items()}
+    y, fin = ssd.chunk_scan(z["x"], z["dt"], g["A"], z["B"], z["C"], g["D"], chunk_size=64,
+                            return_final_state=True)
+    torch.cuda.synchronize()
+    assert y.shape[0] == 0 and fin.shape[0] == 0
+
+
+def test_invalid_arguments_raise():
+    import mamba_ssd_chunked_chunk_amd as ssd
+    inp = syn.random_case(17, 1, 64, 4, 64, 128, 1, io="bf16")
+    g = gpu_inputs(inp)
+    with pytest.raises(ssd.SsdError):
+        ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk_size=0)
+    with pytest.raises(ValueError):
+        ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"].float(), g["D"])
+    with pytest.raises(ssd.SsdError):
+        ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk_size=64,
+                       workspace=torch_mod().empty(256, dtype=torch_mod().uint8, device="cuda"))
+
+
+def _ws_layout(b, l, h, Q, io):
+    T = 64 if io == "bf16" else 32
+    nc = -(-l // Q)
+    Qp = -(-Q // T) * T
+    lp = nc * Qp
+    a256 = lambda v: (v + 255) // 256 * 256
+    off_dtp = a256(b * h * lp * 4)
+    off_hb = off_dtp + a256(b * h * lp * 4)
+    return T, nc, Qp, lp, off_dtp, off_hb
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_stage_intermediates(orc, io):
+    """Row a1 (time step, cumulative log decay) and row a3 (boundary states)
+    read back from the workspace, against the chunked fp64 steps.  The shape
+    has enough heads for a single segment, so the stored boundary states are
+    the final ones."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    from oracle import chunked
+    torch = torch_mod()
+    T = 64 if io == "bf16" else 32
+    b, l, h, p, n, g, Q = 8, 5 * T + 11, 64, 64, 128, 4, T
+    inp = syn.random_case(18, b, l, h, p, n, g, io=io, init_std=0.1)
+    G = gpu_inputs(inp)
+    wsb = ssd.workspace_bytes(b, l, h, p, n, g, Q)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ssd.chunk_scan(G["x"], G["dt"], G["A"], G["B"], G["C"], G["D"], chunk_size=Q,
+                   dt_bias=G["dt_bias"], initial_state=G["init"], workspace=ws)
+    torch.cuda.synchronize()
+    T, nc, Qp, lp, off_dtp, off_hb = _ws_layout(b, l, h, Q, io)
+    wsf = ws.view(torch.float32)
+    lcs = wsf[:b * h * lp].view(b, h, nc, Qp)[..., :Q].reshape(b, h, nc * Q)[..., :l]
+    dtp = wsf[off_dtp // 4: off_dtp // 4 + b * h * lp].view(b, h, nc, Qp)[..., :Q] \
+        .reshape(b, h, nc * Q)[..., :l]
+    hb = wsf[off_hb // 4: off_hb // 4 + b * nc * h * n * p].view(b, nc, h, n, p)
+    _, _, inter = chunked.chunked_scan(**oracle_kw(inp), chunk=Q)
+    check_close(to_f64(dtp), inter["d"], "f32", "processed time step")
+    # per-chunk cumsum (natural log) == lcs / log2(e) since blocks == chunks
+    cs = to_f64(lcs) / math.log2(math.e)
+    err = np.abs(cs - inter["cs"])
+    assert (err <= 1e-5 * (1 + np.abs(inter["cs"]))).all(), err.max()
+    check_close(to_f64(hb), inter["H_prev"], io, "boundary states")

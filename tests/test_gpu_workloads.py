@@ -1,0 +1,181 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times, and decode-step parity.
+
+The GPU runs each workload whole; the fp64 oracle recomputes a seeded
+sample of (batch, head) pairs (every token of each), which are compared
+element by element.  The decode workload runs the 1024-token prefill, then
+128 ssd_step calls, and compares every step's y and the final state of the
+sampled pairs with the oracle carrying its own fp64 state.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import ssd_synth as syn
+from gpu_util import (check_close, dev_tensor, gpu_inputs, log, oracle_kw, run_scan,
+                      sample_pairs, to_f64, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    log("start", request.node.nodeid)
+    yield
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build()
+    return oracle
+
+
+SAMPLES = {"tiny_fp32": None, "mamba2_130m": 24, "mamba2_2p7b": 16, "grouped_long": 8}
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_workload_parity(orc, name):
+    w = syn.WORKLOADS[name]
+    log("generating", name)
+    inp = syn.make_inputs(w)
+    log("gpu scan", name, w)
+    y, fin = run_scan(inp, w.chunk, final=True)
+    k = SAMPLES[name]
+    if k is None:
+        yo, fo = orc.scan(**oracle_kw(inp))
+        s = check_close(to_f64(y), yo, w.io, "y")
+        check_close(to_f64(fin), fo, w.io, "final_state")
+    else:
+        pairs = sample_pairs(w.batch, w.heads, k, seed=w.seed)
+        log("oracle on", len(pairs), "pairs")
+        yo, fo = orc.scan(**oracle_kw(inp), pairs=pairs)
+        yg = np.stack([to_f64(y[pb, :, ph, :]) for pb, ph in pairs])
+        fg = np.stack([to_f64(fin[pb, ph]) for pb, ph in pairs])
+        s = check_close(yg, yo, w.io, "y")
+        check_close(fg, fo, w.io, "final_state")
+    log(name, "y max_abs %.3g max_rel %.3g normwise %.3g" % s)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_step_small(orc, io):
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, h, p, n, g = 3, 8, 64, 128, 2
+    inp = syn.random_case(31, b, 1, h, p, n, g, io=io)
+    st0 = (0.5 * np.random.default_rng(3).standard_normal((b, h, n, p))).astype(np.float32)
+    st = dev_tensor(st0)
+    y = ssd.step(st, dev_tensor(inp["x"][:, 0]), dev_tensor(inp["dt"][:, 0]),
+                 dev_tensor(inp["A"]), dev_tensor(inp["B"][:, 0]), dev_tensor(inp["C"][:, 0]),
+                 dev_tensor(inp["D"]), dt_bias=dev_tensor(inp["dt_bias"]))
+    torch.cuda.synchronize()
+    yo, so = orc.step(st0, inp["x"][:, 0], inp["dt"][:, 0], inp["A"], inp["B"][:, 0],
+                      inp["C"][:, 0], inp["D"], inp["dt_bias"], io=io)
+    check_close(to_f64(y), yo, io, "y")
+    check_close(to_f64(st), so, "f32", "state")   # state arithmetic is fp32 for both io
+
+
+@pytest.mark.parametrize("p,n", [(16, 64), (32, 32), (128, 128)])
+def test_step_shapes(orc, p, n):
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, h, g = 5, 6, 3
+    inp = syn.random_case(32 + p + n, b, 1, h, p, n, g, io="f32")
+    st0 = np.random.default_rng(4).standard_normal((b, h, n, p)).astype(np.float32)
+    st = dev_tensor(st0)
+    y = ssd.step(st, dev_tensor(inp["x"][:, 0]), dev_tensor(inp["dt"][:, 0]),
+                 dev_tensor(inp["A"]), dev_tensor(inp["B"][:, 0]), dev_tensor(inp["C"][:, 0]),
+                 None, dt_bias=dev_tensor(inp["dt_bias"]))
+    torch.cuda.synchronize()
+    yo, so = orc.step(st0, inp["x"][:, 0], inp["dt"][:, 0], inp["A"], inp["B"][:, 0],
+                      inp["C"][:, 0], None, inp["dt_bias"])
+    check_close(to_f64(y), yo, "f32", "y")
+    check_close(to_f64(st), so, "f32", "state")
+
+
+def test_step_zero_time_step_leaves_state_equal():
+    """dt = 0 is the exact skip (nnterp, "betas and decays are one argument"):
+    exp(0) = 1 and no write, so the state is value-equal afterwards."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, h, p, n = 4, 8, 64, 128
+    st = torch.randn(b, h, n, p, device="cuda")
+    ref = st.clone()
+    x = torch.randn(b, h, p, device="cuda").bfloat16()
+    dt = torch.zeros(b, h, device="cuda").bfloat16()
+    B = torch.randn(b, 1, n, device="cuda").bfloat16()
+    C = torch.randn(b, 1, n, device="cuda").bfloat16()
+    A = -torch.rand(h, device="cuda") * 15 - 1
+    y = ssd.step(st, x, dt, A, B, C, None, dt_softplus=False)
+    torch.cuda.synchronize()
+    assert torch.equal(st, ref)
+    # y reads the unchanged state
+    yref = (C[:, 0].float().cpu()[:, None, :, None] * ref.cpu()).sum(dim=2)
+    assert torch.allclose(y.float().cpu(), yref, rtol=2e-2, atol=2e-2 * yref.abs().max().item())
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_forward_then_steps_equals_long_forward(orc, io):
+    """A prompt scan followed by single steps continues it (nnterp, "The state
+    between steps": the state one call leaves is the state the next enters)."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, l, l1, h, p, n, g = 2, 90, 70, 4, 64, 128, 1
+    inp = syn.random_case(33, b, l, h, p, n, g, io=io, init_std=0.1)
+    first = {k: (v[:, :l1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    y1, st = run_scan(first, 32)
+    ys = []
+    G = gpu_inputs(inp)
+    for t in range(l1, l):
+        ys.append(ssd.step(st, G["x"][:, t].contiguous(), G["dt"][:, t].contiguous(), G["A"],
+                           G["B"][:, t].contiguous(), G["C"][:, t].contiguous(), G["D"],
+                           dt_bias=G["dt_bias"]))
+    torch.cuda.synchronize()
+    yo, fo = orc.scan(**oracle_kw(inp))
+    yg = np.concatenate([to_f64(y1), np.stack([to_f64(v) for v in ys], axis=1)], axis=1)
+    check_close(yg, yo, io, "y")
+    check_close(to_f64(st), fo, io, "state")
+
+
+def test_decode_workload(orc):
+    """The decode workload at full size: prefill (256 x 1024 tokens, 80 heads),
+    then 128 steps at batch 256; sampled pairs against the oracle."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    w = syn.WORKLOADS["decode_2p7b"]
+    log("generating prefill")
+    inp = syn.make_inputs(w)
+    log("gpu prefill")
+    G = gpu_inputs(inp)
+    del inp["x"]
+    _, st = run_scan(None, w.chunk, final=True, g=G)
+    del G
+    pairs = sample_pairs(w.batch, w.heads, 12, seed=w.seed)
+    inp_s = syn.make_inputs(w)   # regenerate for the oracle (same seed, same draws)
+    log("oracle prefill on", len(pairs), "pairs")
+    _, so = orc.scan(**oracle_kw(inp_s), pairs=pairs)
+    del inp_s
+    check_close(np.stack([to_f64(st[pb, ph]) for pb, ph in pairs]), so, w.io, "prefill state")
+    A = dev_tensor(syn.make_inputs(w.replace(seqlen=1), batch=1)["A"])
+    base = syn.make_inputs(w.replace(seqlen=1), batch=1)
+    Dv, bias = dev_tensor(base["D"]), dev_tensor(base["dt_bias"])
+    state_o = so.reshape(len(pairs), 1, w.state_dim, w.head_dim)
+    for s in range(syn.DECODE_STEPS):
+        si = syn.make_step_inputs(w, s)
+        y = ssd.step(st, dev_tensor(si["x"]), dev_tensor(si["dt"]), A, dev_tensor(si["B"]),
+                     dev_tensor(si["C"]), Dv, dt_bias=bias)
+        # oracle: each sampled pair as its own batch row of one head
+        ys = []
+        for k, (pb, ph) in enumerate(pairs):
+            sel = [ph]
+            yk, stk = orc.step(state_o[k:k + 1], si["x"][pb:pb + 1, sel], si["dt"][pb:pb + 1, sel],
+                               base["A"][sel], si["B"][pb:pb + 1], si["C"][pb:pb + 1],
+                               base["D"][sel], base["dt_bias"][sel], io=w.io)
+            state_o[k:k + 1] = stk
+            ys.append(yk[0, 0])
+        torch.cuda.synchronize()
+        check_close(np.stack([to_f64(y[pb, ph]) for pb, ph in pairs]), np.stack(ys), w.io,
+                    "y at step %d" % s)
+    check_close(np.stack([to_f64(st[pb, ph]) for pb, ph in pairs]), state_o[:, 0], w.io,
+                "state after 128 steps")
