@@ -1,15 +1,18 @@
 // Device-side building blocks shared by the SSD scan kernels (gfx950).
 //
-// Matrix products run on the CDNA matrix cores through 16x16 MFMA tiles:
-// v_mfma_f32_16x16x32_bf16 for bf16 operands and v_mfma_f32_16x16x4_f32 for
-// fp32 operands, both accumulating in fp32.  Operand tiles are staged in LDS
-// with the contraction index contiguous, so each lane reads its fragment
-// with one vector load.  Fragment / accumulator lane layout (wave64):
-//   A fragment of rows i0..i0+15, k block k0: lane l holds row i0 + (l & 15),
-//     k = k0 + KPL * (l >> 4) + e, e < KPL;
-//   B fragment of columns j0..j0+15: lane l holds column j0 + (l & 15) with
-//     the same k indices;
-//   accumulator: element r of lane l is (i0 + 4 * (l >> 4) + r, j0 + (l & 15)).
+// Matrix products run on the CDNA matrix cores through 16x16 MFMA tiles with
+// fp32 accumulation: v_mfma_f32_16x16x32_f16 on the bf16 path and
+// v_mfma_f32_16x16x4_f32 on the fp32 path.  On the bf16 path the operands
+// are fp16: the bf16 inputs (x, B, C) convert to fp16 exactly while they lie
+// in fp16's normal range, and the operands derived inside the scan (masked
+// scores, decay-weighted x, the carried state) keep 11 significant bits
+// instead of bf16's 8.
+//
+// Fragment / accumulator lane layout (wave64), with g = lane >> 4:
+//   row-major A fragment (rows i0..i0+15, contraction block k0): lane l holds
+//     row i0 + (l & 15), k = k0 + KPL * g + e, e < KPL;
+//   row-major B fragment (columns j0..j0+15): column j0 + (l & 15), same k;
+//   accumulator: element r of lane l is (i0 + 4 g + r, j0 + (l & 15)).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,8 +21,10 @@
 namespace ssd {
 
 typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -28,11 +33,13 @@ constexpr int kThreads = 256;  // threads per workgroup
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
-// fp32 -> bf16 round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+// fp32 -> bf16 / fp16, round to nearest even
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }
 
 // 2^x on the transcendental unit (v_exp_f32); 2^(-large) -> 0, never NaN
 // for finite x.
@@ -49,19 +56,31 @@ __device__ __forceinline__ float time_step(float raw, float bias, int use_softpl
     return d;
 }
 
-// ---------------------------------------------------------------- MFMA ----
-template <typename OP> struct Mfma;
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-template <> struct Mfma<bf16> {
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, so a register prefetch issued before it stays in
+// flight across the barrier.  Global memory written before it is not made
+// visible to other waves (no kernel here relies on that).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ------------------------------------------------------------- operands ----
+template <typename IO> struct Op { typedef float type; };
+template <> struct Op<bf16> { typedef f16 type; };
+
+template <typename OP> struct Mfma;
+template <> struct Mfma<f16> {
     static constexpr int K = 32;   // contraction length of one instruction
     static constexpr int KPL = 8;  // contraction elements per lane
-    static constexpr int PAD = 8;  // LDS row padding (elements): 16 bytes
-    typedef bf16x8 frag;
+    static constexpr int PAD = 8;  // row-major LDS row padding (16 bytes)
+    typedef f16x8 frag;
     __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
 };
-
 template <> struct Mfma<float> {
     static constexpr int K = 4;
     static constexpr int KPL = 1;
@@ -72,8 +91,7 @@ template <> struct Mfma<float> {
     }
 };
 
-// Fragment of an LDS matrix M[row][k] (k contiguous, row stride ld): lane l
-// reads row `row0 + (l & 15)` at k = k0 + KPL * (l >> 4).
+// Row-major fragment of an LDS matrix M[row][k] (k contiguous, row stride ld).
 template <typename OP>
 __device__ __forceinline__ typename Mfma<OP>::frag
 lds_frag(const OP *M, int ld, int row0, int k0, int lane) {
@@ -81,68 +99,117 @@ lds_frag(const OP *M, int ld, int row0, int k0, int lane) {
     return *reinterpret_cast<const typename Mfma<OP>::frag *>(p);
 }
 
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// ------------------------------------------------------- 8x8 staging ------
-// A thread moves one 8 x 8 block of a row-major global matrix (8 rows of 8
-// consecutive elements) into LDS, either in the same orientation or
-// transposed (so that the former row index becomes contiguous).
-
-template <typename IO> struct Row8;
-template <> struct Row8<bf16> {
-    typedef bf16x8 vec;  // 16 bytes
-};
-template <> struct Row8<float> {
-    struct vec { f32x4 lo, hi; };  // 32 bytes
-};
-
-template <typename IO>
-__device__ __forceinline__ typename Row8<IO>::vec load_row8(const IO *p) {
-    return *reinterpret_cast<const typename Row8<IO>::vec *>(p);
-}
-template <typename IO> __device__ __forceinline__ typename Row8<IO>::vec zero_row8() {
-    typename Row8<IO>::vec v;
-    __builtin_memset(&v, 0, sizeof(v));
-    return v;
+// Operands stored k-major in LDS (M[k][col], col contiguous) are read with
+// the gfx950 transposing LDS load ds_read_b64_tr_b16: inside each group of
+// 16 lanes, lane 4r + c supplies the address of elements 4c..4c+3 of row r
+// of a 4 x 16 tile, and lane i receives column i of the tile's 4 rows.
+// lds_tr4 returns, for lane l (group g), M[k0 + 4g + r][c0 + (l & 15)],
+// r = 0..3.
+typedef __fp16 fp16x4_raw __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_raw lds_fp16x4;
+__device__ __forceinline__ f16x4 lds_tr4(const f16 *M, int ld, int k0, int c0, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const f16 *p = M + (k0 + 4 * g + (j >> 2)) * ld + c0 + 4 * (j & 3);
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p));
 }
 
-__device__ __forceinline__ float row8_get(const Row8<bf16>::vec &v, int e) { return (float)v[e]; }
-__device__ __forceinline__ float row8_get(const Row8<float>::vec &v, int e) {
-    return e < 4 ? v.lo[e] : v.hi[e - 4];
+// Contraction-order convention for k-major operands.  Within a block of 32
+// contraction indices starting at kb, lane group g of an fp16 fragment
+// carries k = kb + 4g + r (elements 0..3) and kb + 16 + 4g + r (elements
+// 4..7); an fp32 MFMA step q (0..7) carries k = kb + 16 (q >> 2) + 4g + (q & 3).
+// Both operands of a product use the same convention, so the sum is the same
+// as in natural order.  The accumulator layout of 16 x 16 tiles (lane l holds
+// rows 4g + r of column l & 15) produces values in exactly this order, so a
+// product's result can feed the next product straight from registers.
+__device__ __forceinline__ f16x8 frag_kmajor(const f16 *M, int ld, int kb, int, int c0,
+                                             int lane) {
+    const f16x4 a = lds_tr4(M, ld, kb, c0, lane);
+    const f16x4 b = lds_tr4(M, ld, kb + 16, c0, lane);
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ float frag_kmajor(const float *M, int ld, int kb, int q, int c0,
+                                             int lane) {
+    return M[(kb + 16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)) * ld + c0 + (lane & 15)];
 }
 
-// Store 8 values (fp32 in registers) to LDS as OP, contiguous.
-template <typename OP> __device__ __forceinline__ void lds_store8(OP *dst, const float *v);
-template <> __device__ __forceinline__ void lds_store8<bf16>(bf16 *dst, const float *v) {
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
-    *reinterpret_cast<bf16x8 *>(dst) = o;
+// Column c0 + (lane & 15), rows k0 + 4g + r (r = 0..3) of a k-major matrix:
+// the accumulator layout of a tile.
+__device__ __forceinline__ f32x4 lds_col4(const f16 *M, int ld, int k0, int c0, int lane) {
+    const f16x4 v = lds_tr4(M, ld, k0, c0, lane);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
-template <> __device__ __forceinline__ void lds_store8<float>(float *dst, const float *v) {
-    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+__device__ __forceinline__ f32x4 lds_col4(const float *M, int ld, int k0, int c0, int lane) {
+    const float *p = M + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
 
-// Store 4 fp32 values to LDS as OP, contiguous (8 or 16 bytes).
-template <typename OP> __device__ __forceinline__ void lds_store4(OP *dst, f32x4 v);
-template <> __device__ __forceinline__ void lds_store4<bf16>(bf16 *dst, f32x4 v) {
-    bf16x4 o;
-    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
-    *reinterpret_cast<bf16x4 *>(dst) = o;
+// An A fragment made from two accumulator tiles (contraction blocks jt = 0, 1
+// of a 32-block) in the k-major convention above (round to nearest).
+template <typename OP>
+__device__ __forceinline__ typename Mfma<OP>::frag frag_from_acc(const f32x4 &t0,
+                                                                 const f32x4 &t1, int q);
+template <>
+__device__ __forceinline__ f16x8 frag_from_acc<f16>(const f32x4 &t0, const f32x4 &t1, int) {
+    return f16x8{(f16)t0[0], (f16)t0[1], (f16)t0[2], (f16)t0[3],
+                 (f16)t1[0], (f16)t1[1], (f16)t1[2], (f16)t1[3]};
 }
-template <> __device__ __forceinline__ void lds_store4<float>(float *dst, f32x4 v) {
+template <>
+__device__ __forceinline__ float frag_from_acc<float>(const f32x4 &t0, const f32x4 &t1, int q) {
+    return (q >> 2) ? t1[q & 3] : t0[q & 3];
+}
+
+// Store 4 fp32 values to LDS as an operand type (round to nearest), contiguous.
+__device__ __forceinline__ void lds_store4(f16 *dst, f32x4 v) {
+    *reinterpret_cast<f16x4 *>(dst) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+}
+__device__ __forceinline__ void lds_store4(float *dst, f32x4 v) {
     *reinterpret_cast<f32x4 *>(dst) = v;
 }
 
-// Load 4 contiguous OP values from LDS as fp32.
-template <typename OP> __device__ __forceinline__ f32x4 lds_load4(const OP *src);
-template <> __device__ __forceinline__ f32x4 lds_load4<bf16>(const bf16 *src) {
-    bf16x4 v = *reinterpret_cast<const bf16x4 *>(src);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+// ---------------------------------------------------------- row pieces ----
+// 8 consecutive elements of one row, moved with vector loads and stores.
+template <typename T> struct alignas(16) Row8v { T e[8]; };
+
+template <typename T> __device__ __forceinline__ Row8v<T> ld_row8(const T *p) {
+    return *reinterpret_cast<const Row8v<T> *>(p);
 }
-template <> __device__ __forceinline__ f32x4 lds_load4<float>(const float *src) {
-    return *reinterpret_cast<const f32x4 *>(src);
+template <typename T> __device__ __forceinline__ void st_row8(T *dst, const Row8v<T> &v) {
+    *reinterpret_cast<Row8v<T> *>(dst) = v;
+}
+
+// Input piece -> operand piece, or zeros when !keep.  bf16 -> fp16 uses the
+// packed round-toward-zero conversion, which is exact for every bf16 value in
+// fp16's normal range.  The select is applied only here, when the value is
+// consumed, so the load that filled v is not waited for any earlier.
+__device__ __forceinline__ Row8v<f16> to_op(const Row8v<bf16> &v, bool keep) {
+    Row8v<f16> o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const auto pk = __builtin_amdgcn_cvt_pkrtz(keep ? (float)v.e[e] : 0.f,
+                                                   keep ? (float)v.e[e + 1] : 0.f);
+        o.e[e] = pk[0];
+        o.e[e + 1] = pk[1];
+    }
+    return o;
+}
+__device__ __forceinline__ Row8v<float> to_op(const Row8v<float> &v, bool keep) {
+    Row8v<float> o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.e[e] = keep ? v.e[e] : 0.f;
+    return o;
+}
+// w * v as an operand piece (round to nearest).
+__device__ __forceinline__ Row8v<f16> to_op_scaled(const Row8v<bf16> &v, float w) {
+    Row8v<f16> o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.e[e] = (f16)((float)v.e[e] * w);
+    return o;
+}
+__device__ __forceinline__ Row8v<float> to_op_scaled(const Row8v<float> &v, float w) {
+    Row8v<float> o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.e[e] = v.e[e] * w;
+    return o;
 }
 
 // ----------------------------------------------- workgroup -> work item ----

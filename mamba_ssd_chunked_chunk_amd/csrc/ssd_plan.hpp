@@ -8,8 +8,8 @@
 
 namespace ssd {
 
-// Rows are processed in blocks of T rows (T = 64 for bf16 operands, 32 for
-// fp32).  A block never straddles a chunk boundary: chunk c owns padded rows
+// Rows are processed in blocks of T = 32 rows.  A block never straddles a
+// chunk boundary: chunk c owns padded rows
 // [c * Qp, (c + 1) * Qp) with Qp = ceil(Q / T) * T; padded rows past the end
 // of a chunk or of the sequence carry d = 0 (no write, no decay).
 struct ScanPlan {
@@ -37,7 +37,7 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     if (b < 0 || l < 0 || h <= 0 || p <= 0 || n <= 0 || g <= 0 || Q <= 0) return false;
     if (h % g != 0) return false;
     P.b = b; P.l = l; P.h = h; P.p = p; P.n = n; P.g = g; P.Q = Q; P.io = io;
-    P.T = (io == 1) ? 64 : 32;
+    P.T = 32;
     P.nc = (l + Q - 1) / Q;
     P.nsb = (Q + P.T - 1) / P.T;
     P.Qp = P.nsb * P.T;

@@ -8,12 +8,12 @@
 // state, and the state entering every chunk is stored as one boundary-state
 // tensor (nnterp, "The state after every token").
 //
-// Rows are handled in blocks of T rows that never straddle a chunk boundary.
-// With lcs_i the cumulative log2 decay inside a block (inclusive) and H the
-// state entering the block:
-//   y_i   = sum_{j<=i} (C_i . B_j) 2^(lcs_i - lcs_j) d_j x_j
-//           + 2^lcs_i C_i^T H + D x_i                         (intra + read)
-//   H'    = 2^lcs_last H + sum_j 2^(lcs_last - lcs_j) d_j B_j x_j^T  (write)
+// Rows are handled in blocks of kT = 32 rows that never straddle a chunk
+// boundary.  With lcs_i the cumulative log2 decay inside a block (inclusive)
+// and H the state entering the block:
+//   y_i = sum_{j<=i} (C_i . B_j) 2^(lcs_i - lcs_j) d_j x_j
+//         + 2^lcs_i C_i^T H + D x_i                          (intra + read)
+//   H'  = 2^lcs_last H + sum_j B_j (2^(lcs_last - lcs_j) d_j x_j)^T   (write)
 // Every exponent is <= 0 when A <= 0; the j > i half is removed by a select
 // before any exponential is taken, so no inf * 0 can arise.
 //
@@ -32,28 +32,7 @@
 
 namespace ssd {
 
-template <typename IO> struct Blk { static constexpr int T = 64; };
-template <> struct Blk<float> { static constexpr int T = 32; };
-
-// 8 consecutive elements of a row, loaded with vector loads.
-template <typename IO> struct alignas(16) Row8v { IO e[8]; };
-
-template <typename IO>
-__device__ __forceinline__ Row8v<IO> ld_row8(const IO *p, bool valid) {
-    Row8v<IO> v;
-    if (valid) {
-        v = *reinterpret_cast<const Row8v<IO> *>(p);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v.e[e] = from_f32<IO>(0.f);
-    }
-    return v;
-}
-
-template <typename IO>
-__device__ __forceinline__ void st_row8(IO *dst, const Row8v<IO> &v) {
-    *reinterpret_cast<Row8v<IO> *>(dst) = v;
-}
+constexpr int kT = 32;  // rows per block
 
 // ----------------------------------------------------------------------------
 // 1. Time step and per-block cumulative log2 decay.
@@ -65,7 +44,7 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
     const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
     int softplus, float dt_min, float dt_max, int64_t l, int h, int64_t Q, int64_t nc,
     int64_t Qp, float *__restrict__ lcs, float *__restrict__ dtp) {
-    constexpr int T = Blk<IO>::T;
+    constexpr int T = kT;
     const int64_t c = blockIdx.x, b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hh = blockIdx.z * kWaves + wave;
@@ -93,16 +72,101 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(
 }
 
 // ----------------------------------------------------------------------------
+// Staging of the state pass: one slab = SLAB blocks of kT rows.  Pieces are
+// 8 consecutive elements of one row of x (P / 8 per row) or of the
+// workgroup's NW-column slice of B (NW / 8 per row).  The prefetch only
+// issues loads (row index clamped to a readable row) and records which
+// pieces are real rows; conversions and selects happen in the stage step,
+// so nothing waits on a load before it is needed.
+template <typename IO, int P, int NW, int SLAB> struct SpBuf {
+    static constexpr int NPX = SLAB * kT * P / 8, NPB = SLAB * kT * NW / 8;
+    static constexpr int KX = (NPX + kThreads - 1) / kThreads;
+    static constexpr int KB = (NPB + kThreads - 1) / kThreads;
+    Row8v<IO> xv[KX], bv[KB];
+    float xl[KX], xd[KX], xe[KX];  // lcs, d of the x piece's row; lcs at its block end
+    float lam[SLAB];               // log2 decay of each block of the slab
+    uint32_t okx, okb;             // bit k: piece k is a real row
+};
+
+template <typename IO, int P, int NW, int SLAB>
+__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, NW, SLAB> &f, int64_t s0, int64_t sb1,
+                                            int64_t nsb, const IO *xb, const IO *Bb,
+                                            const float *lcs_bh, const float *dtp_bh, int64_t l,
+                                            int64_t Q, int64_t xstride, int64_t bstride, int tid) {
+    typedef SpBuf<IO, P, NW, SLAB> F;
+    constexpr int T = kT;
+    const int nb = (int)((sb1 - s0) < SLAB ? (sb1 - s0) : SLAB);
+    f.okx = 0;
+    f.okb = 0;
+#pragma unroll
+    for (int k = 0; k < F::KX; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPX % kThreads == 0 || q < F::NPX) {
+            const int j = q / (P / 8), cc = q % (P / 8), jb = j / T;
+            const int64_t sb = s0 + (jb < nb ? jb : 0);
+            const int64_t rp = (sb % nsb) * T + (j % T), t = (sb / nsb) * Q + rp;
+            const bool ok = jb < nb && rp < Q && t < l;
+            f.xv[k] = ld_row8(xb + (ok ? t : 0) * xstride + cc * 8);
+            const int64_t R = sb * T + (j % T);
+            f.xl[k] = lcs_bh[R];
+            f.xd[k] = dtp_bh[R];
+            f.xe[k] = lcs_bh[sb * T + T - 1];
+            f.okx |= (uint32_t)ok << k;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < F::KB; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPB % kThreads == 0 || q < F::NPB) {
+            const int j = q / (NW / 8), cc = q % (NW / 8), jb = j / T;
+            const int64_t sb = s0 + (jb < nb ? jb : 0);
+            const int64_t rp = (sb % nsb) * T + (j % T), t = (sb / nsb) * Q + rp;
+            const bool ok = jb < nb && rp < Q && t < l;
+            f.bv[k] = ld_row8(Bb + (ok ? t : 0) * bstride + cc * 8);
+            f.okb |= (uint32_t)ok << k;
+        }
+    }
+#pragma unroll
+    for (int jb = 0; jb < SLAB; ++jb) f.lam[jb] = lcs_bh[(s0 + (jb < nb ? jb : 0)) * T + T - 1];
+}
+
+template <typename IO, int P, int NW, int SLAB>
+__device__ __forceinline__ void sp_stage(const SpBuf<IO, P, NW, SLAB> &f,
+                                         typename Op<IO>::type *Xw,
+                                         typename Op<IO>::type *Bs, int tid) {
+    typedef SpBuf<IO, P, NW, SLAB> F;
+    constexpr int LDX = P + 16, LDB = NW + 16;
+#pragma unroll
+    for (int k = 0; k < F::KX; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPX % kThreads == 0 || q < F::NPX) {
+            const bool ok = (f.okx >> k) & 1;
+            const float w = ok ? exp2_fast(f.xe[k] - f.xl[k]) * f.xd[k] : 0.f;
+            st_row8(Xw + (q / (P / 8)) * LDX + (q % (P / 8)) * 8, to_op_scaled(f.xv[k], w));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < F::KB; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPB % kThreads == 0 || q < F::NPB)
+            st_row8(Bs + (q / (NW / 8)) * LDB + (q % (NW / 8)) * 8,
+                    to_op(f.bv[k], (f.okb >> k) & 1));
+    }
+}
+
+// ----------------------------------------------------------------------------
 // 2. Chunk states and the serial pass over chunks.
-//    One workgroup per (batch, segment, head, 32-row slice of the state).
-//    The slice H[n0:n0+32, :] lives in MFMA accumulators for the whole
-//    segment; each iteration stages up to 4 blocks (x^T and the weighted
-//    B^T) in LDS and applies, block by block,
-//        H <- 2^lcs_last H + (w B)^T x,  w_j = 2^(lcs_last - lcs_j) d_j.
-//    Before the first block of every chunk the slice is written out as that
-//    chunk's boundary state.  Segment 0 starts from init_state; later
-//    segments start from zero and are corrected by k_seg_combine and in
-//    k_chunk_out.
+//    One workgroup per (batch, segment, head, NW-row slice of the state).  The
+//    slice H[n0:n0+NW, :] lives in MFMA accumulators for the whole segment.
+//    Each iteration takes a slab of up to SLAB row blocks: B (raw) and the
+//    decay-weighted x (w_j x_j, w_j = 2^(lcs_last - lcs_j) d_j) are copied row
+//    by row into LDS while the next slab is already being fetched, then block
+//    by block
+//        H <- 2^lcs_last H + B^T (w x)      (contraction over the block rows)
+//    with both operands read k-major through transposing LDS loads.  Before
+//    the first block of every chunk the slice is written out as that chunk's
+//    boundary state.  Segment 0 starts from init_state; later segments start
+//    from zero and are corrected by k_seg_combine and in k_chunk_out.
 template <typename IO, int P, int N>
 __global__ __launch_bounds__(256) void k_state_pass(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const float *__restrict__ lcs,
@@ -110,18 +174,19 @@ __global__ __launch_bounds__(256) void k_state_pass(
     float *__restrict__ Eseg, float *__restrict__ Dlog, float *__restrict__ Lseg,
     float *__restrict__ final_state, int64_t l, int h, int g, int64_t Q, int64_t nc,
     int64_t Qp, int64_t cps, int64_t nseg) {
-    typedef Mfma<IO> M;
-    constexpr int T = Blk<IO>::T;
+    typedef typename Op<IO>::type OP;
+    typedef Mfma<OP> M;
+    constexpr int T = kT;
+    constexpr int KS = T / M::K;            // MFMA steps per block
     constexpr int NW = 32;                  // state rows per workgroup
     constexpr int NSPLIT = N / NW;
     constexpr int SLAB = 4;                 // blocks per iteration
-    constexpr int LDK = SLAB * T + M::PAD;  // LDS row: contraction axis
+    constexpr int SR = SLAB * T;            // rows per slab
+    constexpr int LDX = P + 16, LDB = NW + 16;
     constexpr int TILES = (NW / 16) * (P / 16);
     constexpr int TPW = (TILES + kWaves - 1) / kWaves;
-    constexpr int XBLK = (T / 8) * (P / 8);
-    constexpr int BBLK = (T / 8) * (NW / 8);
-    __shared__ __attribute__((aligned(16))) IO XT[P * LDK];
-    __shared__ __attribute__((aligned(16))) IO BT[NW * LDK];
+    __shared__ __attribute__((aligned(16))) OP Xw[SR * LDX];  // w x  [row][p]
+    __shared__ __attribute__((aligned(16))) OP Bs[SR * LDB];  // B    [row][n - n0]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
@@ -141,71 +206,38 @@ __global__ __launch_bounds__(256) void k_state_pass(
 
     f32x4 acc[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        acc[i] = zero4();
-        const int ti = wave + kWaves * i;
-        if (ti < TILES && seg == 0 && init) {
+    for (int i = 0; i < TPW; ++i) acc[i] = zero4();
+    if (seg == 0 && init) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int ti = wave + kWaves * i;
             const int tr = ti / (P / 16), tc = ti % (P / 16);
             const float *src = init + (b * h + hh) * NP +
                                (int64_t)(n0 + tr * 16 + 4 * (lane >> 4)) * P + tc * 16 + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][r] = src[r * P];
+            for (int r = 0; r < 4; ++r) acc[i][r] = ti < TILES ? src[r * P] : 0.f;
         }
     }
     float logdec = 0.f;
 
+    SpBuf<IO, P, NW, SLAB> pf;
+    const IO *xb = x + (b * l * h + hh) * P;         // row t at xb + t * h * P
+    const IO *Bb = Bm + (b * l * g + gi) * N + n0;    // row t at Bb + t * g * N
+    if (sb0 < sb1)
+        sp_prefetch(pf, sb0, sb1, nsb, xb, Bb, lcs_bh, dtp_bh, l, Q, (int64_t)h * P,
+                    (int64_t)g * N, tid);
     for (int64_t s0 = sb0; s0 < sb1; s0 += SLAB) {
         const int nb = (int)((sb1 - s0) < SLAB ? (sb1 - s0) : SLAB);
-        // ---- stage x^T and (w B)^T of nb blocks
-        for (int q = tid; q < nb * (XBLK + BBLK); q += kThreads) {
-            const int j = q / (XBLK + BBLK);
-            int rem = q % (XBLK + BBLK);
-            const int64_t sb = s0 + j;
-            const int64_t c = sb / nsb;
-            const int64_t rpb = (sb % nsb) * T;  // padded row (in chunk) of block start
-            if (rem < XBLK) {
-                const int rb = rem / (P / 8), cb = rem % (P / 8);
-                Row8v<IO> v[8];
+        float lam[SLAB];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int64_t rp = rpb + rb * 8 + r, t = c * Q + rp;
-                    const bool ok = rp < Q && t < l;
-                    v[r] = ld_row8(x + ((b * l + (ok ? t : 0)) * h + hh) * P + cb * 8, ok);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Row8v<IO> o;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) o.e[r] = v[r].e[e];
-                    st_row8(XT + (cb * 8 + e) * LDK + j * T + rb * 8, o);
-                }
-            } else {
-                rem -= XBLK;
-                const int rb = rem / (NW / 8), cb = rem % (NW / 8);
-                const float last = lcs_bh[sb * T + T - 1];
-                float w[8];
-                Row8v<IO> v[8];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int64_t R = sb * T + rb * 8 + r;
-                    w[r] = exp2_fast(last - lcs_bh[R]) * dtp_bh[R];
-                    const int64_t rp = rpb + rb * 8 + r, t = c * Q + rp;
-                    const bool ok = rp < Q && t < l;
-                    v[r] = ld_row8(Bm + ((b * l + (ok ? t : 0)) * g + gi) * N + n0 + cb * 8, ok);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Row8v<IO> o;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) o.e[r] = from_f32<IO>(to_f32(v[r].e[e]) * w[r]);
-                    st_row8(BT + (cb * 8 + e) * LDK + j * T + rb * 8, o);
-                }
-            }
-        }
-        __syncthreads();
-        // ---- apply the blocks in order
-        for (int j = 0; j < nb; ++j) {
-            const int64_t sb = s0 + j;
+        for (int jb = 0; jb < SLAB; ++jb) lam[jb] = pf.lam[jb];
+        sp_stage(pf, Xw, Bs, tid);
+        if (s0 + SLAB < sb1)
+            sp_prefetch(pf, s0 + SLAB, sb1, nsb, xb, Bb, lcs_bh, dtp_bh, l, Q, (int64_t)h * P,
+                        (int64_t)g * N, tid);
+        lds_barrier();
+        for (int jb = 0; jb < nb; ++jb) {
+            const int64_t sb = s0 + jb;
             if (sb % nsb == 0) {  // first block of a chunk: emit the boundary state
                 const int64_t c = sb / nsb;
                 float *dst = Hb + ((b * nc + c) * h + hh) * NP;
@@ -222,26 +254,24 @@ __global__ __launch_bounds__(256) void k_state_pass(
                 }
                 if (nseg > 1 && split == 0 && tid == 0) Dlog[(b * h + hh) * nc + c] = logdec;
             }
-            const float lam = lcs_bh[sb * T + T - 1];
-            const float decay = exp2_fast(lam);
-            logdec += lam;
+            const float decay = exp2_fast(lam[jb]);
+            logdec += lam[jb];
 #pragma unroll
             for (int i = 0; i < TPW; ++i) acc[i] *= decay;
 #pragma unroll
-            for (int kk = 0; kk < T / M::K; ++kk) {
+            for (int q = 0; q < KS; ++q) {
 #pragma unroll
                 for (int i = 0; i < TPW; ++i) {
                     const int ti = wave + kWaves * i;
                     if (ti < TILES) {
                         const int tr = ti / (P / 16), tc = ti % (P / 16);
-                        const auto fa = lds_frag(BT, LDK, tr * 16, j * T + kk * M::K, lane);
-                        const auto fb = lds_frag(XT, LDK, tc * 16, j * T + kk * M::K, lane);
-                        acc[i] = M::mma(fa, fb, acc[i]);
+                        acc[i] = M::mma(frag_kmajor(Bs, LDB, jb * T, q, tr * 16, lane),
+                                        frag_kmajor(Xw, LDX, jb * T, q, tc * 16, lane), acc[i]);
                     }
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     float *out = nullptr;
@@ -281,23 +311,120 @@ static __global__ __launch_bounds__(256) void k_seg_combine(float *__restrict__ 
     if (idx >= bh * np4) return;
     const int64_t pair = idx / np4, e4 = idx % np4;
     const int64_t b = pair / h, hh = pair % h;
-    f32x4 *E = reinterpret_cast<f32x4 *>(Eseg);
-    auto slot = [&](int64_t k) { return ((b * nseg + k) * h + hh) * np4 + e4; };
-    f32x4 H = E[slot(0)];
+    f32x4 *E = reinterpret_cast<f32x4 *>(Eseg) + (b * nseg * h + hh) * np4 + e4;
+    const int64_t stride = (int64_t)h * np4;  // from one segment slot to the next
+    f32x4 H = E[0];
     for (int64_t k = 1; k < nseg; ++k) {
-        const f32x4 Ek = E[slot(k)];
-        E[slot(k - 1)] = H;
+        const f32x4 Ek = E[k * stride];
+        E[(k - 1) * stride] = H;
         H = exp2_fast(Lseg[pair * nseg + k]) * H + Ek;
     }
     if (final_state) reinterpret_cast<f32x4 *>(final_state)[pair * np4 + e4] = H;
 }
 
 // ----------------------------------------------------------------------------
+// Staging of the chunk output: one block of kT rows.  Pieces are 8
+// consecutive elements of one row of C and of B (same row and columns, N / 8
+// per row) or of x (P / 8 per row).  As in the state pass, the prefetch only
+// issues loads and records which pieces are real rows.
+template <typename IO, int P, int N> struct CoBuf {
+    static constexpr int NPC = kT * N / 8, NPX = kT * P / 8;
+    static constexpr int KC = (NPC + kThreads - 1) / kThreads;
+    static constexpr int KX = (NPX + kThreads - 1) / kThreads;
+    Row8v<IO> cv[KC], bv[KC], xv[KX];
+    float xl[KX], xd[KX];  // lcs and d of the x piece's row
+    float last, ls, ds;    // lcs at the block end; lcs and d of row tid (tid < kT)
+    uint32_t okc, okx;
+};
+
+template <typename IO, int P, int N>
+__device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N> &f, int s, const IO *xb,
+                                            const IO *Bb, const IO *Cb, const float *lcs_c,
+                                            const float *dtp_c, int64_t t0, int64_t l, int64_t Q,
+                                            int64_t xstride, int64_t bstride, int tid) {
+    typedef CoBuf<IO, P, N> F;
+    constexpr int T = kT;
+    const int64_t rpb = (int64_t)s * T;
+    f.okc = 0;
+    f.okx = 0;
+#pragma unroll
+    for (int k = 0; k < F::KC; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPC % kThreads == 0 || q < F::NPC) {
+            const int j = q / (N / 8), cc = q % (N / 8);
+            const int64_t rp = rpb + j, t = t0 + rp;
+            const bool ok = rp < Q && t < l;
+            const int64_t off = (ok ? t : 0) * bstride + cc * 8;
+            f.cv[k] = ld_row8(Cb + off);
+            f.bv[k] = ld_row8(Bb + off);
+            f.okc |= (uint32_t)ok << k;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < F::KX; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPX % kThreads == 0 || q < F::NPX) {
+            const int j = q / (P / 8), cc = q % (P / 8);
+            const int64_t rp = rpb + j, t = t0 + rp;
+            const bool ok = rp < Q && t < l;
+            f.xv[k] = ld_row8(xb + (ok ? t : 0) * xstride + cc * 8);
+            f.xl[k] = lcs_c[rp];
+            f.xd[k] = dtp_c[rp];
+            f.okx |= (uint32_t)ok << k;
+        }
+    }
+    f.last = lcs_c[rpb + T - 1];
+    const int64_t rt = rpb + (tid < T ? tid : 0);
+    f.ls = lcs_c[rt];
+    f.ds = dtp_c[rt];
+}
+
+template <typename IO, int P, int N>
+__device__ __forceinline__ void co_stage(const CoBuf<IO, P, N> &f, typename Op<IO>::type *Cs,
+                                         typename Op<IO>::type *Bs, typename Op<IO>::type *Xs,
+                                         typename Op<IO>::type *Xw, float *lcs_s, float *d_s,
+                                         int tid) {
+    typedef CoBuf<IO, P, N> F;
+    typedef typename Op<IO>::type OP;
+    constexpr int LDN = N + Mfma<OP>::PAD, LDX = P + 16;
+#pragma unroll
+    for (int k = 0; k < F::KC; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPC % kThreads == 0 || q < F::NPC) {
+            const int o = (q / (N / 8)) * LDN + (q % (N / 8)) * 8;
+            const bool ok = (f.okc >> k) & 1;
+            st_row8(Cs + o, to_op(f.cv[k], ok));
+            st_row8(Bs + o, to_op(f.bv[k], ok));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < F::KX; ++k) {
+        const int q = tid + k * kThreads;
+        if (F::NPX % kThreads == 0 || q < F::NPX) {
+            const int o = (q / (P / 8)) * LDX + (q % (P / 8)) * 8;
+            const bool ok = (f.okx >> k) & 1;
+            st_row8(Xs + o, to_op(f.xv[k], ok));
+            const float w = ok ? exp2_fast(f.last - f.xl[k]) * f.xd[k] : 0.f;
+            st_row8(Xw + o, to_op_scaled(f.xv[k], w));
+        }
+    }
+    if (tid < kT) {
+        lcs_s[tid] = f.ls;
+        d_s[tid] = f.ds;
+    }
+}
+
+// ----------------------------------------------------------------------------
 // 4. Chunk output.  One workgroup per (batch, chunk, head); the blocks of the
 //    chunk are taken in order with the running state H in MFMA accumulators
-//    (fp32) and, as the bf16/fp32 operand copy H^T, in LDS.  Per block:
-//      G^T = B C^T (causal tiles), P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i),
-//      Y = 2^lcs_i (C H) + P x + D x,  then H <- 2^lcs_last H + (w B)^T x.
+//    (fp32) and, as the operand copy H^T, in LDS.  Per block, with C, B, x and
+//    the decay-weighted x staged row by row while the next block is already
+//    being fetched:
+//      G^T = B C^T on the causal tiles of the wave's row strip, and
+//      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i), kept in registers;
+//      Y = 2^lcs_i (C H) + P x + D x, written to y;
+//      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
+//    Two workgroup barriers per block.
 template <typename IO, int P, int N>
 __global__ __launch_bounds__(256) void k_chunk_out(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
@@ -305,29 +432,27 @@ __global__ __launch_bounds__(256) void k_chunk_out(
     const float *__restrict__ Hb, const float *__restrict__ Hin, const float *__restrict__ Dlog,
     IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp,
     int64_t cps, int64_t nseg) {
-    typedef Mfma<IO> M;
-    constexpr int T = Blk<IO>::T;
-    constexpr int LDN = N + M::PAD;  // rows with the state index contiguous
-    constexpr int LDT = T + M::PAD;  // rows with the block-row index contiguous
-    constexpr int BSZ = (T * LDN > T * LDT) ? T * LDN : T * LDT;
-    constexpr int HTILES = (N / 16) * (P / 16);
+    typedef typename Op<IO>::type OP;
+    typedef Mfma<OP> M;
+    constexpr int T = kT;
+    constexpr int KS = T / M::K;          // MFMA steps over the block rows
+    constexpr int NS = N / M::K;          // MFMA steps over the state index
+    constexpr int LDN = N + M::PAD;       // [row][n]: C, B (row-major and k-major), H^T
+    constexpr int LDX = P + 16;           // k-major [row][p]: x, w x
+    constexpr int CT = P / 16;            // column tiles of y and H
+    constexpr int HTILES = (N / 16) * CT;
     constexpr int HPW = (HTILES + kWaves - 1) / kWaves;
-    constexpr int RT = T / 16;                       // row tiles per block
-    constexpr int GTILES = RT * (RT + 1) / 2;        // causal tiles of P
-    constexpr int GPW = (GTILES + kWaves - 1) / kWaves;
-    constexpr int YTILES = RT * (P / 16);
-    constexpr int YPW = (YTILES + kWaves - 1) / kWaves;
-    constexpr int CBLK = (T / 8) * (N / 8);
-    constexpr int XBLK = (T / 8) * (P / 8);
-    __shared__ __attribute__((aligned(16))) IO Cs[T * LDN];   // C    [row][n]
-    __shared__ __attribute__((aligned(16))) IO BP[BSZ];       // B [row][n], then P [i][j]
-    __shared__ __attribute__((aligned(16))) IO BTw[N * LDT];  // (w B)^T [n][row]
-    __shared__ __attribute__((aligned(16))) IO XT[P * LDT];   // x^T  [p][row]
-    __shared__ __attribute__((aligned(16))) IO HT[P * LDN];   // H^T  [p][n]
+    constexpr int YPW = CT >= 2 ? CT / 2 : 1;  // y tiles per wave (one row strip)
+    __shared__ __attribute__((aligned(16))) OP Cs[T * LDN];   // C    [row][n]
+    __shared__ __attribute__((aligned(16))) OP Bs[T * LDN];   // B    [row][n]
+    __shared__ __attribute__((aligned(16))) OP Xs[T * LDX];   // x    [row][p]
+    __shared__ __attribute__((aligned(16))) OP Xw[T * LDX];   // w x  [row][p]
+    __shared__ __attribute__((aligned(16))) OP HT[P * LDN];   // H^T  [p][n]
     __shared__ float lcs_s[T];
     __shared__ float d_s[T];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lg = lane >> 4, li = lane & 15;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
     const int hh = (int)(item % h); item /= h;
     const int64_t c = item % nc;
@@ -338,168 +463,108 @@ __global__ __launch_bounds__(256) void k_chunk_out(
     const float *lcs_c = lcs + ((b * h + hh) * nc + c) * Qp;
     const float *dtp_c = dtp + ((b * h + hh) * nc + c) * Qp;
     const float Dh = D ? D[hh] : 0.f;
+    const int64_t rows = (Q < l - c * Q) ? Q : (l - c * Q);  // valid rows of this chunk
+    const int nblk = (int)((rows + T - 1) / T);
+    // the wave's row strip and y tiles
+    const bool yact = CT >= 2 || wave < 2;
+    const int it = CT >= 2 ? (wave >> 1) : wave;
+    const int pt0 = CT >= 2 ? (wave & 1) * (CT / 2) : 0;
 
-    // ---- state entering the chunk
+    CoBuf<IO, P, N> pf;
+    const IO *xb = x + (b * l * h + hh) * P;        // row t at xb + t * h * P
+    const IO *Bb = Bm + (b * l * g + gi) * N;        // row t at Bb + t * g * N
+    const IO *Cb = Cm + (b * l * g + gi) * N;
+    if (nblk > 0)
+        co_prefetch(pf, 0, xb, Bb, Cb, lcs_c, dtp_c, c * Q, l, Q, (int64_t)h * P, (int64_t)g * N,
+                    tid);
+
+    // ---- state entering the chunk (all loads issued before any is used)
     f32x4 accH[HPW];
     {
         const float *hb = Hb + ((b * nc + c) * h + hh) * NP;
-        const float *hin = nullptr;
-        float corr = 0.f;
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int ti = wave + kWaves * i;
+            const int tr = ti / CT, tc = ti % CT;
+            const int64_t off = (int64_t)(tr * 16 + 4 * lg) * P + tc * 16 + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accH[i][r] = ti < HTILES ? hb[off + r * P] : 0.f;
+        }
         if (seg > 0) {
-            hin = Hin + ((b * nseg + seg - 1) * h + hh) * NP;
-            corr = exp2_fast(Dlog[(b * h + hh) * nc + c]);
+            const float *hin = Hin + ((b * nseg + seg - 1) * h + hh) * NP;
+            f32x4 iv[HPW];
+#pragma unroll
+            for (int i = 0; i < HPW; ++i) {
+                const int ti = wave + kWaves * i;
+                const int tr = ti / CT, tc = ti % CT;
+                const int64_t off = (int64_t)(tr * 16 + 4 * lg) * P + tc * 16 + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) iv[i][r] = ti < HTILES ? hin[off + r * P] : 0.f;
+            }
+            const float corr = exp2_fast(Dlog[(b * h + hh) * nc + c]);
+#pragma unroll
+            for (int i = 0; i < HPW; ++i) accH[i] += corr * iv[i];
         }
 #pragma unroll
         for (int i = 0; i < HPW; ++i) {
-            accH[i] = zero4();
             const int ti = wave + kWaves * i;
             if (ti < HTILES) {
-                const int tr = ti / (P / 16), tc = ti % (P / 16);
-                const int64_t off = (int64_t)(tr * 16 + 4 * (lane >> 4)) * P + tc * 16 + (lane & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = hb[off + r * P];
-                    if (hin) v += corr * hin[off + r * P];
-                    accH[i][r] = v;
-                }
-                lds_store4(HT + (tc * 16 + (lane & 15)) * LDN + tr * 16 + 4 * (lane >> 4), accH[i]);
+                const int tr = ti / CT, tc = ti % CT;
+                lds_store4(HT + (tc * 16 + li) * LDN + tr * 16 + 4 * lg, accH[i]);
             }
         }
     }
 
-    const int64_t rows = (Q < l - c * Q) ? Q : (l - c * Q);  // valid rows of this chunk
-    const int nblk = (int)((rows + T - 1) / T);
-
     for (int s = 0; s < nblk; ++s) {
-        const int64_t rpb = (int64_t)s * T;  // padded row (in chunk) of the block start
-        const float last = lcs_c[rpb + T - 1];
-        // ---- stage C, B (natural), (w B)^T, x^T of this block
-        for (int q = tid; q < 2 * CBLK + XBLK; q += kThreads) {
-            if (q < 2 * CBLK) {
-                const bool isB = q >= CBLK;
-                const int qq = isB ? q - CBLK : q;
-                const int rb = qq / (N / 8), cb = qq % (N / 8);
-                const IO *src = isB ? Bm : Cm;
-                Row8v<IO> v[8];
+        const int64_t rpb = (int64_t)s * T;
+        co_stage(pf, Cs, Bs, Xs, Xw, lcs_s, d_s, tid);
+        if (s + 1 < nblk)
+            co_prefetch(pf, s + 1, xb, Bb, Cb, lcs_c, dtp_c, c * Q, l, Q, (int64_t)h * P,
+                        (int64_t)g * N, tid);
+        lds_barrier();
+
+        if (yact) {
+            // ---- masked, decayed scores of the wave's row strip (registers)
+            const int i = it * 16 + li;
+            const float li_cs = lcs_s[i];
+            f32x4 pv[2];
+            pv[0] = zero4();
+            pv[1] = zero4();
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int64_t rp = rpb + rb * 8 + r, t = c * Q + rp;
-                    const bool ok = rp < Q && t < l;
-                    v[r] = ld_row8(src + ((b * l + (ok ? t : 0)) * g + gi) * N + cb * 8, ok);
-                }
-                IO *nat = isB ? BP : Cs;
+            for (int jt = 0; jt < 2; ++jt) {
+                if (jt <= it) {
+                    f32x4 gacc = zero4();
 #pragma unroll
-                for (int r = 0; r < 8; ++r) st_row8(nat + (rb * 8 + r) * LDN + cb * 8, v[r]);
-                if (isB) {
-                    float w[8];
+                    for (int ks = 0; ks < NS; ++ks)
+                        gacc = M::mma(lds_frag(Bs, LDN, jt * 16, ks * M::K, lane),
+                                      lds_frag(Cs, LDN, it * 16, ks * M::K, lane), gacc);
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        const int64_t R = rpb + rb * 8 + r;
-                        w[r] = exp2_fast(last - lcs_c[R]) * dtp_c[R];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        Row8v<IO> o;
-#pragma unroll
-                        for (int r = 0; r < 8; ++r) o.e[r] = from_f32<IO>(to_f32(v[r].e[e]) * w[r]);
-                        st_row8(BTw + (cb * 8 + e) * LDT + rb * 8, o);
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = jt * 16 + 4 * lg + r;
+                        pv[jt][r] = (j <= i) ? gacc[r] * exp2_fast(li_cs - lcs_s[j]) * d_s[j] : 0.f;
                     }
                 }
-            } else {
-                const int qq = q - 2 * CBLK;
-                const int rb = qq / (P / 8), cb = qq % (P / 8);
-                Row8v<IO> v[8];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int64_t rp = rpb + rb * 8 + r, t = c * Q + rp;
-                    const bool ok = rp < Q && t < l;
-                    v[r] = ld_row8(x + ((b * l + (ok ? t : 0)) * h + hh) * P + cb * 8, ok);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Row8v<IO> o;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) o.e[r] = v[r].e[e];
-                    st_row8(XT + (cb * 8 + e) * LDT + rb * 8, o);
-                }
             }
-        }
-        if (tid < T) {
-            lcs_s[tid] = lcs_c[rpb + tid];
-            d_s[tid] = dtp_c[rpb + tid];
-        }
-        __syncthreads();
-
-        // ---- G^T tiles (rows j, columns i) and the masked, decayed P
-        f32x4 pv[GPW];
+            // ---- y tiles of the strip
+            const int i0 = it * 16 + 4 * lg;
+            f32x4 rowscale;
 #pragma unroll
-        for (int u = 0; u < GPW; ++u) {
-            pv[u] = zero4();
-            const int q = wave + kWaves * u;
-            if (q < GTILES) {
-                int it = 0;
-                while ((it + 1) * (it + 2) / 2 <= q) ++it;
-                const int jt = q - it * (it + 1) / 2;
-                f32x4 gacc = zero4();
+            for (int r = 0; r < 4; ++r) rowscale[r] = exp2_fast(lcs_s[i0 + r]);
 #pragma unroll
-                for (int kk = 0; kk < N / M::K; ++kk) {
-                    const auto fa = lds_frag(BP, LDN, jt * 16, kk * M::K, lane);
-                    const auto fb = lds_frag(Cs, LDN, it * 16, kk * M::K, lane);
-                    gacc = M::mma(fa, fb, gacc);
-                }
-                const int i = it * 16 + (lane & 15);
-                const float li = lcs_s[i];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = jt * 16 + 4 * (lane >> 4) + r;
-                    pv[u][r] = (j <= i) ? gacc[r] * exp2_fast(li - lcs_s[j]) * d_s[j] : 0.f;
-                }
-            }
-        }
-        __syncthreads();  // every read of B (natural) is done: BP becomes P
-#pragma unroll
-        for (int u = 0; u < GPW; ++u) {
-            const int q = wave + kWaves * u;
-            if (q < GTILES) {
-                int it = 0;
-                while ((it + 1) * (it + 2) / 2 <= q) ++it;
-                const int jt = q - it * (it + 1) / 2;
-                lds_store4(BP + (it * 16 + (lane & 15)) * LDT + jt * 16 + 4 * (lane >> 4), pv[u]);
-            }
-        }
-        // tiles above the diagonal that a contraction step of the next
-        // product reaches are zero
-        for (int it = wave; it < RT; it += kWaves) {
-            const int kend = ((it + 1) * 16 + M::K - 1) / M::K * M::K;
-            for (int jt = it + 1; jt * 16 < kend && jt < RT; ++jt)
-                lds_store4(BP + (it * 16 + (lane & 15)) * LDT + jt * 16 + 4 * (lane >> 4), zero4());
-        }
-        __syncthreads();
-
-        // ---- outputs of the block
-#pragma unroll
-        for (int u = 0; u < YPW; ++u) {
-            const int ti = wave + kWaves * u;
-            if (ti < YTILES) {
-                const int it = ti / (P / 16), pt = ti % (P / 16);
+            for (int u = 0; u < YPW; ++u) {
+                const int pt = pt0 + u;
                 f32x4 ya = zero4();
 #pragma unroll
-                for (int kk = 0; kk < N / M::K; ++kk) {
-                    const auto fa = lds_frag(Cs, LDN, it * 16, kk * M::K, lane);
-                    const auto fb = lds_frag(HT, LDN, pt * 16, kk * M::K, lane);
-                    ya = M::mma(fa, fb, ya);
-                }
-                const int i0 = it * 16 + 4 * (lane >> 4);
+                for (int ks = 0; ks < NS; ++ks)
+                    ya = M::mma(lds_frag(Cs, LDN, it * 16, ks * M::K, lane),
+                                lds_frag(HT, LDN, pt * 16, ks * M::K, lane), ya);
+                ya *= rowscale;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ya[r] *= exp2_fast(lcs_s[i0 + r]);
-                const int kend = ((it + 1) * 16 + M::K - 1) / M::K;
-                for (int kk = 0; kk < kend; ++kk) {
-                    const auto fa = lds_frag(BP, LDT, it * 16, kk * M::K, lane);
-                    const auto fb = lds_frag(XT, LDT, pt * 16, kk * M::K, lane);
-                    ya = M::mma(fa, fb, ya);
-                }
-                const int p = pt * 16 + (lane & 15);
-                const f32x4 xv = lds_load4(XT + p * LDT + i0);
+                for (int q = 0; q < KS; ++q)
+                    ya = M::mma(frag_from_acc<OP>(pv[0], pv[1], q),
+                                frag_kmajor(Xs, LDX, 0, q, pt * 16, lane), ya);
+                const f32x4 xv = lds_col4(Xs, LDX, it * 16, pt * 16, lane);  // rows i0 + r
+                const int p = pt * 16 + li;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int64_t rp = rpb + i0 + r, t = c * Q + rp;
@@ -511,30 +576,30 @@ __global__ __launch_bounds__(256) void k_chunk_out(
 
         // ---- carry the state to the next block of the chunk
         if (s + 1 < nblk) {
-            const float decay = exp2_fast(last);
+            const float decay = exp2_fast(lcs_s[T - 1]);
 #pragma unroll
             for (int i = 0; i < HPW; ++i) accH[i] *= decay;
 #pragma unroll
-            for (int kk = 0; kk < T / M::K; ++kk) {
+            for (int q = 0; q < KS; ++q) {
 #pragma unroll
                 for (int i = 0; i < HPW; ++i) {
                     const int ti = wave + kWaves * i;
                     if (ti < HTILES) {
-                        const int tr = ti / (P / 16), tc = ti % (P / 16);
-                        const auto fa = lds_frag(BTw, LDT, tr * 16, kk * M::K, lane);
-                        const auto fb = lds_frag(XT, LDT, tc * 16, kk * M::K, lane);
-                        accH[i] = M::mma(fa, fb, accH[i]);
+                        const int tr = ti / CT, tc = ti % CT;
+                        accH[i] = M::mma(frag_kmajor(Bs, LDN, 0, q, tr * 16, lane),
+                                         frag_kmajor(Xw, LDX, 0, q, tc * 16, lane), accH[i]);
                     }
                 }
             }
-            __syncthreads();  // every read of this block's operands is done
+        }
+        lds_barrier();  // every read of this block's operands is done
+        if (s + 1 < nblk) {
 #pragma unroll
             for (int i = 0; i < HPW; ++i) {
                 const int ti = wave + kWaves * i;
                 if (ti < HTILES) {
-                    const int tr = ti / (P / 16), tc = ti % (P / 16);
-                    lds_store4(HT + (tc * 16 + (lane & 15)) * LDN + tr * 16 + 4 * (lane >> 4),
-                               accH[i]);
+                    const int tr = ti / CT, tc = ti % CT;
+                    lds_store4(HT + (tc * 16 + li) * LDN + tr * 16 + 4 * lg, accH[i]);
                 }
             }
         }

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import ssd_synth as syn
-from gpu_util import (check_close, gpu_inputs, log, oracle_kw, run_scan, to_f64, torch_mod)
+from gpu_util import (STATE_AXES, Y_AXES, check_close, gpu_inputs, log, oracle_kw, run_scan,
+                      to_f64, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,8 +54,8 @@ def test_small_parity(orc, case, io):
     inp = syn.random_case(1000 + sum(case[:7]), b, l, h, p, n, g, io=io, init_std=init)
     y, fin = run_scan(inp, Q)
     yo, fo = orc.scan(**oracle_kw(inp))
-    s1 = check_close(to_f64(y), yo, io, "y")
-    s2 = check_close(to_f64(fin), fo, io, "final_state")
+    s1 = check_close(to_f64(y), yo, io, "y", Y_AXES)
+    s2 = check_close(to_f64(fin), fo, io, "final_state", STATE_AXES)
     log("y max_abs %.3g max_rel %.3g | final max_abs %.3g" % (s1[0], s1[1], s2[0]))
 
 
@@ -65,8 +66,8 @@ def test_no_skip_no_bias_clamped(orc, io):
     inp["dt_bias"] = None
     y, fin = run_scan(inp, 64, dt_limit=(0.05, 0.5))
     yo, fo = orc.scan(**oracle_kw(inp, dt_limit=(0.05, 0.5)))
-    check_close(to_f64(y), yo, io, "y")
-    check_close(to_f64(fin), fo, io, "final_state")
+    check_close(to_f64(y), yo, io, "y", Y_AXES)
+    check_close(to_f64(fin), fo, io, "final_state", STATE_AXES)
 
 
 def test_raw_time_step_without_softplus(orc):
@@ -75,8 +76,8 @@ def test_raw_time_step_without_softplus(orc):
     inp["dt_bias"] = None
     y, fin = run_scan(inp, 32, dt_softplus=False)
     yo, fo = orc.scan(**oracle_kw(inp, dt_softplus=False))
-    check_close(to_f64(y), yo, "f32", "y")
-    check_close(to_f64(fin), fo, "f32", "final_state")
+    check_close(to_f64(y), yo, "f32", "y", Y_AXES)
+    check_close(to_f64(fin), fo, "f32", "final_state", STATE_AXES)
 
 
 def test_deterministic_bitwise():
@@ -102,8 +103,8 @@ def test_extreme_decays_stay_finite(orc):
     y, fin = run_scan(inp, 256)
     assert torch_mod().isfinite(y.float()).all() and torch_mod().isfinite(fin).all()
     yo, fo = orc.scan(**oracle_kw(inp))
-    check_close(to_f64(y), yo, "bf16", "y")
-    check_close(to_f64(fin), fo, "bf16", "final_state")
+    check_close(to_f64(y), yo, "bf16", "y", Y_AXES)
+    check_close(to_f64(fin), fo, "bf16", "final_state", STATE_AXES)
 
 
 def test_literal_dt_bias_reading_stress(orc):
@@ -112,8 +113,8 @@ def test_literal_dt_bias_reading_stress(orc):
     inp = syn.random_case(11, 1, 2048, 16, 64, 128, 8, io="bf16", literal=True)
     y, fin = run_scan(inp, 256)
     yo, fo = orc.scan(**oracle_kw(inp))
-    check_close(to_f64(y), yo, "bf16", "y")
-    check_close(to_f64(fin), fo, "bf16", "final_state")
+    check_close(to_f64(y), yo, "bf16", "y", Y_AXES)
+    check_close(to_f64(fin), fo, "bf16", "final_state", STATE_AXES)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -130,8 +131,8 @@ def test_split_forward_equals_one_forward(orc, io):
     g2["init"] = f1
     y2, f2 = run_scan(second, 64, g=g2)
     yo, fo = orc.scan(**oracle_kw(inp))
-    check_close(np.concatenate([to_f64(y1), to_f64(y2)], axis=1), yo, io, "y")
-    check_close(to_f64(f2), fo, io, "final_state")
+    check_close(np.concatenate([to_f64(y1), to_f64(y2)], axis=1), yo, io, "y", Y_AXES)
+    check_close(to_f64(f2), fo, io, "final_state", STATE_AXES)
 
 
 def test_final_state_may_alias_initial_state(orc):
@@ -145,8 +146,8 @@ def test_final_state_may_alias_initial_state(orc):
     torch_mod().cuda.synchronize()
     assert fin.data_ptr() == st.data_ptr()
     yo, fo = orc.scan(**oracle_kw(inp))
-    check_close(to_f64(y), yo, "bf16", "y")
-    check_close(to_f64(st), fo, "bf16", "final_state")
+    check_close(to_f64(y), yo, "bf16", "y", Y_AXES)
+    check_close(to_f64(st), fo, "bf16", "final_state", STATE_AXES)
 
 
 def test_group_expansion():
@@ -214,7 +215,7 @@ def test_invalid_arguments_raise():
 
 
 def _ws_layout(b, l, h, Q, io):
-    T = 64 if io == "bf16" else 32
+    T = 32   # rows per block, both io dtypes
     nc = -(-l // Q)
     Qp = -(-Q // T) * T
     lp = nc * Qp
@@ -233,7 +234,7 @@ def test_stage_intermediates(orc, io):
     import mamba_ssd_chunked_chunk_amd as ssd
     from oracle import chunked
     torch = torch_mod()
-    T = 64 if io == "bf16" else 32
+    T = 32
     b, l, h, p, n, g, Q = 8, 5 * T + 11, 64, 64, 128, 4, T
     inp = syn.random_case(18, b, l, h, p, n, g, io=io, init_std=0.1)
     G = gpu_inputs(inp)
@@ -254,4 +255,4 @@ def test_stage_intermediates(orc, io):
     cs = to_f64(lcs) / math.log2(math.e)
     err = np.abs(cs - inter["cs"])
     assert (err <= 1e-5 * (1 + np.abs(inter["cs"]))).all(), err.max()
-    check_close(to_f64(hb), inter["H_prev"], io, "boundary states")
+    check_close(to_f64(hb), inter["H_prev"], io, "boundary states", (1, 3, 4))

@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 import ssd_synth as syn
-from gpu_util import (check_close, dev_tensor, gpu_inputs, log, oracle_kw, run_scan,
-                      sample_pairs, to_f64, torch_mod)
+from gpu_util import (PAIR_AXES, STATE_AXES, Y_AXES, check_close, dev_tensor, gpu_inputs, log,
+                      oracle_kw, run_scan, sample_pairs, to_f64, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,16 +45,16 @@ def test_workload_parity(orc, name):
     k = SAMPLES[name]
     if k is None:
         yo, fo = orc.scan(**oracle_kw(inp))
-        s = check_close(to_f64(y), yo, w.io, "y")
-        check_close(to_f64(fin), fo, w.io, "final_state")
+        s = check_close(to_f64(y), yo, w.io, "y", Y_AXES)
+        check_close(to_f64(fin), fo, w.io, "final_state", STATE_AXES)
     else:
         pairs = sample_pairs(w.batch, w.heads, k, seed=w.seed)
         log("oracle on", len(pairs), "pairs")
         yo, fo = orc.scan(**oracle_kw(inp), pairs=pairs)
         yg = np.stack([to_f64(y[pb, :, ph, :]) for pb, ph in pairs])
         fg = np.stack([to_f64(fin[pb, ph]) for pb, ph in pairs])
-        s = check_close(yg, yo, w.io, "y")
-        check_close(fg, fo, w.io, "final_state")
+        s = check_close(yg, yo, w.io, "y", PAIR_AXES)
+        check_close(fg, fo, w.io, "final_state", PAIR_AXES)
     log(name, "y max_abs %.3g max_rel %.3g normwise %.3g" % s)
 
 
@@ -72,8 +72,8 @@ def test_step_small(orc, io):
     torch.cuda.synchronize()
     yo, so = orc.step(st0, inp["x"][:, 0], inp["dt"][:, 0], inp["A"], inp["B"][:, 0],
                       inp["C"][:, 0], inp["D"], inp["dt_bias"], io=io)
-    check_close(to_f64(y), yo, io, "y")
-    check_close(to_f64(st), so, "f32", "state")   # state arithmetic is fp32 for both io
+    check_close(to_f64(y), yo, io, "y", (2,))
+    check_close(to_f64(st), so, "f32", "state", STATE_AXES)   # state arithmetic is fp32
 
 
 @pytest.mark.parametrize("p,n", [(16, 64), (32, 32), (128, 128)])
@@ -90,8 +90,8 @@ def test_step_shapes(orc, p, n):
     torch.cuda.synchronize()
     yo, so = orc.step(st0, inp["x"][:, 0], inp["dt"][:, 0], inp["A"], inp["B"][:, 0],
                       inp["C"][:, 0], None, inp["dt_bias"])
-    check_close(to_f64(y), yo, "f32", "y")
-    check_close(to_f64(st), so, "f32", "state")
+    check_close(to_f64(y), yo, "f32", "y", (2,))
+    check_close(to_f64(st), so, "f32", "state", STATE_AXES)
 
 
 def test_step_zero_time_step_leaves_state_equal():
@@ -134,8 +134,8 @@ def test_forward_then_steps_equals_long_forward(orc, io):
     torch.cuda.synchronize()
     yo, fo = orc.scan(**oracle_kw(inp))
     yg = np.concatenate([to_f64(y1), np.stack([to_f64(v) for v in ys], axis=1)], axis=1)
-    check_close(yg, yo, io, "y")
-    check_close(to_f64(st), fo, io, "state")
+    check_close(yg, yo, io, "y", Y_AXES)
+    check_close(to_f64(st), fo, io, "state", STATE_AXES)
 
 
 def test_decode_workload(orc):
@@ -156,7 +156,8 @@ def test_decode_workload(orc):
     log("oracle prefill on", len(pairs), "pairs")
     _, so = orc.scan(**oracle_kw(inp_s), pairs=pairs)
     del inp_s
-    check_close(np.stack([to_f64(st[pb, ph]) for pb, ph in pairs]), so, w.io, "prefill state")
+    check_close(np.stack([to_f64(st[pb, ph]) for pb, ph in pairs]), so, w.io, "prefill state",
+                PAIR_AXES)
     A = dev_tensor(syn.make_inputs(w.replace(seqlen=1), batch=1)["A"])
     base = syn.make_inputs(w.replace(seqlen=1), batch=1)
     Dv, bias = dev_tensor(base["D"]), dev_tensor(base["dt_bias"])
@@ -176,6 +177,6 @@ def test_decode_workload(orc):
             ys.append(yk[0, 0])
         torch.cuda.synchronize()
         check_close(np.stack([to_f64(y[pb, ph]) for pb, ph in pairs]), np.stack(ys), w.io,
-                    "y at step %d" % s)
+                    "y at step %d" % s, (1,))
     check_close(np.stack([to_f64(st[pb, ph]) for pb, ph in pairs]), state_o[:, 0], w.io,
-                "state after 128 steps")
+                "state after 128 steps", PAIR_AXES)
