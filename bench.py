@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD scan tokens/sec at 1 GPU; % of MFMA/HBM roofline; decode steps/sec"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_IDS = ("dt_cumsum", "state_pass", "seg_combine", "chunk_out")
+KERNEL_IDS = ("prep", "state_pass", "seg_combine", "chunk_out")
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan.hpp",
                   "mamba_ssd_chunked_chunk_amd/csrc/ssd_device.hpp",
@@ -48,10 +48,11 @@ def source_digest() -> str:
 
 
 # ----------------------------------------------------------- byte counts ---
-def plan_sizes(b, l, h, p, n, g, Q, T=64, target_chains=2048):
+def plan_sizes(b, l, h, p, n, g, Q, T=32, target_chains=512):
+    """Chunks, segments of the serial pass and padded rows, as the library
+    plans them (32-row blocks; about 512 independent serial chains)."""
     nc = -(-l // Q)
-    nsplit = max(1, n // 32)
-    chains = b * h * nsplit
+    chains = b * h
     nseg = min(max(1, -(-target_chains // chains)), nc)
     cps = -(-nc // nseg)
     nseg = -(-nc // cps)
@@ -83,8 +84,9 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
     hb = b * nc * h * n * p * 4        # boundary states
     seg = b * nseg * h * n * p * 4 if nseg > 1 else 0
     st = b * h * n * p * 4
-    if name == "dt_cumsum":
-        return th * s + 2 * rows
+    if name == "prep":
+        # dt read, lcs and d written; bf16 io also converts B and C to fp16
+        return th * s + 2 * rows + (4 * BC if s == 2 else 0)
     if name == "state_pass":
         return x + BC + 2 * rows + hb + seg + (st if final and nseg == 1 else 0)
     if name == "seg_combine":

@@ -92,6 +92,14 @@ enum ssd_status {
  * Supported: head_dim in {16, 32, 64, 128}, state_dim in {32, 64, 128}.
  * batch == 0 or seqlen == 0 is valid: nothing is computed except that
  * final_state (if given) receives init_state, or zeros.
+ *
+ * Precision (bf16 io): the matrix products take fp16 operands with fp32
+ * accumulation.  x, B and C convert to fp16 exactly while their magnitudes
+ * lie in [2^-14, 65504]; smaller magnitudes keep fewer significant bits
+ * (below 2^-24 they count as zero) and larger ones saturate at 65504.  The
+ * decay-weighted x, the masked scores and the carried state are rounded to
+ * fp16 (toward zero) as operands; all sums, decays and states are fp32.
+ * fp32 io uses fp32 operands throughout.
  */
 int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
                        const void *C, const float *D, const float *dt_bias,
@@ -108,7 +116,9 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
  * [batch, heads, padded seqlen] fp32 each; chunk-boundary states
  * [batch, chunks, heads, state_dim, head_dim] fp32; then, when the sequence
  * is cut into several segments, segment states [batch, segments, heads,
- * state_dim, head_dim] fp32 and per-chunk / per-segment log2 decays.
+ * state_dim, head_dim] fp32 and per-chunk / per-segment log2 decays; then,
+ * for bf16 io, fp16 copies of B and C [batch, seqlen, groups, state_dim].
+ * The size returned covers both io dtypes.
  */
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim,
@@ -122,10 +132,11 @@ size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t hea
  *
  *   state   [batch, heads, state_dim, head_dim] fp32, read and overwritten;
  *           16-byte aligned
- *   x       [batch, heads, head_dim] io dtype; dt [batch, heads] io dtype
+ *   x       [batch, heads, head_dim] io dtype, aligned to 4 elements (16
+ *           bytes fp32, 8 bytes bf16); dt [batch, heads] io dtype
  *   B, C    [batch, groups, state_dim] io dtype
  *   A, D, dt_bias, dt_softplus, dt_min, dt_max: as for ssd_chunk_scan
- *   y       [batch, heads, head_dim] io dtype, written
+ *   y       [batch, heads, head_dim] io dtype, written; aligned as x
  *
  * With d = 0 (dt_softplus = 0, dt + dt_bias = 0) the state is left exactly
  * unchanged (exp(0) = 1 and nothing is written).
@@ -151,7 +162,8 @@ int32_t ssd_abi_version(void);
  * clears that kernel's record.  Not thread-safe with concurrent scan calls.
  */
 enum ssd_kernel_id {
-    SSD_K_DT_CUMSUM = 0,   /* time step, log decay and per-block cumulative sum */
+    SSD_K_PREP = 0,        /* time step, per-block cumulative log decay; bf16 io:
+                              fp16 copies of B and C */
     SSD_K_STATE_PASS = 1,  /* chunk states and serial state passing */
     SSD_K_SEG_COMBINE = 2, /* combination of segment states (long sequences) */
     SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */

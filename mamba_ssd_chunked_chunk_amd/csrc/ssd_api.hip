@@ -128,7 +128,7 @@ size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t hea
                                       int64_t head_dim, int64_t state_dim, int64_t groups,
                                       int64_t chunk) {
     ScanPlan pl;
-    // the larger of the two io layouts (fp32 pads rows to 32, bf16 to 64)
+    // the larger of the two io layouts (bf16 adds the fp16 copies of B and C)
     size_t best = 0;
     for (int io = 0; io < 2; ++io) {
         if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io))
@@ -179,8 +179,8 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
         return SSD_ERR_SHAPE;
     // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
     const int64_t gmax = ((int64_t)1 << 31) - 1;
-    if (pl.nc > gmax || batch > 65535 || (heads + 3) / 4 > 65535 ||
-        pl.b * pl.nc * pl.h > gmax || pl.b * pl.nseg * pl.h * (state_dim / 32) > gmax)
+    const int64_t prep_groups = (pl.b * pl.h * ((pl.lp + 63) / 64) + 3) / 4 + 2048;
+    if (prep_groups > gmax || pl.b * pl.nc * pl.h > gmax || pl.b * pl.nseg * pl.h > gmax)
         return SSD_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < ssd_chunk_scan_workspace_bytes(
                                             batch, seqlen, heads, head_dim, state_dim, groups,
@@ -208,7 +208,7 @@ int32_t ssd_step(float *state, const void *x, const void *dt, const float *A, co
     if (!mul_ok(batch, heads, (int64_t)1 << 40)) return SSD_ERR_UNSUPPORTED;
     if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
-    if (!aligned(state, 16) || !aligned(x, 8) || !aligned(y, 8) || !aligned(dt, es) ||
+    if (!aligned(state, 16) || !aligned(x, 4 * es) || !aligned(y, 4 * es) || !aligned(dt, es) ||
         !aligned(B, es) || !aligned(C, es) || !aligned(A, 4) || !aligned(D, 4) ||
         !aligned(dt_bias, 4))
         return SSD_ERR_ALIGN;

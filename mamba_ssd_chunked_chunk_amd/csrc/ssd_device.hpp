@@ -143,28 +143,64 @@ __device__ __forceinline__ f32x4 lds_col4(const float *M, int ld, int k0, int c0
     return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
 
-// An A fragment made from two accumulator tiles (contraction blocks jt = 0, 1
-// of a 32-block) in the k-major convention above (round to nearest).
+// Row-major matrix M[row][k] read in the k-major contraction convention:
+// lane l gets row row0 + (l & 15) at k = kb + 4g + r and kb + 16 + 4g + r
+// (fp16), or at k = kb + 16 (q >> 2) + 4g + (q & 3) for fp32 step q.  Pairs
+// with a k-major or accumulator-made partner operand.
+__device__ __forceinline__ f16x8 frag_rows_kconv(const f16 *M, int ld, int row0, int kb, int,
+                                                 int lane) {
+    const f16 *p = M + (row0 + (lane & 15)) * ld + kb + 4 * (lane >> 4);
+    const f16x4 a = *reinterpret_cast<const f16x4 *>(p);
+    const f16x4 b = *reinterpret_cast<const f16x4 *>(p + 16);
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ float frag_rows_kconv(const float *M, int ld, int row0, int kb, int q,
+                                                 int lane) {
+    return M[(row0 + (lane & 15)) * ld + kb + 16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)];
+}
+
+// Two fp32 values -> packed fp16 pair, rounded toward zero (one instruction;
+// error below 2^-11 relative).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x2 pk2(float a, float b) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ void pack2(float a, float b, f16 &lo, f16 &hi) {
+    const f16x2 pk = pk2(a, b);
+    lo = pk[0];
+    hi = pk[1];
+}
+
+// An operand fragment made from two accumulator tiles (contraction blocks
+// jt = 0, 1 of a 32-block) in the k-major convention above.
 template <typename OP>
 __device__ __forceinline__ typename Mfma<OP>::frag frag_from_acc(const f32x4 &t0,
                                                                  const f32x4 &t1, int q);
 template <>
 __device__ __forceinline__ f16x8 frag_from_acc<f16>(const f32x4 &t0, const f32x4 &t1, int) {
-    return f16x8{(f16)t0[0], (f16)t0[1], (f16)t0[2], (f16)t0[3],
-                 (f16)t1[0], (f16)t1[1], (f16)t1[2], (f16)t1[3]};
+    const f16x2 a = pk2(t0[0], t0[1]), b = pk2(t0[2], t0[3]);
+    const f16x2 c = pk2(t1[0], t1[1]), d = pk2(t1[2], t1[3]);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 template <>
 __device__ __forceinline__ float frag_from_acc<float>(const f32x4 &t0, const f32x4 &t1, int q) {
     return (q >> 2) ? t1[q & 3] : t0[q & 3];
 }
 
-// Store 4 fp32 values to LDS as an operand type (round to nearest), contiguous.
-__device__ __forceinline__ void lds_store4(f16 *dst, f32x4 v) {
-    *reinterpret_cast<f16x4 *>(dst) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+// 4 consecutive operand values from LDS, as fp32.
+__device__ __forceinline__ f32x4 lds_load4(const f16 *p) {
+    const f16x4 v = *reinterpret_cast<const f16x4 *>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
-__device__ __forceinline__ void lds_store4(float *dst, f32x4 v) {
-    *reinterpret_cast<f32x4 *>(dst) = v;
+__device__ __forceinline__ f32x4 lds_load4(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
 }
+
+// 4 consecutive outputs (round to nearest even for bf16).
+__device__ __forceinline__ void store4(bf16 *p, f32x4 v) {
+    *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+__device__ __forceinline__ void store4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
 
 // ---------------------------------------------------------- row pieces ----
 // 8 consecutive elements of one row, moved with vector loads and stores.
@@ -177,35 +213,48 @@ template <typename T> __device__ __forceinline__ void st_row8(T *dst, const Row8
     *reinterpret_cast<Row8v<T> *>(dst) = v;
 }
 
-// Input piece -> operand piece, or zeros when !keep.  bf16 -> fp16 uses the
-// packed round-toward-zero conversion, which is exact for every bf16 value in
-// fp16's normal range.  The select is applied only here, when the value is
-// consumed, so the load that filled v is not waited for any earlier.
-__device__ __forceinline__ Row8v<f16> to_op(const Row8v<bf16> &v, bool keep) {
-    Row8v<f16> o;
+// v, or zeros when !keep (select on 32-bit words).  Applied only when the
+// value is consumed, so the load that filled v is not waited for earlier.
+template <typename T>
+__device__ __forceinline__ Row8v<T> keep_or_zero(const Row8v<T> &v, bool keep) {
+    constexpr int W = sizeof(Row8v<T>) / 4;
+    uint32_t u[W];
+    __builtin_memcpy(u, &v, sizeof(u));
+#pragma unroll
+    for (int i = 0; i < W; ++i) u[i] = keep ? u[i] : 0u;
+    Row8v<T> o;
+    __builtin_memcpy(&o, u, sizeof(u));
+    return o;
+}
+
+// An x piece as the two operand pieces x and w x (zeros when !keep).  bf16
+// -> fp16 is exact for values in fp16's normal range (round toward zero
+// changes nothing there); w x is rounded toward zero.
+__device__ __forceinline__ void x_pieces(const Row8v<bf16> &v, float w, bool keep,
+                                         Row8v<f16> &xo, Row8v<f16> &wo) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-        const auto pk = __builtin_amdgcn_cvt_pkrtz(keep ? (float)v.e[e] : 0.f,
-                                                   keep ? (float)v.e[e + 1] : 0.f);
-        o.e[e] = pk[0];
-        o.e[e + 1] = pk[1];
+        const float a = keep ? (float)v.e[e] : 0.f, b = keep ? (float)v.e[e + 1] : 0.f;
+        pack2(a, b, xo.e[e], xo.e[e + 1]);
+        pack2(a * w, b * w, wo.e[e], wo.e[e + 1]);
     }
-    return o;
 }
-__device__ __forceinline__ Row8v<float> to_op(const Row8v<float> &v, bool keep) {
-    Row8v<float> o;
+__device__ __forceinline__ void x_pieces(const Row8v<float> &v, float w, bool keep,
+                                         Row8v<float> &xo, Row8v<float> &wo) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o.e[e] = keep ? v.e[e] : 0.f;
-    return o;
+    for (int e = 0; e < 8; ++e) {
+        xo.e[e] = keep ? v.e[e] : 0.f;
+        wo.e[e] = xo.e[e] * w;
+    }
 }
-// w * v as an operand piece (round to nearest).
-__device__ __forceinline__ Row8v<f16> to_op_scaled(const Row8v<bf16> &v, float w) {
+// w x only.
+__device__ __forceinline__ Row8v<f16> wx_piece(const Row8v<bf16> &v, float w) {
     Row8v<f16> o;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o.e[e] = (f16)((float)v.e[e] * w);
+    for (int e = 0; e < 8; e += 2) pack2((float)v.e[e] * w, (float)v.e[e + 1] * w, o.e[e], o.e[e + 1]);
     return o;
 }
-__device__ __forceinline__ Row8v<float> to_op_scaled(const Row8v<float> &v, float w) {
+__device__ __forceinline__ Row8v<float> wx_piece(const Row8v<float> &v, float w) {
     Row8v<float> o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o.e[e] = v.e[e] * w;

@@ -20,14 +20,15 @@ struct ScanPlan {
     int64_t nsb;  // blocks per chunk (Qp / T)
     int64_t Qp;   // padded rows per chunk
     int64_t lp;   // padded rows per sequence (nc * Qp)
-    int nsplit;   // workgroups sharing one state (state_dim split)
     int64_t nseg; // segments of the serial chunk pass
     int64_t cps;  // chunks per segment
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_hb, off_seg, off_dlog, off_lseg, total;
+    size_t off_lcs, off_dtp, off_hb, off_seg, off_dlog, off_lseg, off_bf, off_cf, total;
 };
 
-constexpr int64_t kTargetChains = 2048;  // independent serial chains wanted
+// Independent serial chains (batch x head x segment) wanted in the state pass:
+// two resident workgroups on each of the 256 compute units.
+constexpr int64_t kTargetChains = 512;
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
@@ -42,8 +43,7 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     P.nsb = (Q + P.T - 1) / P.T;
     P.Qp = P.nsb * P.T;
     P.lp = P.nc * P.Qp;
-    P.nsplit = n >= 32 ? (int)(n / 32) : 1;
-    const int64_t chains = b * h * P.nsplit;
+    const int64_t chains = b * h;
     int64_t nseg = chains > 0 ? (kTargetChains + chains - 1) / chains : 1;
     if (nseg < 1) nseg = 1;
     if (nseg > P.nc) nseg = P.nc > 0 ? P.nc : 1;
@@ -61,6 +61,12 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     } else {
         P.off_seg = P.off_dlog = P.off_lseg = o;
     }
+    // bf16 io: fp16 copies of B and C (matrix-core operands, shared by the
+    // heads of a group, converted once)
+    P.off_bf = o;
+    if (io == 1) o += align256(b * l * g * n * 2);
+    P.off_cf = o;
+    if (io == 1) o += align256(b * l * g * n * 2);
     P.total = o;
     return true;
 }
