@@ -4,7 +4,8 @@
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel)
 and linked into mamba_ssd_chunked_chunk_amd/libssd.so.  All device code is
-compiled with packed fp32 instructions disabled.
+compiled with packed fp32 instructions disabled and MFMA results kept in
+VGPRs.
 """
 from __future__ import annotations
 
@@ -25,6 +26,10 @@ ARCH = os.environ.get("SSD_OFFLOAD_ARCH", "gfx950")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the scan kernels convert
+    # accumulators into operands of the next product, which AGPRs would
+    # force through a copy every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -182,6 +182,12 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
     const int64_t prep_groups = (pl.b * pl.h * ((pl.lp + 63) / 64) + 3) / 4 + 2048;
     if (prep_groups > gmax || pl.b * pl.nc * pl.h > gmax || pl.b * pl.nseg * pl.h > gmax)
         return SSD_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
+    // one (batch, head)
+    const int64_t lim32 = ((int64_t)1 << 31);
+    if (64 * heads * head_dim * 4 >= lim32 || 64 * groups * state_dim * 4 >= lim32 ||
+        pl.lp * 4 >= lim32)
+        return SSD_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < ssd_chunk_scan_workspace_bytes(
                                             batch, seqlen, heads, head_dim, state_dim, groups,
                                             chunk))

@@ -213,38 +213,24 @@ template <typename T> __device__ __forceinline__ void st_row8(T *dst, const Row8
     *reinterpret_cast<Row8v<T> *>(dst) = v;
 }
 
-// v, or zeros when !keep (select on 32-bit words).  Applied only when the
-// value is consumed, so the load that filled v is not waited for earlier.
-template <typename T>
-__device__ __forceinline__ Row8v<T> keep_or_zero(const Row8v<T> &v, bool keep) {
-    constexpr int W = sizeof(Row8v<T>) / 4;
-    uint32_t u[W];
-    __builtin_memcpy(u, &v, sizeof(u));
-#pragma unroll
-    for (int i = 0; i < W; ++i) u[i] = keep ? u[i] : 0u;
-    Row8v<T> o;
-    __builtin_memcpy(&o, u, sizeof(u));
-    return o;
-}
-
-// An x piece as the two operand pieces x and w x (zeros when !keep).  bf16
-// -> fp16 is exact for values in fp16's normal range (round toward zero
-// changes nothing there); w x is rounded toward zero.
-__device__ __forceinline__ void x_pieces(const Row8v<bf16> &v, float w, bool keep,
-                                         Row8v<f16> &xo, Row8v<f16> &wo) {
+// An x piece as the two operand pieces x and w x.  bf16 -> fp16 is exact for
+// values in fp16's normal range (round toward zero changes nothing there);
+// w x is rounded toward zero.
+__device__ __forceinline__ void x_pieces(const Row8v<bf16> &v, float w, Row8v<f16> &xo,
+                                         Row8v<f16> &wo) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-        const float a = keep ? (float)v.e[e] : 0.f, b = keep ? (float)v.e[e + 1] : 0.f;
+        const float a = (float)v.e[e], b = (float)v.e[e + 1];
         pack2(a, b, xo.e[e], xo.e[e + 1]);
         pack2(a * w, b * w, wo.e[e], wo.e[e + 1]);
     }
 }
-__device__ __forceinline__ void x_pieces(const Row8v<float> &v, float w, bool keep,
-                                         Row8v<float> &xo, Row8v<float> &wo) {
+__device__ __forceinline__ void x_pieces(const Row8v<float> &v, float w, Row8v<float> &xo,
+                                         Row8v<float> &wo) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        xo.e[e] = keep ? v.e[e] : 0.f;
-        wo.e[e] = xo.e[e] * w;
+        xo.e[e] = v.e[e];
+        wo.e[e] = v.e[e] * w;
     }
 }
 // w x only.
@@ -259,6 +245,36 @@ __device__ __forceinline__ Row8v<float> wx_piece(const Row8v<float> &v, float w)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o.e[e] = v.e[e] * w;
     return o;
+}
+
+// ------------------------------------------------------ buffer access ----
+// Raw buffer resources: loads whose offset lies at or beyond the resource's
+// byte size return zeros and such stores are dropped, so rows past the end of
+// a chunk or of the sequence need no masks.  Offsets are 32-bit; every
+// resource here spans at most a few rows of one tensor.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (CDNA)
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
+    const int64_t c = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)(uint32_t)c, kRsrcWord3);
+}
+template <typename T> __device__ __forceinline__ Row8v<T> buf_row8(Rsrc r, uint32_t off) {
+    constexpr int NV = sizeof(Row8v<T>) / 16;
+    u32x4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+    Row8v<T> o;
+    __builtin_memcpy(&o, v, sizeof(o));
+    return o;
+}
+__device__ __forceinline__ float buf_f32(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store16(Rsrc r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
 // ----------------------------------------------- workgroup -> work item ----

@@ -23,7 +23,7 @@ struct ScanPlan {
     int64_t nseg; // segments of the serial chunk pass
     int64_t cps;  // chunks per segment
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_hb, off_seg, off_dlog, off_lseg, off_bf, off_cf, total;
+    size_t off_lcs, off_dtp, off_wgt, off_hb, off_seg, off_dlog, off_lseg, off_bf, off_cf, total;
 };
 
 // Independent serial chains (batch x head x segment) wanted in the state pass:
@@ -53,6 +53,7 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     size_t o = 0;
     P.off_lcs = o;  o += align256(b * h * P.lp * 4);
     P.off_dtp = o;  o += align256(b * h * P.lp * 4);
+    P.off_wgt = o;  o += align256(b * h * P.lp * 4);
     P.off_hb = o;   o += align256(b * P.nc * h * st);
     if (P.nseg > 1) {
         P.off_seg = o;  o += align256(b * P.nseg * h * st);

@@ -44,10 +44,12 @@ constexpr bool kOpCopy = !std::is_same<IO, typename Op<IO>::type>::value;
 
 // ----------------------------------------------------------------------------
 // 1. Preparation.
-//    (a) Time step and per-block cumulative log2 decay, one wave per
-//        (batch, head, 64 padded rows), one row per lane:
-//          dtp[b, h, R] = d,   lcs[b, h, R] = log2(e) sum_{block start..R} A d
-//        over the padded row space (R = c Qp + r); padded rows have d = 0.
+//    (a) Per padded row R = c Qp + r of every (batch, head), one wave per 64
+//        rows, one row per lane:
+//          dtp[R] = d (0 on padded rows),
+//          lcs[R] = log2(e) sum_{block start..R} A d   (inclusive),
+//          wgt[R] = 2^(lcs[block end] - lcs[R]) d     (weight of row R in the
+//                   state at the end of its block).
 //    (b) bf16 io only: B and C converted once to fp16 for the matrix cores of
 //        every head of the group (exact inside fp16's normal range).
 //    Workgroups [0, na) do (a); the others stride over the pieces of (b).
@@ -55,9 +57,10 @@ template <typename IO>
 __global__ __launch_bounds__(256) void k_prep(
     const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
     int softplus, float dt_min, float dt_max, int64_t nbatch, int64_t l, int h, int64_t Q,
-    int64_t nc, int64_t Qp, float *__restrict__ lcs, float *__restrict__ dtp, int64_t na,
-    const IO *__restrict__ Bm, const IO *__restrict__ Cm, typename Op<IO>::type *__restrict__ Bf,
-    typename Op<IO>::type *__restrict__ Cf, int64_t pieces) {
+    int64_t nc, int64_t Qp, float *__restrict__ lcs, float *__restrict__ dtp,
+    float *__restrict__ wgt, int64_t na, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
+    typename Op<IO>::type *__restrict__ Bf, typename Op<IO>::type *__restrict__ Cf,
+    int64_t pieces) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if ((int64_t)blockIdx.x < na) {
         const int64_t lp = nc * Qp, ns = (lp + 63) / 64;
@@ -80,9 +83,11 @@ __global__ __launch_bounds__(256) void k_prep(
             const float v = __shfl_up(a, off, kT);
             if ((lane & (kT - 1)) >= off) a += v;
         }
+        const float last = __shfl(a, kT - 1, kT);
         if (R < lp) {
             lcs[bh * lp + R] = a;
             dtp[bh * lp + R] = d;
+            wgt[bh * lp + R] = exp2_fast(last - a) * d;
         }
         return;
     }
@@ -104,12 +109,26 @@ __global__ __launch_bounds__(256) void k_prep(
 }
 
 // ----------------------------------------------------------------------------
-// Staging of the state pass: one slab = SLAB blocks of kT rows.  Pieces are
-// 8 consecutive elements of one row of x (P / 8 per row) or of B (N / 8 per
-// row).  The prefetch only issues loads (row index clamped to row 0 of the
-// sequence, which is always readable) and records which pieces are real
-// rows; conversions and selects happen in the stage step, so nothing waits
-// on a load before it is needed.
+// Slabs of the state pass: SLAB consecutive blocks of one chunk (the last
+// slab of a chunk may hold fewer).  Slab si of a segment is slab si % nspc of
+// chunk c0 + si / nspc.
+struct SlabPos {
+    int64_t c;   // chunk
+    int bi0;     // first block of the slab inside the chunk
+    int nb;      // blocks in the slab
+};
+__device__ __forceinline__ SlabPos slab_pos(int64_t si, int64_t c0, int nspc, int nsb, int slab) {
+    SlabPos s;
+    s.c = c0 + si / nspc;
+    s.bi0 = (int)(si % nspc) * slab;
+    s.nb = nsb - s.bi0 < slab ? nsb - s.bi0 : slab;
+    return s;
+}
+
+// Register prefetch of one slab.  Pieces are 8 consecutive elements of one
+// row of x (P / 8 per row) or of B (N / 8 per row).  The loads go through
+// buffer resources that end at the chunk's last valid row, so pieces of
+// padded rows or rows past the sequence come back as zeros.
 template <typename IO, int P, int N, int SLAB> struct SpBuf {
     typedef typename Op<IO>::type OP;
     static constexpr int NPX = SLAB * kT * P / 8, NPB = SLAB * kT * N / 8;
@@ -117,52 +136,44 @@ template <typename IO, int P, int N, int SLAB> struct SpBuf {
     static constexpr int KB = (NPB + kThreads - 1) / kThreads;
     Row8v<IO> xv[KX];
     Row8v<OP> bv[KB];
-    float xl[KX], xd[KX], xe[KX];  // lcs, d of the x piece's row; lcs at its block end
-    float lam[SLAB];               // log2 decay of each block of the slab
-    uint32_t okx, okb;             // bit k: piece k is a real row
+    float xw[KX];      // weight of the x piece's row
+    float lam[SLAB];   // log2 decay of each block of the slab
 };
 
 template <typename IO, int P, int N, int SLAB>
-__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, SLAB> &f, int64_t s0, int64_t sb1,
-                                            int64_t nsb, const IO *xb,
-                                            const typename Op<IO>::type *Bb,
-                                            const float *lcs_bh, const float *dtp_bh, int64_t l,
-                                            int64_t Q, int64_t xstride, int64_t bstride, int tid) {
+__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, SLAB> &f, const SlabPos &sp,
+                                            const IO *xb, const typename Op<IO>::type *Bb,
+                                            Rsrc rw, const float *lcs_bh, int64_t l, int64_t Q,
+                                            int64_t nsb, int64_t xs, int64_t bs, int tid) {
     typedef SpBuf<IO, P, N, SLAB> F;
+    typedef typename Op<IO>::type OP;
     constexpr int T = kT;
-    const int nb = (int)((sb1 - s0) < SLAB ? (sb1 - s0) : SLAB);
-    f.okx = 0;
-    f.okb = 0;
+    const int64_t row0 = sp.c * Q + (int64_t)sp.bi0 * T;          // sequence row
+    const int64_t cend = (sp.c + 1) * Q < l ? (sp.c + 1) * Q : l;  // end of the chunk
+    const int64_t valid = cend - row0;
+    const Rsrc rx = make_rsrc(xb + row0 * xs, valid * xs * (int64_t)sizeof(IO));
+    const Rsrc rb = make_rsrc(Bb + row0 * bs, valid * bs * (int64_t)sizeof(OP));
+    const uint32_t wrow = (uint32_t)((sp.c * nsb + sp.bi0) * T) * 4u;
 #pragma unroll
     for (int k = 0; k < F::KX; ++k) {
         const int q = tid + k * kThreads;
         if (F::NPX % kThreads == 0 || q < F::NPX) {
-            const int j = q / (P / 8), cc = q % (P / 8), jb = j / T;
-            const int64_t sb = s0 + (jb < nb ? jb : 0);
-            const int64_t rp = (sb % nsb) * T + (j % T), t = (sb / nsb) * Q + rp;
-            const bool ok = jb < nb && rp < Q && t < l;
-            f.xv[k] = ld_row8(xb + (ok ? t : 0) * xstride + cc * 8);
-            const int64_t R = sb * T + (j % T);
-            f.xl[k] = lcs_bh[R];
-            f.xd[k] = dtp_bh[R];
-            f.xe[k] = lcs_bh[sb * T + T - 1];
-            f.okx |= (uint32_t)ok << k;
+            const int j = q / (P / 8), cc = q % (P / 8);
+            f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * xs + cc * 8) * (uint32_t)sizeof(IO));
+            f.xw[k] = buf_f32(rw, (uint32_t)j * 4u, wrow);
         }
     }
 #pragma unroll
     for (int k = 0; k < F::KB; ++k) {
         const int q = tid + k * kThreads;
         if (F::NPB % kThreads == 0 || q < F::NPB) {
-            const int j = q / (N / 8), cc = q % (N / 8), jb = j / T;
-            const int64_t sb = s0 + (jb < nb ? jb : 0);
-            const int64_t rp = (sb % nsb) * T + (j % T), t = (sb / nsb) * Q + rp;
-            const bool ok = jb < nb && rp < Q && t < l;
-            f.bv[k] = ld_row8(Bb + (ok ? t : 0) * bstride + cc * 8);
-            f.okb |= (uint32_t)ok << k;
+            const int j = q / (N / 8), cc = q % (N / 8);
+            f.bv[k] = buf_row8<OP>(rb, (uint32_t)(j * bs + cc * 8) * (uint32_t)sizeof(OP));
         }
     }
 #pragma unroll
-    for (int jb = 0; jb < SLAB; ++jb) f.lam[jb] = lcs_bh[(s0 + (jb < nb ? jb : 0)) * T + T - 1];
+    for (int jb = 0; jb < SLAB; ++jb)
+        f.lam[jb] = lcs_bh[(sp.c * nsb + sp.bi0 + (jb < sp.nb ? jb : 0)) * T + T - 1];
 }
 
 template <typename IO, int P, int N, int SLAB>
@@ -170,23 +181,18 @@ __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, SLAB> &f,
                                          typename Op<IO>::type *Xw,
                                          typename Op<IO>::type *Bs, int tid) {
     typedef SpBuf<IO, P, N, SLAB> F;
-    typedef typename Op<IO>::type OP;
     constexpr int LDX = P + 16, LDB = N + 16;
 #pragma unroll
     for (int k = 0; k < F::KX; ++k) {
         const int q = tid + k * kThreads;
-        if (F::NPX % kThreads == 0 || q < F::NPX) {
-            const bool ok = (f.okx >> k) & 1;
-            const float w = ok ? exp2_fast(f.xe[k] - f.xl[k]) * f.xd[k] : 0.f;
-            st_row8(Xw + (q / (P / 8)) * LDX + (q % (P / 8)) * 8, wx_piece(f.xv[k], w));
-        }
+        if (F::NPX % kThreads == 0 || q < F::NPX)
+            st_row8(Xw + (q / (P / 8)) * LDX + (q % (P / 8)) * 8, wx_piece(f.xv[k], f.xw[k]));
     }
 #pragma unroll
     for (int k = 0; k < F::KB; ++k) {
         const int q = tid + k * kThreads;
         if (F::NPB % kThreads == 0 || q < F::NPB)
-            st_row8(Bs + (q / (N / 8)) * LDB + (q % (N / 8)) * 8,
-                    keep_or_zero<OP>(f.bv[k], (f.okb >> k) & 1));
+            st_row8(Bs + (q / (N / 8)) * LDB + (q % (N / 8)) * 8, f.bv[k]);
     }
 }
 
@@ -194,33 +200,85 @@ __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, SLAB> &f,
 // 2. Chunk states and the serial pass over chunks.
 //    One workgroup per (batch, segment, head).  The state H (state_dim x
 //    head_dim, fp32) lives in MFMA accumulators for the whole segment, its
-//    16 x 16 tiles dealt round-robin to the 4 waves.  Slabs of SLAB row
-//    blocks are double-buffered in LDS: while one slab is applied, the next
-//    is staged and the one after it is being fetched.  Per block:
+//    16 x 16 tiles dealt round-robin to the 4 waves.  Slabs are fetched two
+//    ahead into registers and staged through one LDS buffer.  Per block:
 //        H <- 2^lcs_last H + B^T (w x),  w_j = 2^(lcs_last - lcs_j) d_j,
 //    both operands read k-major through transposing LDS loads.  Before the
 //    first block of every chunk the state is written out as that chunk's
 //    boundary state.  Segment 0 starts from init_state; later segments start
 //    from zero and are corrected by k_seg_combine and in k_chunk_out.
+template <typename IO, int P, int N> struct SpState {
+    typedef typename Op<IO>::type OP;
+    typedef Mfma<OP> M;
+    static constexpr int SLAB = 2;
+    static constexpr int SR = SLAB * kT;
+    static constexpr int LDX = P + 16, LDB = N + 16;
+    static constexpr int CT = P / 16;
+    static constexpr int TILES = (N / 16) * CT;
+    static constexpr int TPW = (TILES + kWaves - 1) / kWaves;
+};
+
+// Applies one staged slab to the accumulators (acc: the wave's TPW tiles;
+// inlined, so they stay in registers).
+template <typename IO, int P, int N>
+__device__ __forceinline__ void sp_apply(f32x4 *acc, float &logdec,
+                                         const typename Op<IO>::type *lds, const SlabPos &sp,
+                                         const float *lam, float *Hb_bh, float *Dlog_bh,
+                                         int64_t NPh, int nsegs, int wave, int lane, int tid) {
+    typedef SpState<IO, P, N> S;
+    typedef typename S::M M;
+    constexpr int T = kT, KS = T / M::K;
+    const auto *Xw = lds;
+    const auto *Bs = lds + S::SR * S::LDX;
+#pragma unroll
+    for (int jb = 0; jb < S::SLAB; ++jb) {
+        if (jb < sp.nb) {
+            if (sp.bi0 + jb == 0) {  // first block of a chunk: emit the boundary state
+                float *dst = Hb_bh + sp.c * NPh;
+#pragma unroll
+                for (int i = 0; i < S::TPW; ++i) {
+                    const int ti = wave + kWaves * i;
+                    if (ti < S::TILES) {
+                        const int tr = ti / S::CT, tc = ti % S::CT;
+                        float *d0 = dst + (tr * 16 + 4 * (lane >> 4)) * P + tc * 16 + (lane & 15);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) d0[r * P] = acc[i][r];
+                    }
+                }
+                if (nsegs > 1 && tid == 0) Dlog_bh[sp.c] = logdec;
+            }
+            const float decay = exp2_fast(lam[jb]);
+            logdec += lam[jb];
+#pragma unroll
+            for (int i = 0; i < S::TPW; ++i) acc[i] *= decay;
+#pragma unroll
+            for (int q = 0; q < KS; ++q) {
+#pragma unroll
+                for (int i = 0; i < S::TPW; ++i) {
+                    const int ti = wave + kWaves * i;
+                    if (ti < S::TILES) {
+                        const int tr = ti / S::CT, tc = ti % S::CT;
+                        acc[i] = M::mma(frag_kmajor(Bs, S::LDB, jb * T, q, tr * 16, lane),
+                                        frag_kmajor(Xw, S::LDX, jb * T, q, tc * 16, lane),
+                                        acc[i]);
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <typename IO, int P, int N>
 __global__ __launch_bounds__(256) void k_state_pass(
     const IO *__restrict__ x, const typename Op<IO>::type *__restrict__ Bm,
-    const float *__restrict__ lcs, const float *__restrict__ dtp, const float *__restrict__ init,
+    const float *__restrict__ lcs, const float *__restrict__ wgt, const float *__restrict__ init,
     float *__restrict__ Hb, float *__restrict__ Eseg, float *__restrict__ Dlog,
     float *__restrict__ Lseg, float *__restrict__ final_state, int64_t l, int h, int g, int64_t Q,
     int64_t nc, int64_t Qp, int64_t cps, int64_t nseg) {
     typedef typename Op<IO>::type OP;
-    typedef Mfma<OP> M;
-    constexpr int T = kT;
-    constexpr int KS = T / M::K;            // MFMA steps per block
-    constexpr int SLAB = 2;                 // blocks per slab
-    constexpr int SR = SLAB * T;            // rows per slab
-    constexpr int LDX = P + 16, LDB = N + 16;
-    constexpr int CT = P / 16;
-    constexpr int TILES = (N / 16) * CT;
-    constexpr int TPW = (TILES + kWaves - 1) / kWaves;
-    constexpr int BUF = SR * LDX + SR * LDB;
-    __shared__ __attribute__((aligned(16))) OP lds[2 * BUF];  // [w x | B] x 2 buffers
+    typedef SpState<IO, P, N> S;
+    constexpr int T = kT, SLAB = S::SLAB, TPW = S::TPW, CT = S::CT, TILES = S::TILES;
+    __shared__ __attribute__((aligned(16))) OP lds[S::SR * S::LDX + S::SR * S::LDB];  // [w x | B]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
@@ -228,16 +286,19 @@ __global__ __launch_bounds__(256) void k_state_pass(
     const int64_t seg = item % nseg;
     const int64_t b = item / nseg;
     const int gi = hh / (h / g);
-    const int64_t nsb = Qp / T;
+    const int nsb = (int)(Qp / T);
+    const int nspc = (nsb + SLAB - 1) / SLAB;  // slabs per chunk
     const int64_t c0 = seg * cps;
     const int64_t c1 = (c0 + cps < nc) ? c0 + cps : nc;
-    const int64_t sb0 = c0 * nsb, sb1 = c1 * nsb;
+    const int64_t nslab = (c1 - c0) * nspc;
     const float *lcs_bh = lcs + (b * h + hh) * nc * Qp;
-    const float *dtp_bh = dtp + (b * h + hh) * nc * Qp;
+    const Rsrc rw = make_rsrc(wgt + (b * h + hh) * nc * Qp, nc * Qp * 4);
     const int64_t NP = (int64_t)N * P;
     const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N;
     const IO *xb = x + (b * l * h + hh) * P;   // row t at xb + t * xs
     const OP *Bb = Bm + (b * l * g + gi) * N;   // row t at Bb + t * bs
+    float *Hb_bh = Hb + (b * nc * h + hh) * NP;  // chunk c at Hb_bh + c * h * NP
+    float *Dlog_bh = Dlog + (b * h + hh) * nc;
 
     f32x4 acc[TPW];
 #pragma unroll
@@ -258,75 +319,43 @@ __global__ __launch_bounds__(256) void k_state_pass(
     }
     float logdec = 0.f;
 
-    SpBuf<IO, P, N, SLAB> pf;
-    const int64_t nslab = (sb1 - sb0 + SLAB - 1) / SLAB;
-    float lam_next[SLAB];
-    if (nslab > 0) {
-        sp_prefetch(pf, sb0, sb1, nsb, xb, Bb, lcs_bh, dtp_bh, l, Q, xs, bs, tid);
+    // two slabs in flight in registers; slab si lives in pf[si & 1]
+    SpBuf<IO, P, N, SLAB> pa, pb;
+    if (nslab > 0)
+        sp_prefetch(pa, slab_pos(0, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q, nsb, xs, bs,
+                    tid);
+    if (nslab > 1)
+        sp_prefetch(pb, slab_pos(1, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q, nsb, xs, bs,
+                    tid);
+    for (int64_t si = 0; si < nslab; si += 2) {
+        {
+            const SlabPos sp = slab_pos(si, c0, nspc, nsb, SLAB);
+            float lam[SLAB];
 #pragma unroll
-        for (int jb = 0; jb < SLAB; ++jb) lam_next[jb] = pf.lam[jb];
-        sp_stage(pf, lds, lds + SR * LDX, tid);
-        if (nslab > 1)
-            sp_prefetch(pf, sb0 + SLAB, sb1, nsb, xb, Bb, lcs_bh, dtp_bh, l, Q, xs, bs, tid);
-    }
-    lds_barrier();
-    for (int64_t si = 0; si < nslab; ++si) {
-        const int64_t s0 = sb0 + si * SLAB;
-        const int nb = (int)((sb1 - s0) < SLAB ? (sb1 - s0) : SLAB);
-        float lam[SLAB];
-#pragma unroll
-        for (int jb = 0; jb < SLAB; ++jb) lam[jb] = lam_next[jb];
-        const OP *Xw = lds + (si & 1) * BUF;
-        const OP *Bs = Xw + SR * LDX;
-        if (si + 1 < nslab) {  // stage the next slab into the other buffer
-#pragma unroll
-            for (int jb = 0; jb < SLAB; ++jb) lam_next[jb] = pf.lam[jb];
-            OP *nx = lds + ((si + 1) & 1) * BUF;
-            sp_stage(pf, nx, nx + SR * LDX, tid);
+            for (int jb = 0; jb < SLAB; ++jb) lam[jb] = pa.lam[jb];
+            lds_barrier();  // the previous slab's reads are done
+            sp_stage(pa, lds, lds + S::SR * S::LDX, tid);
             if (si + 2 < nslab)
-                sp_prefetch(pf, s0 + 2 * SLAB, sb1, nsb, xb, Bb, lcs_bh, dtp_bh, l, Q, xs, bs,
-                            tid);
+                sp_prefetch(pa, slab_pos(si + 2, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q,
+                            nsb, xs, bs, tid);
+            lds_barrier();
+            sp_apply<IO, P, N>(acc, logdec, lds, sp, lam, Hb_bh, Dlog_bh, h * NP, (int)nseg,
+                               wave, lane, tid);
         }
+        if (si + 1 < nslab) {
+            const SlabPos sp = slab_pos(si + 1, c0, nspc, nsb, SLAB);
+            float lam[SLAB];
 #pragma unroll
-        for (int jb = 0; jb < SLAB; ++jb) {
-            if (jb < nb) {
-                const int64_t sb = s0 + jb;
-                if (sb % nsb == 0) {  // first block of a chunk: emit the boundary state
-                    const int64_t c = sb / nsb;
-                    float *dst = Hb + ((b * nc + c) * h + hh) * NP;
-#pragma unroll
-                    for (int i = 0; i < TPW; ++i) {
-                        const int ti = wave + kWaves * i;
-                        if (ti < TILES) {
-                            const int tr = ti / CT, tc = ti % CT;
-                            float *d0 = dst + (int64_t)(tr * 16 + 4 * (lane >> 4)) * P +
-                                        tc * 16 + (lane & 15);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) d0[r * P] = acc[i][r];
-                        }
-                    }
-                    if (nseg > 1 && tid == 0) Dlog[(b * h + hh) * nc + c] = logdec;
-                }
-                const float decay = exp2_fast(lam[jb]);
-                logdec += lam[jb];
-#pragma unroll
-                for (int i = 0; i < TPW; ++i) acc[i] *= decay;
-#pragma unroll
-                for (int q = 0; q < KS; ++q) {
-#pragma unroll
-                    for (int i = 0; i < TPW; ++i) {
-                        const int ti = wave + kWaves * i;
-                        if (ti < TILES) {
-                            const int tr = ti / CT, tc = ti % CT;
-                            acc[i] = M::mma(frag_kmajor(Bs, LDB, jb * T, q, tr * 16, lane),
-                                            frag_kmajor(Xw, LDX, jb * T, q, tc * 16, lane),
-                                            acc[i]);
-                        }
-                    }
-                }
-            }
+            for (int jb = 0; jb < SLAB; ++jb) lam[jb] = pb.lam[jb];
+            lds_barrier();
+            sp_stage(pb, lds, lds + S::SR * S::LDX, tid);
+            if (si + 3 < nslab)
+                sp_prefetch(pb, slab_pos(si + 3, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q,
+                            nsb, xs, bs, tid);
+            lds_barrier();
+            sp_apply<IO, P, N>(acc, logdec, lds, sp, lam, Hb_bh, Dlog_bh, h * NP, (int)nseg,
+                               wave, lane, tid);
         }
-        lds_barrier();
     }
 
     float *out = nullptr;
@@ -393,8 +422,8 @@ static __global__ __launch_bounds__(256) void k_seg_combine(float *__restrict__ 
 // ----------------------------------------------------------------------------
 // Staging of the chunk output: one block of kT rows.  Pieces are 8
 // consecutive elements of one row of C and of B (same row and columns, N / 8
-// per row) or of x (P / 8 per row).  As in the state pass, the prefetch only
-// issues loads and records which pieces are real rows.
+// per row) or of x (P / 8 per row), loaded through buffer resources that end
+// at the chunk's last valid row (zeros beyond).
 template <typename IO, int P, int N, int NT> struct CoBuf {
     typedef typename Op<IO>::type OP;
     static constexpr int NPC = kT * N / 8, NPX = kT * P / 8;
@@ -402,33 +431,34 @@ template <typename IO, int P, int N, int NT> struct CoBuf {
     static constexpr int KX = (NPX + NT - 1) / NT;
     Row8v<OP> cv[KC], bv[KC];
     Row8v<IO> xv[KX];
-    float xl[KX], xd[KX];  // lcs and d of the x piece's row
-    float last, ls, ds;    // lcs at the block end; lcs and d of row tid (tid < kT)
-    uint32_t okc, okx;
+    float xw[KX];  // weight of the x piece's row
+    float ls, ds;  // lcs and d of row tid (tid < kT)
+    float l15;     // lcs of the block's row 15
 };
 
 template <typename IO, int P, int N, int NT>
 __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, NT> &f, int s, const IO *xb,
                                             const typename Op<IO>::type *Bb,
-                                            const typename Op<IO>::type *Cb, const float *lcs_c,
-                                            const float *dtp_c, int64_t t0, int64_t l, int64_t Q,
-                                            int64_t xstride, int64_t bstride, int tid) {
+                                            const typename Op<IO>::type *Cb, Rsrc rl, Rsrc rd,
+                                            Rsrc rw, const float *lcs_c, int64_t rows,
+                                            int64_t xs, int64_t bs, int tid) {
     typedef CoBuf<IO, P, N, NT> F;
+    typedef typename Op<IO>::type OP;
     constexpr int T = kT;
-    const int64_t rpb = (int64_t)s * T;
-    f.okc = 0;
-    f.okx = 0;
+    const int64_t r0 = (int64_t)s * T;  // first row of the block inside the chunk
+    const int64_t valid = rows - r0;
+    const Rsrc rb = make_rsrc(Bb + r0 * bs, valid * bs * (int64_t)sizeof(OP));
+    const Rsrc rc = make_rsrc(Cb + r0 * bs, valid * bs * (int64_t)sizeof(OP));
+    const Rsrc rx = make_rsrc(xb + r0 * xs, valid * xs * (int64_t)sizeof(IO));
+    const uint32_t soff = (uint32_t)r0 * 4u;
 #pragma unroll
     for (int k = 0; k < F::KC; ++k) {
         const int q = tid + k * NT;
         if (F::NPC % NT == 0 || q < F::NPC) {
             const int j = q / (N / 8), cc = q % (N / 8);
-            const int64_t rp = rpb + j, t = t0 + rp;
-            const bool ok = rp < Q && t < l;
-            const int64_t off = (ok ? t : 0) * bstride + cc * 8;
-            f.cv[k] = ld_row8(Cb + off);
-            f.bv[k] = ld_row8(Bb + off);
-            f.okc |= (uint32_t)ok << k;
+            const uint32_t off = (uint32_t)(j * bs + cc * 8) * (uint32_t)sizeof(OP);
+            f.cv[k] = buf_row8<OP>(rc, off);
+            f.bv[k] = buf_row8<OP>(rb, off);
         }
     }
 #pragma unroll
@@ -436,25 +466,28 @@ __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, NT> &f, int s, const
         const int q = tid + k * NT;
         if (F::NPX % NT == 0 || q < F::NPX) {
             const int j = q / (P / 8), cc = q % (P / 8);
-            const int64_t rp = rpb + j, t = t0 + rp;
-            const bool ok = rp < Q && t < l;
-            f.xv[k] = ld_row8(xb + (ok ? t : 0) * xstride + cc * 8);
-            f.xl[k] = lcs_c[rp];
-            f.xd[k] = dtp_c[rp];
-            f.okx |= (uint32_t)ok << k;
+            f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * xs + cc * 8) * (uint32_t)sizeof(IO));
+            f.xw[k] = buf_f32(rw, (uint32_t)j * 4u, soff);
         }
     }
-    f.last = lcs_c[rpb + T - 1];
-    const int64_t rt = rpb + (tid < T ? tid : 0);
-    f.ls = lcs_c[rt];
-    f.ds = dtp_c[rt];
+    const uint32_t rt = (uint32_t)(tid < T ? tid : 0) * 4u;
+    f.ls = buf_f32(rl, rt, soff);
+    f.ds = buf_f32(rd, rt, soff);
+    f.l15 = lcs_c[r0 + 15];
 }
+
+// Per-row factors of a staged block (LDS), T floats each.
+struct alignas(16) CoRows {
+    float lcs[kT];   // cumulative log2 decay inside the block
+    float d[kT];     // time step
+    float a[kT];     // 2^(lcs_i - lcs_15)
+    float bw[kT];    // 2^(lcs_15 - lcs_j) d_j
+};
 
 template <typename IO, int P, int N, int NT>
 __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, NT> &f, typename Op<IO>::type *Cs,
                                          typename Op<IO>::type *Bs, typename Op<IO>::type *Xs,
-                                         typename Op<IO>::type *Xw, float *lcs_s, float *lcsd_s,
-                                         int tid) {
+                                         typename Op<IO>::type *Xw, CoRows &rows, int tid) {
     typedef CoBuf<IO, P, N, NT> F;
     typedef typename Op<IO>::type OP;
     constexpr int LDN = N + Mfma<OP>::PAD, LDX = P + 16;
@@ -463,9 +496,8 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, NT> &f, typename 
         const int q = tid + k * NT;
         if (F::NPC % NT == 0 || q < F::NPC) {
             const int o = (q / (N / 8)) * LDN + (q % (N / 8)) * 8;
-            const bool ok = (f.okc >> k) & 1;
-            st_row8(Cs + o, keep_or_zero<OP>(f.cv[k], ok));
-            st_row8(Bs + o, keep_or_zero<OP>(f.bv[k], ok));
+            st_row8(Cs + o, f.cv[k]);
+            st_row8(Bs + o, f.bv[k]);
         }
     }
 #pragma unroll
@@ -473,19 +505,17 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, NT> &f, typename 
         const int q = tid + k * NT;
         if (F::NPX % NT == 0 || q < F::NPX) {
             const int o = (q / (P / 8)) * LDX + (q % (P / 8)) * 8;
-            const bool ok = (f.okx >> k) & 1;
-            const float w = ok ? exp2_fast(f.last - f.xl[k]) * f.xd[k] : 0.f;
             Row8v<OP> xo, wo;
-            x_pieces(f.xv[k], w, ok, xo, wo);
+            x_pieces(f.xv[k], f.xw[k], xo, wo);
             st_row8(Xs + o, xo);
             st_row8(Xw + o, wo);
         }
     }
     if (tid < kT) {
-        lcs_s[tid] = f.ls;
-        // the score weight 2^(lcs_i - lcs_j) d_j is taken as 2^(lcs_i - lcsd_j)
-        // with lcsd_j = lcs_j - log2 d_j; d = 0 gives +inf and weight 0
-        lcsd_s[tid] = f.ls - __builtin_amdgcn_logf(f.ds);
+        rows.lcs[tid] = f.ls;
+        rows.d[tid] = f.ds;
+        rows.a[tid] = exp2_fast(f.ls - f.l15);
+        rows.bw[tid] = exp2_fast(f.l15 - f.ls) * f.ds;
     }
 }
 
@@ -495,15 +525,19 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, NT> &f, typename 
 //    pt = w, w + W, ... of everything it produces: its columns of the running
 //    state H (all state_dim rows) stay in MFMA accumulators across the
 //    chunk's blocks and feed the output product straight from registers, and
-//    it computes y^T for those columns, so that each lane holds 4
-//    consecutive head_dim values of one row (one vector store).  Per block,
-//    with C, B, x and w x double-buffered in LDS and the block after next
-//    already being fetched:
+//    it computes y^T for those columns.  Per block, with C, B, x and w x
+//    double-buffered in LDS and the block after next already being fetched:
 //      G^T = B C^T on the 3 causal 16 x 16 tiles, and
 //      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i), in registers;
-//      y^T = 2^lcs_i (H^T C^T) + x^T P^T + D x^T, written to y;
+//      y^T = 2^lcs_i (H^T C^T) + x^T P^T + D x^T, staged in LDS and written
+//            out as whole rows after the block's barrier;
 //      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
-//    One workgroup barrier per block.
+//    The decay factor of P is taken as a_i b_j with a_i = 2^(lcs_i - lcs_15)
+//    and b_j = 2^(lcs_15 - lcs_j) d_j, both per row, when the block's total
+//    log2 decay is above -kSplitLimit (every factor then stays inside fp32's
+//    normal range); otherwise as one exponential per element.
+constexpr float kSplitLimit = 60.f;
+
 template <int P> struct CoShape {
     static constexpr int W = P >= 64 ? 4 : P / 16;  // waves
     static constexpr int NT = 64 * W;               // threads
@@ -513,9 +547,10 @@ template <typename IO, int P, int N>
 __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
     const IO *__restrict__ x, const typename Op<IO>::type *__restrict__ Bm,
     const typename Op<IO>::type *__restrict__ Cm, const float *__restrict__ D,
-    const float *__restrict__ lcs, const float *__restrict__ dtp, const float *__restrict__ Hb,
-    const float *__restrict__ Hin, const float *__restrict__ Dlog, IO *__restrict__ y,
-    int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp, int64_t cps, int64_t nseg) {
+    const float *__restrict__ lcs, const float *__restrict__ dtp, const float *__restrict__ wgt,
+    const float *__restrict__ Hb, const float *__restrict__ Hin, const float *__restrict__ Dlog,
+    IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp, int64_t cps,
+    int64_t nseg) {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
     constexpr int W = CoShape<P>::W, NT = CoShape<P>::NT;
@@ -525,13 +560,20 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
     constexpr int NB = N / 32;            // 32-blocks of the state index
     constexpr int LDN = N + M::PAD;       // [row][n]: C, B
     constexpr int LDX = P + 16;           // [row][p]: x, w x
+    constexpr int LDY = P + 16 / (int)sizeof(IO);  // [row][p]: y staging
     constexpr int CT = P / 16;            // head_dim column tiles
     constexpr int CPW = CT / W;           // column tiles per wave
     constexpr int RT = N / 16;            // state row tiles
     constexpr int BUF = 2 * T * LDN + 2 * T * LDX;
+    constexpr int YV = 16 / (int)sizeof(IO);     // y elements per 16-byte store
+    constexpr int YTPR = P / YV;                 // threads per y row
+    constexpr int YRPP = NT / YTPR;              // y rows per store pass
+    // 2-byte y is staged in LDS and written as whole rows; 4-byte y goes out
+    // straight from the tiles (16 consecutive columns = 64 bytes per row)
+    constexpr bool kStageY = sizeof(IO) == 2;
     __shared__ __attribute__((aligned(16))) OP lds[2 * BUF];  // [C | B | x | w x] x 2
-    __shared__ float lcs_s[2][T];
-    __shared__ float lcsd_s[2][T];
+    __shared__ __attribute__((aligned(16))) IO Ys[2][kStageY ? T * LDY : 1];
+    __shared__ CoRows rowsf[2];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, li = lane & 15;
@@ -542,19 +584,21 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
     const int gi = hh / (h / g);
     const int64_t seg = c / cps;
     const int64_t NP = (int64_t)N * P;
-    const float *lcs_c = lcs + ((b * h + hh) * nc + c) * Qp;
-    const float *dtp_c = dtp + ((b * h + hh) * nc + c) * Qp;
+    const int64_t rbase = ((b * h + hh) * nc + c) * Qp;
+    const float *lcs_c = lcs + rbase;
+    const Rsrc rl = make_rsrc(lcs_c, Qp * 4), rd = make_rsrc(dtp + rbase, Qp * 4);
+    const Rsrc rw = make_rsrc(wgt + rbase, Qp * 4);
     const float Dh = D ? D[hh] : 0.f;
     const int64_t rows = (Q < l - c * Q) ? Q : (l - c * Q);  // valid rows of this chunk
     const int nblk = (int)((rows + T - 1) / T);
     const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N, t0 = c * Q;
-    const IO *xb = x + (b * l * h + hh) * P;   // row t at xb + t * xs
-    const OP *Bb = Bm + (b * l * g + gi) * N;   // row t at Bb + t * bs
-    const OP *Cb = Cm + (b * l * g + gi) * N;
-    IO *yb = y + (b * l * h + hh) * P;
+    const IO *xb = x + ((b * l + t0) * h + hh) * P;   // chunk row r at xb + r * xs
+    const OP *Bb = Bm + ((b * l + t0) * g + gi) * N;   // chunk row r at Bb + r * bs
+    const OP *Cb = Cm + ((b * l + t0) * g + gi) * N;
+    IO *yb = y + ((b * l + t0) * h + hh) * P;
 
     CoBuf<IO, P, N, NT> pf;
-    co_prefetch(pf, 0, xb, Bb, Cb, lcs_c, dtp_c, t0, l, Q, xs, bs, tid);
+    co_prefetch(pf, 0, xb, Bb, Cb, rl, rd, rw, lcs_c, rows, xs, bs, tid);
 
     // ---- the wave's state columns entering the chunk (all loads issued first)
     f32x4 accH[CPW][RT];
@@ -564,7 +608,7 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
         for (int u = 0; u < CPW; ++u)
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) {
-                const int64_t off = (int64_t)(tr * 16 + 4 * lg) * P + (wave + W * u) * 16 + li;
+                const int off = (tr * 16 + 4 * lg) * P + (wave + W * u) * 16 + li;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) accH[u][tr][r] = hb[off + r * P];
             }
@@ -575,8 +619,7 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
             for (int u = 0; u < CPW; ++u)
 #pragma unroll
                 for (int tr = 0; tr < RT; ++tr) {
-                    const int64_t off =
-                        (int64_t)(tr * 16 + 4 * lg) * P + (wave + W * u) * 16 + li;
+                    const int off = (tr * 16 + 4 * lg) * P + (wave + W * u) * 16 + li;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) iv[u][tr][r] = hin[off + r * P];
                 }
@@ -588,9 +631,9 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
         }
     }
 
-    co_stage(pf, lds, lds + T * LDN, lds + 2 * T * LDN, lds + 2 * T * LDN + T * LDX, lcs_s[0],
-             lcsd_s[0], tid);
-    if (nblk > 1) co_prefetch(pf, 1, xb, Bb, Cb, lcs_c, dtp_c, t0, l, Q, xs, bs, tid);
+    co_stage(pf, lds, lds + T * LDN, lds + 2 * T * LDN, lds + 2 * T * LDN + T * LDX, rowsf[0],
+             tid);
+    if (nblk > 1) co_prefetch(pf, 1, xb, Bb, Cb, rl, rd, rw, lcs_c, rows, xs, bs, tid);
     lds_barrier();
 
     for (int s = 0; s < nblk; ++s) {
@@ -599,42 +642,79 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
         const OP *Bs = Cs + T * LDN;
         const OP *Xs = Bs + T * LDN;
         const OP *Xw = Xs + T * LDX;
-        const float *ls = lcs_s[cur];
-        const float *lsd = lcsd_s[cur];
+        const CoRows &rf = rowsf[cur];
+        IO *Yc = Ys[cur];
         if (s + 1 < nblk) {  // stage the next block into the other buffer
             OP *nC = lds + (cur ^ 1) * BUF;
             co_stage(pf, nC, nC + T * LDN, nC + 2 * T * LDN, nC + 2 * T * LDN + T * LDX,
-                     lcs_s[cur ^ 1], lcsd_s[cur ^ 1], tid);
+                     rowsf[cur ^ 1], tid);
             if (s + 2 < nblk)
-                co_prefetch(pf, s + 2, xb, Bb, Cb, lcs_c, dtp_c, t0, l, Q, xs, bs, tid);
+                co_prefetch(pf, s + 2, xb, Bb, Cb, rl, rd, rw, lcs_c, rows, xs, bs, tid);
         }
 
         // ---- masked, decayed scores: G^T tiles (jt, it), jt <= it.
         //      pv[it][jt] element r: j = 16 jt + 4 lg + r, i = 16 it + li
+        const float lam = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rf.lcs[T - 1])));
+        const bool split = lam > -kSplitLimit;
+        f32x4 gt[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int it = k == 0 ? 0 : 1, jt = k == 2 ? 1 : 0;
+            gt[k] = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NS; ++ks)
+                gt[k] = M::mma(lds_frag(Bs, LDN, jt * 16, ks * M::K, lane),
+                               lds_frag(Cs, LDN, it * 16, ks * M::K, lane), gt[k]);
+        }
         f32x4 pv[2][2];
+        float colscale[2];
         pv[0][1] = zero4();
+        if (split) {
+            const float s15 = exp2_fast(rf.lcs[15]);
+            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&rf.bw[4 * lg]);
+            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&rf.bw[16 + 4 * lg]);
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int i = it * 16 + li;
-            const float lci = ls[i];
-#pragma unroll
-            for (int jt = 0; jt <= it; ++jt) {
-                f32x4 gacc = zero4();
-#pragma unroll
-                for (int ks = 0; ks < NS; ++ks)
-                    gacc = M::mma(lds_frag(Bs, LDN, jt * 16, ks * M::K, lane),
-                                  lds_frag(Cs, LDN, it * 16, ks * M::K, lane), gacc);
+            for (int it = 0; it < 2; ++it) {
+                const int i = it * 16 + li;
+                const float ai = rf.a[i];
+                colscale[it] = ai * s15;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int j = jt * 16 + 4 * lg + r;
-                    pv[it][jt][r] = (j <= i) ? gacc[r] * exp2_fast(lci - lsd[j]) : 0.f;
+                    const int j0 = 4 * lg + r;
+                    if (it == 0) {
+                        pv[0][0][r] = (j0 <= li) ? gt[0][r] * (ai * b0[r]) : 0.f;
+                    } else {
+                        pv[1][0][r] = gt[1][r] * (ai * b0[r]);
+                        pv[1][1][r] = (j0 <= li) ? gt[2][r] * (ai * b1[r]) : 0.f;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int i = it * 16 + li;
+                const float lci = rf.lcs[i];
+                colscale[it] = exp2_fast(lci);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j0 = 4 * lg + r;
+                    if (it == 0) {
+                        pv[0][0][r] = (j0 <= li)
+                                          ? gt[0][r] * exp2_fast(lci - rf.lcs[j0]) * rf.d[j0]
+                                          : 0.f;
+                    } else {
+                        pv[1][0][r] = gt[1][r] * exp2_fast(lci - rf.lcs[j0]) * rf.d[j0];
+                        pv[1][1][r] = (j0 <= li) ? gt[2][r] * exp2_fast(lci - rf.lcs[16 + j0]) *
+                                                       rf.d[16 + j0]
+                                                 : 0.f;
+                    }
                 }
             }
         }
 
         // ---- y^T tiles of the wave's columns: element r of lane l is
-        //      (p = 16 pt + 4 lg + r, i = 16 it + li)
-        const int64_t rpb = (int64_t)s * T;
+        //      (p = 16 pt + 4 lg + r, i = 16 it + li); staged in Ys
 #pragma unroll
         for (int u = 0; u < CPW; ++u) {
             const int pt = wave + W * u;
@@ -648,20 +728,26 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
                     for (int q = 0; q < KS; ++q)
                         ya = M::mma(frag_from_acc<OP>(accH[u][2 * m], accH[u][2 * m + 1], q),
                                     frag_rows_kconv(Cs, LDN, it * 16, 32 * m, q, lane), ya);
-                ya *= exp2_fast(ls[i]);
+                ya *= colscale[it];
 #pragma unroll
                 for (int q = 0; q < KS; ++q)
                     ya = M::mma(frag_kmajor(Xs, LDX, 0, q, pt * 16, lane),
                                 frag_from_acc<OP>(pv[it][0], pv[it][1], q), ya);
                 const f32x4 xv = lds_load4(Xs + i * LDX + pt * 16 + 4 * lg);
-                const int64_t rp = rpb + i;
-                if (rp < rows) store4(yb + (t0 + rp) * xs + pt * 16 + 4 * lg, ya + Dh * xv);
+                if constexpr (kStageY) {
+                    store4(Yc + i * LDY + pt * 16 + 4 * lg, ya + Dh * xv);
+                } else {
+                    const int64_t r0 = (int64_t)s * T;
+                    const Rsrc ry = make_rsrc(yb + r0 * xs, (rows - r0) * xs * (int64_t)sizeof(IO));
+                    buf_store16(ry, (uint32_t)(i * xs + pt * 16 + 4 * lg) * (uint32_t)sizeof(IO),
+                                __builtin_bit_cast(u32x4, ya + Dh * xv));
+                }
             }
         }
 
         // ---- carry the state to the next block of the chunk
         if (s + 1 < nblk) {
-            const float decay = exp2_fast(ls[T - 1]);
+            const float decay = exp2_fast(lam);
 #pragma unroll
             for (int u = 0; u < CPW; ++u) {
                 const int pt = wave + W * u;
@@ -676,7 +762,21 @@ __global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
                 }
             }
         }
-        lds_barrier();  // this block's buffer is free; the next one is staged
+        lds_barrier();  // this block's operands are free, its y rows staged
+
+        // ---- write the block's y rows (whole rows, 16 bytes per thread)
+        if constexpr (kStageY) {
+            const int64_t r0 = (int64_t)s * T;
+            const Rsrc ry = make_rsrc(yb + r0 * xs, (rows - r0) * xs * (int64_t)sizeof(IO));
+#pragma unroll
+            for (int rr = 0; rr < T; rr += YRPP) {
+                const int row = rr + tid / YTPR, cv = tid % YTPR;
+                if (YRPP <= T || row < T) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(Yc + row * LDY + cv * YV);
+                    buf_store16(ry, (uint32_t)(row * xs + cv * YV) * (uint32_t)sizeof(IO), v);
+                }
+            }
+        }
     }
 }
 
@@ -686,6 +786,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     typedef typename Op<IO>::type OP;
     float *lcs = reinterpret_cast<float *>(a.ws + pl.off_lcs);
     float *dtp = reinterpret_cast<float *>(a.ws + pl.off_dtp);
+    float *wgt = reinterpret_cast<float *>(a.ws + pl.off_wgt);
     float *Hb = reinterpret_cast<float *>(a.ws + pl.off_hb);
     float *Eseg = reinterpret_cast<float *>(a.ws + pl.off_seg);
     float *Dlog = reinterpret_cast<float *>(a.ws + pl.off_dlog);
@@ -713,14 +814,14 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     trace_begin(0, s);
     hipLaunchKernelGGL(k_prep<IO>, dim3((unsigned)(na + ncopy)), dim3(kThreads), 0, s, dt, a.A,
                        a.dt_bias, a.softplus, a.dt_min, a.dt_max, pl.b, pl.l, h, pl.Q, pl.nc,
-                       pl.Qp, lcs, dtp, na, Bm, Cm, Bf, Cf, pieces);
+                       pl.Qp, lcs, dtp, wgt, na, Bm, Cm, Bf, Cf, pieces);
     trace_end(0, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     trace_begin(1, s);
     hipLaunchKernelGGL((k_state_pass<IO, P, N>), dim3((unsigned)(pl.b * pl.nseg * pl.h)),
-                       dim3(kThreads), 0, s, x, Bop, lcs, dtp, a.init, Hb, Eseg, Dlog, Lseg,
+                       dim3(kThreads), 0, s, x, Bop, lcs, wgt, a.init, Hb, Eseg, Dlog, Lseg,
                        a.final_state, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
     trace_end(1, s);
     e = hipGetLastError();
@@ -740,7 +841,8 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
 
     trace_begin(3, s);
     hipLaunchKernelGGL((k_chunk_out<IO, P, N>), dim3((unsigned)(pl.b * pl.nc * pl.h)),
-                       dim3(CoShape<P>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, Hb, Eseg, Dlog, y,
+                       dim3(CoShape<P>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb, Eseg,
+                       Dlog, y,
                        pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
     trace_end(3, s);
     return hipGetLastError();

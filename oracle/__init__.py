@@ -69,10 +69,16 @@ def _load():
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when that is set (a machine's share of its cores)."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _c(a, dtype):

@@ -221,8 +221,9 @@ def _ws_layout(b, l, h, Q, io):
     lp = nc * Qp
     a256 = lambda v: (v + 255) // 256 * 256
     off_dtp = a256(b * h * lp * 4)
-    off_hb = off_dtp + a256(b * h * lp * 4)
-    return T, nc, Qp, lp, off_dtp, off_hb
+    off_wgt = off_dtp + a256(b * h * lp * 4)
+    off_hb = off_wgt + a256(b * h * lp * 4)
+    return T, nc, Qp, lp, off_dtp, off_wgt, off_hb
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -243,10 +244,12 @@ def test_stage_intermediates(orc, io):
     ssd.chunk_scan(G["x"], G["dt"], G["A"], G["B"], G["C"], G["D"], chunk_size=Q,
                    dt_bias=G["dt_bias"], initial_state=G["init"], workspace=ws)
     torch.cuda.synchronize()
-    T, nc, Qp, lp, off_dtp, off_hb = _ws_layout(b, l, h, Q, io)
+    T, nc, Qp, lp, off_dtp, off_wgt, off_hb = _ws_layout(b, l, h, Q, io)
     wsf = ws.view(torch.float32)
     lcs = wsf[:b * h * lp].view(b, h, nc, Qp)[..., :Q].reshape(b, h, nc * Q)[..., :l]
     dtp = wsf[off_dtp // 4: off_dtp // 4 + b * h * lp].view(b, h, nc, Qp)[..., :Q] \
+        .reshape(b, h, nc * Q)[..., :l]
+    wgt = wsf[off_wgt // 4: off_wgt // 4 + b * h * lp].view(b, h, nc, Qp)[..., :Q] \
         .reshape(b, h, nc * Q)[..., :l]
     hb = wsf[off_hb // 4: off_hb // 4 + b * nc * h * n * p].view(b, nc, h, n, p)
     _, _, inter = chunked.chunked_scan(**oracle_kw(inp), chunk=Q)
@@ -256,3 +259,9 @@ def test_stage_intermediates(orc, io):
     err = np.abs(cs - inter["cs"])
     assert (err <= 1e-5 * (1 + np.abs(inter["cs"]))).all(), err.max()
     check_close(to_f64(hb), inter["H_prev"], io, "boundary states", (1, 3, 4))
+    # weight of each row in the state at its block's (here: chunk's) end:
+    # exp(cs[last row of the chunk] - cs[row]) d[row]
+    cs_o = inter["cs"]
+    last = np.minimum(np.arange(l) // Q * Q + Q, l) - 1
+    w_o = np.exp(cs_o[..., last] - cs_o) * inter["d"]
+    check_close(to_f64(wgt), w_o, "f32", "row weights")
