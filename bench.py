@@ -75,24 +75,30 @@ def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
 
 
 def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
-    """Algorithmic bytes one launch of a kernel moves (each operand once)."""
+    """Algorithmic bytes of one launch of a scan kernel: every operand of its
+    step of the method moved once (per-row workspace arrays fp32, boundary
+    states fp32).  Reads of the segment-entry states, which exist only
+    because the serial pass is cut into segments, are not counted for the
+    chunk output; the segment combine's traffic is all of that kind."""
     nc, nseg, lp = plan_sizes(b, l, h, p, n, g, Q)
     th = b * l * h
-    x = th * p * s
-    BC = b * l * g * n * s
-    rows = b * h * lp * 4              # lcs or dtp
+    x = th * p * s                     # x (and y) in the io dtype
+    BC = b * l * g * n * s             # B or C, once per group (the fp16 copies for bf16)
+    rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
     hb = b * nc * h * n * p * 4        # boundary states
     seg = b * nseg * h * n * p * 4 if nseg > 1 else 0
     st = b * h * n * p * 4
     if name == "prep":
-        # dt read, lcs and d written; bf16 io also converts B and C to fp16
-        return th * s + 2 * rows + (4 * BC if s == 2 else 0)
+        # dt read; lcs, d and weights written; bf16: B and C read, fp16 copies written
+        return th * s + 3 * rows + (4 * BC if s == 2 else 0)
     if name == "state_pass":
-        return x + BC + 2 * rows + hb + seg + (st if final and nseg == 1 else 0)
+        # x and B read, row weights read, boundary states written
+        return x + BC + rows + hb + (st if final and nseg == 1 else 0)
     if name == "seg_combine":
         return 2 * seg + (st if final else 0)
     if name == "chunk_out":
-        return x + 2 * BC + 2 * rows + hb + seg + x   # x read, y written
+        # x, B, C and the lcs, d and weight rows read, boundary states read, y written
+        return x + 2 * BC + 3 * rows + hb + x
     raise KeyError(name)
 
 
@@ -184,14 +190,35 @@ def main():
     torch.cuda.synchronize()
 
     if args.traffic_probe:
+        # three scans, three decode steps on a decode-shaped state, then the
+        # calibration kernels: a 256 MiB fill (writes only) and a sum over the
+        # same 256 MiB (reads only)
         for i in range(3):
             run(i)
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
+        wd = syn.WORKLOADS["decode_2p7b"]
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wd.seed)
+        st = torch.randn(wd.batch, wd.heads, wd.state_dim, wd.head_dim, generator=gen,
+                         device=dev)
+        Ad = -torch.rand(wd.heads, generator=gen, device=dev) - 0.5
+        Dd = torch.ones(wd.heads, device=dev)
+        yd = torch.empty(wd.batch, wd.heads, wd.head_dim, dtype=torch.bfloat16, device=dev)
         for _ in range(3):
-            dst.copy_(src)
+            xd = torch.randn(wd.batch, wd.heads, wd.head_dim, generator=gen, device=dev).bfloat16()
+            dtd = torch.randn(wd.batch, wd.heads, generator=gen, device=dev).bfloat16()
+            Bd = torch.randn(wd.batch, wd.groups, wd.state_dim, generator=gen, device=dev).bfloat16()
+            Cd = torch.randn(wd.batch, wd.groups, wd.state_dim, generator=gen, device=dev).bfloat16()
+            ssd.step(st, xd, dtd, Ad, Bd, Cd, Dd, out=yd)
         torch.cuda.synchronize()
-        print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel()}))
+        cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            cal.fill_(1.0)
+        tot = 0.0
+        for _ in range(3):
+            tot += float(cal.sum())
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "calibration_bytes": cal.numel() * 4,
+                          "check": tot}))
         return
 
     log("timed", args.steps, "steps")

@@ -50,21 +50,25 @@ def build(force: bool = False) -> str:
     return _SO
 
 
+def _bind(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.ssd_oracle_scan.restype = ctypes.c_int
+    lib.ssd_oracle_scan.argtypes = [P, P, P, P, P, P, P, ctypes.c_int,
+                                    ctypes.c_double, ctypes.c_double, P,
+                                    I64, I64, I64, I64, I64, I64, ctypes.c_int,
+                                    P, I64, P, P, ctypes.c_int]
+    lib.ssd_oracle_dt.restype = ctypes.c_int
+    lib.ssd_oracle_dt.argtypes = [P, P, P, ctypes.c_int, ctypes.c_double,
+                                  ctypes.c_double, I64, I64, I64, ctypes.c_int, P, P]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
-        P = ctypes.c_void_p
-        I64 = ctypes.c_int64
-        lib.ssd_oracle_scan.restype = ctypes.c_int
-        lib.ssd_oracle_scan.argtypes = [P, P, P, P, P, P, P, ctypes.c_int,
-                                        ctypes.c_double, ctypes.c_double, P,
-                                        I64, I64, I64, I64, I64, I64, ctypes.c_int,
-                                        P, I64, P, P, ctypes.c_int]
-        lib.ssd_oracle_dt.restype = ctypes.c_int
-        lib.ssd_oracle_dt.argtypes = [P, P, P, ctypes.c_int, ctypes.c_double,
-                                      ctypes.c_double, I64, I64, I64, ctypes.c_int, P, P]
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(build()))
     return _lib
 
 
