@@ -113,10 +113,12 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
  * Bytes of workspace ssd_chunk_scan needs for these sizes (a pure function
  * of its arguments; 0 for invalid sizes).  Layout, in order, each part
  * 256-byte aligned: per-row cumulative log2 decay and processed time step
- * [batch, heads, padded seqlen] fp32 each; chunk-boundary states
- * [batch, chunks, heads, state_dim, head_dim] fp32; then, when the sequence
- * is cut into several segments, segment states [batch, segments, heads,
- * state_dim, head_dim] fp32 and per-chunk / per-segment log2 decays; then,
+ * [batch, heads, padded seqlen] fp32 each (cumulative log2 decay inside
+ * 32-row blocks, processed time step, weight in the state at the block end);
+ * chunk-boundary states [batch, chunks, heads, head_dim, state_dim] fp32
+ * (transposed); then, when the sequence is cut into several segments,
+ * segment states [batch, segments, heads, head_dim, state_dim] fp32 and
+ * per-chunk / per-segment log2 decays; then,
  * for bf16 io, fp16 copies of B and C [batch, seqlen, groups, state_dim].
  * The size returned covers both io dtypes.
  */

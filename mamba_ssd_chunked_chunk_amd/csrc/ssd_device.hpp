@@ -26,6 +26,8 @@ typedef _Float16 f16;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;      // waves per workgroup of the scan kernels
@@ -202,6 +204,82 @@ __device__ __forceinline__ void store4(bf16 *p, f32x4 v) {
 }
 __device__ __forceinline__ void store4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
 
+// ------------------------------------------------- swizzled LDS matrices ----
+// An LDS matrix M[row][col] with NCOL columns and no row padding, whose
+// 16-byte chunks are stored at chunk index (col / EPC) ^ f(row).  f maps
+// rows 0..15 one-to-one onto chunk offsets, and rows 0..7 (and 8..15) onto
+// distinct chunk pairs {2k, 2k + 1}; for NCOL = 128 fp16 this makes the
+// row-major 16-byte fragment reads (16 rows, one chunk each), the transposing
+// 8-byte reads (8 rows, two chunks each) and the row-piece stores all free of
+// bank conflicts.
+template <typename T, int NCOL> struct Swz {
+    static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+    static constexpr int CH = NCOL / EPC;            // chunks per row (a power of 2)
+    __device__ static __forceinline__ int f(int r) {
+        return ((((r & 7) << 1) | ((r >> 3) & 1))) & (CH - 1);
+    }
+    __device__ static __forceinline__ int at(int r, int c) {
+        return r * NCOL + (((c / EPC) ^ f(r)) * EPC) + (c % EPC);
+    }
+};
+
+// Row-major fragment (as lds_frag) of a swizzled matrix.
+template <typename OP, int NCOL>
+__device__ __forceinline__ typename Mfma<OP>::frag swz_frag(const OP *M, int row0, int k0,
+                                                            int lane) {
+    typedef Swz<OP, NCOL> S;
+    const OP *p = M + S::at(row0 + (lane & 15), k0 + Mfma<OP>::KPL * (lane >> 4));
+    return *reinterpret_cast<const typename Mfma<OP>::frag *>(p);
+}
+
+// Row-major rows read in the k-major contraction convention (as
+// frag_rows_kconv) from a swizzled matrix.
+template <typename OP, int NCOL>
+__device__ __forceinline__ typename Mfma<OP>::frag swz_rows_kconv(const OP *M, int row0, int kb,
+                                                                  int q, int lane) {
+    typedef Swz<OP, NCOL> S;
+    const int r = row0 + (lane & 15), g = lane >> 4;
+    if constexpr (sizeof(OP) == 2) {
+        const f16x4 a = *reinterpret_cast<const f16x4 *>(M + S::at(r, kb + 4 * g));
+        const f16x4 b = *reinterpret_cast<const f16x4 *>(M + S::at(r, kb + 16 + 4 * g));
+        return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        return M[S::at(r, kb + 16 * (q >> 2) + 4 * g + (q & 3))];
+    }
+}
+
+// k-major fragment (as frag_kmajor: rows = contraction index) of a swizzled
+// matrix, through the transposing LDS read for fp16.
+template <typename OP, int NCOL>
+__device__ __forceinline__ typename Mfma<OP>::frag swz_kmajor(const OP *M, int kb, int q, int c0,
+                                                              int lane) {
+    typedef Swz<OP, NCOL> S;
+    const int g = lane >> 4, j = lane & 15;
+    if constexpr (sizeof(OP) == 2) {
+        const f16 *pa = M + S::at(kb + 4 * g + (j >> 2), c0 + 4 * (j & 3));
+        const f16 *pb = M + S::at(kb + 16 + 4 * g + (j >> 2), c0 + 4 * (j & 3));
+        const f16x4 a = __builtin_bit_cast(
+            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pa));
+        const f16x4 b = __builtin_bit_cast(
+            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pb));
+        return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+        return M[S::at(kb + 16 * (q >> 2) + 4 * g + (q & 3), c0 + j)];
+    }
+}
+
+// A row piece of 8 elements stored into a swizzled matrix.
+template <typename T, int NCOL, typename V>
+__device__ __forceinline__ void swz_store8(T *M, int r, int c0, const V &v) {
+    typedef Swz<T, NCOL> S;
+    static_assert(sizeof(V) == 8 * sizeof(T), "row piece of 8 elements");
+    constexpr int NV = sizeof(V) / 16;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(&v);
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+        *reinterpret_cast<u32x4 *>(M + S::at(r, c0 + i * S::EPC)) = src[i];
+}
+
 // ---------------------------------------------------------- row pieces ----
 // 8 consecutive elements of one row, moved with vector loads and stores.
 template <typename T> struct alignas(16) Row8v { T e[8]; };
@@ -253,7 +331,6 @@ __device__ __forceinline__ Row8v<float> wx_piece(const Row8v<float> &v, float w)
 // a chunk or of the sequence need no masks.  Offsets are 32-bit; every
 // resource here spans at most a few rows of one tensor.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (CDNA)
 
 __device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {

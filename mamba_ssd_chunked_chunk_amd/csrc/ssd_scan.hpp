@@ -234,15 +234,16 @@ __device__ __forceinline__ void sp_apply(f32x4 *acc, float &logdec,
     for (int jb = 0; jb < S::SLAB; ++jb) {
         if (jb < sp.nb) {
             if (sp.bi0 + jb == 0) {  // first block of a chunk: emit the boundary state
+                // transposed layout [head_dim][state_dim]: the 4 accumulator
+                // values of a lane (consecutive n) are one 16-byte store
                 float *dst = Hb_bh + sp.c * NPh;
 #pragma unroll
                 for (int i = 0; i < S::TPW; ++i) {
                     const int ti = wave + kWaves * i;
                     if (ti < S::TILES) {
                         const int tr = ti / S::CT, tc = ti % S::CT;
-                        float *d0 = dst + (tr * 16 + 4 * (lane >> 4)) * P + tc * 16 + (lane & 15);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) d0[r * P] = acc[i][r];
+                        *reinterpret_cast<f32x4 *>(dst + (tc * 16 + (lane & 15)) * N + tr * 16 +
+                                                   4 * (lane >> 4)) = acc[i];
                     }
                 }
                 if (nsegs > 1 && tid == 0) Dlog_bh[sp.c] = logdec;
@@ -358,20 +359,30 @@ __global__ __launch_bounds__(256) void k_state_pass(
         }
     }
 
-    float *out = nullptr;
-    if (nseg == 1)
-        out = final_state ? final_state + (b * h + hh) * NP : nullptr;
-    else
-        out = Eseg + ((b * nseg + seg) * h + hh) * NP;
-    if (out) {
+    if (nseg == 1) {  // the final state, [state_dim][head_dim]
+        if (final_state) {
+            float *out = final_state + (b * h + hh) * NP;
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int ti = wave + kWaves * i;
+                if (ti < TILES) {
+                    const int tr = ti / CT, tc = ti % CT;
+                    float *d0 = out + (int64_t)(tr * 16 + 4 * (lane >> 4)) * P + tc * 16 +
+                                (lane & 15);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) d0[r * P] = acc[i][r];
+                }
+            }
+        }
+    } else {  // the segment's state from its start, transposed like Hb
+        float *out = Eseg + ((b * nseg + seg) * h + hh) * NP;
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int ti = wave + kWaves * i;
             if (ti < TILES) {
                 const int tr = ti / CT, tc = ti % CT;
-                float *d0 = out + (int64_t)(tr * 16 + 4 * (lane >> 4)) * P + tc * 16 + (lane & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) d0[r * P] = acc[i][r];
+                *reinterpret_cast<f32x4 *>(out + (tc * 16 + (lane & 15)) * N + tr * 16 +
+                                           4 * (lane >> 4)) = acc[i];
             }
         }
     }
@@ -384,14 +395,17 @@ __global__ __launch_bounds__(256) void k_state_pass(
 //    with E_k the state segment k reaches from zero (segment 0: from the
 //    initial state) and L_k its total log2 decay.  Hin_k overwrites slot
 //    k - 1 of Eseg; the state after the last segment is the final state.
+//    Segment states are stored transposed ([head_dim][state_dim]); the final
+//    state is written in the [state_dim][head_dim] layout of the interface.
 //    One thread per 4 consecutive state elements of one (batch, head); the
 //    segment states are loaded in groups of 8 before any of them is used.
 static __global__ __launch_bounds__(256) void k_seg_combine(float *__restrict__ Eseg,
                                                             const float *__restrict__ Lseg,
                                                             float *__restrict__ final_state,
                                                             int64_t bh, int h, int64_t nseg,
-                                                            int64_t np4) {
+                                                            int n, int p) {
     constexpr int G8 = 8;
+    const int64_t np4 = (int64_t)n * p / 4;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= bh * np4) return;
     const int64_t pair = idx / np4, e4 = idx % np4;
@@ -416,367 +430,465 @@ static __global__ __launch_bounds__(256) void k_seg_combine(float *__restrict__ 
             }
         }
     }
-    if (final_state) reinterpret_cast<f32x4 *>(final_state)[pair * np4 + e4] = H;
+    if (final_state) {
+        // element e of this thread: head_dim column pc, state row n0 + e
+        const int64_t pc = (e4 * 4) / n, n0 = (e4 * 4) % n;
+        float *dst = final_state + pair * (int64_t)n * p + n0 * p + pc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e * p] = H[e];
+    }
 }
 
 // ----------------------------------------------------------------------------
-// Staging of the chunk output: one block of kT rows.  Pieces are 8
-// consecutive elements of one row of C and of B (same row and columns, N / 8
-// per row) or of x (P / 8 per row), loaded through buffer resources that end
-// at the chunk's last valid row (zeros beyond).
-template <typename IO, int P, int N, int NT> struct CoBuf {
+// 4. Chunk output.  One workgroup per (batch, chunk, HPW consecutive heads of
+//    one group); WPH = max(1, head_dim / 32) waves per head, each owning 32
+//    (or head_dim, if smaller) head_dim columns.  C and B of a block are
+//    staged once for all the workgroup's heads (they share the group), x per
+//    head.  A wave keeps its columns of the running state H (all state_dim
+//    rows) in MFMA accumulators across the chunk's blocks.  Per block:
+//      G^T = B C^T on the 3 causal 16 x 16 tiles, and
+//      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i), in registers;
+//      y^T = 2^lcs_i (H^T C^T) + x^T P^T + D x^T, stored straight from the
+//            accumulators (4 consecutive columns per lane);
+//      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
+//    The scores and the state read-out take the same C fragments (one LDS
+//    read for both).  The decay factor of P is taken as a_i b_j with
+//    a_i = 2^(lcs_i - lcs_15) and b_j = 2^(lcs_15 - lcs_j) d_j, both per
+//    row, when the block's total log2 decay is above -kSplitLimit (every
+//    factor then stays inside fp32's normal range); otherwise as one
+//    exponential per element.
+constexpr float kSplitLimit = 60.f;
+
+template <typename IO, int P, int N, int HPW> struct Co {
     typedef typename Op<IO>::type OP;
-    static constexpr int NPC = kT * N / 8, NPX = kT * P / 8;
-    static constexpr int KC = (NPC + NT - 1) / NT;
-    static constexpr int KX = (NPX + NT - 1) / NT;
-    Row8v<OP> cv[KC], bv[KC];
-    Row8v<IO> xv[KX];
-    float xw[KX];  // weight of the x piece's row
-    float ls, ds;  // lcs and d of row tid (tid < kT)
-    float l15;     // lcs of the block's row 15
+    typedef Mfma<OP> M;
+    static constexpr int T = kT;
+    static constexpr int WPH = P >= 64 ? P / 32 : 1;  // waves per head
+    static constexpr int PW = P / WPH;                // head_dim columns per wave
+    static constexpr int CPW = PW / 16;               // column tiles per wave
+    static constexpr int W = HPW * WPH, NT = 64 * W;  // waves, threads
+    static constexpr int RT = N / 16;                 // state row tiles
+    static constexpr int NB = N / 32;                 // 32-blocks of the state index
+    static constexpr int KS = T / M::K;               // MFMA steps per 32-block
+    static constexpr int LDX = P + 16;                // [row][p]: x
+    static constexpr int XS = T * LDX;                // one head's staged x
+    static constexpr int BUF = 2 * T * N + HPW * XS;  // [C | B | x of each head]
+    // staging pieces (8 elements) per thread
+    static constexpr int NPC = T * N / 8, NPX = HPW * T * P / 8;
+    static constexpr int KC = (NPC + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
 };
 
-template <typename IO, int P, int N, int NT>
-__device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, NT> &f, int s, const IO *xb,
-                                            const typename Op<IO>::type *Bb,
-                                            const typename Op<IO>::type *Cb, Rsrc rl, Rsrc rd,
-                                            Rsrc rw, const float *lcs_c, int64_t rows,
-                                            int64_t xs, int64_t bs, int tid) {
-    typedef CoBuf<IO, P, N, NT> F;
-    typedef typename Op<IO>::type OP;
-    constexpr int T = kT;
-    const int64_t r0 = (int64_t)s * T;  // first row of the block inside the chunk
-    const int64_t valid = rows - r0;
-    const Rsrc rb = make_rsrc(Bb + r0 * bs, valid * bs * (int64_t)sizeof(OP));
-    const Rsrc rc = make_rsrc(Cb + r0 * bs, valid * bs * (int64_t)sizeof(OP));
-    const Rsrc rx = make_rsrc(xb + r0 * xs, valid * xs * (int64_t)sizeof(IO));
-    const uint32_t soff = (uint32_t)r0 * 4u;
-#pragma unroll
-    for (int k = 0; k < F::KC; ++k) {
-        const int q = tid + k * NT;
-        if (F::NPC % NT == 0 || q < F::NPC) {
-            const int j = q / (N / 8), cc = q % (N / 8);
-            const uint32_t off = (uint32_t)(j * bs + cc * 8) * (uint32_t)sizeof(OP);
-            f.cv[k] = buf_row8<OP>(rc, off);
-            f.bv[k] = buf_row8<OP>(rb, off);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < F::KX; ++k) {
-        const int q = tid + k * NT;
-        if (F::NPX % NT == 0 || q < F::NPX) {
-            const int j = q / (P / 8), cc = q % (P / 8);
-            f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * xs + cc * 8) * (uint32_t)sizeof(IO));
-            f.xw[k] = buf_f32(rw, (uint32_t)j * 4u, soff);
-        }
-    }
-    const uint32_t rt = (uint32_t)(tid < T ? tid : 0) * 4u;
-    f.ls = buf_f32(rl, rt, soff);
-    f.ds = buf_f32(rd, rt, soff);
-    f.l15 = lcs_c[r0 + 15];
-}
+// Heads per workgroup used for head_dim P when the group size allows it.
+template <int P> constexpr int kCoHeads = P >= 64 ? 128 / P : 4;
 
-// Per-row factors of a staged block (LDS), T floats each.
+// Per-row factors of one head's staged block (LDS), T floats each.
 struct alignas(16) CoRows {
     float lcs[kT];   // cumulative log2 decay inside the block
     float d[kT];     // time step
     float a[kT];     // 2^(lcs_i - lcs_15)
     float bw[kT];    // 2^(lcs_15 - lcs_j) d_j
+    float w[kT];     // 2^(lcs_31 - lcs_j) d_j: weight in the state at the block's end
 };
 
-template <typename IO, int P, int N, int NT>
-__device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, NT> &f, typename Op<IO>::type *Cs,
-                                         typename Op<IO>::type *Bs, typename Op<IO>::type *Xs,
-                                         typename Op<IO>::type *Xw, CoRows &rows, int tid) {
-    typedef CoBuf<IO, P, N, NT> F;
+// Register prefetch of one block for the whole workgroup.  Loads go through
+// buffer resources that end at the chunk's last valid row (zeros beyond).
+template <typename IO, int P, int N, int HPW> struct CoBuf {
+    typedef Co<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    Row8v<OP> cv[K::KC], bv[K::KC];
+    Row8v<IO> xv[K::KX];
+    float ls, ds, ws, l15;  // row factors of (head tid / kT, row tid % kT)
+};
+
+// Per-workgroup addressing.
+template <typename IO> struct CoPtrs {
     typedef typename Op<IO>::type OP;
-    constexpr int LDN = N + Mfma<OP>::PAD, LDX = P + 16;
+    const IO *x;        // row 0 of the chunk, first head of the workgroup
+    const OP *B, *C;    // row 0 of the chunk, the group
+    IO *y;
+    Rsrc rl, rd, rw;    // lcs, d, weights: the workgroup's heads, this chunk
+    int64_t xs, bs;     // row strides (elements) of x / y and of B / C
+    uint32_t hstride;   // bytes from one head's row arrays to the next
+    int rows;           // valid rows of the chunk
+};
+
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, const CoPtrs<IO> &cp,
+                                            int tid) {
+    typedef Co<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    constexpr int T = kT;
+    const int r0 = s * T;
+    int valid = cp.rows - r0;
+    valid = valid < 0 ? 0 : (valid > T ? T : valid);
+    const int rr0 = valid > 0 ? r0 : 0;
+    const Rsrc rb = make_rsrc(cp.B + rr0 * cp.bs, (int64_t)valid * cp.bs * (int)sizeof(OP));
+    const Rsrc rc = make_rsrc(cp.C + rr0 * cp.bs, (int64_t)valid * cp.bs * (int)sizeof(OP));
+    const Rsrc rx = make_rsrc(cp.x + rr0 * cp.xs, (int64_t)valid * cp.xs * (int)sizeof(IO));
 #pragma unroll
-    for (int k = 0; k < F::KC; ++k) {
-        const int q = tid + k * NT;
-        if (F::NPC % NT == 0 || q < F::NPC) {
-            const int o = (q / (N / 8)) * LDN + (q % (N / 8)) * 8;
-            st_row8(Cs + o, f.cv[k]);
-            st_row8(Bs + o, f.bv[k]);
+    for (int k = 0; k < K::KC; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPC % K::NT == 0 || q < K::NPC) {
+            const int j = q / (N / 8), cc = q % (N / 8);
+            const uint32_t off = (uint32_t)(j * cp.bs + cc * 8) * (uint32_t)sizeof(OP);
+            f.cv[k] = buf_row8<OP>(rc, off);
+            f.bv[k] = buf_row8<OP>(rb, off);
         }
     }
 #pragma unroll
-    for (int k = 0; k < F::KX; ++k) {
-        const int q = tid + k * NT;
-        if (F::NPX % NT == 0 || q < F::NPX) {
-            const int o = (q / (P / 8)) * LDX + (q % (P / 8)) * 8;
-            Row8v<OP> xo, wo;
-            x_pieces(f.xv[k], f.xw[k], xo, wo);
-            st_row8(Xs + o, xo);
-            st_row8(Xw + o, wo);
+    for (int k = 0; k < K::KX; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPX % K::NT == 0 || q < K::NPX) {
+            const int hs = q / (T * P / 8), qq = q % (T * P / 8);
+            const int j = qq / (P / 8), cc = qq % (P / 8);
+            f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * cp.xs + hs * P + cc * 8) *
+                                           (uint32_t)sizeof(IO));
         }
     }
-    if (tid < kT) {
-        rows.lcs[tid] = f.ls;
-        rows.d[tid] = f.ds;
-        rows.a[tid] = exp2_fast(f.ls - f.l15);
-        rows.bw[tid] = exp2_fast(f.l15 - f.ls) * f.ds;
+    const int hs = tid < HPW * T ? tid / T : 0, row = tid % T;
+    const uint32_t soff = (uint32_t)r0 * 4u;
+    const uint32_t ro = (uint32_t)hs * cp.hstride + (uint32_t)row * 4u;
+    f.ls = buf_f32(cp.rl, ro, soff);
+    f.ds = buf_f32(cp.rd, ro, soff);
+    f.ws = buf_f32(cp.rw, ro, soff);
+    f.l15 = buf_f32(cp.rl, (uint32_t)hs * cp.hstride + 15u * 4u, soff);
+}
+
+// x piece -> operand piece (bf16 -> fp16 exact in fp16's normal range).
+__device__ __forceinline__ Row8v<f16> op_piece(const Row8v<bf16> &v) {
+    Row8v<f16> o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) pack2((float)v.e[e], (float)v.e[e + 1], o.e[e], o.e[e + 1]);
+    return o;
+}
+__device__ __forceinline__ Row8v<float> op_piece(const Row8v<float> &v) { return v; }
+
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
+                                         typename Op<IO>::type *buf, CoRows *rows, int tid) {
+    typedef Co<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    constexpr int T = kT;
+    OP *Cs = buf, *Bs = buf + T * N, *Xs = buf + 2 * T * N;
+#pragma unroll
+    for (int k = 0; k < K::KC; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPC % K::NT == 0 || q < K::NPC) {
+            const int r = q / (N / 8), c0 = (q % (N / 8)) * 8;
+            swz_store8<OP, N>(Cs, r, c0, f.cv[k]);
+            swz_store8<OP, N>(Bs, r, c0, f.bv[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K::KX; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPX % K::NT == 0 || q < K::NPX) {
+            const int hs = q / (T * P / 8), qq = q % (T * P / 8);
+            st_row8(Xs + hs * K::XS + (qq / (P / 8)) * K::LDX + (qq % (P / 8)) * 8,
+                    op_piece(f.xv[k]));
+        }
+    }
+    if (tid < HPW * T) {
+        CoRows &rw = rows[tid / T];
+        const int r = tid % T;
+        rw.lcs[r] = f.ls;
+        rw.d[r] = f.ds;
+        rw.a[r] = exp2_fast(f.ls - f.l15);
+        rw.bw[r] = exp2_fast(f.l15 - f.ls) * f.ds;
+        rw.w[r] = f.ws;
     }
 }
 
-// ----------------------------------------------------------------------------
-// 4. Chunk output.  One workgroup per (batch, chunk, head), W = min(4,
-//    head_dim / 16) waves.  Wave w owns the head_dim column tiles
-//    pt = w, w + W, ... of everything it produces: its columns of the running
-//    state H (all state_dim rows) stay in MFMA accumulators across the
-//    chunk's blocks and feed the output product straight from registers, and
-//    it computes y^T for those columns.  Per block, with C, B, x and w x
-//    double-buffered in LDS and the block after next already being fetched:
-//      G^T = B C^T on the 3 causal 16 x 16 tiles, and
-//      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i), in registers;
-//      y^T = 2^lcs_i (H^T C^T) + x^T P^T + D x^T, staged in LDS and written
-//            out as whole rows after the block's barrier;
-//      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
-//    The decay factor of P is taken as a_i b_j with a_i = 2^(lcs_i - lcs_15)
-//    and b_j = 2^(lcs_15 - lcs_j) d_j, both per row, when the block's total
-//    log2 decay is above -kSplitLimit (every factor then stays inside fp32's
-//    normal range); otherwise as one exponential per element.
-constexpr float kSplitLimit = 60.f;
+// Decay-weighted x, w_j x_j, as the k-major B operand of the state carry:
+// the x fragment scaled row by row (rows 4g + r and 16 + 4g + r of lane
+// group g; fp32: row 16 (q >> 2) + 4g + (q & 3)).
+__device__ __forceinline__ f16x8 xw_frag(const f16x8 &xf, int q, int lane, const float *w) {
+    const int g = lane >> 4;
+    const f32x4 wa = *reinterpret_cast<const f32x4 *>(w + 4 * g);
+    const f32x4 wb = *reinterpret_cast<const f32x4 *>(w + 16 + 4 * g);
+    const f16x2 o0 = pk2((float)xf[0] * wa[0], (float)xf[1] * wa[1]);
+    const f16x2 o1 = pk2((float)xf[2] * wa[2], (float)xf[3] * wa[3]);
+    const f16x2 o2 = pk2((float)xf[4] * wb[0], (float)xf[5] * wb[1]);
+    const f16x2 o3 = pk2((float)xf[6] * wb[2], (float)xf[7] * wb[3]);
+    return f16x8{o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
+}
+__device__ __forceinline__ float xw_frag(float xf, int q, int lane, const float *w) {
+    return xf * w[16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)];
+}
 
-template <int P> struct CoShape {
-    static constexpr int W = P >= 64 ? 4 : P / 16;  // waves
-    static constexpr int NT = 64 * W;               // threads
-};
+// head_dim column of row rho (0..15) of the wave's column tile u.  Tiles are
+// taken in pairs that interleave in groups of 4 columns (tile 2v holds
+// columns 32v + 8m + e, tile 2v + 1 holds 32v + 8m + 4 + e, m, e < 4), so that
+// a lane's output rows of the two tiles are 8 consecutive columns.
+template <int CPW> __device__ __forceinline__ int co_col(int u, int rho) {
+    if constexpr (CPW % 2 == 0)
+        return 32 * (u >> 1) + 8 * (rho >> 2) + 4 * (u & 1) + (rho & 3);
+    else
+        return 16 * u + rho;
+}
 
-template <typename IO, int P, int N>
-__global__ __launch_bounds__(CoShape<P>::NT) void k_chunk_out(
+// k-major x fragment of column tile u (rows = block rows, columns co_col).
+template <int CPW>
+__device__ __forceinline__ f16x8 xs_frag(const f16 *Xs, int ldx, int q, int c0, int u, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int col = c0 + co_col<CPW>(u, 4 * (j & 3));
+    const f16 *pa = Xs + (4 * g + (j >> 2)) * ldx + col;
+    const f16 *pb = Xs + (16 + 4 * g + (j >> 2)) * ldx + col;
+    const f16x4 a = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pa));
+    const f16x4 b = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pb));
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <int CPW>
+__device__ __forceinline__ float xs_frag(const float *Xs, int ldx, int q, int c0, int u, int lane) {
+    return Xs[(16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)) * ldx + c0 + co_col<CPW>(u, lane & 15)];
+}
+
+// One block of the chunk output for one wave: head slot hs, columns
+// c0 .. c0 + PW - 1 of that head.  accH: the wave's CPW x RT state tiles
+// (inlined: stays in registers).
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::type *buf,
+                                           const CoRows &rf, bool carry, float Dh,
+                                           const CoPtrs<IO> &cp, int r0, int hs, int c0,
+                                           int lane) {
+    typedef Co<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    typedef typename K::M M;
+    constexpr int T = kT, KS = K::KS, NB = K::NB, LDX = K::LDX, CPW = K::CPW, RT = K::RT;
+    const int lg = lane >> 4, li = lane & 15;
+    const OP *Cs = buf;
+    const OP *Bs = buf + T * N;
+    const OP *Xs = buf + 2 * T * N + hs * K::XS;
+
+    // ---- G^T tiles and the state read-out, sharing the C fragments.
+    //      gt[k]: tiles (it, jt) = (0,0), (1,0), (1,1); element r of lane l:
+    //      j = 16 jt + 4 lg + r, i = 16 it + li.  yh[it][u]: H^T C^T for
+    //      rows 16 it.. and columns c0 + 16 u..
+    f32x4 gt[3], yh[2][CPW];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) gt[k] = zero4();
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) yh[it][u] = zero4();
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+            const auto c0f = swz_rows_kconv<OP, N>(Cs, 0, 32 * m, q, lane);
+            const auto c1f = swz_rows_kconv<OP, N>(Cs, 16, 32 * m, q, lane);
+            const auto b0f = swz_rows_kconv<OP, N>(Bs, 0, 32 * m, q, lane);
+            const auto b1f = swz_rows_kconv<OP, N>(Bs, 16, 32 * m, q, lane);
+            gt[0] = M::mma(b0f, c0f, gt[0]);
+            gt[1] = M::mma(b0f, c1f, gt[1]);
+            gt[2] = M::mma(b1f, c1f, gt[2]);
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) {
+                const auto hf = frag_from_acc<OP>(accH[u * RT + 2 * m], accH[u * RT + 2 * m + 1], q);
+                yh[0][u] = M::mma(hf, c0f, yh[0][u]);
+                yh[1][u] = M::mma(hf, c1f, yh[1][u]);
+            }
+        }
+    }
+
+    // ---- masked, decayed scores pv[it][jt] (registers)
+    const float lam = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rf.lcs[T - 1])));
+    f32x4 pv[2][2];
+    float colscale[2];
+    pv[0][1] = zero4();
+    if (lam > -kSplitLimit) {
+        const float s15 = exp2_fast(rf.lcs[15]);
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&rf.bw[4 * lg]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&rf.bw[16 + 4 * lg]);
+        const float a0 = rf.a[li], a1 = rf.a[16 + li];
+        colscale[0] = a0 * s15;
+        colscale[1] = a1 * s15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j0 = 4 * lg + r;
+            pv[0][0][r] = (j0 <= li) ? gt[0][r] * (a0 * b0[r]) : 0.f;
+            pv[1][0][r] = gt[1][r] * (a1 * b0[r]);
+            pv[1][1][r] = (j0 <= li) ? gt[2][r] * (a1 * b1[r]) : 0.f;
+        }
+    } else {
+        const float l0 = rf.lcs[li], l1 = rf.lcs[16 + li];
+        colscale[0] = exp2_fast(l0);
+        colscale[1] = exp2_fast(l1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j0 = 4 * lg + r;
+            pv[0][0][r] = (j0 <= li) ? gt[0][r] * exp2_fast(l0 - rf.lcs[j0]) * rf.d[j0] : 0.f;
+            pv[1][0][r] = gt[1][r] * exp2_fast(l1 - rf.lcs[j0]) * rf.d[j0];
+            pv[1][1][r] =
+                (j0 <= li) ? gt[2][r] * exp2_fast(l1 - rf.lcs[16 + j0]) * rf.d[16 + j0] : 0.f;
+        }
+    }
+
+    // ---- y^T = colscale (H^T C^T) + x^T P^T + D x^T, straight to y:
+    //      element r of lane l is (p = c0 + co_col(u, 4 lg + r), i = 16 it + li)
+    int valid = cp.rows - r0;
+    valid = valid < 0 ? 0 : (valid > T ? T : valid);
+    const Rsrc ry = make_rsrc(cp.y + (valid > 0 ? r0 : 0) * cp.xs,
+                              (int64_t)valid * cp.xs * (int)sizeof(IO));
+    typename Mfma<OP>::frag xf[CPW][KS];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u)
+#pragma unroll
+        for (int q = 0; q < KS; ++q) xf[u][q] = xs_frag<CPW>(Xs, LDX, q, c0, u, lane);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int i = it * 16 + li;
+        f32x4 yv[CPW];
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+            f32x4 yp = zero4();
+#pragma unroll
+            for (int q = 0; q < KS; ++q)
+                yp = M::mma(xf[u][q], frag_from_acc<OP>(pv[it][0], pv[it][1], q), yp);
+            const f32x4 xv = lds_load4(Xs + i * LDX + c0 + co_col<CPW>(u, 4 * lg));
+            yv[u] = colscale[it] * yh[it][u] + yp + Dh * xv;
+        }
+        if constexpr (CPW % 2 == 0) {
+            // tiles 2v, 2v + 1: 8 consecutive columns c0 + 32 v + 8 lg ..
+#pragma unroll
+            for (int v = 0; v < CPW / 2; ++v) {
+                const f32x4 lo = yv[2 * v], hi = yv[2 * v + 1];
+                const uint32_t off = (uint32_t)(i * cp.xs + hs * P + c0 + 32 * v + 8 * lg) *
+                                     (uint32_t)sizeof(IO);
+                if constexpr (sizeof(IO) == 2) {
+                    const bf16x4 a{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3]};
+                    const bf16x4 bq{(bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+                    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, bq);
+                    buf_store16(ry, off, u32x4{ua[0], ua[1], ub[0], ub[1]});
+                } else {
+                    buf_store16(ry, off, __builtin_bit_cast(u32x4, lo));
+                    buf_store16(ry, off + 16u, __builtin_bit_cast(u32x4, hi));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) {
+                const uint32_t off = (uint32_t)(i * cp.xs + hs * P + c0 + co_col<CPW>(u, 4 * lg)) *
+                                     (uint32_t)sizeof(IO);
+                if constexpr (sizeof(IO) == 2) {
+                    const bf16x4 o{(bf16)yv[u][0], (bf16)yv[u][1], (bf16)yv[u][2], (bf16)yv[u][3]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), ry, off, 0,
+                                                          0);
+                } else {
+                    buf_store16(ry, off, __builtin_bit_cast(u32x4, yv[u]));
+                }
+            }
+        }
+    }
+
+    // ---- carry the state to the next block of the chunk
+    if (carry) {
+        const float decay = exp2_fast(lam);
+        typename Mfma<OP>::frag xw[CPW][KS];
+#pragma unroll
+        for (int u = 0; u < CPW; ++u)
+#pragma unroll
+            for (int q = 0; q < KS; ++q) xw[u][q] = xw_frag(xf[u][q], q, lane, rf.w);
+#pragma unroll
+        for (int k = 0; k < CPW * RT; ++k) accH[k] *= decay;
+#pragma unroll
+        for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+            for (int q = 0; q < KS; ++q) {
+                const auto bt = swz_kmajor<OP, N>(Bs, 0, q, tr * 16, lane);
+#pragma unroll
+                for (int u = 0; u < CPW; ++u)
+                    accH[u * RT + tr] = M::mma(bt, xw[u][q], accH[u * RT + tr]);
+            }
+    }
+}
+
+template <typename IO, int P, int N, int HPW>
+__global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     const IO *__restrict__ x, const typename Op<IO>::type *__restrict__ Bm,
     const typename Op<IO>::type *__restrict__ Cm, const float *__restrict__ D,
     const float *__restrict__ lcs, const float *__restrict__ dtp, const float *__restrict__ wgt,
     const float *__restrict__ Hb, const float *__restrict__ Hin, const float *__restrict__ Dlog,
     IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp, int64_t cps,
     int64_t nseg) {
-    typedef typename Op<IO>::type OP;
-    typedef Mfma<OP> M;
-    constexpr int W = CoShape<P>::W, NT = CoShape<P>::NT;
-    constexpr int T = kT;
-    constexpr int KS = T / M::K;          // MFMA steps over 32 contraction indices
-    constexpr int NS = N / M::K;          // MFMA steps over the state index
-    constexpr int NB = N / 32;            // 32-blocks of the state index
-    constexpr int LDN = N + M::PAD;       // [row][n]: C, B
-    constexpr int LDX = P + 16;           // [row][p]: x, w x
-    constexpr int LDY = P + 16 / (int)sizeof(IO);  // [row][p]: y staging
-    constexpr int CT = P / 16;            // head_dim column tiles
-    constexpr int CPW = CT / W;           // column tiles per wave
-    constexpr int RT = N / 16;            // state row tiles
-    constexpr int BUF = 2 * T * LDN + 2 * T * LDX;
-    constexpr int YV = 16 / (int)sizeof(IO);     // y elements per 16-byte store
-    constexpr int YTPR = P / YV;                 // threads per y row
-    constexpr int YRPP = NT / YTPR;              // y rows per store pass
-    // 2-byte y is staged in LDS and written as whole rows; 4-byte y goes out
-    // straight from the tiles (16 consecutive columns = 64 bytes per row)
-    constexpr bool kStageY = sizeof(IO) == 2;
-    __shared__ __attribute__((aligned(16))) OP lds[2 * BUF];  // [C | B | x | w x] x 2
-    __shared__ __attribute__((aligned(16))) IO Ys[2][kStageY ? T * LDY : 1];
-    __shared__ CoRows rowsf[2];
+    typedef Co<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
+    __shared__ __attribute__((aligned(16))) OP lds[2 * BUF];
+    __shared__ CoRows rowsf[2][HPW];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lg = lane >> 4, li = lane & 15;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
-    const int hh = (int)(item % h); item /= h;
+    const int hq = (int)(item % (h / HPW)); item /= (h / HPW);
     const int64_t c = item % nc;
     const int64_t b = item / nc;
-    const int gi = hh / (h / g);
+    const int hh0 = hq * HPW;                // first head of the workgroup
+    const int gi = hh0 / (h / g);
+    const int hs = wave / WPH;               // this wave's head slot
+    const int hh = hh0 + hs;
+    const int c0 = (wave % WPH) * K::PW;     // this wave's first column
     const int64_t seg = c / cps;
     const int64_t NP = (int64_t)N * P;
-    const int64_t rbase = ((b * h + hh) * nc + c) * Qp;
-    const float *lcs_c = lcs + rbase;
-    const Rsrc rl = make_rsrc(lcs_c, Qp * 4), rd = make_rsrc(dtp + rbase, Qp * 4);
-    const Rsrc rw = make_rsrc(wgt + rbase, Qp * 4);
+    const int64_t t0 = c * Q;
+    CoPtrs<IO> cp;
+    cp.xs = (int64_t)h * P;
+    cp.bs = (int64_t)g * N;
+    cp.x = x + ((b * l + t0) * h + hh0) * P;
+    cp.y = y + ((b * l + t0) * h + hh0) * P;
+    cp.B = Bm + ((b * l + t0) * g + gi) * N;
+    cp.C = Cm + ((b * l + t0) * g + gi) * N;
+    const int64_t rbase = ((b * h + hh0) * nc + c) * Qp;
+    const int64_t rspan = ((int64_t)(HPW - 1) * nc * Qp + Qp) * 4;
+    cp.rl = make_rsrc(lcs + rbase, rspan);
+    cp.rd = make_rsrc(dtp + rbase, rspan);
+    cp.rw = make_rsrc(wgt + rbase, rspan);
+    cp.hstride = (uint32_t)(nc * Qp * 4);
+    cp.rows = (int)((Q < l - t0) ? Q : (l - t0));
+    const int nblk = (cp.rows + T - 1) / T;
     const float Dh = D ? D[hh] : 0.f;
-    const int64_t rows = (Q < l - c * Q) ? Q : (l - c * Q);  // valid rows of this chunk
-    const int nblk = (int)((rows + T - 1) / T);
-    const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N, t0 = c * Q;
-    const IO *xb = x + ((b * l + t0) * h + hh) * P;   // chunk row r at xb + r * xs
-    const OP *Bb = Bm + ((b * l + t0) * g + gi) * N;   // chunk row r at Bb + r * bs
-    const OP *Cb = Cm + ((b * l + t0) * g + gi) * N;
-    IO *yb = y + ((b * l + t0) * h + hh) * P;
 
-    CoBuf<IO, P, N, NT> pf;
-    co_prefetch(pf, 0, xb, Bb, Cb, rl, rd, rw, lcs_c, rows, xs, bs, tid);
-
-    // ---- the wave's state columns entering the chunk (all loads issued first)
-    f32x4 accH[CPW][RT];
+    // ---- the wave's state columns entering the chunk: the boundary state,
+    //      plus (later segments) the decayed state entering the segment.
+    //      Both are stored transposed ([head_dim][state_dim]), so a lane's 4
+    //      accumulator values (consecutive state rows) are one 16-byte load
+    f32x4 accH[CPW * RT];
     {
-        const float *hb = Hb + ((b * nc + c) * h + hh) * NP;
+        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * 4);
+        const Rsrc ri = make_rsrc(Hin + (seg > 0 ? ((b * nseg + seg - 1) * h + hh) * NP : 0),
+                                  seg > 0 ? NP * 4 : 0);
+        f32x4 iv[CPW * RT];
 #pragma unroll
         for (int u = 0; u < CPW; ++u)
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) {
-                const int off = (tr * 16 + 4 * lg) * P + (wave + W * u) * 16 + li;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) accH[u][tr][r] = hb[off + r * P];
+                const uint32_t off =
+                    (uint32_t)((c0 + co_col<CPW>(u, li)) * N + tr * 16 + 4 * lg) * 4u;
+                accH[u * RT + tr] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+                iv[u * RT + tr] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off, 0, 0));
             }
-        if (seg > 0) {
-            const float *hin = Hin + ((b * nseg + seg - 1) * h + hh) * NP;
-            f32x4 iv[CPW][RT];
+        const float corr = seg > 0 ? exp2_fast(Dlog[(b * h + hh) * nc + c]) : 0.f;
 #pragma unroll
-            for (int u = 0; u < CPW; ++u)
-#pragma unroll
-                for (int tr = 0; tr < RT; ++tr) {
-                    const int off = (tr * 16 + 4 * lg) * P + (wave + W * u) * 16 + li;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) iv[u][tr][r] = hin[off + r * P];
-                }
-            const float corr = exp2_fast(Dlog[(b * h + hh) * nc + c]);
-#pragma unroll
-            for (int u = 0; u < CPW; ++u)
-#pragma unroll
-                for (int tr = 0; tr < RT; ++tr) accH[u][tr] += corr * iv[u][tr];
-        }
+        for (int k = 0; k < CPW * RT; ++k) accH[k] += corr * iv[k];
     }
 
-    co_stage(pf, lds, lds + T * LDN, lds + 2 * T * LDN, lds + 2 * T * LDN + T * LDX, rowsf[0],
-             tid);
-    if (nblk > 1) co_prefetch(pf, 1, xb, Bb, Cb, rl, rd, rw, lcs_c, rows, xs, bs, tid);
+    // block s is staged in LDS buffer s & 1 while the previous one is
+    // computed; its loads were issued one block earlier
+    CoBuf<IO, P, N, HPW> pf;
+    co_prefetch(pf, 0, cp, tid);
+    co_stage(pf, lds, rowsf[0], tid);
+    co_prefetch(pf, 1, cp, tid);
     lds_barrier();
-
     for (int s = 0; s < nblk; ++s) {
         const int cur = s & 1;
-        const OP *Cs = lds + cur * BUF;
-        const OP *Bs = Cs + T * LDN;
-        const OP *Xs = Bs + T * LDN;
-        const OP *Xw = Xs + T * LDX;
-        const CoRows &rf = rowsf[cur];
-        IO *Yc = Ys[cur];
-        if (s + 1 < nblk) {  // stage the next block into the other buffer
-            OP *nC = lds + (cur ^ 1) * BUF;
-            co_stage(pf, nC, nC + T * LDN, nC + 2 * T * LDN, nC + 2 * T * LDN + T * LDX,
-                     rowsf[cur ^ 1], tid);
-            if (s + 2 < nblk)
-                co_prefetch(pf, s + 2, xb, Bb, Cb, rl, rd, rw, lcs_c, rows, xs, bs, tid);
-        }
-
-        // ---- masked, decayed scores: G^T tiles (jt, it), jt <= it.
-        //      pv[it][jt] element r: j = 16 jt + 4 lg + r, i = 16 it + li
-        const float lam = __builtin_bit_cast(
-            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rf.lcs[T - 1])));
-        const bool split = lam > -kSplitLimit;
-        f32x4 gt[3];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int it = k == 0 ? 0 : 1, jt = k == 2 ? 1 : 0;
-            gt[k] = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NS; ++ks)
-                gt[k] = M::mma(lds_frag(Bs, LDN, jt * 16, ks * M::K, lane),
-                               lds_frag(Cs, LDN, it * 16, ks * M::K, lane), gt[k]);
-        }
-        f32x4 pv[2][2];
-        float colscale[2];
-        pv[0][1] = zero4();
-        if (split) {
-            const float s15 = exp2_fast(rf.lcs[15]);
-            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&rf.bw[4 * lg]);
-            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&rf.bw[16 + 4 * lg]);
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int i = it * 16 + li;
-                const float ai = rf.a[i];
-                colscale[it] = ai * s15;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j0 = 4 * lg + r;
-                    if (it == 0) {
-                        pv[0][0][r] = (j0 <= li) ? gt[0][r] * (ai * b0[r]) : 0.f;
-                    } else {
-                        pv[1][0][r] = gt[1][r] * (ai * b0[r]);
-                        pv[1][1][r] = (j0 <= li) ? gt[2][r] * (ai * b1[r]) : 0.f;
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int i = it * 16 + li;
-                const float lci = rf.lcs[i];
-                colscale[it] = exp2_fast(lci);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j0 = 4 * lg + r;
-                    if (it == 0) {
-                        pv[0][0][r] = (j0 <= li)
-                                          ? gt[0][r] * exp2_fast(lci - rf.lcs[j0]) * rf.d[j0]
-                                          : 0.f;
-                    } else {
-                        pv[1][0][r] = gt[1][r] * exp2_fast(lci - rf.lcs[j0]) * rf.d[j0];
-                        pv[1][1][r] = (j0 <= li) ? gt[2][r] * exp2_fast(lci - rf.lcs[16 + j0]) *
-                                                       rf.d[16 + j0]
-                                                 : 0.f;
-                    }
-                }
-            }
-        }
-
-        // ---- y^T tiles of the wave's columns: element r of lane l is
-        //      (p = 16 pt + 4 lg + r, i = 16 it + li); staged in Ys
-#pragma unroll
-        for (int u = 0; u < CPW; ++u) {
-            const int pt = wave + W * u;
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int i = it * 16 + li;
-                f32x4 ya = zero4();
-#pragma unroll
-                for (int m = 0; m < NB; ++m)
-#pragma unroll
-                    for (int q = 0; q < KS; ++q)
-                        ya = M::mma(frag_from_acc<OP>(accH[u][2 * m], accH[u][2 * m + 1], q),
-                                    frag_rows_kconv(Cs, LDN, it * 16, 32 * m, q, lane), ya);
-                ya *= colscale[it];
-#pragma unroll
-                for (int q = 0; q < KS; ++q)
-                    ya = M::mma(frag_kmajor(Xs, LDX, 0, q, pt * 16, lane),
-                                frag_from_acc<OP>(pv[it][0], pv[it][1], q), ya);
-                const f32x4 xv = lds_load4(Xs + i * LDX + pt * 16 + 4 * lg);
-                if constexpr (kStageY) {
-                    store4(Yc + i * LDY + pt * 16 + 4 * lg, ya + Dh * xv);
-                } else {
-                    const int64_t r0 = (int64_t)s * T;
-                    const Rsrc ry = make_rsrc(yb + r0 * xs, (rows - r0) * xs * (int64_t)sizeof(IO));
-                    buf_store16(ry, (uint32_t)(i * xs + pt * 16 + 4 * lg) * (uint32_t)sizeof(IO),
-                                __builtin_bit_cast(u32x4, ya + Dh * xv));
-                }
-            }
-        }
-
-        // ---- carry the state to the next block of the chunk
-        if (s + 1 < nblk) {
-            const float decay = exp2_fast(lam);
-#pragma unroll
-            for (int u = 0; u < CPW; ++u) {
-                const int pt = wave + W * u;
-#pragma unroll
-                for (int tr = 0; tr < RT; ++tr) {
-                    accH[u][tr] *= decay;
-#pragma unroll
-                    for (int q = 0; q < KS; ++q)
-                        accH[u][tr] = M::mma(frag_kmajor(Bs, LDN, 0, q, tr * 16, lane),
-                                             frag_kmajor(Xw, LDX, 0, q, pt * 16, lane),
-                                             accH[u][tr]);
-                }
-            }
-        }
-        lds_barrier();  // this block's operands are free, its y rows staged
-
-        // ---- write the block's y rows (whole rows, 16 bytes per thread)
-        if constexpr (kStageY) {
-            const int64_t r0 = (int64_t)s * T;
-            const Rsrc ry = make_rsrc(yb + r0 * xs, (rows - r0) * xs * (int64_t)sizeof(IO));
-#pragma unroll
-            for (int rr = 0; rr < T; rr += YRPP) {
-                const int row = rr + tid / YTPR, cv = tid % YTPR;
-                if (YRPP <= T || row < T) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(Yc + row * LDY + cv * YV);
-                    buf_store16(ry, (uint32_t)(row * xs + cv * YV) * (uint32_t)sizeof(IO), v);
-                }
-            }
-        }
+        co_stage(pf, lds + (cur ^ 1) * BUF, rowsf[cur ^ 1], tid);  // block s + 1
+        co_prefetch(pf, s + 2, cp, tid);
+        co_compute<IO, P, N, HPW>(accH, lds + cur * BUF, rowsf[cur][hs], s + 1 < nblk, Dh, cp,
+                                  s * T, hs, c0, lane);
+        lds_barrier();
     }
 }
 
@@ -833,17 +945,22 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
         trace_begin(2, s);
         hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, s, Eseg, Lseg, a.final_state, pl.b * pl.h, h,
-                           pl.nseg, np4);
+                           pl.nseg, N, P);
         trace_end(2, s);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
 
     trace_begin(3, s);
-    hipLaunchKernelGGL((k_chunk_out<IO, P, N>), dim3((unsigned)(pl.b * pl.nc * pl.h)),
-                       dim3(CoShape<P>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb, Eseg,
-                       Dlog, y,
-                       pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
+    constexpr int HP = kCoHeads<P>;
+    if (HP > 1 && (h / g) % HP == 0)
+        hipLaunchKernelGGL((k_chunk_out<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
+                           dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb,
+                           Eseg, Dlog, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
+    else
+        hipLaunchKernelGGL((k_chunk_out<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
+                           dim3(Co<IO, P, N, 1>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb,
+                           Eseg, Dlog, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
     trace_end(3, s);
     return hipGetLastError();
 }

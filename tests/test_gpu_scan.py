@@ -251,7 +251,8 @@ def test_stage_intermediates(orc, io):
         .reshape(b, h, nc * Q)[..., :l]
     wgt = wsf[off_wgt // 4: off_wgt // 4 + b * h * lp].view(b, h, nc, Qp)[..., :Q] \
         .reshape(b, h, nc * Q)[..., :l]
-    hb = wsf[off_hb // 4: off_hb // 4 + b * nc * h * n * p].view(b, nc, h, n, p)
+    # boundary states are stored transposed: [b, chunks, heads, head_dim, state_dim]
+    hb = wsf[off_hb // 4: off_hb // 4 + b * nc * h * n * p].view(b, nc, h, p, n).transpose(3, 4)
     _, _, inter = chunked.chunked_scan(**oracle_kw(inp), chunk=Q)
     check_close(to_f64(dtp), inter["d"], "f32", "processed time step")
     # per-chunk cumsum (natural log) == lcs / log2(e) since blocks == chunks
