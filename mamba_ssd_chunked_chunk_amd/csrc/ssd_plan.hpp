@@ -32,6 +32,14 @@ constexpr int64_t kTargetChains = 512;
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Heads per workgroup of the serial pass and of the chunk output: 128 /
+// head_dim (4 for head_dim <= 32) consecutive heads of one group when the
+// group size is a multiple of that, else 1.
+inline int group_heads(int p, int64_t heads_per_group) {
+    const int hp = p >= 64 ? 128 / p : 4;
+    return (hp > 1 && heads_per_group % hp == 0) ? hp : 1;
+}
+
 // Fills the plan from the sizes; returns false if they are invalid.
 inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, int64_t n,
                       int64_t g, int64_t Q, int io) {
@@ -43,7 +51,7 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     P.nsb = (Q + P.T - 1) / P.T;
     P.Qp = P.nsb * P.T;
     P.lp = P.nc * P.Qp;
-    const int64_t chains = b * h;
+    const int64_t chains = b * h / group_heads((int)p, h / g);  // workgroups per segment
     int64_t nseg = chains > 0 ? (kTargetChains + chains - 1) / chains : 1;
     if (nseg < 1) nseg = 1;
     if (nseg > P.nc) nseg = P.nc > 0 ? P.nc : 1;

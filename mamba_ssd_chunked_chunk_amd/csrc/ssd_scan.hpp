@@ -42,6 +42,11 @@ constexpr int kT = 32;  // rows per block
 template <typename IO>
 constexpr bool kOpCopy = !std::is_same<IO, typename Op<IO>::type>::value;
 
+// Heads of one group handled by one workgroup of the state pass and of the
+// chunk output when the group size allows it (see group_heads in the plan):
+// B and C are staged once for all of them.
+template <int P> constexpr int kGroupHeads = P >= 64 ? 128 / P : 4;
+
 // ----------------------------------------------------------------------------
 // 1. Preparation.
 //    (a) Per padded row R = c Qp + r of every (batch, head), one wave per 64
@@ -109,253 +114,268 @@ __global__ __launch_bounds__(256) void k_prep(
 }
 
 // ----------------------------------------------------------------------------
-// Slabs of the state pass: SLAB consecutive blocks of one chunk (the last
-// slab of a chunk may hold fewer).  Slab si of a segment is slab si % nspc of
-// chunk c0 + si / nspc.
-struct SlabPos {
-    int64_t c;   // chunk
-    int bi0;     // first block of the slab inside the chunk
-    int nb;      // blocks in the slab
-};
-__device__ __forceinline__ SlabPos slab_pos(int64_t si, int64_t c0, int nspc, int nsb, int slab) {
-    SlabPos s;
-    s.c = c0 + si / nspc;
-    s.bi0 = (int)(si % nspc) * slab;
-    s.nb = nsb - s.bi0 < slab ? nsb - s.bi0 : slab;
-    return s;
-}
-
-// Register prefetch of one slab.  Pieces are 8 consecutive elements of one
-// row of x (P / 8 per row) or of B (N / 8 per row).  The loads go through
-// buffer resources that end at the chunk's last valid row, so pieces of
-// padded rows or rows past the sequence come back as zeros.
-template <typename IO, int P, int N, int SLAB> struct SpBuf {
-    typedef typename Op<IO>::type OP;
-    static constexpr int NPX = SLAB * kT * P / 8, NPB = SLAB * kT * N / 8;
-    static constexpr int KX = (NPX + kThreads - 1) / kThreads;
-    static constexpr int KB = (NPB + kThreads - 1) / kThreads;
-    Row8v<IO> xv[KX];
-    Row8v<OP> bv[KB];
-    float xw[KX];      // weight of the x piece's row
-    float lam[SLAB];   // log2 decay of each block of the slab
-};
-
-template <typename IO, int P, int N, int SLAB>
-__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, SLAB> &f, const SlabPos &sp,
-                                            const IO *xb, const typename Op<IO>::type *Bb,
-                                            Rsrc rw, const float *lcs_bh, int64_t l, int64_t Q,
-                                            int64_t nsb, int64_t xs, int64_t bs, int tid) {
-    typedef SpBuf<IO, P, N, SLAB> F;
-    typedef typename Op<IO>::type OP;
-    constexpr int T = kT;
-    const int64_t row0 = sp.c * Q + (int64_t)sp.bi0 * T;          // sequence row
-    const int64_t cend = (sp.c + 1) * Q < l ? (sp.c + 1) * Q : l;  // end of the chunk
-    const int64_t valid = cend - row0;
-    const Rsrc rx = make_rsrc(xb + row0 * xs, valid * xs * (int64_t)sizeof(IO));
-    const Rsrc rb = make_rsrc(Bb + row0 * bs, valid * bs * (int64_t)sizeof(OP));
-    const uint32_t wrow = (uint32_t)((sp.c * nsb + sp.bi0) * T) * 4u;
-#pragma unroll
-    for (int k = 0; k < F::KX; ++k) {
-        const int q = tid + k * kThreads;
-        if (F::NPX % kThreads == 0 || q < F::NPX) {
-            const int j = q / (P / 8), cc = q % (P / 8);
-            f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * xs + cc * 8) * (uint32_t)sizeof(IO));
-            f.xw[k] = buf_f32(rw, (uint32_t)j * 4u, wrow);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < F::KB; ++k) {
-        const int q = tid + k * kThreads;
-        if (F::NPB % kThreads == 0 || q < F::NPB) {
-            const int j = q / (N / 8), cc = q % (N / 8);
-            f.bv[k] = buf_row8<OP>(rb, (uint32_t)(j * bs + cc * 8) * (uint32_t)sizeof(OP));
-        }
-    }
-#pragma unroll
-    for (int jb = 0; jb < SLAB; ++jb)
-        f.lam[jb] = lcs_bh[(sp.c * nsb + sp.bi0 + (jb < sp.nb ? jb : 0)) * T + T - 1];
-}
-
-template <typename IO, int P, int N, int SLAB>
-__device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, SLAB> &f,
-                                         typename Op<IO>::type *Xw,
-                                         typename Op<IO>::type *Bs, int tid) {
-    typedef SpBuf<IO, P, N, SLAB> F;
-    constexpr int LDX = P + 16, LDB = N + 16;
-#pragma unroll
-    for (int k = 0; k < F::KX; ++k) {
-        const int q = tid + k * kThreads;
-        if (F::NPX % kThreads == 0 || q < F::NPX)
-            st_row8(Xw + (q / (P / 8)) * LDX + (q % (P / 8)) * 8, wx_piece(f.xv[k], f.xw[k]));
-    }
-#pragma unroll
-    for (int k = 0; k < F::KB; ++k) {
-        const int q = tid + k * kThreads;
-        if (F::NPB % kThreads == 0 || q < F::NPB)
-            st_row8(Bs + (q / (N / 8)) * LDB + (q % (N / 8)) * 8, f.bv[k]);
-    }
-}
-
-// ----------------------------------------------------------------------------
 // 2. Chunk states and the serial pass over chunks.
-//    One workgroup per (batch, segment, head).  The state H (state_dim x
-//    head_dim, fp32) lives in MFMA accumulators for the whole segment, its
-//    16 x 16 tiles dealt round-robin to the 4 waves.  Slabs are fetched two
-//    ahead into registers and staged through one LDS buffer.  Per block:
+//    One workgroup per (batch, segment, HPW consecutive heads of one group);
+//    WPH = max(1, head_dim / 32) waves per head, each owning 32 (or head_dim)
+//    head_dim columns of its head's state H (state_dim x head_dim, fp32) in
+//    MFMA accumulators for the whole segment.  Slabs of SLAB row blocks of
+//    one chunk are fetched two ahead into registers (B once for all heads, x
+//    per head) and staged through one LDS buffer.  Per block:
 //        H <- 2^lcs_last H + B^T (w x),  w_j = 2^(lcs_last - lcs_j) d_j,
 //    both operands read k-major through transposing LDS loads.  Before the
-//    first block of every chunk the state is written out as that chunk's
-//    boundary state.  Segment 0 starts from init_state; later segments start
-//    from zero and are corrected by k_seg_combine and in k_chunk_out.
-template <typename IO, int P, int N> struct SpState {
+//    first block of every chunk the state is written out, transposed
+//    ([head_dim][state_dim], one 16-byte store per lane and tile), as that
+//    chunk's boundary state.  Segment 0 starts from init_state; later
+//    segments start from zero and are corrected by k_seg_combine and in
+//    k_chunk_out.  The slab position is kept as (chunk, slab of the chunk)
+//    counters, so the loop has no divisions.
+template <typename IO, int P, int N, int HPW> struct Sp {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
-    static constexpr int SLAB = 2;
-    static constexpr int SR = SLAB * kT;
-    static constexpr int LDX = P + 16, LDB = N + 16;
-    static constexpr int CT = P / 16;
-    static constexpr int TILES = (N / 16) * CT;
-    static constexpr int TPW = (TILES + kWaves - 1) / kWaves;
+    static constexpr int T = kT;
+    static constexpr int SLAB = 2, SR = SLAB * T;     // blocks and rows per slab
+    static constexpr int WPH = P >= 64 ? P / 32 : 1;  // waves per head
+    static constexpr int PW = P / WPH;                // head_dim columns per wave
+    static constexpr int CPW = PW / 16;               // column tiles per wave
+    static constexpr int W = HPW * WPH, NT = 64 * W;  // waves, threads
+    static constexpr int RT = N / 16;                 // state row tiles
+    static constexpr int TPW = CPW * RT;              // tiles per wave
+    static constexpr int KS = T / M::K;               // MFMA steps per block
+    static constexpr int LDX = P + 16, LDB = N + 16;  // padded rows (transposing reads)
+    static constexpr int XS = SR * LDX;               // one head's staged w x
+    static constexpr int BUF = SR * LDB + HPW * XS;   // [B | w x of each head]
+    static constexpr int NPB = SR * N / 8, NPX = HPW * SR * P / 8;  // pieces of 8
+    static constexpr int KB = (NPB + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
 };
 
-// Applies one staged slab to the accumulators (acc: the wave's TPW tiles;
-// inlined, so they stay in registers).
-template <typename IO, int P, int N>
-__device__ __forceinline__ void sp_apply(f32x4 *acc, float &logdec,
-                                         const typename Op<IO>::type *lds, const SlabPos &sp,
-                                         const float *lam, float *Hb_bh, float *Dlog_bh,
-                                         int64_t NPh, int nsegs, int wave, int lane, int tid) {
-    typedef SpState<IO, P, N> S;
-    typedef typename S::M M;
-    constexpr int T = kT, KS = T / M::K;
-    const auto *Xw = lds;
-    const auto *Bs = lds + S::SR * S::LDX;
+// Register prefetch of one slab.  Loads go through buffer resources that end
+// at the chunk's last valid row (zeros beyond), so padded rows and rows past
+// the sequence need no masks; a slab past the segment's end (dead) issues the
+// same loads with empty resources.
+template <typename IO, int P, int N, int HPW> struct SpBuf {
+    typedef Sp<IO, P, N, HPW> K;
+    Row8v<typename K::OP> bv[K::KB];
+    Row8v<IO> xv[K::KX];
+    float xw[K::KX];            // weight of the x piece's row
+    float lam[HPW][K::SLAB];    // log2 decay of each block, per head (uniform)
+};
+
+// Addressing of one workgroup's serial pass.
+template <typename IO> struct SpPtrs {
+    typedef typename Op<IO>::type OP;
+    const IO *x;          // row 0 of the sequence, first head of the workgroup
+    const OP *B;          // row 0 of the sequence, the group
+    const float *lcs;     // (batch, first head) row arrays
+    Rsrc rw;              // weights of the workgroup's heads
+    int64_t xs, bs;       // row strides (elements) of x and of B
+    int64_t l, Q, hrow;   // sequence length, chunk, elements from one head's row arrays to the next
+    int nsb;              // blocks per chunk
+};
+
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, int bi0, bool live,
+                                            const SpPtrs<IO> &sp, int tid) {
+    typedef Sp<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    constexpr int T = kT;
+    const int64_t row0 = c * sp.Q + (int64_t)bi0 * T;                  // sequence row
+    const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;  // end of the chunk
+    int64_t valid = live ? cend - row0 : 0;
+    valid = valid < 0 ? 0 : (valid > K::SR ? K::SR : valid);
+    const int64_t rr0 = valid > 0 ? row0 : 0;
+    const Rsrc rx = make_rsrc(sp.x + rr0 * sp.xs, valid * sp.xs * (int64_t)sizeof(IO));
+    const Rsrc rb = make_rsrc(sp.B + rr0 * sp.bs, valid * sp.bs * (int64_t)sizeof(OP));
+    const int64_t R0 = live ? (c * sp.nsb + bi0) * T : 0;             // padded row of the slab
 #pragma unroll
-    for (int jb = 0; jb < S::SLAB; ++jb) {
-        if (jb < sp.nb) {
-            if (sp.bi0 + jb == 0) {  // first block of a chunk: emit the boundary state
-                // transposed layout [head_dim][state_dim]: the 4 accumulator
-                // values of a lane (consecutive n) are one 16-byte store
-                float *dst = Hb_bh + sp.c * NPh;
+    for (int k = 0; k < K::KB; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPB % K::NT == 0 || q < K::NPB) {
+            const int j = q / (N / 8), cc = q % (N / 8);
+            f.bv[k] = buf_row8<OP>(rb, (uint32_t)(j * sp.bs + cc * 8) * (uint32_t)sizeof(OP));
+        }
+    }
 #pragma unroll
-                for (int i = 0; i < S::TPW; ++i) {
-                    const int ti = wave + kWaves * i;
-                    if (ti < S::TILES) {
-                        const int tr = ti / S::CT, tc = ti % S::CT;
-                        *reinterpret_cast<f32x4 *>(dst + (tc * 16 + (lane & 15)) * N + tr * 16 +
-                                                   4 * (lane >> 4)) = acc[i];
-                    }
-                }
-                if (nsegs > 1 && tid == 0) Dlog_bh[sp.c] = logdec;
-            }
+    for (int k = 0; k < K::KX; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPX % K::NT == 0 || q < K::NPX) {
+            const int hs = q / (K::SR * P / 8), qq = q % (K::SR * P / 8);
+            const int j = qq / (P / 8), cc = qq % (P / 8);
+            f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * sp.xs + hs * P + cc * 8) *
+                                           (uint32_t)sizeof(IO));
+            f.xw[k] = buf_f32(sp.rw, (uint32_t)(hs * sp.hrow + j) * 4u, (uint32_t)R0 * 4u);
+        }
+    }
+#pragma unroll
+    for (int hs = 0; hs < HPW; ++hs)
+#pragma unroll
+        for (int jb = 0; jb < K::SLAB; ++jb) {
+            const int b = bi0 + jb < sp.nsb ? bi0 + jb : sp.nsb - 1;
+            f.lam[hs][jb] = live ? sp.lcs[hs * sp.hrow + (c * sp.nsb + b) * T + T - 1] : 0.f;
+        }
+}
+
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f,
+                                         typename Op<IO>::type *buf, int tid) {
+    typedef Sp<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    OP *Bs = buf, *Xw = buf + K::SR * K::LDB;
+#pragma unroll
+    for (int k = 0; k < K::KB; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPB % K::NT == 0 || q < K::NPB)
+            st_row8(Bs + (q / (N / 8)) * K::LDB + (q % (N / 8)) * 8, f.bv[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < K::KX; ++k) {
+        const int q = tid + k * K::NT;
+        if (K::NPX % K::NT == 0 || q < K::NPX) {
+            const int hs = q / (K::SR * P / 8), qq = q % (K::SR * P / 8);
+            st_row8(Xw + hs * K::XS + (qq / (P / 8)) * K::LDX + (qq % (P / 8)) * 8,
+                    wx_piece(f.xv[k], f.xw[k]));
+        }
+    }
+}
+
+// Transposed store of the wave's state tiles ([head_dim][state_dim]).
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_store_t(float *dst, const f32x4 *acc, int c0, int lane) {
+    typedef Sp<IO, P, N, HPW> K;
+#pragma unroll
+    for (int u = 0; u < K::CPW; ++u)
+#pragma unroll
+        for (int tr = 0; tr < K::RT; ++tr)
+            *reinterpret_cast<f32x4 *>(dst + (c0 + 16 * u + (lane & 15)) * N + tr * 16 +
+                                       4 * (lane >> 4)) = acc[u * K::RT + tr];
+}
+
+// Applies the staged slab's nb blocks to the wave's tiles.
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type *buf, int nb,
+                                         const float *lam, int hs, int c0, int lane) {
+    typedef Sp<IO, P, N, HPW> K;
+    typedef typename K::M M;
+    constexpr int T = kT, KS = K::KS;
+    const auto *Bs = buf;
+    const auto *Xw = buf + K::SR * K::LDB + hs * K::XS;
+#pragma unroll
+    for (int jb = 0; jb < K::SLAB; ++jb) {
+        if (jb < nb) {
             const float decay = exp2_fast(lam[jb]);
-            logdec += lam[jb];
 #pragma unroll
-            for (int i = 0; i < S::TPW; ++i) acc[i] *= decay;
+            for (int k = 0; k < K::TPW; ++k) acc[k] *= decay;
 #pragma unroll
             for (int q = 0; q < KS; ++q) {
+                typename Mfma<typename K::OP>::frag xf[K::CPW];
 #pragma unroll
-                for (int i = 0; i < S::TPW; ++i) {
-                    const int ti = wave + kWaves * i;
-                    if (ti < S::TILES) {
-                        const int tr = ti / S::CT, tc = ti % S::CT;
-                        acc[i] = M::mma(frag_kmajor(Bs, S::LDB, jb * T, q, tr * 16, lane),
-                                        frag_kmajor(Xw, S::LDX, jb * T, q, tc * 16, lane),
-                                        acc[i]);
-                    }
+                for (int u = 0; u < K::CPW; ++u)
+                    xf[u] = frag_kmajor(Xw, K::LDX, jb * T, q, c0 + 16 * u, lane);
+#pragma unroll
+                for (int tr = 0; tr < K::RT; ++tr) {
+                    const auto bt = frag_kmajor(Bs, K::LDB, jb * T, q, tr * 16, lane);
+#pragma unroll
+                    for (int u = 0; u < K::CPW; ++u)
+                        acc[u * K::RT + tr] = M::mma(bt, xf[u], acc[u * K::RT + tr]);
                 }
             }
         }
     }
 }
 
-template <typename IO, int P, int N>
-__global__ __launch_bounds__(256) void k_state_pass(
+template <typename IO, int P, int N, int HPW>
+__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_state_pass(
     const IO *__restrict__ x, const typename Op<IO>::type *__restrict__ Bm,
     const float *__restrict__ lcs, const float *__restrict__ wgt, const float *__restrict__ init,
     float *__restrict__ Hb, float *__restrict__ Eseg, float *__restrict__ Dlog,
     float *__restrict__ Lseg, float *__restrict__ final_state, int64_t l, int h, int g, int64_t Q,
     int64_t nc, int64_t Qp, int64_t cps, int64_t nseg) {
-    typedef typename Op<IO>::type OP;
-    typedef SpState<IO, P, N> S;
-    constexpr int T = kT, SLAB = S::SLAB, TPW = S::TPW, CT = S::CT, TILES = S::TILES;
-    __shared__ __attribute__((aligned(16))) OP lds[S::SR * S::LDX + S::SR * S::LDB];  // [w x | B]
+    typedef Sp<IO, P, N, HPW> K;
+    typedef typename K::OP OP;
+    constexpr int T = kT, SLAB = K::SLAB, TPW = K::TPW, RT = K::RT, CPW = K::CPW;
+    __shared__ __attribute__((aligned(16))) OP lds[K::BUF];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
-    const int hh = (int)(item % h); item /= h;
+    const int hq = (int)(item % (h / HPW)); item /= (h / HPW);
     const int64_t seg = item % nseg;
     const int64_t b = item / nseg;
-    const int gi = hh / (h / g);
+    const int hh0 = hq * HPW;
+    const int gi = hh0 / (h / g);
+    const int hs = wave / K::WPH;                  // this wave's head slot
+    const int hh = hh0 + hs;
+    const int c0 = (wave % K::WPH) * K::PW;        // this wave's first column
     const int nsb = (int)(Qp / T);
-    const int nspc = (nsb + SLAB - 1) / SLAB;  // slabs per chunk
-    const int64_t c0 = seg * cps;
-    const int64_t c1 = (c0 + cps < nc) ? c0 + cps : nc;
-    const int64_t nslab = (c1 - c0) * nspc;
-    const float *lcs_bh = lcs + (b * h + hh) * nc * Qp;
-    const Rsrc rw = make_rsrc(wgt + (b * h + hh) * nc * Qp, nc * Qp * 4);
+    const int nspc = (nsb + SLAB - 1) / SLAB;      // slabs per chunk
+    const int64_t ca = seg * cps;
+    const int64_t cb = (ca + cps < nc) ? ca + cps : nc;
+    const int64_t nslab = (cb - ca) * nspc;
     const int64_t NP = (int64_t)N * P;
-    const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N;
-    const IO *xb = x + (b * l * h + hh) * P;   // row t at xb + t * xs
-    const OP *Bb = Bm + (b * l * g + gi) * N;   // row t at Bb + t * bs
-    float *Hb_bh = Hb + (b * nc * h + hh) * NP;  // chunk c at Hb_bh + c * h * NP
-    float *Dlog_bh = Dlog + (b * h + hh) * nc;
+    SpPtrs<IO> sp;
+    sp.xs = (int64_t)h * P;
+    sp.bs = (int64_t)g * N;
+    sp.x = x + (b * l * h + hh0) * P;
+    sp.B = Bm + (b * l * g + gi) * N;
+    sp.lcs = lcs + (b * h + hh0) * nc * Qp;
+    sp.hrow = nc * Qp;
+    sp.rw = make_rsrc(wgt + (b * h + hh0) * nc * Qp, ((int64_t)(HPW - 1) * nc * Qp + nc * Qp) * 4);
+    sp.l = l;
+    sp.Q = Q;
+    sp.nsb = nsb;
+    float *Hb_h = Hb + (b * nc * h + hh) * NP;      // chunk c at Hb_h + c * h * NP
+    float *Dlog_h = Dlog + (b * h + hh) * nc;
 
     f32x4 acc[TPW];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) acc[i] = zero4();
-    if (seg == 0 && init) {
+    for (int k = 0; k < TPW; ++k) acc[k] = zero4();
+    if (seg == 0 && init) {  // [state_dim][head_dim]
+        const float *src = init + (b * h + hh) * NP;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int ti = wave + kWaves * i;
-            if (ti < TILES) {
-                const int tr = ti / CT, tc = ti % CT;
-                const float *src = init + (b * h + hh) * NP +
-                                   (int64_t)(tr * 16 + 4 * (lane >> 4)) * P + tc * 16 +
-                                   (lane & 15);
+        for (int u = 0; u < CPW; ++u)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][r] = src[r * P];
-            }
-        }
+            for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[u * RT + tr][r] =
+                        src[(tr * 16 + 4 * (lane >> 4) + r) * P + c0 + 16 * u + (lane & 15)];
     }
     float logdec = 0.f;
 
-    // two slabs in flight in registers; slab si lives in pf[si & 1]
-    SpBuf<IO, P, N, SLAB> pa, pb;
-    if (nslab > 0)
-        sp_prefetch(pa, slab_pos(0, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q, nsb, xs, bs,
-                    tid);
-    if (nslab > 1)
-        sp_prefetch(pb, slab_pos(1, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q, nsb, xs, bs,
-                    tid);
+    // apply position (ac, ak) and prefetch position (pc, pk), two slabs ahead
+    int64_t ac = ca, pc = ca;
+    int ak = 0, pk = 0;
+    SpBuf<IO, P, N, HPW> pa, pb;
+    sp_prefetch(pa, pc, pk * SLAB, nslab > 0, sp, tid);
+    if (++pk == nspc) { pk = 0; ++pc; }
+    sp_prefetch(pb, pc, pk * SLAB, nslab > 1, sp, tid);
+    if (++pk == nspc) { pk = 0; ++pc; }
     for (int64_t si = 0; si < nslab; si += 2) {
-        {
-            const SlabPos sp = slab_pos(si, c0, nspc, nsb, SLAB);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            SpBuf<IO, P, N, HPW> &pf = half == 0 ? pa : pb;
+            const bool live = si + half < nslab;
+            const int bi0 = ak * SLAB;
+            const int nb = live ? (nsb - bi0 < SLAB ? nsb - bi0 : SLAB) : 0;
             float lam[SLAB];
 #pragma unroll
-            for (int jb = 0; jb < SLAB; ++jb) lam[jb] = pa.lam[jb];
+            for (int jb = 0; jb < SLAB; ++jb) {
+                float v = pf.lam[0][jb];
+#pragma unroll
+                for (int k = 1; k < HPW; ++k) v = hs == k ? pf.lam[k][jb] : v;
+                lam[jb] = v;
+            }
             lds_barrier();  // the previous slab's reads are done
-            sp_stage(pa, lds, lds + S::SR * S::LDX, tid);
-            if (si + 2 < nslab)
-                sp_prefetch(pa, slab_pos(si + 2, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q,
-                            nsb, xs, bs, tid);
+            sp_stage(pf, lds, tid);
+            sp_prefetch(pf, pc, pk * SLAB, si + half + 2 < nslab, sp, tid);
+            if (++pk == nspc) { pk = 0; ++pc; }
             lds_barrier();
-            sp_apply<IO, P, N>(acc, logdec, lds, sp, lam, Hb_bh, Dlog_bh, h * NP, (int)nseg,
-                               wave, lane, tid);
-        }
-        if (si + 1 < nslab) {
-            const SlabPos sp = slab_pos(si + 1, c0, nspc, nsb, SLAB);
-            float lam[SLAB];
+            if (live && ak == 0) {  // first slab of a chunk: emit the boundary state
+                sp_store_t<IO, P, N, HPW>(Hb_h + ac * h * NP, acc, c0, lane);
+                if (nseg > 1 && lane == 0) Dlog_h[ac] = logdec;
+            }
+            sp_apply<IO, P, N, HPW>(acc, lds, nb, lam, hs, c0, lane);
 #pragma unroll
-            for (int jb = 0; jb < SLAB; ++jb) lam[jb] = pb.lam[jb];
-            lds_barrier();
-            sp_stage(pb, lds, lds + S::SR * S::LDX, tid);
-            if (si + 3 < nslab)
-                sp_prefetch(pb, slab_pos(si + 3, c0, nspc, nsb, SLAB), xb, Bb, rw, lcs_bh, l, Q,
-                            nsb, xs, bs, tid);
-            lds_barrier();
-            sp_apply<IO, P, N>(acc, logdec, lds, sp, lam, Hb_bh, Dlog_bh, h * NP, (int)nseg,
-                               wave, lane, tid);
+            for (int jb = 0; jb < SLAB; ++jb) logdec += jb < nb ? lam[jb] : 0.f;
+            if (++ak == nspc) { ak = 0; ++ac; }
         }
     }
 
@@ -363,30 +383,18 @@ __global__ __launch_bounds__(256) void k_state_pass(
         if (final_state) {
             float *out = final_state + (b * h + hh) * NP;
 #pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int ti = wave + kWaves * i;
-                if (ti < TILES) {
-                    const int tr = ti / CT, tc = ti % CT;
-                    float *d0 = out + (int64_t)(tr * 16 + 4 * (lane >> 4)) * P + tc * 16 +
-                                (lane & 15);
+            for (int u = 0; u < CPW; ++u)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) d0[r * P] = acc[i][r];
-                }
-            }
+                for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        out[(tr * 16 + 4 * (lane >> 4) + r) * P + c0 + 16 * u + (lane & 15)] =
+                            acc[u * RT + tr][r];
         }
     } else {  // the segment's state from its start, transposed like Hb
-        float *out = Eseg + ((b * nseg + seg) * h + hh) * NP;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int ti = wave + kWaves * i;
-            if (ti < TILES) {
-                const int tr = ti / CT, tc = ti % CT;
-                *reinterpret_cast<f32x4 *>(out + (tc * 16 + (lane & 15)) * N + tr * 16 +
-                                           4 * (lane >> 4)) = acc[i];
-            }
-        }
+        sp_store_t<IO, P, N, HPW>(Eseg + ((b * nseg + seg) * h + hh) * NP, acc, c0, lane);
+        if (lane == 0) Lseg[(b * h + hh) * nseg + seg] = logdec;
     }
-    if (nseg > 1 && tid == 0) Lseg[(b * h + hh) * nseg + seg] = logdec;
 }
 
 // ----------------------------------------------------------------------------
@@ -478,8 +486,6 @@ template <typename IO, int P, int N, int HPW> struct Co {
     static constexpr int KC = (NPC + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
 };
 
-// Heads per workgroup used for head_dim P when the group size allows it.
-template <int P> constexpr int kCoHeads = P >= 64 ? 128 / P : 4;
 
 // Per-row factors of one head's staged block (LDS), T floats each.
 struct alignas(16) CoRows {
@@ -932,9 +938,18 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
 
     trace_begin(1, s);
-    hipLaunchKernelGGL((k_state_pass<IO, P, N>), dim3((unsigned)(pl.b * pl.nseg * pl.h)),
-                       dim3(kThreads), 0, s, x, Bop, lcs, wgt, a.init, Hb, Eseg, Dlog, Lseg,
-                       a.final_state, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
+    constexpr int HP = kGroupHeads<P>;
+    const int hpw = group_heads((int)P, h / g);  // HP or 1
+    if (hpw == HP && HP > 1)
+        hipLaunchKernelGGL((k_state_pass<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nseg * (h / HP))),
+                           dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bop, lcs, wgt, a.init, Hb, Eseg,
+                           Dlog, Lseg, a.final_state, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps,
+                           pl.nseg);
+    else
+        hipLaunchKernelGGL((k_state_pass<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nseg * h)),
+                           dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bop, lcs, wgt, a.init, Hb, Eseg,
+                           Dlog, Lseg, a.final_state, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps,
+                           pl.nseg);
     trace_end(1, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -952,8 +967,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     }
 
     trace_begin(3, s);
-    constexpr int HP = kCoHeads<P>;
-    if (HP > 1 && (h / g) % HP == 0)
+    if (hpw == HP && HP > 1)
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
                            dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb,
                            Eseg, Dlog, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
