@@ -60,6 +60,13 @@ __device__ __forceinline__ float time_step(float raw, float bias, int use_softpl
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: values derived from it (head slot, column offset, buffer resources)
+// then stay in scalar registers instead of being treated as per-lane.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations, then s_barrier.  Unlike __syncthreads() it does not wait for
 // outstanding global loads, so a register prefetch issued before it stays in
@@ -333,10 +340,17 @@ __device__ __forceinline__ Row8v<float> wx_piece(const Row8v<float> &v, float w)
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (CDNA)
 
+// Every resource here is wave-uniform by construction; the base and size are
+// passed through readfirstlane so that the compiler keeps the descriptor in
+// scalar registers (a descriptor it believes per-lane costs a loop per load).
 __device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
     const int64_t c = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                             (int)(uint32_t)c, kRsrcWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)(uint32_t)c);
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, kRsrcWord3);
 }
 template <typename T> __device__ __forceinline__ Row8v<T> buf_row8(Rsrc r, uint32_t off) {
     constexpr int NV = sizeof(Row8v<T>) / 16;

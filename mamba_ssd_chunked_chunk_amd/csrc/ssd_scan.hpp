@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_prep(
     float *__restrict__ wgt, int64_t na, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
     typename Op<IO>::type *__restrict__ Bf, typename Op<IO>::type *__restrict__ Cf,
     int64_t pieces) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     if ((int64_t)blockIdx.x < na) {
         const int64_t lp = nc * Qp, ns = (lp + 63) / 64;
         const int64_t item = (int64_t)blockIdx.x * kWaves + wave;  // (batch, head, slice)
@@ -294,7 +294,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_state_pass(
     constexpr int T = kT, SLAB = K::SLAB, TPW = K::TPW, RT = K::RT, CPW = K::CPW;
     __shared__ __attribute__((aligned(16))) OP lds[K::BUF];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
     const int hq = (int)(item % (h / HPW)); item /= (h / HPW);
     const int64_t seg = item % nseg;
@@ -824,7 +824,7 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     __shared__ __attribute__((aligned(16))) OP lds[2 * BUF];
     __shared__ CoRows rowsf[2][HPW];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int lg = lane >> 4, li = lane & 15;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
     const int hq = (int)(item % (h / HPW)); item /= (h / HPW);

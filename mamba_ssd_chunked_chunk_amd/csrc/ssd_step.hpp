@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void k_step(
     constexpr int RPI = 64 / LPR;          // rows per vector access of the wave
     constexpr int ITER = N / RPI;          // accesses per lane
     constexpr int RB = ITER < 16 ? ITER : 16;  // rows batched per lane
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int64_t pair = (int64_t)blockIdx.x * kWaves + wave;
     if (pair >= pairs) return;
     const int hh = (int)(pair % h);
