@@ -881,19 +881,30 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
         for (int k = 0; k < CPW * RT; ++k) accH[k] += corr * iv[k];
     }
 
-    // block s is staged in LDS buffer s & 1 while the previous one is
-    // computed; its loads were issued one block earlier
-    CoBuf<IO, P, N, HPW> pf;
-    co_prefetch(pf, 0, cp, tid);
-    co_stage(pf, lds, rowsf[0], tid);
-    co_prefetch(pf, 1, cp, tid);
+    // Block k is fetched into registers pa (k even) or pb (k odd) two blocks
+    // ahead and staged into LDS buffer k & 1 while block k - 1 is computed.
+    // Blocks go in pairs, every load and store issued unconditionally (past
+    // the chunk's end: empty resources; a block past the end is computed on
+    // zeros and stores nothing), so the loop has one path and the memory
+    // counters never need a full drain.
+    CoBuf<IO, P, N, HPW> pa, pb;
+    OP *const buf0 = lds;
+    OP *const buf1 = lds + BUF;
+    co_prefetch(pa, 0, cp, tid);
+    co_prefetch(pb, 1, cp, tid);
+    co_stage(pa, buf0, rowsf[0], tid);
+    co_prefetch(pa, 2, cp, tid);
     lds_barrier();
-    for (int s = 0; s < nblk; ++s) {
-        const int cur = s & 1;
-        co_stage(pf, lds + (cur ^ 1) * BUF, rowsf[cur ^ 1], tid);  // block s + 1
-        co_prefetch(pf, s + 2, cp, tid);
-        co_compute<IO, P, N, HPW>(accH, lds + cur * BUF, rowsf[cur][hs], s + 1 < nblk, Dh, cp,
-                                  s * T, hs, c0, lane);
+    for (int s = 0; s < nblk; s += 2) {
+        co_stage(pb, buf1, rowsf[1], tid);  // block s + 1
+        co_prefetch(pb, s + 3, cp, tid);
+        co_compute<IO, P, N, HPW>(accH, buf0, rowsf[0][hs], s + 1 < nblk, Dh, cp, s * T, hs, c0,
+                                  lane);
+        lds_barrier();
+        co_stage(pa, buf0, rowsf[0], tid);  // block s + 2
+        co_prefetch(pa, s + 4, cp, tid);
+        co_compute<IO, P, N, HPW>(accH, buf1, rowsf[1][hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+                                  hs, c0, lane);
         lds_barrier();
     }
 }
