@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD scan tokens/sec at 1 GPU; % of MFMA/HBM roofline; decode steps/sec"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_IDS = ("prep", "state_pass", "seg_combine", "chunk_out")
+KERNEL_IDS = ("prep", "chunk_state", "state_scan", "chunk_out")
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan.hpp",
                   "mamba_ssd_chunked_chunk_amd/csrc/ssd_device.hpp",
@@ -48,16 +48,12 @@ def source_digest() -> str:
 
 
 # ----------------------------------------------------------- byte counts ---
-def plan_sizes(b, l, h, p, n, g, Q, T=32, target_chains=512):
-    """Chunks, segments of the serial pass and padded rows, as the library
-    plans them (32-row blocks; about 512 independent serial chains)."""
+def plan_sizes(b, l, h, p, n, g, Q, T=32):
+    """Chunks and padded rows per sequence, as the library plans them
+    (32-row blocks that never straddle a chunk boundary)."""
     nc = -(-l // Q)
-    chains = b * h
-    nseg = min(max(1, -(-target_chains // chains)), nc)
-    cps = -(-nc // nseg)
-    nseg = -(-nc // cps)
     lp = nc * (-(-Q // T) * T)
-    return nc, nseg, lp
+    return nc, lp
 
 
 def bytes_scan_alg(b, l, h, p, n, g, Q, s, init=False, final=False):
@@ -76,29 +72,29 @@ def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
 
 def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
     """Algorithmic bytes of one launch of a scan kernel: every operand of its
-    step of the method moved once (per-row workspace arrays fp32, boundary
-    states fp32).  Reads of the segment-entry states, which exist only
-    because the serial pass is cut into segments, are not counted for the
-    chunk output; the segment combine's traffic is all of that kind."""
-    nc, nseg, lp = plan_sizes(b, l, h, p, n, g, Q)
+    step of the method moved once (per-row workspace arrays fp32, chunk
+    states fp32, boundary states in the read-out's operand type: fp16 on the
+    bf16 path, fp32 on the fp32 path)."""
+    nc, lp = plan_sizes(b, l, h, p, n, g, Q)
     th = b * l * h
     x = th * p * s                     # x (and y) in the io dtype
-    BC = b * l * g * n * s             # B or C, once per group (the fp16 copies for bf16)
+    BC = b * l * g * n * s             # B or C, once per group
     rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
-    hb = b * nc * h * n * p * 4        # boundary states
-    seg = b * nseg * h * n * p * 4 if nseg > 1 else 0
-    st = b * h * n * p * 4
+    so = 2 if s == 2 else 4            # boundary-state element
+    st = b * nc * h * n * p            # elements of all chunk (or boundary) states
+    fin = b * h * n * p * 4 if final else 0
     if name == "prep":
-        # dt read; lcs, d and weights written; bf16: B and C read, fp16 copies written
-        return th * s + 3 * rows + (4 * BC if s == 2 else 0)
-    if name == "state_pass":
-        # x and B read, row weights read, boundary states written
-        return x + BC + rows + hb + (st if final and nseg == 1 else 0)
-    if name == "seg_combine":
-        return 2 * seg + (st if final else 0)
+        # dt read; lcs, d and weights written
+        return th * s + 3 * rows
+    if name == "chunk_state":
+        # x, B and the row weights read, chunk states and decays written
+        return x + BC + rows + 4 * st + b * h * nc * 4
+    if name == "state_scan":
+        # chunk states and decays read, boundary states written
+        return 4 * st + b * h * nc * 4 + so * st + fin
     if name == "chunk_out":
         # x, B, C and the lcs, d and weight rows read, boundary states read, y written
-        return x + 2 * BC + 3 * rows + hb + x
+        return x + 2 * BC + 3 * rows + so * st + x
     raise KeyError(name)
 
 

@@ -98,8 +98,10 @@ enum ssd_status {
  * lie in [2^-14, 65504]; smaller magnitudes keep fewer significant bits
  * (below 2^-24 they count as zero) and larger ones saturate at 65504.  The
  * decay-weighted x, the masked scores and the carried state are rounded to
- * fp16 (toward zero) as operands; all sums, decays and states are fp32.
- * fp32 io uses fp32 operands throughout.
+ * fp16 (toward zero) as operands; the state entering each chunk is kept in
+ * the workspace as fp16 (rounded to nearest), the operand it feeds.  The
+ * recurrence across chunks, all sums and decays, and final_state are fp32.
+ * fp32 io uses fp32 operands and fp32 boundary states throughout.
  */
 int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
                        const void *C, const float *D, const float *dt_bias,
@@ -115,12 +117,11 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
  * 256-byte aligned: per-row cumulative log2 decay and processed time step
  * [batch, heads, padded seqlen] fp32 each (cumulative log2 decay inside
  * 32-row blocks, processed time step, weight in the state at the block end);
- * chunk-boundary states [batch, chunks, heads, head_dim, state_dim] fp32
- * (transposed); then, when the sequence is cut into several segments,
- * segment states [batch, segments, heads, head_dim, state_dim] fp32 and
- * per-chunk / per-segment log2 decays; then,
- * for bf16 io, fp16 copies of B and C [batch, seqlen, groups, state_dim].
- * The size returned covers both io dtypes.
+ * chunk-boundary states [batch, chunks, heads, head_dim, state_dim]
+ * (transposed; fp16 for bf16 io, fp32 for fp32 io, room reserved for fp32);
+ * every chunk's own state from zero, same shape, fp32; the log2 decay of
+ * every chunk [batch, heads, chunks] fp32.  The layout is the same for both
+ * io dtypes.
  */
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim,
@@ -164,10 +165,9 @@ int32_t ssd_abi_version(void);
  * clears that kernel's record.  Not thread-safe with concurrent scan calls.
  */
 enum ssd_kernel_id {
-    SSD_K_PREP = 0,        /* time step, per-block cumulative log decay; bf16 io:
-                              fp16 copies of B and C */
-    SSD_K_STATE_PASS = 1,  /* chunk states and serial state passing */
-    SSD_K_SEG_COMBINE = 2, /* combination of segment states (long sequences) */
+    SSD_K_PREP = 0,        /* time step, per-block cumulative log decay, state weights */
+    SSD_K_CHUNK_STATE = 1, /* every chunk's state from zero, in parallel */
+    SSD_K_STATE_SCAN = 2,  /* serial pass over chunks: boundary and final states */
     SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */
     SSD_K_STEP = 4,        /* decode step */
     SSD_K_COUNT = 5

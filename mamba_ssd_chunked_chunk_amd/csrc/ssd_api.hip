@@ -127,15 +127,9 @@ const char *ssd_status_string(int32_t status) {
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim, int64_t groups,
                                       int64_t chunk) {
-    ScanPlan pl;
-    // the larger of the two io layouts (bf16 adds the fp16 copies of B and C)
-    size_t best = 0;
-    for (int io = 0; io < 2; ++io) {
-        if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io))
-            return 0;
-        if (pl.total > best) best = pl.total;
-    }
-    return best;
+    ScanPlan pl;  // the layout does not depend on the io type
+    if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, 0)) return 0;
+    return pl.total;
 }
 
 int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
@@ -179,9 +173,8 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
         return SSD_ERR_SHAPE;
     // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
     const int64_t gmax = ((int64_t)1 << 31) - 1;
-    const int64_t prep_groups = (pl.b * pl.h * ((pl.lp + 63) / 64) + 3) / 4 + 2048;
-    if (prep_groups > gmax || pl.b * pl.nc * pl.h > gmax || pl.b * pl.nseg * pl.h > gmax)
-        return SSD_ERR_UNSUPPORTED;
+    const int64_t prep_groups = (pl.b * pl.h * ((pl.lp + 63) / 64) + 3) / 4;
+    if (prep_groups > gmax || pl.b * pl.nc * pl.h > gmax) return SSD_ERR_UNSUPPORTED;
     // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
     // one (batch, head)
     const int64_t lim32 = ((int64_t)1 << 31);

@@ -20,19 +20,13 @@ struct ScanPlan {
     int64_t nsb;  // blocks per chunk (Qp / T)
     int64_t Qp;   // padded rows per chunk
     int64_t lp;   // padded rows per sequence (nc * Qp)
-    int64_t nseg; // segments of the serial chunk pass
-    int64_t cps;  // chunks per segment
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_wgt, off_hb, off_seg, off_dlog, off_lseg, off_bf, off_cf, total;
+    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, total;
 };
-
-// Independent serial chains (batch x head x segment) wanted in the state pass:
-// two resident workgroups on each of the 256 compute units.
-constexpr int64_t kTargetChains = 512;
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-// Heads per workgroup of the serial pass and of the chunk output: 128 /
+// Heads per workgroup of the chunk-state pass and of the chunk output: 128 /
 // head_dim (4 for head_dim <= 32) consecutive heads of one group when the
 // group size is a multiple of that, else 1.
 inline int group_heads(int p, int64_t heads_per_group) {
@@ -51,31 +45,16 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     P.nsb = (Q + P.T - 1) / P.T;
     P.Qp = P.nsb * P.T;
     P.lp = P.nc * P.Qp;
-    const int64_t chains = b * h / group_heads((int)p, h / g);  // workgroups per segment
-    int64_t nseg = chains > 0 ? (kTargetChains + chains - 1) / chains : 1;
-    if (nseg < 1) nseg = 1;
-    if (nseg > P.nc) nseg = P.nc > 0 ? P.nc : 1;
-    P.cps = P.nc > 0 ? (P.nc + nseg - 1) / nseg : 1;
-    P.nseg = P.nc > 0 ? (P.nc + P.cps - 1) / P.cps : 1;
-    const int64_t st = n * p * 4;  // one fp32 state
+    const int64_t st = n * p;  // elements of one state
     size_t o = 0;
     P.off_lcs = o;  o += align256(b * h * P.lp * 4);
     P.off_dtp = o;  o += align256(b * h * P.lp * 4);
     P.off_wgt = o;  o += align256(b * h * P.lp * 4);
-    P.off_hb = o;   o += align256(b * P.nc * h * st);
-    if (P.nseg > 1) {
-        P.off_seg = o;  o += align256(b * P.nseg * h * st);
-        P.off_dlog = o; o += align256(b * h * P.nc * 4);
-        P.off_lseg = o; o += align256(b * h * P.nseg * 4);
-    } else {
-        P.off_seg = P.off_dlog = P.off_lseg = o;
-    }
-    // bf16 io: fp16 copies of B and C (matrix-core operands, shared by the
-    // heads of a group, converted once)
-    P.off_bf = o;
-    if (io == 1) o += align256(b * l * g * n * 2);
-    P.off_cf = o;
-    if (io == 1) o += align256(b * l * g * n * 2);
+    // boundary states: matrix-core operand type (fp16 for bf16 io, fp32 for
+    // fp32 io); room for fp32 so the layout does not depend on the io type
+    P.off_hb = o;   o += align256(b * P.nc * h * st * 4);
+    P.off_st = o;   o += align256(b * P.nc * h * st * 4);  // chunk states, fp32
+    P.off_lam = o;  o += align256(b * h * P.nc * 4);       // chunk log2 decays
     P.total = o;
     return true;
 }

@@ -9,26 +9,26 @@
 // tensor (nnterp, "The state after every token").
 //
 // Rows are handled in blocks of kT = 32 rows that never straddle a chunk
-// boundary.  With lcs_i the cumulative log2 decay inside a block (inclusive)
-// and H the state entering the block:
-//   y_i = sum_{j<=i} (C_i . B_j) 2^(lcs_i - lcs_j) d_j x_j
-//         + 2^lcs_i C_i^T H + D x_i                          (intra + read)
-//   H'  = 2^lcs_last H + sum_j B_j (2^(lcs_last - lcs_j) d_j x_j)^T   (write)
+// boundary; lcs_i is the cumulative log2 decay inside a block (inclusive),
+// lam_K the total of block K.  With Lambda_i the cumulative log2 decay from
+// the chunk start (a sum of block totals plus one lcs) and H_c the state
+// entering chunk c:
+//   S_c     = sum_j 2^(Lambda_last - Lambda_j) d_j B_j x_j^T   (chunk state)
+//   H_{c+1} = 2^(Lambda_last) H_c + S_c                        (state scan)
+//   y_i     = sum_{j<=i} (C_i . B_j) 2^(Lambda_i - Lambda_j) d_j x_j
+//             + 2^Lambda_i C_i^T H_c + D x_i                    (chunk output)
 // Every exponent is <= 0 when A <= 0; the j > i half is removed by a select,
 // so no inf * 0 reaches a result.
 //
 // Launch sequence on one stream:
-//   1. k_prep        d and lcs per block (row a1); on the bf16 path also the
-//                    fp16 matrix-core copies of B and C
-//   2. k_state_pass  chunk states on the matrix cores, serial over chunks
-//                    inside a segment; writes the boundary states (rows a2, a3)
-//   3. k_seg_combine only when the sequence is cut into several segments:
-//                    carries the state across segment ends     (row a3)
-//   4. k_chunk_out   per (batch, chunk, head): intra-chunk masked product,
-//                    read of the boundary state, skip term     (rows a4, a5)
+//   1. k_prep         d, lcs and the state weights per row
+//   2. k_chunk_state  every chunk's state from zero and its total decay,
+//                     all chunks in parallel, on the matrix cores
+//   3. k_state_scan   the serial pass over chunks: boundary states (as the
+//                     read-out's matrix-core operand) and the final state
+//   4. k_chunk_out    per (batch, chunk, heads): intra-chunk masked product,
+//                     read-out of the boundary state, skip term
 #pragma once
-
-#include <type_traits>
 
 #include "ssd_device.hpp"
 #include "ssd_plan.hpp"
@@ -37,98 +37,76 @@ namespace ssd {
 
 constexpr int kT = 32;  // rows per block
 
-// True when the matrix-core operand type differs from the io type (bf16 io,
-// fp16 operands): B and C are then converted once into the workspace.
-template <typename IO>
-constexpr bool kOpCopy = !std::is_same<IO, typename Op<IO>::type>::value;
-
 // Heads of one group handled by one workgroup of the state pass and of the
 // chunk output when the group size allows it (see group_heads in the plan):
 // B and C are staged once for all of them.
 template <int P> constexpr int kGroupHeads = P >= 64 ? 128 / P : 4;
 
 // ----------------------------------------------------------------------------
-// 1. Preparation.
-//    (a) Per padded row R = c Qp + r of every (batch, head), one wave per 64
-//        rows, one row per lane:
-//          dtp[R] = d (0 on padded rows),
-//          lcs[R] = log2(e) sum_{block start..R} A d   (inclusive),
-//          wgt[R] = 2^(lcs[block end] - lcs[R]) d     (weight of row R in the
-//                   state at the end of its block).
-//    (b) bf16 io only: B and C converted once to fp16 for the matrix cores of
-//        every head of the group (exact inside fp16's normal range).
-//    Workgroups [0, na) do (a); the others stride over the pieces of (b).
+// 1. Preparation.  Per padded row R = c Qp + r of every (batch, head), one
+//    wave per 64 rows, one row per lane:
+//      dtp[R] = d (0 on padded rows),
+//      lcs[R] = log2(e) sum_{block start..R} A d   (inclusive),
+//      wgt[R] = 2^(lcs[block end] - lcs[R]) d     (weight of row R in the
+//               state at the end of its block).
 template <typename IO>
 __global__ __launch_bounds__(256) void k_prep(
     const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
     int softplus, float dt_min, float dt_max, int64_t nbatch, int64_t l, int h, int64_t Q,
     int64_t nc, int64_t Qp, float *__restrict__ lcs, float *__restrict__ dtp,
-    float *__restrict__ wgt, int64_t na, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
-    typename Op<IO>::type *__restrict__ Bf, typename Op<IO>::type *__restrict__ Cf,
-    int64_t pieces) {
+    float *__restrict__ wgt) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    if ((int64_t)blockIdx.x < na) {
-        const int64_t lp = nc * Qp, ns = (lp + 63) / 64;
-        const int64_t item = (int64_t)blockIdx.x * kWaves + wave;  // (batch, head, slice)
-        if (item >= nbatch * h * ns) return;
-        const int64_t slice = item % ns, bh = item / ns;
-        const int hh = (int)(bh % h);
-        const int64_t b = bh / h;
-        const int64_t R = slice * 64 + lane;
-        const int64_t c = R / Qp, rp = R % Qp, t = c * Q + rp;
-        float d = 0.f;
-        if (R < lp && rp < Q && t < l)
-            d = time_step(to_f32(dt[(b * l + t) * h + hh]), dt_bias ? dt_bias[hh] : 0.f,
-                          softplus, dt_min, dt_max);
-        float a = A[hh] * kLog2e * d;
-        // inclusive scan inside each 32-lane half (a block: Qp and 64 are
-        // multiples of kT, so blocks start at lane 0 or 32)
+    const int64_t lp = nc * Qp, ns = (lp + 63) / 64;
+    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;  // (batch, head, slice)
+    if (item >= nbatch * h * ns) return;
+    const int64_t slice = item % ns, bh = item / ns;
+    const int hh = (int)(bh % h);
+    const int64_t b = bh / h;
+    const int64_t R = slice * 64 + lane;
+    const int64_t c = R / Qp, rp = R % Qp, t = c * Q + rp;
+    float d = 0.f;
+    if (R < lp && rp < Q && t < l)
+        d = time_step(to_f32(dt[(b * l + t) * h + hh]), dt_bias ? dt_bias[hh] : 0.f, softplus,
+                      dt_min, dt_max);
+    float a = A[hh] * kLog2e * d;
+    // inclusive scan inside each 32-lane half (a block: Qp and 64 are
+    // multiples of kT, so blocks start at lane 0 or 32)
 #pragma unroll
-        for (int off = 1; off < kT; off <<= 1) {
-            const float v = __shfl_up(a, off, kT);
-            if ((lane & (kT - 1)) >= off) a += v;
-        }
-        const float last = __shfl(a, kT - 1, kT);
-        if (R < lp) {
-            lcs[bh * lp + R] = a;
-            dtp[bh * lp + R] = d;
-            wgt[bh * lp + R] = exp2_fast(last - a) * d;
-        }
-        return;
+    for (int off = 1; off < kT; off <<= 1) {
+        const float v = __shfl_up(a, off, kT);
+        if ((lane & (kT - 1)) >= off) a += v;
     }
-    if constexpr (kOpCopy<IO>) {
-        // 8 elements per piece; the pieces of B, then those of C
-        const int64_t stride = ((int64_t)gridDim.x - na) * kThreads;
-        for (int64_t q = ((int64_t)blockIdx.x - na) * kThreads + threadIdx.x; q < 2 * pieces;
-             q += stride) {
-            const bool isB = q < pieces;
-            const int64_t off = (isB ? q : q - pieces) * 8;
-            const Row8v<IO> v = ld_row8((isB ? Bm : Cm) + off);
-            Row8v<f16> o;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2)
-                pack2((float)v.e[e], (float)v.e[e + 1], o.e[e], o.e[e + 1]);
-            st_row8((isB ? Bf : Cf) + off, o);
-        }
+    const float last = __shfl(a, kT - 1, kT);
+    if (R < lp) {
+        lcs[bh * lp + R] = a;
+        dtp[bh * lp + R] = d;
+        wgt[bh * lp + R] = exp2_fast(last - a) * d;
     }
 }
 
+// An io piece of 8 elements -> matrix-core operand piece (bf16 -> fp16:
+// exact inside fp16's normal range).
+__device__ __forceinline__ Row8v<f16> op_piece(const Row8v<bf16> &v) {
+    Row8v<f16> o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) pack2((float)v.e[e], (float)v.e[e + 1], o.e[e], o.e[e + 1]);
+    return o;
+}
+__device__ __forceinline__ Row8v<float> op_piece(const Row8v<float> &v) { return v; }
+
 // ----------------------------------------------------------------------------
-// 2. Chunk states and the serial pass over chunks.
-//    One workgroup per (batch, segment, HPW consecutive heads of one group);
-//    WPH = max(1, head_dim / 32) waves per head, each owning 32 (or head_dim)
-//    head_dim columns of its head's state H (state_dim x head_dim, fp32) in
-//    MFMA accumulators for the whole segment.  Slabs of SLAB row blocks of
-//    one chunk are fetched two ahead into registers (B once for all heads, x
-//    per head) and staged through one LDS buffer.  Per block:
-//        H <- 2^lcs_last H + B^T (w x),  w_j = 2^(lcs_last - lcs_j) d_j,
-//    both operands read k-major through transposing LDS loads.  Before the
-//    first block of every chunk the state is written out, transposed
-//    ([head_dim][state_dim], one 16-byte store per lane and tile), as that
-//    chunk's boundary state.  Segment 0 starts from init_state; later
-//    segments start from zero and are corrected by k_seg_combine and in
-//    k_chunk_out.  The slab position is kept as (chunk, slab of the chunk)
-//    counters, so the loop has no divisions.
+
+// ----------------------------------------------------------------------------
+// 2. Chunk states.  One workgroup per (batch, chunk, HPW consecutive heads of
+//    one group); WPH = max(1, head_dim / 32) waves per head, each owning 32
+//    (or head_dim) head_dim columns of its head's chunk state (state_dim x
+//    head_dim, fp32) in MFMA accumulators.  Slabs of SLAB row blocks are
+//    fetched two ahead into registers (B once for all heads, x per head) and
+//    staged through one LDS buffer.  Per block, from zero at the chunk start:
+//        S <- 2^lam S + B^T (w x),  w_j = 2^(lcs_last - lcs_j) d_j,
+//    both operands read k-major through transposing LDS loads.  The state is
+//    written transposed ([head_dim][state_dim], one 16-byte store per lane
+//    and tile) with the chunk's total log2 decay.
 template <typename IO, int P, int N, int HPW> struct Sp {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
@@ -154,17 +132,16 @@ template <typename IO, int P, int N, int HPW> struct Sp {
 // same loads with empty resources.
 template <typename IO, int P, int N, int HPW> struct SpBuf {
     typedef Sp<IO, P, N, HPW> K;
-    Row8v<typename K::OP> bv[K::KB];
+    Row8v<IO> bv[K::KB];
     Row8v<IO> xv[K::KX];
     float xw[K::KX];            // weight of the x piece's row
     float lam[HPW][K::SLAB];    // log2 decay of each block, per head (uniform)
 };
 
-// Addressing of one workgroup's serial pass.
+// Addressing of one workgroup's chunk.
 template <typename IO> struct SpPtrs {
-    typedef typename Op<IO>::type OP;
     const IO *x;          // row 0 of the sequence, first head of the workgroup
-    const OP *B;          // row 0 of the sequence, the group
+    const IO *B;          // row 0 of the sequence, the group
     const float *lcs;     // (batch, first head) row arrays
     Rsrc rw;              // weights of the workgroup's heads
     int64_t xs, bs;       // row strides (elements) of x and of B
@@ -176,7 +153,6 @@ template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, int bi0, bool live,
                                             const SpPtrs<IO> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
-    typedef typename K::OP OP;
     constexpr int T = kT;
     const int64_t row0 = c * sp.Q + (int64_t)bi0 * T;                  // sequence row
     const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;  // end of the chunk
@@ -184,14 +160,14 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
     valid = valid < 0 ? 0 : (valid > K::SR ? K::SR : valid);
     const int64_t rr0 = valid > 0 ? row0 : 0;
     const Rsrc rx = make_rsrc(sp.x + rr0 * sp.xs, valid * sp.xs * (int64_t)sizeof(IO));
-    const Rsrc rb = make_rsrc(sp.B + rr0 * sp.bs, valid * sp.bs * (int64_t)sizeof(OP));
+    const Rsrc rb = make_rsrc(sp.B + rr0 * sp.bs, valid * sp.bs * (int64_t)sizeof(IO));
     const int64_t R0 = live ? (c * sp.nsb + bi0) * T : 0;             // padded row of the slab
 #pragma unroll
     for (int k = 0; k < K::KB; ++k) {
         const int q = tid + k * K::NT;
         if (K::NPB % K::NT == 0 || q < K::NPB) {
             const int j = q / (N / 8), cc = q % (N / 8);
-            f.bv[k] = buf_row8<OP>(rb, (uint32_t)(j * sp.bs + cc * 8) * (uint32_t)sizeof(OP));
+            f.bv[k] = buf_row8<IO>(rb, (uint32_t)(j * sp.bs + cc * 8) * (uint32_t)sizeof(IO));
         }
     }
 #pragma unroll
@@ -224,7 +200,7 @@ __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f,
     for (int k = 0; k < K::KB; ++k) {
         const int q = tid + k * K::NT;
         if (K::NPB % K::NT == 0 || q < K::NPB)
-            st_row8(Bs + (q / (N / 8)) * K::LDB + (q % (N / 8)) * 8, f.bv[k]);
+            st_row8(Bs + (q / (N / 8)) * K::LDB + (q % (N / 8)) * 8, op_piece(f.bv[k]));
     }
 #pragma unroll
     for (int k = 0; k < K::KX; ++k) {
@@ -282,33 +258,29 @@ __device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type
     }
 }
 
+
 template <typename IO, int P, int N, int HPW>
-__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_state_pass(
-    const IO *__restrict__ x, const typename Op<IO>::type *__restrict__ Bm,
-    const float *__restrict__ lcs, const float *__restrict__ wgt, const float *__restrict__ init,
-    float *__restrict__ Hb, float *__restrict__ Eseg, float *__restrict__ Dlog,
-    float *__restrict__ Lseg, float *__restrict__ final_state, int64_t l, int h, int g, int64_t Q,
-    int64_t nc, int64_t Qp, int64_t cps, int64_t nseg) {
+__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
+    const IO *__restrict__ x, const IO *__restrict__ Bm, const float *__restrict__ lcs,
+    const float *__restrict__ wgt, float *__restrict__ St, float *__restrict__ Lam, int64_t l,
+    int h, int g, int64_t Q, int64_t nc, int64_t Qp) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
-    constexpr int T = kT, SLAB = K::SLAB, TPW = K::TPW, RT = K::RT, CPW = K::CPW;
+    constexpr int T = kT, SLAB = K::SLAB, TPW = K::TPW;
     __shared__ __attribute__((aligned(16))) OP lds[K::BUF];
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
     const int hq = (int)(item % (h / HPW)); item /= (h / HPW);
-    const int64_t seg = item % nseg;
-    const int64_t b = item / nseg;
+    const int64_t c = item % nc;
+    const int64_t b = item / nc;
     const int hh0 = hq * HPW;
     const int gi = hh0 / (h / g);
     const int hs = wave / K::WPH;                  // this wave's head slot
     const int hh = hh0 + hs;
     const int c0 = (wave % K::WPH) * K::PW;        // this wave's first column
     const int nsb = (int)(Qp / T);
-    const int nspc = (nsb + SLAB - 1) / SLAB;      // slabs per chunk
-    const int64_t ca = seg * cps;
-    const int64_t cb = (ca + cps < nc) ? ca + cps : nc;
-    const int64_t nslab = (cb - ca) * nspc;
+    const int nspc = (nsb + SLAB - 1) / SLAB;      // slabs of the chunk
     const int64_t NP = (int64_t)N * P;
     SpPtrs<IO> sp;
     sp.xs = (int64_t)h * P;
@@ -321,129 +293,107 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_state_pass(
     sp.l = l;
     sp.Q = Q;
     sp.nsb = nsb;
-    float *Hb_h = Hb + (b * nc * h + hh) * NP;      // chunk c at Hb_h + c * h * NP
-    float *Dlog_h = Dlog + (b * h + hh) * nc;
 
     f32x4 acc[TPW];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) acc[k] = zero4();
-    if (seg == 0 && init) {  // [state_dim][head_dim]
-        const float *src = init + (b * h + hh) * NP;
-#pragma unroll
-        for (int u = 0; u < CPW; ++u)
-#pragma unroll
-            for (int tr = 0; tr < RT; ++tr)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[u * RT + tr][r] =
-                        src[(tr * 16 + 4 * (lane >> 4) + r) * P + c0 + 16 * u + (lane & 15)];
-    }
     float logdec = 0.f;
 
-    // apply position (ac, ak) and prefetch position (pc, pk), two slabs ahead
-    int64_t ac = ca, pc = ca;
-    int ak = 0, pk = 0;
     SpBuf<IO, P, N, HPW> pa, pb;
-    sp_prefetch(pa, pc, pk * SLAB, nslab > 0, sp, tid);
-    if (++pk == nspc) { pk = 0; ++pc; }
-    sp_prefetch(pb, pc, pk * SLAB, nslab > 1, sp, tid);
-    if (++pk == nspc) { pk = 0; ++pc; }
-    for (int64_t si = 0; si < nslab; si += 2) {
+    sp_prefetch(pa, c, 0, true, sp, tid);
+    sp_prefetch(pb, c, SLAB, nspc > 1, sp, tid);
+    for (int si = 0; si < nspc; si += 2) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             SpBuf<IO, P, N, HPW> &pf = half == 0 ? pa : pb;
-            const bool live = si + half < nslab;
-            const int bi0 = ak * SLAB;
+            const int k = si + half;
+            const bool live = k < nspc;
+            const int bi0 = k * SLAB;
             const int nb = live ? (nsb - bi0 < SLAB ? nsb - bi0 : SLAB) : 0;
             float lam[SLAB];
 #pragma unroll
             for (int jb = 0; jb < SLAB; ++jb) {
                 float v = pf.lam[0][jb];
 #pragma unroll
-                for (int k = 1; k < HPW; ++k) v = hs == k ? pf.lam[k][jb] : v;
+                for (int q = 1; q < HPW; ++q) v = hs == q ? pf.lam[q][jb] : v;
                 lam[jb] = v;
             }
             lds_barrier();  // the previous slab's reads are done
             sp_stage(pf, lds, tid);
-            sp_prefetch(pf, pc, pk * SLAB, si + half + 2 < nslab, sp, tid);
-            if (++pk == nspc) { pk = 0; ++pc; }
+            sp_prefetch(pf, c, (k + 2) * SLAB, k + 2 < nspc, sp, tid);
             lds_barrier();
-            if (live && ak == 0) {  // first slab of a chunk: emit the boundary state
-                sp_store_t<IO, P, N, HPW>(Hb_h + ac * h * NP, acc, c0, lane);
-                if (nseg > 1 && lane == 0) Dlog_h[ac] = logdec;
-            }
             sp_apply<IO, P, N, HPW>(acc, lds, nb, lam, hs, c0, lane);
 #pragma unroll
             for (int jb = 0; jb < SLAB; ++jb) logdec += jb < nb ? lam[jb] : 0.f;
-            if (++ak == nspc) { ak = 0; ++ac; }
         }
     }
-
-    if (nseg == 1) {  // the final state, [state_dim][head_dim]
-        if (final_state) {
-            float *out = final_state + (b * h + hh) * NP;
-#pragma unroll
-            for (int u = 0; u < CPW; ++u)
-#pragma unroll
-                for (int tr = 0; tr < RT; ++tr)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        out[(tr * 16 + 4 * (lane >> 4) + r) * P + c0 + 16 * u + (lane & 15)] =
-                            acc[u * RT + tr][r];
-        }
-    } else {  // the segment's state from its start, transposed like Hb
-        sp_store_t<IO, P, N, HPW>(Eseg + ((b * nseg + seg) * h + hh) * NP, acc, c0, lane);
-        if (lane == 0) Lseg[(b * h + hh) * nseg + seg] = logdec;
-    }
+    sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
+    if (c0 == 0 && lane == 0) Lam[(b * h + hh) * nc + c] = logdec;
 }
 
 // ----------------------------------------------------------------------------
-// 3. Segment combine: the state entering segment k (k >= 1) is
-//        Hin_{k+1} = 2^L_k Hin_k + E_k,   Hin_1 = E_0,
-//    with E_k the state segment k reaches from zero (segment 0: from the
-//    initial state) and L_k its total log2 decay.  Hin_k overwrites slot
-//    k - 1 of Eseg; the state after the last segment is the final state.
-//    Segment states are stored transposed ([head_dim][state_dim]); the final
-//    state is written in the [state_dim][head_dim] layout of the interface.
+// 3. State scan: the serial pass over chunks,
+//        H_0 = init (or 0),   H_{c+1} = 2^L_c H_c + S_c,
+//    with S_c and L_c from k_chunk_state.  H_c is stored as chunk c's
+//    boundary state in the read-out's matrix-core operand type (fp16 rounded
+//    to nearest on the bf16 path, fp32 on the fp32 path), transposed
+//    ([head_dim][state_dim]); the state after the last chunk is the final
+//    state ([state_dim][head_dim]).  The recurrence itself runs in fp32.
 //    One thread per 4 consecutive state elements of one (batch, head); the
-//    segment states are loaded in groups of 8 before any of them is used.
-static __global__ __launch_bounds__(256) void k_seg_combine(float *__restrict__ Eseg,
-                                                            const float *__restrict__ Lseg,
-                                                            float *__restrict__ final_state,
-                                                            int64_t bh, int h, int64_t nseg,
-                                                            int n, int p) {
+//    chunk states are loaded 8 chunks ahead of their use.
+__device__ __forceinline__ void store_state4(f16 *p, const f32x4 &v) {
+    *reinterpret_cast<f16x4 *>(p) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+}
+__device__ __forceinline__ void store_state4(float *p, const f32x4 &v) {
+    *reinterpret_cast<f32x4 *>(p) = v;
+}
+
+template <typename OP>
+__global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St,
+                                                    const float *__restrict__ Lam,
+                                                    const float *__restrict__ init,
+                                                    OP *__restrict__ Hb,
+                                                    float *__restrict__ final_state, int64_t bh,
+                                                    int h, int64_t nc, int n, int p) {
     constexpr int G8 = 8;
     const int64_t np4 = (int64_t)n * p / 4;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= bh * np4) return;
     const int64_t pair = idx / np4, e4 = idx % np4;
     const int64_t b = pair / h, hh = pair % h;
-    f32x4 *E = reinterpret_cast<f32x4 *>(Eseg) + (b * nseg * h + hh) * np4 + e4;
-    const int64_t stride = (int64_t)h * np4;  // from one segment slot to the next
-    f32x4 H = E[0];
-    for (int64_t k0 = 1; k0 < nseg; k0 += G8) {
-        f32x4 Ek[G8];
+    // element e of this thread: head_dim column pc, state row n0 + e
+    const int64_t pc = (e4 * 4) / n, n0 = (e4 * 4) % n;
+    f32x4 H = zero4();
+    if (init) {
+        const float *src = init + pair * (int64_t)n * p + n0 * p + pc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) H[e] = src[e * p];
+    }
+    const int64_t cstride = (int64_t)h * np4;  // from one chunk to the next, in f32x4
+    const f32x4 *S = reinterpret_cast<const f32x4 *>(St) + (b * nc * h + hh) * np4 + e4;
+    OP *dst = Hb + ((b * nc * h + hh) * np4 + e4) * 4;
+    const float *L = Lam + pair * nc;
+    for (int64_t k0 = 0; k0 < nc; k0 += G8) {
+        f32x4 Sk[G8];
         float Lk[G8];
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
-            const int64_t k = k0 + u < nseg ? k0 + u : nseg - 1;
-            Ek[u] = E[k * stride];
-            Lk[u] = Lseg[pair * nseg + k];
+            const int64_t k = k0 + u < nc ? k0 + u : nc - 1;
+            Sk[u] = S[k * cstride];
+            Lk[u] = L[k];
         }
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
-            if (k0 + u < nseg) {
-                E[(k0 + u - 1) * stride] = H;      // Hin_k, k = k0 + u
-                H = exp2_fast(Lk[u]) * H + Ek[u];  // Hin_{k+1}
+            if (k0 + u < nc) {
+                store_state4(dst + (k0 + u) * cstride * 4, H);
+                H = exp2_fast(Lk[u]) * H + Sk[u];
             }
         }
     }
     if (final_state) {
-        // element e of this thread: head_dim column pc, state row n0 + e
-        const int64_t pc = (e4 * 4) / n, n0 = (e4 * 4) % n;
-        float *dst = final_state + pair * (int64_t)n * p + n0 * p + pc;
+        float *o = final_state + pair * (int64_t)n * p + n0 * p + pc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e * p] = H[e];
+        for (int e = 0; e < 4; ++e) o[e * p] = H[e];
     }
 }
 
@@ -501,7 +451,7 @@ struct alignas(16) CoRows {
 template <typename IO, int P, int N, int HPW> struct CoBuf {
     typedef Co<IO, P, N, HPW> K;
     typedef typename K::OP OP;
-    Row8v<OP> cv[K::KC], bv[K::KC];
+    Row8v<IO> cv[K::KC], bv[K::KC];
     Row8v<IO> xv[K::KX];
     float ls, ds, ws, l15;  // row factors of (head tid / kT, row tid % kT)
 };
@@ -510,7 +460,7 @@ template <typename IO, int P, int N, int HPW> struct CoBuf {
 template <typename IO> struct CoPtrs {
     typedef typename Op<IO>::type OP;
     const IO *x;        // row 0 of the chunk, first head of the workgroup
-    const OP *B, *C;    // row 0 of the chunk, the group
+    const IO *B, *C;    // row 0 of the chunk, the group
     IO *y;
     Rsrc rl, rd, rw;    // lcs, d, weights: the workgroup's heads, this chunk
     int64_t xs, bs;     // row strides (elements) of x / y and of B / C
@@ -528,17 +478,17 @@ __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, cons
     int valid = cp.rows - r0;
     valid = valid < 0 ? 0 : (valid > T ? T : valid);
     const int rr0 = valid > 0 ? r0 : 0;
-    const Rsrc rb = make_rsrc(cp.B + rr0 * cp.bs, (int64_t)valid * cp.bs * (int)sizeof(OP));
-    const Rsrc rc = make_rsrc(cp.C + rr0 * cp.bs, (int64_t)valid * cp.bs * (int)sizeof(OP));
+    const Rsrc rb = make_rsrc(cp.B + rr0 * cp.bs, (int64_t)valid * cp.bs * (int)sizeof(IO));
+    const Rsrc rc = make_rsrc(cp.C + rr0 * cp.bs, (int64_t)valid * cp.bs * (int)sizeof(IO));
     const Rsrc rx = make_rsrc(cp.x + rr0 * cp.xs, (int64_t)valid * cp.xs * (int)sizeof(IO));
 #pragma unroll
     for (int k = 0; k < K::KC; ++k) {
         const int q = tid + k * K::NT;
         if (K::NPC % K::NT == 0 || q < K::NPC) {
             const int j = q / (N / 8), cc = q % (N / 8);
-            const uint32_t off = (uint32_t)(j * cp.bs + cc * 8) * (uint32_t)sizeof(OP);
-            f.cv[k] = buf_row8<OP>(rc, off);
-            f.bv[k] = buf_row8<OP>(rb, off);
+            const uint32_t off = (uint32_t)(j * cp.bs + cc * 8) * (uint32_t)sizeof(IO);
+            f.cv[k] = buf_row8<IO>(rc, off);
+            f.bv[k] = buf_row8<IO>(rb, off);
         }
     }
 #pragma unroll
@@ -560,15 +510,6 @@ __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, cons
     f.l15 = buf_f32(cp.rl, (uint32_t)hs * cp.hstride + 15u * 4u, soff);
 }
 
-// x piece -> operand piece (bf16 -> fp16 exact in fp16's normal range).
-__device__ __forceinline__ Row8v<f16> op_piece(const Row8v<bf16> &v) {
-    Row8v<f16> o;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) pack2((float)v.e[e], (float)v.e[e + 1], o.e[e], o.e[e + 1]);
-    return o;
-}
-__device__ __forceinline__ Row8v<float> op_piece(const Row8v<float> &v) { return v; }
-
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
                                          typename Op<IO>::type *buf, CoRows *rows, int tid) {
@@ -581,8 +522,8 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
         const int q = tid + k * K::NT;
         if (K::NPC % K::NT == 0 || q < K::NPC) {
             const int r = q / (N / 8), c0 = (q % (N / 8)) * 8;
-            swz_store8<OP, N>(Cs, r, c0, f.cv[k]);
-            swz_store8<OP, N>(Bs, r, c0, f.bv[k]);
+            swz_store8<OP, N>(Cs, r, c0, op_piece(f.cv[k]));
+            swz_store8<OP, N>(Bs, r, c0, op_piece(f.bv[k]));
         }
     }
 #pragma unroll
@@ -812,12 +753,10 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
 
 template <typename IO, int P, int N, int HPW>
 __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
-    const IO *__restrict__ x, const typename Op<IO>::type *__restrict__ Bm,
-    const typename Op<IO>::type *__restrict__ Cm, const float *__restrict__ D,
-    const float *__restrict__ lcs, const float *__restrict__ dtp, const float *__restrict__ wgt,
-    const float *__restrict__ Hb, const float *__restrict__ Hin, const float *__restrict__ Dlog,
-    IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp, int64_t cps,
-    int64_t nseg) {
+    const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
+    const float *__restrict__ D, const float *__restrict__ lcs, const float *__restrict__ dtp,
+    const float *__restrict__ wgt, const typename Op<IO>::type *__restrict__ Hb,
+    IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp) {
     typedef Co<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
@@ -835,7 +774,6 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     const int hs = wave / WPH;               // this wave's head slot
     const int hh = hh0 + hs;
     const int c0 = (wave % WPH) * K::PW;     // this wave's first column
-    const int64_t seg = c / cps;
     const int64_t NP = (int64_t)N * P;
     const int64_t t0 = c * Q;
     CoPtrs<IO> cp;
@@ -856,29 +794,26 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     const float Dh = D ? D[hh] : 0.f;
 
     // ---- the wave's state columns entering the chunk: the boundary state,
-    //      plus (later segments) the decayed state entering the segment.
-    //      Both are stored transposed ([head_dim][state_dim]), so a lane's 4
-    //      accumulator values (consecutive state rows) are one 16-byte load
+    //      stored transposed ([head_dim][state_dim]) in the operand type, so
+    //      a lane's 4 accumulator values (consecutive state rows) are one load
     f32x4 accH[CPW * RT];
     {
-        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * 4);
-        const Rsrc ri = make_rsrc(Hin + (seg > 0 ? ((b * nseg + seg - 1) * h + hh) * NP : 0),
-                                  seg > 0 ? NP * 4 : 0);
-        f32x4 iv[CPW * RT];
+        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * (int64_t)sizeof(OP));
 #pragma unroll
         for (int u = 0; u < CPW; ++u)
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) {
-                const uint32_t off =
-                    (uint32_t)((c0 + co_col<CPW>(u, li)) * N + tr * 16 + 4 * lg) * 4u;
-                accH[u * RT + tr] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
-                iv[u * RT + tr] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off, 0, 0));
+                const uint32_t off = (uint32_t)((c0 + co_col<CPW>(u, li)) * N + tr * 16 + 4 * lg) *
+                                     (uint32_t)sizeof(OP);
+                if constexpr (sizeof(OP) == 2) {
+                    const f16x4 v = __builtin_bit_cast(
+                        f16x4, __builtin_amdgcn_raw_buffer_load_b64(rh, off, 0, 0));
+                    accH[u * RT + tr] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+                } else {
+                    accH[u * RT + tr] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+                }
             }
-        const float corr = seg > 0 ? exp2_fast(Dlog[(b * h + hh) * nc + c]) : 0.f;
-#pragma unroll
-        for (int k = 0; k < CPW * RT; ++k) accH[k] += corr * iv[k];
     }
 
     // Block k is fetched into registers pa (k even) or pb (k odd) two blocks
@@ -916,76 +851,60 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     float *lcs = reinterpret_cast<float *>(a.ws + pl.off_lcs);
     float *dtp = reinterpret_cast<float *>(a.ws + pl.off_dtp);
     float *wgt = reinterpret_cast<float *>(a.ws + pl.off_wgt);
-    float *Hb = reinterpret_cast<float *>(a.ws + pl.off_hb);
-    float *Eseg = reinterpret_cast<float *>(a.ws + pl.off_seg);
-    float *Dlog = reinterpret_cast<float *>(a.ws + pl.off_dlog);
-    float *Lseg = reinterpret_cast<float *>(a.ws + pl.off_lseg);
+    OP *Hb = reinterpret_cast<OP *>(a.ws + pl.off_hb);
+    float *St = reinterpret_cast<float *>(a.ws + pl.off_st);
+    float *Lam = reinterpret_cast<float *>(a.ws + pl.off_lam);
     const IO *x = static_cast<const IO *>(a.x);
     const IO *dt = static_cast<const IO *>(a.dt);
     const IO *Bm = static_cast<const IO *>(a.B);
     const IO *Cm = static_cast<const IO *>(a.C);
     IO *y = static_cast<IO *>(a.y);
     const int h = (int)pl.h, g = (int)pl.g;
-    // matrix-core operands B and C: the fp16 copies, or the fp32 inputs
-    OP *Bf = reinterpret_cast<OP *>(a.ws + pl.off_bf);
-    OP *Cf = reinterpret_cast<OP *>(a.ws + pl.off_cf);
-    const OP *Bop = kOpCopy<IO> ? Bf : reinterpret_cast<const OP *>(Bm);
-    const OP *Cop = kOpCopy<IO> ? Cf : reinterpret_cast<const OP *>(Cm);
 
     const int64_t ns = (pl.lp + 63) / 64;
     const int64_t na = (pl.b * pl.h * ns + kWaves - 1) / kWaves;
-    const int64_t pieces = pl.b * pl.l * pl.g * pl.n / 8;
-    int64_t ncopy = 0;
-    if (kOpCopy<IO>) {
-        ncopy = (2 * pieces + kThreads - 1) / kThreads;
-        if (ncopy > 2048) ncopy = 2048;
-    }
     trace_begin(0, s);
-    hipLaunchKernelGGL(k_prep<IO>, dim3((unsigned)(na + ncopy)), dim3(kThreads), 0, s, dt, a.A,
-                       a.dt_bias, a.softplus, a.dt_min, a.dt_max, pl.b, pl.l, h, pl.Q, pl.nc,
-                       pl.Qp, lcs, dtp, wgt, na, Bm, Cm, Bf, Cf, pieces);
+    hipLaunchKernelGGL(k_prep<IO>, dim3((unsigned)na), dim3(kThreads), 0, s, dt, a.A, a.dt_bias,
+                       a.softplus, a.dt_min, a.dt_max, pl.b, pl.l, h, pl.Q, pl.nc, pl.Qp, lcs,
+                       dtp, wgt);
     trace_end(0, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    trace_begin(1, s);
     constexpr int HP = kGroupHeads<P>;
-    const int hpw = group_heads((int)P, h / g);  // HP or 1
-    if (hpw == HP && HP > 1)
-        hipLaunchKernelGGL((k_state_pass<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nseg * (h / HP))),
-                           dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bop, lcs, wgt, a.init, Hb, Eseg,
-                           Dlog, Lseg, a.final_state, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps,
-                           pl.nseg);
+    const bool grouped = HP > 1 && group_heads((int)P, h / g) == HP;
+    trace_begin(1, s);
+    if (grouped)
+        hipLaunchKernelGGL((k_chunk_state<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
+                           dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bm, lcs, wgt, St, Lam, pl.l, h, g,
+                           pl.Q, pl.nc, pl.Qp);
     else
-        hipLaunchKernelGGL((k_state_pass<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nseg * h)),
-                           dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bop, lcs, wgt, a.init, Hb, Eseg,
-                           Dlog, Lseg, a.final_state, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps,
-                           pl.nseg);
+        hipLaunchKernelGGL((k_chunk_state<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
+                           dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bm, lcs, wgt, St, Lam, pl.l, h, g,
+                           pl.Q, pl.nc, pl.Qp);
     trace_end(1, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    if (pl.nseg > 1) {
-        const int64_t np4 = (int64_t)N * P / 4;
-        const int64_t tot = pl.b * pl.h * np4;
-        trace_begin(2, s);
-        hipLaunchKernelGGL(k_seg_combine, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, s, Eseg, Lseg, a.final_state, pl.b * pl.h, h,
-                           pl.nseg, N, P);
-        trace_end(2, s);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const int64_t np4 = (int64_t)N * P / 4;
+    const int64_t tot = pl.b * pl.h * np4;
+    trace_begin(2, s);
+    hipLaunchKernelGGL(k_state_scan<OP>, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h,
+                       pl.nc, N, P);
+    trace_end(2, s);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
 
     trace_begin(3, s);
-    if (hpw == HP && HP > 1)
+    if (grouped)
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
-                           dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb,
-                           Eseg, Dlog, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
+                           dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb,
+                           y, pl.l, h, g, pl.Q, pl.nc, pl.Qp);
     else
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
-                           dim3(Co<IO, P, N, 1>::NT), 0, s, x, Bop, Cop, a.D, lcs, dtp, wgt, Hb,
-                           Eseg, Dlog, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, pl.cps, pl.nseg);
+                           dim3(Co<IO, P, N, 1>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb, y,
+                           pl.l, h, g, pl.Q, pl.nc, pl.Qp);
     trace_end(3, s);
     return hipGetLastError();
 }

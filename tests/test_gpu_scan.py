@@ -228,10 +228,10 @@ def _ws_layout(b, l, h, Q, io):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_stage_intermediates(orc, io):
-    """Row a1 (time step, cumulative log decay) and row a3 (boundary states)
-    read back from the workspace, against the chunked fp64 steps.  The shape
-    has 2048 (batch, head) pairs, which the library never cuts into segments,
-    so the stored boundary states are the final ones."""
+    """The per-row time step, cumulative log decay and state weights, and the
+    boundary states, read back from the workspace, against the chunked fp64
+    steps.  Boundary states are stored as the read-out's operand: fp16 on
+    the bf16 path, fp32 on the fp32 path."""
     import mamba_ssd_chunked_chunk_amd as ssd
     from oracle import chunked
     torch = torch_mod()
@@ -252,7 +252,11 @@ def test_stage_intermediates(orc, io):
     wgt = wsf[off_wgt // 4: off_wgt // 4 + b * h * lp].view(b, h, nc, Qp)[..., :Q] \
         .reshape(b, h, nc * Q)[..., :l]
     # boundary states are stored transposed: [b, chunks, heads, head_dim, state_dim]
-    hb = wsf[off_hb // 4: off_hb // 4 + b * nc * h * n * p].view(b, nc, h, p, n).transpose(3, 4)
+    if io == "bf16":
+        hb = ws[off_hb: off_hb + 2 * b * nc * h * n * p].view(torch.float16).float()
+    else:
+        hb = wsf[off_hb // 4: off_hb // 4 + b * nc * h * n * p]
+    hb = hb.view(b, nc, h, p, n).transpose(3, 4)
     _, _, inter = chunked.chunked_scan(**oracle_kw(inp), chunk=Q)
     check_close(to_f64(dtp), inter["d"], "f32", "processed time step")
     # per-chunk cumsum (natural log) == lcs / log2(e) since blocks == chunks
