@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD scan tokens/sec at 1 GPU; % of MFMA/HBM roofline; decode steps/sec"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_IDS = ("prep", "chunk_state", "state_scan", "chunk_out")
+KERNEL_IDS = ("chunk_state", "state_scan", "chunk_out")
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan.hpp",
                   "mamba_ssd_chunked_chunk_amd/csrc/ssd_device.hpp",
@@ -83,12 +83,10 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
     so = 2 if s == 2 else 4            # boundary-state element
     st = b * nc * h * n * p            # elements of all chunk (or boundary) states
     fin = b * h * n * p * 4 if final else 0
-    if name == "prep":
-        # dt read; lcs, d and weights written
-        return th * s + 3 * rows
     if name == "chunk_state":
-        # x, B and the row weights read, chunk states and decays written
-        return x + BC + rows + 4 * st + b * h * nc * 4
+        # x, B and dt read; the per-row lcs, d and weights, the chunk states
+        # and decays written
+        return x + BC + th * s + 3 * rows + 4 * st + b * h * nc * 4
     if name == "state_scan":
         # chunk states and decays read, boundary states written
         return 4 * st + b * h * nc * 4 + so * st + fin

@@ -165,8 +165,9 @@ int32_t ssd_abi_version(void);
  * clears that kernel's record.  Not thread-safe with concurrent scan calls.
  */
 enum ssd_kernel_id {
-    SSD_K_PREP = 0,        /* time step, per-block cumulative log decay, state weights */
-    SSD_K_CHUNK_STATE = 1, /* every chunk's state from zero, in parallel */
+    SSD_K_PREP = 0,        /* reserved: the per-row time step, cumulative log decay
+                              and state weights are computed inside SSD_K_CHUNK_STATE */
+    SSD_K_CHUNK_STATE = 1, /* per-row values; every chunk's state from zero, in parallel */
     SSD_K_STATE_SCAN = 2,  /* serial pass over chunks: boundary and final states */
     SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */
     SSD_K_STEP = 4,        /* decode step */

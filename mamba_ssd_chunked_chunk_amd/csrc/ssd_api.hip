@@ -173,8 +173,8 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
         return SSD_ERR_SHAPE;
     // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
     const int64_t gmax = ((int64_t)1 << 31) - 1;
-    const int64_t prep_groups = (pl.b * pl.h * ((pl.lp + 63) / 64) + 3) / 4;
-    if (prep_groups > gmax || pl.b * pl.nc * pl.h > gmax) return SSD_ERR_UNSUPPORTED;
+    if (pl.b * pl.nc * pl.h > gmax || pl.b * pl.h * pl.n * pl.p / 4 / 256 + 1 > gmax)
+        return SSD_ERR_UNSUPPORTED;
     // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
     // one (batch, head)
     const int64_t lim32 = ((int64_t)1 << 31);

@@ -298,40 +298,6 @@ template <typename T> __device__ __forceinline__ void st_row8(T *dst, const Row8
     *reinterpret_cast<Row8v<T> *>(dst) = v;
 }
 
-// An x piece as the two operand pieces x and w x.  bf16 -> fp16 is exact for
-// values in fp16's normal range (round toward zero changes nothing there);
-// w x is rounded toward zero.
-__device__ __forceinline__ void x_pieces(const Row8v<bf16> &v, float w, Row8v<f16> &xo,
-                                         Row8v<f16> &wo) {
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-        const float a = (float)v.e[e], b = (float)v.e[e + 1];
-        pack2(a, b, xo.e[e], xo.e[e + 1]);
-        pack2(a * w, b * w, wo.e[e], wo.e[e + 1]);
-    }
-}
-__device__ __forceinline__ void x_pieces(const Row8v<float> &v, float w, Row8v<float> &xo,
-                                         Row8v<float> &wo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        xo.e[e] = v.e[e];
-        wo.e[e] = v.e[e] * w;
-    }
-}
-// w x only.
-__device__ __forceinline__ Row8v<f16> wx_piece(const Row8v<bf16> &v, float w) {
-    Row8v<f16> o;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) pack2((float)v.e[e] * w, (float)v.e[e + 1] * w, o.e[e], o.e[e + 1]);
-    return o;
-}
-__device__ __forceinline__ Row8v<float> wx_piece(const Row8v<float> &v, float w) {
-    Row8v<float> o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o.e[e] = v.e[e] * w;
-    return o;
-}
-
 // ------------------------------------------------------ buffer access ----
 // Raw buffer resources: loads whose offset lies at or beyond the resource's
 // byte size return zeros and such stores are dropped, so rows past the end of

@@ -21,12 +21,12 @@
 // so no inf * 0 reaches a result.
 //
 // Launch sequence on one stream:
-//   1. k_prep         d, lcs and the state weights per row
-//   2. k_chunk_state  every chunk's state from zero and its total decay,
-//                     all chunks in parallel, on the matrix cores
-//   3. k_state_scan   the serial pass over chunks: boundary states (as the
+//   1. k_chunk_state  per row: d, lcs and the state weights; every chunk's
+//                     state from zero and its total decay, all chunks in
+//                     parallel, on the matrix cores
+//   2. k_state_scan   the serial pass over chunks: boundary states (as the
 //                     read-out's matrix-core operand) and the final state
-//   4. k_chunk_out    per (batch, chunk, heads): intra-chunk masked product,
+//   3. k_chunk_out    per (batch, chunk, heads): intra-chunk masked product,
 //                     read-out of the boundary state, skip term
 #pragma once
 
@@ -43,47 +43,6 @@ constexpr int kT = 32;  // rows per block
 template <int P> constexpr int kGroupHeads = P >= 64 ? 128 / P : 4;
 
 // ----------------------------------------------------------------------------
-// 1. Preparation.  Per padded row R = c Qp + r of every (batch, head), one
-//    wave per 64 rows, one row per lane:
-//      dtp[R] = d (0 on padded rows),
-//      lcs[R] = log2(e) sum_{block start..R} A d   (inclusive),
-//      wgt[R] = 2^(lcs[block end] - lcs[R]) d     (weight of row R in the
-//               state at the end of its block).
-template <typename IO>
-__global__ __launch_bounds__(256) void k_prep(
-    const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
-    int softplus, float dt_min, float dt_max, int64_t nbatch, int64_t l, int h, int64_t Q,
-    int64_t nc, int64_t Qp, float *__restrict__ lcs, float *__restrict__ dtp,
-    float *__restrict__ wgt) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int64_t lp = nc * Qp, ns = (lp + 63) / 64;
-    const int64_t item = (int64_t)blockIdx.x * kWaves + wave;  // (batch, head, slice)
-    if (item >= nbatch * h * ns) return;
-    const int64_t slice = item % ns, bh = item / ns;
-    const int hh = (int)(bh % h);
-    const int64_t b = bh / h;
-    const int64_t R = slice * 64 + lane;
-    const int64_t c = R / Qp, rp = R % Qp, t = c * Q + rp;
-    float d = 0.f;
-    if (R < lp && rp < Q && t < l)
-        d = time_step(to_f32(dt[(b * l + t) * h + hh]), dt_bias ? dt_bias[hh] : 0.f, softplus,
-                      dt_min, dt_max);
-    float a = A[hh] * kLog2e * d;
-    // inclusive scan inside each 32-lane half (a block: Qp and 64 are
-    // multiples of kT, so blocks start at lane 0 or 32)
-#pragma unroll
-    for (int off = 1; off < kT; off <<= 1) {
-        const float v = __shfl_up(a, off, kT);
-        if ((lane & (kT - 1)) >= off) a += v;
-    }
-    const float last = __shfl(a, kT - 1, kT);
-    if (R < lp) {
-        lcs[bh * lp + R] = a;
-        dtp[bh * lp + R] = d;
-        wgt[bh * lp + R] = exp2_fast(last - a) * d;
-    }
-}
-
 // An io piece of 8 elements -> matrix-core operand piece (bf16 -> fp16:
 // exact inside fp16's normal range).
 __device__ __forceinline__ Row8v<f16> op_piece(const Row8v<bf16> &v) {
@@ -95,18 +54,26 @@ __device__ __forceinline__ Row8v<f16> op_piece(const Row8v<bf16> &v) {
 __device__ __forceinline__ Row8v<float> op_piece(const Row8v<float> &v) { return v; }
 
 // ----------------------------------------------------------------------------
-
-// ----------------------------------------------------------------------------
-// 2. Chunk states.  One workgroup per (batch, chunk, HPW consecutive heads of
-//    one group); WPH = max(1, head_dim / 32) waves per head, each owning 32
-//    (or head_dim) head_dim columns of its head's chunk state (state_dim x
-//    head_dim, fp32) in MFMA accumulators.  Slabs of SLAB row blocks are
-//    fetched two ahead into registers (B once for all heads, x per head) and
-//    staged through one LDS buffer.  Per block, from zero at the chunk start:
-//        S <- 2^lam S + B^T (w x),  w_j = 2^(lcs_last - lcs_j) d_j,
-//    both operands read k-major through transposing LDS loads.  The state is
-//    written transposed ([head_dim][state_dim], one 16-byte store per lane
-//    and tile) with the chunk's total log2 decay.
+// 1. Chunk states, with the per-row preparation folded in.  One workgroup
+//    per (batch, chunk, HPW consecutive heads of one group); WPH = max(1,
+//    head_dim / 32) waves per head, each owning 32 (or head_dim) head_dim
+//    columns of its head's chunk state (state_dim x head_dim, fp32) in MFMA
+//    accumulators.  Slabs of SLAB = 2 row blocks are fetched two ahead into
+//    registers (B once for all heads, x and the raw time steps per head) and
+//    staged through one LDS buffer.  While a slab is staged, waves 0 .. HPW-1
+//    turn its raw time steps into the per-row values of each head (one row
+//    per lane, a block per 32-lane half):
+//        d_r   = clamp(softplus(dt_r + bias))  (0 on padded rows),
+//        lcs_r = log2(e) sum_{block start..r} A d   (inclusive),
+//        w_r   = 2^(lcs_last - lcs_r) d_r   (weight of row r in the state at
+//                the block's end),
+//    keep them in LDS for this pass and write them out for the chunk output.
+//    Per block, from zero at the chunk start:
+//        S <- 2^lam S + B^T (w x),
+//    both operands read k-major through transposing LDS loads, w applied to
+//    the x fragments in registers.  The state is written transposed
+//    ([head_dim][state_dim], one 16-byte store per lane and tile) with the
+//    chunk's total log2 decay.
 template <typename IO, int P, int N, int HPW> struct Sp {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
@@ -120,34 +87,53 @@ template <typename IO, int P, int N, int HPW> struct Sp {
     static constexpr int TPW = CPW * RT;              // tiles per wave
     static constexpr int KS = T / M::K;               // MFMA steps per block
     static constexpr int LDX = P + 16, LDB = N + 16;  // padded rows (transposing reads)
-    static constexpr int XS = SR * LDX;               // one head's staged w x
-    static constexpr int BUF = SR * LDB + HPW * XS;   // [B | w x of each head]
+    static constexpr int XS = SR * LDX;               // one head's staged x
+    static constexpr int BUF = SR * LDB + HPW * XS;   // [B | x of each head]
     static constexpr int NPB = SR * N / 8, NPX = HPW * SR * P / 8;  // pieces of 8
     static constexpr int KB = (NPB + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
+    static_assert(SR == 64 && HPW * SR <= NT, "one slab row per lane of waves 0 .. HPW-1");
+};
+
+// Per-row values of the staged slab, per head (LDS).
+template <int HPW> struct SpRows {
+    float w[HPW][2 * kT];    // weight in the state at the block's end
+    float lcs[HPW][2 * kT];  // cumulative log2 decay inside the block
 };
 
 // Register prefetch of one slab.  Loads go through buffer resources that end
-// at the chunk's last valid row (zeros beyond), so padded rows and rows past
-// the sequence need no masks; a slab past the segment's end (dead) issues the
-// same loads with empty resources.
+// at the chunk's last valid row (zeros beyond); a slab past the chunk's end
+// issues the same loads with empty resources.
 template <typename IO, int P, int N, int HPW> struct SpBuf {
     typedef Sp<IO, P, N, HPW> K;
     Row8v<IO> bv[K::KB];
     Row8v<IO> xv[K::KX];
-    float xw[K::KX];            // weight of the x piece's row
-    float lam[HPW][K::SLAB];    // log2 decay of each block, per head (uniform)
+    float dtv;  // raw time step of (head tid / SR, slab row tid % SR)
+    int nv;     // valid rows of the slab
 };
 
-// Addressing of one workgroup's chunk.
+// Addressing and time-step processing of one workgroup's chunk.
 template <typename IO> struct SpPtrs {
     const IO *x;          // row 0 of the sequence, first head of the workgroup
     const IO *B;          // row 0 of the sequence, the group
-    const float *lcs;     // (batch, first head) row arrays
-    Rsrc rw;              // weights of the workgroup's heads
+    const IO *dt;         // row 0 of the sequence, first head of the workgroup
+    float *lcs, *dtp, *wgt;  // (batch, first head) padded row arrays, written
+    float a2, bias;       // A log2(e) and dt_bias of the row thread's head
+    int softplus;
+    float dt_min, dt_max;
     int64_t xs, bs;       // row strides (elements) of x and of B
     int64_t l, Q, hrow;   // sequence length, chunk, elements from one head's row arrays to the next
-    int nsb;              // blocks per chunk
+    int h, nsb;           // heads (row stride of dt), blocks per chunk
+    int64_t Qp;           // padded rows per chunk
 };
+
+// One io element through a buffer resource, as fp32.
+__device__ __forceinline__ float buf_io1(Rsrc r, uint32_t off, const float *) {
+    return buf_f32(r, off, 0u);
+}
+__device__ __forceinline__ float buf_io1(Rsrc r, uint32_t off, const bf16 *) {
+    const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    return __builtin_bit_cast(float, (uint32_t)v << 16);
+}
 
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, int bi0, bool live,
@@ -161,7 +147,7 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
     const int64_t rr0 = valid > 0 ? row0 : 0;
     const Rsrc rx = make_rsrc(sp.x + rr0 * sp.xs, valid * sp.xs * (int64_t)sizeof(IO));
     const Rsrc rb = make_rsrc(sp.B + rr0 * sp.bs, valid * sp.bs * (int64_t)sizeof(IO));
-    const int64_t R0 = live ? (c * sp.nsb + bi0) * T : 0;             // padded row of the slab
+    const Rsrc rd = make_rsrc(sp.dt + rr0 * sp.h, valid * sp.h * (int64_t)sizeof(IO));
 #pragma unroll
     for (int k = 0; k < K::KB; ++k) {
         const int q = tid + k * K::NT;
@@ -178,24 +164,24 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
             const int j = qq / (P / 8), cc = qq % (P / 8);
             f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * sp.xs + hs * P + cc * 8) *
                                            (uint32_t)sizeof(IO));
-            f.xw[k] = buf_f32(sp.rw, (uint32_t)(hs * sp.hrow + j) * 4u, (uint32_t)R0 * 4u);
         }
     }
-#pragma unroll
-    for (int hs = 0; hs < HPW; ++hs)
-#pragma unroll
-        for (int jb = 0; jb < K::SLAB; ++jb) {
-            const int b = bi0 + jb < sp.nsb ? bi0 + jb : sp.nsb - 1;
-            f.lam[hs][jb] = live ? sp.lcs[hs * sp.hrow + (c * sp.nsb + b) * T + T - 1] : 0.f;
-        }
+    if (tid < HPW * K::SR) {
+        const int hs = tid / K::SR, r = tid % K::SR;
+        f.dtv = buf_io1(rd, (uint32_t)(r * sp.h + hs) * (uint32_t)sizeof(IO), sp.x);
+    }
+    f.nv = (int)valid;
 }
 
+// Stages the slab (B and x as operands) and derives its per-row values.
 template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f,
-                                         typename Op<IO>::type *buf, int tid) {
+__device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f, typename Op<IO>::type *buf,
+                                         SpRows<HPW> &rows, int64_t c, int bi0,
+                                         const SpPtrs<IO> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
-    OP *Bs = buf, *Xw = buf + K::SR * K::LDB;
+    constexpr int T = kT;
+    OP *Bs = buf, *Xs = buf + K::SR * K::LDB;
 #pragma unroll
     for (int k = 0; k < K::KB; ++k) {
         const int q = tid + k * K::NT;
@@ -207,8 +193,31 @@ __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f,
         const int q = tid + k * K::NT;
         if (K::NPX % K::NT == 0 || q < K::NPX) {
             const int hs = q / (K::SR * P / 8), qq = q % (K::SR * P / 8);
-            st_row8(Xw + hs * K::XS + (qq / (P / 8)) * K::LDX + (qq % (P / 8)) * 8,
-                    wx_piece(f.xv[k], f.xw[k]));
+            st_row8(Xs + hs * K::XS + (qq / (P / 8)) * K::LDX + (qq % (P / 8)) * 8,
+                    op_piece(f.xv[k]));
+        }
+    }
+    if (tid < HPW * K::SR) {  // whole waves: lane = slab row
+        const int hs = tid / K::SR, r = tid % K::SR;
+        const float d = r < f.nv ? time_step(f.dtv, sp.bias, sp.softplus, sp.dt_min, sp.dt_max)
+                                 : 0.f;
+        float a = sp.a2 * d;
+        // inclusive scan inside each 32-lane half (one block each)
+#pragma unroll
+        for (int off = 1; off < T; off <<= 1) {
+            const float v = __shfl_up(a, off, T);
+            if ((r & (T - 1)) >= off) a += v;
+        }
+        const float last = __shfl(a, T - 1, T);
+        const float w = exp2_fast(last - a) * d;
+        rows.w[hs][r] = w;
+        rows.lcs[hs][r] = a;
+        const int64_t R = (int64_t)bi0 * T + r;  // padded row inside the chunk
+        if (R < sp.Qp) {
+            const int64_t idx = hs * sp.hrow + c * sp.Qp + R;
+            sp.lcs[idx] = a;
+            sp.dtp[idx] = d;
+            sp.wgt[idx] = w;
         }
     }
 }
@@ -225,19 +234,41 @@ __device__ __forceinline__ void sp_store_t(float *dst, const f32x4 *acc, int c0,
                                        4 * (lane >> 4)) = acc[u * K::RT + tr];
 }
 
-// Applies the staged slab's nb blocks to the wave's tiles.
+// A k-major x fragment (rows = block rows kb + 4g + r, kb + 16 + 4g + r)
+// scaled row by row by w.
+__device__ __forceinline__ f16x8 wx_frag(const f16x8 &xf, int q, int lane, const float *w) {
+    const int g = lane >> 4;
+    const f32x4 wa = *reinterpret_cast<const f32x4 *>(w + 4 * g);
+    const f32x4 wb = *reinterpret_cast<const f32x4 *>(w + 16 + 4 * g);
+    const f16x2 o0 = pk2((float)xf[0] * wa[0], (float)xf[1] * wa[1]);
+    const f16x2 o1 = pk2((float)xf[2] * wa[2], (float)xf[3] * wa[3]);
+    const f16x2 o2 = pk2((float)xf[4] * wb[0], (float)xf[5] * wb[1]);
+    const f16x2 o3 = pk2((float)xf[6] * wb[2], (float)xf[7] * wb[3]);
+    return f16x8{o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
+}
+__device__ __forceinline__ float wx_frag(float xf, int q, int lane, const float *w) {
+    return xf * w[16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)];
+}
+
+// Applies the staged slab's nb blocks to the wave's tiles; returns the
+// slab's log2 decay.
 template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type *buf, int nb,
-                                         const float *lam, int hs, int c0, int lane) {
+__device__ __forceinline__ float sp_apply(f32x4 *acc, const typename Op<IO>::type *buf, int nb,
+                                          const SpRows<HPW> &rows, int hs, int c0, int lane) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::M M;
     constexpr int T = kT, KS = K::KS;
     const auto *Bs = buf;
-    const auto *Xw = buf + K::SR * K::LDB + hs * K::XS;
+    const auto *Xs = buf + K::SR * K::LDB + hs * K::XS;
+    float ld = 0.f;
 #pragma unroll
     for (int jb = 0; jb < K::SLAB; ++jb) {
         if (jb < nb) {
-            const float decay = exp2_fast(lam[jb]);
+            const float lam = __builtin_bit_cast(
+                float, __builtin_amdgcn_readfirstlane(
+                           __builtin_bit_cast(int, rows.lcs[hs][jb * T + T - 1])));
+            ld += lam;
+            const float decay = exp2_fast(lam);
 #pragma unroll
             for (int k = 0; k < K::TPW; ++k) acc[k] *= decay;
 #pragma unroll
@@ -245,7 +276,8 @@ __device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type
                 typename Mfma<typename K::OP>::frag xf[K::CPW];
 #pragma unroll
                 for (int u = 0; u < K::CPW; ++u)
-                    xf[u] = frag_kmajor(Xw, K::LDX, jb * T, q, c0 + 16 * u, lane);
+                    xf[u] = wx_frag(frag_kmajor(Xs, K::LDX, jb * T, q, c0 + 16 * u, lane), q, lane,
+                                    &rows.w[hs][jb * T]);
 #pragma unroll
                 for (int tr = 0; tr < K::RT; ++tr) {
                     const auto bt = frag_kmajor(Bs, K::LDB, jb * T, q, tr * 16, lane);
@@ -256,18 +288,21 @@ __device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type
             }
         }
     }
+    return ld;
 }
-
 
 template <typename IO, int P, int N, int HPW>
 __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
-    const IO *__restrict__ x, const IO *__restrict__ Bm, const float *__restrict__ lcs,
-    const float *__restrict__ wgt, float *__restrict__ St, float *__restrict__ Lam, int64_t l,
-    int h, int g, int64_t Q, int64_t nc, int64_t Qp) {
+    const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ dt,
+    const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
+    float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
+    float *__restrict__ St, float *__restrict__ Lam, int64_t l, int h, int g, int64_t Q,
+    int64_t nc, int64_t Qp) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, SLAB = K::SLAB, TPW = K::TPW;
     __shared__ __attribute__((aligned(16))) OP lds[K::BUF];
+    __shared__ __attribute__((aligned(16))) SpRows<HPW> rows;
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
@@ -287,12 +322,24 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
     sp.bs = (int64_t)g * N;
     sp.x = x + (b * l * h + hh0) * P;
     sp.B = Bm + (b * l * g + gi) * N;
+    sp.dt = dt + b * l * h + hh0;
     sp.lcs = lcs + (b * h + hh0) * nc * Qp;
+    sp.dtp = dtp + (b * h + hh0) * nc * Qp;
+    sp.wgt = wgt + (b * h + hh0) * nc * Qp;
+    {
+        const int rh = hh0 + (tid < HPW * K::SR ? tid / K::SR : 0);  // the row thread's head
+        sp.a2 = A[rh] * kLog2e;
+        sp.bias = dt_bias ? dt_bias[rh] : 0.f;
+    }
+    sp.softplus = softplus;
+    sp.dt_min = dt_min;
+    sp.dt_max = dt_max;
     sp.hrow = nc * Qp;
-    sp.rw = make_rsrc(wgt + (b * h + hh0) * nc * Qp, ((int64_t)(HPW - 1) * nc * Qp + nc * Qp) * 4);
     sp.l = l;
     sp.Q = Q;
+    sp.h = h;
     sp.nsb = nsb;
+    sp.Qp = Qp;
 
     f32x4 acc[TPW];
 #pragma unroll
@@ -310,21 +357,11 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
             const bool live = k < nspc;
             const int bi0 = k * SLAB;
             const int nb = live ? (nsb - bi0 < SLAB ? nsb - bi0 : SLAB) : 0;
-            float lam[SLAB];
-#pragma unroll
-            for (int jb = 0; jb < SLAB; ++jb) {
-                float v = pf.lam[0][jb];
-#pragma unroll
-                for (int q = 1; q < HPW; ++q) v = hs == q ? pf.lam[q][jb] : v;
-                lam[jb] = v;
-            }
             lds_barrier();  // the previous slab's reads are done
-            sp_stage(pf, lds, tid);
+            if (live) sp_stage(pf, lds, rows, c, bi0, sp, tid);
             sp_prefetch(pf, c, (k + 2) * SLAB, k + 2 < nspc, sp, tid);
             lds_barrier();
-            sp_apply<IO, P, N, HPW>(acc, lds, nb, lam, hs, c0, lane);
-#pragma unroll
-            for (int jb = 0; jb < SLAB; ++jb) logdec += jb < nb ? lam[jb] : 0.f;
+            logdec += sp_apply<IO, P, N, HPW>(acc, lds, nb, rows, hs, c0, lane);
         }
     }
     sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
@@ -332,7 +369,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
 }
 
 // ----------------------------------------------------------------------------
-// 3. State scan: the serial pass over chunks,
+// 2. State scan: the serial pass over chunks,
 //        H_0 = init (or 0),   H_{c+1} = 2^L_c H_c + S_c,
 //    with S_c and L_c from k_chunk_state.  H_c is stored as chunk c's
 //    boundary state in the read-out's matrix-core operand type (fp16 rounded
@@ -398,7 +435,7 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
 }
 
 // ----------------------------------------------------------------------------
-// 4. Chunk output.  One workgroup per (batch, chunk, HPW consecutive heads of
+// 3. Chunk output.  One workgroup per (batch, chunk, HPW consecutive heads of
 //    one group); WPH = max(1, head_dim / 32) waves per head, each owning 32
 //    (or head_dim, if smaller) head_dim columns.  C and B of a block are
 //    staged once for all the workgroup's heads (they share the group), x per
@@ -861,29 +898,21 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     IO *y = static_cast<IO *>(a.y);
     const int h = (int)pl.h, g = (int)pl.g;
 
-    const int64_t ns = (pl.lp + 63) / 64;
-    const int64_t na = (pl.b * pl.h * ns + kWaves - 1) / kWaves;
-    trace_begin(0, s);
-    hipLaunchKernelGGL(k_prep<IO>, dim3((unsigned)na), dim3(kThreads), 0, s, dt, a.A, a.dt_bias,
-                       a.softplus, a.dt_min, a.dt_max, pl.b, pl.l, h, pl.Q, pl.nc, pl.Qp, lcs,
-                       dtp, wgt);
-    trace_end(0, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
     constexpr int HP = kGroupHeads<P>;
     const bool grouped = HP > 1 && group_heads((int)P, h / g) == HP;
     trace_begin(1, s);
     if (grouped)
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
-                           dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bm, lcs, wgt, St, Lam, pl.l, h, g,
+                           dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bm, dt, a.A, a.dt_bias,
+                           a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam, pl.l, h, g,
                            pl.Q, pl.nc, pl.Qp);
     else
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
-                           dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bm, lcs, wgt, St, Lam, pl.l, h, g,
+                           dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bm, dt, a.A, a.dt_bias,
+                           a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam, pl.l, h, g,
                            pl.Q, pl.nc, pl.Qp);
     trace_end(1, s);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     const int64_t np4 = (int64_t)N * P / 4;
