@@ -287,6 +287,50 @@ __device__ __forceinline__ void swz_store8(T *M, int r, int c0, const V &v) {
         *reinterpret_cast<u32x4 *>(M + S::at(r, c0 + i * S::EPC)) = src[i];
 }
 
+// Paired column order for fp16 matrices contracted over their columns in the
+// k convention above: inside every 32 columns, column n = 32m + 16h + 4g + r
+// is kept at 32m + 8g + 4h + r, so the two 4-element halves of a fragment
+// (k = kb + 4g + r and kb + 16 + 4g + r) form one 16-byte chunk, and a
+// transposing read's 4 consecutive columns stay 4 consecutive elements.
+__device__ __forceinline__ int pair_col(int n) {
+    return (n & ~31) | (((n >> 2) & 3) << 3) | (((n >> 4) & 1) << 2) | (n & 3);
+}
+
+// Row piece of 8 consecutive columns c0 .. c0 + 7 (c0 % 8 == 0) stored into a
+// swizzled matrix in paired order: two 8-byte halves.
+template <int NCOL, typename V>
+__device__ __forceinline__ void swzp_store8(f16 *M, int r, int c0, const V &v) {
+    typedef Swz<f16, NCOL> S;
+    static_assert(sizeof(V) == 16, "row piece of 8 fp16 elements");
+    const u32x4 w = __builtin_bit_cast(u32x4, v);
+    *reinterpret_cast<u32x2 *>(M + S::at(r, pair_col(c0))) = u32x2{w[0], w[1]};
+    *reinterpret_cast<u32x2 *>(M + S::at(r, pair_col(c0 + 4))) = u32x2{w[2], w[3]};
+}
+
+// Row-major rows in the k convention from a swizzled paired matrix: one
+// 16-byte read per lane.
+template <int NCOL>
+__device__ __forceinline__ f16x8 swzp_rows_kconv(const f16 *M, int row0, int kb, int lane) {
+    typedef Swz<f16, NCOL> S;
+    return *reinterpret_cast<const f16x8 *>(M + S::at(row0 + (lane & 15), kb + 8 * (lane >> 4)));
+}
+
+// k-major fragment (rows = contraction index, as frag_kmajor) of a swizzled
+// paired matrix, columns c0 .. c0 + 15 in logical order.
+template <int NCOL>
+__device__ __forceinline__ f16x8 swzp_kmajor(const f16 *M, int kb, int c0, int lane) {
+    typedef Swz<f16, NCOL> S;
+    const int g = lane >> 4, j = lane & 15;
+    const int pc = pair_col(c0 + 4 * (j & 3));
+    const f16 *pa = M + S::at(kb + 4 * g + (j >> 2), pc);
+    const f16 *pb = M + S::at(kb + 16 + 4 * g + (j >> 2), pc);
+    const f16x4 a =
+        __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pa));
+    const f16x4 b =
+        __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pb));
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // ---------------------------------------------------------- row pieces ----
 // 8 consecutive elements of one row, moved with vector loads and stores.
 template <typename T> struct alignas(16) Row8v { T e[8]; };

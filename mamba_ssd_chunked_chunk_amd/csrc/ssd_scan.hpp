@@ -559,8 +559,13 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
         const int q = tid + k * K::NT;
         if (K::NPC % K::NT == 0 || q < K::NPC) {
             const int r = q / (N / 8), c0 = (q % (N / 8)) * 8;
-            swz_store8<OP, N>(Cs, r, c0, op_piece(f.cv[k]));
-            swz_store8<OP, N>(Bs, r, c0, op_piece(f.bv[k]));
+            if constexpr (sizeof(OP) == 2) {
+                swzp_store8<N>(Cs, r, c0, op_piece(f.cv[k]));
+                swzp_store8<N>(Bs, r, c0, op_piece(f.bv[k]));
+            } else {
+                swz_store8<OP, N>(Cs, r, c0, op_piece(f.cv[k]));
+                swz_store8<OP, N>(Bs, r, c0, op_piece(f.bv[k]));
+            }
         }
     }
 #pragma unroll
@@ -659,10 +664,18 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
     for (int m = 0; m < NB; ++m) {
 #pragma unroll
         for (int q = 0; q < KS; ++q) {
-            const auto c0f = swz_rows_kconv<OP, N>(Cs, 0, 32 * m, q, lane);
-            const auto c1f = swz_rows_kconv<OP, N>(Cs, 16, 32 * m, q, lane);
-            const auto b0f = swz_rows_kconv<OP, N>(Bs, 0, 32 * m, q, lane);
-            const auto b1f = swz_rows_kconv<OP, N>(Bs, 16, 32 * m, q, lane);
+            typename M::frag c0f, c1f, b0f, b1f;
+            if constexpr (sizeof(OP) == 2) {
+                c0f = swzp_rows_kconv<N>(Cs, 0, 32 * m, lane);
+                c1f = swzp_rows_kconv<N>(Cs, 16, 32 * m, lane);
+                b0f = swzp_rows_kconv<N>(Bs, 0, 32 * m, lane);
+                b1f = swzp_rows_kconv<N>(Bs, 16, 32 * m, lane);
+            } else {
+                c0f = swz_rows_kconv<OP, N>(Cs, 0, 32 * m, q, lane);
+                c1f = swz_rows_kconv<OP, N>(Cs, 16, 32 * m, q, lane);
+                b0f = swz_rows_kconv<OP, N>(Bs, 0, 32 * m, q, lane);
+                b1f = swz_rows_kconv<OP, N>(Bs, 16, 32 * m, q, lane);
+            }
             gt[0] = M::mma(b0f, c0f, gt[0]);
             gt[1] = M::mma(b0f, c1f, gt[1]);
             gt[2] = M::mma(b1f, c1f, gt[2]);
@@ -780,7 +793,11 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
         for (int tr = 0; tr < RT; ++tr)
 #pragma unroll
             for (int q = 0; q < KS; ++q) {
-                const auto bt = swz_kmajor<OP, N>(Bs, 0, q, tr * 16, lane);
+                typename M::frag bt;
+                if constexpr (sizeof(OP) == 2)
+                    bt = swzp_kmajor<N>(Bs, 0, tr * 16, lane);
+                else
+                    bt = swz_kmajor<OP, N>(Bs, 0, q, tr * 16, lane);
 #pragma unroll
                 for (int u = 0; u < CPW; ++u)
                     accH[u * RT + tr] = M::mma(bt, xw[u][q], accH[u * RT + tr]);
