@@ -58,11 +58,11 @@ __device__ __forceinline__ Row8v<float> op_piece(const Row8v<float> &v) { return
 //    per (batch, chunk, HPW consecutive heads of one group); WPH = max(1,
 //    head_dim / 32) waves per head, each owning 32 (or head_dim) head_dim
 //    columns of its head's chunk state (state_dim x head_dim, fp32) in MFMA
-//    accumulators.  Slabs of SLAB = 2 row blocks are fetched two ahead into
+//    accumulators.  Slabs of SLAB = 1 row block are fetched two ahead into
 //    registers (B once for all heads, x and the raw time steps per head) and
-//    staged through one LDS buffer.  While a slab is staged, waves 0 .. HPW-1
-//    turn its raw time steps into the per-row values of each head (one row
-//    per lane, a block per 32-lane half):
+//    staged through one LDS buffer.  While a slab is staged, the first
+//    HPW * 32 threads turn its raw time steps into the per-row values of
+//    each head (one row per lane, a block per 32 lanes):
 //        d_r   = clamp(softplus(dt_r + bias))  (0 on padded rows),
 //        lcs_r = log2(e) sum_{block start..r} A d   (inclusive),
 //        w_r   = 2^(lcs_last - lcs_r) d_r   (weight of row r in the state at
@@ -78,7 +78,9 @@ template <typename IO, int P, int N, int HPW> struct Sp {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
     static constexpr int T = kT;
-    static constexpr int SLAB = 2, SR = SLAB * T;     // blocks and rows per slab
+    // one block per slab: the small register prefetch lets 3 workgroups
+    // share a compute unit
+    static constexpr int SLAB = 1, SR = SLAB * T;     // blocks and rows per slab
     static constexpr int WPH = P >= 64 ? P / 32 : 1;  // waves per head
     static constexpr int PW = P / WPH;                // head_dim columns per wave
     static constexpr int CPW = PW / 16;               // column tiles per wave
@@ -91,13 +93,13 @@ template <typename IO, int P, int N, int HPW> struct Sp {
     static constexpr int BUF = SR * LDB + HPW * XS;   // [B | x of each head]
     static constexpr int NPB = SR * N / 8, NPX = HPW * SR * P / 8;  // pieces of 8
     static constexpr int KB = (NPB + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
-    static_assert(SR == 64 && HPW * SR <= NT, "one slab row per lane of waves 0 .. HPW-1");
+    static_assert(HPW * SR <= NT, "one thread per slab row of every head");
 };
 
 // Per-row values of the staged slab, per head (LDS).
 template <int HPW> struct SpRows {
-    float w[HPW][2 * kT];    // weight in the state at the block's end
-    float lcs[HPW][2 * kT];  // cumulative log2 decay inside the block
+    float w[HPW][kT];    // weight in the state at the block's end
+    float lcs[HPW][kT];  // cumulative log2 decay inside the block
 };
 
 // Register prefetch of one slab.  Loads go through buffer resources that end
@@ -197,7 +199,7 @@ __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f, typename
                     op_piece(f.xv[k]));
         }
     }
-    if (tid < HPW * K::SR) {  // whole waves: lane = slab row
+    if (tid < HPW * K::SR) {  // one row per thread; 32-lane groups scan a block
         const int hs = tid / K::SR, r = tid % K::SR;
         const float d = r < f.nv ? time_step(f.dtv, sp.bias, sp.softplus, sp.dt_min, sp.dt_max)
                                  : 0.f;
