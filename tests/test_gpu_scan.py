@@ -25,8 +25,12 @@ SMALL = [
     (1, 129, 2, 128, 128, 1, 256, 0.1),   # sequence shorter than a chunk, head_dim 128
     (3, 40, 4, 64, 32, 4, 1, 0.2),        # one token per chunk
     (2, 1, 4, 64, 128, 1, 64, 0.3),       # a single token
-    (16, 100, 32, 16, 128, 1, 32, 0.1),   # many heads: one segment in the serial pass
-    (1, 1000, 2, 64, 64, 2, 64, 0.0),     # long, few heads: many segments
+    (16, 100, 32, 16, 128, 1, 32, 0.1),   # many heads: four heads per workgroup
+    (1, 1000, 2, 64, 64, 2, 64, 0.0),     # 16 chunks through the state scan
+    (1, 1500, 4, 64, 128, 1, 512, 0.1),   # long chunks: 16 row blocks carried per chunk
+    (2, 1400, 2, 64, 128, 1, 700, 0.2),   # chunk of 700 rows, ragged blocks
+    (1, 200, 3, 64, 128, 1, 64, 0.1),     # odd group size: one head per workgroup
+    (2, 130, 8, 32, 128, 2, 64, 0.1),     # head_dim 32, four heads per workgroup
 ]
 
 
@@ -199,6 +203,26 @@ def test_empty_sequence_and_batch():
                             return_final_state=True)
     torch.cuda.synchronize()
     assert y.shape[0] == 0 and fin.shape[0] == 0
+
+
+def test_workspace_contents_ignored(orc):
+    """The workspace is filled with NaN bytes before the call: nothing the
+    scan reads from it may come from an earlier call or be left unwritten."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, l, h, p, n, g, Q = 2, 300, 4, 64, 128, 2, 64
+    for io in ("f32", "bf16"):
+        inp = syn.random_case(19, b, l, h, p, n, g, io=io, init_std=0.2)
+        G = gpu_inputs(inp)
+        ws = torch.full((ssd.workspace_bytes(b, l, h, p, n, g, Q),), 0xFF, dtype=torch.uint8,
+                        device="cuda")
+        y, fin = ssd.chunk_scan(G["x"], G["dt"], G["A"], G["B"], G["C"], G["D"], chunk_size=Q,
+                                dt_bias=G["dt_bias"], initial_state=G["init"],
+                                return_final_state=True, workspace=ws)
+        torch.cuda.synchronize()
+        yo, fo = orc.scan(**oracle_kw(inp))
+        check_close(to_f64(y), yo, io, "y", Y_AXES)
+        check_close(to_f64(fin), fo, io, "final state", STATE_AXES)
 
 
 def test_invalid_arguments_raise():
