@@ -445,7 +445,8 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
 //    rows) in MFMA accumulators across the chunk's blocks.  Per block:
 //      G^T = B C^T on the 3 causal 16 x 16 tiles, and
 //      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i), in registers;
-//      y^T = 2^lcs_i (H^T C^T) + x^T P^T + D x^T, stored straight from the
+//      y^T = 2^lcs_i (H^T C^T) + x^T (P + D I)^T (the skip term on the
+//            scores' diagonal), stored straight from the
 //            accumulators (4 consecutive columns per lane);
 //      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
 //    The scores and the state read-out take the same C fragments (one LDS
@@ -723,8 +724,15 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
                 (j0 <= li) ? gt[2][r] * exp2_fast(l1 - rf.lcs[16 + j0]) * rf.d[16 + j0] : 0.f;
         }
     }
+    // the skip term rides on the diagonal: (P + D I) x = P x + D x
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float dg = 4 * lg + r == li ? Dh : 0.f;
+        pv[0][0][r] += dg;
+        pv[1][1][r] += dg;
+    }
 
-    // ---- y^T = colscale (H^T C^T) + x^T P^T + D x^T, straight to y:
+    // ---- y^T = colscale (H^T C^T) + x^T (P + D I)^T, straight to y:
     //      element r of lane l is (p = c0 + co_col(u, 4 lg + r), i = 16 it + li)
     int valid = cp.rows - r0;
     valid = valid < 0 ? 0 : (valid > T ? T : valid);
@@ -739,14 +747,14 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
     for (int it = 0; it < 2; ++it) {
         const int i = it * 16 + li;
         f32x4 yv[CPW];
+        (void)LDX;
 #pragma unroll
         for (int u = 0; u < CPW; ++u) {
             f32x4 yp = zero4();
 #pragma unroll
             for (int q = 0; q < KS; ++q)
                 yp = M::mma(xf[u][q], frag_from_acc<OP>(pv[it][0], pv[it][1], q), yp);
-            const f32x4 xv = lds_load4(Xs + i * LDX + c0 + co_col<CPW>(u, 4 * lg));
-            yv[u] = colscale[it] * yh[it][u] + yp + Dh * xv;
+            yv[u] = colscale[it] * yh[it][u] + yp;
         }
         if constexpr (CPW % 2 == 0) {
             // tiles 2v, 2v + 1: 8 consecutive columns c0 + 32 v + 8 lg ..
