@@ -30,6 +30,8 @@
 //                     read-out of the boundary state, skip term
 #pragma once
 
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_plan.hpp"
 
@@ -857,29 +859,6 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     const int nblk = (cp.rows + T - 1) / T;
     const float Dh = D ? D[hh] : 0.f;
 
-    // ---- the wave's state columns entering the chunk: the boundary state,
-    //      stored transposed ([head_dim][state_dim]) in the operand type, so
-    //      a lane's 4 accumulator values (consecutive state rows) are one load
-    f32x4 accH[CPW * RT];
-    {
-        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * (int64_t)sizeof(OP));
-#pragma unroll
-        for (int u = 0; u < CPW; ++u)
-#pragma unroll
-            for (int tr = 0; tr < RT; ++tr) {
-                const uint32_t off = (uint32_t)((c0 + co_col<CPW>(u, li)) * N + tr * 16 + 4 * lg) *
-                                     (uint32_t)sizeof(OP);
-                if constexpr (sizeof(OP) == 2) {
-                    const f16x4 v = __builtin_bit_cast(
-                        f16x4, __builtin_amdgcn_raw_buffer_load_b64(rh, off, 0, 0));
-                    accH[u * RT + tr] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-                } else {
-                    accH[u * RT + tr] = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
-                }
-            }
-    }
-
     // Block k is fetched into registers pa (k even) or pb (k odd) two blocks
     // ahead and staged into LDS buffer k & 1 while block k - 1 is computed.
     // Blocks go in pairs, every load and store issued unconditionally (past
@@ -891,9 +870,37 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     OP *const buf1 = lds + BUF;
     co_prefetch(pa, 0, cp, tid);
     co_prefetch(pb, 1, cp, tid);
+
+    // ---- the wave's state columns entering the chunk: the boundary state,
+    //      stored transposed ([head_dim][state_dim]) in the operand type, so
+    //      a lane's 4 accumulator values (consecutive state rows) are one
+    //      load.  Loaded after the first blocks, so that staging block 0
+    //      does not wait for them.
+    typedef typename std::conditional<sizeof(OP) == 2, f16x4, f32x4>::type HRaw;
+    HRaw hraw[CPW * RT];
+    {
+        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * (int64_t)sizeof(OP));
+#pragma unroll
+        for (int u = 0; u < CPW; ++u)
+#pragma unroll
+            for (int tr = 0; tr < RT; ++tr) {
+                const uint32_t off = (uint32_t)((c0 + co_col<CPW>(u, li)) * N + tr * 16 + 4 * lg) *
+                                     (uint32_t)sizeof(OP);
+                if constexpr (sizeof(OP) == 2)
+                    hraw[u * RT + tr] = __builtin_bit_cast(
+                        f16x4, __builtin_amdgcn_raw_buffer_load_b64(rh, off, 0, 0));
+                else
+                    hraw[u * RT + tr] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+            }
+    }
     co_stage(pa, buf0, rowsf[0], tid);
     co_prefetch(pa, 2, cp, tid);
     lds_barrier();
+    f32x4 accH[CPW * RT];
+#pragma unroll
+    for (int k = 0; k < CPW * RT; ++k)
+        accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
     for (int s = 0; s < nblk; s += 2) {
         co_stage(pb, buf1, rowsf[1], tid);  // block s + 1
         co_prefetch(pb, s + 3, cp, tid);
