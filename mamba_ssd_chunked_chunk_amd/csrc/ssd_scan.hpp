@@ -60,29 +60,30 @@ __device__ __forceinline__ Row8v<float> op_piece(const Row8v<float> &v) { return
 //    per (batch, chunk, HPW consecutive heads of one group); WPH = max(1,
 //    head_dim / 32) waves per head, each owning 32 (or head_dim) head_dim
 //    columns of its head's chunk state (state_dim x head_dim, fp32) in MFMA
-//    accumulators.  Slabs of SLAB = 1 row block are fetched two ahead into
-//    registers (B once for all heads, x and the raw time steps per head) and
-//    staged through one LDS buffer.  While a slab is staged, the first
-//    HPW * 32 threads turn its raw time steps into the per-row values of
-//    each head (one row per lane, a block per 32 lanes):
+//    accumulators.
+//    The chunk goes in spans of up to SPAN = 8 blocks (256 rows).  At the
+//    start of a span the workgroup turns the span's raw time steps into the
+//    per-row values of each head (one row per thread, a block per 32 lanes):
 //        d_r   = clamp(softplus(dt_r + bias))  (0 on padded rows),
 //        lcs_r = log2(e) sum_{block start..r} A d   (inclusive),
 //        w_r   = 2^(lcs_last - lcs_r) d_r   (weight of row r in the state at
-//                the block's end),
-//    keep them in LDS for this pass and write them out for the chunk output.
-//    Per block, from zero at the chunk start:
-//        S <- 2^lam S + B^T (w x),
-//    both operands read k-major through transposing LDS loads, w applied to
-//    the x fragments in registers.  The state is written transposed
-//    ([head_dim][state_dim], one 16-byte store per lane and tile) with the
-//    chunk's total log2 decay.
+//                the end of its block),
+//    writes them out for the chunk output and keeps in LDS the weight of
+//    every row in the state at the span's end,
+//        v_r = w_r 2^(lam_{J+1} + ... + lam_{span's last block})
+//    (row r in block J, every factor <= 1).  The state then decays once per
+//    span, S <- 2^L S (L the span's log2 decay), and every block adds
+//    S += B^T (v x) with x weighted as it is staged, so a block costs its
+//    staging and its products only.  Blocks are fetched two ahead into
+//    registers (B once for all heads, x per head) and staged through one
+//    LDS buffer; both operands are read k-major through transposing LDS
+//    loads.  The state is written transposed ([head_dim][state_dim], one
+//    16-byte store per lane and tile) with the chunk's total log2 decay.
 template <typename IO, int P, int N, int HPW> struct Sp {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
     static constexpr int T = kT;
-    // one block per slab: the small register prefetch lets 3 workgroups
-    // share a compute unit
-    static constexpr int SLAB = 1, SR = SLAB * T;     // blocks and rows per slab
+    static constexpr int SPAN = 8, SPR = SPAN * T;    // blocks and rows per span
     static constexpr int WPH = P >= 64 ? P / 32 : 1;  // waves per head
     static constexpr int PW = P / WPH;                // head_dim columns per wave
     static constexpr int CPW = PW / 16;               // column tiles per wave
@@ -91,67 +92,56 @@ template <typename IO, int P, int N, int HPW> struct Sp {
     static constexpr int TPW = CPW * RT;              // tiles per wave
     static constexpr int KS = T / M::K;               // MFMA steps per block
     static constexpr int LDX = P + 16, LDB = N + 16;  // padded rows (transposing reads)
-    static constexpr int XS = SR * LDX;               // one head's staged x
-    static constexpr int BUF = SR * LDB + HPW * XS;   // [B | x of each head]
-    static constexpr int NPB = SR * N / 8, NPX = HPW * SR * P / 8;  // pieces of 8
+    static constexpr int XS = T * LDX;                // one head's staged v x
+    static constexpr int BUF = T * LDB + HPW * XS;    // [B | v x of each head]
+    static constexpr int NPB = T * N / 8, NPX = HPW * T * P / 8;  // pieces of 8
     static constexpr int KB = (NPB + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
-    static_assert(HPW * SR <= NT, "one thread per slab row of every head");
+    static constexpr int NPASS = HPW * SPR / NT;      // span rows per thread
+    static_assert(NPASS * NT == HPW * SPR && NT % 64 == 0, "span rows in whole waves");
 };
 
-// Per-row values of the staged slab, per head (LDS).
-template <int HPW> struct SpRows {
-    float w[HPW][kT];    // weight in the state at the block's end
-    float lcs[HPW][kT];  // cumulative log2 decay inside the block
+// Per-row weights of the current span, per head (LDS).
+template <int HPW> struct SpSpan {
+    float v[HPW][8 * kT];  // weight in the state at the span's end
+    float lam[HPW][8];     // log2 decay of each block of the span
 };
 
-// Register prefetch of one slab.  Loads go through buffer resources that end
-// at the chunk's last valid row (zeros beyond); a slab past the chunk's end
-// issues the same loads with empty resources.
+// Register prefetch of one block.  Loads go through buffer resources that
+// end at the chunk's last valid row (zeros beyond); a block past the chunk's
+// end issues the same loads with empty resources.
 template <typename IO, int P, int N, int HPW> struct SpBuf {
     typedef Sp<IO, P, N, HPW> K;
     Row8v<IO> bv[K::KB];
     Row8v<IO> xv[K::KX];
-    float dtv;  // raw time step of (head tid / SR, slab row tid % SR)
-    int nv;     // valid rows of the slab
 };
 
 // Addressing and time-step processing of one workgroup's chunk.
-template <typename IO> struct SpPtrs {
-    const IO *x;          // row 0 of the sequence, first head of the workgroup
-    const IO *B;          // row 0 of the sequence, the group
-    const IO *dt;         // row 0 of the sequence, first head of the workgroup
+template <typename IO, int HPW> struct SpPtrs {
+    const IO *x;             // row 0 of the sequence, first head of the workgroup
+    const IO *B;             // row 0 of the sequence, the group
+    const IO *dt;            // row 0 of the sequence, first head of the workgroup
     float *lcs, *dtp, *wgt;  // (batch, first head) padded row arrays, written
-    float a2, bias;       // A log2(e) and dt_bias of the row thread's head
+    float a2[HPW], bias[HPW];  // A log2(e) and dt_bias of the workgroup's heads
     int softplus;
     float dt_min, dt_max;
-    int64_t xs, bs;       // row strides (elements) of x and of B
-    int64_t l, Q, hrow;   // sequence length, chunk, elements from one head's row arrays to the next
-    int h, nsb;           // heads (row stride of dt), blocks per chunk
-    int64_t Qp;           // padded rows per chunk
+    int64_t xs, bs;          // row strides (elements) of x and of B
+    int64_t l, Q, hrow;      // sequence length, chunk, elements from one head's row arrays to the next
+    int h;                   // heads (row stride of dt)
+    int64_t Qp;              // padded rows per chunk
 };
 
-// One io element through a buffer resource, as fp32.
-__device__ __forceinline__ float buf_io1(Rsrc r, uint32_t off, const float *) {
-    return buf_f32(r, off, 0u);
-}
-__device__ __forceinline__ float buf_io1(Rsrc r, uint32_t off, const bf16 *) {
-    const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-    return __builtin_bit_cast(float, (uint32_t)v << 16);
-}
-
 template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, int bi0, bool live,
-                                            const SpPtrs<IO> &sp, int tid) {
+__device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, int blk,
+                                            bool live, const SpPtrs<IO, HPW> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     constexpr int T = kT;
-    const int64_t row0 = c * sp.Q + (int64_t)bi0 * T;                  // sequence row
+    const int64_t row0 = c * sp.Q + (int64_t)blk * T;                  // sequence row
     const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;  // end of the chunk
     int64_t valid = live ? cend - row0 : 0;
-    valid = valid < 0 ? 0 : (valid > K::SR ? K::SR : valid);
+    valid = valid < 0 ? 0 : (valid > T ? T : valid);
     const int64_t rr0 = valid > 0 ? row0 : 0;
     const Rsrc rx = make_rsrc(sp.x + rr0 * sp.xs, valid * sp.xs * (int64_t)sizeof(IO));
     const Rsrc rb = make_rsrc(sp.B + rr0 * sp.bs, valid * sp.bs * (int64_t)sizeof(IO));
-    const Rsrc rd = make_rsrc(sp.dt + rr0 * sp.h, valid * sp.h * (int64_t)sizeof(IO));
 #pragma unroll
     for (int k = 0; k < K::KB; ++k) {
         const int q = tid + k * K::NT;
@@ -164,28 +154,98 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
     for (int k = 0; k < K::KX; ++k) {
         const int q = tid + k * K::NT;
         if (K::NPX % K::NT == 0 || q < K::NPX) {
-            const int hs = q / (K::SR * P / 8), qq = q % (K::SR * P / 8);
+            const int hs = q / (T * P / 8), qq = q % (T * P / 8);
             const int j = qq / (P / 8), cc = qq % (P / 8);
             f.xv[k] = buf_row8<IO>(rx, (uint32_t)(j * sp.xs + hs * P + cc * 8) *
                                            (uint32_t)sizeof(IO));
         }
     }
-    if (tid < HPW * K::SR) {
-        const int hs = tid / K::SR, r = tid % K::SR;
-        f.dtv = buf_io1(rd, (uint32_t)(r * sp.h + hs) * (uint32_t)sizeof(IO), sp.x);
-    }
-    f.nv = (int)valid;
 }
 
-// Stages the slab (B and x as operands) and derives its per-row values.
+// The per-row values of the span starting at block blk0 (see above); ends
+// with the span's weights visible to the whole workgroup.
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, int64_t c, int blk0,
+                                        const SpPtrs<IO, HPW> &sp, int tid) {
+    typedef Sp<IO, P, N, HPW> K;
+    constexpr int T = kT;
+    const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;
+    float dtv[K::NPASS];
+#pragma unroll
+    for (int ps = 0; ps < K::NPASS; ++ps) {  // all raw time steps first
+        const int idx = ps * K::NT + tid;
+        const int hs = idx / K::SPR, r = idx % K::SPR;
+        const int64_t row = c * sp.Q + (int64_t)blk0 * T + r;
+        dtv[ps] = row < cend ? to_f32(sp.dt[row * sp.h + hs]) : 0.f;
+    }
+#pragma unroll
+    for (int ps = 0; ps < K::NPASS; ++ps) {
+        const int idx = ps * K::NT + tid;
+        const int hs = idx / K::SPR, r = idx % K::SPR;
+        const int64_t row = c * sp.Q + (int64_t)blk0 * T + r;
+        // the head's constants, selected without indexing (registers)
+        float bias = sp.bias[0], a2 = sp.a2[0];
+#pragma unroll
+        for (int k = 1; k < HPW; ++k) {
+            bias = hs == k ? sp.bias[k] : bias;
+            a2 = hs == k ? sp.a2[k] : a2;
+        }
+        const float d = row < cend ? time_step(dtv[ps], bias, sp.softplus, sp.dt_min, sp.dt_max)
+                                   : 0.f;
+        float a = a2 * d;
+        // inclusive scan inside each 32-lane group (one block each)
+#pragma unroll
+        for (int off = 1; off < T; off <<= 1) {
+            const float v = __shfl_up(a, off, T);
+            if ((r & (T - 1)) >= off) a += v;
+        }
+        const float last = __shfl(a, T - 1, T);
+        const float w = exp2_fast(last - a) * d;
+        const int64_t R = (int64_t)blk0 * T + r;  // padded row inside the chunk
+        if (R < sp.Qp) {
+            const int64_t idx2 = hs * sp.hrow + c * sp.Qp + R;
+            sp.lcs[idx2] = a;
+            sp.dtp[idx2] = d;
+            sp.wgt[idx2] = w;
+        }
+        sv.v[hs][r] = w;
+        if ((r & (T - 1)) == T - 1) sv.lam[hs][r / T] = last;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int ps = 0; ps < K::NPASS; ++ps) {
+        const int idx = ps * K::NT + tid;
+        const int hs = idx / K::SPR, r = idx % K::SPR;
+        float sfx = 0.f;  // decay of the span's later blocks
+#pragma unroll
+        for (int k = 0; k < K::SPAN; ++k) sfx += k > r / T ? sv.lam[hs][k] : 0.f;
+        sv.v[hs][r] *= exp2_fast(sfx);
+    }
+    lds_barrier();
+}
+
+// v x piece of 8 elements as operands.
+__device__ __forceinline__ Row8v<f16> vx_piece(const Row8v<bf16> &x, float v) {
+    Row8v<f16> o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) pack2((float)x.e[e] * v, (float)x.e[e + 1] * v, o.e[e], o.e[e + 1]);
+    return o;
+}
+__device__ __forceinline__ Row8v<float> vx_piece(const Row8v<float> &x, float v) {
+    Row8v<float> o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.e[e] = x.e[e] * v;
+    return o;
+}
+
+// Stages block jb of the span: B as operand, x weighted by v.
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f, typename Op<IO>::type *buf,
-                                         SpRows<HPW> &rows, int64_t c, int bi0,
-                                         const SpPtrs<IO> &sp, int tid) {
+                                         const SpSpan<HPW> &sv, int jb, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT;
-    OP *Bs = buf, *Xs = buf + K::SR * K::LDB;
+    OP *Bs = buf, *Xs = buf + T * K::LDB;
 #pragma unroll
     for (int k = 0; k < K::KB; ++k) {
         const int q = tid + k * K::NT;
@@ -196,32 +256,10 @@ __device__ __forceinline__ void sp_stage(const SpBuf<IO, P, N, HPW> &f, typename
     for (int k = 0; k < K::KX; ++k) {
         const int q = tid + k * K::NT;
         if (K::NPX % K::NT == 0 || q < K::NPX) {
-            const int hs = q / (K::SR * P / 8), qq = q % (K::SR * P / 8);
-            st_row8(Xs + hs * K::XS + (qq / (P / 8)) * K::LDX + (qq % (P / 8)) * 8,
-                    op_piece(f.xv[k]));
-        }
-    }
-    if (tid < HPW * K::SR) {  // one row per thread; 32-lane groups scan a block
-        const int hs = tid / K::SR, r = tid % K::SR;
-        const float d = r < f.nv ? time_step(f.dtv, sp.bias, sp.softplus, sp.dt_min, sp.dt_max)
-                                 : 0.f;
-        float a = sp.a2 * d;
-        // inclusive scan inside each 32-lane half (one block each)
-#pragma unroll
-        for (int off = 1; off < T; off <<= 1) {
-            const float v = __shfl_up(a, off, T);
-            if ((r & (T - 1)) >= off) a += v;
-        }
-        const float last = __shfl(a, T - 1, T);
-        const float w = exp2_fast(last - a) * d;
-        rows.w[hs][r] = w;
-        rows.lcs[hs][r] = a;
-        const int64_t R = (int64_t)bi0 * T + r;  // padded row inside the chunk
-        if (R < sp.Qp) {
-            const int64_t idx = hs * sp.hrow + c * sp.Qp + R;
-            sp.lcs[idx] = a;
-            sp.dtp[idx] = d;
-            sp.wgt[idx] = w;
+            const int hs = q / (T * P / 8), qq = q % (T * P / 8);
+            const int j = qq / (P / 8);
+            st_row8(Xs + hs * K::XS + j * K::LDX + (qq % (P / 8)) * 8,
+                    vx_piece(f.xv[k], sv.v[hs][jb * T + j]));
         }
     }
 }
@@ -238,65 +276,33 @@ __device__ __forceinline__ void sp_store_t(float *dst, const f32x4 *acc, int c0,
                                        4 * (lane >> 4)) = acc[u * K::RT + tr];
 }
 
-// A k-major x fragment (rows = block rows kb + 4g + r, kb + 16 + 4g + r)
-// scaled row by row by w.
-__device__ __forceinline__ f16x8 wx_frag(const f16x8 &xf, int q, int lane, const float *w) {
-    const int g = lane >> 4;
-    const f32x4 wa = *reinterpret_cast<const f32x4 *>(w + 4 * g);
-    const f32x4 wb = *reinterpret_cast<const f32x4 *>(w + 16 + 4 * g);
-    const f16x2 o0 = pk2((float)xf[0] * wa[0], (float)xf[1] * wa[1]);
-    const f16x2 o1 = pk2((float)xf[2] * wa[2], (float)xf[3] * wa[3]);
-    const f16x2 o2 = pk2((float)xf[4] * wb[0], (float)xf[5] * wb[1]);
-    const f16x2 o3 = pk2((float)xf[6] * wb[2], (float)xf[7] * wb[3]);
-    return f16x8{o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
-}
-__device__ __forceinline__ float wx_frag(float xf, int q, int lane, const float *w) {
-    return xf * w[16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)];
-}
-
-// Applies the staged slab's nb blocks to the wave's tiles; returns the
-// slab's log2 decay.
+// Adds the staged block to the wave's tiles: S += B^T (v x).
 template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ float sp_apply(f32x4 *acc, const typename Op<IO>::type *buf, int nb,
-                                          const SpRows<HPW> &rows, int hs, int c0, int lane) {
+__device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type *buf, int hs,
+                                         int c0, int lane) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::M M;
-    constexpr int T = kT, KS = K::KS;
+    constexpr int KS = K::KS;
     const auto *Bs = buf;
-    const auto *Xs = buf + K::SR * K::LDB + hs * K::XS;
-    float ld = 0.f;
+    const auto *Xs = buf + kT * K::LDB + hs * K::XS;
 #pragma unroll
-    for (int jb = 0; jb < K::SLAB; ++jb) {
-        if (jb < nb) {
-            const float lam = __builtin_bit_cast(
-                float, __builtin_amdgcn_readfirstlane(
-                           __builtin_bit_cast(int, rows.lcs[hs][jb * T + T - 1])));
-            ld += lam;
-            const float decay = exp2_fast(lam);
+    for (int q = 0; q < KS; ++q) {
+        typename Mfma<typename K::OP>::frag xf[K::CPW];
 #pragma unroll
-            for (int k = 0; k < K::TPW; ++k) acc[k] *= decay;
+        for (int u = 0; u < K::CPW; ++u) xf[u] = frag_kmajor(Xs, K::LDX, 0, q, c0 + 16 * u, lane);
 #pragma unroll
-            for (int q = 0; q < KS; ++q) {
-                typename Mfma<typename K::OP>::frag xf[K::CPW];
+        for (int tr = 0; tr < K::RT; ++tr) {
+            const auto bt = frag_kmajor(Bs, K::LDB, 0, q, tr * 16, lane);
 #pragma unroll
-                for (int u = 0; u < K::CPW; ++u)
-                    xf[u] = wx_frag(frag_kmajor(Xs, K::LDX, jb * T, q, c0 + 16 * u, lane), q, lane,
-                                    &rows.w[hs][jb * T]);
-#pragma unroll
-                for (int tr = 0; tr < K::RT; ++tr) {
-                    const auto bt = frag_kmajor(Bs, K::LDB, jb * T, q, tr * 16, lane);
-#pragma unroll
-                    for (int u = 0; u < K::CPW; ++u)
-                        acc[u * K::RT + tr] = M::mma(bt, xf[u], acc[u * K::RT + tr]);
-                }
-            }
+            for (int u = 0; u < K::CPW; ++u)
+                acc[u * K::RT + tr] = M::mma(bt, xf[u], acc[u * K::RT + tr]);
         }
     }
-    return ld;
 }
 
 template <typename IO, int P, int N, int HPW>
-__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
+// bf16 io: three workgroups per compute unit (at most 168 VGPRs)
+__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1)) void k_chunk_state(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
@@ -304,9 +310,9 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
     int64_t nc, int64_t Qp) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
-    constexpr int T = kT, SLAB = K::SLAB, TPW = K::TPW;
+    constexpr int T = kT, SPAN = K::SPAN, TPW = K::TPW;
     __shared__ __attribute__((aligned(16))) OP lds[K::BUF];
-    __shared__ __attribute__((aligned(16))) SpRows<HPW> rows;
+    __shared__ __attribute__((aligned(16))) SpSpan<HPW> span;
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
@@ -319,9 +325,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
     const int hh = hh0 + hs;
     const int c0 = (wave % K::WPH) * K::PW;        // this wave's first column
     const int nsb = (int)(Qp / T);
-    const int nspc = (nsb + SLAB - 1) / SLAB;      // slabs of the chunk
     const int64_t NP = (int64_t)N * P;
-    SpPtrs<IO> sp;
+    SpPtrs<IO, HPW> sp;
     sp.xs = (int64_t)h * P;
     sp.bs = (int64_t)g * N;
     sp.x = x + (b * l * h + hh0) * P;
@@ -330,10 +335,10 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
     sp.lcs = lcs + (b * h + hh0) * nc * Qp;
     sp.dtp = dtp + (b * h + hh0) * nc * Qp;
     sp.wgt = wgt + (b * h + hh0) * nc * Qp;
-    {
-        const int rh = hh0 + (tid < HPW * K::SR ? tid / K::SR : 0);  // the row thread's head
-        sp.a2 = A[rh] * kLog2e;
-        sp.bias = dt_bias ? dt_bias[rh] : 0.f;
+#pragma unroll
+    for (int k = 0; k < HPW; ++k) {
+        sp.a2[k] = A[hh0 + k] * kLog2e;
+        sp.bias[k] = dt_bias ? dt_bias[hh0 + k] : 0.f;
     }
     sp.softplus = softplus;
     sp.dt_min = dt_min;
@@ -342,7 +347,6 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
     sp.l = l;
     sp.Q = Q;
     sp.h = h;
-    sp.nsb = nsb;
     sp.Qp = Qp;
 
     f32x4 acc[TPW];
@@ -352,20 +356,32 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT)) void k_chunk_state(
 
     SpBuf<IO, P, N, HPW> pa, pb;
     sp_prefetch(pa, c, 0, true, sp, tid);
-    sp_prefetch(pb, c, SLAB, nspc > 1, sp, tid);
-    for (int si = 0; si < nspc; si += 2) {
+    sp_prefetch(pb, c, 1, nsb > 1, sp, tid);
+    for (int k0 = 0; k0 < nsb; k0 += 2) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             SpBuf<IO, P, N, HPW> &pf = half == 0 ? pa : pb;
-            const int k = si + half;
-            const bool live = k < nspc;
-            const int bi0 = k * SLAB;
-            const int nb = live ? (nsb - bi0 < SLAB ? nsb - bi0 : SLAB) : 0;
-            lds_barrier();  // the previous slab's reads are done
-            if (live) sp_stage(pf, lds, rows, c, bi0, sp, tid);
-            sp_prefetch(pf, c, (k + 2) * SLAB, k + 2 < nspc, sp, tid);
+            const int k = k0 + half;
+            const bool live = k < nsb;
+            if (live && k % SPAN == 0) {  // a new span: its weights, then the decay
+                sp_span<IO, P, N, HPW>(span, c, k, sp, tid);
+                float L = 0.f;
+#pragma unroll
+                for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
+                L = __builtin_bit_cast(float,
+                                       __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L)));
+                if (k > 0) {
+                    const float decay = exp2_fast(L);
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) acc[t] *= decay;
+                }
+                logdec += L;
+            }
+            lds_barrier();  // the previous block's reads are done
+            if (live) sp_stage(pf, lds, span, k % SPAN, tid);
+            sp_prefetch(pf, c, k + 2, k + 2 < nsb, sp, tid);
             lds_barrier();
-            logdec += sp_apply<IO, P, N, HPW>(acc, lds, nb, rows, hs, c0, lane);
+            if (live) sp_apply<IO, P, N, HPW>(acc, lds, hs, c0, lane);
         }
     }
     sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
