@@ -37,12 +37,6 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
 __device__ __forceinline__ float to_f32(f16 v) { return (float)v; }
 
-template <typename T> __device__ __forceinline__ T from_f32(float v);
-template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
-// fp32 -> bf16 / fp16, round to nearest even
-template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
-template <> __device__ __forceinline__ f16 from_f32<f16>(float v) { return (f16)v; }
-
 // 2^x on the transcendental unit (v_exp_f32); 2^(-large) -> 0, never NaN
 // for finite x.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -100,14 +94,6 @@ template <> struct Mfma<float> {
     }
 };
 
-// Row-major fragment of an LDS matrix M[row][k] (k contiguous, row stride ld).
-template <typename OP>
-__device__ __forceinline__ typename Mfma<OP>::frag
-lds_frag(const OP *M, int ld, int row0, int k0, int lane) {
-    const OP *p = M + (row0 + (lane & 15)) * ld + k0 + Mfma<OP>::KPL * (lane >> 4);
-    return *reinterpret_cast<const typename Mfma<OP>::frag *>(p);
-}
-
 // Operands stored k-major in LDS (M[k][col], col contiguous) are read with
 // the gfx950 transposing LDS load ds_read_b64_tr_b16: inside each group of
 // 16 lanes, lane 4r + c supplies the address of elements 4c..4c+3 of row r
@@ -141,33 +127,6 @@ __device__ __forceinline__ float frag_kmajor(const float *M, int ld, int kb, int
     return M[(kb + 16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)) * ld + c0 + (lane & 15)];
 }
 
-// Column c0 + (lane & 15), rows k0 + 4g + r (r = 0..3) of a k-major matrix:
-// the accumulator layout of a tile.
-__device__ __forceinline__ f32x4 lds_col4(const f16 *M, int ld, int k0, int c0, int lane) {
-    const f16x4 v = lds_tr4(M, ld, k0, c0, lane);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ f32x4 lds_col4(const float *M, int ld, int k0, int c0, int lane) {
-    const float *p = M + (k0 + 4 * (lane >> 4)) * ld + c0 + (lane & 15);
-    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
-}
-
-// Row-major matrix M[row][k] read in the k-major contraction convention:
-// lane l gets row row0 + (l & 15) at k = kb + 4g + r and kb + 16 + 4g + r
-// (fp16), or at k = kb + 16 (q >> 2) + 4g + (q & 3) for fp32 step q.  Pairs
-// with a k-major or accumulator-made partner operand.
-__device__ __forceinline__ f16x8 frag_rows_kconv(const f16 *M, int ld, int row0, int kb, int,
-                                                 int lane) {
-    const f16 *p = M + (row0 + (lane & 15)) * ld + kb + 4 * (lane >> 4);
-    const f16x4 a = *reinterpret_cast<const f16x4 *>(p);
-    const f16x4 b = *reinterpret_cast<const f16x4 *>(p + 16);
-    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ float frag_rows_kconv(const float *M, int ld, int row0, int kb, int q,
-                                                 int lane) {
-    return M[(row0 + (lane & 15)) * ld + kb + 16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)];
-}
-
 // Two fp32 values -> packed fp16 pair, rounded toward zero (one instruction;
 // error below 2^-11 relative).
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -196,21 +155,6 @@ __device__ __forceinline__ float frag_from_acc<float>(const f32x4 &t0, const f32
     return (q >> 2) ? t1[q & 3] : t0[q & 3];
 }
 
-// 4 consecutive operand values from LDS, as fp32.
-__device__ __forceinline__ f32x4 lds_load4(const f16 *p) {
-    const f16x4 v = *reinterpret_cast<const f16x4 *>(p);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-__device__ __forceinline__ f32x4 lds_load4(const float *p) {
-    return *reinterpret_cast<const f32x4 *>(p);
-}
-
-// 4 consecutive outputs (round to nearest even for bf16).
-__device__ __forceinline__ void store4(bf16 *p, f32x4 v) {
-    *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-}
-__device__ __forceinline__ void store4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
-
 // ------------------------------------------------- swizzled LDS matrices ----
 // An LDS matrix M[row][col] with NCOL columns and no row padding, whose
 // 16-byte chunks are stored at chunk index (col / EPC) ^ f(row).  f maps
@@ -230,17 +174,10 @@ template <typename T, int NCOL> struct Swz {
     }
 };
 
-// Row-major fragment (as lds_frag) of a swizzled matrix.
-template <typename OP, int NCOL>
-__device__ __forceinline__ typename Mfma<OP>::frag swz_frag(const OP *M, int row0, int k0,
-                                                            int lane) {
-    typedef Swz<OP, NCOL> S;
-    const OP *p = M + S::at(row0 + (lane & 15), k0 + Mfma<OP>::KPL * (lane >> 4));
-    return *reinterpret_cast<const typename Mfma<OP>::frag *>(p);
-}
-
-// Row-major rows read in the k-major contraction convention (as
-// frag_rows_kconv) from a swizzled matrix.
+// Row-major rows M[row][k] read in the k-major contraction convention from a
+// swizzled matrix: lane l gets row row0 + (l & 15) at k = kb + 4g + r and
+// kb + 16 + 4g + r (fp16), or at k = kb + 16 (q >> 2) + 4g + (q & 3) for fp32
+// step q.  Pairs with a k-major or accumulator-made partner operand.
 template <typename OP, int NCOL>
 __device__ __forceinline__ typename Mfma<OP>::frag swz_rows_kconv(const OP *M, int row0, int kb,
                                                                   int q, int lane) {
@@ -335,9 +272,6 @@ __device__ __forceinline__ f16x8 swzp_kmajor(const f16 *M, int kb, int c0, int l
 // 8 consecutive elements of one row, moved with vector loads and stores.
 template <typename T> struct alignas(16) Row8v { T e[8]; };
 
-template <typename T> __device__ __forceinline__ Row8v<T> ld_row8(const T *p) {
-    return *reinterpret_cast<const Row8v<T> *>(p);
-}
 template <typename T> __device__ __forceinline__ void st_row8(T *dst, const Row8v<T> &v) {
     *reinterpret_cast<Row8v<T> *>(dst) = v;
 }
