@@ -88,10 +88,13 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
         # and decays written
         return x + BC + th * s + 3 * rows + 4 * st + b * h * nc * 4
     if name == "state_scan":
-        # chunk states and decays read, boundary states written
-        return 4 * st + b * h * nc * 4 + so * st + fin
+        # chunk states and decays read, boundary states written; on the bf16
+        # path also B and C read once and their fp16 block images written
+        img = 2 * BC + 2 * b * nc * g * (-(-Q // 32) * 32) * n * 2 if s == 2 else 0
+        return 4 * st + b * h * nc * 4 + so * st + fin + img
     if name == "chunk_out":
-        # x, B, C and the lcs, d and weight rows read, boundary states read, y written
+        # x, B and C (bf16 path: their fp16 block images, the same size), the
+        # lcs, d and weight rows and the boundary states read, y written
         return x + 2 * BC + 3 * rows + so * st + x
     raise KeyError(name)
 

@@ -120,8 +120,11 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
  * chunk-boundary states [batch, chunks, heads, head_dim, state_dim]
  * (transposed; fp16 for bf16 io, fp32 for fp32 io, room reserved for fp32);
  * every chunk's own state from zero, same shape, fp32; the log2 decay of
- * every chunk [batch, heads, chunks] fp32.  The layout is the same for both
- * io dtypes.
+ * every chunk [batch, heads, chunks] fp32; C and B of every 32-row block of
+ * every (batch, chunk, group) converted to fp16 and ordered as the chunk
+ * output holds them on chip ([batch, chunks, groups, ceil(chunk / 32)]
+ * blocks of 2 x 32 x state_dim elements; written and read with bf16 io
+ * only).  The layout is the same for both io dtypes.
  */
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim,

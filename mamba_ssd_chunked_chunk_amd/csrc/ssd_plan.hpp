@@ -1,5 +1,5 @@
 // Host-side launch plan of one ssd_chunk_scan call: sizes, the padded row
-// space, the segment split of the serial chunk pass and the workspace map.
+// space and the workspace map.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,7 +21,7 @@ struct ScanPlan {
     int64_t Qp;   // padded rows per chunk
     int64_t lp;   // padded rows per sequence (nc * Qp)
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, total;
+    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, off_img, total;
 };
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
@@ -55,6 +55,9 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     P.off_hb = o;   o += align256(b * P.nc * h * st * 4);
     P.off_st = o;   o += align256(b * P.nc * h * st * 4);  // chunk states, fp32
     P.off_lam = o;  o += align256(b * h * P.nc * 4);       // chunk log2 decays
+    // C and B of every 32-row block of every (batch, chunk, group) as fp16,
+    // in the chunk output's LDS layout (bf16 io only; room kept for both)
+    P.off_img = o;  o += align256(b * P.nc * g * P.nsb * 2 * P.T * n * 2);
     P.total = o;
     return true;
 }

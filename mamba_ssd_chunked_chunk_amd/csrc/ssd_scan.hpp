@@ -405,16 +405,79 @@ __device__ __forceinline__ void store_state4(float *p, const f32x4 &v) {
     *reinterpret_cast<f32x4 *>(p) = v;
 }
 
-template <typename OP>
+// Block images for the chunk output (bf16 io): C and B of every 32-row block
+// of every (batch, chunk, group) converted to fp16 and laid out exactly as
+// the chunk output keeps them in LDS (swizzled, paired column order), so
+// that it can copy a block straight from memory into LDS.  Image of block
+// (b, c, gi, j): [C (T x N) | B (T x N)], fp16; rows past the chunk's or
+// the sequence's end are zero.  One thread per 16-byte chunk of the image:
+// in paired order, chunk 4m + g of a row holds columns 32m + 4g .. + 3 and
+// 32m + 16 + 4g .. + 3, and the swizzle stores logical chunk k at k ^ f(r).
+// The image workgroups come first in the state-scan grid and are few (each
+// thread converts kImgPerThread chunks), so that they run beside the long
+// scan workgroups instead of after them.
+constexpr int kImgPerThread = 8;
+struct ImgArgs {
+    const void *B, *C;  // io dtype [batch, seqlen, groups, N]
+    f16 *img;
+    int64_t l, Q, nc, nsb, pieces;
+    int g;
+};
+
+template <typename IO, int N>
+__device__ __forceinline__ void bc_image_piece(const ImgArgs &ia, int64_t q) {
+    if constexpr (sizeof(IO) == 2) {
+        constexpr int T = kT, CPR = N / 8;  // 16-byte chunks per row
+        const int k = (int)(q % CPR);       // stored chunk
+        q /= CPR;
+        const int r = (int)(q % T);
+        q /= T;
+        const int which = (int)(q & 1);  // 0: C, 1: B
+        q >>= 1;
+        const int64_t blk = q;  // (b, c, gi, j) flattened
+        const int j = (int)(blk % ia.nsb);
+        const int64_t cgi = blk / ia.nsb;
+        const int gi = (int)(cgi % ia.g);
+        const int64_t bc = cgi / ia.g;
+        const int64_t c = bc % ia.nc, b = bc / ia.nc;
+        const int64_t row = (int64_t)j * T + r, t = c * ia.Q + row;
+        const int kl = k ^ Swz<f16, N>::f(r);                 // logical chunk
+        const int col = 32 * (kl >> 2) + 4 * (kl & 3);        // first of 4 + 4 columns
+        u32x2 lo{0u, 0u}, hi{0u, 0u};
+        if (row < ia.Q && t < ia.l) {
+            const IO *src = static_cast<const IO *>(which ? ia.B : ia.C) +
+                            ((b * ia.l + t) * ia.g + gi) * N + col;
+            lo = *reinterpret_cast<const u32x2 *>(src);
+            hi = *reinterpret_cast<const u32x2 *>(src + 16);
+        }
+        Row8v<IO> v;
+        __builtin_memcpy(&v.e[0], &lo, 8);
+        __builtin_memcpy(&v.e[4], &hi, 8);
+        *reinterpret_cast<Row8v<f16> *>(ia.img + blk * (2 * T * N) + which * (T * N) + r * N +
+                                        k * 8) = op_piece(v);
+    }
+}
+
+template <typename OP, typename IO, int N>
 __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St,
                                                     const float *__restrict__ Lam,
                                                     const float *__restrict__ init,
                                                     OP *__restrict__ Hb,
                                                     float *__restrict__ final_state, int64_t bh,
-                                                    int h, int64_t nc, int n, int p) {
+                                                    int h, int64_t nc, int n, int p,
+                                                    int64_t img_blocks, ImgArgs ia) {
     constexpr int G8 = 8;
+    if ((int64_t)blockIdx.x < img_blocks) {  // block images: kImgPerThread chunks per thread
+        const int64_t q0 = (int64_t)blockIdx.x * blockDim.x * kImgPerThread + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < kImgPerThread; ++i) {
+            const int64_t q = q0 + (int64_t)i * blockDim.x;
+            if (q < ia.pieces) bc_image_piece<IO, N>(ia, q);
+        }
+        return;
+    }
     const int64_t np4 = (int64_t)n * p / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t idx = ((int64_t)blockIdx.x - img_blocks) * blockDim.x + threadIdx.x;
     if (idx >= bh * np4) return;
     const int64_t pair = idx / np4, e4 = idx % np4;
     const int64_t b = pair / h, hh = pair % h;
@@ -486,32 +549,63 @@ template <typename IO, int P, int N, int HPW> struct Co {
     static constexpr int RT = N / 16;                 // state row tiles
     static constexpr int NB = N / 32;                 // 32-blocks of the state index
     static constexpr int KS = T / M::K;               // MFMA steps per 32-block
-    static constexpr int LDX = P + 16;                // [row][p]: x
+    // bf16 io: blocks are copied into LDS by the buffer unit (C and B from
+    // their fp16 block images, x as raw bf16 in rows of head_dim elements);
+    // fp32 io: staged through registers, x rows padded
+    static constexpr bool DMA = sizeof(IO) == 2;
+    static constexpr int LDX = DMA ? P : P + 16;      // [row][p]: x
     static constexpr int XS = T * LDX;                // one head's staged x
     static constexpr int BUF = 2 * T * N + HPW * XS;  // [C | B | x of each head]
-    // staging pieces (8 elements) per thread
+    // staging pieces (8 elements) per thread (fp32 io)
     static constexpr int NPC = T * N / 8, NPX = HPW * T * P / 8;
     static constexpr int KC = (NPC + NT - 1) / NT, KX = (NPX + NT - 1) / NT;
+    // 16-byte copies per block (bf16 io): C and B image, x of all heads
+    static constexpr int CBQ = T * N / 4, XQ = HPW * T * P / 8;
+    static constexpr int ND = DMA ? (CBQ + XQ) / NT : 0;  // copy instructions per thread
+    static_assert(!DMA || (CBQ % NT == 0 && XQ % NT == 0), "whole copy rounds per wave");
+    // buffer stores of y per thread and block
+    static constexpr int NS = CPW % 2 == 0 ? CPW * (DMA ? 1 : 2) : 2 * CPW;
 };
+
+// Raw bf16 x in LDS (bf16 io): row r of a head holds head_dim elements in
+// 16-byte chunks, chunk k at position k ^ xsw(r).  With 8-byte pieces read
+// by the transposing loads, this leaves at most two lanes per bank.
+template <int P> __device__ __forceinline__ int xsw(int r) {
+    return ((((r >> 1) & 3) << 2)) & (P / 8 - 1);
+}
+template <int P> __device__ __forceinline__ int xsw_at(int r, int col) {
+    return r * P + (((col >> 3) ^ xsw<P>(r)) << 3) + (col & 7);
+}
 
 
 // Per-row factors of one head's staged block (LDS), T floats each.
+// Values read per output row i are kept in pairs (i, i + 16), so that a lane
+// reads the two rows it owns with one 8-byte access.
 struct alignas(16) CoRows {
     float lcs[kT];   // cumulative log2 decay inside the block
     float d[kT];     // time step
-    float a[kT];     // 2^(lcs_i - lcs_15)
+    float a2[kT];    // 2^(lcs_i - lcs_15), pairs (i, i + 16) at 2 (i % 16)
+    float l2[kT];    // lcs_i in the same pairs
     float bw[kT];    // 2^(lcs_15 - lcs_j) d_j
     float w[kT];     // 2^(lcs_31 - lcs_j) d_j: weight in the state at the block's end
 };
+__device__ __forceinline__ int row_pair(int r) { return 2 * (r & 15) + (r >> 4); }
 
-// Register prefetch of one block for the whole workgroup.  Loads go through
-// buffer resources that end at the chunk's last valid row (zeros beyond).
+// Row factors of one block, loaded by thread tid for head tid / kT, row
+// tid % kT (threads past HPW * kT load and discard).
+struct CoRowV {
+    float ls, ds, ws, l15;
+};
+
+// Register prefetch of one block for the whole workgroup (fp32 io).  Loads
+// go through buffer resources that end at the chunk's last valid row (zeros
+// beyond).
 template <typename IO, int P, int N, int HPW> struct CoBuf {
     typedef Co<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     Row8v<IO> cv[K::KC], bv[K::KC];
     Row8v<IO> xv[K::KX];
-    float ls, ds, ws, l15;  // row factors of (head tid / kT, row tid % kT)
+    CoRowV r;
 };
 
 // Per-workgroup addressing.
@@ -524,7 +618,80 @@ template <typename IO> struct CoPtrs {
     int64_t xs, bs;     // row strides (elements) of x / y and of B / C
     uint32_t hstride;   // bytes from one head's row arrays to the next
     int rows;           // valid rows of the chunk
+    Rsrc rimg;          // block images of this (batch, chunk, group) (bf16 io)
 };
+
+template <int HPW, typename IO>
+__device__ __forceinline__ void co_rows_prefetch(CoRowV &f, int s, const CoPtrs<IO> &cp, int tid) {
+    constexpr int T = kT;
+    const int hs = tid < HPW * T ? tid / T : 0, row = tid % T;
+    const uint32_t soff = (uint32_t)(s * T) * 4u;
+    const uint32_t ro = (uint32_t)hs * cp.hstride + (uint32_t)row * 4u;
+    f.ls = buf_f32(cp.rl, ro, soff);
+    f.ds = buf_f32(cp.rd, ro, soff);
+    f.ws = buf_f32(cp.rw, ro, soff);
+    f.l15 = buf_f32(cp.rl, (uint32_t)hs * cp.hstride + 15u * 4u, soff);
+}
+
+template <int HPW>
+__device__ __forceinline__ void co_rows_stage(const CoRowV &f, CoRows *rows, int tid) {
+    constexpr int T = kT;
+    if (tid < HPW * T) {
+        CoRows &rw = rows[tid / T];
+        const int r = tid % T;
+        rw.lcs[r] = f.ls;
+        rw.d[r] = f.ds;
+        rw.a2[row_pair(r)] = exp2_fast(f.ls - f.l15);
+        rw.l2[row_pair(r)] = f.ls;
+        rw.bw[r] = exp2_fast(f.l15 - f.ls) * f.ds;
+        rw.w[r] = f.ws;
+    }
+}
+
+// bf16 io: block s copied into LDS buffer buf by the buffer unit, 16 bytes
+// per lane and instruction, each wave filling 1 KB of consecutive LDS per
+// instruction: C and B from the block image (already in LDS order), x as
+// raw bf16 with each lane fetching the 16-byte chunk its LDS slot holds.
+// Rows past the chunk's end read as zeros.  Issues exactly K::ND copies per
+// thread.
+typedef __attribute__((address_space(3))) void lds_void;
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void co_dma(typename Op<IO>::type *buf, int s, const CoPtrs<IO> &cp,
+                                       int wave, int lane) {
+    typedef Co<IO, P, N, HPW> K;
+    constexpr int T = kT, CH = P / 8;
+#pragma unroll
+    for (int q0 = 0; q0 < K::CBQ; q0 += K::NT) {
+        const int q = q0 + wave * 64;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cp.rimg, (lds_void *)(buf + q * 8), 16, (uint32_t)((s * K::CBQ + q + lane) * 16), 0, 0, 0);
+    }
+    const int r0 = s * T;
+    int valid = cp.rows - r0;
+    valid = valid < 0 ? 0 : (valid > T ? T : valid);
+    const Rsrc rx = make_rsrc(cp.x + (valid > 0 ? r0 : 0) * cp.xs,
+                              (int64_t)valid * cp.xs * (int)sizeof(IO));
+    typename Op<IO>::type *Xs = buf + 2 * T * N;
+#pragma unroll
+    for (int q0 = 0; q0 < K::XQ; q0 += K::NT) {
+        const int qw = q0 + wave * 64, q = qw + lane;
+        const int hs = q / (T * CH), rem = q % (T * CH), r = rem / CH, k = rem % CH;
+        const uint32_t off =
+            (uint32_t)(r * cp.xs + hs * P + ((k ^ xsw<P>(r)) << 3)) * (uint32_t)sizeof(IO);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(Xs + qw * 8), 16, off, 0, 0, 0);
+    }
+}
+
+// Keeps the memory operations before and after it in program order, so that
+// the counts given to vm_wait match the order of issue.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (they complete in issue order).
+template <int N> __device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, const CoPtrs<IO> &cp,
@@ -559,13 +726,7 @@ __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, cons
                                            (uint32_t)sizeof(IO));
         }
     }
-    const int hs = tid < HPW * T ? tid / T : 0, row = tid % T;
-    const uint32_t soff = (uint32_t)r0 * 4u;
-    const uint32_t ro = (uint32_t)hs * cp.hstride + (uint32_t)row * 4u;
-    f.ls = buf_f32(cp.rl, ro, soff);
-    f.ds = buf_f32(cp.rd, ro, soff);
-    f.ws = buf_f32(cp.rw, ro, soff);
-    f.l15 = buf_f32(cp.rl, (uint32_t)hs * cp.hstride + 15u * 4u, soff);
+    co_rows_prefetch<HPW>(f.r, s, cp, tid);
 }
 
 template <typename IO, int P, int N, int HPW>
@@ -598,15 +759,7 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
                     op_piece(f.xv[k]));
         }
     }
-    if (tid < HPW * T) {
-        CoRows &rw = rows[tid / T];
-        const int r = tid % T;
-        rw.lcs[r] = f.ls;
-        rw.d[r] = f.ds;
-        rw.a[r] = exp2_fast(f.ls - f.l15);
-        rw.bw[r] = exp2_fast(f.l15 - f.ls) * f.ds;
-        rw.w[r] = f.ws;
-    }
+    co_rows_stage<HPW>(f.r, rows, tid);
 }
 
 // Decay-weighted x, w_j x_j, as the k-major B operand of the state carry:
@@ -651,6 +804,30 @@ __device__ __forceinline__ f16x8 xs_frag(const f16 *Xs, int ldx, int q, int c0, 
 template <int CPW>
 __device__ __forceinline__ float xs_frag(const float *Xs, int ldx, int q, int c0, int u, int lane) {
     return Xs[(16 * (q >> 2) + 4 * (lane >> 4) + (q & 3)) * ldx + c0 + co_col<CPW>(u, lane & 15)];
+}
+
+// The same fragment from raw bf16 x in the swizzled rows of the copied
+// layout, converted to fp16 operands (exact bf16 -> fp32, then rounded
+// toward zero, as the register-staged path does).
+template <int CPW, int P>
+__device__ __forceinline__ f16x8 xs_frag_raw(const f16 *Xs, int c0, int u, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int col = c0 + co_col<CPW>(u, 4 * (j & 3));
+    const int ra = 4 * g + (j >> 2), rb = 16 + ra;
+    const u32x2 a = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(Xs + xsw_at<P>(ra, col))));
+    const u32x2 b = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(Xs + xsw_at<P>(rb, col))));
+    const u32x4 w{a[0], a[1], b[0], b[1]};
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f16x2 pk = pk2(__builtin_bit_cast(float, w[i] << 16),
+                             __builtin_bit_cast(float, w[i] & 0xffff0000u));
+        o[2 * i] = pk[0];
+        o[2 * i + 1] = pk[1];
+    }
+    return o;
 }
 
 // One block of the chunk output for one wave: head slot hs, columns
@@ -719,7 +896,8 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
         const float s15 = exp2_fast(rf.lcs[15]);
         const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&rf.bw[4 * lg]);
         const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&rf.bw[16 + 4 * lg]);
-        const float a0 = rf.a[li], a1 = rf.a[16 + li];
+        const f32x2 ap = *reinterpret_cast<const f32x2 *>(&rf.a2[2 * li]);
+        const float a0 = ap[0], a1 = ap[1];
         colscale[0] = a0 * s15;
         colscale[1] = a1 * s15;
 #pragma unroll
@@ -730,16 +908,20 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
             pv[1][1][r] = (j0 <= li) ? gt[2][r] * (a1 * b1[r]) : 0.f;
         }
     } else {
-        const float l0 = rf.lcs[li], l1 = rf.lcs[16 + li];
+        const f32x2 lp = *reinterpret_cast<const f32x2 *>(&rf.l2[2 * li]);
+        const float l0 = lp[0], l1 = lp[1];
+        const f32x4 lj0 = *reinterpret_cast<const f32x4 *>(&rf.lcs[4 * lg]);
+        const f32x4 lj1 = *reinterpret_cast<const f32x4 *>(&rf.lcs[16 + 4 * lg]);
+        const f32x4 dj0 = *reinterpret_cast<const f32x4 *>(&rf.d[4 * lg]);
+        const f32x4 dj1 = *reinterpret_cast<const f32x4 *>(&rf.d[16 + 4 * lg]);
         colscale[0] = exp2_fast(l0);
         colscale[1] = exp2_fast(l1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j0 = 4 * lg + r;
-            pv[0][0][r] = (j0 <= li) ? gt[0][r] * exp2_fast(l0 - rf.lcs[j0]) * rf.d[j0] : 0.f;
-            pv[1][0][r] = gt[1][r] * exp2_fast(l1 - rf.lcs[j0]) * rf.d[j0];
-            pv[1][1][r] =
-                (j0 <= li) ? gt[2][r] * exp2_fast(l1 - rf.lcs[16 + j0]) * rf.d[16 + j0] : 0.f;
+            pv[0][0][r] = (j0 <= li) ? gt[0][r] * exp2_fast(l0 - lj0[r]) * dj0[r] : 0.f;
+            pv[1][0][r] = gt[1][r] * exp2_fast(l1 - lj0[r]) * dj0[r];
+            pv[1][1][r] = (j0 <= li) ? gt[2][r] * exp2_fast(l1 - lj1[r]) * dj1[r] : 0.f;
         }
     }
     // the skip term rides on the diagonal: (P + D I) x = P x + D x
@@ -760,7 +942,12 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
 #pragma unroll
     for (int u = 0; u < CPW; ++u)
 #pragma unroll
-        for (int q = 0; q < KS; ++q) xf[u][q] = xs_frag<CPW>(Xs, LDX, q, c0, u, lane);
+        for (int q = 0; q < KS; ++q) {
+            if constexpr (K::DMA)
+                xf[u][q] = xs_frag_raw<CPW, P>(Xs, c0, u, lane);
+            else
+                xf[u][q] = xs_frag<CPW>(Xs, LDX, q, c0, u, lane);
+        }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int i = it * 16 + li;
@@ -834,16 +1021,21 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
 }
 
 template <typename IO, int P, int N, int HPW>
-__global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
+__global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1)) void k_chunk_out(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ lcs, const float *__restrict__ dtp,
     const float *__restrict__ wgt, const typename Op<IO>::type *__restrict__ Hb,
-    IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp) {
+    IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp,
+    const f16 *__restrict__ img, int64_t nsb) {
     typedef Co<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
-    __shared__ __attribute__((aligned(16))) OP lds[2 * BUF];
-    __shared__ CoRows rowsf[2][HPW];
+    // two block buffers as separate objects, so that the compiler can tell
+    // a copy into one from reads of the other
+    __shared__ __attribute__((aligned(16))) OP lds0[BUF];
+    __shared__ __attribute__((aligned(16))) OP lds1[BUF];
+    __shared__ CoRows rows0[HPW];
+    __shared__ CoRows rows1[HPW];
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int lg = lane >> 4, li = lane & 15;
@@ -872,29 +1064,23 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
     cp.rw = make_rsrc(wgt + rbase, rspan);
     cp.hstride = (uint32_t)(nc * Qp * 4);
     cp.rows = (int)((Q < l - t0) ? Q : (l - t0));
+    if constexpr (K::DMA)
+        cp.rimg = make_rsrc(img + ((b * nc + c) * g + gi) * nsb * (2 * T * N),
+                            nsb * (int64_t)(4 * T * N));
     const int nblk = (cp.rows + T - 1) / T;
     const float Dh = D ? D[hh] : 0.f;
 
-    // Block k is fetched into registers pa (k even) or pb (k odd) two blocks
-    // ahead and staged into LDS buffer k & 1 while block k - 1 is computed.
-    // Blocks go in pairs, every load and store issued unconditionally (past
-    // the chunk's end: empty resources; a block past the end is computed on
-    // zeros and stores nothing), so the loop has one path and the memory
-    // counters never need a full drain.
-    CoBuf<IO, P, N, HPW> pa, pb;
-    OP *const buf0 = lds;
-    OP *const buf1 = lds + BUF;
-    co_prefetch(pa, 0, cp, tid);
-    co_prefetch(pb, 1, cp, tid);
+    OP *const buf0 = lds0;
+    OP *const buf1 = lds1;
 
     // ---- the wave's state columns entering the chunk: the boundary state,
     //      stored transposed ([head_dim][state_dim]) in the operand type, so
     //      a lane's 4 accumulator values (consecutive state rows) are one
-    //      load.  Loaded after the first blocks, so that staging block 0
-    //      does not wait for them.
+    //      load.  Loaded after the first block is requested, so that staging
+    //      block 0 does not wait for them.
     typedef typename std::conditional<sizeof(OP) == 2, f16x4, f32x4>::type HRaw;
     HRaw hraw[CPW * RT];
-    {
+    auto load_boundary = [&]() {
         const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * (int64_t)sizeof(OP));
 #pragma unroll
         for (int u = 0; u < CPW; ++u)
@@ -909,25 +1095,83 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT)) void k_chunk_out(
                     hraw[u * RT + tr] = __builtin_bit_cast(
                         f32x4, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
             }
-    }
-    co_stage(pa, buf0, rowsf[0], tid);
-    co_prefetch(pa, 2, cp, tid);
-    lds_barrier();
+    };
     f32x4 accH[CPW * RT];
+
+    if constexpr (K::DMA) {
+        // Block k is copied into LDS buffer k & 1 (its row factors into
+        // registers ra / rb) one block ahead: the copy of block k + 1 is in
+        // flight while block k is computed.  Before each barrier a wave waits
+        // for its own copies of the next block; only the y stores of the
+        // block just computed may still be in flight then.  Blocks go in
+        // pairs with every copy and store issued unconditionally (past the
+        // chunk's end the copies read zeros and a block computed on them
+        // stores nothing), so every wave issues the same operations and the
+        // counts waited for are exact.
+        CoRowV ra, rb;
+        co_dma<IO, P, N, HPW>(buf0, 0, cp, wave, lane);
+        co_rows_prefetch<HPW>(ra, 0, cp, tid);
+        issue_fence();
+        load_boundary();
+        issue_fence();
+        co_dma<IO, P, N, HPW>(buf1, 1, cp, wave, lane);
+        co_rows_prefetch<HPW>(rb, 1, cp, tid);
+        issue_fence();
+        vm_wait<K::ND + 4>();  // block 0 and the boundary state have landed
+        co_rows_stage<HPW>(ra, rows0, tid);
+        lds_barrier();
 #pragma unroll
-    for (int k = 0; k < CPW * RT; ++k)
-        accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
-    for (int s = 0; s < nblk; s += 2) {
-        co_stage(pb, buf1, rowsf[1], tid);  // block s + 1
-        co_prefetch(pb, s + 3, cp, tid);
-        co_compute<IO, P, N, HPW>(accH, buf0, rowsf[0][hs], s + 1 < nblk, Dh, cp, s * T, hs, c0,
-                                  lane);
+        for (int k = 0; k < CPW * RT; ++k)
+            accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
+        for (int s = 0; s < nblk; s += 2) {
+            co_compute<IO, P, N, HPW>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
+                                      c0, lane);
+            vm_wait<K::NS>();  // block s + 1
+            co_rows_stage<HPW>(rb, rows1, tid);
+            lds_barrier();
+            co_dma<IO, P, N, HPW>(buf0, s + 2, cp, wave, lane);
+            co_rows_prefetch<HPW>(ra, s + 2, cp, tid);
+            issue_fence();
+            co_compute<IO, P, N, HPW>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+                                      hs, c0, lane);
+            vm_wait<K::NS>();  // block s + 2
+            co_rows_stage<HPW>(ra, rows0, tid);
+            lds_barrier();
+            co_dma<IO, P, N, HPW>(buf1, s + 3, cp, wave, lane);
+            co_rows_prefetch<HPW>(rb, s + 3, cp, tid);
+            issue_fence();
+        }
+        // no copy may still be writing this workgroup's LDS when it exits
+        vm_wait<0>();
+    } else {
+        // Block k is fetched into registers pa (k even) or pb (k odd) two
+        // blocks ahead and staged into LDS buffer k & 1 while block k - 1 is
+        // computed.  Blocks go in pairs, every load and store issued
+        // unconditionally (past the chunk's end: empty resources; a block
+        // past the end is computed on zeros and stores nothing), so the loop
+        // has one path and the memory counters never need a full drain.
+        CoBuf<IO, P, N, HPW> pa, pb;
+        co_prefetch(pa, 0, cp, tid);
+        co_prefetch(pb, 1, cp, tid);
+        load_boundary();
+        co_stage(pa, buf0, rows0, tid);
+        co_prefetch(pa, 2, cp, tid);
         lds_barrier();
-        co_stage(pa, buf0, rowsf[0], tid);  // block s + 2
-        co_prefetch(pa, s + 4, cp, tid);
-        co_compute<IO, P, N, HPW>(accH, buf1, rowsf[1][hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
-                                  hs, c0, lane);
-        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < CPW * RT; ++k)
+            accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
+        for (int s = 0; s < nblk; s += 2) {
+            co_stage(pb, buf1, rows1, tid);  // block s + 1
+            co_prefetch(pb, s + 3, cp, tid);
+            co_compute<IO, P, N, HPW>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
+                                      c0, lane);
+            lds_barrier();
+            co_stage(pa, buf0, rows0, tid);  // block s + 2
+            co_prefetch(pa, s + 4, cp, tid);
+            co_compute<IO, P, N, HPW>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+                                      hs, c0, lane);
+            lds_barrier();
+        }
     }
 }
 
@@ -967,10 +1211,23 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
 
     const int64_t np4 = (int64_t)N * P / 4;
     const int64_t tot = pl.b * pl.h * np4;
+    const int64_t scan_blocks = (tot + kThreads - 1) / kThreads;
+    ImgArgs ia;
+    ia.B = a.B;
+    ia.C = a.C;
+    ia.img = reinterpret_cast<f16 *>(a.ws + pl.off_img);
+    ia.l = pl.l;
+    ia.Q = pl.Q;
+    ia.nc = pl.nc;
+    ia.nsb = pl.nsb;
+    ia.g = g;
+    ia.pieces = sizeof(IO) == 2 ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
+    const int64_t img_blocks =
+        (ia.pieces + (int64_t)kThreads * kImgPerThread - 1) / ((int64_t)kThreads * kImgPerThread);
     trace_begin(2, s);
-    hipLaunchKernelGGL(k_state_scan<OP>, dim3((unsigned)((tot + kThreads - 1) / kThreads)),
+    hipLaunchKernelGGL((k_state_scan<OP, IO, N>), dim3((unsigned)(scan_blocks + img_blocks)),
                        dim3(kThreads), 0, s, St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h,
-                       pl.nc, N, P);
+                       pl.nc, N, P, img_blocks, ia);
     trace_end(2, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -979,11 +1236,11 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     if (grouped)
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
                            dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb,
-                           y, pl.l, h, g, pl.Q, pl.nc, pl.Qp);
+                           y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb);
     else
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
                            dim3(Co<IO, P, N, 1>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb, y,
-                           pl.l, h, g, pl.Q, pl.nc, pl.Qp);
+                           pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb);
     trace_end(3, s);
     return hipGetLastError();
 }
