@@ -162,22 +162,32 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
     }
 }
 
-// The per-row values of the span starting at block blk0 (see above); ends
-// with the span's weights visible to the whole workgroup.
+// The raw time steps of the span starting at block blk0, one row of one head
+// per thread and pass.
 template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, int64_t c, int blk0,
-                                        const SpPtrs<IO, HPW> &sp, int tid) {
+__device__ __forceinline__ void sp_dt_load(float *dtv, int64_t c, int blk0,
+                                           const SpPtrs<IO, HPW> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     constexpr int T = kT;
     const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;
-    float dtv[K::NPASS];
 #pragma unroll
-    for (int ps = 0; ps < K::NPASS; ++ps) {  // all raw time steps first
+    for (int ps = 0; ps < K::NPASS; ++ps) {
         const int idx = ps * K::NT + tid;
         const int hs = idx / K::SPR, r = idx % K::SPR;
         const int64_t row = c * sp.Q + (int64_t)blk0 * T + r;
         dtv[ps] = row < cend ? to_f32(sp.dt[row * sp.h + hs]) : 0.f;
     }
+}
+
+// The per-row values of the span starting at block blk0 (see above) from
+// its raw time steps; ends with the span's weights visible to the whole
+// workgroup.
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, int64_t c, int blk0,
+                                        const SpPtrs<IO, HPW> &sp, int tid) {
+    typedef Sp<IO, P, N, HPW> K;
+    constexpr int T = kT;
+    const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;
 #pragma unroll
     for (int ps = 0; ps < K::NPASS; ++ps) {
         const int idx = ps * K::NT + tid;
@@ -354,6 +364,10 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     for (int k = 0; k < TPW; ++k) acc[k] = zero4();
     float logdec = 0.f;
 
+    // the first span's raw time steps are requested before the first blocks,
+    // so that its per-row values are ready as soon as possible
+    float dtv[K::NPASS];
+    sp_dt_load<IO, P, N, HPW>(dtv, c, 0, sp, tid);
     SpBuf<IO, P, N, HPW> pa, pb;
     sp_prefetch(pa, c, 0, true, sp, tid);
     sp_prefetch(pb, c, 1, nsb > 1, sp, tid);
@@ -364,7 +378,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
             const int k = k0 + half;
             const bool live = k < nsb;
             if (live && k % SPAN == 0) {  // a new span: its weights, then the decay
-                sp_span<IO, P, N, HPW>(span, c, k, sp, tid);
+                if (k > 0) sp_dt_load<IO, P, N, HPW>(dtv, c, k, sp, tid);
+                sp_span<IO, P, N, HPW>(span, dtv, c, k, sp, tid);
                 float L = 0.f;
 #pragma unroll
                 for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
