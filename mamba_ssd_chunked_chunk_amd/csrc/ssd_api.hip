@@ -173,8 +173,7 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
         return SSD_ERR_SHAPE;
     // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
     const int64_t gmax = ((int64_t)1 << 31) - 1;
-    if (pl.b * pl.nc * pl.h > gmax ||
-        pl.b * pl.h * pl.n * pl.p / 4 / 256 + pl.b * pl.nc * pl.g * pl.nsb * 8 * pl.n / 256 + 2 > gmax)
+    if (pl.b * pl.nc * pl.h > gmax || pl.b * pl.h * pl.n * pl.p / 4 / 256 + 1 > gmax)
         return SSD_ERR_UNSUPPORTED;
     // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
     // one (batch, head)

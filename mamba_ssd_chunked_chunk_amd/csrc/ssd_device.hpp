@@ -313,6 +313,25 @@ __device__ __forceinline__ void buf_store16(Rsrc r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
+// Issue priority of this wave (0..3, uniform).  Workgroups that share a
+// compute unit advance at different rates under the default oldest-first
+// issue order; raising the priority of waves that are behind in their walk
+// keeps them together, so the unit does not idle at the end.
+__device__ __forceinline__ void wave_priority(int level) {
+    if (level >= 3)
+        __builtin_amdgcn_s_setprio(3);
+    else if (level == 2)
+        __builtin_amdgcn_s_setprio(2);
+    else if (level == 1)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+// Priority for a wave at block k of nblk: 3 at the start, 0 in the last quarter.
+__device__ __forceinline__ int progress_priority(int k, int nblk) {
+    return 3 - (4 * k) / (nblk > 0 ? nblk : 1);
+}
+
 // ----------------------------------------------- workgroup -> work item ----
 // Workgroups are handed to the 8 XCDs round-robin by id (id % 8).  Work items
 // that share data (the heads of one group, the slices of one state) are

@@ -377,6 +377,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
             SpBuf<IO, P, N, HPW> &pf = half == 0 ? pa : pb;
             const int k = k0 + half;
             const bool live = k < nsb;
+            if (half == 0) wave_priority(progress_priority(k, nsb));
             if (live && k % SPAN == 0) {  // a new span: its weights, then the decay
                 if (k > 0) sp_dt_load<IO, P, N, HPW>(dtv, c, k, sp, tid);
                 sp_span<IO, P, N, HPW>(span, dtv, c, k, sp, tid);
@@ -428,10 +429,8 @@ __device__ __forceinline__ void store_state4(float *p, const f32x4 &v) {
 // the sequence's end are zero.  One thread per 16-byte chunk of the image:
 // in paired order, chunk 4m + g of a row holds columns 32m + 4g .. + 3 and
 // 32m + 16 + 4g .. + 3, and the swizzle stores logical chunk k at k ^ f(r).
-// The image workgroups come first in the state-scan grid and are few (each
-// thread converts kImgPerThread chunks), so that they run beside the long
-// scan workgroups instead of after them.
-constexpr int kImgPerThread = 8;
+// Every thread of the state-scan grid converts image chunks in a grid-stride
+// loop before its share of the scan, so the grid stays the scan's own size.
 struct ImgArgs {
     const void *B, *C;  // io dtype [batch, seqlen, groups, N]
     f16 *img;
@@ -480,19 +479,12 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
                                                     OP *__restrict__ Hb,
                                                     float *__restrict__ final_state, int64_t bh,
                                                     int h, int64_t nc, int n, int p,
-                                                    int64_t img_blocks, ImgArgs ia) {
+                                                    ImgArgs ia) {
     constexpr int G8 = 8;
-    if ((int64_t)blockIdx.x < img_blocks) {  // block images: kImgPerThread chunks per thread
-        const int64_t q0 = (int64_t)blockIdx.x * blockDim.x * kImgPerThread + threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < kImgPerThread; ++i) {
-            const int64_t q = q0 + (int64_t)i * blockDim.x;
-            if (q < ia.pieces) bc_image_piece<IO, N>(ia, q);
-        }
-        return;
-    }
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = idx; q < ia.pieces; q += nthreads) bc_image_piece<IO, N>(ia, q);
     const int64_t np4 = (int64_t)n * p / 4;
-    const int64_t idx = ((int64_t)blockIdx.x - img_blocks) * blockDim.x + threadIdx.x;
     if (idx >= bh * np4) return;
     const int64_t pair = idx / np4, e4 = idx % np4;
     const int64_t b = pair / h, hh = pair % h;
@@ -1139,6 +1131,7 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
         for (int k = 0; k < CPW * RT; ++k)
             accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
         for (int s = 0; s < nblk; s += 2) {
+            wave_priority(progress_priority(s, nblk));
             co_compute<IO, P, N, HPW>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
                                       c0, lane);
             vm_wait<K::NS>();  // block s + 1
@@ -1237,12 +1230,9 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     ia.nsb = pl.nsb;
     ia.g = g;
     ia.pieces = sizeof(IO) == 2 ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
-    const int64_t img_blocks =
-        (ia.pieces + (int64_t)kThreads * kImgPerThread - 1) / ((int64_t)kThreads * kImgPerThread);
     trace_begin(2, s);
-    hipLaunchKernelGGL((k_state_scan<OP, IO, N>), dim3((unsigned)(scan_blocks + img_blocks)),
-                       dim3(kThreads), 0, s, St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h,
-                       pl.nc, N, P, img_blocks, ia);
+    hipLaunchKernelGGL((k_state_scan<OP, IO, N>), dim3((unsigned)scan_blocks), dim3(kThreads), 0, s,
+                       St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h, pl.nc, N, P, ia);
     trace_end(2, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
