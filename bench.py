@@ -82,16 +82,19 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
     rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
     so = 2 if s == 2 else 4            # boundary-state element
     st = b * nc * h * n * p            # elements of all chunk (or boundary) states
+    # chunk states needed: the last chunk's only feeds the final state
+    ns = nc if final else nc - 1
+    sn = b * ns * h * n * p
     fin = b * h * n * p * 4 if final else 0
     if name == "chunk_state":
-        # x, B and dt read; the per-row lcs, d and weights, the chunk states
-        # and decays written
-        return x + BC + th * s + 3 * rows + 4 * st + b * h * nc * 4
+        # x, B and dt read; the per-row lcs, d and weights, the needed chunk
+        # states and decays written
+        return x + BC + th * s + 3 * rows + 4 * sn + b * h * ns * 4
     if name == "state_scan":
-        # chunk states and decays read, boundary states written; on the bf16
-        # path also B and C read once and their fp16 block images written
+        # needed chunk states and decays read, boundary states written; on the
+        # bf16 path also B and C read once and their fp16 block images written
         img = 2 * BC + 2 * b * nc * g * (-(-Q // 32) * 32) * n * 2 if s == 2 else 0
-        return 4 * st + b * h * nc * 4 + so * st + fin + img
+        return 4 * sn + b * h * ns * 4 + so * st + fin + img
     if name == "chunk_out":
         # x, B and C (bf16 path: their fp16 block images, the same size), the
         # lcs, d and weight rows and the boundary states read, y written

@@ -317,7 +317,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
     float *__restrict__ St, float *__restrict__ Lam, int64_t l, int h, int g, int64_t Q,
-    int64_t nc, int64_t Qp) {
+    int64_t nc, int64_t Qp, int keep_last) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, SPAN = K::SPAN, TPW = K::TPW;
@@ -400,8 +400,11 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
             if (live) sp_apply<IO, P, N, HPW>(acc, lds, hs, c0, lane);
         }
     }
-    sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
-    if (c0 == 0 && lane == 0) Lam[(b * h + hh) * nc + c] = logdec;
+    // the last chunk's own state only feeds the final state
+    if (c + 1 < nc || keep_last) {
+        sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
+        if (c0 == 0 && lane == 0) Lam[(b * h + hh) * nc + c] = logdec;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -500,21 +503,23 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
     const f32x4 *S = reinterpret_cast<const f32x4 *>(St) + (b * nc * h + hh) * np4 + e4;
     OP *dst = Hb + ((b * nc * h + hh) * np4 + e4) * 4;
     const float *L = Lam + pair * nc;
+    // chunks whose own state is needed: all but the last unless the final
+    // state is asked for (the last chunk's state is then not even written)
+    const int64_t ns = final_state ? nc : nc - 1;
+    const int64_t klast = ns > 0 ? ns - 1 : 0;
     for (int64_t k0 = 0; k0 < nc; k0 += G8) {
         f32x4 Sk[G8];
         float Lk[G8];
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
-            const int64_t k = k0 + u < nc ? k0 + u : nc - 1;
+            const int64_t k = k0 + u < klast ? k0 + u : klast;
             Sk[u] = S[k * cstride];
             Lk[u] = L[k];
         }
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
-            if (k0 + u < nc) {
-                store_state4(dst + (k0 + u) * cstride * 4, H);
-                H = exp2_fast(Lk[u]) * H + Sk[u];
-            }
+            if (k0 + u < nc) store_state4(dst + (k0 + u) * cstride * 4, H);
+            if (k0 + u < ns) H = exp2_fast(Lk[u]) * H + Sk[u];
         }
     }
     if (final_state) {
@@ -1207,12 +1212,12 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
                            dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bm, dt, a.A, a.dt_bias,
                            a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam, pl.l, h, g,
-                           pl.Q, pl.nc, pl.Qp);
+                           pl.Q, pl.nc, pl.Qp, a.final_state != nullptr);
     else
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
                            dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bm, dt, a.A, a.dt_bias,
                            a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam, pl.l, h, g,
-                           pl.Q, pl.nc, pl.Qp);
+                           pl.Q, pl.nc, pl.Qp, a.final_state != nullptr);
     trace_end(1, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
