@@ -70,7 +70,7 @@ def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
     return th * (2 * p * s + 2 * n * s * g / h + s) + 4 * n * p * b * h * (int(init) + int(final))
 
 
-def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
+def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False):
     """Algorithmic bytes of one launch of a scan kernel: every operand of its
     step of the method moved once (per-row workspace arrays fp32, chunk
     states fp32, boundary states in the read-out's operand type: fp16 on the
@@ -85,6 +85,9 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
     # chunk states needed: the last chunk's only feeds the final state
     ns = nc if final else nc - 1
     sn = b * ns * h * n * p
+    # boundary states stored and read: chunk 0's is the initial state, zero
+    # (and neither stored nor read) when none is given
+    sb = b * (nc if init else nc - 1) * h * n * p
     fin = b * h * n * p * 4 if final else 0
     if name == "chunk_state":
         # x, B and dt read; the per-row lcs, d and weights, the needed chunk
@@ -94,11 +97,11 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False):
         # needed chunk states and decays read, boundary states written; on the
         # bf16 path also B and C read once and their fp16 block images written
         img = 2 * BC + 2 * b * nc * g * (-(-Q // 32) * 32) * n * 2 if s == 2 else 0
-        return 4 * sn + b * h * ns * 4 + so * st + fin + img
+        return 4 * sn + b * h * ns * 4 + so * sb + fin + img
     if name == "chunk_out":
         # x, B and C (bf16 path: their fp16 block images, the same size), the
         # lcs, d and weight rows and the boundary states read, y written
-        return x + 2 * BC + 3 * rows + so * st + x
+        return x + 2 * BC + 3 * rows + so * sb + x
     raise KeyError(name)
 
 

@@ -518,7 +518,9 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
         }
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
-            if (k0 + u < nc) store_state4(dst + (k0 + u) * cstride * 4, H);
+            // the boundary state of chunk 0 is only stored for a given
+            // initial state (the chunk output reads zeros otherwise)
+            if (k0 + u < nc && (k0 + u > 0 || init)) store_state4(dst + (k0 + u) * cstride * 4, H);
             if (k0 + u < ns) H = exp2_fast(Lk[u]) * H + Sk[u];
         }
     }
@@ -1038,7 +1040,7 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     const float *__restrict__ D, const float *__restrict__ lcs, const float *__restrict__ dtp,
     const float *__restrict__ wgt, const typename Op<IO>::type *__restrict__ Hb,
     IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp,
-    const f16 *__restrict__ img, int64_t nsb) {
+    const f16 *__restrict__ img, int64_t nsb, int has_init) {
     typedef Co<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
@@ -1093,7 +1095,9 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     typedef typename std::conditional<sizeof(OP) == 2, f16x4, f32x4>::type HRaw;
     HRaw hraw[CPW * RT];
     auto load_boundary = [&]() {
-        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, NP * (int64_t)sizeof(OP));
+        // chunk 0 from a zero initial state: nothing stored, loads read zeros
+        const int64_t hbytes = (c > 0 || has_init) ? NP * (int64_t)sizeof(OP) : 0;
+        const Rsrc rh = make_rsrc(Hb + ((b * nc + c) * h + hh) * NP, hbytes);
 #pragma unroll
         for (int u = 0; u < CPW; ++u)
 #pragma unroll
@@ -1246,11 +1250,11 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     if (grouped)
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
                            dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb,
-                           y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb);
+                           y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb, a.init != nullptr);
     else
         hipLaunchKernelGGL((k_chunk_out<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
                            dim3(Co<IO, P, N, 1>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb, y,
-                           pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb);
+                           pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb, a.init != nullptr);
     trace_end(3, s);
     return hipGetLastError();
 }
