@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace ssd {
 
@@ -32,6 +33,21 @@ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 inline int group_heads(int p, int64_t heads_per_group) {
     const int hp = p >= 64 ? 128 / p : 4;
     return (hp > 1 && heads_per_group % hp == 0) ? hp : 1;
+}
+
+// Whether the bf16 chunk output, with workgroups that share B and C over
+// several heads, copies its blocks into LDS from fp16 block images (written
+// by the state-scan launch) instead of staging them through registers.  The
+// images cost one read of B and C and one write of their fp16 copies; they
+// pay off where that is small against the x stream (8 g n <= h p).
+// SSD_CHUNK_OUT_COPY=0 or 1 in the environment forces either path; both give
+// the same results.
+inline bool chunk_out_copy(int64_t h, int64_t g, int64_t p, int64_t n) {
+    if (const char *e = getenv("SSD_CHUNK_OUT_COPY")) {
+        if (e[0] == '0') return false;
+        if (e[0] == '1') return true;
+    }
+    return 8 * g * n <= h * p;
 }
 
 // Fills the plan from the sizes; returns false if they are invalid.

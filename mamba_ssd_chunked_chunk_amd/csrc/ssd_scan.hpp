@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
 //    exponential per element.
 constexpr float kSplitLimit = 60.f;
 
-template <typename IO, int P, int N, int HPW> struct Co {
+template <typename IO, int P, int N, int HPW, bool COPY = (sizeof(IO) == 2)> struct Co {
     typedef typename Op<IO>::type OP;
     typedef Mfma<OP> M;
     static constexpr int T = kT;
@@ -563,10 +563,10 @@ template <typename IO, int P, int N, int HPW> struct Co {
     static constexpr int RT = N / 16;                 // state row tiles
     static constexpr int NB = N / 32;                 // 32-blocks of the state index
     static constexpr int KS = T / M::K;               // MFMA steps per 32-block
-    // bf16 io: blocks are copied into LDS by the buffer unit (C and B from
-    // their fp16 block images, x as raw bf16 in rows of head_dim elements);
-    // fp32 io: staged through registers, x rows padded
-    static constexpr bool DMA = sizeof(IO) == 2;
+    // COPY (bf16 io only): blocks are copied into LDS by the buffer unit (C
+    // and B from their fp16 block images, x as raw bf16 in rows of head_dim
+    // elements); otherwise staged through registers, x rows padded
+    static constexpr bool DMA = COPY && sizeof(IO) == 2;
     static constexpr int LDX = DMA ? P : P + 16;      // [row][p]: x
     static constexpr int XS = T * LDX;                // one head's staged x
     static constexpr int BUF = 2 * T * N + HPW * XS;  // [C | B | x of each head]
@@ -615,7 +615,7 @@ struct CoRowV {
 // go through buffer resources that end at the chunk's last valid row (zeros
 // beyond).
 template <typename IO, int P, int N, int HPW> struct CoBuf {
-    typedef Co<IO, P, N, HPW> K;
+    typedef Co<IO, P, N, HPW, false> K;
     typedef typename K::OP OP;
     Row8v<IO> cv[K::KC], bv[K::KC];
     Row8v<IO> xv[K::KX];
@@ -672,7 +672,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_dma(typename Op<IO>::type *buf, int s, const CoPtrs<IO> &cp,
                                        int wave, int lane) {
-    typedef Co<IO, P, N, HPW> K;
+    typedef Co<IO, P, N, HPW, true> K;
     constexpr int T = kT, CH = P / 8;
 #pragma unroll
     for (int q0 = 0; q0 < K::CBQ; q0 += K::NT) {
@@ -710,7 +710,7 @@ template <int N> __device__ __forceinline__ void vm_wait() {
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, const CoPtrs<IO> &cp,
                                             int tid) {
-    typedef Co<IO, P, N, HPW> K;
+    typedef Co<IO, P, N, HPW, false> K;
     typedef typename K::OP OP;
     constexpr int T = kT;
     const int r0 = s * T;
@@ -746,7 +746,7 @@ __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, cons
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
                                          typename Op<IO>::type *buf, CoRows *rows, int tid) {
-    typedef Co<IO, P, N, HPW> K;
+    typedef Co<IO, P, N, HPW, false> K;
     typedef typename K::OP OP;
     constexpr int T = kT;
     OP *Cs = buf, *Bs = buf + T * N, *Xs = buf + 2 * T * N;
@@ -847,12 +847,12 @@ __device__ __forceinline__ f16x8 xs_frag_raw(const f16 *Xs, int c0, int u, int l
 // One block of the chunk output for one wave: head slot hs, columns
 // c0 .. c0 + PW - 1 of that head.  accH: the wave's CPW x RT state tiles
 // (inlined: stays in registers).
-template <typename IO, int P, int N, int HPW>
+template <typename IO, int P, int N, int HPW, bool COPY>
 __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::type *buf,
                                            const CoRows &rf, bool carry, float Dh,
                                            const CoPtrs<IO> &cp, int r0, int hs, int c0,
                                            int lane) {
-    typedef Co<IO, P, N, HPW> K;
+    typedef Co<IO, P, N, HPW, COPY> K;
     typedef typename K::OP OP;
     typedef typename K::M M;
     constexpr int T = kT, KS = K::KS, NB = K::NB, LDX = K::LDX, CPW = K::CPW, RT = K::RT;
@@ -924,18 +924,31 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
     } else {
         const f32x2 lp = *reinterpret_cast<const f32x2 *>(&rf.l2[2 * li]);
         const float l0 = lp[0], l1 = lp[1];
-        const f32x4 lj0 = *reinterpret_cast<const f32x4 *>(&rf.lcs[4 * lg]);
-        const f32x4 lj1 = *reinterpret_cast<const f32x4 *>(&rf.lcs[16 + 4 * lg]);
-        const f32x4 dj0 = *reinterpret_cast<const f32x4 *>(&rf.d[4 * lg]);
-        const f32x4 dj1 = *reinterpret_cast<const f32x4 *>(&rf.d[16 + 4 * lg]);
         colscale[0] = exp2_fast(l0);
         colscale[1] = exp2_fast(l1);
+        if constexpr (K::DMA) {
+            // whole 16-byte reads: the compiler can then tell them from the
+            // block copies in flight and does not wait for those
+            const f32x4 lj0 = *reinterpret_cast<const f32x4 *>(&rf.lcs[4 * lg]);
+            const f32x4 lj1 = *reinterpret_cast<const f32x4 *>(&rf.lcs[16 + 4 * lg]);
+            const f32x4 dj0 = *reinterpret_cast<const f32x4 *>(&rf.d[4 * lg]);
+            const f32x4 dj1 = *reinterpret_cast<const f32x4 *>(&rf.d[16 + 4 * lg]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j0 = 4 * lg + r;
-            pv[0][0][r] = (j0 <= li) ? gt[0][r] * exp2_fast(l0 - lj0[r]) * dj0[r] : 0.f;
-            pv[1][0][r] = gt[1][r] * exp2_fast(l1 - lj0[r]) * dj0[r];
-            pv[1][1][r] = (j0 <= li) ? gt[2][r] * exp2_fast(l1 - lj1[r]) * dj1[r] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int j0 = 4 * lg + r;
+                pv[0][0][r] = (j0 <= li) ? gt[0][r] * exp2_fast(l0 - lj0[r]) * dj0[r] : 0.f;
+                pv[1][0][r] = gt[1][r] * exp2_fast(l1 - lj0[r]) * dj0[r];
+                pv[1][1][r] = (j0 <= li) ? gt[2][r] * exp2_fast(l1 - lj1[r]) * dj1[r] : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j0 = 4 * lg + r;
+                pv[0][0][r] = (j0 <= li) ? gt[0][r] * exp2_fast(l0 - rf.lcs[j0]) * rf.d[j0] : 0.f;
+                pv[1][0][r] = gt[1][r] * exp2_fast(l1 - rf.lcs[j0]) * rf.d[j0];
+                pv[1][1][r] =
+                    (j0 <= li) ? gt[2][r] * exp2_fast(l1 - rf.lcs[16 + j0]) * rf.d[16 + j0] : 0.f;
+            }
         }
     }
     // the skip term rides on the diagonal: (P + D I) x = P x + D x
@@ -1034,14 +1047,14 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
     }
 }
 
-template <typename IO, int P, int N, int HPW>
-__global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1)) void k_chunk_out(
+template <typename IO, int P, int N, int HPW, bool COPY>
+__global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT), (Co<IO, P, N, HPW, COPY>::DMA ? 3 : 1)) void k_chunk_out(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ lcs, const float *__restrict__ dtp,
     const float *__restrict__ wgt, const typename Op<IO>::type *__restrict__ Hb,
     IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp,
     const f16 *__restrict__ img, int64_t nsb, int has_init) {
-    typedef Co<IO, P, N, HPW> K;
+    typedef Co<IO, P, N, HPW, COPY> K;
     typedef typename K::OP OP;
     constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
     // two block buffers as separate objects, so that the compiler can tell
@@ -1141,7 +1154,7 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
             accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
         for (int s = 0; s < nblk; s += 2) {
             wave_priority(progress_priority(s, nblk));
-            co_compute<IO, P, N, HPW>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
+            co_compute<IO, P, N, HPW, COPY>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
                                       c0, lane);
             vm_wait<K::NS>();  // block s + 1
             co_rows_stage<HPW>(rb, rows1, tid);
@@ -1149,7 +1162,7 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
             co_dma<IO, P, N, HPW>(buf0, s + 2, cp, wave, lane);
             co_rows_prefetch<HPW>(ra, s + 2, cp, tid);
             issue_fence();
-            co_compute<IO, P, N, HPW>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+            co_compute<IO, P, N, HPW, COPY>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
                                       hs, c0, lane);
             vm_wait<K::NS>();  // block s + 2
             co_rows_stage<HPW>(ra, rows0, tid);
@@ -1180,12 +1193,12 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
         for (int s = 0; s < nblk; s += 2) {
             co_stage(pb, buf1, rows1, tid);  // block s + 1
             co_prefetch(pb, s + 3, cp, tid);
-            co_compute<IO, P, N, HPW>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
+            co_compute<IO, P, N, HPW, COPY>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
                                       c0, lane);
             lds_barrier();
             co_stage(pa, buf0, rows0, tid);  // block s + 2
             co_prefetch(pa, s + 4, cp, tid);
-            co_compute<IO, P, N, HPW>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+            co_compute<IO, P, N, HPW, COPY>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
                                       hs, c0, lane);
             lds_barrier();
         }
@@ -1238,7 +1251,11 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     ia.nc = pl.nc;
     ia.nsb = pl.nsb;
     ia.g = g;
-    ia.pieces = sizeof(IO) == 2 ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
+    // bf16: one-head workgroups always copy (staging a whole block through
+    // one or two waves' registers costs more registers than the output's
+    // accumulators); head-sharing workgroups by the size rule
+    const bool copy = sizeof(IO) == 2 && (!grouped || chunk_out_copy(h, g, P, N));
+    ia.pieces = copy ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
     trace_begin(2, s);
     hipLaunchKernelGGL((k_state_scan<OP, IO, N>), dim3((unsigned)scan_blocks), dim3(kThreads), 0, s,
                        St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h, pl.nc, N, P, ia);
@@ -1247,14 +1264,28 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
 
     trace_begin(3, s);
-    if (grouped)
-        hipLaunchKernelGGL((k_chunk_out<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
-                           dim3(Co<IO, P, N, HP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb,
-                           y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb, a.init != nullptr);
-    else
-        hipLaunchKernelGGL((k_chunk_out<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
-                           dim3(Co<IO, P, N, 1>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt, Hb, y,
-                           pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb, a.init != nullptr);
+    auto launch_out = [&](auto hp_c, auto copy_c) {
+        constexpr int HPn = decltype(hp_c)::value;
+        constexpr bool CP = decltype(copy_c)::value;
+        hipLaunchKernelGGL((k_chunk_out<IO, P, N, HPn, CP>),
+                           dim3((unsigned)(pl.b * pl.nc * (h / HPn))),
+                           dim3(Co<IO, P, N, HPn, CP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt,
+                           Hb, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb,
+                           a.init != nullptr);
+    };
+    if constexpr (sizeof(IO) == 2) {
+        if (!grouped)
+            launch_out(std::integral_constant<int, 1>{}, std::true_type{});
+        else if (copy)
+            launch_out(std::integral_constant<int, HP>{}, std::true_type{});
+        else
+            launch_out(std::integral_constant<int, HP>{}, std::false_type{});
+    } else {
+        if (grouped)
+            launch_out(std::integral_constant<int, HP>{}, std::false_type{});
+        else
+            launch_out(std::integral_constant<int, 1>{}, std::false_type{});
+    }
     trace_end(3, s);
     return hipGetLastError();
 }

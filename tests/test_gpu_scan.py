@@ -63,6 +63,36 @@ def test_small_parity(orc, case, io):
     log("y max_abs %.3g max_rel %.3g | final max_abs %.3g" % (s1[0], s1[1], s2[0]))
 
 
+# workgroups sharing B and C over heads, on both sides of the rule that picks
+# the bf16 chunk output's staging (copied fp16 block images, or registers)
+PATHS = [
+    (2, 300, 4, 64, 128, 1, 256, 0.1),    # rule: registers
+    (1, 700, 8, 32, 64, 2, 100, 0.2),     # rule: registers; ragged 100-row chunks
+    (2, 200, 16, 16, 128, 4, 64, 0.0),    # rule: registers; four heads per workgroup
+    (1, 520, 24, 64, 128, 1, 256, 0.0),   # rule: copies (the bench workload's shape)
+]
+
+
+@pytest.mark.parametrize("case", PATHS, ids=_id)
+def test_chunk_output_staging_paths_agree(orc, case, monkeypatch):
+    """The bf16 chunk output staged through registers and copied into LDS
+    from the fp16 block images (SSD_CHUNK_OUT_COPY=0 / 1 forces either) does
+    the same conversions and the same arithmetic: the outputs agree bit for
+    bit, and both meet the bar against the oracle."""
+    b, l, h, p, n, g, Q, init = case
+    inp = syn.random_case(2000 + sum(case[:7]), b, l, h, p, n, g, io="bf16", init_std=init)
+    out = {}
+    for v in ("0", "1"):
+        monkeypatch.setenv("SSD_CHUNK_OUT_COPY", v)
+        out[v] = run_scan(inp, Q)
+    torch = torch_mod()
+    assert torch.equal(out["0"][0], out["1"][0])
+    assert torch.equal(out["0"][1], out["1"][1])
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(to_f64(out["1"][0]), yo, "bf16", "y", Y_AXES)
+    check_close(to_f64(out["1"][1]), fo, "bf16", "final_state", STATE_AXES)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_no_skip_no_bias_clamped(orc, io):
     inp = syn.random_case(7, 2, 150, 4, 64, 64, 2, io=io, init_std=0.2)
