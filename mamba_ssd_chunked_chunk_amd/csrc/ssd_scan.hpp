@@ -321,7 +321,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, SPAN = K::SPAN, TPW = K::TPW;
-    __shared__ __attribute__((aligned(16))) OP lds[K::BUF];
+    __shared__ __attribute__((aligned(16))) OP lds0[K::BUF];
+    __shared__ __attribute__((aligned(16))) OP lds1[K::BUF];
     __shared__ __attribute__((aligned(16))) SpSpan<HPW> span;
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -371,33 +372,51 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     SpBuf<IO, P, N, HPW> pa, pb;
     sp_prefetch(pa, c, 0, true, sp, tid);
     sp_prefetch(pb, c, 1, nsb > 1, sp, tid);
+
+    // Two LDS buffers: block k + 1 is staged (buffer (k + 1) & 1, register
+    // set pa / pb by parity) while block k is applied, one barrier per
+    // block.  A span's weights are computed before its first block is
+    // staged; the state decays by the new span's total after the previous
+    // span's last block has been applied.
+    {
+        sp_span<IO, P, N, HPW>(span, dtv, c, 0, sp, tid);
+        float L = 0.f;
+#pragma unroll
+        for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
+        logdec = __builtin_bit_cast(float,
+                                    __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L)));
+    }
+    sp_stage(pa, lds0, span, 0, tid);
+    sp_prefetch(pa, c, 2, 2 < nsb, sp, tid);
+    lds_barrier();
     for (int k0 = 0; k0 < nsb; k0 += 2) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            SpBuf<IO, P, N, HPW> &pf = half == 0 ? pa : pb;
-            const int k = k0 + half;
-            const bool live = k < nsb;
+            const int k = k0 + half, nxt = k + 1;
+            SpBuf<IO, P, N, HPW> &pn = half == 0 ? pb : pa;  // holds block nxt
+            typename K::OP *const bk = half == 0 ? lds0 : lds1;
+            typename K::OP *const bn = half == 0 ? lds1 : lds0;
             if (half == 0) wave_priority(progress_priority(k, nsb));
-            if (live && k % SPAN == 0) {  // a new span: its weights, then the decay
-                if (k > 0) sp_dt_load<IO, P, N, HPW>(dtv, c, k, sp, tid);
-                sp_span<IO, P, N, HPW>(span, dtv, c, k, sp, tid);
-                float L = 0.f;
+            const bool new_span = nxt < nsb && nxt % SPAN == 0;
+            float L = 0.f;
+            if (new_span) {
+                sp_dt_load<IO, P, N, HPW>(dtv, c, nxt, sp, tid);
+                sp_span<IO, P, N, HPW>(span, dtv, c, nxt, sp, tid);
 #pragma unroll
                 for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
                 L = __builtin_bit_cast(float,
                                        __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, L)));
-                if (k > 0) {
-                    const float decay = exp2_fast(L);
+            }
+            if (nxt < nsb) sp_stage(pn, bn, span, nxt % SPAN, tid);
+            sp_prefetch(pn, c, nxt + 2, nxt + 2 < nsb, sp, tid);
+            if (k < nsb) sp_apply<IO, P, N, HPW>(acc, bk, hs, c0, lane);
+            if (new_span) {
+                const float decay = exp2_fast(L);
 #pragma unroll
-                    for (int t = 0; t < TPW; ++t) acc[t] *= decay;
-                }
+                for (int t = 0; t < TPW; ++t) acc[t] *= decay;
                 logdec += L;
             }
-            lds_barrier();  // the previous block's reads are done
-            if (live) sp_stage(pf, lds, span, k % SPAN, tid);
-            sp_prefetch(pf, c, k + 2, k + 2 < nsb, sp, tid);
             lds_barrier();
-            if (live) sp_apply<IO, P, N, HPW>(acc, lds, hs, c0, lane);
         }
     }
     // the last chunk's own state only feeds the final state
