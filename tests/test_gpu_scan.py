@@ -94,6 +94,24 @@ def test_chunk_output_staging_paths_agree(orc, case, monkeypatch):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("init", [0.0, 0.3])
+def test_outputs_independent_of_final_state_request(orc, io, init):
+    """Without a requested final state the last chunk's own state is neither
+    stored nor read, and without an initial state chunk 0's boundary state
+    is neither stored nor read; y must not change with either choice."""
+    inp = syn.random_case(31, 2, 700, 4, 64, 128, 2, io=io, init_std=init)
+    g = gpu_inputs(inp)
+    y_f, fin = run_scan(inp, 128, final=True, g=g)
+    y_n = run_scan(inp, 128, final=False, g=g)
+    if isinstance(y_n, tuple):
+        y_n = y_n[0]
+    assert torch_mod().equal(y_f, y_n)
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(to_f64(y_n), yo, io, "y", Y_AXES)
+    check_close(to_f64(fin), fo, io, "final_state", STATE_AXES)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_no_skip_no_bias_clamped(orc, io):
     inp = syn.random_case(7, 2, 150, 4, 64, 64, 2, io=io, init_std=0.2)
     inp["D"] = None
