@@ -9,7 +9,10 @@ Three independent fp64 formulations live here:
 
 * `scan` / `step` -- the sequential recurrence, token by token, in plain C
   (ssd_oracle.c).  This is the oracle proper (nnterp guide, "Mamba-2" page,
-  opening section: h = exp(dt A) h + dt B x^T, y = C^T h + D x).
+  opening section: h = exp(dt A) h + dt B x^T, y = C^T h + D x).  Options:
+  packed sequences (a per-token document index; a zero state wherever it
+  changes -- the sample-packing reset of the Mamba2 news page) and the state
+  after every chunk boundary (nnterp, "The state after every token").
 * `oracle.quadratic.dual_form` -- the same result written as one masked
   matrix product per head (the "matrix multiplication form" of the kongchang
   "Mamba2" page), derived by unrolling the recurrence.  Used only to pin the
@@ -58,7 +61,7 @@ def _bind(lib):
     lib.ssd_oracle_scan.argtypes = [P, P, P, P, P, P, P, ctypes.c_int,
                                     ctypes.c_double, ctypes.c_double, P,
                                     I64, I64, I64, I64, I64, I64, ctypes.c_int,
-                                    P, I64, P, P, ctypes.c_int]
+                                    P, I64, P, P, P, I64, P, ctypes.c_int]
     lib.ssd_oracle_dt.restype = ctypes.c_int
     lib.ssd_oracle_dt.argtypes = [P, P, P, ctypes.c_int, ctypes.c_double,
                                   ctypes.c_double, I64, I64, I64, ctypes.c_int, P, P]
@@ -99,15 +102,20 @@ def _io_arr(a, io):
 
 def scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,
          dt_limit=(0.0, math.inf), init_state=None, io="f32",
-         pairs: Optional[Sequence] = None, nthreads: Optional[int] = None):
+         pairs: Optional[Sequence] = None, nthreads: Optional[int] = None,
+         seq_idx=None, states_chunk: Optional[int] = None):
     """Sequential fp64 recurrence.
 
     x [b,l,h,p], dt [b,l,h], B, C [b,l,g,n] as stored (float32, or uint16
     bf16 bits when io == "bf16"); A, D, dt_bias [h]; init_state [b,h,n,p]
-    (any float dtype; None -> zeros).
+    (any float dtype; None -> zeros).  seq_idx [b,l] integers or None:
+    packed sequences, a zero state wherever the index changes from one token
+    to the next.
 
     pairs None: returns y [b,l,h,p] fp64 and final [b,h,n,p] fp64.
     pairs [(b, h), ...]: returns y [k,l,p] and final [k,n,p] for those pairs.
+    states_chunk c: also returns the state after the last token of every
+    chunk of c tokens, [b, ceil(l/c), h, n, p] (pairs: [k, ceil(l/c), n, p]).
     """
     x, dt, B, C = (_io_arr(a, io) for a in (x, dt, B, C))
     b, l, h, p = x.shape
@@ -127,16 +135,27 @@ def scan(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,
     A = _c(A, np.float32)
     D = _c(D, np.float32)
     dt_bias = _c(dt_bias, np.float32)
+    seq = None if seq_idx is None else np.ascontiguousarray(np.asarray(seq_idx).reshape(b, l),
+                                                            dtype=np.int32)
+    nc = 0
+    states = None
+    if states_chunk is not None:
+        nc = -(-l // int(states_chunk))
+        states = np.empty((k, nc, n, p), np.float64)
     rc = _load().ssd_oracle_scan(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
         int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]), _ptr(init),
-        b, l, h, p, n, g, IO_CODES[io], _ptr(pr), k, _ptr(y), _ptr(st),
-        int(nthreads or default_threads()))
+        b, l, h, p, n, g, IO_CODES[io], _ptr(pr), k, _ptr(y), _ptr(st), _ptr(seq),
+        int(states_chunk or 0), _ptr(states), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("ssd_oracle_scan rejected its arguments")
     if full:
         y = y.reshape(b, h, l, p).transpose(0, 2, 1, 3).copy()
         st = st.reshape(b, h, n, p)
+        if states is not None:
+            states = states.reshape(b, h, nc, n, p).transpose(0, 2, 1, 3, 4).copy()
+    if states is not None:
+        return y, st, states
     return y, st
 
 

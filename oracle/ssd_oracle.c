@@ -72,6 +72,9 @@ typedef struct {
     int64_t npairs;
     double *y;     /* [npairs, l, p] */
     double *state; /* [npairs, n, p] */
+    const int32_t *seq_idx; /* [b, l] or NULL */
+    int64_t chunk;          /* states output: one state per chunk of this many tokens */
+    double *states;         /* [npairs, ceil(l / chunk), n, p] or NULL */
     int64_t next;  /* work counter */
 } job_t;
 
@@ -94,6 +97,10 @@ static void run_pair(const job_t *J, int64_t k)
 
     for (int64_t t = 0; t < l; ++t) {
         const int64_t row = bb * l + t;
+        /* packed sequences: a token whose document index differs from the
+           previous token's starts from a zero state */
+        if (J->seq_idx && t > 0 && J->seq_idx[row] != J->seq_idx[row - 1])
+            memset(H, 0, sizeof(double) * (size_t)(n * p));
         const double d = proc_dt(ld(J->dt, row * h + hh, J->io), bias, J->softplus,
                                  J->dt_min, J->dt_max);
         const double decay = exp(Ah * d);
@@ -115,6 +122,12 @@ static void run_pair(const job_t *J, int64_t k)
             const double *Hi = H + i * p;
             for (int64_t j = 0; j < p; ++j)
                 yt[j] += ci * Hi[j];
+        }
+        /* the state after the last token of each chunk */
+        if (J->states && ((t + 1) % J->chunk == 0 || t == l - 1)) {
+            const int64_t nc = (l + J->chunk - 1) / J->chunk;
+            memcpy(J->states + (k * nc + t / J->chunk) * n * p, H,
+                   sizeof(double) * (size_t)(n * p));
         }
     }
     free(xv);
@@ -139,6 +152,13 @@ static void *worker(void *arg)
  *   dt_bias may be NULL: no skip, zero bias); init [npairs,n,p] fp64 or NULL.
  *   pairs: npairs (b, h) index pairs.
  *   y out [npairs,l,p] fp64; state out [npairs,n,p] fp64.
+ *   seq_idx [b,l] int32 or NULL: packed sequences; wherever the index
+ *   changes from one token to the next, the later token starts from a zero
+ *   state (the initial state belongs to the first sequence of each row).
+ *   states out [npairs, ceil(l/chunk), n, p] fp64 or NULL: the state after
+ *   the last token of every chunk of `chunk` tokens (nnterp guide, "The
+ *   state after every token": one state per chunk boundary; chunk 1 gives
+ *   the state after every token, and the last one is the final state).
  * Returns 0, or -1 on a bad argument.
  */
 int ssd_oracle_scan(const void *x, const void *dt, const float *A, const void *B,
@@ -146,9 +166,12 @@ int ssd_oracle_scan(const void *x, const void *dt, const float *A, const void *B
                     int dt_softplus, double dt_min, double dt_max, const double *init,
                     int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
                     int64_t state_dim, int64_t groups, int io, const int64_t *pairs,
-                    int64_t npairs, double *y, double *state, int nthreads)
+                    int64_t npairs, double *y, double *state, const int32_t *seq_idx,
+                    int64_t chunk, double *states, int nthreads)
 {
     if (!A || !pairs || !state || (seqlen > 0 && (!x || !dt || !B || !C || !y)))
+        return -1;
+    if (states && chunk < 1)
         return -1;
     if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
         groups <= 0 || heads % groups != 0 || (io != IO_F32 && io != IO_BF16))
@@ -159,7 +182,7 @@ int ssd_oracle_scan(const void *x, const void *dt, const float *A, const void *B
             return -1;
     job_t J = {x, dt, B, C, A, D, dt_bias, dt_softplus, io, dt_min, dt_max, init,
                batch, seqlen, heads, head_dim, state_dim, groups, pairs, npairs,
-               y, state, 0};
+               y, state, seq_idx, chunk, states, 0};
     if (nthreads < 1)
         nthreads = 1;
     if (nthreads > npairs)

@@ -285,3 +285,87 @@ def test_synth_deterministic_and_distributions():
     assert a["dt_bias"].min() >= lo - 1e-5 and a["dt_bias"].max() <= hi + 1e-5
     s = syn.make_step_inputs(syn.WORKLOADS["decode_2p7b"], 3, batch=2)
     assert s["x"].shape == (2, 80, 64) and s["x"].dtype == np.uint16
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences and the chunk-boundary states output.
+
+def _slice(inp, t0, t1):
+    return dict(x=inp["x"][:, t0:t1], dt=inp["dt"][:, t0:t1], B=inp["B"][:, t0:t1],
+                C=inp["C"][:, t0:t1])
+
+
+@pytest.mark.parametrize("cuts", [(11,), (5, 6, 30), (1, 36)])
+def test_packed_sequences_equal_separate_runs(oracle_mod, cuts):
+    """Documents packed into one row with a per-token document index behave
+    as if run one by one: the first from the initial state, every later one
+    from a zero state; the final state is the last document's.  (Sample
+    packing with a reset at document boundaries, the packing fix on the
+    Mamba2 news page.)  Includes a one-token document."""
+    inp = _small(81, l=37)
+    b, l = inp["x"].shape[:2]
+    edges = (0,) + tuple(cuts) + (l,)
+    seq = np.zeros((b, l), np.int32)
+    for k in range(len(edges) - 1):
+        seq[:, edges[k]:edges[k + 1]] = 3 * k + 1
+    y, fin = oracle_mod.scan(**_kw(inp), seq_idx=seq)
+    init = inp["init_state"]
+    for k in range(len(edges) - 1):
+        t0, t1 = edges[k], edges[k + 1]
+        yk, fk = oracle_mod.scan(**_kw(inp, **_slice(inp, t0, t1),
+                                       init_state=init if k == 0 else None))
+        np.testing.assert_array_equal(y[:, t0:t1], yk)
+    np.testing.assert_array_equal(fin, fk)
+
+
+def test_constant_document_index_changes_nothing(oracle_mod):
+    inp = _small(82)
+    y, fin = oracle_mod.scan(**_kw(inp))
+    seq = np.full(inp["x"].shape[:2], 7, np.int32)
+    ys, fs = oracle_mod.scan(**_kw(inp), seq_idx=seq)
+    np.testing.assert_array_equal(ys, y)
+    np.testing.assert_array_equal(fs, fin)
+
+
+@pytest.mark.parametrize("chunk", [1, 5, 37, 64])
+def test_chunk_states_are_prefix_final_states(oracle_mod, chunk):
+    """The state after every chunk boundary is the final state of the prompt
+    cut at that boundary, and the last one is the final state (nnterp, "The
+    state after every token": states[:, -1] equals the final state)."""
+    inp = _small(83, l=37)
+    l = inp["x"].shape[1]
+    y, fin, states = oracle_mod.scan(**_kw(inp), states_chunk=chunk)
+    assert states.shape[1] == -(-l // chunk)
+    np.testing.assert_array_equal(states[:, -1], fin)
+    for c in range(states.shape[1]):
+        t1 = min((c + 1) * chunk, l)
+        _, fc = oracle_mod.scan(**_kw(inp, **_slice(inp, 0, t1)))
+        np.testing.assert_array_equal(states[:, c], fc)
+
+
+def test_per_token_states_hold_at_a_zero_time_step(oracle_mod):
+    """With one state per token, a zero time step at token 3 leaves the state
+    after token 3 equal to the state after token 2 (nnterp, "The state after
+    every token": held[:, 3] equals held[:, 2] with betas[:, 3] = 0)."""
+    inp = _small(84, l=10)
+    dt = np.abs(inp["dt"]).astype(np.float32)
+    dt[:, 3, :] = 0.0
+    _, _, states = oracle_mod.scan(**_kw(inp, dt=dt, dt_softplus=False, dt_bias=None),
+                                   states_chunk=1)
+    np.testing.assert_array_equal(states[:, 3], states[:, 2])
+    assert not np.array_equal(states[:, 4], states[:, 3])
+
+
+def test_chunk_states_with_packed_sequences(oracle_mod):
+    """Chunk states of a packed row are the prefix states of the same packed
+    row, and a boundary state right after a document ends is that
+    document's final state."""
+    inp = _small(85, l=30)
+    seq = np.zeros(inp["x"].shape[:2], np.int32)
+    seq[:, 10:] = 1
+    _, fin, states = oracle_mod.scan(**_kw(inp), seq_idx=seq, states_chunk=10)
+    _, f_doc0 = oracle_mod.scan(**_kw(inp, **_slice(inp, 0, 10)))
+    np.testing.assert_array_equal(states[:, 0], f_doc0)
+    np.testing.assert_array_equal(states[:, -1], fin)
+    _, f20 = oracle_mod.scan(**_kw(inp, **_slice(inp, 0, 20)), seq_idx=seq[:, :20])
+    np.testing.assert_array_equal(states[:, 1], f20)
