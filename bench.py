@@ -81,7 +81,6 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False):
     BC = b * l * g * n * s             # B or C, once per group
     rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
     so = 2 if s == 2 else 4            # boundary-state element
-    st = b * nc * h * n * p            # elements of all chunk (or boundary) states
     # chunk states needed: the last chunk's only feeds the final state
     ns = nc if final else nc - 1
     sn = b * ns * h * n * p

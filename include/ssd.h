@@ -112,6 +112,36 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
                        void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * ssd_chunk_scan_ex -- ssd_chunk_scan with packed sequences and the state
+ * after every chunk.  ssd_chunk_scan is this call with both new pointers
+ * NULL; every other argument, the workspace and the error behaviour are
+ * the same.
+ *
+ *   seq_idx       [batch, seqlen] int32 document index of every token, or
+ *                 NULL; 4-byte aligned.  Wherever it changes from one token
+ *                 to the next, the later token starts from a zero state
+ *                 (documents packed into one row; the sample-packing reset
+ *                 of the Mamba2 news page).  The initial state, if given,
+ *                 belongs to the row's first document; the final state is
+ *                 the last document's.  Only whether neighbouring values are
+ *                 equal matters.
+ *   chunk_states  output [batch, chunks, heads, state_dim, head_dim] fp32, or
+ *                 NULL; 16-byte aligned; chunks = ceil(seqlen / chunk).
+ *                 Entry c is the state after the last token of chunk c
+ *                 (nnterp guide, "The state after every token": one state
+ *                 per chunk boundary; chunk = 1 gives the state after every
+ *                 token, and the last entry equals the final state).
+ */
+int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const void *B,
+                          const void *C, const float *D, const float *dt_bias,
+                          int32_t dt_softplus, float dt_min, float dt_max,
+                          const float *init_state, const int32_t *seq_idx, void *y,
+                          float *final_state, float *chunk_states, int64_t batch,
+                          int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
+                          int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
+                          size_t workspace_bytes, void *hip_stream);
+
+/*
  * Bytes of workspace ssd_chunk_scan needs for these sizes (a pure function
  * of its arguments; 0 for invalid sizes).  Layout, in order, each part
  * 256-byte aligned: per-row cumulative log2 decay and processed time step

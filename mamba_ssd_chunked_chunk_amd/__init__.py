@@ -75,12 +75,17 @@ def workspace_bytes(batch, seqlen, heads, head_dim, state_dim, groups, chunk) ->
 def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
                dt_softplus: bool = True, dt_limit: Tuple[float, float] = (0.0, math.inf),
                initial_state=None, return_final_state: bool = False, out=None,
-               final_out=None, workspace=None):
-    """The chunked SSD scan of a whole sequence (ssd_chunk_scan).
+               final_out=None, workspace=None, seq_idx=None,
+               return_chunk_states: bool = False, chunk_states_out=None):
+    """The chunked SSD scan of a whole sequence (ssd_chunk_scan_ex).
 
-    Returns y, or (y, final_state) when return_final_state.  `out`,
-    `final_out` and `workspace` (uint8, at least workspace_bytes(...)) may be
-    given to avoid allocations; final_out may alias initial_state.
+    Returns y, followed by final_state when return_final_state and by the
+    state after every chunk [b, ceil(l / chunk_size), h, n, p] when
+    return_chunk_states (a tuple when either is asked for).  seq_idx
+    [b, l] int32: packed documents, a zero state wherever the index changes
+    from one token to the next.  `out`, `final_out`, `chunk_states_out` and
+    `workspace` (uint8, at least workspace_bytes(...)) may be given to avoid
+    allocations; final_out may alias initial_state.
     """
     torch = _torch()
     lib = load()
@@ -103,6 +108,7 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
     _check("D", D, torch.float32, (h,), dev)
     _check("dt_bias", dt_bias, torch.float32, (h,), dev)
     _check("initial_state", initial_state, torch.float32, (b, h, n, p), dev)
+    _check("seq_idx", seq_idx, torch.int32, (b, l), dev)
     y = torch.empty_like(x) if out is None else out
     _check("out", y, io, (b, l, h, p), dev)
     fin = None
@@ -110,19 +116,28 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
         fin = torch.empty((b, h, n, p), dtype=torch.float32, device=dev) \
             if final_out is None else final_out
         _check("final_out", fin, torch.float32, (b, h, n, p), dev)
+    states = None
+    if return_chunk_states:
+        nck = -(-l // int(chunk_size)) if chunk_size > 0 else 0
+        states = torch.empty((b, nck, h, n, p), dtype=torch.float32, device=dev) \
+            if chunk_states_out is None else chunk_states_out
+        _check("chunk_states_out", states, torch.float32, (b, nck, h, n, p), dev)
     wsb = int(lib.ssd_chunk_scan_workspace_bytes(b, l, h, p, n, g, int(chunk_size)))
     ws = workspace
     if ws is None:
         ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.ssd_chunk_scan(
+    rc = lib.ssd_chunk_scan_ex(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
         int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
-        _ptr(initial_state), _ptr(y), _ptr(fin), b, l, h, p, n, g, int(chunk_size),
-        _io_code(io), _ptr(ws), ws.numel() * ws.element_size(), stream)
+        _ptr(initial_state), _ptr(seq_idx), _ptr(y), _ptr(fin), _ptr(states), b, l, h, p, n,
+        g, int(chunk_size), _io_code(io), _ptr(ws), ws.numel() * ws.element_size(), stream)
     if rc != 0:
-        raise SsdError("ssd_chunk_scan", rc)
-    return (y, fin) if return_final_state else y
+        raise SsdError("ssd_chunk_scan_ex", rc)
+    if not return_final_state and not return_chunk_states:
+        return y
+    return (y,) + ((fin,) if return_final_state else ()) + \
+        ((states,) if return_chunk_states else ())
 
 
 def step(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softplus: bool = True,

@@ -20,7 +20,7 @@ SSD_ERR_HIP = -6
 KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step": 4}
 
 # every symbol include/ssd.h declares
-EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_workspace_bytes", "ssd_step",
+EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",
            "ssd_status_string", "ssd_abi_version", "ssd_trace_enable", "ssd_trace_read")
 
 _lib = None
@@ -45,6 +45,10 @@ def load() -> ctypes.CDLL:
     lib.ssd_chunk_scan.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P,
                                    I64, I64, I64, I64, I64, I64, I64, I32,
                                    P, ctypes.c_size_t, P]
+    lib.ssd_chunk_scan_ex.restype = I32
+    lib.ssd_chunk_scan_ex.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P, P, P,
+                                      I64, I64, I64, I64, I64, I64, I64, I32,
+                                      P, ctypes.c_size_t, P]
     lib.ssd_chunk_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_workspace_bytes.argtypes = [I64] * 7
     lib.ssd_step.restype = I32

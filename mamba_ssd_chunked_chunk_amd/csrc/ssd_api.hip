@@ -139,6 +139,20 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
                        int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
                        int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
                        size_t workspace_bytes, void *hip_stream) {
+    return ssd_chunk_scan_ex(x, dt, A, B, C, D, dt_bias, dt_softplus, dt_min, dt_max,
+                             init_state, nullptr, y, final_state, nullptr, batch, seqlen,
+                             heads, head_dim, state_dim, groups, chunk, io_dtype, workspace,
+                             workspace_bytes, hip_stream);
+}
+
+int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const void *B,
+                          const void *C, const float *D, const float *dt_bias,
+                          int32_t dt_softplus, float dt_min, float dt_max,
+                          const float *init_state, const int32_t *seq_idx, void *y,
+                          float *final_state, float *chunk_states, int64_t batch,
+                          int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
+                          int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
+                          size_t workspace_bytes, void *hip_stream) {
     if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
         groups <= 0 || chunk <= 0 || heads % groups != 0)
@@ -154,7 +168,8 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
     const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
         !aligned(dt, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) ||
-        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256))
+        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256) ||
+        !aligned(seq_idx, 4) || !aligned(chunk_states, 16))
         return SSD_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
@@ -187,7 +202,8 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
         return SSD_ERR_WORKSPACE;
 
     ScanArgs a{x, dt, B, C, A, D, dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max,
-               init_state, y, final_state, static_cast<char *>(workspace)};
+               init_state, y, final_state, static_cast<char *>(workspace), seq_idx,
+               chunk_states};
     hipError_t e = io_dtype == SSD_BF16 ? dispatch_scan<bf16>(pl, a, s)
                                         : dispatch_scan<float>(pl, a, s);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;

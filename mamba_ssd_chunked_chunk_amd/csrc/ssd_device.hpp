@@ -297,6 +297,20 @@ __device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
     void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, n, kRsrcWord3);
 }
+// One 16-byte copy per lane from a buffer resource straight into LDS: the
+// wave writes 64 consecutive 16-byte slots starting at dst (lane i at
+// dst + 16 i), whatever offset each lane reads; offsets past the resource
+// write zeros.  The builtin exists only for the device: in the host pass
+// of the compiler it would mark every template that calls it as invalid
+// (the host never runs this code), so the body is compiled there as empty.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void lds_copy16(Rsrc r, lds_void *dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+#else
+    (void)r, (void)dst, (void)voff;
+#endif
+}
 template <typename T> __device__ __forceinline__ Row8v<T> buf_row8(Rsrc r, uint32_t off) {
     constexpr int NV = sizeof(Row8v<T>) / 16;
     u32x4 v[NV];

@@ -87,6 +87,8 @@ struct ScanArgs {
     void *y;
     float *final_state;
     char *ws;
+    const int32_t *seq;  // [b, l] document index of every token, or NULL
+    float *states;       // [b, nc, h, n, p] state after every chunk, or NULL
 };
 
 struct StepArgs {

@@ -128,6 +128,7 @@ template <typename IO, int HPW> struct SpPtrs {
     int64_t l, Q, hrow;      // sequence length, chunk, elements from one head's row arrays to the next
     int h;                   // heads (row stride of dt)
     int64_t Qp;              // padded rows per chunk
+    const int32_t *seq;      // row 0 of the sequence's document indices (packed sequences)
 };
 
 template <typename IO, int P, int N, int HPW>
@@ -164,8 +165,8 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
 
 // The raw time steps of the span starting at block blk0, one row of one head
 // per thread and pass.
-template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ void sp_dt_load(float *dtv, int64_t c, int blk0,
+template <typename IO, int P, int N, int HPW, bool SEQ>
+__device__ __forceinline__ void sp_dt_load(float *dtv, int *rst, int64_t c, int blk0,
                                            const SpPtrs<IO, HPW> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     constexpr int T = kT;
@@ -176,15 +177,20 @@ __device__ __forceinline__ void sp_dt_load(float *dtv, int64_t c, int blk0,
         const int hs = idx / K::SPR, r = idx % K::SPR;
         const int64_t row = c * sp.Q + (int64_t)blk0 * T + r;
         dtv[ps] = row < cend ? to_f32(sp.dt[row * sp.h + hs]) : 0.f;
+        // packed sequences: a row whose document index differs from the
+        // previous row's starts from a zero state
+        if constexpr (SEQ)
+            rst[ps] = (row < cend && row > 0) ? (sp.seq[row] != sp.seq[row - 1]) : 0;
     }
 }
 
 // The per-row values of the span starting at block blk0 (see above) from
 // its raw time steps; ends with the span's weights visible to the whole
 // workgroup.
-template <typename IO, int P, int N, int HPW>
-__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, int64_t c, int blk0,
-                                        const SpPtrs<IO, HPW> &sp, int tid) {
+template <typename IO, int P, int N, int HPW, bool SEQ>
+__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const int *rst,
+                                        int64_t c, int blk0, const SpPtrs<IO, HPW> &sp,
+                                        int tid) {
     typedef Sp<IO, P, N, HPW> K;
     constexpr int T = kT;
     const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;
@@ -210,7 +216,17 @@ __device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, int64
             if ((r & (T - 1)) >= off) a += v;
         }
         const float last = __shfl(a, T - 1, T);
-        const float w = exp2_fast(last - a) * d;
+        float w = exp2_fast(last - a) * d;
+        float lam = last;  // the block's log2 decay
+        if constexpr (SEQ) {
+            // resets in this block (its 32 lanes): rows before the last one
+            // do not reach the block's end, and nothing crosses the block
+            const uint32_t m = (uint32_t)(__ballot(rst[ps] != 0) >> (tid & 32));
+            if (m) {
+                if ((r & (T - 1)) < 31 - __builtin_clz(m)) w = 0.f;
+                lam = -INFINITY;
+            }
+        }
         const int64_t R = (int64_t)blk0 * T + r;  // padded row inside the chunk
         if (R < sp.Qp) {
             const int64_t idx2 = hs * sp.hrow + c * sp.Qp + R;
@@ -219,7 +235,7 @@ __device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, int64
             sp.wgt[idx2] = w;
         }
         sv.v[hs][r] = w;
-        if ((r & (T - 1)) == T - 1) sv.lam[hs][r / T] = last;
+        if ((r & (T - 1)) == T - 1) sv.lam[hs][r / T] = lam;
     }
     lds_barrier();
 #pragma unroll
@@ -310,14 +326,16 @@ __device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type
     }
 }
 
-template <typename IO, int P, int N, int HPW>
-// bf16 io: three workgroups per compute unit (at most 168 VGPRs)
-__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1)) void k_chunk_state(
+// bf16 io: three workgroups per compute unit (at most 168 VGPRs; two with
+// packed sequences, whose reset flags need more)
+template <typename IO, int P, int N, int HPW, bool SEQ>
+__global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
+                             (sizeof(IO) == 2 ? (SEQ ? 2 : 3) : 1)) void k_chunk_state(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
     float *__restrict__ St, float *__restrict__ Lam, int64_t l, int h, int g, int64_t Q,
-    int64_t nc, int64_t Qp, int keep_last) {
+    int64_t nc, int64_t Qp, int keep_last, const int32_t *__restrict__ seq) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, SPAN = K::SPAN, TPW = K::TPW;
@@ -343,6 +361,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     sp.x = x + (b * l * h + hh0) * P;
     sp.B = Bm + (b * l * g + gi) * N;
     sp.dt = dt + b * l * h + hh0;
+    sp.seq = SEQ ? seq + b * l : nullptr;
     sp.lcs = lcs + (b * h + hh0) * nc * Qp;
     sp.dtp = dtp + (b * h + hh0) * nc * Qp;
     sp.wgt = wgt + (b * h + hh0) * nc * Qp;
@@ -368,7 +387,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     // the first span's raw time steps are requested before the first blocks,
     // so that its per-row values are ready as soon as possible
     float dtv[K::NPASS];
-    sp_dt_load<IO, P, N, HPW>(dtv, c, 0, sp, tid);
+    int rst[K::NPASS];
+    sp_dt_load<IO, P, N, HPW, SEQ>(dtv, rst, c, 0, sp, tid);
     SpBuf<IO, P, N, HPW> pa, pb;
     sp_prefetch(pa, c, 0, true, sp, tid);
     sp_prefetch(pb, c, 1, nsb > 1, sp, tid);
@@ -379,7 +399,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
     // staged; the state decays by the new span's total after the previous
     // span's last block has been applied.
     {
-        sp_span<IO, P, N, HPW>(span, dtv, c, 0, sp, tid);
+        sp_span<IO, P, N, HPW, SEQ>(span, dtv, rst, c, 0, sp, tid);
         float L = 0.f;
 #pragma unroll
         for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
@@ -400,8 +420,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT), (sizeof(IO) == 2 ? 3 : 1))
             const bool new_span = nxt < nsb && nxt % SPAN == 0;
             float L = 0.f;
             if (new_span) {
-                sp_dt_load<IO, P, N, HPW>(dtv, c, nxt, sp, tid);
-                sp_span<IO, P, N, HPW>(span, dtv, c, nxt, sp, tid);
+                sp_dt_load<IO, P, N, HPW, SEQ>(dtv, rst, c, nxt, sp, tid);
+                sp_span<IO, P, N, HPW, SEQ>(span, dtv, rst, c, nxt, sp, tid);
 #pragma unroll
                 for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
                 L = __builtin_bit_cast(float,
@@ -501,7 +521,7 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
                                                     OP *__restrict__ Hb,
                                                     float *__restrict__ final_state, int64_t bh,
                                                     int h, int64_t nc, int n, int p,
-                                                    ImgArgs ia) {
+                                                    ImgArgs ia, float *__restrict__ states) {
     constexpr int G8 = 8;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
@@ -523,8 +543,11 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
     OP *dst = Hb + ((b * nc * h + hh) * np4 + e4) * 4;
     const float *L = Lam + pair * nc;
     // chunks whose own state is needed: all but the last unless the final
-    // state is asked for (the last chunk's state is then not even written)
-    const int64_t ns = final_state ? nc : nc - 1;
+    // state or the state after every chunk is asked for (the last chunk's
+    // state is otherwise not even written)
+    const int64_t ns = (final_state || states) ? nc : nc - 1;
+    // the state after chunk k, [b, nc, h, n, p]: this thread's 4 state rows
+    float *so = states ? states + ((b * nc) * h + hh) * (int64_t)n * p + n0 * p + pc : nullptr;
     const int64_t klast = ns > 0 ? ns - 1 : 0;
     for (int64_t k0 = 0; k0 < nc; k0 += G8) {
         f32x4 Sk[G8];
@@ -541,6 +564,11 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
             // initial state (the chunk output reads zeros otherwise)
             if (k0 + u < nc && (k0 + u > 0 || init)) store_state4(dst + (k0 + u) * cstride * 4, H);
             if (k0 + u < ns) H = exp2_fast(Lk[u]) * H + Sk[u];
+            if (so && k0 + u < nc) {
+                float *o = so + (k0 + u) * h * (int64_t)n * p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e * p] = H[e];
+            }
         }
     }
     if (final_state) {
@@ -621,6 +649,8 @@ struct alignas(16) CoRows {
     float l2[kT];    // lcs_i in the same pairs
     float bw[kT];    // 2^(lcs_15 - lcs_j) d_j
     float w[kT];     // 2^(lcs_31 - lcs_j) d_j: weight in the state at the block's end
+    int seg[kT];     // packed sequences: the last row <= i of the block that starts
+                     // from a zero state, or -1
 };
 __device__ __forceinline__ int row_pair(int r) { return 2 * (r & 15) + (r >> 4); }
 
@@ -628,6 +658,8 @@ __device__ __forceinline__ int row_pair(int r) { return 2 * (r & 15) + (r >> 4);
 // tid % kT (threads past HPW * kT load and discard).
 struct CoRowV {
     float ls, ds, ws, l15;
+    int sq, sqp, sv;  // packed sequences: document index of the row and of the row
+                      // before it, and whether the row is a real one after token 0
 };
 
 // Register prefetch of one block for the whole workgroup (fp32 io).  Loads
@@ -652,9 +684,14 @@ template <typename IO> struct CoPtrs {
     uint32_t hstride;   // bytes from one head's row arrays to the next
     int rows;           // valid rows of the chunk
     Rsrc rimg;          // block images of this (batch, chunk, group) (bf16 io)
+    Rsrc rsq;           // document indices of the batch row (packed sequences)
+    int64_t t0;         // the chunk's first token
 };
 
-template <int HPW, typename IO>
+// Vector memory loads co_rows_prefetch issues per thread.
+template <bool SEQ> constexpr int kRowLoads = SEQ ? 6 : 4;
+
+template <int HPW, bool SEQ, typename IO>
 __device__ __forceinline__ void co_rows_prefetch(CoRowV &f, int s, const CoPtrs<IO> &cp, int tid) {
     constexpr int T = kT;
     const int hs = tid < HPW * T ? tid / T : 0, row = tid % T;
@@ -664,14 +701,32 @@ __device__ __forceinline__ void co_rows_prefetch(CoRowV &f, int s, const CoPtrs<
     f.ds = buf_f32(cp.rd, ro, soff);
     f.ws = buf_f32(cp.rw, ro, soff);
     f.l15 = buf_f32(cp.rl, (uint32_t)hs * cp.hstride + 15u * 4u, soff);
+    if constexpr (SEQ) {
+        // whole offsets in the lane operand, so that the row before token 0
+        // (offset -4) falls outside the resource and reads 0
+        const int64_t t = cp.t0 + s * T + row;
+        f.sq = (int)__builtin_bit_cast(
+            uint32_t, buf_f32(cp.rsq, (uint32_t)(t * 4), 0u));
+        f.sqp = (int)__builtin_bit_cast(
+            uint32_t, buf_f32(cp.rsq, (uint32_t)(t * 4 - 4), 0u));
+        f.sv = (s * T + row < cp.rows) && t > 0;
+    }
 }
 
-template <int HPW>
+template <int HPW, bool SEQ>
 __device__ __forceinline__ void co_rows_stage(const CoRowV &f, CoRows *rows, int tid) {
     constexpr int T = kT;
     if (tid < HPW * T) {
         CoRows &rw = rows[tid / T];
         const int r = tid % T;
+        if constexpr (SEQ) {
+            // rows of this block that start from a zero state (one 32-lane
+            // group per head, all holding the same rows)
+            const uint32_t m =
+                (uint32_t)(__ballot(f.sv && f.sq != f.sqp) >> (tid & 32)) &
+                ((2u << r) - 1u);
+            rw.seg[r] = m ? 31 - __builtin_clz(m) : -1;
+        }
         rw.lcs[r] = f.ls;
         rw.d[r] = f.ds;
         rw.a2[row_pair(r)] = exp2_fast(f.ls - f.l15);
@@ -687,7 +742,6 @@ __device__ __forceinline__ void co_rows_stage(const CoRowV &f, CoRows *rows, int
 // raw bf16 with each lane fetching the 16-byte chunk its LDS slot holds.
 // Rows past the chunk's end read as zeros.  Issues exactly K::ND copies per
 // thread.
-typedef __attribute__((address_space(3))) void lds_void;
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_dma(typename Op<IO>::type *buf, int s, const CoPtrs<IO> &cp,
                                        int wave, int lane) {
@@ -696,8 +750,7 @@ __device__ __forceinline__ void co_dma(typename Op<IO>::type *buf, int s, const 
 #pragma unroll
     for (int q0 = 0; q0 < K::CBQ; q0 += K::NT) {
         const int q = q0 + wave * 64;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            cp.rimg, (lds_void *)(buf + q * 8), 16, (uint32_t)((s * K::CBQ + q + lane) * 16), 0, 0, 0);
+        lds_copy16(cp.rimg, (lds_void *)(buf + q * 8), (uint32_t)((s * K::CBQ + q + lane) * 16));
     }
     const int r0 = s * T;
     int valid = cp.rows - r0;
@@ -711,7 +764,7 @@ __device__ __forceinline__ void co_dma(typename Op<IO>::type *buf, int s, const 
         const int hs = q / (T * CH), rem = q % (T * CH), r = rem / CH, k = rem % CH;
         const uint32_t off =
             (uint32_t)(r * cp.xs + hs * P + ((k ^ xsw<P>(r)) << 3)) * (uint32_t)sizeof(IO);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void *)(Xs + qw * 8), 16, off, 0, 0, 0);
+        lds_copy16(rx, (lds_void *)(Xs + qw * 8), off);
     }
 }
 
@@ -726,7 +779,7 @@ template <int N> __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <typename IO, int P, int N, int HPW>
+template <bool SEQ, typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, const CoPtrs<IO> &cp,
                                             int tid) {
     typedef Co<IO, P, N, HPW, false> K;
@@ -759,10 +812,10 @@ __device__ __forceinline__ void co_prefetch(CoBuf<IO, P, N, HPW> &f, int s, cons
                                            (uint32_t)sizeof(IO));
         }
     }
-    co_rows_prefetch<HPW>(f.r, s, cp, tid);
+    co_rows_prefetch<HPW, SEQ>(f.r, s, cp, tid);
 }
 
-template <typename IO, int P, int N, int HPW>
+template <bool SEQ, typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
                                          typename Op<IO>::type *buf, CoRows *rows, int tid) {
     typedef Co<IO, P, N, HPW, false> K;
@@ -792,7 +845,7 @@ __device__ __forceinline__ void co_stage(const CoBuf<IO, P, N, HPW> &f,
                     op_piece(f.xv[k]));
         }
     }
-    co_rows_stage<HPW>(f.r, rows, tid);
+    co_rows_stage<HPW, SEQ>(f.r, rows, tid);
 }
 
 // Decay-weighted x, w_j x_j, as the k-major B operand of the state carry:
@@ -866,7 +919,7 @@ __device__ __forceinline__ f16x8 xs_frag_raw(const f16 *Xs, int c0, int u, int l
 // One block of the chunk output for one wave: head slot hs, columns
 // c0 .. c0 + PW - 1 of that head.  accH: the wave's CPW x RT state tiles
 // (inlined: stays in registers).
-template <typename IO, int P, int N, int HPW, bool COPY>
+template <typename IO, int P, int N, int HPW, bool COPY, bool SEQ>
 __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::type *buf,
                                            const CoRows &rf, bool carry, float Dh,
                                            const CoPtrs<IO> &cp, int r0, int hs, int c0,
@@ -970,6 +1023,20 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
             }
         }
     }
+    if constexpr (SEQ) {
+        // packed sequences: scores only between rows of one document, and
+        // the state entering the block only for rows before its first reset
+        const int sA = rf.seg[li], sB = rf.seg[16 + li];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j0 = 4 * lg + r;
+            if (j0 < sA) pv[0][0][r] = 0.f;
+            if (j0 < sB) pv[1][0][r] = 0.f;
+            if (16 + j0 < sB) pv[1][1][r] = 0.f;
+        }
+        if (sA >= 0) colscale[0] = 0.f;
+        if (sB >= 0) colscale[1] = 0.f;
+    }
     // the skip term rides on the diagonal: (P + D I) x = P x + D x
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1042,7 +1109,8 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
 
     // ---- carry the state to the next block of the chunk
     if (carry) {
-        const float decay = exp2_fast(lam);
+        // packed sequences: nothing carried across a reset in the block
+        const float decay = (SEQ && rf.seg[T - 1] >= 0) ? 0.f : exp2_fast(lam);
         typename Mfma<OP>::frag xw[CPW][KS];
 #pragma unroll
         for (int u = 0; u < CPW; ++u)
@@ -1066,13 +1134,16 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
     }
 }
 
-template <typename IO, int P, int N, int HPW, bool COPY>
-__global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT), (Co<IO, P, N, HPW, COPY>::DMA ? 3 : 1)) void k_chunk_out(
+// copying path: three workgroups per compute unit (two with packed sequences,
+// whose masks need more registers than three allow without spilling)
+template <typename IO, int P, int N, int HPW, bool COPY, bool SEQ>
+__global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT),
+                             (Co<IO, P, N, HPW, COPY>::DMA ? (SEQ ? 2 : 3) : 1)) void k_chunk_out(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ lcs, const float *__restrict__ dtp,
     const float *__restrict__ wgt, const typename Op<IO>::type *__restrict__ Hb,
     IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp,
-    const f16 *__restrict__ img, int64_t nsb, int has_init) {
+    const f16 *__restrict__ img, int64_t nsb, int has_init, const int32_t *__restrict__ seq) {
     typedef Co<IO, P, N, HPW, COPY> K;
     typedef typename K::OP OP;
     constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
@@ -1110,6 +1181,8 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT), (Co<IO, P, N, HPW, C
     cp.rw = make_rsrc(wgt + rbase, rspan);
     cp.hstride = (uint32_t)(nc * Qp * 4);
     cp.rows = (int)((Q < l - t0) ? Q : (l - t0));
+    cp.t0 = t0;
+    if constexpr (SEQ) cp.rsq = make_rsrc(seq + b * l, l * 4);
     if constexpr (K::DMA)
         cp.rimg = make_rsrc(img + ((b * nc + c) * g + gi) * nsb * (2 * T * N),
                             nsb * (int64_t)(4 * T * N));
@@ -1158,36 +1231,36 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT), (Co<IO, P, N, HPW, C
         // counts waited for are exact.
         CoRowV ra, rb;
         co_dma<IO, P, N, HPW>(buf0, 0, cp, wave, lane);
-        co_rows_prefetch<HPW>(ra, 0, cp, tid);
+        co_rows_prefetch<HPW, SEQ>(ra, 0, cp, tid);
         issue_fence();
         load_boundary();
         issue_fence();
         co_dma<IO, P, N, HPW>(buf1, 1, cp, wave, lane);
-        co_rows_prefetch<HPW>(rb, 1, cp, tid);
+        co_rows_prefetch<HPW, SEQ>(rb, 1, cp, tid);
         issue_fence();
-        vm_wait<K::ND + 4>();  // block 0 and the boundary state have landed
-        co_rows_stage<HPW>(ra, rows0, tid);
+        vm_wait<K::ND + kRowLoads<SEQ>>();  // block 0 and the boundary state have landed
+        co_rows_stage<HPW, SEQ>(ra, rows0, tid);
         lds_barrier();
 #pragma unroll
         for (int k = 0; k < CPW * RT; ++k)
             accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
         for (int s = 0; s < nblk; s += 2) {
             wave_priority(progress_priority(s, nblk));
-            co_compute<IO, P, N, HPW, COPY>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
+            co_compute<IO, P, N, HPW, COPY, SEQ>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
                                       c0, lane);
             vm_wait<K::NS>();  // block s + 1
-            co_rows_stage<HPW>(rb, rows1, tid);
+            co_rows_stage<HPW, SEQ>(rb, rows1, tid);
             lds_barrier();
             co_dma<IO, P, N, HPW>(buf0, s + 2, cp, wave, lane);
-            co_rows_prefetch<HPW>(ra, s + 2, cp, tid);
+            co_rows_prefetch<HPW, SEQ>(ra, s + 2, cp, tid);
             issue_fence();
-            co_compute<IO, P, N, HPW, COPY>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+            co_compute<IO, P, N, HPW, COPY, SEQ>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
                                       hs, c0, lane);
             vm_wait<K::NS>();  // block s + 2
-            co_rows_stage<HPW>(ra, rows0, tid);
+            co_rows_stage<HPW, SEQ>(ra, rows0, tid);
             lds_barrier();
             co_dma<IO, P, N, HPW>(buf1, s + 3, cp, wave, lane);
-            co_rows_prefetch<HPW>(rb, s + 3, cp, tid);
+            co_rows_prefetch<HPW, SEQ>(rb, s + 3, cp, tid);
             issue_fence();
         }
         // no copy may still be writing this workgroup's LDS when it exits
@@ -1200,24 +1273,24 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT), (Co<IO, P, N, HPW, C
         // past the end is computed on zeros and stores nothing), so the loop
         // has one path and the memory counters never need a full drain.
         CoBuf<IO, P, N, HPW> pa, pb;
-        co_prefetch(pa, 0, cp, tid);
-        co_prefetch(pb, 1, cp, tid);
+        co_prefetch<SEQ>(pa, 0, cp, tid);
+        co_prefetch<SEQ>(pb, 1, cp, tid);
         load_boundary();
-        co_stage(pa, buf0, rows0, tid);
-        co_prefetch(pa, 2, cp, tid);
+        co_stage<SEQ>(pa, buf0, rows0, tid);
+        co_prefetch<SEQ>(pa, 2, cp, tid);
         lds_barrier();
 #pragma unroll
         for (int k = 0; k < CPW * RT; ++k)
             accH[k] = f32x4{(float)hraw[k][0], (float)hraw[k][1], (float)hraw[k][2], (float)hraw[k][3]};
         for (int s = 0; s < nblk; s += 2) {
-            co_stage(pb, buf1, rows1, tid);  // block s + 1
-            co_prefetch(pb, s + 3, cp, tid);
-            co_compute<IO, P, N, HPW, COPY>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
+            co_stage<SEQ>(pb, buf1, rows1, tid);  // block s + 1
+            co_prefetch<SEQ>(pb, s + 3, cp, tid);
+            co_compute<IO, P, N, HPW, COPY, SEQ>(accH, buf0, rows0[hs], s + 1 < nblk, Dh, cp, s * T, hs,
                                       c0, lane);
             lds_barrier();
-            co_stage(pa, buf0, rows0, tid);  // block s + 2
-            co_prefetch(pa, s + 4, cp, tid);
-            co_compute<IO, P, N, HPW, COPY>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
+            co_stage<SEQ>(pa, buf0, rows0, tid);  // block s + 2
+            co_prefetch<SEQ>(pa, s + 4, cp, tid);
+            co_compute<IO, P, N, HPW, COPY, SEQ>(accH, buf1, rows1[hs], s + 2 < nblk, Dh, cp, (s + 1) * T,
                                       hs, c0, lane);
             lds_barrier();
         }
@@ -1243,17 +1316,30 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
 
     constexpr int HP = kGroupHeads<P>;
     const bool grouped = HP > 1 && group_heads((int)P, h / g) == HP;
+    // the last chunk's own state is needed for the final state and for the
+    // state after the last chunk
+    const int keep_last = a.final_state != nullptr || a.states != nullptr;
+    const bool seq = a.seq != nullptr;
+    auto launch_state = [&](auto hp_c, auto seq_c) {
+        constexpr int HPn = decltype(hp_c)::value;
+        constexpr bool SQ = decltype(seq_c)::value;
+        hipLaunchKernelGGL((k_chunk_state<IO, P, N, HPn, SQ>),
+                           dim3((unsigned)(pl.b * pl.nc * (h / HPn))), dim3(Sp<IO, P, N, HPn>::NT),
+                           0, s, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min, a.dt_max, lcs,
+                           dtp, wgt, St, Lam, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq);
+    };
     trace_begin(1, s);
-    if (grouped)
-        hipLaunchKernelGGL((k_chunk_state<IO, P, N, HP>), dim3((unsigned)(pl.b * pl.nc * (h / HP))),
-                           dim3(Sp<IO, P, N, HP>::NT), 0, s, x, Bm, dt, a.A, a.dt_bias,
-                           a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam, pl.l, h, g,
-                           pl.Q, pl.nc, pl.Qp, a.final_state != nullptr);
-    else
-        hipLaunchKernelGGL((k_chunk_state<IO, P, N, 1>), dim3((unsigned)(pl.b * pl.nc * h)),
-                           dim3(Sp<IO, P, N, 1>::NT), 0, s, x, Bm, dt, a.A, a.dt_bias,
-                           a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam, pl.l, h, g,
-                           pl.Q, pl.nc, pl.Qp, a.final_state != nullptr);
+    if (grouped) {
+        if (seq)
+            launch_state(std::integral_constant<int, HP>{}, std::true_type{});
+        else
+            launch_state(std::integral_constant<int, HP>{}, std::false_type{});
+    } else {
+        if (seq)
+            launch_state(std::integral_constant<int, 1>{}, std::true_type{});
+        else
+            launch_state(std::integral_constant<int, 1>{}, std::false_type{});
+    }
     trace_end(1, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1277,33 +1363,39 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     ia.pieces = copy ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
     trace_begin(2, s);
     hipLaunchKernelGGL((k_state_scan<OP, IO, N>), dim3((unsigned)scan_blocks), dim3(kThreads), 0, s,
-                       St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h, pl.nc, N, P, ia);
+                       St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h, pl.nc, N, P, ia,
+                       a.states);
     trace_end(2, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     trace_begin(3, s);
-    auto launch_out = [&](auto hp_c, auto copy_c) {
+    auto launch_out = [&](auto hp_c, auto copy_c, auto seq_c) {
         constexpr int HPn = decltype(hp_c)::value;
         constexpr bool CP = decltype(copy_c)::value;
-        hipLaunchKernelGGL((k_chunk_out<IO, P, N, HPn, CP>),
+        constexpr bool SQ = decltype(seq_c)::value;
+        hipLaunchKernelGGL((k_chunk_out<IO, P, N, HPn, CP, SQ>),
                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))),
                            dim3(Co<IO, P, N, HPn, CP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt,
                            Hb, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb,
-                           a.init != nullptr);
+                           a.init != nullptr, a.seq);
     };
+    typedef std::integral_constant<int, 1> One;
+    typedef std::integral_constant<int, HP> Grp;
+    typedef std::true_type Yes;
+    typedef std::false_type No;
     if constexpr (sizeof(IO) == 2) {
         if (!grouped)
-            launch_out(std::integral_constant<int, 1>{}, std::true_type{});
+            seq ? launch_out(One{}, Yes{}, Yes{}) : launch_out(One{}, Yes{}, No{});
         else if (copy)
-            launch_out(std::integral_constant<int, HP>{}, std::true_type{});
+            seq ? launch_out(Grp{}, Yes{}, Yes{}) : launch_out(Grp{}, Yes{}, No{});
         else
-            launch_out(std::integral_constant<int, HP>{}, std::false_type{});
+            seq ? launch_out(Grp{}, No{}, Yes{}) : launch_out(Grp{}, No{}, No{});
     } else {
         if (grouped)
-            launch_out(std::integral_constant<int, HP>{}, std::false_type{});
+            seq ? launch_out(Grp{}, No{}, Yes{}) : launch_out(Grp{}, No{}, No{});
         else
-            launch_out(std::integral_constant<int, 1>{}, std::false_type{});
+            seq ? launch_out(One{}, No{}, Yes{}) : launch_out(One{}, No{}, No{});
     }
     trace_end(3, s);
     return hipGetLastError();

@@ -1,0 +1,128 @@
+"""GPU parity of the packed-sequence reset and of the state after every
+chunk (ssd_chunk_scan_ex, through the C ABI) against the fp64 oracle.
+
+Packed rows hold several documents back to back; wherever the per-token
+document index changes, the next token starts from a zero state (the
+sample-packing reset of the Mamba2 news page).  The state after every chunk
+boundary is the nnterp guide's "state after every token" with chunk 1.
+"""
+import numpy as np
+import pytest
+
+import ssd_synth as syn
+from gpu_util import (STATE_AXES, Y_AXES, check_close, gpu_inputs, log, oracle_kw, to_f64,
+                      torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    oracle.build()
+    return oracle
+
+
+def _seq(b, l, cuts_per_row):
+    seq = np.zeros((b, l), np.int32)
+    for bi, cuts in enumerate(cuts_per_row):
+        for k, c in enumerate(cuts):
+            seq[bi, c:] = 10 * (k + 1) + bi
+    return seq
+
+
+def _run(inp, Q, seq=None, states=False, final=True):
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    g = gpu_inputs(inp)
+    sq = None if seq is None else torch.from_numpy(seq).to("cuda")
+    out = ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk_size=Q,
+                         dt_bias=g["dt_bias"], initial_state=g["init"],
+                         return_final_state=final, seq_idx=sq,
+                         return_chunk_states=states)
+    torch.cuda.synchronize()
+    return out
+
+
+# (batch, seqlen, heads, head_dim, state_dim, groups, chunk, init_std, resets per row)
+PACKED = [
+    (2, 300, 4, 64, 128, 2, 64, 0.2, [(5, 40, 41, 64, 200), (1, 299)]),  # chunk starts, one-token documents
+    (1, 520, 24, 64, 128, 1, 256, 0.0, [(17, 256, 300, 513)]),         # bench shape, reset at a chunk start
+    (2, 130, 8, 32, 64, 2, 100, 0.1, [(31, 32, 33, 99), ()]),          # ragged chunks, block edges
+    (3, 77, 4, 16, 32, 4, 16, 0.0, [(1,), (7, 8, 9, 10), (76,)]),      # short chunks, resets on the last token
+    (1, 200, 3, 128, 128, 1, 64, 0.3, [(63, 64, 65, 128)]),            # head_dim 128, odd group size
+]
+
+
+def _pid(c):
+    return "b%d_l%d_h%d_p%d_n%d_g%d_Q%d" % c[:7]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("case", PACKED, ids=_pid)
+def test_packed_sequences_parity(orc, case, io):
+    b, l, h, p, n, g, Q, init, cuts = case
+    inp = syn.random_case(3000 + sum(case[:7]), b, l, h, p, n, g, io=io, init_std=init)
+    seq = _seq(b, l, cuts)
+    y, fin, st = _run(inp, Q, seq=seq, states=True)
+    yo, fo, so = orc.scan(**oracle_kw(inp), seq_idx=seq, states_chunk=Q)
+    s1 = check_close(to_f64(y), yo, io, "y", Y_AXES)
+    check_close(to_f64(fin), fo, io, "final_state", STATE_AXES)
+    check_close(to_f64(st), so, io, "chunk states", (1, 3, 4))
+    log("y max_abs %.3g max_rel %.3g" % (s1[0], s1[1]))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("init", [0.0, 0.4])
+@pytest.mark.parametrize("Q,l", [(64, 300), (100, 250), (256, 256), (32, 33)])
+def test_chunk_states_parity(orc, io, init, Q, l):
+    """The state after every chunk boundary, [b, chunks, h, n, p]; the last
+    one equals the final state."""
+    inp = syn.random_case(3100 + Q + l, 2, l, 4, 64, 64, 2, io=io, init_std=init)
+    y, fin, st = _run(inp, Q, states=True)
+    assert st.shape[1] == -(-l // Q)
+    assert torch_mod().equal(st[:, -1], fin)
+    yo, fo, so = orc.scan(**oracle_kw(inp), states_chunk=Q)
+    check_close(to_f64(y), yo, io, "y", Y_AXES)
+    check_close(to_f64(st), so, io, "chunk states", (1, 3, 4))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_per_token_states(orc, io):
+    """chunk 1: the state after every token (nnterp guide, "The state after
+    every token"), with packed documents as well."""
+    inp = syn.random_case(3200, 2, 40, 4, 32, 64, 1, io=io, init_std=0.2)
+    seq = _seq(2, 40, [(9, 10, 30), ()])
+    y, st = _run(inp, 1, seq=seq, states=True, final=False)
+    assert tuple(st.shape) == (2, 40, 4, 64, 32)
+    yo, fo, so = orc.scan(**oracle_kw(inp), seq_idx=seq, states_chunk=1)
+    check_close(to_f64(y), yo, io, "y", Y_AXES)
+    check_close(to_f64(st), so, io, "per-token states", (1, 3, 4))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_constant_document_index_changes_nothing(io):
+    """A document index that never changes gives the same bits as none."""
+    inp = syn.random_case(3300, 2, 333, 4, 64, 128, 2, io=io, init_std=0.1)
+    seq = np.full((2, 333), 5, np.int32)
+    y0, f0 = _run(inp, 64)
+    y1, f1 = _run(inp, 64, seq=seq)
+    torch = torch_mod()
+    assert torch.equal(y0, y1)
+    assert torch.equal(f0, f1)
+
+
+@pytest.mark.parametrize("case", PACKED[:2], ids=_pid)
+def test_packed_staging_paths_agree(orc, case, monkeypatch):
+    """Both bf16 chunk-output stagings (registers, copied block images) with
+    packed documents give the same bits."""
+    b, l, h, p, n, g, Q, init, cuts = case
+    inp = syn.random_case(3400 + sum(case[:7]), b, l, h, p, n, g, io="bf16", init_std=init)
+    seq = _seq(b, l, cuts)
+    out = {}
+    for v in ("0", "1"):
+        monkeypatch.setenv("SSD_CHUNK_OUT_COPY", v)
+        out[v] = _run(inp, Q, seq=seq)
+    torch = torch_mod()
+    assert torch.equal(out["0"][0], out["1"][0])
+    assert torch.equal(out["0"][1], out["1"][1])
