@@ -70,24 +70,27 @@ def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
     return th * (2 * p * s + 2 * n * s * g / h + s) + 4 * n * p * b * h * (int(init) + int(final))
 
 
-def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False):
+def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False, states=False):
     """Algorithmic bytes of one launch of a scan kernel: every operand of its
     step of the method moved once (per-row workspace arrays fp32, chunk
     states fp32, boundary states in the read-out's operand type: fp16 on the
-    bf16 path, fp32 on the fp32 path)."""
+    bf16 path, fp32 on the fp32 path; with `states`, the state after every
+    chunk written in fp32)."""
     nc, lp = plan_sizes(b, l, h, p, n, g, Q)
     th = b * l * h
     x = th * p * s                     # x (and y) in the io dtype
     BC = b * l * g * n * s             # B or C, once per group
     rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
     so = 2 if s == 2 else 4            # boundary-state element
-    # chunk states needed: the last chunk's only feeds the final state
-    ns = nc if final else nc - 1
+    # chunk states needed: the last chunk's only feeds the final state and
+    # the state after the last chunk
+    ns = nc if (final or states) else nc - 1
     sn = b * ns * h * n * p
     # boundary states stored and read: chunk 0's is the initial state, zero
     # (and neither stored nor read) when none is given
     sb = b * (nc if init else nc - 1) * h * n * p
     fin = b * h * n * p * 4 if final else 0
+    sout = b * nc * h * n * p * 4 if states else 0
     if name == "chunk_state":
         # x, B and dt read; the per-row lcs, d and weights, the needed chunk
         # states and decays written
@@ -96,7 +99,7 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False):
         # needed chunk states and decays read, boundary states written; on the
         # bf16 path also B and C read once and their fp16 block images written
         img = 2 * BC + 2 * b * nc * g * (-(-Q // 32) * 32) * n * 2 if s == 2 else 0
-        return 4 * sn + b * h * ns * 4 + so * sb + fin + img
+        return 4 * sn + b * h * ns * 4 + so * sb + fin + img + sout
     if name == "chunk_out":
         # x, B and C (bf16 path: their fp16 block images, the same size), the
         # lcs, d and weight rows and the boundary states read, y written
@@ -138,6 +141,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="input/output sets cycled through")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-states", action="store_true",
+                    help="skip the packed-sequence and state-output measurements")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0, help="oracle sample size (0: all)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -234,21 +239,8 @@ def main():
     value = b * l * args.steps / (t1 - t0)
     log("scan: %.3f ms/step, %.4g tokens/s" % (ms_step, value))
 
-    # per-kernel durations: HIP events recorded by the library on the launch stream
-    ssd.trace_enable(True)
-    for name in KERNEL_IDS:
-        ssd.trace_read(name)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        run(i)
-    torch.cuda.synchronize()
-    ssd.trace_enable(False)
-    kern = {}
-    for name in KERNEL_IDS:
-        tot, cnt = ssd.trace_read(name)
-        if cnt:
-            kern[name] = dict(avg_us=1e3 * tot / cnt, launches=cnt,
-                              alg_bytes=bytes_kernel(name, b, l, h, p, n, g, Q, s))
+    kern = kernel_times(ssd, torch, run, args.steps,
+                        lambda name: bytes_kernel(name, b, l, h, p, n, g, Q, s))
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
     dk = kern[dom]
     achieved = dk["alg_bytes"] / (dk["avg_us"] * 1e-6) / 1e9
@@ -270,6 +262,10 @@ def main():
                  "frac_min": round(bmin / (HBM_PEAK_GBS * 1e9) / (ms_step * 1e-3), 4),
                  "kernels": kern}
 
+    states = None
+    if not args.no_states:
+        states = bench_states(args, torch, ssd, np, sets, ws, w, dev)
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(args, torch, ssd, syn, dev)
@@ -289,10 +285,128 @@ def main():
                    "state": "fp32", "input_sets": args.sets},
         "roofline": roofline,
         "scan_roofline": scan_roof,
+        "states": states,
         "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def kernel_times(ssd, torch, run, steps, alg_bytes):
+    """Average duration of each scan kernel over `steps` calls of run(i),
+    from HIP events the library records on its launch stream, with the
+    kernel's algorithmic bytes and the rate they imply."""
+    ssd.trace_enable(True)
+    for name in KERNEL_IDS:
+        ssd.trace_read(name)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    ssd.trace_enable(False)
+    kern = {}
+    for name in KERNEL_IDS:
+        tot, cnt = ssd.trace_read(name)
+        if cnt:
+            kern[name] = dict(avg_us=1e3 * tot / cnt, launches=cnt, alg_bytes=alg_bytes(name))
+    return kern
+
+
+def doc_index(np, rng, b, l, lo=32, hi=2048):
+    """Document index of packed rows: documents back to back, lengths
+    log-uniform in [lo, hi] tokens, the last one cut at the row's end."""
+    seq = np.zeros((b, l), np.int32)
+    for bi in range(b):
+        t = k = 0
+        while t < l:
+            m = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+            seq[bi, t:t + m] = k
+            t += m
+            k += 1
+    return seq
+
+
+def bench_states(args, torch, ssd, np, sets, ws, w, dev):
+    """The scan with packed documents (a per-token document index) and with
+    the state after every chunk written, on the same workload and input sets
+    as the headline; and the state after every token (chunk 1) on one batch
+    row of it."""
+    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
+    s = 2
+    nc, _ = plan_sizes(b, l, h, p, n, g, Q)
+    rng = np.random.default_rng(w.seed + 77)
+    seqs = [torch.from_numpy(doc_index(np, rng, b, l)).to(dev) for _ in sets]
+    docs = sum(int(q[:, -1].sum()) + b for q in seqs) / len(seqs)
+    st_out = torch.empty((b, nc, h, n, p), dtype=torch.float32, device=dev)
+    steps = max(args.steps // 2, 10)
+
+    def measure(tag, run, alg_extra):
+        for i in range(5):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        kern = kernel_times(ssd, torch, run, steps,
+                            lambda k: bytes_kernel(k, b, l, h, p, n, g, Q, s,
+                                                   states=tag == "chunk_states")
+                            + alg_extra.get(k, 0))
+        for v in kern.values():
+            v["GBs"] = round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1)
+            v["avg_us"] = round(v["avg_us"], 2)
+        log("%s: %.4f ms/step %s" % (tag, ms, json.dumps(kern)))
+        return {"value": round(b * l / (ms * 1e-3), 1), "unit": "tokens/s",
+                "ms_per_step": round(ms, 4), "kernels": kern}
+
+    def run_packed(i):
+        S = sets[i % len(sets)]
+        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
+                       dt_bias=S["bias"], out=S["y"], workspace=ws, seq_idx=seqs[i % len(seqs)])
+
+    def run_states(i):
+        S = sets[i % len(sets)]
+        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
+                       dt_bias=S["bias"], out=S["y"], workspace=ws,
+                       return_chunk_states=True, chunk_states_out=st_out)
+
+    # the document index is read by the chunk-state pass and the chunk output
+    # (4 bytes per token each); every chunk's state is written once (fp32)
+    packed = measure("packed", run_packed, {"chunk_state": 4 * b * l, "chunk_out": 4 * b * l})
+    packed["documents_per_step"] = round(docs, 1)
+    packed["doc_lengths"] = "log-uniform in [32, 2048] tokens, seeded"
+    chunks = measure("chunk_states", run_states, {})
+
+    # the state after every token: chunk 1, one batch row, each token's
+    # state written in fp32 (the rate that bounds this mode)
+    S = sets[0]
+    x1, dt1, B1, C1 = S["x"][:1], S["dt"][:1], S["B"][:1], S["C"][:1]
+    y1 = torch.empty((1, l, h, p), dtype=torch.bfloat16, device=dev)
+    tok_states = torch.empty((1, l, h, n, p), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(ssd.workspace_bytes(1, l, h, p, n, g, 1), dtype=torch.uint8, device=dev)
+
+    def run_tok(i):
+        ssd.chunk_scan(x1, dt1, S["A"], B1, C1, S["D"], chunk_size=1, dt_bias=S["bias"],
+                       out=y1, workspace=ws1, return_chunk_states=True,
+                       chunk_states_out=tok_states)
+    for i in range(3):
+        run_tok(i)
+    torch.cuda.synchronize()
+    nt = max(steps // 10, 5)
+    t0 = time.perf_counter()
+    for i in range(nt):
+        run_tok(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / nt
+    wbytes = l * h * n * p * 4
+    log("per-token states: %.3f ms per row, %.0f GB/s of state written" %
+        (ms, wbytes / (ms * 1e-3) / 1e9))
+    per_token = {"value": round(l / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(ms, 4),
+                 "config": {"batch": 1, "seqlen": l, "heads": h, "chunk": 1},
+                 "state_bytes_written": wbytes,
+                 "state_write_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+    return {"packed": packed, "chunk_states": chunks, "per_token": per_token}
 
 
 def bench_decode(args, torch, ssd, syn, dev):

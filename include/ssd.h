@@ -84,7 +84,10 @@ enum ssd_status {
  *                 written); may equal init_state (in-place continuation);
  *                 16-byte aligned
  *   chunk         chunk length (any value >= 1; boundary states every chunk
- *                 tokens; the last chunk may be shorter)
+ *                 tokens; the last chunk may be shorter).  A chunk shorter
+ *                 than 32 tokens is computed as chunks of a whole number of
+ *                 them (the smallest multiple >= 64 tokens): the same sum in
+ *                 a coarser blocking, equal up to rounding.
  *   workspace     device scratch of at least ssd_chunk_scan_workspace_bytes
  *                 (...) bytes, 256-byte aligned; contents on entry ignored
  *   hip_stream    hipStream_t to launch on
@@ -130,7 +133,11 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
  *                 Entry c is the state after the last token of chunk c
  *                 (nnterp guide, "The state after every token": one state
  *                 per chunk boundary; chunk = 1 gives the state after every
- *                 token, and the last entry equals the final state).
+ *                 token, and the last entry is the final state).  For a
+ *                 chunk shorter than 32 tokens the states are stepped token
+ *                 by token (fp32) from the states at the computed chunks'
+ *                 boundaries, in one extra launch (SSD_K_TOKEN_STATES); the
+ *                 last entry then equals final_state up to rounding only.
  */
 int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const void *B,
                           const void *C, const float *D, const float *dt_bias,
@@ -204,7 +211,8 @@ enum ssd_kernel_id {
     SSD_K_STATE_SCAN = 2,  /* serial pass over chunks: boundary and final states */
     SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */
     SSD_K_STEP = 4,        /* decode step */
-    SSD_K_COUNT = 5
+    SSD_K_TOKEN_STATES = 5, /* states after chunks shorter than 32 tokens, token by token */
+    SSD_K_COUNT = 6
 };
 int32_t ssd_trace_enable(int32_t on);
 int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches);

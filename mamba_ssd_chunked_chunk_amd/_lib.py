@@ -17,7 +17,8 @@ SSD_ERR_WORKSPACE = -4
 SSD_ERR_ALIGN = -5
 SSD_ERR_HIP = -6
 
-KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step": 4}
+KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step": 4,
+           "token_states": 5}
 
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",

@@ -188,7 +188,7 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
         return SSD_ERR_SHAPE;
     // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
     const int64_t gmax = ((int64_t)1 << 31) - 1;
-    if (pl.b * pl.nc * pl.h > gmax || pl.b * pl.h * pl.n * pl.p / 4 / 256 + 1 > gmax)
+    if (pl.b * pl.nc * pl.h * 8 > gmax || pl.b * pl.h * pl.n * pl.p / 4 / 256 + 1 > gmax)
         return SSD_ERR_UNSUPPORTED;
     // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
     // one (batch, head)
@@ -204,8 +204,18 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
     ScanArgs a{x, dt, B, C, A, D, dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max,
                init_state, y, final_state, static_cast<char *>(workspace), seq_idx,
                chunk_states};
+    // caller chunks shorter than the computed ones: the scan keeps the states
+    // after its own chunks in the workspace, and the states the caller asked
+    // for are stepped from those
+    const bool fill = chunk_states && pl.Qs != pl.Q;
+    float *Hc = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.off_hc);
+    if (fill) a.states = Hc;
     hipError_t e = io_dtype == SSD_BF16 ? dispatch_scan<bf16>(pl, a, s)
                                         : dispatch_scan<float>(pl, a, s);
+    if (e == hipSuccess && fill) {
+        a.states = chunk_states;
+        e = launch_token_states(pl, a, Hc, s);
+    }
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -14,7 +14,10 @@ namespace ssd {
 // [c * Qp, (c + 1) * Qp) with Qp = ceil(Q / T) * T; padded rows past the end
 // of a chunk or of the sequence carry d = 0 (no write, no decay).
 struct ScanPlan {
-    int64_t b, l, h, p, n, g, Q;
+    int64_t b, l, h, p, n, g;
+    int64_t Q;    // tokens per chunk of the computation
+    int64_t Qs;   // tokens per chunk of the caller: the chunk states' spacing
+    int64_t ns;   // chunk states of the caller (ceil(l / Qs))
     int io;
     int T;        // rows per block
     int64_t nc;   // chunks
@@ -22,8 +25,19 @@ struct ScanPlan {
     int64_t Qp;   // padded rows per chunk
     int64_t lp;   // padded rows per sequence (nc * Qp)
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, off_img, total;
+    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, off_img, off_hc, total;
 };
+
+// Chunks shorter than one 32-row block are computed as chunks of a whole
+// number of them (at least 64 tokens): the kernels pad every chunk to whole
+// blocks, so a short chunk would mostly compute on padding.  The result is
+// the same up to rounding (the chunk size is a blocking of the same sum);
+// the states at the caller's chunk boundaries are then filled in token by
+// token from the states at the computed chunks' boundaries.
+constexpr int64_t kMinBlockChunk = 32, kFillChunk = 64;
+inline int64_t compute_chunk(int64_t Q) {
+    return Q >= kMinBlockChunk ? Q : Q * ((kFillChunk + Q - 1) / Q);
+}
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
@@ -55,7 +69,11 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
                       int64_t g, int64_t Q, int io) {
     if (b < 0 || l < 0 || h <= 0 || p <= 0 || n <= 0 || g <= 0 || Q <= 0) return false;
     if (h % g != 0) return false;
-    P.b = b; P.l = l; P.h = h; P.p = p; P.n = n; P.g = g; P.Q = Q; P.io = io;
+    P.b = b; P.l = l; P.h = h; P.p = p; P.n = n; P.g = g; P.io = io;
+    P.Qs = Q;
+    P.Q = compute_chunk(Q);
+    P.ns = (l + Q - 1) / Q;
+    Q = P.Q;
     P.T = 32;
     P.nc = (l + Q - 1) / Q;
     P.nsb = (Q + P.T - 1) / P.T;
@@ -74,6 +92,9 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     // C and B of every 32-row block of every (batch, chunk, group) as fp16,
     // in the chunk output's LDS layout (bf16 io only; room kept for both)
     P.off_img = o;  o += align256(b * P.nc * g * P.nsb * 2 * P.T * n * 2);
+    // fp32 states after the computed chunks, read by the per-token fill
+    // (short caller chunks only)
+    P.off_hc = o;   o += P.Qs != P.Q ? align256(b * P.nc * h * st * 4) : 0;
     P.total = o;
     return true;
 }
@@ -88,7 +109,7 @@ struct ScanArgs {
     float *final_state;
     char *ws;
     const int32_t *seq;  // [b, l] document index of every token, or NULL
-    float *states;       // [b, nc, h, n, p] state after every chunk, or NULL
+    float *states;       // [b, ns, h, n, p] state after every caller chunk, or NULL
 };
 
 struct StepArgs {
@@ -105,6 +126,12 @@ struct StepArgs {
 // Kernel-timing hooks (ssd_trace_*): called around every launch.
 void trace_begin(int kernel, hipStream_t s);
 void trace_end(int kernel, hipStream_t s);
+
+// States after every caller chunk, stepped token by token from Hc (the fp32
+// states after the computed chunks), for caller chunks shorter than the
+// computed ones.
+hipError_t launch_token_states(const ScanPlan &pl, const ScanArgs &a, const float *Hc,
+                               hipStream_t s);
 
 // Launchers, one per (io, head_dim, state_dim) instantiation.
 template <typename IO, int P, int N>

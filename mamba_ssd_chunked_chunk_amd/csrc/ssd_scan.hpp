@@ -326,11 +326,17 @@ __device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type
     }
 }
 
-// bf16 io: three workgroups per compute unit (at most 168 VGPRs; two with
-// packed sequences, whose reset flags need more)
+// Workgroups per compute unit the bf16 chunk-state pass is compiled for:
+// three (at most 168 VGPRs), except for packed-sequence instances whose
+// reset masks would then spill (one-head workgroups, and four heads of
+// head_dim 32 with state_dim 128), which get two.
+template <int P, int N, int HPW, bool SEQ> constexpr int cs_waves() {
+    return SEQ && (HPW == 1 || (P == 32 && N == 128)) ? 2 : 3;
+}
+
 template <typename IO, int P, int N, int HPW, bool SEQ>
 __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
-                             (sizeof(IO) == 2 ? (SEQ ? 2 : 3) : 1)) void k_chunk_state(
+                             (sizeof(IO) == 2 ? cs_waves<P, N, HPW, SEQ>() : 1)) void k_chunk_state(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
@@ -514,7 +520,45 @@ __device__ __forceinline__ void bc_image_piece(const ImgArgs &ia, int64_t q) {
     }
 }
 
-template <typename OP, typename IO, int N>
+// The state scan's threads cover each (batch, head) state in tiles of R
+// state rows by Cc head_dim columns (R = min(state_dim, 64), R Cc = 1024 or
+// all of a small state); a thread holds 4 consecutive state rows of one
+// column, the tile's threads running down the rows first.  Chunk states and
+// boundary states ([head_dim][state_dim]) are then read and written in runs
+// of R elements, and a tile's rows of the [state_dim][head_dim] outputs in
+// runs of Cc.
+struct ScanTile {
+    int R, Cc, TT;  // rows, columns, threads of a tile
+    __device__ ScanTile(int n, int p) {
+        R = n < 64 ? n : 64;
+        Cc = p < 1024 / R ? p : 1024 / R;
+        TT = R * Cc / 4;
+    }
+};
+
+// Stores a tile of the state ([state_dim][head_dim] order, 16 bytes per lane
+// along the rows) through LDS: thread t of the tile passes its 4 elements v
+// and the tile's output `out` (rows row0.., columns col0..).  Every thread of
+// the workgroup takes part (two barriers, which wait for LDS only: the global
+// stores before them stay in flight); `live` false stores nothing.
+__device__ __forceinline__ void store_state_rows(float *lds, const f32x4 &v, const ScanTile &st,
+                                                 bool live, float *out, int row0, int col0,
+                                                 int p) {
+    const int tid = threadIdx.x, tw = tid / st.TT, loc = tid % st.TT;
+    lds_barrier();  // earlier reads of the tile are done
+    *reinterpret_cast<f32x4 *>(lds + 4 * tid) = v;
+    lds_barrier();
+    const int v0 = 4 * loc, row = v0 / st.Cc, col = v0 % st.Cc;
+    const float *t = lds + tw * st.TT * 4;
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = t[(col + i) * st.R + row];
+    if (live) *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + row) * p + col0 + col) = o;
+}
+
+// ROWS: the final state or the state after every chunk is written (the
+// instance without them keeps fewer registers).
+template <typename OP, typename IO, int N, bool ROWS>
 __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St,
                                                     const float *__restrict__ Lam,
                                                     const float *__restrict__ init,
@@ -523,15 +567,27 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
                                                     int h, int64_t nc, int n, int p,
                                                     ImgArgs ia, float *__restrict__ states) {
     constexpr int G8 = 8;
+    __shared__ __attribute__((aligned(16))) float lds[4 * 256];
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
     for (int64_t q = idx; q < ia.pieces; q += nthreads) bc_image_piece<IO, N>(ia, q);
     const int64_t np4 = (int64_t)n * p / 4;
-    if (idx >= bh * np4) return;
-    const int64_t pair = idx / np4, e4 = idx % np4;
+    // threads past the last element stay for the barriers of the state
+    // stores (computing on the last element, storing nothing)
+    const bool live = idx < bh * np4;
+    if (!ROWS) states = final_state = nullptr;
+    if (!live && !ROWS) return;
+    const int64_t ie = live ? idx : bh * np4 - 1;
+    const ScanTile st(n, p);
+    const int64_t tile = ie / st.TT;
+    const int loc = (int)(ie % st.TT);
+    const int64_t tpp = (int64_t)(n / st.R) * (p / st.Cc);  // tiles per state
+    const int64_t pair = tile / tpp, tip = tile % tpp;
+    const int row0 = (int)(tip % (n / st.R)) * st.R, col0 = (int)(tip / (n / st.R)) * st.Cc;
     const int64_t b = pair / h, hh = pair % h;
     // element e of this thread: head_dim column pc, state row n0 + e
-    const int64_t pc = (e4 * 4) / n, n0 = (e4 * 4) % n;
+    const int64_t n0 = row0 + (loc % (st.R / 4)) * 4, pc = col0 + loc / (st.R / 4);
+    const int64_t e4 = (pc * n + n0) / 4;
     f32x4 H = zero4();
     if (init) {
         const float *src = init + pair * (int64_t)n * p + n0 * p + pc;
@@ -546,8 +602,6 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
     // state or the state after every chunk is asked for (the last chunk's
     // state is otherwise not even written)
     const int64_t ns = (final_state || states) ? nc : nc - 1;
-    // the state after chunk k, [b, nc, h, n, p]: this thread's 4 state rows
-    float *so = states ? states + ((b * nc) * h + hh) * (int64_t)n * p + n0 * p + pc : nullptr;
     const int64_t klast = ns > 0 ? ns - 1 : 0;
     for (int64_t k0 = 0; k0 < nc; k0 += G8) {
         f32x4 Sk[G8];
@@ -562,20 +616,18 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
         for (int u = 0; u < G8; ++u) {
             // the boundary state of chunk 0 is only stored for a given
             // initial state (the chunk output reads zeros otherwise)
-            if (k0 + u < nc && (k0 + u > 0 || init)) store_state4(dst + (k0 + u) * cstride * 4, H);
+            if (live && k0 + u < nc && (k0 + u > 0 || init))
+                store_state4(dst + (k0 + u) * cstride * 4, H);
             if (k0 + u < ns) H = exp2_fast(Lk[u]) * H + Sk[u];
-            if (so && k0 + u < nc) {
-                float *o = so + (k0 + u) * h * (int64_t)n * p;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e * p] = H[e];
-            }
+            // the state after chunk k0 + u, [b, nc, h, n, p]
+            if (ROWS && states && k0 + u < nc)
+                store_state_rows(lds, H, st, live,
+                                 states + ((b * nc + k0 + u) * h + hh) * (int64_t)n * p, row0,
+                                 col0, p);
         }
     }
-    if (final_state) {
-        float *o = final_state + pair * (int64_t)n * p + n0 * p + pc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e * p] = H[e];
-    }
+    if (ROWS && final_state)
+        store_state_rows(lds, H, st, live, final_state + pair * (int64_t)n * p, row0, col0, p);
 }
 
 // ----------------------------------------------------------------------------
@@ -1362,9 +1414,14 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     const bool copy = sizeof(IO) == 2 && (!grouped || chunk_out_copy(h, g, P, N));
     ia.pieces = copy ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
     trace_begin(2, s);
-    hipLaunchKernelGGL((k_state_scan<OP, IO, N>), dim3((unsigned)scan_blocks), dim3(kThreads), 0, s,
-                       St, Lam, a.init, Hb, a.final_state, pl.b * pl.h, h, pl.nc, N, P, ia,
-                       a.states);
+    if (keep_last)
+        hipLaunchKernelGGL((k_state_scan<OP, IO, N, true>), dim3((unsigned)scan_blocks),
+                           dim3(kThreads), 0, s, St, Lam, a.init, Hb, a.final_state,
+                           pl.b * pl.h, h, pl.nc, N, P, ia, a.states);
+    else
+        hipLaunchKernelGGL((k_state_scan<OP, IO, N, false>), dim3((unsigned)scan_blocks),
+                           dim3(kThreads), 0, s, St, Lam, a.init, Hb, nullptr, pl.b * pl.h, h,
+                           pl.nc, N, P, ia, nullptr);
     trace_end(2, s);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

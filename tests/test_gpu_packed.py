@@ -126,3 +126,38 @@ def test_packed_staging_paths_agree(orc, case, monkeypatch):
     torch = torch_mod()
     assert torch.equal(out["0"][0], out["1"][0])
     assert torch.equal(out["0"][1], out["1"][1])
+
+
+# (chunk, seqlen, head_dim, state_dim): chunks shorter than one 32-row block
+# are computed as whole multiples of themselves, and the states at the
+# caller's boundaries are stepped token by token from the computed chunks'
+# boundary states
+SHORT = [(1, 70, 16, 64), (3, 100, 32, 128), (7, 70, 128, 32), (16, 64, 64, 128),
+         (31, 200, 64, 64)]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("Qs,l,p,n", SHORT, ids=lambda c: str(c))
+def test_short_chunk_states(orc, io, Qs, l, p, n):
+    inp = syn.random_case(3500 + Qs + l + p + n, 2, l, 4, p, n, 2, io=io, init_std=0.3)
+    seq = _seq(2, l, [(5, l // 2, l // 2 + 1), ()])
+    y, fin, st = _run(inp, Qs, seq=seq, states=True)
+    assert st.shape[1] == -(-l // Qs)
+    # the last state is stepped token by token, the final state comes from
+    # the chunked pass: equal up to rounding, each checked against the oracle
+    yo, fo, so = orc.scan(**oracle_kw(inp), seq_idx=seq, states_chunk=Qs)
+    check_close(to_f64(y), yo, io, "y", Y_AXES)
+    check_close(to_f64(fin), fo, io, "final_state", STATE_AXES)
+    check_close(to_f64(st), so, io, "chunk states", (1, 3, 4))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_short_chunk_output_independent_of_states_request(io):
+    """y and the final state are the same bits whether or not the states
+    after every (short) chunk are asked for."""
+    inp = syn.random_case(3600, 2, 90, 4, 64, 64, 2, io=io, init_std=0.2)
+    y0, f0 = _run(inp, 5)
+    y1, f1, _ = _run(inp, 5, states=True)
+    torch = torch_mod()
+    assert torch.equal(y0, y1)
+    assert torch.equal(f0, f1)
