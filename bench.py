@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-states", action="store_true",
                     help="skip the packed-sequence and state-output measurements")
+    ap.add_argument("--no-neighbors", action="store_true",
+                    help="skip the conv1d and gated-norm measurements")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0, help="oracle sample size (0: all)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -266,6 +268,10 @@ def main():
     if not args.no_states:
         states = bench_states(args, torch, ssd, np, sets, ws, w, dev)
 
+    neighbors = None
+    if not args.no_neighbors:
+        neighbors = bench_neighbors(args, torch, ssd, syn, np, dev)
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(args, torch, ssd, syn, dev)
@@ -286,6 +292,7 @@ def main():
         "roofline": roofline,
         "scan_roofline": scan_roof,
         "states": states,
+        "neighbors": neighbors,
         "decode": decode,
         "cpu_baseline": cpu,
     }
@@ -407,6 +414,65 @@ def bench_states(args, torch, ssd, np, sets, ws, w, dev):
                  "state_bytes_written": wbytes,
                  "state_write_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1)}
     return {"packed": packed, "chunk_states": chunks, "per_token": per_token}
+
+
+def bench_neighbors(args, torch, ssd, syn, np, dev):
+    """The steps around the scan at the 130m mixer's shape (8 x 2048 tokens,
+    24 heads of 64, state 128, 1 group, bf16): the width-4 causal conv1d +
+    SiLU + split of the 1792 projection channels, and the silu(z) gate with
+    one RMS norm over the 1536 channels.  Each is one pass over HBM; its
+    rate is priced on those bytes."""
+    b, l, h, p, n, g, K = 8, 2048, 24, 64, 128, 1, 4
+    ch = h * p + 2 * g * n
+    steps = max(args.steps // 2, 10)
+    sets = []
+    for k in range(2):
+        c = syn.conv_case(900 + k, b, l, h, p, n, g, K, io="bf16", with_init=False)
+        nc = syn.norm_case(950 + k, b * l, h * p, io="bf16")
+
+        def t16(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        sets.append(dict(xbc=t16(c["xbc"]), w=torch.from_numpy(c["weight"]).to(dev),
+                         bias=torch.from_numpy(c["bias"]).to(dev), y=t16(nc["y"]), z=t16(nc["z"]),
+                         nw=torch.from_numpy(nc["weight"]).to(dev),
+                         out=(torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev),
+                              torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev),
+                              torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev)),
+                         nout=torch.empty((b * l, h * p), dtype=torch.bfloat16, device=dev)))
+
+    def conv(i):
+        S = sets[i % 2]
+        ssd.conv1d_silu(S["xbc"], S["w"], h, p, n, g, bias=S["bias"], out=S["out"])
+
+    def norm(i):
+        S = sets[i % 2]
+        ssd.gated_norm(S["y"], S["z"], S["nw"], eps=1e-5, out=S["nout"])
+
+    res = {}
+    for name, fn, tid, alg in (
+            ("conv1d_silu", conv, "conv1d", 2 * b * l * ch * 2 + ch * (K + 1) * 4),
+            ("gated_norm", norm, "gated_norm", 3 * b * l * h * p * 2 + h * p * 4)):
+        for i in range(5):
+            fn(i)
+        torch.cuda.synchronize()
+        ssd.trace_enable(True)
+        ssd.trace_read(tid)
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        ssd.trace_enable(False)
+        tot, cnt = ssd.trace_read(tid)
+        us = 1e3 * tot / cnt
+        gbs = alg / (us * 1e-6) / 1e9
+        log("%s: %.2f us, %.0f GB/s" % (name, us, gbs))
+        res[name] = {"avg_launch_us": round(us, 2), "alg_bytes_per_launch": alg,
+                     "tokens_per_s": round(b * l / (us * 1e-6), 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    res["config"] = {"workload": "mamba2_130m mixer", "batch": b, "seqlen": l, "heads": h,
+                     "head_dim": p, "state_dim": n, "groups": g, "conv_width": K,
+                     "norm_groups": 1, "io": "bf16"}
+    return res
 
 
 def bench_decode(args, torch, ssd, syn, dev):

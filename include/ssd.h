@@ -190,6 +190,64 @@ int32_t ssd_step(float *state, const void *x, const void *dt, const float *A,
                  int64_t heads, int64_t head_dim, int64_t state_dim, int64_t groups,
                  int32_t io_dtype, void *hip_stream);
 
+/*
+ * ssd_conv1d_silu -- the short causal convolution in front of the scan, in
+ * one pass (the transformers issue page on a Mamba-2 layer's two paths: the
+ * causal conv1d, then the chunk scan).  The packed projection channels
+ * x | B | C go through a depthwise causal convolution over time, a bias and
+ * SiLU, and are written straight into the scan's inputs:
+ *
+ *   pre[t, c] = bias[c] + sum_{k < width} weight[c, k] * in[t - (width-1) + k, c]
+ *   x, B, C   = split(silu(pre))  (silu(v) = v / (1 + exp(-v)); or pre as is
+ *                                  with apply_silu = 0)
+ *
+ *   xbc         [batch, seqlen, ch] io dtype, ch = heads*head_dim +
+ *               2*groups*state_dim, channels ordered x (head-major), B, C
+ *               (group-major); 16-byte aligned
+ *   weight      [ch, width] fp32 (tap width-1 multiplies the current token);
+ *               4-byte aligned.  bias [ch] fp32 or NULL; 16-byte aligned
+ *   conv_init   [batch, width-1, ch] fp32 inputs before token 0 (oldest
+ *               first), or NULL (zeros); 16-byte aligned
+ *   seq_idx     [batch, seqlen] int32 document index or NULL: a tap whose
+ *               source token lies in another document than the output token
+ *               reads zero (conv_init belongs to the first document)
+ *   x, B, C     outputs [b,l,h,p], [b,l,g,n], [b,l,g,n] io dtype (bf16
+ *               rounded to nearest even); 16-byte aligned
+ *   conv_final  output [batch, width-1, ch] fp32 or NULL: the last width-1
+ *               inputs (rows of earlier documents zero), the conv_init of a
+ *               continuation
+ *   width       1..4; head_dim and state_dim multiples of 4
+ *
+ * fp32 arithmetic.  Errors as for ssd_chunk_scan; SSD_ERR_UNSUPPORTED also
+ * for width > 4, more than 65535 batch rows or 2^19 tokens.
+ */
+int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
+                        const float *conv_init, const int32_t *seq_idx, void *x, void *B,
+                        void *C, float *conv_final, int64_t batch, int64_t seqlen,
+                        int64_t heads, int64_t head_dim, int64_t state_dim, int64_t groups,
+                        int64_t width, int32_t apply_silu, int32_t io_dtype, void *hip_stream);
+
+/*
+ * ssd_gated_norm -- the steps after the scan, in one pass (nnterp guide: the
+ * heads' y is read before the gated norm and the output projection; with
+ * Falcon-H1's RMS norm off, y is gated by silu(z)):
+ *
+ *   v   = y * silu(z)                       (v = y when z is NULL)
+ *   out = v / sqrt(mean_group(v^2) + eps) * weight   (normalize != 0;
+ *                                            out = v otherwise)
+ *
+ *   y, z, out   [rows, dim] io dtype (y of [b, l, h, p] is rows = b*l,
+ *               dim = h*p); 16-byte aligned; out may equal y
+ *   weight      [dim] fp32 or NULL (ones); 16-byte aligned
+ *   group_size  channels per norm group (dim % group_size == 0, a multiple
+ *               of 4); eps >= 0
+ *
+ * fp32 arithmetic, bf16 output rounded to nearest even.
+ */
+int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *out,
+                       int64_t rows, int64_t dim, int64_t group_size, float eps,
+                       int32_t normalize, int32_t io_dtype, void *hip_stream);
+
 /* Static text for a status code (never NULL). */
 const char *ssd_status_string(int32_t status);
 
@@ -212,7 +270,9 @@ enum ssd_kernel_id {
     SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */
     SSD_K_STEP = 4,        /* decode step */
     SSD_K_TOKEN_STATES = 5, /* states after chunks shorter than 32 tokens, token by token */
-    SSD_K_COUNT = 6
+    SSD_K_CONV1D = 6,      /* ssd_conv1d_silu */
+    SSD_K_GATED_NORM = 7,  /* ssd_gated_norm */
+    SSD_K_COUNT = 8
 };
 int32_t ssd_trace_enable(int32_t on);
 int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches);

@@ -22,8 +22,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import LibraryMissing, load, status_string  # noqa: F401
 
-__all__ = ["chunk_scan", "step", "workspace_bytes", "abi_version", "trace_enable",
-           "trace_read", "LibraryMissing", "SsdError"]
+__all__ = ["chunk_scan", "step", "conv1d_silu", "gated_norm", "workspace_bytes", "abi_version",
+           "trace_enable", "trace_read", "LibraryMissing", "SsdError"]
 
 
 class SsdError(RuntimeError):
@@ -171,6 +171,80 @@ def step(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softplus: bool = True,
     if rc != 0:
         raise SsdError("ssd_step", rc)
     return y
+
+
+def conv1d_silu(xbc, weight, heads, head_dim, state_dim, groups, bias=None, conv_init=None,
+                seq_idx=None, apply_silu: bool = True, return_conv_state: bool = False, out=None):
+    """Causal depthwise conv1d + bias + SiLU over the packed x | B | C
+    channels xbc [b, l, ch], split into the scan's inputs (ssd_conv1d_silu).
+    weight [ch, width] fp32; conv_init [b, width-1, ch] fp32.  Returns
+    (x, B, C), plus the final conv state [b, width-1, ch] when asked for.
+    `out` may pass preallocated (x, B, C)."""
+    torch = _torch()
+    lib = load()
+    if xbc.dim() != 3:
+        raise ValueError("xbc must be [batch, seqlen, channels]")
+    b, l, ch = xbc.shape
+    dev = xbc.device
+    if dev.type != "cuda":
+        raise ValueError("xbc must be a GPU tensor")
+    io = xbc.dtype
+    h, p, n, g = int(heads), int(head_dim), int(state_dim), int(groups)
+    if ch != h * p + 2 * g * n:
+        raise ValueError("xbc has %d channels, expected heads*head_dim + 2*groups*state_dim = %d"
+                         % (ch, h * p + 2 * g * n))
+    K = int(weight.shape[1]) if weight.dim() == 2 else -1
+    _check("xbc", xbc, io)
+    _check("weight", weight, torch.float32, (ch, K), dev)
+    _check("bias", bias, torch.float32, (ch,), dev)
+    _check("conv_init", conv_init, torch.float32, (b, K - 1, ch), dev)
+    _check("seq_idx", seq_idx, torch.int32, (b, l), dev)
+    if out is None:
+        x = torch.empty((b, l, h, p), dtype=io, device=dev)
+        B = torch.empty((b, l, g, n), dtype=io, device=dev)
+        C = torch.empty((b, l, g, n), dtype=io, device=dev)
+    else:
+        x, B, C = out
+    _check("x", x, io, (b, l, h, p), dev)
+    _check("B", B, io, (b, l, g, n), dev)
+    _check("C", C, io, (b, l, g, n), dev)
+    fin = None
+    if return_conv_state:
+        fin = torch.empty((b, K - 1, ch), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_conv1d_silu(_ptr(xbc), _ptr(weight), _ptr(bias), _ptr(conv_init), _ptr(seq_idx),
+                             _ptr(x), _ptr(B), _ptr(C), _ptr(fin), b, l, h, p, n, g, K,
+                             int(bool(apply_silu)), _io_code(io), stream)
+    if rc != 0:
+        raise SsdError("ssd_conv1d_silu", rc)
+    return (x, B, C, fin) if return_conv_state else (x, B, C)
+
+
+def gated_norm(y, z=None, weight=None, group_size: Optional[int] = None, eps: float = 1e-5,
+               normalize: bool = True, out=None):
+    """y * silu(z), then an RMS norm over groups of `group_size` channels of
+    the last axis times `weight` (ssd_gated_norm).  y [..., dim] in the io
+    dtype; z like y or None; weight [dim] fp32 or None.  `out` may be y."""
+    torch = _torch()
+    lib = load()
+    dev = y.device
+    if dev.type != "cuda":
+        raise ValueError("y must be a GPU tensor")
+    io = y.dtype
+    dim = int(y.shape[-1])
+    rows = y.numel() // dim if dim else 0
+    G = dim if group_size is None else int(group_size)
+    _check("y", y, io)
+    _check("z", z, io, tuple(y.shape), dev)
+    _check("weight", weight, torch.float32, (dim,), dev)
+    o = torch.empty_like(y) if out is None else out
+    _check("out", o, io, tuple(y.shape), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_gated_norm(_ptr(y), _ptr(z), _ptr(weight), _ptr(o), rows, dim, G, float(eps),
+                            int(bool(normalize)), _io_code(io), stream)
+    if rc != 0:
+        raise SsdError("ssd_gated_norm", rc)
+    return o
 
 
 def trace_enable(on: bool = True) -> None:

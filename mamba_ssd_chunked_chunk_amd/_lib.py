@@ -18,11 +18,12 @@ SSD_ERR_ALIGN = -5
 SSD_ERR_HIP = -6
 
 KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step": 4,
-           "token_states": 5}
+           "token_states": 5, "conv1d": 6, "gated_norm": 7}
 
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",
-           "ssd_status_string", "ssd_abi_version", "ssd_trace_enable", "ssd_trace_read")
+           "ssd_conv1d_silu", "ssd_gated_norm", "ssd_status_string", "ssd_abi_version",
+           "ssd_trace_enable", "ssd_trace_read")
 
 _lib = None
 
@@ -55,6 +56,11 @@ def load() -> ctypes.CDLL:
     lib.ssd_step.restype = I32
     lib.ssd_step.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, P,
                              I64, I64, I64, I64, I64, I32, P]
+    lib.ssd_conv1d_silu.restype = I32
+    lib.ssd_conv1d_silu.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64,
+                                    I64, I32, I32, P]
+    lib.ssd_gated_norm.restype = I32
+    lib.ssd_gated_norm.argtypes = [P, P, P, P, I64, I64, I64, F, I32, I32, P]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [I32]
     lib.ssd_abi_version.restype = I32

@@ -27,15 +27,6 @@ namespace ssd {
 
 namespace {
 
-template <typename IO> __device__ __forceinline__ f32x4 load4(const IO *p);
-template <> __device__ __forceinline__ f32x4 load4<float>(const float *p) {
-    return *reinterpret_cast<const f32x4 *>(p);
-}
-template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
-    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-
 constexpr int kFillRows = 4;  // state rows per lane at most (state_dim <= 128)
 
 // One token's inputs for a lane: time step, x columns, B at the lane's rows,
@@ -52,7 +43,7 @@ __device__ __forceinline__ void load_tok(TokIn &v, int64_t t, const IO *dp, cons
                                          const IO *bp, const int32_t *sq, int64_t xs,
                                          int64_t bs, int dts, int r0, int RS, int n) {
     v.dt = to_f32(dp[t * dts]);
-    v.x = load4(xp + t * xs);
+    v.x = ld4(xp + t * xs);
 #pragma unroll
     for (int k = 0; k < kFillRows; ++k) {
         const int row = r0 + k * RS;

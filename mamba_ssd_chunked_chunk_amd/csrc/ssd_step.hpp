@@ -19,24 +19,6 @@
 
 namespace ssd {
 
-template <typename IO> __device__ __forceinline__ f32x4 ld4(const IO *p);
-template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) {
-    return *reinterpret_cast<const f32x4 *>(p);
-}
-template <> __device__ __forceinline__ f32x4 ld4<bf16>(const bf16 *p) {
-    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-}
-template <typename IO> __device__ __forceinline__ void st4(IO *p, f32x4 v);
-template <> __device__ __forceinline__ void st4<float>(float *p, f32x4 v) {
-    *reinterpret_cast<f32x4 *>(p) = v;
-}
-template <> __device__ __forceinline__ void st4<bf16>(bf16 *p, f32x4 v) {
-    bf16x4 o;
-    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
-    *reinterpret_cast<bf16x4 *>(p) = o;
-}
-
 template <typename IO, int P, int N>
 __global__ __launch_bounds__(256) void k_step(
     float *__restrict__ state, const IO *__restrict__ x, const IO *__restrict__ dt,

@@ -175,3 +175,34 @@ def random_case(seed: int, batch: int, seqlen: int, heads: int, head_dim: int,
 def as_f32(a: np.ndarray, io: str) -> np.ndarray:
     """Stored io array -> float32 values (exact widening for bf16)."""
     return bf16_to_f32(a) if io == BF16 else np.asarray(a, np.float32)
+
+
+def conv_case(seed: int, batch: int, seqlen: int, heads: int, head_dim: int, state_dim: int,
+              groups: int, width: int, io: str = F32, with_init: bool = True):
+    """Inputs of the short convolution before the scan: the projection's
+    x | B | C channels ~ N(0, 1) (stored in io), taps and bias
+    ~ U(-1/sqrt(width), 1/sqrt(width)) (a depthwise filter's fan-in is its
+    width), and width-1 earlier input rows ~ N(0, 1) at io precision, in
+    fp32."""
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    ch = heads * head_dim + 2 * groups * state_dim
+    bound = 1.0 / math.sqrt(width)
+    xbc = _store(_normal(rng, (batch, seqlen, ch)), io)
+    weight = rng.uniform(-bound, bound, (ch, width)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, ch).astype(np.float32)
+    init = None
+    if with_init:
+        init = np.ascontiguousarray(as_f32(_store(_normal(rng, (batch, width - 1, ch)), io), io))
+    return dict(xbc=xbc, weight=weight, bias=bias, conv_init=init, io=io, heads=heads,
+                head_dim=head_dim, state_dim=state_dim, groups=groups)
+
+
+def norm_case(seed: int, rows: int, dim: int, io: str = F32):
+    """Inputs of the gate and norm after the scan: y, z ~ N(0, 1) (stored in
+    io) and a per-channel weight 1 + N(0, 0.1^2)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 8]))
+    y = _store(_normal(rng, (rows, dim)), io)
+    z = _store(_normal(rng, (rows, dim)), io)
+    weight = (1.0 + 0.1 * rng.standard_normal(dim)).astype(np.float32)
+    return dict(y=y, z=z, weight=weight, io=io)
+
