@@ -248,6 +248,57 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
                        int64_t rows, int64_t dim, int64_t group_size, float eps,
                        int32_t normalize, int32_t io_dtype, void *hip_stream);
 
+/*
+ * ssd_chunk_scan_bwd -- gradients of ssd_chunk_scan_ex's y and final state,
+ * deterministic (every sum in a fixed order; the same inputs give the same
+ * bits).  The pages note the backward of the reference kernels is not
+ * deterministic (transformers issue page); the gradients here are the exact
+ * derivatives of the forward (nnterp guide, "Mamba-2" page recurrence):
+ *
+ *   adjoint g_t = dL/dh_t = C_t dy_t^T + alpha_{t+1} g_{t+1}  (inside a
+ *   document; g of the last token also gets d_final), alpha_t = exp(A d_t)
+ *   dx_t = D dy_t + d_t g_t^T B_t,   dB_t = sum_heads d_t g_t x_t,
+ *   dC_t = sum_heads h_t dy_t,       da_t = alpha_t <g_t, h_{t-1}>,
+ *   ddt_t = (g_t . B_t x_t^T + A da_t) * [dt_min <= softplus(z) <= dt_max]
+ *           * sigmoid(z)   (z = dt + dt_bias; without softplus the last
+ *           factor is 1),
+ *   dA = sum d da,  d dt_bias = sum ddt,  dD = sum dy . x,  d init = alpha_0 g_0.
+ *
+ *   forward inputs  as for ssd_chunk_scan_ex (init_state, seq_idx optional)
+ *   dy              [batch, seqlen, heads, head_dim] io dtype, required
+ *   d_final         [batch, heads, state_dim, head_dim] fp32 or NULL (zero)
+ *   dx              [b, l, h, p] io dtype          (required)
+ *   ddt             [b, l, h] io dtype              (required)
+ *   dA              [h] fp32                        (required)
+ *   dB, dC          [b, l, g, n] io dtype           (required)
+ *   dD, d_dt_bias   [h] fp32 or NULL (not written)
+ *   d_init          [b, h, n, p] fp32 or NULL (not written)
+ *   workspace       ssd_chunk_scan_bwd_workspace_bytes(...) bytes,
+ *                   256-byte aligned
+ *
+ * Supported: head_dim and state_dim in {32, 64, 128} (the transposed scans
+ * take head_dim as their state size).  batch and seqlen >= 1.  All
+ * arithmetic fp32 (the scans use the fp32 path whatever the io dtype), the
+ * running sums behind ddt, dA, d dt_bias and dD in fp64.  16-byte
+ * alignment for x, B, C, dy, dx, dB, dC and the states.  Several launches:
+ * three fp32 chunk scans (traced as SSD_K_CHUNK_STATE .. SSD_K_CHUNK_OUT)
+ * and the pass's own kernels (SSD_K_BWD_AUX).
+ */
+int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, const float *dt_bias,
+                           int32_t dt_softplus, float dt_min, float dt_max,
+                           const float *init_state, const int32_t *seq_idx, const void *dy,
+                           const float *d_final, void *dx, void *ddt, float *dA, void *dB,
+                           void *dC, float *dD, float *d_dt_bias, float *d_init, int64_t batch,
+                           int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
+                           int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of workspace ssd_chunk_scan_bwd needs (0 for invalid sizes). */
+size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                                          int64_t head_dim, int64_t state_dim, int64_t groups,
+                                          int64_t chunk);
+
 /* Static text for a status code (never NULL). */
 const char *ssd_status_string(int32_t status);
 
@@ -272,7 +323,8 @@ enum ssd_kernel_id {
     SSD_K_TOKEN_STATES = 5, /* states after chunks shorter than 32 tokens, token by token */
     SSD_K_CONV1D = 6,      /* ssd_conv1d_silu */
     SSD_K_GATED_NORM = 7,  /* ssd_gated_norm */
-    SSD_K_COUNT = 8
+    SSD_K_BWD_AUX = 8,     /* ssd_chunk_scan_bwd's own kernels (its scans count as above) */
+    SSD_K_COUNT = 9
 };
 int32_t ssd_trace_enable(int32_t on);
 int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches);

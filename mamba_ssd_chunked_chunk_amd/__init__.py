@@ -22,7 +22,8 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import LibraryMissing, load, status_string  # noqa: F401
 
-__all__ = ["chunk_scan", "step", "conv1d_silu", "gated_norm", "workspace_bytes", "abi_version",
+__all__ = ["chunk_scan", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
+           "workspace_bytes", "abi_version",
            "trace_enable", "trace_read", "LibraryMissing", "SsdError"]
 
 
@@ -138,6 +139,59 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
         return y
     return (y,) + ((fin,) if return_final_state else ()) + \
         ((states,) if return_chunk_states else ())
+
+
+def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, chunk_size: int = 256, dt_bias=None,
+                   initial_state=None, d_final=None, dt_softplus: bool = True,
+                   dt_limit: Tuple[float, float] = (0.0, math.inf), seq_idx=None,
+                   workspace=None):
+    """Gradients of chunk_scan's y (cotangent dy) and final state (d_final)
+    with respect to every input (ssd_chunk_scan_bwd), deterministic.
+    Returns a dict: dx, ddt, dB, dC (io dtype), dA, and dD, d_dt_bias,
+    d_init (fp32) for the inputs that were given."""
+    torch = _torch()
+    lib = load()
+    b, l, h, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = x.dtype
+    _io_code(io)
+    _check("x", x, io)
+    _check("dt", dt, io, (b, l, h), dev)
+    _check("B", B, io, (b, l, g, n), dev)
+    _check("C", C, io, (b, l, g, n), dev)
+    _check("dy", dy, io, (b, l, h, p), dev)
+    _check("A", A, torch.float32, (h,), dev)
+    _check("D", D, torch.float32, (h,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (h,), dev)
+    _check("initial_state", initial_state, torch.float32, (b, h, n, p), dev)
+    _check("d_final", d_final, torch.float32, (b, h, n, p), dev)
+    _check("seq_idx", seq_idx, torch.int32, (b, l), dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt),
+               dA=torch.empty((h,), dtype=torch.float32, device=dev),
+               dB=torch.empty_like(B), dC=torch.empty_like(C))
+    if D is not None:
+        out["dD"] = torch.empty((h,), dtype=torch.float32, device=dev)
+    if dt_bias is not None:
+        out["d_dt_bias"] = torch.empty((h,), dtype=torch.float32, device=dev)
+    if initial_state is not None:
+        out["d_init"] = torch.empty((b, h, n, p), dtype=torch.float32, device=dev)
+    wsb = int(lib.ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, int(chunk_size)))
+    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8,
+                                                             device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_chunk_scan_bwd(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+        int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]), _ptr(initial_state),
+        _ptr(seq_idx), _ptr(dy), _ptr(d_final), _ptr(out["dx"]), _ptr(out["ddt"]),
+        _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
+        _ptr(out.get("d_dt_bias")), _ptr(out.get("d_init")), b, l, h, p, n, g,
+        int(chunk_size), _io_code(io), _ptr(ws), ws.numel() * ws.element_size(), stream)
+    if rc != 0:
+        raise SsdError("ssd_chunk_scan_bwd", rc)
+    return out
 
 
 def step(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softplus: bool = True,

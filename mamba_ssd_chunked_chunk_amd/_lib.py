@@ -18,11 +18,12 @@ SSD_ERR_ALIGN = -5
 SSD_ERR_HIP = -6
 
 KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step": 4,
-           "token_states": 5, "conv1d": 6, "gated_norm": 7}
+           "token_states": 5, "conv1d": 6, "gated_norm": 7, "bwd_aux": 8}
 
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",
-           "ssd_conv1d_silu", "ssd_gated_norm", "ssd_status_string", "ssd_abi_version",
+           "ssd_conv1d_silu", "ssd_gated_norm", "ssd_chunk_scan_bwd",
+           "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version",
            "ssd_trace_enable", "ssd_trace_read")
 
 _lib = None
@@ -61,6 +62,13 @@ def load() -> ctypes.CDLL:
                                     I64, I32, I32, P]
     lib.ssd_gated_norm.restype = I32
     lib.ssd_gated_norm.argtypes = [P, P, P, P, I64, I64, I64, F, I32, I32, P]
+    lib.ssd_chunk_scan_bwd.restype = I32
+    lib.ssd_chunk_scan_bwd.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P, P,
+                                       P, P, P, P, P, P, P, P,
+                                       I64, I64, I64, I64, I64, I64, I64, I32,
+                                       P, ctypes.c_size_t, P]
+    lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [I64] * 7
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [I32]
     lib.ssd_abi_version.restype = I32

@@ -94,6 +94,12 @@ __global__ void k_fill_state(float *__restrict__ dst, const float *__restrict__ 
     if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// The fp32 scan on any compiled shape (the gradient pass runs its scans
+// through this).
+hipError_t scan_f32(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
+    return dispatch_scan<float>(pl, a, s);
+}
+
 static bool supported_dims(int64_t p, int64_t n) {
     return (p == 16 || p == 32 || p == 64 || p == 128) && (n == 32 || n == 64 || n == 128);
 }

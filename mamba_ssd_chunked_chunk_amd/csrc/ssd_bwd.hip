@@ -1,0 +1,455 @@
+// Gradient pass of the chunked scan, deterministic (every sum in a fixed
+// order, no atomics).
+//
+// The forward is the per-head recurrence of the nnterp guide's "Mamba-2"
+// page: h_t = alpha_t h_{t-1} + d_t B_t x_t^T, y_t = C_t^T h_t + D x_t, with
+// alpha_t = exp(A d_t).  Its adjoint state g_t = dL/dh_t obeys the same
+// kind of recurrence backwards in time,
+//     g_t = alpha_{t+1} g_{t+1} + C_t dy_t^T,
+// so the gradients come from three runs of the fp32 chunked scan on
+// rearranged operands (t' = l - 1 - t reverses time):
+//   1. the adjoint:  state g (n x p), inputs C (as B) and dy (as x), weight
+//      1, decay alpha_{t+1}, reversed; its read-out with B gives
+//      yb_t = g_t^T B_t, hence dx_t = D dy_t + d_t yb_t, and its final state
+//      g_0 gives d init = alpha_0 g_0;
+//   2. the forward transposed:  state h^T (p x n), inputs x (as B, one group
+//      per head) and B (as x), the forward's own time steps; its read-out
+//      with dy gives h_t dy_t, every head's part of dC_t; its final state is
+//      h_l^T;
+//   3. the adjoint transposed:  state g^T, inputs dy (as B) and C (as x),
+//      reversed; its read-out with x gives g_t x_t, every head's part of
+//      dB_t / d_t.
+// The log-decay gradient da_t = alpha_t <g_t, h_{t-1}> needs no state: with
+// u_t = dy_t . (C_t^T h_t) and v_t = d_t yb_t . x_t, the identity
+// <g_t, h_t> = u_t + <g_{t+1}, h_{t+1}> - v_{t+1} (inside a document) makes
+// da_t a reverse running sum of u - v (plus <d_final, h_l> in the last
+// document), taken per (batch, head) in fp64.  Then dd_t = yb_t . x_t +
+// A da_t, ddt through the clamp and softplus, dA = sum d da, and the sums
+// over the group's heads and over the batch in fixed order.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "../../include/ssd.h"
+#include "ssd_device.hpp"
+#include "ssd_plan.hpp"
+
+namespace ssd {
+
+namespace {
+
+// fp32 workspace of the gradient pass (offsets in bytes)
+struct BwdPlan {
+    ScanPlan s1, s2;  // the adjoint scan (p, n, g); the transposed scans (n, p, h groups)
+    size_t dyR, xR, xF, dyF, CR, BR, Bh, CRh, dtF, lw, la, seqR, y1, y2, y3, sc, part, term,
+        fin1, finT, initT, dfT, ws, total;
+};
+
+bool make_bwd_plan(BwdPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, int64_t n,
+                   int64_t g, int64_t Q) {
+    if (!make_plan(P.s1, b, l, h, p, n, g, Q, 0)) return false;
+    if (!make_plan(P.s2, b, l, h, n, p, h, Q, 0)) return false;
+    const int64_t thp = b * l * h * p * 4, tgn = b * l * g * n * 4, thn = b * l * h * n * 4;
+    const int64_t th = b * l * h * 4, st = b * h * n * p * 4;
+    size_t o = 0;
+    auto take = [&](size_t &off, int64_t bytes) { off = o; o += align256(bytes); };
+    take(P.dyR, thp); take(P.xR, thp); take(P.xF, thp); take(P.dyF, thp);
+    take(P.CR, tgn); take(P.BR, tgn); take(P.Bh, thn); take(P.CRh, thn);
+    take(P.dtF, th); take(P.lw, th); take(P.la, th); take(P.seqR, b * l * 4);
+    take(P.y1, thp); take(P.y2, thn); take(P.y3, thn);
+    take(P.sc, th * 4); take(P.part, b * h * 3 * 8); take(P.term, b * h * 8);
+    take(P.fin1, st); take(P.finT, st); take(P.initT, st); take(P.dfT, st);
+    take(P.ws, (int64_t)(P.s1.total > P.s2.total ? P.s1.total : P.s2.total));
+    P.total = o;
+    return true;
+}
+
+struct BwdBufs {
+    float *dyR, *xR, *xF, *dyF, *CR, *BR, *Bh, *CRh, *dtF, *lw, *la, *y1, *y2, *y3, *sc;
+    int32_t *seqR;
+    double *part, *term;
+    float *fin1, *finT, *initT, *dfT;
+};
+
+// The rearranged operands of the three scans, one workgroup per token.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_prep(
+    const IO *__restrict__ x, const IO *__restrict__ dt, const float *__restrict__ A,
+    const IO *__restrict__ Bm, const IO *__restrict__ Cm, const IO *__restrict__ dy,
+    const float *__restrict__ dt_bias, int softplus, float dt_min, float dt_max,
+    const int32_t *__restrict__ seq, BwdBufs w, int64_t l, int h, int g, int p, int n) {
+    const int64_t bt = blockIdx.x, b = bt / l, t = bt % l;
+    const int64_t rt = b * l + (l - 1 - t);  // the reversed token's row
+    const int tid = threadIdx.x;
+    const int hp = h * p, gn = g * n, hn = h * n, hpg = h / g;
+    for (int i = tid; i < hp; i += 256) {
+        const float dv = to_f32(dy[bt * hp + i]), xv = to_f32(x[bt * hp + i]);
+        w.dyR[rt * hp + i] = dv;
+        w.xR[rt * hp + i] = xv;
+        w.dyF[bt * hp + i] = dv;
+        w.xF[bt * hp + i] = xv;
+    }
+    for (int i = tid; i < gn; i += 256) {
+        w.CR[rt * gn + i] = to_f32(Cm[bt * gn + i]);
+        w.BR[rt * gn + i] = to_f32(Bm[bt * gn + i]);
+    }
+    for (int i = tid; i < hn; i += 256) {
+        const int hh = i / n, k = i % n;
+        const int64_t src = bt * gn + (hh / hpg) * n + k;
+        w.Bh[bt * hn + i] = to_f32(Bm[src]);
+        w.CRh[rt * hn + i] = to_f32(Cm[src]);
+    }
+    for (int i = tid; i < h; i += 256) {
+        w.dtF[bt * h + i] = to_f32(dt[bt * h + i]);
+        w.lw[rt * h + i] = 1.f;
+        // the reversed step t' carries the decay of forward token t + 1
+        float la = 0.f;
+        if (t + 1 < l) {
+            const float d1 = time_step(to_f32(dt[(bt + 1) * h + i]), dt_bias ? dt_bias[i] : 0.f,
+                                       softplus, dt_min, dt_max);
+            la = A[i] * d1 * kLog2e;
+        }
+        w.la[rt * h + i] = la;
+    }
+    if (seq && tid == 0) w.seqR[rt] = seq[bt];
+}
+
+// [pairs][n][p] -> [pairs][p][n]
+__global__ void k_transpose_np(const float *__restrict__ src, float *__restrict__ dst,
+                               int64_t pairs, int n, int p) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t np = (int64_t)n * p;
+    if (i >= pairs * np) return;
+    const int64_t pr = i / np, r = i % np, k = r / p, j = r % p;
+    dst[pr * np + j * n + k] = src[i];
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Per token and head (one wave): dx, and the scalars u - v, yb . x,
+// dy . x and d for the running sums.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_tok(
+    const IO *__restrict__ x, const IO *__restrict__ dt, const IO *__restrict__ Cm,
+    const IO *__restrict__ dy, const float *__restrict__ D, const float *__restrict__ dt_bias,
+    int softplus, float dt_min, float dt_max, BwdBufs w, IO *__restrict__ dx, int64_t bl,
+    int64_t l, int h, int g, int p, int n) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= bl * h) return;
+    const int64_t bt = item / h, b = bt / l, t = bt % l;
+    const int hh = (int)(item % h), gi = hh / (h / g);
+    const int64_t rt = b * l + (l - 1 - t);
+    const float d = time_step(to_f32(dt[bt * h + hh]), dt_bias ? dt_bias[hh] : 0.f, softplus,
+                              dt_min, dt_max);
+    const float Dh = D ? D[hh] : 0.f;
+    float wsum = 0.f, dsum = 0.f, usum = 0.f;
+    for (int j = lane; j < p; j += 64) {
+        const int64_t at = (bt * h + hh) * p + j;
+        const float yb = w.y1[(rt * h + hh) * p + j];
+        const float xv = to_f32(x[at]), dv = to_f32(dy[at]);
+        wsum += yb * xv;
+        dsum += dv * xv;
+        dx[at] = (IO)(Dh * dv + d * yb);
+    }
+    for (int k = lane; k < n; k += 64)
+        usum += to_f32(Cm[(bt * g + gi) * n + k]) * w.y2[(bt * h + hh) * n + k];
+    wsum = wave_sum_f(wsum);
+    dsum = wave_sum_f(dsum);
+    usum = wave_sum_f(usum);
+    if (lane == 0) {
+        float *o = w.sc + ((b * h + hh) * l + t) * 4;
+        o[0] = usum - d * wsum;
+        o[1] = wsum;
+        o[2] = dsum;
+        o[3] = d;
+    }
+}
+
+// <d_final, h_l> per (batch, head), h_l^T from the transposed forward scan.
+__global__ __launch_bounds__(256) void k_bwd_term(const float *__restrict__ dfin,
+                                                  const float *__restrict__ finT,
+                                                  double *__restrict__ term, int n, int p) {
+    __shared__ double red[256];
+    const int64_t pr = blockIdx.x;
+    const int64_t np = (int64_t)n * p;
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < np; i += 256) {
+        const int64_t k = i / p, j = i % p;
+        s += (double)dfin[pr * np + i] * (double)finT[pr * np + j * n + k];
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) term[pr] = red[0];
+}
+
+// Per (batch, head), one thread, tokens in reverse: the running sum of
+// u - v gives da_t; then ddt and the (batch, head) parts of dA, d dt_bias
+// and dD, all in fp64.
+template <typename IO>
+__global__ __launch_bounds__(64) void k_bwd_cum(
+    const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
+    int softplus, float dt_min, float dt_max, const int32_t *__restrict__ seq, int has_init,
+    BwdBufs w, IO *__restrict__ ddt, int64_t b_, int64_t l, int h) {
+    const int64_t pr = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (pr >= b_ * h) return;
+    const int64_t b = pr / h;
+    const int hh = (int)(pr % h);
+    const float Ah = A[hh], bias = dt_bias ? dt_bias[hh] : 0.f;
+    const float *sc = w.sc + pr * l * 4;
+    const int32_t *sq = seq ? seq + b * l : nullptr;
+    double acc = w.term ? w.term[pr] : 0.0;
+    double sA = 0.0, sB = 0.0, sD = 0.0;
+    for (int64_t t = l - 1; t >= 0; --t) {
+        // a document ending at t starts the sum afresh (the final-state
+        // term belongs to the last document only)
+        if (sq && t + 1 < l && sq[t + 1] != sq[t]) acc = 0.0;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(sc + t * 4);
+        acc += (double)v[0];
+        double da = acc;
+        // no state before a document's first token (or before token 0
+        // without an initial state): no decay acts there
+        if ((sq && t > 0 && sq[t] != sq[t - 1]) || (t == 0 && !has_init)) da = 0.0;
+        const double dd = (double)v[1] + (double)Ah * da;
+        const float z = to_f32(dt[(b * l + t) * h + hh]) + bias;
+        const float spv = softplus ? (z > 20.f ? z : log1pf(expf(z))) : z;
+        const bool pass = spv >= dt_min && spv <= dt_max;
+        const double dsp = softplus ? 1.0 / (1.0 + exp(-(double)z)) : 1.0;
+        const double g = pass ? dd * dsp : 0.0;
+        ddt[(b * l + t) * h + hh] = (IO)(float)g;
+        sA += (double)v[3] * da;
+        sB += g;
+        sD += (double)v[2];
+    }
+    w.part[pr * 3 + 0] = sA;
+    w.part[pr * 3 + 1] = sB;
+    w.part[pr * 3 + 2] = sD;
+}
+
+// dB and dC of one token: the group's heads summed in order.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_bwd_group(BwdBufs w, IO *__restrict__ dB,
+                                                   IO *__restrict__ dC, int64_t l, int h, int g,
+                                                   int n) {
+    const int64_t bt = blockIdx.x, b = bt / l, t = bt % l;
+    const int64_t rt = b * l + (l - 1 - t);
+    const int hpg = h / g;
+    for (int i = threadIdx.x; i < g * n; i += 256) {
+        const int gi = i / n, k = i % n;
+        float sb = 0.f, sc = 0.f;
+        for (int q = 0; q < hpg; ++q) {
+            const int hh = gi * hpg + q;
+            const float d = w.sc[((b * h + hh) * l + t) * 4 + 3];
+            sb += d * w.y3[(rt * h + hh) * n + k];
+            sc += w.y2[(bt * h + hh) * n + k];
+        }
+        dB[bt * g * n + i] = (IO)sb;
+        dC[bt * g * n + i] = (IO)sc;
+    }
+}
+
+// dA, d dt_bias, dD: the (batch, head) parts summed over the batch in order.
+__global__ void k_bwd_sum(const double *__restrict__ part, float *__restrict__ dA,
+                          float *__restrict__ dbias, float *__restrict__ dD, int64_t b_, int h) {
+    const int hh = blockIdx.x * blockDim.x + threadIdx.x;
+    if (hh >= h) return;
+    double a = 0.0, bi = 0.0, d = 0.0;
+    for (int64_t b = 0; b < b_; ++b) {
+        a += part[(b * h + hh) * 3 + 0];
+        bi += part[(b * h + hh) * 3 + 1];
+        d += part[(b * h + hh) * 3 + 2];
+    }
+    dA[hh] = (float)a;
+    if (dbias) dbias[hh] = (float)bi;
+    if (dD) dD[hh] = (float)d;
+}
+
+// d init = alpha_0 g_0.
+__global__ void k_bwd_init(const float *__restrict__ fin1, const float *__restrict__ sc,
+                           const float *__restrict__ A, float *__restrict__ dinit, int64_t pairs,
+                           int h, int64_t l, int64_t np) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= pairs * np) return;
+    const int64_t pr = i / np;
+    const float d0 = sc[pr * l * 4 + 3];
+    dinit[i] = expf(A[pr % h] * d0) * fin1[i];
+}
+
+bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
+
+}  // namespace
+
+}  // namespace ssd
+
+using namespace ssd;
+
+extern "C" {
+
+size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
+                                          int64_t head_dim, int64_t state_dim, int64_t groups,
+                                          int64_t chunk) {
+    BwdPlan P;
+    if (!make_bwd_plan(P, batch, seqlen, heads, head_dim, state_dim, groups, chunk)) return 0;
+    return P.total;
+}
+
+int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const void *B,
+                           const void *C, const float *D, const float *dt_bias,
+                           int32_t dt_softplus, float dt_min, float dt_max,
+                           const float *init_state, const int32_t *seq_idx, const void *dy,
+                           const float *d_final, void *dx, void *ddt, float *dA, void *dB,
+                           void *dC, float *dD, float *d_dt_bias, float *d_init, int64_t batch,
+                           int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
+                           int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
+                           size_t workspace_bytes, void *hip_stream) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (batch <= 0 || seqlen <= 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
+        groups <= 0 || chunk <= 0 || heads % groups != 0)
+        return SSD_ERR_SHAPE;
+    // the transposed scans take head_dim as their state size
+    const bool dims = (head_dim == 32 || head_dim == 64 || head_dim == 128) &&
+                      (state_dim == 32 || state_dim == 64 || state_dim == 128);
+    if (!dims) return SSD_ERR_UNSUPPORTED;
+    const int64_t lim32 = (int64_t)1 << 31;
+    if (batch * seqlen > lim32 / 2 || 64 * heads * 128 * 4 >= lim32 ||
+        batch * seqlen * heads * 128 >= ((int64_t)1 << 40))
+        return SSD_ERR_UNSUPPORTED;
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC)
+        return SSD_ERR_NULL;
+    if (!al16(x) || !al16(B) || !al16(C) || !al16(dy) || !al16(dx) || !al16(dB) || !al16(dC) ||
+        !al16(init_state) || !al16(d_final) || !al16(d_init) || !al16(workspace))
+        return SSD_ERR_ALIGN;
+    BwdPlan P;
+    if (!make_bwd_plan(P, batch, seqlen, heads, head_dim, state_dim, groups, chunk))
+        return SSD_ERR_SHAPE;
+    if (P.s1.lp * 4 >= lim32 || P.s2.lp * 4 >= lim32) return SSD_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < P.total) return SSD_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    char *ws = static_cast<char *>(workspace);
+    BwdBufs w;
+    w.dyR = reinterpret_cast<float *>(ws + P.dyR);
+    w.xR = reinterpret_cast<float *>(ws + P.xR);
+    w.xF = reinterpret_cast<float *>(ws + P.xF);
+    w.dyF = reinterpret_cast<float *>(ws + P.dyF);
+    w.CR = reinterpret_cast<float *>(ws + P.CR);
+    w.BR = reinterpret_cast<float *>(ws + P.BR);
+    w.Bh = reinterpret_cast<float *>(ws + P.Bh);
+    w.CRh = reinterpret_cast<float *>(ws + P.CRh);
+    w.dtF = reinterpret_cast<float *>(ws + P.dtF);
+    w.lw = reinterpret_cast<float *>(ws + P.lw);
+    w.la = reinterpret_cast<float *>(ws + P.la);
+    w.seqR = reinterpret_cast<int32_t *>(ws + P.seqR);
+    w.y1 = reinterpret_cast<float *>(ws + P.y1);
+    w.y2 = reinterpret_cast<float *>(ws + P.y2);
+    w.y3 = reinterpret_cast<float *>(ws + P.y3);
+    w.sc = reinterpret_cast<float *>(ws + P.sc);
+    w.part = reinterpret_cast<double *>(ws + P.part);
+    w.term = d_final ? reinterpret_cast<double *>(ws + P.term) : nullptr;
+    w.fin1 = reinterpret_cast<float *>(ws + P.fin1);
+    w.finT = reinterpret_cast<float *>(ws + P.finT);
+    w.initT = reinterpret_cast<float *>(ws + P.initT);
+    w.dfT = reinterpret_cast<float *>(ws + P.dfT);
+    char *scan_ws = ws + P.ws;
+
+    const int64_t b = batch, l = seqlen, h = heads, p = head_dim, n = state_dim, g = groups;
+    const int64_t bl = b * l, pairs = b * h, np = n * p;
+    const unsigned eblk = (unsigned)((pairs * np + 255) / 256);
+    const float inf = INFINITY;
+    hipError_t e = hipSuccess;
+    auto ok = [&]() { return (e = hipGetLastError()) == hipSuccess; };
+
+    trace_begin(SSD_K_BWD_AUX, s);
+    if (io_dtype == SSD_BF16)
+        hipLaunchKernelGGL((k_bwd_prep<bf16>), dim3((unsigned)bl), dim3(256), 0, s,
+                           static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt), A,
+                           static_cast<const bf16 *>(B), static_cast<const bf16 *>(C),
+                           static_cast<const bf16 *>(dy), dt_bias, dt_softplus ? 1 : 0, dt_min,
+                           dt_max, seq_idx, w, l, (int)h, (int)g, (int)p, (int)n);
+    else
+        hipLaunchKernelGGL((k_bwd_prep<float>), dim3((unsigned)bl), dim3(256), 0, s,
+                           static_cast<const float *>(x), static_cast<const float *>(dt), A,
+                           static_cast<const float *>(B), static_cast<const float *>(C),
+                           static_cast<const float *>(dy), dt_bias, dt_softplus ? 1 : 0, dt_min,
+                           dt_max, seq_idx, w, l, (int)h, (int)g, (int)p, (int)n);
+    if (init_state)
+        hipLaunchKernelGGL(k_transpose_np, dim3(eblk), dim3(256), 0, s, init_state, w.initT,
+                           pairs, (int)n, (int)p);
+    if (d_final)
+        hipLaunchKernelGGL(k_transpose_np, dim3(eblk), dim3(256), 0, s, d_final, w.dfT, pairs,
+                           (int)n, (int)p);
+    trace_end(SSD_K_BWD_AUX, s);
+    if (!ok()) return SSD_ERR_HIP;
+
+    // 1. the adjoint, reversed: read-out yb_t = g_t^T B_t, final state g_0
+    ScanArgs a1{w.dyR, w.dtF, w.CR, w.BR, A, nullptr, nullptr, 0, 0.f, inf,
+                d_final, w.y1, w.fin1, scan_ws, seq_idx ? w.seqR : nullptr, nullptr};
+    a1.lw = w.lw;
+    a1.la = w.la;
+    if ((e = scan_f32(P.s1, a1, s)) != hipSuccess) return SSD_ERR_HIP;
+    // 2. the forward transposed: read-out h_t dy_t, final state h_l^T
+    ScanArgs a2{w.Bh, w.dtF, w.xF, w.dyF, A, nullptr, dt_bias, dt_softplus ? 1 : 0, dt_min,
+                dt_max, init_state ? w.initT : nullptr, w.y2, d_final ? w.finT : nullptr,
+                scan_ws, seq_idx, nullptr};
+    if ((e = scan_f32(P.s2, a2, s)) != hipSuccess) return SSD_ERR_HIP;
+    // 3. the adjoint transposed, reversed: read-out g_t x_t
+    ScanArgs a3{w.CRh, w.dtF, w.dyR, w.xR, A, nullptr, nullptr, 0, 0.f, inf,
+                d_final ? w.dfT : nullptr, w.y3, nullptr, scan_ws,
+                seq_idx ? w.seqR : nullptr, nullptr};
+    a3.lw = w.lw;
+    a3.la = w.la;
+    if ((e = scan_f32(P.s2, a3, s)) != hipSuccess) return SSD_ERR_HIP;
+
+    trace_begin(SSD_K_BWD_AUX, s);
+    const unsigned tblk = (unsigned)((bl * h + 3) / 4);
+    if (io_dtype == SSD_BF16)
+        hipLaunchKernelGGL((k_bwd_tok<bf16>), dim3(tblk), dim3(256), 0, s,
+                           static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt),
+                           static_cast<const bf16 *>(C), static_cast<const bf16 *>(dy), D,
+                           dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max, w,
+                           static_cast<bf16 *>(dx), bl, l, (int)h, (int)g, (int)p, (int)n);
+    else
+        hipLaunchKernelGGL((k_bwd_tok<float>), dim3(tblk), dim3(256), 0, s,
+                           static_cast<const float *>(x), static_cast<const float *>(dt),
+                           static_cast<const float *>(C), static_cast<const float *>(dy), D,
+                           dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max, w,
+                           static_cast<float *>(dx), bl, l, (int)h, (int)g, (int)p, (int)n);
+    if (d_final)
+        hipLaunchKernelGGL(k_bwd_term, dim3((unsigned)pairs), dim3(256), 0, s, d_final, w.finT,
+                           w.term, (int)n, (int)p);
+    const unsigned cblk = (unsigned)((pairs + 63) / 64);
+    if (io_dtype == SSD_BF16)
+        hipLaunchKernelGGL((k_bwd_cum<bf16>), dim3(cblk), dim3(64), 0, s,
+                           static_cast<const bf16 *>(dt), A, dt_bias, dt_softplus ? 1 : 0,
+                           dt_min, dt_max, seq_idx, init_state ? 1 : 0, w,
+                           static_cast<bf16 *>(ddt), b, l, (int)h);
+    else
+        hipLaunchKernelGGL((k_bwd_cum<float>), dim3(cblk), dim3(64), 0, s,
+                           static_cast<const float *>(dt), A, dt_bias, dt_softplus ? 1 : 0,
+                           dt_min, dt_max, seq_idx, init_state ? 1 : 0, w,
+                           static_cast<float *>(ddt), b, l, (int)h);
+    if (io_dtype == SSD_BF16)
+        hipLaunchKernelGGL((k_bwd_group<bf16>), dim3((unsigned)bl), dim3(256), 0, s, w,
+                           static_cast<bf16 *>(dB), static_cast<bf16 *>(dC), l, (int)h, (int)g,
+                           (int)n);
+    else
+        hipLaunchKernelGGL((k_bwd_group<float>), dim3((unsigned)bl), dim3(256), 0, s, w,
+                           static_cast<float *>(dB), static_cast<float *>(dC), l, (int)h, (int)g,
+                           (int)n);
+    hipLaunchKernelGGL(k_bwd_sum, dim3((unsigned)((h + 63) / 64)), dim3(64), 0, s, w.part, dA,
+                       d_dt_bias, dD, b, (int)h);
+    if (d_init)
+        hipLaunchKernelGGL(k_bwd_init, dim3(eblk), dim3(256), 0, s, w.fin1, w.sc, A, d_init,
+                           pairs, (int)h, l, np);
+    trace_end(SSD_K_BWD_AUX, s);
+    return ok() ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // extern "C"

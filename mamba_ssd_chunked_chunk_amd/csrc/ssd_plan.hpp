@@ -110,6 +110,9 @@ struct ScanArgs {
     char *ws;
     const int32_t *seq;  // [b, l] document index of every token, or NULL
     float *states;       // [b, ns, h, n, p] state after every caller chunk, or NULL
+    // fp32 io only, or NULL: every token's weight and log2 decay [b, l, h],
+    // given in place of the time step (dt, A, dt_bias and the limits unused)
+    const float *lw = nullptr, *la = nullptr;
 };
 
 struct StepArgs {
@@ -132,6 +135,9 @@ void trace_end(int kernel, hipStream_t s);
 // computed ones.
 hipError_t launch_token_states(const ScanPlan &pl, const ScanArgs &a, const float *Hc,
                                hipStream_t s);
+
+// The fp32 scan dispatched over the compiled (head_dim, state_dim) set.
+hipError_t scan_f32(const ScanPlan &pl, const ScanArgs &a, hipStream_t s);
 
 // Launchers, one per (io, head_dim, state_dim) instantiation.
 template <typename IO, int P, int N>

@@ -129,6 +129,10 @@ template <typename IO, int HPW> struct SpPtrs {
     int h;                   // heads (row stride of dt)
     int64_t Qp;              // padded rows per chunk
     const int32_t *seq;      // row 0 of the sequence's document indices (packed sequences)
+    // fp32 io only, or NULL: every row's weight and log2 decay given directly
+    // (row 0 of the sequence, first head of the workgroup; rows h apart) in
+    // place of the time step (the scans of the gradient pass)
+    const float *lw, *la;
 };
 
 template <typename IO, int P, int N, int HPW>
@@ -166,8 +170,8 @@ __device__ __forceinline__ void sp_prefetch(SpBuf<IO, P, N, HPW> &f, int64_t c, 
 // The raw time steps of the span starting at block blk0, one row of one head
 // per thread and pass.
 template <typename IO, int P, int N, int HPW, bool SEQ>
-__device__ __forceinline__ void sp_dt_load(float *dtv, int *rst, int64_t c, int blk0,
-                                           const SpPtrs<IO, HPW> &sp, int tid) {
+__device__ __forceinline__ void sp_dt_load(float *dtv, float *dav, int *rst, int64_t c,
+                                           int blk0, const SpPtrs<IO, HPW> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     constexpr int T = kT;
     const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;
@@ -176,7 +180,12 @@ __device__ __forceinline__ void sp_dt_load(float *dtv, int *rst, int64_t c, int 
         const int idx = ps * K::NT + tid;
         const int hs = idx / K::SPR, r = idx % K::SPR;
         const int64_t row = c * sp.Q + (int64_t)blk0 * T + r;
-        dtv[ps] = row < cend ? to_f32(sp.dt[row * sp.h + hs]) : 0.f;
+        if (sizeof(IO) == 4 && sp.lw) {
+            dtv[ps] = row < cend ? sp.lw[row * sp.h + hs] : 0.f;
+            dav[ps] = row < cend ? sp.la[row * sp.h + hs] : 0.f;
+        } else {
+            dtv[ps] = row < cend ? to_f32(sp.dt[row * sp.h + hs]) : 0.f;
+        }
         // packed sequences: a row whose document index differs from the
         // previous row's starts from a zero state
         if constexpr (SEQ)
@@ -188,9 +197,9 @@ __device__ __forceinline__ void sp_dt_load(float *dtv, int *rst, int64_t c, int 
 // its raw time steps; ends with the span's weights visible to the whole
 // workgroup.
 template <typename IO, int P, int N, int HPW, bool SEQ>
-__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const int *rst,
-                                        int64_t c, int blk0, const SpPtrs<IO, HPW> &sp,
-                                        int tid) {
+__device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const float *dav,
+                                        const int *rst, int64_t c, int blk0,
+                                        const SpPtrs<IO, HPW> &sp, int tid) {
     typedef Sp<IO, P, N, HPW> K;
     constexpr int T = kT;
     const int64_t cend = (c + 1) * sp.Q < sp.l ? (c + 1) * sp.Q : sp.l;
@@ -206,9 +215,14 @@ __device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const
             bias = hs == k ? sp.bias[k] : bias;
             a2 = hs == k ? sp.a2[k] : a2;
         }
-        const float d = row < cend ? time_step(dtv[ps], bias, sp.softplus, sp.dt_min, sp.dt_max)
-                                   : 0.f;
-        float a = a2 * d;
+        float d, a;
+        if (sizeof(IO) == 4 && sp.lw) {
+            d = row < cend ? dtv[ps] : 0.f;
+            a = row < cend ? dav[ps] : 0.f;
+        } else {
+            d = row < cend ? time_step(dtv[ps], bias, sp.softplus, sp.dt_min, sp.dt_max) : 0.f;
+            a = a2 * d;
+        }
         // inclusive scan inside each 32-lane group (one block each)
 #pragma unroll
         for (int off = 1; off < T; off <<= 1) {
@@ -341,7 +355,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
     float *__restrict__ St, float *__restrict__ Lam, int64_t l, int h, int g, int64_t Q,
-    int64_t nc, int64_t Qp, int keep_last, const int32_t *__restrict__ seq) {
+    int64_t nc, int64_t Qp, int keep_last, const int32_t *__restrict__ seq,
+    const float *__restrict__ lw, const float *__restrict__ la) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, SPAN = K::SPAN, TPW = K::TPW;
@@ -368,6 +383,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     sp.B = Bm + (b * l * g + gi) * N;
     sp.dt = dt + b * l * h + hh0;
     sp.seq = SEQ ? seq + b * l : nullptr;
+    sp.lw = lw ? lw + b * l * h + hh0 : nullptr;
+    sp.la = la ? la + b * l * h + hh0 : nullptr;
     sp.lcs = lcs + (b * h + hh0) * nc * Qp;
     sp.dtp = dtp + (b * h + hh0) * nc * Qp;
     sp.wgt = wgt + (b * h + hh0) * nc * Qp;
@@ -392,9 +409,9 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
 
     // the first span's raw time steps are requested before the first blocks,
     // so that its per-row values are ready as soon as possible
-    float dtv[K::NPASS];
+    float dtv[K::NPASS], dav[K::NPASS];
     int rst[K::NPASS];
-    sp_dt_load<IO, P, N, HPW, SEQ>(dtv, rst, c, 0, sp, tid);
+    sp_dt_load<IO, P, N, HPW, SEQ>(dtv, dav, rst, c, 0, sp, tid);
     SpBuf<IO, P, N, HPW> pa, pb;
     sp_prefetch(pa, c, 0, true, sp, tid);
     sp_prefetch(pb, c, 1, nsb > 1, sp, tid);
@@ -405,7 +422,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     // staged; the state decays by the new span's total after the previous
     // span's last block has been applied.
     {
-        sp_span<IO, P, N, HPW, SEQ>(span, dtv, rst, c, 0, sp, tid);
+        sp_span<IO, P, N, HPW, SEQ>(span, dtv, dav, rst, c, 0, sp, tid);
         float L = 0.f;
 #pragma unroll
         for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
@@ -426,8 +443,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
             const bool new_span = nxt < nsb && nxt % SPAN == 0;
             float L = 0.f;
             if (new_span) {
-                sp_dt_load<IO, P, N, HPW, SEQ>(dtv, rst, c, nxt, sp, tid);
-                sp_span<IO, P, N, HPW, SEQ>(span, dtv, rst, c, nxt, sp, tid);
+                sp_dt_load<IO, P, N, HPW, SEQ>(dtv, dav, rst, c, nxt, sp, tid);
+                sp_span<IO, P, N, HPW, SEQ>(span, dtv, dav, rst, c, nxt, sp, tid);
 #pragma unroll
                 for (int j = 0; j < SPAN; ++j) L += span.lam[hs][j];
                 L = __builtin_bit_cast(float,
@@ -1378,7 +1395,8 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, HPn, SQ>),
                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))), dim3(Sp<IO, P, N, HPn>::NT),
                            0, s, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min, a.dt_max, lcs,
-                           dtp, wgt, St, Lam, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq);
+                           dtp, wgt, St, Lam, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq,
+                           a.lw, a.la);
     };
     trace_begin(1, s);
     if (grouped) {

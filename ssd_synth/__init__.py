@@ -206,3 +206,13 @@ def norm_case(seed: int, rows: int, dim: int, io: str = F32):
     weight = (1.0 + 0.1 * rng.standard_normal(dim)).astype(np.float32)
     return dict(y=y, z=z, weight=weight, io=io)
 
+
+
+def cotangent_case(seed: int, batch: int, seqlen: int, heads: int, head_dim: int,
+                   state_dim: int, io: str = F32):
+    """Cotangents for the gradient pass: dy ~ N(0, 1) (stored in io) and
+    d_final ~ N(0, 1) (fp32)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 9]))
+    dy = _store(_normal(rng, (batch, seqlen, heads, head_dim)), io)
+    d_final = _normal(rng, (batch, heads, state_dim, head_dim))
+    return dict(dy=dy, d_final=d_final, io=io)

@@ -55,16 +55,19 @@ def bar(io):
     return (1e-4, 1e-4, 0.0) if io == "f32" else (0.0, 2e-2, 2e-2)
 
 
-def check_close(g, o, io, what, rms_axes=None):
+def check_close(g, o, io, what, rms_axes=None, floor=None):
     """Assert the elementwise bar; return (max_abs, max_rel, normwise).
 
     rms_axes: the axes that do NOT index a (batch, head) pair, i.e. the rms
-    floor is taken over them (None: over the whole tensor)."""
+    floor is taken over them (None: over the whole tensor).  floor: the rms
+    floor's factor instead of the io type's."""
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
     assert g.shape == o.shape, (what, g.shape, o.shape)
     assert np.isfinite(g).all(), "%s: non-finite values" % what
     atol, rtol, rmsf = bar(io)
+    if floor is not None:
+        rmsf = floor
     if o.size == 0:
         return (0.0, 0.0, 0.0)
     rms = np.sqrt(np.mean(o * o, axis=rms_axes, keepdims=rms_axes is not None))
