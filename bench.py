@@ -145,6 +145,8 @@ def main():
                     help="skip the packed-sequence and state-output measurements")
     ap.add_argument("--no-neighbors", action="store_true",
                     help="skip the conv1d and gated-norm measurements")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the gradient-pass measurement")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0, help="oracle sample size (0: all)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -272,6 +274,10 @@ def main():
     if not args.no_neighbors:
         neighbors = bench_neighbors(args, torch, ssd, syn, np, dev)
 
+    backward = None
+    if not args.no_backward:
+        backward = bench_backward(args, torch, ssd, np, sets, w, dev)
+
     decode = None
     if not args.no_decode:
         decode = bench_decode(args, torch, ssd, syn, dev)
@@ -293,6 +299,7 @@ def main():
         "scan_roofline": scan_roof,
         "states": states,
         "neighbors": neighbors,
+        "backward": backward,
         "decode": decode,
         "cpu_baseline": cpu,
     }
@@ -473,6 +480,48 @@ def bench_neighbors(args, torch, ssd, syn, np, dev):
                      "head_dim": p, "state_dim": n, "groups": g, "conv_width": K,
                      "norm_groups": 1, "io": "bf16"}
     return res
+
+
+def bench_backward(args, torch, ssd, np, sets, w, dev):
+    """The gradient pass (ssd_chunk_scan_bwd) on the headline workload and
+    input sets, with a final-state cotangent: tokens/s, and the call's time
+    against the bytes any gradient pass must move (inputs x, dt, B, C, dy
+    read once; dx, ddt, dB, dC written once; the final-state cotangent and
+    d init once)."""
+    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 99)
+    dys = [torch.randn((b, l, h, p), generator=gen, device=dev).bfloat16() for _ in sets]
+    dfin = torch.randn((b, h, n, p), generator=gen, device=dev)
+    wsb = int(ssd._lib.load().ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, Q))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    steps = max(args.steps // 10, 5)
+
+    def run(i):
+        S = sets[i % len(sets)]
+        ssd.chunk_scan_bwd(S["x"], S["dt"], S["A"], S["B"], S["C"], dys[i % len(dys)], D=S["D"],
+                           chunk_size=Q, dt_bias=S["bias"], d_final=dfin, workspace=ws)
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    s = 2
+    min_bytes = (2 * (2 * b * l * h * p * s + 2 * b * l * g * n * s + b * l * h * s)
+                 + 2 * b * h * n * p * 4)
+    gbs = min_bytes / (ms * 1e-3) / 1e9
+    log("backward: %.3f ms per call, %.4g tokens/s, %.0f GB/s on the minimal bytes" %
+        (ms, b * l / (ms * 1e-3), gbs))
+    return {"metric": "gradient pass tokens/s", "value": round(b * l / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_call": round(ms, 4), "calls": steps,
+            "workspace_bytes": wsb, "min_bytes": min_bytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "config": {"workload": "mamba2_130m", "io": "bf16", "d_final": True,
+                       "deterministic": True}}
 
 
 def bench_decode(args, torch, ssd, syn, dev):

@@ -124,23 +124,18 @@ __global__ void k_transpose_np(const float *__restrict__ src, float *__restrict_
     dst[pr * np + j * n + k] = src[i];
 }
 
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-// Per token and head (one wave): dx, and the scalars u - v, yb . x,
-// dy . x and d for the running sums.
+// Per token and head (16 lanes, 4 consecutive elements each): dx, and the
+// scalars u - v, yb . x, dy . x and d for the running sums.
 template <typename IO>
 __global__ __launch_bounds__(256) void k_bwd_tok(
     const IO *__restrict__ x, const IO *__restrict__ dt, const IO *__restrict__ Cm,
     const IO *__restrict__ dy, const float *__restrict__ D, const float *__restrict__ dt_bias,
     int softplus, float dt_min, float dt_max, BwdBufs w, IO *__restrict__ dx, int64_t bl,
     int64_t l, int h, int g, int p, int n) {
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= bl * h) return;
+    const int lane = threadIdx.x & 63, sl = lane & 15;
+    const int64_t item0 = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool valid = item0 < bl * h;
+    const int64_t item = valid ? item0 : 0;  // every lane takes part in the shuffles
     const int64_t bt = item / h, b = bt / l, t = bt % l;
     const int hh = (int)(item % h), gi = hh / (h / g);
     const int64_t rt = b * l + (l - 1 - t);
@@ -148,25 +143,32 @@ __global__ __launch_bounds__(256) void k_bwd_tok(
                               dt_min, dt_max);
     const float Dh = D ? D[hh] : 0.f;
     float wsum = 0.f, dsum = 0.f, usum = 0.f;
-    for (int j = lane; j < p; j += 64) {
+    for (int j = sl * 4; j < p; j += 64) {
         const int64_t at = (bt * h + hh) * p + j;
-        const float yb = w.y1[(rt * h + hh) * p + j];
-        const float xv = to_f32(x[at]), dv = to_f32(dy[at]);
-        wsum += yb * xv;
-        dsum += dv * xv;
-        dx[at] = (IO)(Dh * dv + d * yb);
+        const f32x4 yb = *reinterpret_cast<const f32x4 *>(w.y1 + (rt * h + hh) * p + j);
+        const f32x4 xv = ld4(x + at), dv = ld4(dy + at);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wsum += yb[e] * xv[e];
+            dsum += dv[e] * xv[e];
+        }
+        if (valid) st4(dx + at, Dh * dv + d * yb);
     }
-    for (int k = lane; k < n; k += 64)
-        usum += to_f32(Cm[(bt * g + gi) * n + k]) * w.y2[(bt * h + hh) * n + k];
-    wsum = wave_sum_f(wsum);
-    dsum = wave_sum_f(dsum);
-    usum = wave_sum_f(usum);
-    if (lane == 0) {
+    for (int k = sl * 4; k < n; k += 64) {
+        const f32x4 cv = ld4(Cm + (bt * g + gi) * n + k);
+        const f32x4 yv = *reinterpret_cast<const f32x4 *>(w.y2 + (bt * h + hh) * n + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) usum += cv[e] * yv[e];
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+        wsum += __shfl_xor(wsum, off, 64);
+        dsum += __shfl_xor(dsum, off, 64);
+        usum += __shfl_xor(usum, off, 64);
+    }
+    if (valid && sl == 0) {
         float *o = w.sc + ((b * h + hh) * l + t) * 4;
-        o[0] = usum - d * wsum;
-        o[1] = wsum;
-        o[2] = dsum;
-        o[3] = d;
+        *reinterpret_cast<f32x4 *>(o) = f32x4{usum - d * wsum, wsum, dsum, d};
     }
 }
 
@@ -191,27 +193,61 @@ __global__ __launch_bounds__(256) void k_bwd_term(const float *__restrict__ dfin
     if (threadIdx.x == 0) term[pr] = red[0];
 }
 
-// Per (batch, head), one thread, tokens in reverse: the running sum of
-// u - v gives da_t; then ddt and the (batch, head) parts of dA, d dt_bias
-// and dD, all in fp64.
+// Per (batch, head), one workgroup: the reverse running sum of u - v
+// (restarting where a document ends; the final-state term enters at the
+// last token) gives da_t; then ddt and the (batch, head) parts of dA,
+// d dt_bias and dD, all in fp64.  Thread k owns a contiguous segment of
+// tokens; a segment acts on the sum entering it from the right as either
+// "add S" or, with a document end inside, "restart at S"; thread 0 chains
+// the segments right to left, then every thread walks its own tokens with
+// the sum entering it.  Fixed order throughout.
+constexpr int kCumThreads = 256;
+
 template <typename IO>
-__global__ __launch_bounds__(64) void k_bwd_cum(
+__global__ __launch_bounds__(kCumThreads) void k_bwd_cum(
     const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
     int softplus, float dt_min, float dt_max, const int32_t *__restrict__ seq, int has_init,
-    BwdBufs w, IO *__restrict__ ddt, int64_t b_, int64_t l, int h) {
-    const int64_t pr = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    if (pr >= b_ * h) return;
+    BwdBufs w, IO *__restrict__ ddt, int64_t l, int h) {
+    __shared__ double seg_val[kCumThreads], red[3][kCumThreads];
+    __shared__ int seg_cut[kCumThreads];
+    const int64_t pr = blockIdx.x;
     const int64_t b = pr / h;
-    const int hh = (int)(pr % h);
+    const int hh = (int)(pr % h), tid = threadIdx.x;
     const float Ah = A[hh], bias = dt_bias ? dt_bias[hh] : 0.f;
     const float *sc = w.sc + pr * l * 4;
     const int32_t *sq = seq ? seq + b * l : nullptr;
-    double acc = w.term ? w.term[pr] : 0.0;
+    const int64_t per = (l + kCumThreads - 1) / kCumThreads;
+    const int64_t t0 = tid * per, t1 = (t0 + per < l) ? t0 + per : l;
+    // does a document end after token t (before t + 1)?
+    auto ends = [&](int64_t t) { return sq && t + 1 < l && sq[t + 1] != sq[t]; };
+    // this segment's action on the sum entering it
+    double acc = 0.0;
+    int cut = 0;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        if (ends(t)) {
+            acc = 0.0;
+            cut = 1;
+        }
+        acc += (double)sc[t * 4];
+    }
+    seg_val[tid] = acc;
+    seg_cut[tid] = cut;
+    __syncthreads();
+    if (tid == 0) {
+        // the sum entering each segment from the right, stored in seg_val
+        double carry = w.term ? w.term[pr] : 0.0;
+        for (int k = kCumThreads - 1; k >= 0; --k) {
+            const double v = seg_val[k];
+            const int c = seg_cut[k];
+            seg_val[k] = carry;
+            carry = c ? v : carry + v;
+        }
+    }
+    __syncthreads();
+    acc = seg_val[tid];
     double sA = 0.0, sB = 0.0, sD = 0.0;
-    for (int64_t t = l - 1; t >= 0; --t) {
-        // a document ending at t starts the sum afresh (the final-state
-        // term belongs to the last document only)
-        if (sq && t + 1 < l && sq[t + 1] != sq[t]) acc = 0.0;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        if (ends(t)) acc = 0.0;
         const f32x4 v = *reinterpret_cast<const f32x4 *>(sc + t * 4);
         acc += (double)v[0];
         double da = acc;
@@ -229,9 +265,17 @@ __global__ __launch_bounds__(64) void k_bwd_cum(
         sB += g;
         sD += (double)v[2];
     }
-    w.part[pr * 3 + 0] = sA;
-    w.part[pr * 3 + 1] = sB;
-    w.part[pr * 3 + 2] = sD;
+    red[0][tid] = sA;
+    red[1][tid] = sB;
+    red[2][tid] = sD;
+    __syncthreads();
+    for (int off = kCumThreads / 2; off > 0; off >>= 1) {
+        if (tid < off)
+#pragma unroll
+            for (int q = 0; q < 3; ++q) red[q][tid] += red[q][tid + off];
+        __syncthreads();
+    }
+    if (tid < 3) w.part[pr * 3 + tid] = red[tid][0];
 }
 
 // dB and dC of one token: the group's heads summed in order.
@@ -408,7 +452,7 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
     if ((e = scan_f32(P.s2, a3, s)) != hipSuccess) return SSD_ERR_HIP;
 
     trace_begin(SSD_K_BWD_AUX, s);
-    const unsigned tblk = (unsigned)((bl * h + 3) / 4);
+    const unsigned tblk = (unsigned)((bl * h + 15) / 16);
     if (io_dtype == SSD_BF16)
         hipLaunchKernelGGL((k_bwd_tok<bf16>), dim3(tblk), dim3(256), 0, s,
                            static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt),
@@ -424,17 +468,16 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
     if (d_final)
         hipLaunchKernelGGL(k_bwd_term, dim3((unsigned)pairs), dim3(256), 0, s, d_final, w.finT,
                            w.term, (int)n, (int)p);
-    const unsigned cblk = (unsigned)((pairs + 63) / 64);
     if (io_dtype == SSD_BF16)
-        hipLaunchKernelGGL((k_bwd_cum<bf16>), dim3(cblk), dim3(64), 0, s,
+        hipLaunchKernelGGL((k_bwd_cum<bf16>), dim3((unsigned)pairs), dim3(kCumThreads), 0, s,
                            static_cast<const bf16 *>(dt), A, dt_bias, dt_softplus ? 1 : 0,
                            dt_min, dt_max, seq_idx, init_state ? 1 : 0, w,
-                           static_cast<bf16 *>(ddt), b, l, (int)h);
+                           static_cast<bf16 *>(ddt), l, (int)h);
     else
-        hipLaunchKernelGGL((k_bwd_cum<float>), dim3(cblk), dim3(64), 0, s,
+        hipLaunchKernelGGL((k_bwd_cum<float>), dim3((unsigned)pairs), dim3(kCumThreads), 0, s,
                            static_cast<const float *>(dt), A, dt_bias, dt_softplus ? 1 : 0,
                            dt_min, dt_max, seq_idx, init_state ? 1 : 0, w,
-                           static_cast<float *>(ddt), b, l, (int)h);
+                           static_cast<float *>(ddt), l, (int)h);
     if (io_dtype == SSD_BF16)
         hipLaunchKernelGGL((k_bwd_group<bf16>), dim3((unsigned)bl), dim3(256), 0, s, w,
                            static_cast<bf16 *>(dB), static_cast<bf16 *>(dC), l, (int)h, (int)g,
