@@ -299,6 +299,45 @@ size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t
                                           int64_t head_dim, int64_t state_dim, int64_t groups,
                                           int64_t chunk);
 
+/*
+ * Sequence segments (one per GPU for contexts beyond one GPU).  The state
+ * after a stretch of tokens is a linear function of the state entering it
+ * (nnterp guide, "The state after every token"; kongchang "Mamba2" page:
+ * states pass serially from chunk to chunk), so a sequence cut into K
+ * segments is scanned in two passes:
+ *   1. every segment from a zero state (ssd_chunk_scan_ex with final_state):
+ *      its own final state S_k; and its total log decay L_k
+ *      (ssd_segment_log_decay);
+ *   2. ssd_combine_segments: entry_0 = init, entry_{k+1} = exp(L_k) entry_k
+ *      + S_k; then every segment again from entry_k: its y and states are
+ *      those of one pass over the whole sequence, up to rounding.
+ * Across GPUs only the pairs (L_k, S_k) move.
+ *
+ * ssd_segment_log_decay -- L[b, h] = sum over the segment's tokens of
+ *   A[h] * d_t (d_t processed as in ssd_chunk_scan), fp32, summed in fp64
+ *   in a fixed order; -INFINITY where a new document starts inside the
+ *   segment (after its first token: nothing enters past a reset).
+ *   dt [batch, seqlen, heads] io dtype; seq_idx [batch, seqlen] or NULL.
+ *
+ * ssd_combine_segments -- from log_decay [K, b, h] and seg_states
+ *   [K, b, h, n, p] (each segment's final state from a zero state), the
+ *   entry state of every segment entry_states [K, b, h, n, p] (or NULL) and
+ *   the sequence's final state [b, h, n, p] (or NULL).  init_state
+ *   [b, h, n, p] or NULL (zeros).  starts_document [K, b] int32 or NULL:
+ *   nonzero where segment k's first token starts a new document in row b
+ *   (that segment then takes a zero state in).  fp32, deterministic.
+ */
+int32_t ssd_segment_log_decay(const void *dt, const float *A, const float *dt_bias,
+                              int32_t dt_softplus, float dt_min, float dt_max,
+                              const int32_t *seq_idx, float *log_decay, int64_t batch,
+                              int64_t seqlen, int64_t heads, int32_t io_dtype,
+                              void *hip_stream);
+int32_t ssd_combine_segments(const float *log_decay, const float *seg_states,
+                             const float *init_state, const int32_t *starts_document,
+                             float *entry_states, float *final_state, int64_t segments,
+                             int64_t batch, int64_t heads, int64_t head_dim, int64_t state_dim,
+                             void *hip_stream);
+
 /* Static text for a status code (never NULL). */
 const char *ssd_status_string(int32_t status);
 

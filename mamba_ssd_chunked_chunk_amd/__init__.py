@@ -23,6 +23,7 @@ from . import _lib
 from ._lib import LibraryMissing, load, status_string  # noqa: F401
 
 __all__ = ["chunk_scan", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
+           "segment_log_decay", "combine_segments",
            "workspace_bytes", "abi_version",
            "trace_enable", "trace_read", "LibraryMissing", "SsdError"]
 
@@ -192,6 +193,50 @@ def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, chunk_size: int = 256, dt_bias=No
     if rc != 0:
         raise SsdError("ssd_chunk_scan_bwd", rc)
     return out
+
+
+def segment_log_decay(dt, A, dt_bias=None, dt_softplus: bool = True,
+                      dt_limit: Tuple[float, float] = (0.0, math.inf), seq_idx=None):
+    """Total log decay [b, h] of a segment (ssd_segment_log_decay)."""
+    torch = _torch()
+    lib = load()
+    b, l, h = dt.shape
+    dev = dt.device
+    _check("dt", dt, dt.dtype)
+    _check("A", A, torch.float32, (h,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (h,), dev)
+    _check("seq_idx", seq_idx, torch.int32, (b, l), dev)
+    out = torch.empty((b, h), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_segment_log_decay(_ptr(dt), _ptr(A), _ptr(dt_bias), int(bool(dt_softplus)),
+                                   float(dt_limit[0]), float(dt_limit[1]), _ptr(seq_idx),
+                                   _ptr(out), b, l, h, _io_code(dt.dtype), stream)
+    if rc != 0:
+        raise SsdError("ssd_segment_log_decay", rc)
+    return out
+
+
+def combine_segments(log_decay, seg_states, initial_state=None, starts_document=None):
+    """Entry states [K, b, h, n, p] of K segments and the final state
+    [b, h, n, p] from their log decays [K, b, h] and zero-start final
+    states [K, b, h, n, p] (ssd_combine_segments)."""
+    torch = _torch()
+    lib = load()
+    K, b, h, n, p = seg_states.shape
+    dev = seg_states.device
+    _check("log_decay", log_decay, torch.float32, (K, b, h), dev)
+    _check("seg_states", seg_states, torch.float32)
+    _check("initial_state", initial_state, torch.float32, (b, h, n, p), dev)
+    _check("starts_document", starts_document, torch.int32, (K, b), dev)
+    entry = torch.empty_like(seg_states)
+    fin = torch.empty((b, h, n, p), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_combine_segments(_ptr(log_decay), _ptr(seg_states), _ptr(initial_state),
+                                  _ptr(starts_document), _ptr(entry), _ptr(fin), K, b, h, p, n,
+                                  stream)
+    if rc != 0:
+        raise SsdError("ssd_combine_segments", rc)
+    return entry, fin
 
 
 def step(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softplus: bool = True,

@@ -23,6 +23,7 @@ KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step":
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",
            "ssd_conv1d_silu", "ssd_gated_norm", "ssd_chunk_scan_bwd",
+           "ssd_segment_log_decay", "ssd_combine_segments",
            "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version",
            "ssd_trace_enable", "ssd_trace_read")
 
@@ -69,6 +70,10 @@ def load() -> ctypes.CDLL:
                                        P, ctypes.c_size_t, P]
     lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [I64] * 7
+    lib.ssd_segment_log_decay.restype = I32
+    lib.ssd_segment_log_decay.argtypes = [P, P, P, I32, F, F, P, P, I64, I64, I64, I32, P]
+    lib.ssd_combine_segments.restype = I32
+    lib.ssd_combine_segments.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [I32]
     lib.ssd_abi_version.restype = I32
