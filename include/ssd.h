@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 /* io dtype of x, dt, B, C and y */
 enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 };

@@ -151,3 +151,76 @@ def test_oracle_is_not_on_the_product_path():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), os.path.join(dirpath, f)
+
+
+def test_scan_ex_rejects_bad_arguments(lib):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+
+    def ex(**over):
+        kw = dict(seq=None, states=None, b=2, l=64, io=1, wsb=1 << 30)
+        kw.update(over)
+        return lib.ssd_chunk_scan_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, math.inf,
+                                     None, kw["seq"], FAKE, None, kw["states"], kw["b"], kw["l"],
+                                     4, 64, 128, 1, 64, kw["io"], FAKE, kw["wsb"], None)
+    assert ex(seq=FAKE + 2) == L.SSD_ERR_ALIGN
+    assert ex(states=FAKE + 8) == L.SSD_ERR_ALIGN
+    assert ex(io=5) == L.SSD_ERR_UNSUPPORTED
+    assert ex(wsb=16) == L.SSD_ERR_WORKSPACE
+
+
+def test_conv_and_norm_reject_bad_arguments(lib):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+
+    def conv(**over):
+        kw = dict(xbc=FAKE, w=FAKE, x=FAKE, B=FAKE, C=FAKE, fin=None, b=2, l=64, h=4, p=64, n=64,
+                  g=1, K=4, io=1)
+        kw.update(over)
+        return lib.ssd_conv1d_silu(kw["xbc"], kw["w"], None, None, None, kw["x"], kw["B"],
+                                   kw["C"], kw["fin"], kw["b"], kw["l"], kw["h"], kw["p"],
+                                   kw["n"], kw["g"], kw["K"], 1, kw["io"], None)
+    assert conv(K=5) == L.SSD_ERR_UNSUPPORTED
+    assert conv(K=0) == L.SSD_ERR_SHAPE
+    assert conv(p=18) == L.SSD_ERR_UNSUPPORTED
+    assert conv(io=3) == L.SSD_ERR_UNSUPPORTED
+    assert conv(xbc=None) == L.SSD_ERR_NULL
+    assert conv(x=FAKE + 4) == L.SSD_ERR_ALIGN
+    assert conv(b=0) == L.SSD_OK
+
+    def norm(**over):
+        kw = dict(y=FAKE, out=FAKE, rows=8, dim=64, G=16, eps=1e-5, io=1)
+        kw.update(over)
+        return lib.ssd_gated_norm(kw["y"], None, None, kw["out"], kw["rows"], kw["dim"], kw["G"],
+                                  kw["eps"], 1, kw["io"], None)
+    assert norm(G=24) == L.SSD_ERR_SHAPE          # does not divide dim
+    assert norm(G=6, dim=60) == L.SSD_ERR_UNSUPPORTED
+    assert norm(eps=-1.0) == L.SSD_ERR_SHAPE
+    assert norm(y=None) == L.SSD_ERR_NULL
+    assert norm(out=FAKE + 2) == L.SSD_ERR_ALIGN
+    assert norm(rows=0) == L.SSD_OK
+
+
+def test_backward_and_segments_reject_bad_arguments(lib):
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+
+    def bwd(**over):
+        kw = dict(p=64, n=128, b=2, l=64, dy=FAKE, dx=FAKE, wsb=1 << 34, io=1)
+        kw.update(over)
+        return lib.ssd_chunk_scan_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, math.inf,
+                                      None, None, kw["dy"], None, kw["dx"], FAKE, FAKE, FAKE,
+                                      FAKE, None, None, None, kw["b"], kw["l"], 4, kw["p"],
+                                      kw["n"], 1, 64, kw["io"], FAKE, kw["wsb"], None)
+    assert bwd(p=16) == L.SSD_ERR_UNSUPPORTED      # head_dim becomes a state size
+    assert bwd(b=0) == L.SSD_ERR_SHAPE
+    assert bwd(dy=None) == L.SSD_ERR_NULL
+    assert bwd(dx=FAKE + 8) == L.SSD_ERR_ALIGN
+    assert bwd(wsb=1024) == L.SSD_ERR_WORKSPACE
+    assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 1, 64) > 0
+    assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 3, 64) == 0
+    assert lib.ssd_combine_segments(FAKE, FAKE, None, None, None, None, 0, 2, 4, 64, 64,
+                                    None) == L.SSD_ERR_SHAPE
+    assert lib.ssd_combine_segments(None, FAKE, None, None, None, None, 2, 2, 4, 64, 64,
+                                    None) == L.SSD_ERR_NULL
+    assert lib.ssd_segment_log_decay(FAKE, None, None, 1, 0.0, math.inf, None, FAKE, 2, 64, 4, 1,
+                                     None) == L.SSD_ERR_NULL
+    assert lib.ssd_segment_log_decay(FAKE, FAKE, None, 1, 0.0, math.inf, None, FAKE, 2, 64, 4, 9,
+                                     None) == L.SSD_ERR_UNSUPPORTED
