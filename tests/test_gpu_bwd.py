@@ -110,3 +110,24 @@ def test_gradients_deterministic(io):
         bb = _run(inp, cot, 256, seq=seq)
         for k in a:
             assert torch.equal(a[k], bb[k]), k
+
+
+# edge shapes: one token, fewer tokens than a chunk, one group per head,
+# a document at every token, a long row at the bench head shape
+EDGE = [
+    (1, 1, 2, 32, 32, 1, 64, 0.3, True, [()]),
+    (2, 20, 4, 64, 64, 4, 256, 0.0, True, [(), ()]),
+    (1, 40, 2, 32, 32, 1, 32, 0.2, True, [tuple(range(1, 40))]),
+    (1, 2048, 4, 64, 128, 1, 256, 0.1, True, [(700, 1500)]),
+]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("case", EDGE, ids=_bid)
+def test_gradients_edge_shapes(case, io):
+    b, l, h, p, n, g, Q, init, dfin, cuts = case
+    inp = syn.random_case(5400 + sum(case[:7]), b, l, h, p, n, g, io=io, init_std=init)
+    cot = syn.cotangent_case(5500 + sum(case[:7]), b, l, h, p, n, io=io)
+    seq = _seq(b, l, cuts) if any(cuts) else None
+    gpu = _run(inp, cot, Q, seq=seq, d_final=dfin)
+    _compare(gpu, _oracle(inp, cot, seq=seq, d_final=dfin), io)
