@@ -280,7 +280,8 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
  * take head_dim as their state size).  batch and seqlen >= 1.  All
  * arithmetic fp32 (the scans use the fp32 path whatever the io dtype), the
  * running sums behind ddt, dA, d dt_bias and dD in fp64.  16-byte
- * alignment for x, B, C, dy, dx, dB, dC and the states.  Several launches:
+ * alignment for x, B, C, dy, dx, dB, dC and the states, element alignment
+ * for the rest; SSD_ERR_ALIGN otherwise.  Several launches:
  * three fp32 chunk scans (traced as SSD_K_CHUNK_STATE .. SSD_K_CHUNK_OUT)
  * and the pass's own kernels (SSD_K_BWD_AUX).
  */

@@ -368,8 +368,12 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
         return SSD_ERR_UNSUPPORTED;
     if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC)
         return SSD_ERR_NULL;
+    const uintptr_t es = io_dtype == SSD_BF16 ? 2 : 4;
     if (!al16(x) || !al16(B) || !al16(C) || !al16(dy) || !al16(dx) || !al16(dB) || !al16(dC) ||
-        !al16(init_state) || !al16(d_final) || !al16(d_init) || !al16(workspace))
+        !al16(init_state) || !al16(d_final) || !al16(d_init) || !al16(workspace) ||
+        ((uintptr_t)dt % es) || ((uintptr_t)ddt % es) || ((uintptr_t)seq_idx & 3) ||
+        ((uintptr_t)A & 3) || ((uintptr_t)D & 3) || ((uintptr_t)dt_bias & 3) ||
+        ((uintptr_t)dA & 3) || ((uintptr_t)dD & 3) || ((uintptr_t)d_dt_bias & 3))
         return SSD_ERR_ALIGN;
     BwdPlan P;
     if (!make_bwd_plan(P, batch, seqlen, heads, head_dim, state_dim, groups, chunk))
