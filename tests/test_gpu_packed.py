@@ -161,3 +161,50 @@ def test_short_chunk_output_independent_of_states_request(io):
     torch = torch_mod()
     assert torch.equal(y0, y1)
     assert torch.equal(f0, f1)
+
+
+def _bench_inputs():
+    w = syn.WORKLOADS["mamba2_130m"]
+    return w, syn.make_inputs(w)
+
+
+def test_bench_workload_packed_documents_sampled(orc):
+    """bench.py's packed call at full size: 8 x 2048 tokens of the 130m
+    shape with its seeded document lengths, the state after every chunk
+    written; sampled (batch, head) pairs against the oracle."""
+    import bench
+    from gpu_util import PAIR_AXES, sample_pairs
+    w, inp = _bench_inputs()
+    rng = np.random.default_rng(w.seed + 77)
+    seq = bench.doc_index(np, rng, w.batch, w.seqlen)
+    y, fin, st = _run(inp, w.chunk, seq=seq, states=True)
+    pairs = sample_pairs(w.batch, w.heads, 6, seed=11)
+    pr = np.asarray(pairs)
+    yo, fo, so = orc.scan(**oracle_kw(inp), seq_idx=seq, pairs=pairs, states_chunk=w.chunk)
+    torch = torch_mod()
+    bi = torch.as_tensor(pr[:, 0], device="cuda")
+    hi = torch.as_tensor(pr[:, 1], device="cuda")
+    check_close(to_f64(y[bi, :, hi]), yo, "bf16", "y", PAIR_AXES)
+    check_close(to_f64(fin[bi, hi]), fo, "bf16", "final_state", PAIR_AXES)
+    check_close(to_f64(st[bi, :, hi]), so, "bf16", "chunk states", (1, 2, 3))
+
+
+def test_bench_workload_per_token_states_sampled(orc):
+    """bench.py's per-token call: one 2048-token row of the 130m shape at
+    chunk 1 (1.6 GB of states); two heads against the oracle."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    w, _ = _bench_inputs()
+    inp = syn.make_inputs(w, batch=1)
+    torch = torch_mod()
+    g = gpu_inputs(inp)
+    y, st = ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk_size=1,
+                           dt_bias=g["dt_bias"], return_chunk_states=True)
+    torch.cuda.synchronize()
+    assert tuple(st.shape) == (1, w.seqlen, w.heads, w.state_dim, w.head_dim)
+    pairs = [(0, 0), (0, w.heads - 1)]
+    yo, fo, so = orc.scan(**oracle_kw(inp), pairs=pairs, states_chunk=1)
+    for k, (_, hh) in enumerate(pairs):
+        check_close(to_f64(st[0, :, hh]), so[k], "bf16", "per-token states head %d" % hh,
+                    (1, 2))
+        check_close(to_f64(y[0, :, hh]), yo[k], "bf16", "y head %d" % hh)
+    del st
