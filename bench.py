@@ -72,16 +72,18 @@ def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
 
 def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False, states=False):
     """Algorithmic bytes of one launch of a scan kernel: every operand of its
-    step of the method moved once (per-row workspace arrays fp32, chunk
-    states fp32, boundary states in the read-out's operand type: fp16 on the
-    bf16 path, fp32 on the fp32 path; with `states`, the state after every
-    chunk written in fp32)."""
+    step of the method moved once (per-row workspace arrays fp32; chunk
+    states fp32 on the fp32 path and scaled fp16 on the bf16 path; boundary
+    states in the read-out's operand type: fp16 on the bf16 path, fp32 on
+    the fp32 path; with `states`, the state after every chunk written in
+    fp32)."""
     nc, lp = plan_sizes(b, l, h, p, n, g, Q)
     th = b * l * h
     x = th * p * s                     # x (and y) in the io dtype
     BC = b * l * g * n * s             # B or C, once per group
     rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
     so = 2 if s == 2 else 4            # boundary-state element
+    se = 2 if s == 2 else 4            # chunk-state element (bf16 io: scaled fp16)
     # chunk states needed: the last chunk's only feeds the final state and
     # the state after the last chunk
     ns = nc if (final or states) else nc - 1
@@ -93,13 +95,13 @@ def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False, states=F
     sout = b * nc * h * n * p * 4 if states else 0
     if name == "chunk_state":
         # x, B and dt read; the per-row lcs, d and weights, the needed chunk
-        # states and decays written
-        return x + BC + th * s + 3 * rows + 4 * sn + b * h * ns * 4
+        # states, their decays (and on the bf16 path their scales) written
+        return x + BC + th * s + 3 * rows + se * sn + b * h * ns * (8 if s == 2 else 4)
     if name == "state_scan":
         # needed chunk states and decays read, boundary states written; on the
         # bf16 path also B and C read once and their fp16 block images written
         img = 2 * BC + 2 * b * nc * g * (-(-Q // 32) * 32) * n * 2 if s == 2 else 0
-        return 4 * sn + b * h * ns * 4 + so * sb + fin + img + sout
+        return se * sn + b * h * ns * (8 if s == 2 else 4) + so * sb + fin + img + sout
     if name == "chunk_out":
         # x, B and C (bf16 path: their fp16 block images, the same size), the
         # lcs, d and weight rows and the boundary states read, y written

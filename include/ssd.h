@@ -102,8 +102,11 @@ enum ssd_status {
  * (below 2^-24 they count as zero) and larger ones saturate at 65504.  The
  * decay-weighted x, the masked scores and the carried state are rounded to
  * fp16 (toward zero) as operands; the state entering each chunk is kept in
- * the workspace as fp16 (rounded to nearest), the operand it feeds.  The
- * recurrence across chunks, all sums and decays, and final_state are fp32.
+ * the workspace as fp16 (rounded to nearest), the operand it feeds, and so
+ * is every chunk's own state, times a power-of-two scale per (batch, chunk,
+ * head) that puts its largest magnitude in [2^14, 2^15) (no overflow; 11
+ * bits relative to that maximum).  The recurrence across chunks, all sums
+ * and decays, and final_state are fp32.
  * fp32 io uses fp32 operands and fp32 boundary states throughout.
  */
 int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,

@@ -25,7 +25,7 @@ struct ScanPlan {
     int64_t Qp;   // padded rows per chunk
     int64_t lp;   // padded rows per sequence (nc * Qp)
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, off_img, off_hc, total;
+    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, off_scl, off_img, off_hc, total;
 };
 
 // Chunks shorter than one 32-row block are computed as chunks of a whole
@@ -87,8 +87,10 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     // boundary states: matrix-core operand type (fp16 for bf16 io, fp32 for
     // fp32 io); room for fp32 so the layout does not depend on the io type
     P.off_hb = o;   o += align256(b * P.nc * h * st * 4);
-    P.off_st = o;   o += align256(b * P.nc * h * st * 4);  // chunk states, fp32
+    P.off_st = o;   o += align256(b * P.nc * h * st * 4);  // chunk states (fp32, or scaled fp16)
     P.off_lam = o;  o += align256(b * h * P.nc * 4);       // chunk log2 decays
+    // bf16 io: every chunk state is kept as fp16 times a power-of-two scale
+    P.off_scl = o;  o += align256(b * h * P.nc * 4);       // chunk-state scales
     // C and B of every 32-row block of every (batch, chunk, group) as fp16,
     // in the chunk output's LDS layout (bf16 io only; room kept for both)
     P.off_img = o;  o += align256(b * P.nc * g * P.nsb * 2 * P.T * n * 2);

@@ -316,6 +316,22 @@ __device__ __forceinline__ void sp_store_t(float *dst, const f32x4 *acc, int c0,
                                        4 * (lane >> 4)) = acc[u * K::RT + tr];
 }
 
+// The same tiles as fp16 times inv (an exact power of two), 8 bytes per 4.
+template <typename IO, int P, int N, int HPW>
+__device__ __forceinline__ void sp_store_t16(f16 *dst, const f32x4 *acc, float inv, int c0,
+                                             int lane) {
+    typedef Sp<IO, P, N, HPW> K;
+#pragma unroll
+    for (int u = 0; u < K::CPW; ++u)
+#pragma unroll
+        for (int tr = 0; tr < K::RT; ++tr) {
+            const f32x4 v = acc[u * K::RT + tr] * inv;
+            *reinterpret_cast<f16x4 *>(dst + (c0 + 16 * u + (lane & 15)) * N + tr * 16 +
+                                       4 * (lane >> 4)) =
+                f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+        }
+}
+
 // Adds the staged block to the wave's tiles: S += B^T (v x).
 template <typename IO, int P, int N, int HPW>
 __device__ __forceinline__ void sp_apply(f32x4 *acc, const typename Op<IO>::type *buf, int hs,
@@ -354,8 +370,8 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
-    float *__restrict__ St, float *__restrict__ Lam, int64_t l, int h, int g, int64_t Q,
-    int64_t nc, int64_t Qp, int keep_last, const int32_t *__restrict__ seq,
+    float *__restrict__ St, float *__restrict__ Lam, float *__restrict__ Scl, int64_t l, int h,
+    int g, int64_t Q, int64_t nc, int64_t Qp, int keep_last, const int32_t *__restrict__ seq,
     const float *__restrict__ lw, const float *__restrict__ la) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
@@ -363,6 +379,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     __shared__ __attribute__((aligned(16))) OP lds0[K::BUF];
     __shared__ __attribute__((aligned(16))) OP lds1[K::BUF];
     __shared__ __attribute__((aligned(16))) SpSpan<HPW> span;
+    __shared__ float wmax[K::W];
 
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     int64_t item = xcd_item(blockIdx.x, gridDim.x);
@@ -464,7 +481,29 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     }
     // the last chunk's own state only feeds the final state
     if (c + 1 < nc || keep_last) {
-        sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
+        if constexpr (sizeof(IO) == 2) {
+            // fp16 times a power of two per (batch, chunk, head): the head's
+            // largest magnitude lands in [2^14, 2^15), so nothing overflows
+            // and every element keeps fp16's 11 bits relative to that maximum
+            float m = 0.f;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[t][e]));
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if (lane == 0) wmax[wave] = m;
+            lds_barrier();
+#pragma unroll
+            for (int k = 0; k < K::WPH; ++k) m = fmaxf(m, wmax[hs * K::WPH + k]);
+            int ex = 0;
+            frexpf(m, &ex);  // m = f 2^ex, f in [0.5, 1) (ex = 0 for m = 0)
+            sp_store_t16<IO, P, N, HPW>(reinterpret_cast<f16 *>(St) + ((b * nc + c) * h + hh) * NP,
+                                        acc, ldexpf(1.f, 15 - ex), c0, lane);
+            if (c0 == 0 && lane == 0) Scl[(b * h + hh) * nc + c] = ldexpf(1.f, ex - 15);
+        } else {
+            sp_store_t<IO, P, N, HPW>(St + ((b * nc + c) * h + hh) * NP, acc, c0, lane);
+        }
         if (c0 == 0 && lane == 0) Lam[(b * h + hh) * nc + c] = logdec;
     }
 }
@@ -578,6 +617,7 @@ __device__ __forceinline__ void store_state_rows(float *lds, const f32x4 &v, con
 template <typename OP, typename IO, int N, bool ROWS>
 __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St,
                                                     const float *__restrict__ Lam,
+                                                    const float *__restrict__ Scl,
                                                     const float *__restrict__ init,
                                                     OP *__restrict__ Hb,
                                                     float *__restrict__ final_state, int64_t bh,
@@ -612,7 +652,10 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
         for (int e = 0; e < 4; ++e) H[e] = src[e * p];
     }
     const int64_t cstride = (int64_t)h * np4;  // from one chunk to the next, in f32x4
+    // chunk states: fp32, or (bf16 io) fp16 times the (batch, chunk, head) scale
     const f32x4 *S = reinterpret_cast<const f32x4 *>(St) + (b * nc * h + hh) * np4 + e4;
+    const f16x4 *S16 = reinterpret_cast<const f16x4 *>(St) + (b * nc * h + hh) * np4 + e4;
+    const float *Sc = Scl + pair * nc;
     OP *dst = Hb + ((b * nc * h + hh) * np4 + e4) * 4;
     const float *L = Lam + pair * nc;
     // chunks whose own state is needed: all but the last unless the final
@@ -622,12 +665,24 @@ __global__ __launch_bounds__(256) void k_state_scan(const float *__restrict__ St
     const int64_t klast = ns > 0 ? ns - 1 : 0;
     for (int64_t k0 = 0; k0 < nc; k0 += G8) {
         f32x4 Sk[G8];
-        float Lk[G8];
+        f16x4 Sh[G8];
+        float Lk[G8], Ck[G8];
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
             const int64_t k = k0 + u < klast ? k0 + u : klast;
-            Sk[u] = S[k * cstride];
+            if constexpr (sizeof(IO) == 2) {
+                Sh[u] = S16[k * cstride];
+                Ck[u] = Sc[k];
+            } else {
+                Sk[u] = S[k * cstride];
+            }
             Lk[u] = L[k];
+        }
+        if constexpr (sizeof(IO) == 2) {
+#pragma unroll
+            for (int u = 0; u < G8; ++u)
+                Sk[u] = f32x4{(float)Sh[u][0], (float)Sh[u][1], (float)Sh[u][2], (float)Sh[u][3]} *
+                        Ck[u];
         }
 #pragma unroll
         for (int u = 0; u < G8; ++u) {
@@ -1376,6 +1431,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     OP *Hb = reinterpret_cast<OP *>(a.ws + pl.off_hb);
     float *St = reinterpret_cast<float *>(a.ws + pl.off_st);
     float *Lam = reinterpret_cast<float *>(a.ws + pl.off_lam);
+    float *Scl = reinterpret_cast<float *>(a.ws + pl.off_scl);
     const IO *x = static_cast<const IO *>(a.x);
     const IO *dt = static_cast<const IO *>(a.dt);
     const IO *Bm = static_cast<const IO *>(a.B);
@@ -1395,7 +1451,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, HPn, SQ>),
                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))), dim3(Sp<IO, P, N, HPn>::NT),
                            0, s, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min, a.dt_max, lcs,
-                           dtp, wgt, St, Lam, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq,
+                           dtp, wgt, St, Lam, Scl, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq,
                            a.lw, a.la);
     };
     trace_begin(1, s);
@@ -1434,11 +1490,11 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     trace_begin(2, s);
     if (keep_last)
         hipLaunchKernelGGL((k_state_scan<OP, IO, N, true>), dim3((unsigned)scan_blocks),
-                           dim3(kThreads), 0, s, St, Lam, a.init, Hb, a.final_state,
+                           dim3(kThreads), 0, s, St, Lam, Scl, a.init, Hb, a.final_state,
                            pl.b * pl.h, h, pl.nc, N, P, ia, a.states);
     else
         hipLaunchKernelGGL((k_state_scan<OP, IO, N, false>), dim3((unsigned)scan_blocks),
-                           dim3(kThreads), 0, s, St, Lam, a.init, Hb, nullptr, pl.b * pl.h, h,
+                           dim3(kThreads), 0, s, St, Lam, Scl, a.init, Hb, nullptr, pl.b * pl.h, h,
                            pl.nc, N, P, ia, nullptr);
     trace_end(2, s);
     e = hipGetLastError();
