@@ -25,7 +25,8 @@ struct ScanPlan {
     int64_t Qp;   // padded rows per chunk
     int64_t lp;   // padded rows per sequence (nc * Qp)
     // workspace offsets (bytes)
-    size_t off_lcs, off_dtp, off_wgt, off_hb, off_st, off_lam, off_scl, off_img, off_hc, total;
+    size_t off_lcs, off_dtp, off_wgt, off_sgr, off_hb, off_st, off_lam, off_scl, off_img, off_hc,
+        total;
 };
 
 // Chunks shorter than one 32-row block are computed as chunks of a whole
@@ -84,6 +85,8 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     P.off_lcs = o;  o += align256(b * h * P.lp * 4);
     P.off_dtp = o;  o += align256(b * h * P.lp * 4);
     P.off_wgt = o;  o += align256(b * h * P.lp * 4);
+    // packed sequences: every row's last reset row in its block (or -1)
+    P.off_sgr = o;  o += align256(b * h * P.lp * 4);
     // boundary states: matrix-core operand type (fp16 for bf16 io, fp32 for
     // fp32 io); room for fp32 so the layout does not depend on the io type
     P.off_hb = o;   o += align256(b * P.nc * h * st * 4);

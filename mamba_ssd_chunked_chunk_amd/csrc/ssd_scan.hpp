@@ -121,6 +121,7 @@ template <typename IO, int HPW> struct SpPtrs {
     const IO *B;             // row 0 of the sequence, the group
     const IO *dt;            // row 0 of the sequence, first head of the workgroup
     float *lcs, *dtp, *wgt;  // (batch, first head) padded row arrays, written
+    int *sgr;                // packed sequences: each row's last reset in its block, or -1
     float a2[HPW], bias[HPW];  // A log2(e) and dt_bias of the workgroup's heads
     int softplus;
     float dt_min, dt_max;
@@ -232,6 +233,7 @@ __device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const
         const float last = __shfl(a, T - 1, T);
         float w = exp2_fast(last - a) * d;
         float lam = last;  // the block's log2 decay
+        int seg = -1;      // the last reset at or before this row in its block
         if constexpr (SEQ) {
             // resets in this block (its 32 lanes): rows before the last one
             // do not reach the block's end, and nothing crosses the block
@@ -240,6 +242,8 @@ __device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const
                 if ((r & (T - 1)) < 31 - __builtin_clz(m)) w = 0.f;
                 lam = -INFINITY;
             }
+            const uint32_t mr = m & ((2u << (r & (T - 1))) - 1u);
+            seg = mr ? 31 - __builtin_clz(mr) : -1;
         }
         const int64_t R = (int64_t)blk0 * T + r;  // padded row inside the chunk
         if (R < sp.Qp) {
@@ -247,6 +251,7 @@ __device__ __forceinline__ void sp_span(SpSpan<HPW> &sv, const float *dtv, const
             sp.lcs[idx2] = a;
             sp.dtp[idx2] = d;
             sp.wgt[idx2] = w;
+            if constexpr (SEQ) sp.sgr[idx2] = seg;
         }
         sv.v[hs][r] = w;
         if ((r & (T - 1)) == T - 1) sv.lam[hs][r / T] = lam;
@@ -372,7 +377,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     float dt_max, float *__restrict__ lcs, float *__restrict__ dtp, float *__restrict__ wgt,
     float *__restrict__ St, float *__restrict__ Lam, float *__restrict__ Scl, int64_t l, int h,
     int g, int64_t Q, int64_t nc, int64_t Qp, int keep_last, const int32_t *__restrict__ seq,
-    const float *__restrict__ lw, const float *__restrict__ la) {
+    int *__restrict__ sgr, const float *__restrict__ lw, const float *__restrict__ la) {
     typedef Sp<IO, P, N, HPW> K;
     typedef typename K::OP OP;
     constexpr int T = kT, SPAN = K::SPAN, TPW = K::TPW;
@@ -405,6 +410,7 @@ __global__ __launch_bounds__((Sp<IO, P, N, HPW>::NT),
     sp.lcs = lcs + (b * h + hh0) * nc * Qp;
     sp.dtp = dtp + (b * h + hh0) * nc * Qp;
     sp.wgt = wgt + (b * h + hh0) * nc * Qp;
+    sp.sgr = SEQ ? sgr + (b * h + hh0) * nc * Qp : nullptr;
 #pragma unroll
     for (int k = 0; k < HPW; ++k) {
         sp.a2[k] = A[hh0 + k] * kLog2e;
@@ -782,8 +788,7 @@ __device__ __forceinline__ int row_pair(int r) { return 2 * (r & 15) + (r >> 4);
 // tid % kT (threads past HPW * kT load and discard).
 struct CoRowV {
     float ls, ds, ws, l15;
-    int sq, sqp, sv;  // packed sequences: document index of the row and of the row
-                      // before it, and whether the row is a real one after token 0
+    int sg;  // packed sequences: the row's last reset in its block, or -1
 };
 
 // Register prefetch of one block for the whole workgroup (fp32 io).  Loads
@@ -808,12 +813,12 @@ template <typename IO> struct CoPtrs {
     uint32_t hstride;   // bytes from one head's row arrays to the next
     int rows;           // valid rows of the chunk
     Rsrc rimg;          // block images of this (batch, chunk, group) (bf16 io)
-    Rsrc rsq;           // document indices of the batch row (packed sequences)
+    Rsrc rsg;           // packed sequences: the rows' last resets (as rl)
     int64_t t0;         // the chunk's first token
 };
 
 // Vector memory loads co_rows_prefetch issues per thread.
-template <bool SEQ> constexpr int kRowLoads = SEQ ? 6 : 4;
+template <bool SEQ> constexpr int kRowLoads = SEQ ? 5 : 4;
 
 template <int HPW, bool SEQ, typename IO>
 __device__ __forceinline__ void co_rows_prefetch(CoRowV &f, int s, const CoPtrs<IO> &cp, int tid) {
@@ -825,16 +830,7 @@ __device__ __forceinline__ void co_rows_prefetch(CoRowV &f, int s, const CoPtrs<
     f.ds = buf_f32(cp.rd, ro, soff);
     f.ws = buf_f32(cp.rw, ro, soff);
     f.l15 = buf_f32(cp.rl, (uint32_t)hs * cp.hstride + 15u * 4u, soff);
-    if constexpr (SEQ) {
-        // whole offsets in the lane operand, so that the row before token 0
-        // (offset -4) falls outside the resource and reads 0
-        const int64_t t = cp.t0 + s * T + row;
-        f.sq = (int)__builtin_bit_cast(
-            uint32_t, buf_f32(cp.rsq, (uint32_t)(t * 4), 0u));
-        f.sqp = (int)__builtin_bit_cast(
-            uint32_t, buf_f32(cp.rsq, (uint32_t)(t * 4 - 4), 0u));
-        f.sv = (s * T + row < cp.rows) && t > 0;
-    }
+    if constexpr (SEQ) f.sg = __builtin_bit_cast(int, buf_f32(cp.rsg, ro, soff));
 }
 
 template <int HPW, bool SEQ>
@@ -843,14 +839,7 @@ __device__ __forceinline__ void co_rows_stage(const CoRowV &f, CoRows *rows, int
     if (tid < HPW * T) {
         CoRows &rw = rows[tid / T];
         const int r = tid % T;
-        if constexpr (SEQ) {
-            // rows of this block that start from a zero state (one 32-lane
-            // group per head, all holding the same rows)
-            const uint32_t m =
-                (uint32_t)(__ballot(f.sv && f.sq != f.sqp) >> (tid & 32)) &
-                ((2u << r) - 1u);
-            rw.seg[r] = m ? 31 - __builtin_clz(m) : -1;
-        }
+        if constexpr (SEQ) rw.seg[r] = f.sg;
         rw.lcs[r] = f.ls;
         rw.d[r] = f.ds;
         rw.a2[row_pair(r)] = exp2_fast(f.ls - f.l15);
@@ -1258,16 +1247,17 @@ __device__ __forceinline__ void co_compute(f32x4 *accH, const typename Op<IO>::t
     }
 }
 
-// copying path: three workgroups per compute unit (two with packed sequences,
-// whose masks need more registers than three allow without spilling)
+// copying path: three workgroups per compute unit, also with packed
+// sequences (whose row masks then spill a few bytes at state_dim 128, which
+// still beats two workgroups per CU: 44.6 -> 39.0 us at the 130m shape)
 template <typename IO, int P, int N, int HPW, bool COPY, bool SEQ>
 __global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT),
-                             (Co<IO, P, N, HPW, COPY>::DMA ? (SEQ ? 2 : 3) : 1)) void k_chunk_out(
+                             (Co<IO, P, N, HPW, COPY>::DMA ? 3 : 1)) void k_chunk_out(
     const IO *__restrict__ x, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ lcs, const float *__restrict__ dtp,
     const float *__restrict__ wgt, const typename Op<IO>::type *__restrict__ Hb,
     IO *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t Qp,
-    const f16 *__restrict__ img, int64_t nsb, int has_init, const int32_t *__restrict__ seq) {
+    const f16 *__restrict__ img, int64_t nsb, int has_init, const int *__restrict__ sgr) {
     typedef Co<IO, P, N, HPW, COPY> K;
     typedef typename K::OP OP;
     constexpr int T = kT, BUF = K::BUF, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
@@ -1306,7 +1296,7 @@ __global__ __launch_bounds__((Co<IO, P, N, HPW, COPY>::NT),
     cp.hstride = (uint32_t)(nc * Qp * 4);
     cp.rows = (int)((Q < l - t0) ? Q : (l - t0));
     cp.t0 = t0;
-    if constexpr (SEQ) cp.rsq = make_rsrc(seq + b * l, l * 4);
+    if constexpr (SEQ) cp.rsg = make_rsrc(sgr + rbase, rspan);
     if constexpr (K::DMA)
         cp.rimg = make_rsrc(img + ((b * nc + c) * g + gi) * nsb * (2 * T * N),
                             nsb * (int64_t)(4 * T * N));
@@ -1432,6 +1422,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     float *St = reinterpret_cast<float *>(a.ws + pl.off_st);
     float *Lam = reinterpret_cast<float *>(a.ws + pl.off_lam);
     float *Scl = reinterpret_cast<float *>(a.ws + pl.off_scl);
+    int *sgr = reinterpret_cast<int *>(a.ws + pl.off_sgr);
     const IO *x = static_cast<const IO *>(a.x);
     const IO *dt = static_cast<const IO *>(a.dt);
     const IO *Bm = static_cast<const IO *>(a.B);
@@ -1451,7 +1442,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((k_chunk_state<IO, P, N, HPn, SQ>),
                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))), dim3(Sp<IO, P, N, HPn>::NT),
                            0, s, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min, a.dt_max, lcs,
-                           dtp, wgt, St, Lam, Scl, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq,
+                           dtp, wgt, St, Lam, Scl, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq, sgr,
                            a.lw, a.la);
     };
     trace_begin(1, s);
@@ -1509,7 +1500,7 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))),
                            dim3(Co<IO, P, N, HPn, CP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt,
                            Hb, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb,
-                           a.init != nullptr, a.seq);
+                           a.init != nullptr, sgr);
     };
     typedef std::integral_constant<int, 1> One;
     typedef std::integral_constant<int, HP> Grp;

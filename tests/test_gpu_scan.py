@@ -294,7 +294,8 @@ def _ws_layout(b, l, h, Q, io):
     a256 = lambda v: (v + 255) // 256 * 256
     off_dtp = a256(b * h * lp * 4)
     off_wgt = off_dtp + a256(b * h * lp * 4)
-    off_hb = off_wgt + a256(b * h * lp * 4)
+    off_sgr = off_wgt + a256(b * h * lp * 4)   # reset rows (packed sequences)
+    off_hb = off_sgr + a256(b * h * lp * 4)
     return T, nc, Qp, lp, off_dtp, off_wgt, off_hb
 
 
