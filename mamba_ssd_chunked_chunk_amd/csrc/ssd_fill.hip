@@ -95,8 +95,9 @@ __global__ __launch_bounds__(256) void k_token_states(
     const int32_t *sq = seq ? seq + b * l : nullptr;
     float *op = out + (b * ns * h + hh) * np + col;
 
-    TokIn cur, nxt;
+    TokIn cur;
     load_tok(cur, t0, dp, xp, bp, sq, xs, bs, h, r0, RS, n);
+    TokIn nxt = cur;
     for (int64_t t = t0; t < t1; ++t) {
         if (t + 1 < t1) load_tok(nxt, t + 1, dp, xp, bp, sq, xs, bs, h, r0, RS, n);
         const float d = time_step(cur.dt, bias, softplus, dt_min, dt_max);
