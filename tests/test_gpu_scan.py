@@ -343,3 +343,49 @@ def test_stage_intermediates(orc, io):
     last = np.minimum(np.arange(l) // Q * Q + Q, l) - 1
     w_o = np.exp(cs_o[..., last] - cs_o) * inter["d"]
     check_close(to_f64(wgt), w_o, "f32", "row weights")
+
+
+def test_graph_capture_replays_match_eager(orc):
+    """One ssd_chunk_scan call captured in a HIP graph (preallocated output,
+    final state and workspace; the library allocates and clears nothing) and
+    replayed several times with eager work in between: every replay equals
+    the eager call bit for bit."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    inp = syn.random_case(41, 2, 600, 8, 64, 128, 2, io="bf16", init_std=0.2)
+    g = gpu_inputs(inp)
+    b, l, h, p = g["x"].shape
+    n = g["B"].shape[3]
+    Q = 256
+    ws = torch.empty(ssd.workspace_bytes(b, l, h, p, n, 2, Q), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(g["x"])
+    fin = torch.empty((b, h, n, p), dtype=torch.float32, device="cuda")
+
+    def call():
+        ssd.chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk_size=Q,
+                       dt_bias=g["dt_bias"], initial_state=g["init"], return_final_state=True,
+                       out=y, final_out=fin, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    y_ref, f_ref = y.clone(), fin.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                      # warm the path on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for k in range(3):
+        y.zero_()
+        fin.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), k
+        assert torch.equal(fin.view(torch.int32), f_ref.view(torch.int32)), k
+        call()                      # eager work between replays
+        torch.cuda.synchronize()
+    yo, fo = orc.scan(**oracle_kw(inp))
+    check_close(to_f64(y), yo, "bf16", "y", Y_AXES)
