@@ -2,6 +2,14 @@
  * ssd.h -- C ABI of libssd.so: the Mamba-2 SSD selective-state-space scan on
  * AMD MI355X (gfx950).
  *
+ * Entry points: the chunked scan (ssd_chunk_scan, ssd_chunk_scan_ex with
+ * packed documents and the state after every chunk or token), the decode
+ * step (ssd_step), the steps just before and after the scan in a Mamba-2
+ * mixer (ssd_conv1d_silu, ssd_gated_norm), the deterministic gradient pass
+ * (ssd_chunk_scan_bwd), and the pieces of a sequence split into segments
+ * (ssd_segment_log_decay, ssd_combine_segments); plus workspace queries,
+ * status strings and kernel timing.
+ *
  * The scan (nnterp guide, "Mamba-2" page, opening section): per head the
  * state h is a state_dim x head_dim matrix, and every token t does
  *
