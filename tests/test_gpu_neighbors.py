@@ -151,3 +151,35 @@ def test_norm_bench_shape():
     c = syn.norm_case(4700, 8 * 2048, 1536, io="bf16")
     s = _norm(c)
     log("gated norm bench shape: max_abs %.3g max_rel %.3g" % (s[0], s[1]))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_mixer_chain_matches_composed_oracles(io):
+    """conv1d + SiLU -> chunk scan -> gate + RMS norm on the GPU against the
+    same chain of oracles (each GPU stage fed by the previous GPU stage, as
+    in a layer; the oracle chain in fp64, its scan inputs rounded like the
+    GPU's)."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    import oracle
+    from oracle import neighbors as nb
+    torch = torch_mod()
+    b, l, h, p, n, g, K, Q = 2, 300, 4, 64, 64, 2, 4, 128
+    c = syn.conv_case(4800, b, l, h, p, n, g, K, io=io, with_init=False)
+    sc = syn.random_case(4801, b, l, h, p, n, g, io=io)
+    z = syn.norm_case(4802, b * l, h * p, io=io)
+    x, B, C = ssd.conv1d_silu(dev_tensor(c["xbc"]), dev_tensor(c["weight"]), h, p, n, g,
+                              bias=dev_tensor(c["bias"]))
+    y = ssd.chunk_scan(x, dev_tensor(sc["dt"]), dev_tensor(sc["A"]), B, C, dev_tensor(sc["D"]),
+                       chunk_size=Q, dt_bias=dev_tensor(sc["dt_bias"]))
+    out = ssd.gated_norm(y.reshape(b * l, h * p), dev_tensor(z["z"]), dev_tensor(z["weight"]),
+                         eps=1e-5)
+    torch.cuda.synchronize()
+    # the oracle chain: its conv in fp64, rounded to the io type as the GPU
+    # stores it, then the fp64 scan, then the fp64 gate and norm
+    xo, Bo, Co, _ = nb.conv1d_silu(syn.as_f32(c["xbc"], io), c["weight"], h, p, n, g,
+                                   bias=c["bias"])
+    r = (lambda a: syn.bf16_round(np.asarray(a, np.float32))) if io == "bf16" else \
+        (lambda a: np.asarray(a, np.float32))
+    yo, _ = oracle.scan(r(xo), sc["dt"], sc["A"], r(Bo), r(Co), sc["D"], sc["dt_bias"], io=io)
+    oo = nb.gated_norm(yo.reshape(b * l, h * p), syn.as_f32(z["z"], io), z["weight"], eps=1e-5)
+    check_close(to_f64(out), oo, io, "mixer chain", (1,))
