@@ -1,15 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the SSD scan on one MI355X.
 
-One step = one ssd_chunk_scan over one batch of the Mamba2-130m-shaped
-workload (batch 8, seqlen 2048, 24 heads, head_dim 64, state_dim 128,
-1 group, chunk 256, bf16 io, fp32 state), inputs resident in HBM.  Steps
-cycle through several independently drawn input/output sets so that the
-working set exceeds the 256 MB Infinity Cache.  Printed: one JSON line with
-tokens/s (value), the dominant kernel's roofline (HIP-event durations of
-that kernel on its launch stream), the whole scan against its HBM roofline,
-the decode step rate (ssd_step at batch 256, 80 heads, state from a
-1024-token prefill), and the oracle timed on the host cores.
+The headline step is one ssd_chunk_scan over the grouped long-context
+workload (batch 1, seqlen 65536, 64 heads of head_dim 64, state 128,
+8 groups, chunk 256, bf16 io, fp32 state), the largest single-GPU scan
+workload; inputs resident in HBM, several independently drawn input sets
+cycled through so that the working set exceeds the 256 MB Infinity Cache.
+Every other workload is timed the same way and reported beside it (tiny
+fp32, the Mamba2-130m and 2.7B shapes, the decode workload's 256 x 1024
+prefill), plus 128 decode steps at batch 256.
+
+Kernel durations come from HIP events that the library records at each
+kernel's own dispatch (ssd_chunk_scan_ex's kernel_events), over the timed
+steps themselves.  Algorithmic bytes per launch follow the method: every
+operand of the kernel's step moved once, in the type the kernel stores it.
+
+Printed: one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -20,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -28,9 +35,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD scan tokens/sec at 1 GPU; % of MFMA/HBM roofline; decode steps/sec"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_IDS = ("chunk_state", "state_scan", "chunk_out")
+SLOTS = ("chunk_state", "state_scan", "chunk_out")
+HEADLINE = "grouped_long"
+SCAN_WORKLOADS = ("tiny_fp32", "mamba2_130m", "mamba2_2p7b", "grouped_long", "decode_2p7b")
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan.hpp",
+KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan16.hpp",
                   "mamba_ssd_chunked_chunk_amd/csrc/ssd_device.hpp",
                   "mamba_ssd_chunked_chunk_amd/csrc/ssd_plan.hpp")
 
@@ -48,64 +57,45 @@ def source_digest() -> str:
 
 
 # ----------------------------------------------------------- byte counts ---
-def plan_sizes(b, l, h, p, n, g, Q, T=32):
-    """Chunks and padded rows per sequence, as the library plans them
-    (32-row blocks that never straddle a chunk boundary)."""
-    nc = -(-l // Q)
-    lp = nc * (-(-Q // T) * T)
-    return nc, lp
-
-
 def bytes_scan_alg(b, l, h, p, n, g, Q, s, init=False, final=False):
     """Algorithmic bytes of the whole scan: inputs and outputs once plus one
     write and one read of the fp32 chunk-boundary-state tensor."""
     th = b * l * h
     per = 2 * p * s + 2 * n * s * g / h + s + 8.0 * n * p / Q
-    extra = (4 * n * p * b * h) * (int(init) + int(final))
-    return th * per + extra
+    return th * per + 4 * n * p * b * h * (int(init) + int(final))
 
 
 def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
+    """The same without the boundary-state tensor: inputs and outputs once."""
     th = b * l * h
     return th * (2 * p * s + 2 * n * s * g / h + s) + 4 * n * p * b * h * (int(init) + int(final))
 
 
-def bytes_kernel(name, b, l, h, p, n, g, Q, s, final=False, init=False, states=False):
-    """Algorithmic bytes of one launch of a scan kernel: every operand of its
-    step of the method moved once (per-row workspace arrays fp32; chunk
-    states fp32 on the fp32 path and scaled fp16 on the bf16 path; boundary
-    states in the read-out's operand type: fp16 on the bf16 path, fp32 on
-    the fp32 path; with `states`, the state after every chunk written in
-    fp32)."""
-    nc, lp = plan_sizes(b, l, h, p, n, g, Q)
+def bytes_kernel(name, b, l, h, p, n, g, Q, s, init=False, final=False):
+    """Algorithmic bytes of one launch: every operand of the kernel's step
+    moved once, in the type the kernel keeps it.  bf16 io: chunk states and
+    boundary states are fp16 (with one fp32 scale or maximum per (batch,
+    chunk, head)); fp32 io: fp32.  B and C count once per group."""
+    nc = -(-l // Q)
     th = b * l * h
-    x = th * p * s                     # x (and y) in the io dtype
-    BC = b * l * g * n * s             # B or C, once per group
-    rows = b * h * lp * 4              # one per-row fp32 array (lcs, d or weight)
-    so = 2 if s == 2 else 4            # boundary-state element
-    se = 2 if s == 2 else 4            # chunk-state element (bf16 io: scaled fp16)
-    # chunk states needed: the last chunk's only feeds the final state and
-    # the state after the last chunk
-    ns = nc if (final or states) else nc - 1
-    sn = b * ns * h * n * p
-    # boundary states stored and read: chunk 0's is the initial state, zero
-    # (and neither stored nor read) when none is given
-    sb = b * (nc if init else nc - 1) * h * n * p
-    fin = b * h * n * p * 4 if final else 0
-    sout = b * nc * h * n * p * 4 if states else 0
+    x = th * p * s                      # x (or y)
+    BC = b * l * g * n * s              # B or C
+    dt = th * s
+    es = 2 if s == 2 else 4             # stored state element
+    ns = nc if final else nc - 1        # chunk states needed
+    sn = b * ns * h * n * p * es + b * ns * h * 8
+    sb = b * (nc if init else nc - 1) * h * (n * p * es + 4)   # boundary states stored
+    io_state = b * h * n * p * 4
     if name == "chunk_state":
-        # x, B and dt read; the per-row lcs, d and weights, the needed chunk
-        # states, their decays (and on the bf16 path their scales) written
-        return x + BC + th * s + 3 * rows + se * sn + b * h * ns * (8 if s == 2 else 4)
+        # x, B and dt read; the chunk states, their maxima and log decays written
+        rows = 0 if s == 2 else 3 * b * h * nc * (-(-Q // 32) * 32) * 4
+        return x + BC + dt + sn + rows
     if name == "state_scan":
-        # needed chunk states and decays read, boundary states written; on the
-        # bf16 path also B and C read once and their fp16 block images written
-        img = 2 * BC + 2 * b * nc * g * (-(-Q // 32) * 32) * n * 2 if s == 2 else 0
-        return se * sn + b * h * ns * (8 if s == 2 else 4) + so * sb + fin + img + sout
+        return sn + sb + io_state * (int(init) + int(final))
     if name == "chunk_out":
-        # x, B and C (bf16 path: their fp16 block images, the same size), the
-        # lcs, d and weight rows and the boundary states read, y written
-        return x + 2 * BC + 3 * rows + so * sb + x
+        # x, B, C, dt and the boundary states read, y written
+        rows = 0 if s == 2 else 3 * b * h * nc * (-(-Q // 32) * 32) * 4
+        return 2 * x + 2 * BC + dt + sb + rows
     raise KeyError(name)
 
 
@@ -113,7 +103,6 @@ def bytes_step(b, h, p, n, g, s):
     return b * h * (8 * n * p + 2 * p * s + s) + 2 * b * g * n * s + 12 * h
 
 
-# --------------------------------------------------------------- traffic ---
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel sources changed since."""
@@ -134,14 +123,122 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+# ----------------------------------------------------------------- inputs --
+def device_inputs(torch, w, dev, seed):
+    """One input set of workload w drawn on the device with the workloads'
+    distributions (A = -exp(U[0, ln 16]), dt_bias = softplus^-1 of a
+    log-uniform step in [1e-3, 0.1], x, dt, B, C ~ N(0, 1) rounded to the io
+    dtype, D = 1, initial state N(0, init_std^2) where the workload has one)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    b, l, h, p, n, g = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups
+    io = torch.float32 if w.io == "f32" else torch.bfloat16
+    A = -torch.exp(torch.rand(h, generator=gen, device=dev) * math.log(16.0))
+    dt0 = torch.exp(math.log(1e-3) + torch.rand(h, generator=gen, device=dev)
+                    * (math.log(0.1) - math.log(1e-3)))
+    bias = dt0 + torch.log(-torch.expm1(-dt0))
+
+    def nrm(*shape):
+        return torch.randn(*shape, generator=gen, device=dev).to(io)
+    d = dict(A=A, bias=bias, D=torch.ones(h, device=dev), x=nrm(b, l, h, p), dt=nrm(b, l, h),
+             B=nrm(b, l, g, n), C=nrm(b, l, g, n))
+    d["init"] = (w.init_std * torch.randn(b, h, n, p, generator=gen, device=dev)
+                 if w.init_std > 0 else None)
+    d["y"] = torch.empty_like(d["x"])
+    return d
+
+
+class Events:
+    """8 HIP events (start, end of each kernel slot) per timed call, created
+    through torch (recorded once so that they exist)."""
+
+    def __init__(self, torch, calls):
+        self.torch = torch
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(calls)]
+        for row in self.ev:
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        self.handles = [[e.cuda_event for e in row] for row in self.ev]
+
+    def slot_ms(self, k, calls):
+        """Average duration of slot k over the first `calls` calls (ms)."""
+        tot = 0.0
+        for i in range(calls):
+            tot += self.ev[i][2 * k].elapsed_time(self.ev[i][2 * k + 1])
+        return tot / calls
+
+
+def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4):
+    """W warmup + K timed ssd_chunk_scan calls over cycled input sets; then
+    the same K calls again with kernel events.  Returns the step time and the
+    average duration of every kernel."""
+    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
+    s = 4 if w.io == "f32" else 2
+    per_set = b * l * h * p * s * 2 + 2 * b * l * g * n * s
+    nsets = max(1, min(max_sets, int(math.ceil(600e6 / per_set))))
+    sets = [device_inputs(torch, w, dev, w.seed + 1000 * k) for k in range(nsets)]
+    final = w.return_final
+    fin = torch.empty((b, h, n, p), dtype=torch.float32, device=dev) if final else None
+    ws = torch.empty(ssd.workspace_bytes(b, l, h, p, n, g, Q), dtype=torch.uint8, device=dev)
+
+    def run(i, ev=None):
+        S = sets[i % nsets]
+        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
+                       dt_bias=S["bias"], initial_state=S["init"], return_final_state=final,
+                       final_out=fin, out=S["y"], workspace=ws, kernel_events=ev)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = Events(torch, steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(steps):
+        run(i, evs.handles[i])
+    torch.cuda.synchronize()
+    ms_ev = (time.perf_counter() - t1) * 1e3 / steps
+    init = w.init_std > 0
+    kern = {}
+    for k, name in enumerate(SLOTS):
+        us = 1e3 * evs.slot_ms(k, steps)
+        alg = bytes_kernel(name, b, l, h, p, n, g, Q, s, init=init, final=final)
+        kern[name] = {"avg_us": round(us, 2), "alg_bytes": alg,
+                      "GBs": round(alg / (us * 1e-6) / 1e9, 1),
+                      "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    balg = bytes_scan_alg(b, l, h, p, n, g, Q, s, init=init, final=final)
+    bmin = bytes_scan_min(b, l, h, p, n, g, Q, s, init=init, final=final)
+    res = {"workload": w.name, "batch": b, "seqlen": l, "heads": h, "head_dim": p,
+           "state_dim": n, "groups": g, "chunk": Q, "io": w.io, "init_state": init,
+           "final_state": final, "input_sets": nsets,
+           "ms_per_step": round(ms, 4), "ms_per_step_with_events": round(ms_ev, 4),
+           "tokens_per_s": round(b * l / (ms * 1e-3), 1),
+           "alg_bytes": balg, "min_bytes": bmin,
+           "t_roof_us": round(balg / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+           "frac_alg": round(balg / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4),
+           "frac_min": round(bmin / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3), 4),
+           "kernels": kern}
+    log("%s: %.4f ms/step (%.4f with events), %.4g tokens/s, frac_alg %.3f; %s" % (
+        w.name, ms, ms_ev, res["tokens_per_s"], res["frac_alg"],
+        json.dumps({k: v["avg_us"] for k, v in kern.items()})))
+    del sets, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ main ---
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--sets", type=int, default=4, help="input/output sets cycled through")
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--workloads", default=",".join(SCAN_WORKLOADS),
+                    help="scan workloads timed (the headline is always included)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-states", action="store_true",
                     help="skip the packed-sequence and state-output measurements")
@@ -150,9 +247,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the gradient-pass measurement")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-pairs", type=int, default=0, help="oracle sample size (0: all)")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="run a few scans and a plain copy of known size, for counter runs")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-probe", default="",
+                    help="workload: run a few scans of it, for counter runs, and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -160,7 +257,6 @@ def main():
               "MI355X (no multi-GPU path); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import mamba_ssd_chunked_chunk_amd as ssd
@@ -168,358 +264,195 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = syn.WORKLOADS["mamba2_130m"]
-    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
-    s = 2
-
-    def t(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-
-    log("generating %d input sets of %s" % (args.sets, w))
-    sets = []
-    host0 = None
-    for k in range(args.sets):
-        inp = syn.make_inputs(w.replace(seed=w.seed + 1000 * k))
-        if k == 0:
-            host0 = inp
-        sets.append(dict(x=t(inp["x"]), dt=t(inp["dt"]), A=t(inp["A"]), B=t(inp["B"]),
-                         C=t(inp["C"]), D=t(inp["D"]), bias=t(inp["dt_bias"]),
-                         y=torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev)))
-    wsb = ssd.workspace_bytes(b, l, h, p, n, g, Q)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-
-    def run(i):
-        S = sets[i % len(sets)]
-        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
-                       dt_bias=S["bias"], out=S["y"], workspace=ws)
-
-    log("warmup", args.warmup)
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
 
     if args.traffic_probe:
-        # three scans, three decode steps on a decode-shaped state, then the
-        # calibration kernels: a 256 MiB fill (writes only) and a sum over the
-        # same 256 MiB (reads only)
-        for i in range(3):
-            run(i)
-        wd = syn.WORKLOADS["decode_2p7b"]
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(wd.seed)
-        st = torch.randn(wd.batch, wd.heads, wd.state_dim, wd.head_dim, generator=gen,
-                         device=dev)
-        Ad = -torch.rand(wd.heads, generator=gen, device=dev) - 0.5
-        Dd = torch.ones(wd.heads, device=dev)
-        yd = torch.empty(wd.batch, wd.heads, wd.head_dim, dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            xd = torch.randn(wd.batch, wd.heads, wd.head_dim, generator=gen, device=dev).bfloat16()
-            dtd = torch.randn(wd.batch, wd.heads, generator=gen, device=dev).bfloat16()
-            Bd = torch.randn(wd.batch, wd.groups, wd.state_dim, generator=gen, device=dev).bfloat16()
-            Cd = torch.randn(wd.batch, wd.groups, wd.state_dim, generator=gen, device=dev).bfloat16()
-            ssd.step(st, xd, dtd, Ad, Bd, Cd, Dd, out=yd)
-        torch.cuda.synchronize()
-        cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-        for _ in range(3):
-            cal.fill_(1.0)
-        tot = 0.0
-        for _ in range(3):
-            tot += float(cal.sum())
-        torch.cuda.synchronize()
-        print(json.dumps({"traffic_probe": True, "calibration_bytes": cal.numel() * 4,
-                          "check": tot}))
+        w = syn.WORKLOADS[args.traffic_probe]
+        time_scan(torch, ssd, w, dev, steps=3, warmup=2)
+        print(json.dumps({"traffic_probe": w.name}))
         return
 
-    log("timed", args.steps, "steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    value = b * l * args.steps / (t1 - t0)
-    log("scan: %.3f ms/step, %.4g tokens/s" % (ms_step, value))
-
-    kern = kernel_times(ssd, torch, run, args.steps,
-                        lambda name: bytes_kernel(name, b, l, h, p, n, g, Q, s))
-    dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    dk = kern[dom]
+    names = [nm for nm in args.workloads.split(",") if nm]
+    if HEADLINE not in names:
+        names.append(HEADLINE)
+    results = {}
+    for nm in names:
+        w = syn.WORKLOADS[nm]
+        if nm == "decode_2p7b":
+            w = w.replace(name="decode_2p7b_prefill")
+        results[w.name] = time_scan(torch, ssd, w, dev, args.steps, args.warmup)
+    head = results[HEADLINE]
+    wh = syn.WORKLOADS[HEADLINE]
+    dom = max(SLOTS, key=lambda k: head["kernels"][k]["avg_us"])
+    dk = head["kernels"][dom]
     achieved = dk["alg_bytes"] / (dk["avg_us"] * 1e-6) / 1e9
-    for name, v in kern.items():
-        v["GBs"] = round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1)
-        v["avg_us"] = round(v["avg_us"], 2)
-    log("kernels:", json.dumps(kern))
-    traffic = measured_traffic("k_" + dom, w.name)
-    roofline = {"kernel": "k_" + dom, "bound": "hbm", "achieved": round(achieved, 1),
+    kname = {"chunk_state": "k_state16", "state_scan": "k_scan16", "chunk_out": "k_out16"}[dom]
+    roofline = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "alg_bytes_per_launch": dk["alg_bytes"],
-                "avg_launch_us": dk["avg_us"]}
-    balg = bytes_scan_alg(b, l, h, p, n, g, Q, s)
-    bmin = bytes_scan_min(b, l, h, p, n, g, Q, s)
-    t_roof = balg / (HBM_PEAK_GBS * 1e9)
-    scan_roof = {"bound": "hbm", "alg_bytes": balg, "min_bytes": bmin,
-                 "t_roof_us": round(t_roof * 1e6, 2), "t_step_us": round(ms_step * 1e3, 2),
-                 "frac_alg": round(t_roof / (ms_step * 1e-3), 4),
-                 "frac_min": round(bmin / (HBM_PEAK_GBS * 1e9) / (ms_step * 1e-3), 4),
-                 "kernels": kern}
+                "traffic": measured_traffic(kname, HEADLINE),
+                "alg_bytes_per_launch": dk["alg_bytes"], "avg_launch_us": dk["avg_us"],
+                "launches_timed": args.steps}
+    scan_roof = {"bound": "hbm", "alg_bytes": head["alg_bytes"], "min_bytes": head["min_bytes"],
+                 "t_roof_us": head["t_roof_us"], "t_step_us": round(head["ms_per_step"] * 1e3, 2),
+                 "frac_alg": head["frac_alg"], "frac_min": head["frac_min"],
+                 "kernels": head["kernels"]}
 
-    states = None
+    extra = {}
     if not args.no_states:
-        states = bench_states(args, torch, ssd, np, sets, ws, w, dev)
-
-    neighbors = None
+        extra["states"] = bench_states(args, torch, ssd, syn, dev)
     if not args.no_neighbors:
-        neighbors = bench_neighbors(args, torch, ssd, syn, np, dev)
-
-    backward = None
+        extra["neighbors"] = bench_neighbors(args, torch, ssd, syn, dev)
     if not args.no_backward:
-        backward = bench_backward(args, torch, ssd, np, sets, w, dev)
-
-    decode = None
-    if not args.no_decode:
-        decode = bench_decode(args, torch, ssd, syn, dev)
-
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(args, host0, w)
+        extra["backward"] = bench_backward(args, torch, ssd, syn, dev)
+    decode = None if args.no_decode else bench_decode(args, torch, ssd, syn, dev)
+    cpu = None if args.no_cpu else cpu_baseline(args, syn, wh)
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) x/B/C/dt, A=-exp(U[0,ln16]), "
                 "dt_bias=softplus^-1(loguniform[1e-3,0.1]), D=1, zero initial state)",
-        "config": {"workload": "mamba2_130m", "batch": b, "seqlen": l, "heads": h,
-                   "head_dim": p, "state_dim": n, "groups": g, "chunk": Q, "io": "bf16",
-                   "state": "fp32", "input_sets": args.sets},
+        "config": {"workload": HEADLINE, "batch": wh.batch, "seqlen": wh.seqlen,
+                   "heads": wh.heads, "head_dim": wh.head_dim, "state_dim": wh.state_dim,
+                   "groups": wh.groups, "chunk": wh.chunk, "io": "bf16", "state": "fp32",
+                   "input_sets": head["input_sets"]},
         "roofline": roofline,
         "scan_roofline": scan_roof,
-        "states": states,
-        "neighbors": neighbors,
-        "backward": backward,
+        "workloads": results,
         "decode": decode,
         "cpu_baseline": cpu,
     }
+    out.update(extra)
     print(json.dumps(out))
 
 
-def kernel_times(ssd, torch, run, steps, alg_bytes):
-    """Average duration of each scan kernel over `steps` calls of run(i),
-    from HIP events the library records on its launch stream, with the
-    kernel's algorithmic bytes and the rate they imply."""
-    ssd.trace_enable(True)
-    for name in KERNEL_IDS:
-        ssd.trace_read(name)
+# --------------------------------------------------------------- extras ----
+def _time_calls(torch, fn, calls, warm=3):
+    """Average ms of fn(i) over `calls` calls, each bracketed by events on
+    the current stream (one kernel per call)."""
+    for i in range(warm):
+        fn(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
     torch.cuda.synchronize()
-    for i in range(steps):
-        run(i)
+    t0 = time.perf_counter()
+    for i in range(calls):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
     torch.cuda.synchronize()
-    ssd.trace_enable(False)
-    kern = {}
-    for name in KERNEL_IDS:
-        tot, cnt = ssd.trace_read(name)
-        if cnt:
-            kern[name] = dict(avg_us=1e3 * tot / cnt, launches=cnt, alg_bytes=alg_bytes(name))
-    return kern
+    wall = (time.perf_counter() - t0) * 1e3 / calls
+    return wall, sum(a.elapsed_time(b) for a, b in evs) / calls
 
 
-def doc_index(np, rng, b, l, lo=32, hi=2048):
-    """Document index of packed rows: documents back to back, lengths
-    log-uniform in [lo, hi] tokens, the last one cut at the row's end."""
-    seq = np.zeros((b, l), np.int32)
-    for bi in range(b):
-        t = k = 0
-        while t < l:
-            m = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
-            seq[bi, t:t + m] = k
-            t += m
-            k += 1
-    return seq
-
-
-def bench_states(args, torch, ssd, np, sets, ws, w, dev):
-    """The scan with packed documents (a per-token document index) and with
-    the state after every chunk written, on the same workload and input sets
-    as the headline; and the state after every token (chunk 1) on one batch
-    row of it."""
+def bench_states(args, torch, ssd, syn, dev):
+    """The scan at the Mamba2-130m shape with packed documents (a per-token
+    document index), with the state after every chunk written, and the state
+    after every token (chunk 1) for one batch row."""
+    w = syn.WORKLOADS["mamba2_130m"]
     b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
-    s = 2
-    nc, _ = plan_sizes(b, l, h, p, n, g, Q)
-    rng = np.random.default_rng(w.seed + 77)
-    seqs = [torch.from_numpy(doc_index(np, rng, b, l)).to(dev) for _ in sets]
-    docs = sum(int(q[:, -1].sum()) + b for q in seqs) / len(seqs)
+    S = device_inputs(torch, w, dev, w.seed + 77)
+    ws = torch.empty(ssd.workspace_bytes(b, l, h, p, n, g, Q), dtype=torch.uint8, device=dev)
+    seq = torch.from_numpy(syn.doc_index(w.seed + 77, b, l)).to(dev)
+    nc = -(-l // Q)
     st_out = torch.empty((b, nc, h, n, p), dtype=torch.float32, device=dev)
     steps = max(args.steps // 2, 10)
 
-    def measure(tag, run, alg_extra):
-        for i in range(5):
-            run(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            run(i)
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
-        kern = kernel_times(ssd, torch, run, steps,
-                            lambda k: bytes_kernel(k, b, l, h, p, n, g, Q, s,
-                                                   states=tag == "chunk_states")
-                            + alg_extra.get(k, 0))
-        for v in kern.values():
-            v["GBs"] = round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1)
-            v["avg_us"] = round(v["avg_us"], 2)
-        log("%s: %.4f ms/step %s" % (tag, ms, json.dumps(kern)))
-        return {"value": round(b * l / (ms * 1e-3), 1), "unit": "tokens/s",
-                "ms_per_step": round(ms, 4), "kernels": kern}
-
-    def run_packed(i):
-        S = sets[i % len(sets)]
+    def packed(i):
         ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
-                       dt_bias=S["bias"], out=S["y"], workspace=ws, seq_idx=seqs[i % len(seqs)])
+                       dt_bias=S["bias"], out=S["y"], workspace=ws, seq_idx=seq)
 
-    def run_states(i):
-        S = sets[i % len(sets)]
+    def states(i):
         ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
-                       dt_bias=S["bias"], out=S["y"], workspace=ws,
-                       return_chunk_states=True, chunk_states_out=st_out)
-
-    # the document index is read by the chunk-state pass and the chunk output
-    # (4 bytes per token each); every chunk's state is written once (fp32)
-    packed = measure("packed", run_packed, {"chunk_state": 4 * b * l, "chunk_out": 4 * b * l})
-    packed["documents_per_step"] = round(docs, 1)
-    packed["doc_lengths"] = "log-uniform in [32, 2048] tokens, seeded"
-    chunks = measure("chunk_states", run_states, {})
-
-    # the state after every token: chunk 1, one batch row, each token's
-    # state written in fp32 (the rate that bounds this mode)
-    S = sets[0]
+                       dt_bias=S["bias"], out=S["y"], workspace=ws, return_chunk_states=True,
+                       chunk_states_out=st_out)
+    res = {}
+    for name, fn in (("packed", packed), ("chunk_states", states)):
+        wall, _ = _time_calls(torch, fn, steps)
+        res[name] = {"value": round(b * l / (wall * 1e-3), 1), "unit": "tokens/s",
+                     "ms_per_step": round(wall, 4)}
+        log("%s: %.4f ms/step" % (name, wall))
+    res["packed"]["documents_per_step"] = int(seq[:, -1].sum()) + b
     x1, dt1, B1, C1 = S["x"][:1], S["dt"][:1], S["B"][:1], S["C"][:1]
     y1 = torch.empty((1, l, h, p), dtype=torch.bfloat16, device=dev)
-    tok_states = torch.empty((1, l, h, n, p), dtype=torch.float32, device=dev)
+    tok = torch.empty((1, l, h, n, p), dtype=torch.float32, device=dev)
     ws1 = torch.empty(ssd.workspace_bytes(1, l, h, p, n, g, 1), dtype=torch.uint8, device=dev)
 
-    def run_tok(i):
+    def per_token(i):
         ssd.chunk_scan(x1, dt1, S["A"], B1, C1, S["D"], chunk_size=1, dt_bias=S["bias"],
-                       out=y1, workspace=ws1, return_chunk_states=True,
-                       chunk_states_out=tok_states)
-    for i in range(3):
-        run_tok(i)
-    torch.cuda.synchronize()
-    nt = max(steps // 10, 5)
-    t0 = time.perf_counter()
-    for i in range(nt):
-        run_tok(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / nt
+                       out=y1, workspace=ws1, return_chunk_states=True, chunk_states_out=tok)
+    wall, _ = _time_calls(torch, per_token, max(steps // 10, 5))
     wbytes = l * h * n * p * 4
-    log("per-token states: %.3f ms per row, %.0f GB/s of state written" %
-        (ms, wbytes / (ms * 1e-3) / 1e9))
-    per_token = {"value": round(l / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_call": round(ms, 4),
-                 "config": {"batch": 1, "seqlen": l, "heads": h, "chunk": 1},
-                 "state_bytes_written": wbytes,
-                 "state_write_GBs": round(wbytes / (ms * 1e-3) / 1e9, 1)}
-    return {"packed": packed, "chunk_states": chunks, "per_token": per_token}
-
-
-def bench_neighbors(args, torch, ssd, syn, np, dev):
-    """The steps around the scan at the 130m mixer's shape (8 x 2048 tokens,
-    24 heads of 64, state 128, 1 group, bf16): the width-4 causal conv1d +
-    SiLU + split of the 1792 projection channels, and the silu(z) gate with
-    one RMS norm over the 1536 channels.  Each is one pass over HBM; its
-    rate is priced on those bytes."""
-    b, l, h, p, n, g, K = 8, 2048, 24, 64, 128, 1, 4
-    ch = h * p + 2 * g * n
-    steps = max(args.steps // 2, 10)
-    sets = []
-    for k in range(2):
-        c = syn.conv_case(900 + k, b, l, h, p, n, g, K, io="bf16", with_init=False)
-        nc = syn.norm_case(950 + k, b * l, h * p, io="bf16")
-
-        def t16(a):
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        sets.append(dict(xbc=t16(c["xbc"]), w=torch.from_numpy(c["weight"]).to(dev),
-                         bias=torch.from_numpy(c["bias"]).to(dev), y=t16(nc["y"]), z=t16(nc["z"]),
-                         nw=torch.from_numpy(nc["weight"]).to(dev),
-                         out=(torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev),
-                              torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev),
-                              torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev)),
-                         nout=torch.empty((b * l, h * p), dtype=torch.bfloat16, device=dev)))
-
-    def conv(i):
-        S = sets[i % 2]
-        ssd.conv1d_silu(S["xbc"], S["w"], h, p, n, g, bias=S["bias"], out=S["out"])
-
-    def norm(i):
-        S = sets[i % 2]
-        ssd.gated_norm(S["y"], S["z"], S["nw"], eps=1e-5, out=S["nout"])
-
-    res = {}
-    for name, fn, tid, alg in (
-            ("conv1d_silu", conv, "conv1d", 2 * b * l * ch * 2 + ch * (K + 1) * 4),
-            ("gated_norm", norm, "gated_norm", 3 * b * l * h * p * 2 + h * p * 4)):
-        for i in range(5):
-            fn(i)
-        torch.cuda.synchronize()
-        ssd.trace_enable(True)
-        ssd.trace_read(tid)
-        for i in range(steps):
-            fn(i)
-        torch.cuda.synchronize()
-        ssd.trace_enable(False)
-        tot, cnt = ssd.trace_read(tid)
-        us = 1e3 * tot / cnt
-        gbs = alg / (us * 1e-6) / 1e9
-        log("%s: %.2f us, %.0f GB/s" % (name, us, gbs))
-        res[name] = {"avg_launch_us": round(us, 2), "alg_bytes_per_launch": alg,
-                     "tokens_per_s": round(b * l / (us * 1e-6), 1),
-                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
-    res["config"] = {"workload": "mamba2_130m mixer", "batch": b, "seqlen": l, "heads": h,
-                     "head_dim": p, "state_dim": n, "groups": g, "conv_width": K,
-                     "norm_groups": 1, "io": "bf16"}
+    res["per_token"] = {"value": round(l / (wall * 1e-3), 1), "unit": "tokens/s",
+                        "ms_per_call": round(wall, 4), "state_bytes_written": wbytes,
+                        "state_write_GBs": round(wbytes / (wall * 1e-3) / 1e9, 1)}
+    log("per-token states: %.3f ms per row" % wall)
+    res["config"] = {"workload": "mamba2_130m", "doc_lengths": "log-uniform in [32, 2048]"}
     return res
 
 
-def bench_backward(args, torch, ssd, np, sets, w, dev):
-    """The gradient pass (ssd_chunk_scan_bwd) on the headline workload and
-    input sets, with a final-state cotangent: tokens/s, and the call's time
-    against the bytes any gradient pass must move (inputs x, dt, B, C, dy
-    read once; dx, ddt, dB, dC written once; the final-state cotangent and
-    d init once)."""
-    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
+def bench_neighbors(args, torch, ssd, syn, dev):
+    """The steps around the scan at the 130m mixer's shape (8 x 2048 tokens,
+    24 heads of 64, state 128, 1 group, bf16): the width-4 causal conv1d +
+    SiLU + split of the 1792 projection channels, and the silu(z) gate with
+    one RMS norm over the 1536 channels."""
+    b, l, h, p, n, g, K = 8, 2048, 24, 64, 128, 1, 4
+    ch = h * p + 2 * g * n
     gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed + 99)
-    dys = [torch.randn((b, l, h, p), generator=gen, device=dev).bfloat16() for _ in sets]
+    gen.manual_seed(900)
+    xbc = torch.randn(b, l, ch, generator=gen, device=dev).bfloat16()
+    wt = (torch.rand(ch, K, generator=gen, device=dev) * 2 - 1) / math.sqrt(K)
+    bias = (torch.rand(ch, generator=gen, device=dev) * 2 - 1) / math.sqrt(K)
+    y = torch.randn(b * l, h * p, generator=gen, device=dev).bfloat16()
+    z = torch.randn(b * l, h * p, generator=gen, device=dev).bfloat16()
+    nw = 1 + 0.1 * torch.randn(h * p, generator=gen, device=dev)
+    outs = (torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev),
+            torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev),
+            torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev))
+    nout = torch.empty_like(y)
+    steps = max(args.steps // 2, 10)
+    res = {}
+    for name, fn, alg in (
+            ("conv1d_silu", lambda i: ssd.conv1d_silu(xbc, wt, h, p, n, g, bias=bias, out=outs),
+             2 * b * l * ch * 2 + ch * (K + 1) * 4),
+            ("gated_norm", lambda i: ssd.gated_norm(y, z, nw, eps=1e-5, out=nout),
+             3 * b * l * h * p * 2 + h * p * 4)):
+        _, ms = _time_calls(torch, fn, steps)
+        gbs = alg / (ms * 1e-3) / 1e9
+        log("%s: %.2f us, %.0f GB/s" % (name, ms * 1e3, gbs))
+        res[name] = {"avg_launch_us": round(ms * 1e3, 2), "alg_bytes_per_launch": alg,
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    res["config"] = {"workload": "mamba2_130m mixer", "conv_width": K, "norm_groups": 1}
+    return res
+
+
+def bench_backward(args, torch, ssd, syn, dev):
+    """The gradient pass (ssd_chunk_scan_bwd) at the Mamba2-130m shape with a
+    final-state cotangent, against the bytes any gradient pass must move."""
+    w = syn.WORKLOADS["mamba2_130m"]
+    b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
+    S = device_inputs(torch, w, dev, w.seed + 99)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed + 98)
+    dy = torch.randn((b, l, h, p), generator=gen, device=dev).bfloat16()
     dfin = torch.randn((b, h, n, p), generator=gen, device=dev)
     wsb = int(ssd._lib.load().ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, Q))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    steps = max(args.steps // 10, 5)
 
     def run(i):
-        S = sets[i % len(sets)]
-        ssd.chunk_scan_bwd(S["x"], S["dt"], S["A"], S["B"], S["C"], dys[i % len(dys)], D=S["D"],
-                           chunk_size=Q, dt_bias=S["bias"], d_final=dfin, workspace=ws)
-    for i in range(3):
-        run(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        run(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+        ssd.chunk_scan_bwd(S["x"], S["dt"], S["A"], S["B"], S["C"], dy, D=S["D"], chunk_size=Q,
+                           dt_bias=S["bias"], d_final=dfin, workspace=ws)
+    wall, _ = _time_calls(torch, run, max(args.steps // 10, 5))
     s = 2
     min_bytes = (2 * (2 * b * l * h * p * s + 2 * b * l * g * n * s + b * l * h * s)
                  + 2 * b * h * n * p * 4)
-    gbs = min_bytes / (ms * 1e-3) / 1e9
-    log("backward: %.3f ms per call, %.4g tokens/s, %.0f GB/s on the minimal bytes" %
-        (ms, b * l / (ms * 1e-3), gbs))
-    return {"metric": "gradient pass tokens/s", "value": round(b * l / (ms * 1e-3), 1),
-            "unit": "tokens/s", "ms_per_call": round(ms, 4), "calls": steps,
-            "workspace_bytes": wsb, "min_bytes": min_bytes,
+    gbs = min_bytes / (wall * 1e-3) / 1e9
+    log("backward: %.3f ms per call" % wall)
+    return {"metric": "gradient pass tokens/s", "value": round(b * l / (wall * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_call": round(wall, 4), "workspace_bytes": wsb,
+            "min_bytes": min_bytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
             "config": {"workload": "mamba2_130m", "io": "bf16", "d_final": True,
@@ -531,22 +464,17 @@ def bench_decode(args, torch, ssd, syn, dev):
     fp32 state initialised by a 1024-token chunk-scan prefill."""
     w = syn.WORKLOADS["decode_2p7b"]
     b, l, h, p, n, g = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups
-    head = syn.make_inputs(w.replace(seqlen=1), batch=1)
-    A = torch.from_numpy(head["A"]).to(dev)
-    D = torch.from_numpy(head["D"]).to(dev)
-    bias = torch.from_numpy(head["dt_bias"]).to(dev)
+    S = device_inputs(torch, w, dev, w.seed)
+    _, st = ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=w.chunk,
+                           dt_bias=S["bias"], return_final_state=True)
+    A, D, bias = S["A"], S["D"], S["bias"]
+    del S
     gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed)
+    gen.manual_seed(w.seed + 5)
+    K = args.decode_steps
 
     def rnd(*shape):
-        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).bfloat16()
-
-    log("decode prefill", b, "x", l)
-    x, dt, B, C = rnd(b, l, h, p), rnd(b, l, h), rnd(b, l, g, n), rnd(b, l, g, n)
-    _, st = ssd.chunk_scan(x, dt, A, B, C, D, chunk_size=w.chunk, dt_bias=bias,
-                           return_final_state=True)
-    del x, dt, B, C
-    K = args.decode_steps
+        return torch.randn(*shape, generator=gen, device=dev).bfloat16()
     xs, dts, Bs, Cs = rnd(K, b, h, p), rnd(K, b, h), rnd(K, b, g, n), rnd(K, b, g, n)
     y = torch.empty((b, h, p), dtype=torch.bfloat16, device=dev)
     for k in range(3):
@@ -556,19 +484,12 @@ def bench_decode(args, torch, ssd, syn, dev):
     for k in range(K):
         ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    rate = K / (t1 - t0)
-    ssd.trace_enable(True)
-    ssd.trace_read("step")
-    for k in range(K):
-        ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
-    torch.cuda.synchronize()
-    ssd.trace_enable(False)
-    tot, cnt = ssd.trace_read("step")
-    avg_us = 1e3 * tot / cnt
+    rate = K / (time.perf_counter() - t0)
+    _, ms = _time_calls(torch, lambda k: ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D,
+                                                  dt_bias=bias, out=y), K, warm=0)
     alg = bytes_step(b, h, p, n, g, 2)
-    achieved = alg / (avg_us * 1e-6) / 1e9
-    log("decode: %.1f steps/s, kernel %.2f us, %.0f GB/s" % (rate, avg_us, achieved))
+    achieved = alg / (ms * 1e-3) / 1e9
+    log("decode: %.1f steps/s, kernel %.2f us, %.0f GB/s" % (rate, ms * 1e3, achieved))
     return {"metric": "decode steps/s", "value": round(rate, 1), "unit": "steps/s",
             "tokens_per_s": round(rate * b, 1), "steps": K,
             "config": {"workload": "decode_2p7b", "batch": b, "heads": h, "head_dim": p,
@@ -578,36 +499,53 @@ def bench_decode(args, torch, ssd, syn, dev):
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("k_step", "decode_2p7b"),
-                         "alg_bytes_per_launch": alg, "avg_launch_us": round(avg_us, 2)}}
+                         "alg_bytes_per_launch": alg, "avg_launch_us": round(ms * 1e3, 2)}}
 
 
-def cpu_baseline(args, inp, w, min_seconds=10.0, max_passes=500):
-    """The fp64 oracle on the host cores over the same workload (all its
-    (batch, head) pairs and tokens), repeated until about min_seconds of wall
-    time have passed, reported in tokens/s (a token being one position across
-    all heads)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(args, syn, w):
+    """The fp64 oracle as it stands, on the host cores, over a bounded sample
+    of the headline workload: 16 of its 64 heads over its first 16384
+    tokens, repeated for about --cpu-seconds of wall time; and one thread
+    over 2 heads of the same tokens.  Reported in the headline's unit
+    (a token being one position across all 64 heads)."""
     import oracle
     oracle.build()
-    pairs_all = [(bb, hh) for bb in range(w.batch) for hh in range(w.heads)]
-    k = args.cpu_pairs or len(pairs_all)
-    pairs = pairs_all[:k]
+    L, heads = 16384, 16
+    inp = syn.make_inputs(w, seqlen=L)
+    pairs = [(0, hh) for hh in range(0, w.heads, w.heads // heads)][:heads]
     cores = oracle.default_threads()
-    log("oracle on %d pairs, %d threads, >= %.0f s" % (len(pairs), cores, min_seconds))
-    passes = 0
-    t0 = time.perf_counter()
-    while passes < max_passes:
-        oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
-                    inp["dt_bias"], io=inp["io"], pairs=pairs, nthreads=cores)
-        passes += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt_s = time.perf_counter() - t0
-    tok = passes * len(pairs) * w.seqlen / w.heads
-    log("oracle: %d passes in %.2f s" % (passes, dt_s))
-    return {"value": round(tok / dt_s, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d pass(es) over %d of %d (batch, head) pairs x %d tokens of the "
-                      "mamba2_130m workload, %.1f s wall" % (passes, len(pairs),
-                                                             len(pairs_all), w.seqlen, dt_s)}
+
+    def rate(prs, nthreads, seconds):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                        inp["dt_bias"], io=inp["io"], pairs=prs, nthreads=nthreads)
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt_s = time.perf_counter() - t0
+        return passes * len(prs) * L / w.heads / dt_s, passes, dt_s
+    v, passes, dt_s = rate(pairs, cores, args.cpu_seconds)
+    v1, p1, d1 = rate(pairs[:2], 1, max(args.cpu_seconds / 4, 2.0))
+    log("oracle: %.4g tokens/s on %d threads, %.4g on one" % (v, cores, v1))
+    return {"value": round(v, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "single_thread_value": round(v1, 1),
+            "sample": "%d pass(es) over %d of %d heads x %d of %d tokens of the %s workload "
+                      "(%.1f s wall); single thread: %d pass(es) over 2 heads (%.1f s)"
+                      % (passes, len(pairs), w.heads, L, w.seqlen, w.name, dt_s, p1, d1)}
 
 
 if __name__ == "__main__":

@@ -7,8 +7,8 @@
  * step (ssd_step), the steps just before and after the scan in a Mamba-2
  * mixer (ssd_conv1d_silu, ssd_gated_norm), the deterministic gradient pass
  * (ssd_chunk_scan_bwd), and the pieces of a sequence split into segments
- * (ssd_segment_log_decay, ssd_combine_segments); plus workspace queries,
- * status strings and kernel timing.
+ * (ssd_segment_log_decay, ssd_combine_segments); plus workspace queries
+ * and status strings.
  *
  * The scan (nnterp guide, "Mamba-2" page, opening section): per head the
  * state h is a state_dim x head_dim matrix, and every token t does
@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 /* io dtype of x, dt, B, C and y */
 enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
@@ -104,17 +104,17 @@ enum ssd_status {
  * batch == 0 or seqlen == 0 is valid: nothing is computed except that
  * final_state (if given) receives init_state, or zeros.
  *
- * Precision (bf16 io): the matrix products take fp16 operands with fp32
- * accumulation.  x, B and C convert to fp16 exactly while their magnitudes
- * lie in [2^-14, 65504]; smaller magnitudes keep fewer significant bits
- * (below 2^-24 they count as zero) and larger ones saturate at 65504.  The
- * decay-weighted x, the masked scores and the carried state are rounded to
- * fp16 (toward zero) as operands; the state entering each chunk is kept in
- * the workspace as fp16 (rounded to nearest), the operand it feeds, and so
- * is every chunk's own state, times a power-of-two scale per (batch, chunk,
- * head) that puts its largest magnitude in [2^14, 2^15) (no overflow; 11
- * bits relative to that maximum).  The recurrence across chunks, all sums
- * and decays, and final_state are fp32.
+ * Precision (bf16 io): the matrix products run on bf16 matrix-core
+ * instructions with fp32 accumulation.  x, B and C enter them exactly as
+ * given (any finite bf16 value).  Each operand formed inside the scan (the
+ * decay-weighted x, the masked scores with the skip term, the carried state)
+ * is an fp32 value v split into two bf16 terms, bf16(v) and bf16(v - bf16(v)),
+ * both multiplied: 16 significant bits with fp32's exponent range.  Every
+ * chunk's own state and the state entering every chunk are kept in the
+ * workspace as fp16 times a power of two per (batch, chunk, head) chosen so
+ * that nothing overflows (11 significant bits relative to the largest
+ * magnitude).  The recurrence across chunks, all sums and decays, and
+ * final_state are fp32; y is rounded to nearest even.
  * fp32 io uses fp32 operands and fp32 boundary states throughout.
  */
 int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
@@ -147,8 +147,17 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
  *                 token, and the last entry is the final state).  For a
  *                 chunk shorter than 32 tokens the states are stepped token
  *                 by token (fp32) from the states at the computed chunks'
- *                 boundaries, in one extra launch (SSD_K_TOKEN_STATES); the
- *                 last entry then equals final_state up to rounding only.
+ *                 boundaries, in one extra launch; the last entry then
+ *                 equals final_state up to rounding only.
+ *   kernel_events NULL, or 8 hipEvent_t created by the caller (hipEventCreate):
+ *                 entries 2k and 2k + 1 receive the start and end of the
+ *                 call's kernel in slot k -- 0: the chunk-state pass, 1: the
+ *                 serial pass over chunks, 2: the chunk output, 3: the
+ *                 per-token state fill (only for chunks shorter than 32
+ *                 tokens with chunk_states) -- taken from the dispatch
+ *                 itself, so an event pair measures that kernel alone.
+ *                 Entries may be NULL; a slot the call does not launch is not
+ *                 recorded.  The events stay owned by the caller.
  */
 int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const void *B,
                           const void *C, const float *D, const float *dt_bias,
@@ -157,22 +166,23 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
                           float *final_state, float *chunk_states, int64_t batch,
                           int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
                           int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
-                          size_t workspace_bytes, void *hip_stream);
+                          size_t workspace_bytes, void *hip_stream, void *const *kernel_events);
 
 /*
  * Bytes of workspace ssd_chunk_scan needs for these sizes (a pure function
  * of its arguments; 0 for invalid sizes).  Layout, in order, each part
- * 256-byte aligned: per-row cumulative log2 decay and processed time step
- * [batch, heads, padded seqlen] fp32 each (cumulative log2 decay inside
- * 32-row blocks, processed time step, weight in the state at the block end);
+ * 256-byte aligned (the same for both io dtypes; parts an io dtype does not
+ * use are left alone): four per-row arrays [batch, heads, padded seqlen] fp32
+ * (fp32 io: cumulative log2 decay inside 32-row blocks, processed time step,
+ * weight in the state at the block end, packed-sequence reset row);
  * chunk-boundary states [batch, chunks, heads, head_dim, state_dim]
- * (transposed; fp16 for bf16 io, fp32 for fp32 io, room reserved for fp32);
- * every chunk's own state from zero, same shape, fp32; the log2 decay of
- * every chunk [batch, heads, chunks] fp32; C and B of every 32-row block of
- * every (batch, chunk, group) converted to fp16 and ordered as the chunk
- * output holds them on chip ([batch, chunks, groups, ceil(chunk / 32)]
- * blocks of 2 x 32 x state_dim elements; written and read with bf16 io
- * only).  The layout is the same for both io dtypes.
+ * (transposed; fp32 for fp32 io, scaled fp16 for bf16 io); every chunk's own
+ * state from zero, same shape and types; the log2 decay of every chunk
+ * [batch, heads, chunks] fp32; the chunk states' largest magnitudes (bf16)
+ * or scales, same shape; for chunks shorter than 32 tokens with
+ * chunk_states, the fp32 states after the computed chunks; the boundary
+ * states' scales [batch, heads, chunks] and the initial state's largest
+ * magnitude per (batch, head) (bf16 io).  Contents on entry are ignored.
  */
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim,
@@ -292,9 +302,8 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
  * arithmetic fp32 (the scans use the fp32 path whatever the io dtype), the
  * running sums behind ddt, dA, d dt_bias and dD in fp64.  16-byte
  * alignment for x, B, C, dy, dx, dB, dC and the states, element alignment
- * for the rest; SSD_ERR_ALIGN otherwise.  Several launches:
- * three fp32 chunk scans (traced as SSD_K_CHUNK_STATE .. SSD_K_CHUNK_OUT)
- * and the pass's own kernels (SSD_K_BWD_AUX).
+ * for the rest; SSD_ERR_ALIGN otherwise.  Several launches: three fp32
+ * chunk scans and the pass's own kernels.
  */
 int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const void *B,
                            const void *C, const float *D, const float *dt_bias,
@@ -355,30 +364,6 @@ const char *ssd_status_string(int32_t status);
 
 /* SSD_ABI_VERSION of the built library. */
 int32_t ssd_abi_version(void);
-
-/*
- * Kernel timing for measurement.  While enabled, every kernel the two calls
- * launch is bracketed by a pair of HIP events recorded on the launch stream
- * (at most 65536 pairs are kept; later launches are not timed).
- * ssd_trace_read synchronises those events and returns, for kernel id
- * `kernel` (SSD_K_*), the summed milliseconds and the launch count, then
- * clears that kernel's record.  Not thread-safe with concurrent scan calls.
- */
-enum ssd_kernel_id {
-    SSD_K_PREP = 0,        /* reserved: the per-row time step, cumulative log decay
-                              and state weights are computed inside SSD_K_CHUNK_STATE */
-    SSD_K_CHUNK_STATE = 1, /* per-row values; every chunk's state from zero, in parallel */
-    SSD_K_STATE_SCAN = 2,  /* serial pass over chunks: boundary and final states */
-    SSD_K_CHUNK_OUT = 3,   /* intra-chunk product, state read-out, skip term */
-    SSD_K_STEP = 4,        /* decode step */
-    SSD_K_TOKEN_STATES = 5, /* states after chunks shorter than 32 tokens, token by token */
-    SSD_K_CONV1D = 6,      /* ssd_conv1d_silu */
-    SSD_K_GATED_NORM = 7,  /* ssd_gated_norm */
-    SSD_K_BWD_AUX = 8,     /* ssd_chunk_scan_bwd's own kernels (its scans count as above) */
-    SSD_K_COUNT = 9
-};
-int32_t ssd_trace_enable(int32_t on);
-int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches);
 
 #ifdef __cplusplus
 }

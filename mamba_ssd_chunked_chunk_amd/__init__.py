@@ -25,7 +25,7 @@ from ._lib import LibraryMissing, load, status_string  # noqa: F401
 __all__ = ["chunk_scan", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
            "segment_log_decay", "combine_segments",
            "workspace_bytes", "abi_version",
-           "trace_enable", "trace_read", "LibraryMissing", "SsdError"]
+           "LibraryMissing", "SsdError"]
 
 
 class SsdError(RuntimeError):
@@ -78,7 +78,7 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
                dt_softplus: bool = True, dt_limit: Tuple[float, float] = (0.0, math.inf),
                initial_state=None, return_final_state: bool = False, out=None,
                final_out=None, workspace=None, seq_idx=None,
-               return_chunk_states: bool = False, chunk_states_out=None):
+               return_chunk_states: bool = False, chunk_states_out=None, kernel_events=None):
     """The chunked SSD scan of a whole sequence (ssd_chunk_scan_ex).
 
     Returns y, followed by final_state when return_final_state and by the
@@ -87,7 +87,9 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
     [b, l] int32: packed documents, a zero state wherever the index changes
     from one token to the next.  `out`, `final_out`, `chunk_states_out` and
     `workspace` (uint8, at least workspace_bytes(...)) may be given to avoid
-    allocations; final_out may alias initial_state.
+    allocations; final_out may alias initial_state.  kernel_events: None, or
+    8 raw hipEvent_t handles (ints; 0 for none) that receive the start and
+    end of the call's kernel in each slot of _lib.EVENT_SLOTS.
     """
     torch = _torch()
     lib = load()
@@ -128,12 +130,18 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
     ws = workspace
     if ws is None:
         ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _check("workspace", ws, torch.uint8, None, dev)
+    ev = None
+    if kernel_events is not None:
+        if len(kernel_events) != 2 * len(_lib.EVENT_SLOTS):
+            raise ValueError("kernel_events must hold %d handles" % (2 * len(_lib.EVENT_SLOTS)))
+        ev = (ctypes.c_void_p * len(kernel_events))(*[int(e) or None for e in kernel_events])
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssd_chunk_scan_ex(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
         int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
         _ptr(initial_state), _ptr(seq_idx), _ptr(y), _ptr(fin), _ptr(states), b, l, h, p, n,
-        g, int(chunk_size), _io_code(io), _ptr(ws), ws.numel() * ws.element_size(), stream)
+        g, int(chunk_size), _io_code(io), _ptr(ws), ws.numel() * ws.element_size(), stream, ev)
     if rc != 0:
         raise SsdError("ssd_chunk_scan_ex", rc)
     if not return_final_state and not return_chunk_states:
@@ -182,6 +190,7 @@ def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, chunk_size: int = 256, dt_bias=No
     wsb = int(lib.ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, int(chunk_size)))
     ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8,
                                                              device=dev)
+    _check("workspace", ws, torch.uint8, None, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.ssd_chunk_scan_bwd(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
@@ -344,17 +353,3 @@ def gated_norm(y, z=None, weight=None, group_size: Optional[int] = None, eps: fl
     if rc != 0:
         raise SsdError("ssd_gated_norm", rc)
     return o
-
-
-def trace_enable(on: bool = True) -> None:
-    load().ssd_trace_enable(1 if on else 0)
-
-
-def trace_read(kernel: str):
-    """(total milliseconds, launches) recorded for `kernel` since the last read."""
-    ms = ctypes.c_double()
-    cnt = ctypes.c_int64()
-    rc = load().ssd_trace_read(_lib.KERNELS[kernel], ctypes.byref(ms), ctypes.byref(cnt))
-    if rc != 0:
-        raise SsdError("ssd_trace_read", rc)
-    return ms.value, cnt.value

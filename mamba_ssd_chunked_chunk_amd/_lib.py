@@ -17,15 +17,14 @@ SSD_ERR_WORKSPACE = -4
 SSD_ERR_ALIGN = -5
 SSD_ERR_HIP = -6
 
-KERNELS = {"prep": 0, "chunk_state": 1, "state_scan": 2, "chunk_out": 3, "step": 4,
-           "token_states": 5, "conv1d": 6, "gated_norm": 7, "bwd_aux": 8}
+# kernel_events slots of ssd_chunk_scan_ex
+EVENT_SLOTS = ("chunk_state", "state_scan", "chunk_out", "token_states")
 
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",
            "ssd_conv1d_silu", "ssd_gated_norm", "ssd_chunk_scan_bwd",
            "ssd_segment_log_decay", "ssd_combine_segments",
-           "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version",
-           "ssd_trace_enable", "ssd_trace_read")
+           "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version")
 
 _lib = None
 
@@ -52,7 +51,7 @@ def load() -> ctypes.CDLL:
     lib.ssd_chunk_scan_ex.restype = I32
     lib.ssd_chunk_scan_ex.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P, P, P,
                                       I64, I64, I64, I64, I64, I64, I64, I32,
-                                      P, ctypes.c_size_t, P]
+                                      P, ctypes.c_size_t, P, P]
     lib.ssd_chunk_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_workspace_bytes.argtypes = [I64] * 7
     lib.ssd_step.restype = I32
@@ -78,11 +77,6 @@ def load() -> ctypes.CDLL:
     lib.ssd_status_string.argtypes = [I32]
     lib.ssd_abi_version.restype = I32
     lib.ssd_abi_version.argtypes = []
-    lib.ssd_trace_enable.restype = I32
-    lib.ssd_trace_enable.argtypes = [I32]
-    lib.ssd_trace_read.restype = I32
-    lib.ssd_trace_read.argtypes = [I32, ctypes.POINTER(ctypes.c_double),
-                                   ctypes.POINTER(ctypes.c_int64)]
     _lib = lib
     return lib
 

@@ -4,9 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
-#include <mutex>
-#include <new>
-#include <vector>
+#include <atomic>
 
 #include "../../include/ssd.h"
 #include "ssd_device.hpp"
@@ -14,62 +12,31 @@
 
 namespace ssd {
 
-// ------------------------------------------------------------ timing hooks --
-namespace {
-struct TraceRec {
-    int kernel;
-    hipEvent_t start, end;
-};
-struct Trace {
-    std::mutex mu;
-    bool on = false;
-    std::vector<TraceRec> recs;
-    std::vector<hipEvent_t> pool;
-    int open = -1;  // index of the record whose end is pending
-};
-Trace &tr() {
-    static Trace *t = new Trace();  // never destroyed: events outlive static teardown
-    return *t;
-}
-constexpr size_t kMaxRecs = 65536;
-
-hipEvent_t take_event(Trace &t) {
-    if (!t.pool.empty()) {
-        hipEvent_t e = t.pool.back();
-        t.pool.pop_back();
-        return e;
-    }
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    return e;
-}
-}  // namespace
-
-void trace_begin(int kernel, hipStream_t s) {
-    Trace &t = tr();
-    std::lock_guard<std::mutex> g(t.mu);
-    t.open = -1;
-    if (!t.on || t.recs.size() >= kMaxRecs) return;
-    TraceRec r{kernel, take_event(t), take_event(t)};
-    if (!r.start || !r.end) return;
-    if (hipEventRecord(r.start, s) != hipSuccess) return;
-    t.recs.push_back(r);
-    t.open = (int)t.recs.size() - 1;
-}
-
-void trace_end(int kernel, hipStream_t s) {
-    Trace &t = tr();
-    std::lock_guard<std::mutex> g(t.mu);
-    if (t.open < 0 || t.recs[t.open].kernel != kernel) return;
-    (void)hipEventRecord(t.recs[t.open].end, s);
-    t.open = -1;
+// ------------------------------------------------------ device queries ---
+// Compute units per device, queried once per device id (the only state the
+// library keeps; thread-safe).
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 1;
+    cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 // -------------------------------------------------------------- dispatch ---
 template <typename IO>
 static hipError_t dispatch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
-#define SSD_CASE(PP, NN) \
-    if (pl.p == PP && pl.n == NN) return launch_scan<IO, PP, NN>(pl, a, s);
+#define SSD_CASE(PP, NN)                                                       \
+    if (pl.p == PP && pl.n == NN) {                                            \
+        if constexpr (sizeof(IO) == 2) return launch_scan16<PP, NN>(pl, a, s); \
+        else return launch_scan<IO, PP, NN>(pl, a, s);                         \
+    }
 #define SSD_ROW(PP) SSD_CASE(PP, 32) SSD_CASE(PP, 64) SSD_CASE(PP, 128)
     SSD_ROW(16) SSD_ROW(32) SSD_ROW(64) SSD_ROW(128)
 #undef SSD_ROW
@@ -148,7 +115,7 @@ int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void
     return ssd_chunk_scan_ex(x, dt, A, B, C, D, dt_bias, dt_softplus, dt_min, dt_max,
                              init_state, nullptr, y, final_state, nullptr, batch, seqlen,
                              heads, head_dim, state_dim, groups, chunk, io_dtype, workspace,
-                             workspace_bytes, hip_stream);
+                             workspace_bytes, hip_stream, nullptr);
 }
 
 int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const void *B,
@@ -158,7 +125,7 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
                           float *final_state, float *chunk_states, int64_t batch,
                           int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
                           int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
-                          size_t workspace_bytes, void *hip_stream) {
+                          size_t workspace_bytes, void *hip_stream, void *const *kernel_events) {
     if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
         groups <= 0 || chunk <= 0 || heads % groups != 0)
@@ -210,6 +177,7 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
     ScanArgs a{x, dt, B, C, A, D, dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max,
                init_state, y, final_state, static_cast<char *>(workspace), seq_idx,
                chunk_states};
+    a.ev = kernel_events;
     // caller chunks shorter than the computed ones: the scan keeps the states
     // after its own chunks in the workspace, and the states the caller asked
     // for are stepped from those
@@ -248,43 +216,6 @@ int32_t ssd_step(float *state, const void *x, const void *dt, const float *A, co
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = io_dtype == SSD_BF16 ? dispatch_step<bf16>(a, s) : dispatch_step<float>(a, s);
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
-}
-
-int32_t ssd_trace_enable(int32_t on) {
-    Trace &t = tr();
-    std::lock_guard<std::mutex> g(t.mu);
-    t.on = on != 0;
-    return SSD_OK;
-}
-
-int32_t ssd_trace_read(int32_t kernel, double *total_ms, int64_t *launches) {
-    if (!total_ms || !launches) return SSD_ERR_NULL;
-    if (kernel < 0 || kernel >= SSD_K_COUNT) return SSD_ERR_SHAPE;
-    Trace &t = tr();
-    std::lock_guard<std::mutex> g(t.mu);
-    double sum = 0.0;
-    int64_t cnt = 0;
-    std::vector<TraceRec> keep;
-    keep.reserve(t.recs.size());
-    for (const TraceRec &r : t.recs) {
-        if (r.kernel != kernel) {
-            keep.push_back(r);
-            continue;
-        }
-        float ms = 0.f;
-        if (hipEventSynchronize(r.end) == hipSuccess &&
-            hipEventElapsedTime(&ms, r.start, r.end) == hipSuccess) {
-            sum += ms;
-            ++cnt;
-        }
-        t.pool.push_back(r.start);
-        t.pool.push_back(r.end);
-    }
-    t.recs.swap(keep);
-    t.open = -1;
-    *total_ms = sum;
-    *launches = cnt;
-    return SSD_OK;
 }
 
 }  // extern "C"

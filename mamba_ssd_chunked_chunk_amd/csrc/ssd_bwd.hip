@@ -414,7 +414,6 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
     hipError_t e = hipSuccess;
     auto ok = [&]() { return (e = hipGetLastError()) == hipSuccess; };
 
-    trace_begin(SSD_K_BWD_AUX, s);
     if (io_dtype == SSD_BF16)
         hipLaunchKernelGGL((k_bwd_prep<bf16>), dim3((unsigned)bl), dim3(256), 0, s,
                            static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt), A,
@@ -433,7 +432,6 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
     if (d_final)
         hipLaunchKernelGGL(k_transpose_np, dim3(eblk), dim3(256), 0, s, d_final, w.dfT, pairs,
                            (int)n, (int)p);
-    trace_end(SSD_K_BWD_AUX, s);
     if (!ok()) return SSD_ERR_HIP;
 
     // 1. the adjoint, reversed: read-out yb_t = g_t^T B_t, final state g_0
@@ -455,7 +453,6 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
     a3.la = w.la;
     if ((e = scan_f32(P.s2, a3, s)) != hipSuccess) return SSD_ERR_HIP;
 
-    trace_begin(SSD_K_BWD_AUX, s);
     const unsigned tblk = (unsigned)((bl * h + 15) / 16);
     if (io_dtype == SSD_BF16)
         hipLaunchKernelGGL((k_bwd_tok<bf16>), dim3(tblk), dim3(256), 0, s,
@@ -495,7 +492,6 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
     if (d_init)
         hipLaunchKernelGGL(k_bwd_init, dim3(eblk), dim3(256), 0, s, w.fin1, w.sc, A, d_init,
                            pairs, (int)h, l, np);
-    trace_end(SSD_K_BWD_AUX, s);
     return ok() ? SSD_OK : SSD_ERR_HIP;
 }
 

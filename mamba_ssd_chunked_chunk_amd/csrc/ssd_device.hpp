@@ -365,6 +365,55 @@ __device__ __forceinline__ int progress_priority(int k, int nblk) {
     return 3 - (4 * k) / (nblk > 0 ? nblk : 1);
 }
 
+// ------------------------------------------------ memory ordering ----
+// Keeps the memory operations before and after it in program order, so that
+// the counts given to vm_wait match the order of issue.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (they complete in issue order).
+template <int N> __device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ------------------------------------------------- state tiles ----
+// The state scan's threads cover each (batch, head) state in tiles of R
+// state rows by Cc head_dim columns (R = min(state_dim, 64), R Cc = 1024 or
+// all of a small state); a thread holds 4 consecutive state rows of one
+// column, the tile's threads running down the rows first.  Chunk states and
+// boundary states ([head_dim][state_dim]) are then read and written in runs
+// of R elements, and a tile's rows of the [state_dim][head_dim] outputs in
+// runs of Cc.
+struct ScanTile {
+    int R, Cc, TT;  // rows, columns, threads of a tile
+    __device__ ScanTile(int n, int p) {
+        R = n < 64 ? n : 64;
+        Cc = p < 1024 / R ? p : 1024 / R;
+        TT = R * Cc / 4;
+    }
+};
+
+// Stores a tile of the state ([state_dim][head_dim] order, 16 bytes per lane
+// along the rows) through LDS: thread t of the tile passes its 4 elements v
+// and the tile's output `out` (rows row0.., columns col0..).  Every thread of
+// the workgroup takes part (two barriers, which wait for LDS only: the global
+// stores before them stay in flight); `live` false stores nothing.
+__device__ __forceinline__ void store_state_rows(float *lds, const f32x4 &v, const ScanTile &st,
+                                                 bool live, float *out, int row0, int col0,
+                                                 int p) {
+    const int tid = threadIdx.x, tw = tid / st.TT, loc = tid % st.TT;
+    lds_barrier();  // earlier reads of the tile are done
+    *reinterpret_cast<f32x4 *>(lds + 4 * tid) = v;
+    lds_barrier();
+    const int v0 = 4 * loc, row = v0 / st.Cc, col = v0 % st.Cc;
+    const float *t = lds + tw * st.TT * 4;
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = t[(col + i) * st.R + row];
+    if (live) *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + row) * p + col0 + col) = o;
+}
+
 // ----------------------------------------------- workgroup -> work item ----
 // Workgroups are handed to the 8 XCDs round-robin by id (id % 8).  Work items
 // that share data (the heads of one group, the slices of one state) are

@@ -128,21 +128,17 @@ hipError_t launch_token_states(const ScanPlan &pl, const ScanArgs &a, const floa
                                hipStream_t s) {
     const int64_t npt = pl.p < 32 ? 1 : pl.p / 32;
     const unsigned grid = (unsigned)(pl.b * pl.nc * pl.h * npt);
-    trace_begin(5, s);
     if (pl.io == 1)
-        hipLaunchKernelGGL((k_token_states<bf16>), dim3(grid), dim3(256), 0, s,
-                           static_cast<const bf16 *>(a.x), static_cast<const bf16 *>(a.B),
-                           static_cast<const bf16 *>(a.dt), a.A, a.dt_bias, a.softplus,
-                           a.dt_min, a.dt_max, a.seq, a.init, Hc, a.states, pl.l, (int)pl.h,
-                           (int)pl.g, (int)pl.n, (int)pl.p, pl.Q, pl.Qs, pl.nc, pl.ns);
-    else
-        hipLaunchKernelGGL((k_token_states<float>), dim3(grid), dim3(256), 0, s,
-                           static_cast<const float *>(a.x), static_cast<const float *>(a.B),
-                           static_cast<const float *>(a.dt), a.A, a.dt_bias, a.softplus,
-                           a.dt_min, a.dt_max, a.seq, a.init, Hc, a.states, pl.l, (int)pl.h,
-                           (int)pl.g, (int)pl.n, (int)pl.p, pl.Q, pl.Qs, pl.nc, pl.ns);
-    trace_end(5, s);
-    return hipGetLastError();
+        return launch_timed(&k_token_states<bf16>, dim3(grid), dim3(256), s, a.ev, kSlotFill,
+                            static_cast<const bf16 *>(a.x), static_cast<const bf16 *>(a.B),
+                            static_cast<const bf16 *>(a.dt), a.A, a.dt_bias, a.softplus,
+                            a.dt_min, a.dt_max, a.seq, a.init, Hc, a.states, pl.l, (int)pl.h,
+                            (int)pl.g, (int)pl.n, (int)pl.p, pl.Q, pl.Qs, pl.nc, pl.ns);
+    return launch_timed(&k_token_states<float>, dim3(grid), dim3(256), s, a.ev, kSlotFill,
+                        static_cast<const float *>(a.x), static_cast<const float *>(a.B),
+                        static_cast<const float *>(a.dt), a.A, a.dt_bias, a.softplus,
+                        a.dt_min, a.dt_max, a.seq, a.init, Hc, a.states, pl.l, (int)pl.h,
+                        (int)pl.g, (int)pl.n, (int)pl.p, pl.Q, pl.Qs, pl.nc, pl.ns);
 }
 
 }  // namespace ssd

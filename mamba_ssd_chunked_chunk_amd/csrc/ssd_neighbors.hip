@@ -271,7 +271,6 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
     if (runs > 65535) return SSD_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((ch / 4 + kConvThreads - 1) / kConvThreads), (unsigned)runs,
                     (unsigned)batch);
-    trace_begin(SSD_K_CONV1D, s);
 #define SSD_CONV(IO, KK)                                                                       \
     if (seq_idx)                                                                               \
         hipLaunchKernelGGL((k_conv1d_silu<IO, KK, true>), grid, dim3(kConvThreads), 0, s,      \
@@ -297,7 +296,6 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
     }
 #undef SSD_CONV_W
 #undef SSD_CONV
-    trace_end(SSD_K_CONV1D, s);
     return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
@@ -316,7 +314,6 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
     const int64_t blocks = (waves + 3) / 4;
     if (blocks > ((int64_t)1 << 31) - 1) return SSD_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    trace_begin(SSD_K_GATED_NORM, s);
     if (io_dtype == SSD_BF16)
         hipLaunchKernelGGL((k_gated_norm<bf16>), dim3((unsigned)blocks), dim3(256), 0, s,
                            static_cast<const bf16 *>(y), static_cast<const bf16 *>(z), weight,
@@ -327,7 +324,6 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
                            static_cast<const float *>(y), static_cast<const float *>(z), weight,
                            static_cast<float *>(out), rows, (int)dim, (int)group_size, eps,
                            normalize ? 1 : 0);
-    trace_end(SSD_K_GATED_NORM, s);
     return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -2,10 +2,12 @@
 // space and the workspace map.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <atomic>
 #include <stdint.h>
-#include <stdlib.h>
 
 namespace ssd {
 
@@ -26,7 +28,7 @@ struct ScanPlan {
     int64_t lp;   // padded rows per sequence (nc * Qp)
     // workspace offsets (bytes)
     size_t off_lcs, off_dtp, off_wgt, off_sgr, off_hb, off_st, off_lam, off_scl, off_img, off_hc,
-        total;
+        off_hs, off_imx, total;
 };
 
 // Chunks shorter than one 32-row block are computed as chunks of a whole
@@ -50,20 +52,11 @@ inline int group_heads(int p, int64_t heads_per_group) {
     return (hp > 1 && heads_per_group % hp == 0) ? hp : 1;
 }
 
-// Whether the bf16 chunk output, with workgroups that share B and C over
-// several heads, copies its blocks into LDS from fp16 block images (written
-// by the state-scan launch) instead of staging them through registers.  The
-// images cost one read of B and C and one write of their fp16 copies; they
-// pay off where that is small against the x stream (8 g n <= h p).
-// SSD_CHUNK_OUT_COPY=0 or 1 in the environment forces either path; both give
-// the same results.
-inline bool chunk_out_copy(int64_t h, int64_t g, int64_t p, int64_t n) {
-    if (const char *e = getenv("SSD_CHUNK_OUT_COPY")) {
-        if (e[0] == '0') return false;
-        if (e[0] == '1') return true;
-    }
-    return 8 * g * n <= h * p;
-}
+// Whether the fp32 chunk output, with workgroups that share B and C over
+// several heads, copies its blocks into LDS from fp16 block images.  The fp32
+// path stages through registers; only bf16 io ever copied, and it now has
+// kernels of its own.
+inline bool chunk_out_copy(int64_t, int64_t, int64_t, int64_t) { return false; }
 
 // Fills the plan from the sizes; returns false if they are invalid.
 inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, int64_t n,
@@ -94,12 +87,15 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     P.off_lam = o;  o += align256(b * h * P.nc * 4);       // chunk log2 decays
     // bf16 io: every chunk state is kept as fp16 times a power-of-two scale
     P.off_scl = o;  o += align256(b * h * P.nc * 4);       // chunk-state scales
-    // C and B of every 32-row block of every (batch, chunk, group) as fp16,
-    // in the chunk output's LDS layout (bf16 io only; room kept for both)
-    P.off_img = o;  o += align256(b * P.nc * g * P.nsb * 2 * P.T * n * 2);
+    // (no block images any more: kept as an empty part of the map)
+    P.off_img = o;
     // fp32 states after the computed chunks, read by the per-token fill
     // (short caller chunks only)
     P.off_hc = o;   o += P.Qs != P.Q ? align256(b * P.nc * h * st * 4) : 0;
+    // bf16 io: the boundary states' scales [b, h, nc] and the initial
+    // state's largest magnitude per (batch, head)
+    P.off_hs = o;   o += align256(b * h * P.nc * 4);
+    P.off_imx = o;  o += align256(b * h * 4);
     P.total = o;
     return true;
 }
@@ -118,7 +114,43 @@ struct ScanArgs {
     // fp32 io only, or NULL: every token's weight and log2 decay [b, l, h],
     // given in place of the time step (dt, A, dt_bias and the limits unused)
     const float *lw = nullptr, *la = nullptr;
+    // NULL, or 2 * kEventSlots hipEvent_t owned by the caller: the start and
+    // end of the call's launch in each slot (kernel execution only), see
+    // launch_timed
+    void *const *ev = nullptr;
 };
+
+// Slots of the kernel-timing events of one scan call.
+enum { kSlotState = 0, kSlotScan = 1, kSlotOut = 2, kSlotFill = 3, kEventSlots = 4 };
+
+// Launches a kernel on stream s, recording events ev[2 slot] and
+// ev[2 slot + 1] (when ev is given) at its start and end: the runtime takes
+// them from the dispatch itself, so they measure the kernel alone.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                               void *const *ev, int slot, Args... args) {
+    hipEvent_t e0 = ev ? static_cast<hipEvent_t>(ev[2 * slot]) : nullptr;
+    hipEvent_t e1 = ev ? static_cast<hipEvent_t>(ev[2 * slot + 1]) : nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
+
+// Compute units of the current device and resident workgroups of a kernel
+// per compute unit, queried once per device (thread-safe caches).
+int device_cus();
+template <auto KERN> int resident_per_cu(int threads) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, KERN, threads, 0) != hipSuccess ||
+        nb < 1)
+        nb = 1;
+    cache[dev].store(nb, std::memory_order_relaxed);
+    return nb;
+}
 
 struct StepArgs {
     float *state;
@@ -130,10 +162,6 @@ struct StepArgs {
     int64_t b, h, p, n, g;
     int io;
 };
-
-// Kernel-timing hooks (ssd_trace_*): called around every launch.
-void trace_begin(int kernel, hipStream_t s);
-void trace_end(int kernel, hipStream_t s);
 
 // States after every caller chunk, stepped token by token from Hc (the fp32
 // states after the computed chunks), for caller chunks shorter than the
@@ -147,6 +175,8 @@ hipError_t scan_f32(const ScanPlan &pl, const ScanArgs &a, hipStream_t s);
 // Launchers, one per (io, head_dim, state_dim) instantiation.
 template <typename IO, int P, int N>
 hipError_t launch_scan(const ScanPlan &plan, const ScanArgs &a, hipStream_t s);
+template <int P, int N>
+hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s);
 template <typename IO, int P, int N>
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 

@@ -582,42 +582,6 @@ __device__ __forceinline__ void bc_image_piece(const ImgArgs &ia, int64_t q) {
     }
 }
 
-// The state scan's threads cover each (batch, head) state in tiles of R
-// state rows by Cc head_dim columns (R = min(state_dim, 64), R Cc = 1024 or
-// all of a small state); a thread holds 4 consecutive state rows of one
-// column, the tile's threads running down the rows first.  Chunk states and
-// boundary states ([head_dim][state_dim]) are then read and written in runs
-// of R elements, and a tile's rows of the [state_dim][head_dim] outputs in
-// runs of Cc.
-struct ScanTile {
-    int R, Cc, TT;  // rows, columns, threads of a tile
-    __device__ ScanTile(int n, int p) {
-        R = n < 64 ? n : 64;
-        Cc = p < 1024 / R ? p : 1024 / R;
-        TT = R * Cc / 4;
-    }
-};
-
-// Stores a tile of the state ([state_dim][head_dim] order, 16 bytes per lane
-// along the rows) through LDS: thread t of the tile passes its 4 elements v
-// and the tile's output `out` (rows row0.., columns col0..).  Every thread of
-// the workgroup takes part (two barriers, which wait for LDS only: the global
-// stores before them stay in flight); `live` false stores nothing.
-__device__ __forceinline__ void store_state_rows(float *lds, const f32x4 &v, const ScanTile &st,
-                                                 bool live, float *out, int row0, int col0,
-                                                 int p) {
-    const int tid = threadIdx.x, tw = tid / st.TT, loc = tid % st.TT;
-    lds_barrier();  // earlier reads of the tile are done
-    *reinterpret_cast<f32x4 *>(lds + 4 * tid) = v;
-    lds_barrier();
-    const int v0 = 4 * loc, row = v0 / st.Cc, col = v0 % st.Cc;
-    const float *t = lds + tw * st.TT * 4;
-    f32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = t[(col + i) * st.R + row];
-    if (live) *reinterpret_cast<f32x4 *>(out + (int64_t)(row0 + row) * p + col0 + col) = o;
-}
-
 // ROWS: the final state or the state after every chunk is written (the
 // instance without them keeps fewer registers).
 template <typename OP, typename IO, int N, bool ROWS>
@@ -879,17 +843,6 @@ __device__ __forceinline__ void co_dma(typename Op<IO>::type *buf, int s, const 
             (uint32_t)(r * cp.xs + hs * P + ((k ^ xsw<P>(r)) << 3)) * (uint32_t)sizeof(IO);
         lds_copy16(rx, (lds_void *)(Xs + qw * 8), off);
     }
-}
-
-// Keeps the memory operations before and after it in program order, so that
-// the counts given to vm_wait match the order of issue.
-__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
-
-// Wait until at most N vector memory operations of this wave are in flight
-// (they complete in issue order).
-template <int N> __device__ __forceinline__ void vm_wait() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <bool SEQ, typename IO, int P, int N, int HPW>
@@ -1439,26 +1392,20 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     auto launch_state = [&](auto hp_c, auto seq_c) {
         constexpr int HPn = decltype(hp_c)::value;
         constexpr bool SQ = decltype(seq_c)::value;
-        hipLaunchKernelGGL((k_chunk_state<IO, P, N, HPn, SQ>),
-                           dim3((unsigned)(pl.b * pl.nc * (h / HPn))), dim3(Sp<IO, P, N, HPn>::NT),
-                           0, s, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min, a.dt_max, lcs,
-                           dtp, wgt, St, Lam, Scl, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq, sgr,
-                           a.lw, a.la);
+        return launch_timed(&k_chunk_state<IO, P, N, HPn, SQ>,
+                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))),
+                            dim3(Sp<IO, P, N, HPn>::NT), s, a.ev, kSlotState, x, Bm, dt, a.A,
+                            a.dt_bias, a.softplus, a.dt_min, a.dt_max, lcs, dtp, wgt, St, Lam,
+                            Scl, pl.l, h, g, pl.Q, pl.nc, pl.Qp, keep_last, a.seq, sgr, a.lw,
+                            a.la);
     };
-    trace_begin(1, s);
-    if (grouped) {
-        if (seq)
-            launch_state(std::integral_constant<int, HP>{}, std::true_type{});
-        else
-            launch_state(std::integral_constant<int, HP>{}, std::false_type{});
-    } else {
-        if (seq)
-            launch_state(std::integral_constant<int, 1>{}, std::true_type{});
-        else
-            launch_state(std::integral_constant<int, 1>{}, std::false_type{});
-    }
-    trace_end(1, s);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (grouped)
+        e = seq ? launch_state(std::integral_constant<int, HP>{}, std::true_type{})
+                : launch_state(std::integral_constant<int, HP>{}, std::false_type{});
+    else
+        e = seq ? launch_state(std::integral_constant<int, 1>{}, std::true_type{})
+                : launch_state(std::integral_constant<int, 1>{}, std::false_type{});
     if (e != hipSuccess) return e;
 
     const int64_t np4 = (int64_t)N * P / 4;
@@ -1478,49 +1425,35 @@ hipError_t launch_scan(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     // accumulators); head-sharing workgroups by the size rule
     const bool copy = sizeof(IO) == 2 && (!grouped || chunk_out_copy(h, g, P, N));
     ia.pieces = copy ? pl.b * pl.nc * g * pl.nsb * 2 * kT * (N / 8) : 0;
-    trace_begin(2, s);
     if (keep_last)
-        hipLaunchKernelGGL((k_state_scan<OP, IO, N, true>), dim3((unsigned)scan_blocks),
-                           dim3(kThreads), 0, s, St, Lam, Scl, a.init, Hb, a.final_state,
-                           pl.b * pl.h, h, pl.nc, N, P, ia, a.states);
+        e = launch_timed(&k_state_scan<OP, IO, N, true>, dim3((unsigned)scan_blocks),
+                         dim3(kThreads), s, a.ev, kSlotScan, St, Lam, Scl, a.init, Hb,
+                         a.final_state, pl.b * pl.h, h, pl.nc, N, P, ia, a.states);
     else
-        hipLaunchKernelGGL((k_state_scan<OP, IO, N, false>), dim3((unsigned)scan_blocks),
-                           dim3(kThreads), 0, s, St, Lam, Scl, a.init, Hb, nullptr, pl.b * pl.h, h,
-                           pl.nc, N, P, ia, nullptr);
-    trace_end(2, s);
-    e = hipGetLastError();
+        e = launch_timed(&k_state_scan<OP, IO, N, false>, dim3((unsigned)scan_blocks),
+                         dim3(kThreads), s, a.ev, kSlotScan, St, Lam, Scl, a.init, Hb,
+                         (float *)nullptr, pl.b * pl.h, h, pl.nc, N, P, ia, (float *)nullptr);
     if (e != hipSuccess) return e;
 
-    trace_begin(3, s);
     auto launch_out = [&](auto hp_c, auto copy_c, auto seq_c) {
         constexpr int HPn = decltype(hp_c)::value;
         constexpr bool CP = decltype(copy_c)::value;
         constexpr bool SQ = decltype(seq_c)::value;
-        hipLaunchKernelGGL((k_chunk_out<IO, P, N, HPn, CP, SQ>),
-                           dim3((unsigned)(pl.b * pl.nc * (h / HPn))),
-                           dim3(Co<IO, P, N, HPn, CP>::NT), 0, s, x, Bm, Cm, a.D, lcs, dtp, wgt,
-                           Hb, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb,
-                           a.init != nullptr, sgr);
+        return launch_timed(&k_chunk_out<IO, P, N, HPn, CP, SQ>,
+                            dim3((unsigned)(pl.b * pl.nc * (h / HPn))),
+                            dim3(Co<IO, P, N, HPn, CP>::NT), s, a.ev, kSlotOut, x, Bm, Cm, a.D,
+                            lcs, dtp, wgt, Hb, y, pl.l, h, g, pl.Q, pl.nc, pl.Qp, ia.img, pl.nsb,
+                            a.init != nullptr ? 1 : 0, sgr);
     };
     typedef std::integral_constant<int, 1> One;
     typedef std::integral_constant<int, HP> Grp;
     typedef std::true_type Yes;
     typedef std::false_type No;
-    if constexpr (sizeof(IO) == 2) {
-        if (!grouped)
-            seq ? launch_out(One{}, Yes{}, Yes{}) : launch_out(One{}, Yes{}, No{});
-        else if (copy)
-            seq ? launch_out(Grp{}, Yes{}, Yes{}) : launch_out(Grp{}, Yes{}, No{});
-        else
-            seq ? launch_out(Grp{}, No{}, Yes{}) : launch_out(Grp{}, No{}, No{});
-    } else {
-        if (grouped)
-            seq ? launch_out(Grp{}, No{}, Yes{}) : launch_out(Grp{}, No{}, No{});
-        else
-            seq ? launch_out(One{}, No{}, Yes{}) : launch_out(One{}, No{}, No{});
-    }
-    trace_end(3, s);
-    return hipGetLastError();
+    static_assert(sizeof(IO) == 4, "bf16 io has its own kernels (ssd_scan16.hpp)");
+    (void)copy;
+    if (grouped)
+        return seq ? launch_out(Grp{}, No{}, Yes{}) : launch_out(Grp{}, No{}, No{});
+    return seq ? launch_out(One{}, No{}, Yes{}) : launch_out(One{}, No{}, No{});
 }
 
 }  // namespace ssd

@@ -79,13 +79,11 @@ template <typename IO, int P, int N>
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t pairs = a.b * a.h;
     const unsigned nblk = (unsigned)((pairs + kWaves - 1) / kWaves);
-    trace_begin(4, s);
     hipLaunchKernelGGL((k_step<IO, P, N>), dim3(nblk), dim3(256), 0, s, a.state,
                        static_cast<const IO *>(a.x), static_cast<const IO *>(a.dt), a.A,
                        static_cast<const IO *>(a.B), static_cast<const IO *>(a.C), a.D, a.dt_bias,
                        a.softplus, a.dt_min, a.dt_max, static_cast<IO *>(a.y), pairs, (int)a.h,
                        (int)a.g);
-    trace_end(4, s);
     return hipGetLastError();
 }
 

@@ -208,6 +208,22 @@ def norm_case(seed: int, rows: int, dim: int, io: str = F32):
 
 
 
+def doc_index(seed: int, batch: int, seqlen: int, lo: int = 32, hi: int = 2048) -> np.ndarray:
+    """Document index [batch, seqlen] int32 of packed rows: documents back to
+    back, lengths log-uniform in [lo, hi] tokens (PCG64 seeded with
+    (seed, 10)), the last one cut at the row's end."""
+    rng = np.random.Generator(np.random.PCG64([seed, 10]))
+    seq = np.zeros((batch, seqlen), np.int32)
+    for bi in range(batch):
+        t = k = 0
+        while t < seqlen:
+            m = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+            seq[bi, t:t + m] = k
+            t += m
+            k += 1
+    return seq
+
+
 def cotangent_case(seed: int, batch: int, seqlen: int, heads: int, head_dim: int,
                    state_dim: int, io: str = F32):
     """Cotangents for the gradient pass: dy ~ N(0, 1) (stored in io) and

@@ -3,15 +3,13 @@ sampled oracle comparisons.
 
 Tolerance bar (elementwise, for y and for states):
   fp32 io:  |g - o| <= 1e-4 + 1e-4 |o|
-  bf16 io:  |g - o| <= 2e-2 |o| + 2e-2 rms_head(o)
-with o the fp64 oracle value and rms_head the root mean square of the
-oracle values of the same (batch, head): "relative" is taken per head,
-because every head is its own recurrence (nnterp guide, "Mamba-2" page,
-opening section: "Per head, ...") and heads differ in output scale by
-orders of magnitude (dt_bias spans two decades, A a factor 16), so a floor
-taken over all heads would hold small-scale heads to a far tighter, and
-large-scale heads to a far looser, standard than 2e-2 of their own size.
-The pages' own step-vs-forward differences (5.07e-5 in fp32 and 7.81e-3 in bf16 on an RTX 4090; mirror of
+  bf16 io:  |g - o| <= 2e-2 |o| + 2e-2 rms(o), asserted twice: with rms over
+            the whole compared tensor, and with rms over each (batch, head)'s
+            values (every head is its own recurrence: nnterp guide, "Mamba-2"
+            page, opening section), so every element meets the stricter of
+            the two floors.
+with o the fp64 oracle value.  The pages' own step-vs-forward differences
+(5.07e-5 in fp32 and 7.81e-3 in bf16 on an RTX 4090; mirror of
 state-spaces/mamba issue 1024, "Mamba3 step() is non-deterministic ...")
 sit inside these bounds.
 """
@@ -58,9 +56,11 @@ def bar(io):
 def check_close(g, o, io, what, rms_axes=None, floor=None):
     """Assert the elementwise bar; return (max_abs, max_rel, normwise).
 
-    rms_axes: the axes that do NOT index a (batch, head) pair, i.e. the rms
-    floor is taken over them (None: over the whole tensor).  floor: the rms
-    floor's factor instead of the io type's."""
+    rms_axes: the axes that do NOT index a (batch, head) pair; with bf16 io
+    the rms floor is then asserted both over the whole tensor and per pair
+    (None: over the whole tensor only).  floor: the rms floor's factor
+    instead of the io type's (the fp32 gradient terms that come out of a
+    running sum)."""
     g = np.asarray(g, np.float64)
     o = np.asarray(o, np.float64)
     assert g.shape == o.shape, (what, g.shape, o.shape)
@@ -70,20 +70,32 @@ def check_close(g, o, io, what, rms_axes=None, floor=None):
         rmsf = floor
     if o.size == 0:
         return (0.0, 0.0, 0.0)
-    rms = np.sqrt(np.mean(o * o, axis=rms_axes, keepdims=rms_axes is not None))
     err = np.abs(g - o)
-    lim = atol + rtol * np.abs(o) + rmsf * rms
-    bad = err > lim
-    den = np.maximum(np.abs(o), np.where(rms > 0, rms, 1e-300))
-    stats = (float(err.max()), float((err / den).max()),
-             float(err.max() / max(np.abs(o).max(), 1e-300)))
-    if bad.any():
-        idx = np.unravel_index(np.argmax(err - lim), err.shape)
-        raise AssertionError("%s: %d of %d elements outside the %s bar; worst at %s: gpu %r "
-                             "oracle %r (max_abs %.3g max_rel %.3g)"
-                             % (what, int(bad.sum()), bad.size, io, idx, g[idx], o[idx],
-                                stats[0], stats[1]))
-    return stats
+    rms_t = np.sqrt(np.mean(o * o))
+    floors = [("tensor", rms_t)]
+    if rms_axes is not None:
+        floors.append(("head", np.sqrt(np.mean(o * o, axis=rms_axes, keepdims=True))))
+    for kind, rms in floors:
+        lim = atol + rtol * np.abs(o) + rmsf * rms
+        bad = err > lim
+        if bad.any():
+            idx = np.unravel_index(np.argmax(err - lim), err.shape)
+            raise AssertionError(
+                "%s: %d of %d elements outside the %s bar (rms floor per %s); worst at %s: "
+                "gpu %r oracle %r" % (what, int(bad.sum()), bad.size, io, kind, idx, g[idx], o[idx]))
+        WORST.setdefault((what, kind), 0.0)
+        if rmsf > 0:
+            WORST[(what, kind)] = max(WORST[(what, kind)],
+                                      float(np.max(err / (np.abs(o) + rms + 1e-300))))
+    rms = rms_t
+    den = np.maximum(np.abs(o), rms if rms > 0 else 1e-300)
+    return (float(err.max()), float((err / den).max()),
+            float(err.max() / max(np.abs(o).max(), 1e-300)))
+
+
+# worst err / (|o| + rms) seen per (what, floor kind) in this process, for
+# the logs
+WORST = {}
 
 
 # rms axes per layout: everything except the (batch, head) indices

@@ -126,15 +126,6 @@ def test_step_rejects_bad_arguments(lib):
     assert step(b=0) == L.SSD_OK     # nothing to do, nothing launched
 
 
-def test_trace_read_validates(lib):
-    ms = ctypes.c_double()
-    n = ctypes.c_int64()
-    assert lib.ssd_trace_read(99, ctypes.byref(ms), ctypes.byref(n)) != 0
-    assert lib.ssd_trace_read(0, None, None) != 0
-    assert lib.ssd_trace_read(0, ctypes.byref(ms), ctypes.byref(n)) == 0
-    assert n.value == 0
-
-
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from mamba_ssd_chunked_chunk_amd import _lib as L
     monkeypatch.setattr(L, "_lib", None)
@@ -161,7 +152,7 @@ def test_scan_ex_rejects_bad_arguments(lib):
         kw.update(over)
         return lib.ssd_chunk_scan_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 0.0, math.inf,
                                      None, kw["seq"], FAKE, None, kw["states"], kw["b"], kw["l"],
-                                     4, 64, 128, 1, 64, kw["io"], FAKE, kw["wsb"], None)
+                                     4, 64, 128, 1, 64, kw["io"], FAKE, kw["wsb"], None, None)
     assert ex(seq=FAKE + 2) == L.SSD_ERR_ALIGN
     assert ex(states=FAKE + 8) == L.SSD_ERR_ALIGN
     assert ex(io=5) == L.SSD_ERR_UNSUPPORTED
