@@ -330,6 +330,34 @@ __device__ __forceinline__ void lds_copy16(Rsrc r, lds_void *dst, uint32_t voff)
     (void)r, (void)dst, (void)voff;
 #endif
 }
+// The same 16-byte copy into LDS written out as machine code, with the
+// buffer descriptor as four plain words.  The compiler does not see that it
+// writes LDS or that it counts in vmcnt, so it adds no wait of its own before
+// later LDS reads (with the builtin it waits for every copy in flight before
+// each transposing LDS read, whatever buffer the read uses): the caller
+// orders the copies with vm_wait and lds_barrier.  It has no output
+// register; M0 (the LDS address) is set in the same statement, with the one
+// wait state the hardware needs between that write and the copy.  Waits the
+// compiler adds for its own loads count only its own operations and so stay
+// correct (completion is in issue order).
+typedef uint32_t RsrcW __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ RsrcW make_rsrc_w(const void *base, int64_t bytes) {
+    const int64_t c = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return RsrcW{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu,
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)c), (uint32_t)kRsrcWord3};
+}
+__device__ __forceinline__ void lds_dma16(RsrcW r, lds_void *dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
+                 "s"(r), "s"(a)
+                 : "memory", "m0");
+#else
+    (void)r, (void)dst, (void)voff;
+#endif
+}
 template <typename T> __device__ __forceinline__ Row8v<T> buf_row8(Rsrc r, uint32_t off) {
     constexpr int NV = sizeof(Row8v<T>) / 16;
     u32x4 v[NV];

@@ -36,12 +36,11 @@
 //                 taken from a running bound on their magnitude; the final
 //                 state and the state after every chunk in fp32
 //   3. k_out16    the chunk output from the boundary states
-// The chunk-state pass and the chunk output are persistent: each workgroup
-// walks the 32-row blocks of a fixed list of (batch, chunk, heads) items
-// back to back, the copy of the next block (which may open the next item)
-// in flight while the current one is computed.  Both compute the per-row
-// time step, cumulative decay and weights of each block from the raw time
-// steps with the same code, so they agree bit for bit.
+// The chunk-state pass and the chunk output give one workgroup to each
+// (batch, chunk, heads) item, which walks the chunk's 32-row blocks with the
+// copy of the next block in flight while the current one is computed.  Both
+// compute the per-row time step, cumulative decay and weights of each block
+// from the raw time steps with the same code, so they agree bit for bit.
 #pragma once
 
 #include <type_traits>
@@ -65,13 +64,29 @@ __device__ __forceinline__ f32x4 mma(const bf16x8 &a, const bf16x8 &b, const f32
 struct HL {
     bf16x8 hi, lo;
 };
-__device__ __forceinline__ HL split8(const float (&v)[8]) {
+// The bf16 pairs (-1, 0) and (0, -1), held in registers: the compiler
+// writes (-1, 0) as the inline constant -1.0, which the hardware reads as
+// the fp32 value -1.0, i.e. the pair (0, -1), so the constant is hidden
+// from it.
+struct Neg1 {
+    bf16x2 lo, hi;
+};
+__device__ __forceinline__ Neg1 neg1() {
+    uint32_t a = 0x0000bf80u, b = 0xbf800000u;
+    asm volatile("" : "+v"(a), "+v"(b));
+    return Neg1{__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b)};
+}
+// hi = bf16(v) (nearest); v - hi is exact in fp32 and is formed with one
+// bf16 dot product per value (hi times -1 in one half and 0 in the other,
+// plus v), then rounded to bf16 as lo.
+__device__ __forceinline__ HL split8(const float (&v)[8], const Neg1 &m) {
     HL o;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         const bf16x2 h = __builtin_convertvector((f32x2{v[e], v[e + 1]}), bf16x2);
-        const f32x2 r{v[e] - (float)h[0], v[e + 1] - (float)h[1]};
-        const bf16x2 q = __builtin_convertvector(r, bf16x2);
+        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, m.lo, v[e], false);
+        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, m.hi, v[e + 1], false);
+        const bf16x2 q = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
         o.hi[e] = h[0];
         o.hi[e + 1] = h[1];
         o.lo[e] = q[0];
@@ -81,9 +96,9 @@ __device__ __forceinline__ HL split8(const float (&v)[8]) {
 }
 // Two accumulator tiles (contraction blocks 0..15 and 16..31 of a 32-block)
 // as one operand in the k convention of ssd_device.hpp.
-__device__ __forceinline__ HL split_acc(const f32x4 &t0, const f32x4 &t1) {
+__device__ __forceinline__ HL split_acc(const f32x4 &t0, const f32x4 &t1, const Neg1 &m) {
     const float v[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
-    return split8(v);
+    return split8(v, m);
 }
 // A raw operand fragment (8 bf16 as two 8-byte halves) from LDS bits.
 __device__ __forceinline__ bf16x8 as_bf16x8(const f16x4 &a, const f16x4 &b) {
@@ -97,6 +112,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const f16x4 &a, const f16x4 &b) {
 // scalar parameter.
 __device__ __forceinline__ float as_f32(uint32_t v) { return __builtin_bit_cast(float, v); }
 __device__ __forceinline__ uint32_t as_u32(float v) { return __builtin_bit_cast(uint32_t, v); }
+// A value the compiler must take as changed here: the per-block LDS
+// addresses derived from it are then computed afresh in every block instead
+// of being kept live (or spilled) across the whole block loop.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
     return __builtin_bit_cast(float, w & 0xffff0000u);
@@ -120,8 +142,8 @@ template <int P, int N, int HP> struct Shape {
     static constexpr int XI = XE / 8 / 64, BI = BE / 8 / 64;
     template <bool WITH_C> static constexpr int ninst() { return XI + BI * (WITH_C ? 2 : 1); }
     template <bool WITH_C> static constexpr int per_wave() { return (ninst<WITH_C>() + W - 1) / W; }
-    // y stores per lane and block
-    static constexpr int NS = CPW % 2 == 0 ? CPW : 2 * CPW;
+    // y stores per lane and block (rows li and 16 + li)
+    static constexpr int NS = 2;
     static_assert(XE % 512 == 0 && BE % 512 == 0, "whole copy instructions");
 };
 
@@ -144,45 +166,10 @@ template <int CPW> __device__ __forceinline__ int col_of(int u, int rho) {
         return 16 * u + rho;
 }
 
-// k-major x fragment of column tile u (contraction index = block row).
-template <int CPW, int P>
-__device__ __forceinline__ bf16x8 x_frag(const f16 *Xs, int c0, int u, int lane) {
-    const int g = lane >> 4, j = lane & 15;
-    const int col = c0 + col_of<CPW>(u, 4 * (j & 3));
-    const int ra = 4 * g + (j >> 2), rb = 16 + ra;
-    const f16x4 a = __builtin_bit_cast(
-        f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(Xs + xsw_at<P>(ra, col))));
-    const f16x4 b = __builtin_bit_cast(
-        f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(Xs + xsw_at<P>(rb, col))));
-    return as_bf16x8(a, b);
-}
-// Rows of a swizzled [T][N] matrix in the k convention (contraction over
-// columns kb..kb+31): lane l gets row row0 + (l & 15).
-template <int N>
-__device__ __forceinline__ bf16x8 rows_frag(const f16 *M, int row0, int kb, int lane) {
-    typedef Swz<f16, N> S;
-    const int r = row0 + (lane & 15), g = lane >> 4;
-    const f16x4 a = *reinterpret_cast<const f16x4 *>(M + S::at(r, kb + 4 * g));
-    const f16x4 b = *reinterpret_cast<const f16x4 *>(M + S::at(r, kb + 16 + 4 * g));
-    return as_bf16x8(a, b);
-}
-// k-major fragment (contraction over the 32 rows) of columns c0..c0+15 of a
-// swizzled [T][N] matrix.
-template <int N>
-__device__ __forceinline__ bf16x8 kmajor_frag(const f16 *M, int c0, int lane) {
-    typedef Swz<f16, N> S;
-    const int g = lane >> 4, j = lane & 15;
-    const f16 *pa = M + S::at(4 * g + (j >> 2), c0 + 4 * (j & 3));
-    const f16 *pb = M + S::at(16 + 4 * g + (j >> 2), c0 + 4 * (j & 3));
-    const f16x4 a =
-        __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pa));
-    const f16x4 b =
-        __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)pb));
-    return as_bf16x8(a, b);
-}
 // The k-major x fragment weighted row by row (rows 4g + r and 16 + 4g + r
 // of lane group g) by w, as two bf16 terms.
-__device__ __forceinline__ HL xw_split(const bf16x8 &xf, int lane, const float *w) {
+__device__ __forceinline__ HL xw_split(const bf16x8 &xf, int lane, const float *w,
+                                       const Neg1 &m) {
     const int g = lane >> 4;
     const f32x4 wa = *reinterpret_cast<const f32x4 *>(w + 4 * g);
     const f32x4 wb = *reinterpret_cast<const f32x4 *>(w + 16 + 4 * g);
@@ -191,7 +178,61 @@ __device__ __forceinline__ HL xw_split(const bf16x8 &xf, int lane, const float *
                         bf16_lo(xb[1]) * wa[2], bf16_hi(xb[1]) * wa[3],
                         bf16_lo(xb[2]) * wb[0], bf16_hi(xb[2]) * wb[1],
                         bf16_lo(xb[3]) * wb[2], bf16_hi(xb[3]) * wb[3]};
-    return split8(v);
+    return split8(v, m);
+}
+
+// State-row order.  Accumulator tile tr = 2m + h of a state (rows 16 tr..,
+// element r of lane group g) holds state row
+//     sigma(16 tr + 4g + r) = 32m + 8g + 4h + r,
+// so that the two tiles 2m, 2m + 1 of a lane, taken as one operand (k =
+// 4g + r and 16 + 4g + r of the contraction block m), meet 8 consecutive
+// state rows 32m + 8g .. 32m + 8g + 7: the matching B and C fragments are
+// one 16-byte LDS read each.  The B^T fragments of the carry read B's
+// columns in the same order, and the stored states are written and read in
+// the true order.
+//
+// Per-lane LDS element offsets of a wave's fragment reads inside the
+// regions of a block buffer, computed once per work item.  Every fragment of
+// a block is then one XOR (or add) away from them:
+//   frag_rows  rows of B or C (row l & 15; k = state rows 32m + 8g ..
+//              32m + 8g + 7): rows ^ 32m; rows 16..31: + 16 N
+//   frag_kmaj  B^T of state-row tile 2m + h (k = the block rows 4g + r and
+//              16 + 4g + r): (kmaj ^ 32m) + 4h; rows 16..31: + 16 N
+//   frag_x     x of column tile u (k = the block rows): x + 4 u, rows
+//              16..31: + 16 P
+// (the XORs only touch bits below log2 N, and a block buffer's offset is a
+// multiple of N, so it can be added to the bases first).
+template <int P, int N, int CPW> struct FragBase {
+    int rows, kmaj, x;
+    __device__ __forceinline__ void init(int c0, int lane) {
+        static_assert(CPW == 1 || CPW == 2, "one or two column tiles per wave");
+        typedef Swz<f16, N> S;
+        const int g = lane >> 4, j = lane & 15;
+        rows = j * N + ((g ^ S::f(j)) << 3);
+        const int r = 4 * g + (j >> 2);
+        kmaj = r * N + (((j & 3) ^ S::f(r)) << 3);
+        if constexpr (CPW == 2)
+            x = r * P + ((((c0 >> 3) + (j & 3)) ^ xsw<P>(r)) << 3);
+        else
+            x = r * P + ((((c0 >> 3) + ((j >> 1) & 1)) ^ xsw<P>(r)) << 3) + 4 * (j & 1);
+    }
+};
+// State row of element r of lane group g in accumulator tile tr.
+__device__ __forceinline__ int state_row(int tr, int g) {
+    return 32 * (tr >> 1) + 8 * g + 4 * (tr & 1);
+}
+__device__ __forceinline__ bf16x8 frag_rows(const f16 *M, int base, int m) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(M + (base ^ (32 * m))));
+}
+__device__ __forceinline__ f16x4 ds_tr(const f16 *p) {
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p));
+}
+template <int N> __device__ __forceinline__ bf16x8 frag_kmaj(const f16 *M, int base, int tr) {
+    const int o = (base ^ (32 * (tr >> 1))) + 4 * (tr & 1);
+    return as_bf16x8(ds_tr(M + o), ds_tr(M + o + 16 * N));
+}
+template <int P> __device__ __forceinline__ bf16x8 frag_x(const f16 *Xs, int base, int u) {
+    return as_bf16x8(ds_tr(Xs + base + 4 * u), ds_tr(Xs + base + 4 * u + 16 * P));
 }
 
 // -------------------------------------------------- per-row values ----
@@ -207,62 +248,73 @@ struct alignas(16) Rows {
     float bw[T];   // 2^(lcs_15 - lcs_j) d_j
     int seg[T];    // packed sequences: the last row <= i of the block that starts a
                    // new document, or -1
+    float lam;     // the block's log2 decay for the state carry (-inf across a reset)
 };
 __device__ __forceinline__ int row_pair(int r) { return 2 * (r & 15) + (r >> 4); }
 
 
 // Raw per-row inputs of one block for one head: lane l holds row l & 31
-// (the two halves of a wave hold the same rows).
+// (the two halves of a wave hold the same rows), as loaded: the values are
+// first used in rows_prep, after the wait for the block's copy, so the loads
+// stay in flight while the current block is computed.
 struct RowIn {
-    float dt;
-    int rst;  // packed sequences: the row starts a new document
+    uint32_t dt;   // bf16 bits
+    int cur, prv;  // packed sequences: document index of the row and of the token before
 };
 
-// Where one head's rows of a chunk live.
-struct RowSrc {
-    const bf16 *dt;      // the chunk's first row, this head (rows `h` elements apart)
-    const int32_t *seq;  // the sequence's document indices (packed sequences), or null
-    int64_t t0, l;       // the chunk's first token, the sequence length
-    int h;               // heads
-    int rows;            // valid rows of the chunk
-};
-
-// Loads block k's raw rows: one vector memory operation per lane (three
-// with packed sequences).  Rows past the chunk's end read as zero.
+// Loads block k's raw rows of one head (one vector memory operation per
+// lane, three with packed sequences).  dt0: the chunk's first row of the
+// head's time steps (rows h apart); seq: the sequence's document indices;
+// t0: the chunk's first token; rows: valid rows of the chunk.  Rows past the
+// chunk's end read as zero.
 template <bool SEQ>
-__device__ __forceinline__ void rows_load(RowIn &f, const RowSrc &rs, int k, int lane) {
+__device__ __forceinline__ void rows_load(RowIn &f, const bf16 *dt0, const int32_t *seq,
+                                          int64_t t0, int64_t l, int h, int rows, int k,
+                                          int lane) {
     const int r = lane & 31;
-    int valid = rs.rows - k * T;
+    int valid = rows - k * T;
     valid = valid < 0 ? 0 : (valid > T ? T : valid);
-    const Rsrc rd = make_rsrc(rs.dt + (int64_t)(valid > 0 ? k * T : 0) * rs.h,
-                              (int64_t)valid * rs.h * 2);
-    const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(rd, (uint32_t)(r * rs.h * 2), 0, 0);
-    f.dt = __builtin_bit_cast(float, (uint32_t)v << 16);
-    f.rst = 0;
+    const Rsrc rd = make_rsrc(dt0 + (int64_t)(valid > 0 ? k * T : 0) * h, (int64_t)valid * h * 2);
+    f.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (uint32_t)(r * h * 2), 0, 0);
     if constexpr (SEQ) {
-        // a row whose document index differs from the previous token's
-        // starts from a zero state (token 0 starts from the initial state)
-        const int64_t t = rs.t0 + (int64_t)k * T + r;
-        const Rsrc rq = make_rsrc(rs.seq, rs.l * 4);
-        const int cur = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)(t * 4), 0, 0);
-        const int prv =
-            (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)(t * 4) - 4u, 0, 0);
-        f.rst = (k * T + r < rs.rows && t > 0) ? (cur != prv) : 0;
+        // the token before the chunk's first (t0 - 1) is read for every
+        // chunk but the sequence's first, whose row 0 compares with itself
+        const int64_t t = t0 + (int64_t)k * T + r;
+        const Rsrc rq = make_rsrc(seq, l * 4);
+        f.cur = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)(t * 4), 0, 0);
+        f.prv = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)((t > 0 ? t - 1 : 0) * 4),
+                                                          0, 0);
     }
 }
-template <bool SEQ> constexpr int kRowOps = SEQ ? 3 : 1;
 
-// The block's per-row values from its raw rows, written to R (lanes 0..31)
-// by the wave that owns the head; returns the block's log2 decay as seen
-// by the state carry (-inf when a document starts inside the block:
-// nothing before the reset reaches the block's end).
+// softplus(z) = log(1 + e^z) from the hardware exp2 and log2 (about 1 ulp
+// each): z itself above 20 (the difference is below 2.1e-9), a five-term
+// series in t = e^z below t = 1/16 (relative error below 2e-7), otherwise
+// ln 2 * log2(1 + t) (relative error below 1e-6).
+__device__ __forceinline__ float softplus_fast(float z) {
+    if (z > 20.f) return z;
+    const float t = exp2_fast(z * kLog2e);
+    if (t < 0.0625f)
+        return t * (1.f - t * (0.5f - t * (1.f / 3.f - t * (0.25f - t * 0.2f))));
+    return 0.69314718055994531f * __builtin_amdgcn_logf(1.f + t);
+}
+
+// The block's per-row values for one head from its raw rows, written to R
+// (lanes 0..31); returns the block's log2 decay as seen by the state carry
+// (-inf when a document starts inside the block: nothing before the reset
+// reaches the block's end).
 template <bool SEQ>
 __device__ __forceinline__ float rows_prep(Rows &R, const RowIn &f, float a2, float bias,
                                            int softplus, float lo, float hi, int k, int rows,
                                            int lane) {
     const int r = lane & 31;
-    const bool valid = k * T + r < rows;
-    const float d = valid ? time_step(f.dt, bias, softplus, lo, hi) : 0.f;
+    float d = 0.f;
+    if (k * T + r < rows) {
+        const float z = __builtin_bit_cast(float, f.dt << 16) + bias;
+        d = softplus ? softplus_fast(z) : z;
+        d = d < lo ? lo : d;
+        d = d > hi ? hi : d;
+    }
     float a = a2 * d;
     // inclusive prefix sum over the block's 32 rows (each 32-lane half)
 #pragma unroll
@@ -276,7 +328,10 @@ __device__ __forceinline__ float rows_prep(Rows &R, const RowIn &f, float a2, fl
     float lam = last;
     int seg = -1;
     if constexpr (SEQ) {
-        const uint32_t m = (uint32_t)(__ballot(f.rst != 0) >> (lane & 32));
+        // a row whose document index differs from the previous token's
+        // starts from a zero state (token 0 starts from the initial state)
+        const bool rst = k * T + r < rows && f.cur != f.prv;
+        const uint32_t m = (uint32_t)(__ballot(rst) >> (lane & 32));
         if (m) {
             if (r < 31 - __builtin_clz(m)) w = 0.f;
             lam = -INFINITY;
@@ -291,9 +346,10 @@ __device__ __forceinline__ float rows_prep(Rows &R, const RowIn &f, float a2, fl
         R.a2[row_pair(r)] = exp2_fast(a - l15);
         R.l2[row_pair(r)] = a;
         R.bw[r] = exp2_fast(l15 - a) * d;
+        R.lam = lam;
         if constexpr (SEQ) R.seg[r] = seg;
     }
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lam)));
+    return lam;
 }
 
 // Power-of-two scale of an fp16 store: m (>= the largest magnitude) times
@@ -306,187 +362,225 @@ __device__ __forceinline__ int scale_exp(float m) {
 }
 
 // --------------------------------------------------- work items ----
-// Item = (batch, chunk, HP consecutive heads of one group), heads fastest.
-// Workgroups take items round robin from a worker index that keeps
-// consecutive indices on one XCD (xcd_item), so the heads of one (batch,
+// Item = (batch, chunk, HP consecutive heads of one group), heads fastest;
+// one workgroup per item.  Workgroup ids go to the 8 XCDs round robin, and
+// xcd_item keeps consecutive items on one XCD, so the heads of one (batch,
 // chunk) meet in that XCD's L2.
 struct Item {
-    int64_t b, c;
-    int hh0, gi, rows, nblk;
-    int64_t t0;
-    bool live;
+    int64_t b, t0;  // batch row, the chunk's first token
+    int c, hh0, gi, rows, nblk;
 };
-__device__ __forceinline__ Item decode_item(int64_t item, int64_t items, int64_t nc_items,
-                                            int hpg_items, int h, int g, int64_t l, int64_t Q,
-                                            int HP) {
+__device__ __forceinline__ Item decode_item(int64_t item, int nc, int hpg, int h, int g,
+                                            int64_t l, int64_t Q, int HP) {
     Item it;
-    it.live = item < items;
-    const int64_t q = it.live ? item : 0;
-    const int hq = (int)(q % hpg_items);
-    const int64_t bc = q / hpg_items;
-    it.c = bc % nc_items;
-    it.b = bc / nc_items;
+    const int hq = (int)(item % hpg);
+    const int64_t bc = item / hpg;
+    it.c = (int)(bc % nc);
+    it.b = bc / nc;
     it.hh0 = hq * HP;
     it.gi = it.hh0 / (h / g);
-    it.t0 = it.c * Q;
+    it.t0 = (int64_t)it.c * Q;
     const int64_t rem = l - it.t0;
     it.rows = (int)(rem < Q ? rem : Q);
-    it.nblk = it.live ? (it.rows + T - 1) / T : 0;
+    it.nblk = (it.rows + T - 1) / T;
     return it;
 }
 
-// The 16-byte copies of one block into LDS buffer `buf` ([x of each head |
-// B | C], C only WITH_C): wave instruction q of the block copies 64
-// consecutive slots;
-// each lane fetches the 16-byte source chunk its (swizzled) slot holds.
-// Rows past the chunk's end read as zeros.  Each wave issues exactly
-// per_wave<WITH_C>() copies (the spare slot takes the rest).
-template <int P, int N, int HP, bool WITH_C>
-__device__ __forceinline__ void block_copy(f16 *buf, f16 *spare, const bf16 *x, const bf16 *B,
-                                           const bf16 *C, int64_t xs, int64_t bs, int valid,
-                                           int wave, int lane) {
+// LDS block buffer: [x of each head | B | C], B and C offset by 128 bytes
+// from a bank-aligned position so that reads of B and C at the same
+// in-matrix offset (which the compiler pairs into one instruction) fall in
+// different banks.
+template <int P, int N, int HP> struct Buf {
     typedef Shape<P, N, HP> K;
-    constexpr int CH = P / 8, CB = N / 8;
-    const Rsrc rx = make_rsrc(x, (int64_t)valid * xs * 2);
-    const Rsrc rb = make_rsrc(B, (int64_t)valid * bs * 2);
-    const Rsrc rc = make_rsrc(WITH_C ? C : B, WITH_C ? (int64_t)valid * bs * 2 : 0);
+    static constexpr int XB = 0, BB = K::XE + 64, CB = BB + K::BE + 64;
+    // buffer sizes a multiple of N elements (see FragBase)
+    static constexpr int SIZE_B = (BB + K::BE + N - 1) / N * N;
+    static constexpr int SIZE_BC = (CB + K::BE + N - 1) / N * N;
+};
+
+// Per-lane source offsets (bytes, inside a block) of the block copies of
+// one wave: instruction j of the wave is wave instruction q = wave + j W of
+// the block; x first (XI instructions), then B (BI), then C (BI, WITH_C).
+// Each lane fetches the 16-byte source chunk its swizzled LDS slot holds.
+template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
+    typedef Shape<P, N, HP> K;
+    static constexpr int NJ = K::template per_wave<WITH_C>();
+    // When the x and B blocks are whole multiples of W instructions, all W
+    // instructions j W .. j W + W - 1 copy the same matrix, so which one a
+    // wave's instruction j copies is known at compile time.
+    static constexpr bool STATIC = K::XI % K::W == 0 && K::BI % K::W == 0;
+    __device__ static __forceinline__ int klass(int j, int q) { return STATIC ? j * K::W : q; }
+    uint32_t off[NJ];
+    __device__ __forceinline__ void init(int64_t xs, int64_t bs, int wave, int lane) {
+        constexpr int CH = P / 8, CB = N / 8;
 #pragma unroll
-    for (int j = 0; j < K::template per_wave<WITH_C>(); ++j) {
-        const int q = wave + j * K::W;
-        if (q < K::XI) {
-            const int s = q * 64 + lane;
-            const int hs = s / (T * CH), rem = s % (T * CH), r = rem / CH, kk = rem % CH;
-            const uint32_t off =
-                (uint32_t)(r * xs + hs * P + ((kk ^ xsw<P>(r)) << 3)) * 2u;
-            lds_copy16(rx, (lds_void *)(buf + q * 512), off);
-        } else if (q < K::XI + K::BI * (WITH_C ? 2 : 1)) {
-            const int qb = q - K::XI;
-            const bool isC = WITH_C && qb >= K::BI;
-            const int s = (isC ? qb - K::BI : qb) * 64 + lane;
-            const int r = s / CB, kk = s % CB;
-            const uint32_t off = (uint32_t)(r * bs + ((kk ^ Swz<f16, N>::f(r)) << 3)) * 2u;
-            lds_copy16(isC ? rc : rb, (lds_void *)(buf + q * 512), off);
-        } else {
-            lds_copy16(rc, (lds_void *)spare, 0u);
+        for (int j = 0; j < NJ; ++j) {
+            const int q = wave + j * K::W, qc = klass(j, q);
+            if (qc < K::XI) {
+                const int s = q * 64 + lane;
+                const int hs = s / (T * CH), rem = s % (T * CH), r = rem / CH, kk = rem % CH;
+                off[j] = (uint32_t)(r * xs + hs * P + ((kk ^ xsw<P>(r)) << 3)) * 2u;
+            } else if (qc < K::XI + K::BI * (WITH_C ? 2 : 1)) {
+                const int qb = q - K::XI;
+                const int s = (qb % K::BI) * 64 + lane;
+                const int r = s / CB, kk = s % CB;
+                off[j] = (uint32_t)(r * bs + ((kk ^ Swz<f16, N>::f(r)) << 3)) * 2u;
+            } else {
+                off[j] = 0u;
+            }
         }
     }
-}
+    // Copies block rows r0.. (valid rows) of x (from xrow0, the WG's first
+    // head), B and C (from their row r0) into LDS buffer buf.
+    __device__ __forceinline__ void copy(f16 *buf, f16 *spare, const bf16 *x, const bf16 *B,
+                                         const bf16 *C, int64_t xs, int64_t bs, int valid,
+                                         int wave) const {
+        typedef Buf<P, N, HP> L;
+        const RsrcW rx = make_rsrc_w(x, (int64_t)valid * xs * 2);
+        const RsrcW rb = make_rsrc_w(B, (int64_t)valid * bs * 2);
+        const RsrcW rc = make_rsrc_w(WITH_C ? C : B, WITH_C ? (int64_t)valid * bs * 2 : 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int q = wave + j * K::W, qc = klass(j, q);
+            if (qc < K::XI) {
+                lds_dma16(rx, (lds_void *)(buf + L::XB + q * 512), off[j]);
+            } else if (qc < K::XI + K::BI) {
+                lds_dma16(rb, (lds_void *)(buf + L::BB + (q - K::XI) * 512), off[j]);
+            } else if (WITH_C && qc < K::XI + 2 * K::BI) {
+                lds_dma16(rc, (lds_void *)(buf + L::CB + (q - K::XI - K::BI) * 512), off[j]);
+            } else {
+                lds_dma16(rc, (lds_void *)spare, 0u);
+            }
+        }
+    }
+};
 
 // ----------------------------------------------------------------------------
-// 1. Chunk states: every item's chunk from a zero state,
+// 1. Chunk states: one workgroup per item; its chunk from a zero state,
 //        S <- 2^lam S + B^T (w x)   per block,
 //    each wave holding its head_dim columns of its head's state (all
-//    state_dim rows) in MFMA accumulators.  At an item's end the state is
-//    stored transposed ([head_dim][state_dim]) as fp16 times 2^(15 - e),
-//    e the exponent of the head's largest magnitude m (written as Smax),
-//    with the chunk's total log2 decay (Lam); chunk-0 items also write the
-//    largest magnitude of the initial state of their heads (Imax).
+//    state_dim rows) in MFMA accumulators.  The first wave of every head
+//    computes that head's per-row values of the next block while the
+//    current one is multiplied.  At the end the state is stored transposed
+//    ([head_dim][state_dim]) as fp16 times 2^(15 - e), e the exponent of the
+//    head's largest magnitude m (written as Smax), with the chunk's total
+//    log2 decay (Lam); chunk-0 items also write the largest magnitude of the
+//    initial state of their heads (Imax).
 template <int P, int N, int HP, bool SEQ>
 __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, const int32_t *__restrict__ seq, const float *__restrict__ init,
     f16 *__restrict__ St, float *__restrict__ Smax, float *__restrict__ Lam,
-    float *__restrict__ Imax, int64_t l, int h, int g, int64_t Q, int64_t nc, int64_t nc_items,
-    int64_t items) {
+    float *__restrict__ Imax, int64_t l, int h, int g, int64_t Q, int nc, int nc_items) {
     typedef Shape<P, N, HP> K;
-    constexpr int BUF = K::XE + K::BE, CPW = K::CPW, RT = K::RT, WPH = K::WPH;
-    __shared__ __attribute__((aligned(16))) f16 lds0[BUF];
-    __shared__ __attribute__((aligned(16))) f16 lds1[BUF];
-    __shared__ __attribute__((aligned(16))) f16 spare[512];
-    __shared__ Rows rows0[K::W];
-    __shared__ Rows rows1[K::W];
+    typedef Buf<P, N, HP> L;
+    constexpr int CPW = K::CPW, RT = K::RT, WPH = K::WPH;
+    __shared__ __attribute__((aligned(16))) f16 lds[2 * L::SIZE_B];
+    __shared__ __attribute__((aligned(16))) f16 spare[CopyPlan<P, N, HP, false>::STATIC ? 8 : 512];
+    __shared__ Rows rows[2][HP];
     __shared__ float wmax[K::W], wimax[K::W];
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int hs = wave / WPH, c0 = (wave % WPH) * K::PW;
-    const int64_t G = gridDim.x;
-    const int64_t v = xcd_item(blockIdx.x, G);
-    const int hpg = h / HP;
-    const int64_t NP = (int64_t)N * P;
+    const int hs = wave / WPH, part = wave % WPH, c0 = part * K::PW;
     const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N;
+    const Item it = decode_item(xcd_item(blockIdx.x, gridDim.x), nc_items, h / HP, h, g, l, Q,
+                                HP);
+    const int hh = it.hh0 + hs;
+    const bf16 *xb = x + ((it.b * l + it.t0) * h + it.hh0) * P;
+    const bf16 *bb = Bm + ((it.b * l + it.t0) * g + it.gi) * N;
+    const bf16 *dtb = dt + (it.b * l + it.t0) * h + hh;
+    const int32_t *sq = SEQ ? seq + it.b * l : nullptr;
+    const float a2 = A[hh] * kLog2e;
+    const float bias = dt_bias ? dt_bias[hh] : 0.f;
 
-    int64_t item = v;
-    Item it = decode_item(item, items, nc_items, hpg, h, g, l, Q, HP);
-    if (!it.live) return;
-
-    auto rsrc_of = [&](const Item &q) {
-        RowSrc rs;
-        rs.dt = dt + (q.b * l + q.t0) * h + q.hh0 + hs;
-        rs.seq = SEQ ? seq + q.b * l : nullptr;
-        rs.t0 = q.t0;
-        rs.l = l;
-        rs.h = h;
-        rs.rows = q.rows;
-        return rs;
-    };
-    auto copy = [&](f16 *buf, const Item &q, int k) {
-        int valid = q.live ? q.rows - k * T : 0;
+    CopyPlan<P, N, HP, false> cp;
+    cp.init(xs, bs, wave, lane);
+    auto copy = [&](f16 *buf, int k) {
+        int valid = it.rows - k * T;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const int64_t r0 = valid > 0 ? q.t0 + (int64_t)k * T : 0;
-        block_copy<P, N, HP, false>(buf, spare, x + ((q.b * l + r0) * h + q.hh0) * P,
-                                    Bm + ((q.b * l + r0) * g + q.gi) * N, nullptr, xs, bs, valid,
-                                    wave, lane);
+        const int64_t r0 = valid > 0 ? (int64_t)k * T : 0;
+        cp.copy(buf, spare, xb + r0 * xs, bb + r0 * bs, nullptr, xs, bs, valid, wave);
     };
 
-    float a2 = A[it.hh0 + hs] * kLog2e;
-    float bias = dt_bias ? dt_bias[it.hh0 + hs] : 0.f;
-    RowSrc rs = rsrc_of(it);
-
-    // prologue: block 0 of the first item
+    // the chunk's first block
     RowIn ri;
-    rows_load<SEQ>(ri, rs, 0, lane);
-    copy(lds0, it, 0);
+    rows_load<SEQ>(ri, dtb, sq, it.t0, l, h, it.rows, 0, lane);
+    copy(lds, 0);
     vm_wait<0>();
-    float lam = rows_prep<SEQ>(rows0[wave], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows,
-                               lane);
+    if (part == 0)
+        rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, lane);
 
     f32x4 acc[CPW * RT];
 #pragma unroll
     for (int t = 0; t < CPW * RT; ++t) acc[t] = zero4();
     float logdec = 0.f;
-    int k = 0;  // block of the current item
 
-    // Stores the finished item's state (its wave maxima are in wmax).
-    auto finish = [&](const Item &q) {
-        float m = 0.f, mi = 0.f;
+    FragBase<P, N, CPW> fb;
+    fb.init(c0, lane);
+
+    // One block (in the buffer at element offset bo): the state decays by
+    // the block's total and takes its rows.
+    auto compute = [&](int bo, const Rows &R) {
+        const int ln = opaque(lane);
+        const int bx = opaque(fb.x + bo), bk = opaque(fb.kmaj + bo);
+        const Neg1 nm = neg1();
+        const float lm = R.lam;
+        logdec += lm;
+        const float dec = exp2_fast(lm);
 #pragma unroll
-        for (int w2 = 0; w2 < WPH; ++w2) {
-            m = fmaxf(m, wmax[hs * WPH + w2]);
-            mi = fmaxf(mi, wimax[hs * WPH + w2]);
-        }
-        const int ex = scale_exp(m);
-        const float inv = ldexpf(1.f, 15 - ex);
-        const int hh = q.hh0 + hs;
-        f16 *dst = St + ((q.b * nc + q.c) * h + hh) * NP;
+        for (int t = 0; t < CPW * RT; ++t) acc[t] *= dec;
+        const f16 *Xs = lds + L::XB + hs * T * P;
+        const f16 *Bs = lds + L::BB;
+        HL xw[CPW];
 #pragma unroll
-        for (int u = 0; u < CPW; ++u)
+        for (int u = 0; u < CPW; ++u) xw[u] = xw_split(frag_x<P>(Xs, bx, u), ln, R.w, nm);
 #pragma unroll
-            for (int tr = 0; tr < RT; ++tr) {
-                const f32x4 s = acc[u * RT + tr] * inv;
-                *reinterpret_cast<f16x4 *>(dst + (c0 + col_of<CPW>(u, lane & 15)) * N + tr * 16 +
-                                           4 * (lane >> 4)) =
-                    f16x4{(f16)s[0], (f16)s[1], (f16)s[2], (f16)s[3]};
+        for (int tr = 0; tr < RT; ++tr) {
+            const bf16x8 bt = frag_kmaj<N>(Bs, bk, tr);
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) {
+                acc[u * RT + tr] = mma(bt, xw[u].hi, acc[u * RT + tr]);
+                acc[u * RT + tr] = mma(bt, xw[u].lo, acc[u * RT + tr]);
             }
-        if (c0 == 0 && lane == 0) {
-            Smax[(q.b * h + hh) * nc + q.c] = m;
-            Lam[(q.b * h + hh) * nc + q.c] = logdec;
-            if (init && q.c == 0) Imax[q.b * h + hh] = mi;
         }
     };
-    // The wave's largest magnitudes of the finished item (and of its heads'
-    // initial state on chunk-0 items), for finish() after the next barrier.
-    auto wave_max = [&](const Item &q) {
+
+    // Block k in LDS buffer k & 1.  At the top of a block the barrier tells
+    // that its copy and rows have landed and that every wave is done with the
+    // other buffer, into which the next block is then copied.
+    for (int k = 0; k < it.nblk; ++k) {
+        const int cur = k & 1;
+        lds_barrier();
+        const bool more = k + 1 < it.nblk;
+        // every wave loads the rows (past the chunk's end they read as
+        // zero), so that the loaded registers need no merge before use
+        RowIn rn;
+        rows_load<SEQ>(rn, dtb, sq, it.t0, l, h, it.rows, k + 1, lane);
+        if (more) copy(lds + (cur ^ 1) * L::SIZE_B, k + 1);
+        issue_fence();
+        compute(cur * L::SIZE_B, rows[cur][hs]);
+        vm_wait<0>();
+        // the head's waves take turns at the next block's rows
+        if (more && part == (k + 1) % WPH)
+            rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
+                           it.rows, lane);
+    }
+
+    // ---- the chunk's state: fp16 times a power of two per head
+    const bool first = init != nullptr && it.c == 0;
+    {
         float m = 0.f;
 #pragma unroll
         for (int t = 0; t < CPW * RT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(acc[t][e]));
         float mi = 0.f;
-        if (init && q.c == 0) {
-            const float *src = init + (q.b * h + q.hh0 + hs) * NP;
-            const int part = wave % WPH;
-            for (int64_t e = (int64_t)(part * 64 + lane) * 4; e < NP; e += 64 * WPH * 4) {
+        if (first) {
+            // the initial state's largest magnitude, for the bound on the
+            // boundary states' size
+            const float *src = init + (it.b * h + hh) * (int64_t)N * P;
+            for (int e = (part * 64 + lane) * 4; e < N * P; e += 64 * WPH * 4) {
                 const f32x4 iv = *reinterpret_cast<const f32x4 *>(src + e);
                 mi = fmaxf(mi, fmaxf(fmaxf(fabsf(iv[0]), fabsf(iv[1])),
                                      fmaxf(fabsf(iv[2]), fabsf(iv[3]))));
@@ -501,86 +595,29 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
             wmax[wave] = m;
             wimax[wave] = mi;
         }
-    };
-
-    // One block: the state decays by the block's total and takes its rows.
-    auto compute = [&](const f16 *buf, const Rows &R, float lm) {
-        const float dec = exp2_fast(lm);
+    }
+    lds_barrier();
+    float m = 0.f, mi = 0.f;
 #pragma unroll
-        for (int t = 0; t < CPW * RT; ++t) acc[t] *= dec;
-        const f16 *Xs = buf + hs * T * P;
-        const f16 *Bs = buf + K::XE;
-        HL xw[CPW];
+    for (int w2 = 0; w2 < WPH; ++w2) {
+        m = fmaxf(m, wmax[hs * WPH + w2]);
+        mi = fmaxf(mi, wimax[hs * WPH + w2]);
+    }
+    const float inv = ldexpf(1.f, 15 - scale_exp(m));
+    f16 *dst = St + (((int64_t)it.b * nc + it.c) * h + hh) * (int64_t)N * P;
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) xw[u] = xw_split(x_frag<CPW, P>(Xs, c0, u, lane), lane, R.w);
+    for (int u = 0; u < CPW; ++u)
 #pragma unroll
         for (int tr = 0; tr < RT; ++tr) {
-            const bf16x8 bt = kmajor_frag<N>(Bs, tr * 16, lane);
-#pragma unroll
-            for (int u = 0; u < CPW; ++u) {
-                acc[u * RT + tr] = mma(bt, xw[u].hi, acc[u * RT + tr]);
-                acc[u * RT + tr] = mma(bt, xw[u].lo, acc[u * RT + tr]);
-            }
+            const f32x4 sv = acc[u * RT + tr] * inv;
+            *reinterpret_cast<f16x4 *>(dst + (c0 + col_of<CPW>(u, lane & 15)) * N +
+                                       state_row(tr, lane >> 4)) =
+                f16x4{(f16)sv[0], (f16)sv[1], (f16)sv[2], (f16)sv[3]};
         }
-    };
-
-    // Blocks go in pairs (LDS buffer 0, then 1) so that every access names
-    // its buffer statically.  At the top of a half: the block's copy and
-    // rows have landed; the barrier also tells that every wave is done with
-    // the other buffer, into which the next block is then copied.
-    bool pending = false;  // an item ended with the previous block
-    Item done = it;
-    for (;;) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f16 *const bk = half == 0 ? lds0 : lds1;
-            f16 *const bn = half == 0 ? lds1 : lds0;
-            Rows &Rk = half == 0 ? rows0[wave] : rows1[wave];
-            Rows &Rn = half == 0 ? rows1[wave] : rows0[wave];
-            lds_barrier();
-            if (pending) {
-                finish(done);
-#pragma unroll
-                for (int t = 0; t < CPW * RT; ++t) acc[t] = zero4();
-                logdec = 0.f;
-                pending = false;
-            }
-            // the next block: this item's next, or the next item's first
-            Item nx = it;
-            int kn = k + 1;
-            if (kn >= it.nblk) {
-                nx = decode_item(item + G, items, nc_items, hpg, h, g, l, Q, HP);
-                kn = 0;
-            }
-            const RowSrc rsn = nx.live ? rsrc_of(nx) : rs;
-            RowIn rn;
-            copy(bn, nx, kn);
-            rows_load<SEQ>(rn, rsn, nx.live ? kn : 1 << 20, lane);
-            issue_fence();
-            compute(bk, Rk, lam);
-            logdec += lam;
-            if (k + 1 >= it.nblk) {
-                wave_max(it);
-                pending = true;
-                done = it;
-            }
-            if (!nx.live) {
-                lds_barrier();
-                finish(done);
-                vm_wait<0>();
-                return;
-            }
-            vm_wait<0>();
-            if (kn == 0) {
-                item += G;
-                it = nx;
-                rs = rsn;
-                a2 = A[it.hh0 + hs] * kLog2e;
-                bias = dt_bias ? dt_bias[it.hh0 + hs] : 0.f;
-            }
-            k = kn;
-            lam = rows_prep<SEQ>(Rn, rn, a2, bias, softplus, dt_min, dt_max, k, it.rows, lane);
-        }
+    if (part == 0 && lane == 0) {
+        Smax[(it.b * h + hh) * nc + it.c] = m;
+        Lam[(it.b * h + hh) * nc + it.c] = logdec;
+        if (first) Imax[it.b * h + hh] = mi;
     }
 }
 
@@ -677,125 +714,109 @@ __global__ __launch_bounds__(256) void k_scan16(
 }
 
 // ----------------------------------------------------------------------------
-// 3. Chunk output: every item's chunk from its boundary state.  Each wave
-//    seeds its head_dim columns of the running state H (all state_dim rows,
-//    MFMA accumulators) from the stored boundary state and walks the chunk's
-//    blocks; per block:
+// 3. Chunk output: one workgroup per item, its chunk from its boundary
+//    state.  Each wave seeds its head_dim columns of the running state H
+//    (all state_dim rows, MFMA accumulators) from the stored boundary state
+//    and walks the chunk's blocks; per block:
 //      G^T = B C^T on the 3 causal 16 x 16 tiles, and
 //      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i) in registers;
 //      y^T = 2^lcs_i (H^T C^T) + x^T (P + D I)^T (the skip term on the
 //            scores' diagonal), stored straight from the accumulators;
-//      H <- 2^lcs_last H + B^T (w x)  (except after the item's last block).
+//      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
 //    The scores and the read-out share the C fragments.  The decay factor
 //    of P is taken as a_i b_j with a_i = 2^(lcs_i - lcs_15) and
 //    b_j = 2^(lcs_15 - lcs_j) d_j when the block's total log2 decay is above
 //    -kSplit (every factor then stays inside fp32's normal range); otherwise
-//    as one exponential per element.  In an item's last block, once the
-//    read-out has taken H, the next item's boundary state is requested into
-//    the same registers.
+//    as one exponential per element.  The first wave of every head computes
+//    that head's per-row values of the next block.
 constexpr float kSplit = 60.f;
 
 template <int P, int N, int HP, bool SEQ>
-__global__ __launch_bounds__((Shape<P, N, HP>::NT), 2) void k_out16(
+__global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const bf16 *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ D,
     const float *__restrict__ dt_bias, int softplus, float dt_min, float dt_max,
     const int32_t *__restrict__ seq, const f16 *__restrict__ Hb, const float *__restrict__ Hs,
-    bf16 *__restrict__ y, int64_t l, int h, int g, int64_t Q, int64_t nc, int has_init,
-    int64_t items) {
+    bf16 *__restrict__ y, int64_t l, int h, int g, int64_t Q, int nc, int has_init) {
     typedef Shape<P, N, HP> K;
-    constexpr int BUF = K::XE + 2 * K::BE, CPW = K::CPW, RT = K::RT, WPH = K::WPH,
-                  NB = K::NB, NS = K::NS;
-    __shared__ __attribute__((aligned(16))) f16 lds0[BUF];
-    __shared__ __attribute__((aligned(16))) f16 lds1[BUF];
-    __shared__ __attribute__((aligned(16))) f16 spare[512];
-    __shared__ Rows rows0[K::W];
-    __shared__ Rows rows1[K::W];
+    typedef Buf<P, N, HP> L;
+    constexpr int CPW = K::CPW, RT = K::RT, WPH = K::WPH, NB = K::NB, NS = K::NS;
+    __shared__ __attribute__((aligned(16))) f16 lds[2 * L::SIZE_BC];
+    __shared__ __attribute__((aligned(16))) f16 spare[CopyPlan<P, N, HP, true>::STATIC ? 8 : 512];
+    __shared__ Rows rows[2][HP];
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int lg = lane >> 4, li = lane & 15;
-    const int hs = wave / WPH, c0 = (wave % WPH) * K::PW;
-    const int64_t G = gridDim.x;
-    const int64_t v = xcd_item(blockIdx.x, G);
-    const int hpg = h / HP;
-    const int64_t NP = (int64_t)N * P;
+    const int hs = wave / WPH, part = wave % WPH, c0 = part * K::PW;
     const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N;
+    const Item it = decode_item(xcd_item(blockIdx.x, gridDim.x), nc, h / HP, h, g, l, Q, HP);
+    const int hh = it.hh0 + hs;
+    const bf16 *xb = x + ((it.b * l + it.t0) * h + it.hh0) * P;
+    bf16 *yb = y + ((it.b * l + it.t0) * h + it.hh0) * P;
+    const int64_t bo = ((it.b * l + it.t0) * g + it.gi) * N;
+    const bf16 *bb = Bm + bo, *cb = Cm + bo;
+    const bf16 *dtb = dt + (it.b * l + it.t0) * h + hh;
+    const int32_t *sq = SEQ ? seq + it.b * l : nullptr;
+    const float a2 = A[hh] * kLog2e;
+    const float bias = dt_bias ? dt_bias[hh] : 0.f;
+    const float Dh = D ? D[hh] : 0.f;
 
-    int64_t item = v;
-    Item it = decode_item(item, items, nc, hpg, h, g, l, Q, HP);
-    if (!it.live) return;
-
-    auto rsrc_of = [&](const Item &q) {
-        RowSrc rs;
-        rs.dt = dt + (q.b * l + q.t0) * h + q.hh0 + hs;
-        rs.seq = SEQ ? seq + q.b * l : nullptr;
-        rs.t0 = q.t0;
-        rs.l = l;
-        rs.h = h;
-        rs.rows = q.rows;
-        return rs;
-    };
-    auto copy = [&](f16 *buf, const Item &q, int k) {
-        int valid = q.live ? q.rows - k * T : 0;
+    CopyPlan<P, N, HP, true> cp;
+    cp.init(xs, bs, wave, lane);
+    auto copy = [&](f16 *buf, int k) {
+        int valid = it.rows - k * T;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const int64_t r0 = valid > 0 ? q.t0 + (int64_t)k * T : 0;
-        const int64_t bo = ((q.b * l + r0) * g + q.gi) * N;
-        block_copy<P, N, HP, true>(buf, spare, x + ((q.b * l + r0) * h + q.hh0) * P, Bm + bo,
-                                   Cm + bo, xs, bs, valid, wave, lane);
+        const int64_t r0 = valid > 0 ? (int64_t)k * T : 0;
+        cp.copy(buf, spare, xb + r0 * xs, bb + r0 * bs, cb + r0 * bs, xs, bs, valid, wave);
     };
 
+    // the chunk's first block and the wave's columns of the boundary state
+    // (fp16 times the chunk's scale; zero for chunk 0 without an initial
+    // state)
+    RowIn ri;
+    rows_load<SEQ>(ri, dtb, sq, it.t0, l, h, it.rows, 0, lane);
+    copy(lds, 0);
     f32x4 accH[CPW * RT];
-    // Requests the item's boundary state into accH (fp16 bits in the low
-    // half of each register quad; 16 operations per lane).
-    auto h_load = [&](const Item &q) {
-        const int hh = q.hh0 + hs;
-        const bool have = q.live && (q.c > 0 || has_init);
-        const Rsrc rh = make_rsrc(Hb + ((q.b * nc + q.c) * h + hh) * NP, have ? NP * 2 : 0);
+    {
+        const bool have = it.c > 0 || has_init;
+        const Rsrc rh = make_rsrc(Hb + (((int64_t)it.b * nc + it.c) * h + hh) * (int64_t)N * P,
+                                  have ? (int64_t)N * P * 2 : 0);
+        u32x2 raw[CPW * RT];
 #pragma unroll
         for (int u = 0; u < CPW; ++u)
 #pragma unroll
-            for (int tr = 0; tr < RT; ++tr) {
-                const uint32_t off =
-                    (uint32_t)((c0 + col_of<CPW>(u, li)) * N + tr * 16 + 4 * lg) * 2u;
-                const u32x2 raw = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(rh, off, 0, 0));
-                accH[u * RT + tr] = f32x4{as_f32(raw[0]), as_f32(raw[1]), 0.f, 0.f};
-            }
-    };
-    auto h_convert = [&](const Item &q) {
-        const int hh = q.hh0 + hs;
-        const bool have = q.c > 0 || has_init;
-        const float sc = have ? Hs[(q.b * h + hh) * nc + q.c] : 0.f;
+            for (int tr = 0; tr < RT; ++tr)
+                raw[u * RT + tr] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                               rh, (uint32_t)((c0 + col_of<CPW>(u, li)) * N + state_row(tr, lg)) * 2u,
+                               0, 0));
+        const float sc = have ? Hs[((int64_t)it.b * h + hh) * nc + it.c] : 0.f;
+        vm_wait<0>();
 #pragma unroll
         for (int t = 0; t < CPW * RT; ++t) {
-            const f16x4 hv =
-                __builtin_bit_cast(f16x4, u32x2{as_u32(accH[t][0]), as_u32(accH[t][1])});
+            const f16x4 hv = __builtin_bit_cast(f16x4, raw[t]);
             accH[t] = f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]} * sc;
         }
-    };
+    }
+    if (part == 0)
+        rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, lane);
 
-    float a2 = A[it.hh0 + hs] * kLog2e;
-    float bias = dt_bias ? dt_bias[it.hh0 + hs] : 0.f;
-    float Dh = D ? D[it.hh0 + hs] : 0.f;
-    RowSrc rs = rsrc_of(it);
+    FragBase<P, N, CPW> fb;
+    fb.init(c0, lane);
+    // y offsets (bytes) of rows li and 16 + li of a block, from its first
+    // row: 8 consecutive columns c0 + 8 lg .. (two column tiles) or 4
+    // columns c0 + 4 lg .. (one)
+    const uint32_t yo0 = (uint32_t)(li * xs + hs * P + c0 + (CPW == 2 ? 8 : 4) * lg) * 2u;
+    const uint32_t yo1 = yo0 + (uint32_t)(16 * xs) * 2u;
 
-    RowIn ri;
-    rows_load<SEQ>(ri, rs, 0, lane);
-    copy(lds0, it, 0);
-    h_load(it);
-    vm_wait<0>();
-    rows_prep<SEQ>(rows0[wave], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, lane);
-    h_convert(it);
-    int k = 0;
-
-    // One block of one wave; `last`: the item's last block (no carry; the
-    // next item's boundary state is requested once the read-out is done).
-    auto compute = [&](const f16 *buf, const Rows &rf, const Item &q, int kb, bool last,
-                       const Item &nq) {
-        // buffer layout as block_copy fills it: [x of each head | B | C]
-        const f16 *Bs = buf + K::XE;
-        const f16 *Cs = buf + K::XE + K::BE;
-        const f16 *Xs = buf + hs * T * P;
+    // One block of one wave (in the buffer at element offset bo).
+    auto compute = [&](int bo, const Rows &rf, int kb, bool carry) {
+        const int ln = opaque(lane), lg = ln >> 4, li = ln & 15;
+        const int br = opaque(fb.rows + bo), bx = opaque(fb.x + bo), bk = opaque(fb.kmaj + bo);
+        const Neg1 nm = neg1();
+        const f16 *Bs = lds + L::BB;
+        const f16 *Cs = lds + L::CB;
+        const f16 *Xs = lds + L::XB + hs * T * P;
         // ---- G^T tiles and the state read-out, sharing the C fragments.
         //      gt[k]: tiles (it, jt) = (0,0), (1,0), (1,1); element r of lane
         //      l: j = 16 jt + 4 lg + r, i = 16 it + li.  yh[it][u]: H^T C^T
@@ -809,31 +830,25 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 2) void k_out16(
             for (int u = 0; u < CPW; ++u) yh[i2][u] = zero4();
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
-            const bf16x8 c0f = rows_frag<N>(Cs, 0, 32 * m, lane);
-            const bf16x8 c1f = rows_frag<N>(Cs, 16, 32 * m, lane);
-            const bf16x8 b0f = rows_frag<N>(Bs, 0, 32 * m, lane);
-            const bf16x8 b1f = rows_frag<N>(Bs, 16, 32 * m, lane);
+            const bf16x8 c0f = frag_rows(Cs, br, m);
+            const bf16x8 c1f = frag_rows(Cs + 16 * N, br, m);
+            const bf16x8 b0f = frag_rows(Bs, br, m);
+            const bf16x8 b1f = frag_rows(Bs + 16 * N, br, m);
             gt[0] = mma(b0f, c0f, gt[0]);
             gt[1] = mma(b0f, c1f, gt[1]);
             gt[2] = mma(b1f, c1f, gt[2]);
 #pragma unroll
             for (int u = 0; u < CPW; ++u) {
-                const HL hf = split_acc(accH[u * RT + 2 * m], accH[u * RT + 2 * m + 1]);
+                const HL hf = split_acc(accH[u * RT + 2 * m], accH[u * RT + 2 * m + 1], nm);
                 yh[0][u] = mma(hf.hi, c0f, yh[0][u]);
                 yh[0][u] = mma(hf.lo, c0f, yh[0][u]);
                 yh[1][u] = mma(hf.hi, c1f, yh[1][u]);
                 yh[1][u] = mma(hf.lo, c1f, yh[1][u]);
             }
         }
-        if (last) {
-            issue_fence();
-            h_load(nq);
-            issue_fence();
-        }
 
         // ---- masked, decayed scores pv[it][jt] (registers)
-        const float lam = __builtin_bit_cast(
-            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, rf.lcs[T - 1])));
+        const float lam = rf.lcs[T - 1];
         f32x4 pv[2][2];
         float colscale[2];
         pv[0][1] = zero4();
@@ -893,17 +908,16 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 2) void k_out16(
         // ---- y^T = colscale (H^T C^T) + x^T (P + D I)^T, straight to y:
         //      element r of lane l is (p = c0 + col_of(u, 4 lg + r), i = 16 it + li)
         const int r0 = kb * T;
-        int valid = q.rows - r0;
+        int valid = it.rows - r0;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const Rsrc ry = make_rsrc(y + ((q.b * l + q.t0 + (valid > 0 ? r0 : 0)) * h + q.hh0) * P,
+        const Rsrc ry = make_rsrc(yb + (valid > 0 ? (int64_t)r0 : 0) * xs,
                                   (int64_t)valid * xs * 2);
         bf16x8 xf[CPW];
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) xf[u] = x_frag<CPW, P>(Xs, c0, u, lane);
+        for (int u = 0; u < CPW; ++u) xf[u] = frag_x<P>(Xs, bx, u);
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-            const int i = i2 * 16 + li;
-            const HL pf = split_acc(pv[i2][0], pv[i2][1]);
+            const HL pf = split_acc(pv[i2][0], pv[i2][1], nm);
             f32x4 yv[CPW];
 #pragma unroll
             for (int u = 0; u < CPW; ++u) {
@@ -911,44 +925,31 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 2) void k_out16(
                 yp = mma(xf[u], pf.lo, yp);
                 yv[u] = colscale[i2] * yh[i2][u] + yp;
             }
-            if constexpr (CPW % 2 == 0) {
-                // tiles 2v, 2v + 1: 8 consecutive columns c0 + 32 v + 8 lg ..
-#pragma unroll
-                for (int vv = 0; vv < CPW / 2; ++vv) {
-                    const f32x4 lo = yv[2 * vv], hi = yv[2 * vv + 1];
-                    const uint32_t off =
-                        (uint32_t)(i * xs + hs * P + c0 + 32 * vv + 8 * lg) * 2u;
-                    const bf16x4 a{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3]};
-                    const bf16x4 bq{(bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
-                    const u32x2 ua = __builtin_bit_cast(u32x2, a),
-                                ub = __builtin_bit_cast(u32x2, bq);
-                    buf_store16(ry, off, u32x4{ua[0], ua[1], ub[0], ub[1]});
-                }
+            const uint32_t off = i2 == 0 ? yo0 : yo1;
+            if constexpr (CPW == 2) {
+                // the two tiles interleave: 8 consecutive columns c0 + 8 lg ..
+                const bf16x4 a{(bf16)yv[0][0], (bf16)yv[0][1], (bf16)yv[0][2], (bf16)yv[0][3]};
+                const bf16x4 bq{(bf16)yv[1][0], (bf16)yv[1][1], (bf16)yv[1][2], (bf16)yv[1][3]};
+                const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, bq);
+                buf_store16(ry, off, u32x4{ua[0], ua[1], ub[0], ub[1]});
             } else {
-#pragma unroll
-                for (int u = 0; u < CPW; ++u) {
-                    const uint32_t off =
-                        (uint32_t)(i * xs + hs * P + c0 + col_of<CPW>(u, 4 * lg)) * 2u;
-                    const bf16x4 o{(bf16)yv[u][0], (bf16)yv[u][1], (bf16)yv[u][2],
-                                   (bf16)yv[u][3]};
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), ry, off,
-                                                          0, 0);
-                }
+                const bf16x4 o{(bf16)yv[0][0], (bf16)yv[0][1], (bf16)yv[0][2], (bf16)yv[0][3]};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), ry, off, 0, 0);
             }
         }
 
-        // ---- carry the state to the next block of the item
-        if (!last) {
+        // ---- carry the state to the next block of the chunk
+        if (carry) {
             // packed sequences: nothing carried across a reset in the block
-            const float decay = (SEQ && rf.seg[T - 1] >= 0) ? 0.f : exp2_fast(lam);
+            const float decay = exp2_fast(rf.lam);
             HL xw[CPW];
 #pragma unroll
-            for (int u = 0; u < CPW; ++u) xw[u] = xw_split(xf[u], lane, rf.w);
+            for (int u = 0; u < CPW; ++u) xw[u] = xw_split(xf[u], ln, rf.w, nm);
 #pragma unroll
             for (int t = 0; t < CPW * RT; ++t) accH[t] *= decay;
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) {
-                const bf16x8 bt = kmajor_frag<N>(Bs, tr * 16, lane);
+                const bf16x8 bt = frag_kmaj<N>(Bs, bk, tr);
 #pragma unroll
                 for (int u = 0; u < CPW; ++u) {
                     accH[u * RT + tr] = mma(bt, xw[u].hi, accH[u * RT + tr]);
@@ -958,48 +959,26 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 2) void k_out16(
         }
     };
 
-    for (;;) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f16 *const bk = half == 0 ? lds0 : lds1;
-            f16 *const bn = half == 0 ? lds1 : lds0;
-            Rows &Rk = half == 0 ? rows0[wave] : rows1[wave];
-            Rows &Rn = half == 0 ? rows1[wave] : rows0[wave];
-            lds_barrier();
-            Item nx = it;
-            int kn = k + 1;
-            const bool last = kn >= it.nblk;
-            if (last) {
-                nx = decode_item(item + G, items, nc, hpg, h, g, l, Q, HP);
-                kn = 0;
-            }
-            const RowSrc rsn = nx.live ? rsrc_of(nx) : rs;
-            RowIn rn;
-            copy(bn, nx, kn);
-            rows_load<SEQ>(rn, rsn, nx.live ? kn : 1 << 20, lane);
-            issue_fence();
-            compute(bk, Rk, it, k, last, nx);
-            if (!nx.live) {
-                vm_wait<0>();
-                return;
-            }
-            // the next block's copy and rows (and with a new item its
-            // boundary state) have landed; only this block's y stores may
-            // still be in flight
-            vm_wait<NS>();
-            if (last) {
-                item += G;
-                it = nx;
-                rs = rsn;
-                a2 = A[it.hh0 + hs] * kLog2e;
-                bias = dt_bias ? dt_bias[it.hh0 + hs] : 0.f;
-                Dh = D ? D[it.hh0 + hs] : 0.f;
-            }
-            k = kn;
-            rows_prep<SEQ>(Rn, rn, a2, bias, softplus, dt_min, dt_max, k, it.rows, lane);
-            if (last) h_convert(it);
-        }
+    // Block k in LDS buffer k & 1, as in k_state16; only this block's y
+    // stores may still be in flight when a wave waits for the next block's
+    // copy.
+    for (int k = 0; k < it.nblk; ++k) {
+        const int cur = k & 1;
+        lds_barrier();
+        const bool more = k + 1 < it.nblk;
+        RowIn rn;
+        rows_load<SEQ>(rn, dtb, sq, it.t0, l, h, it.rows, k + 1, lane);
+        if (more) copy(lds + (cur ^ 1) * L::SIZE_BC, k + 1);
+        issue_fence();
+        compute(cur * L::SIZE_BC, rows[cur][hs], k, more);
+        vm_wait<NS>();
+        // the head's waves take turns at the next block's rows
+        if (more && part == (k + 1) % WPH)
+            rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
+                           it.rows, lane);
     }
+    // no copy may still be writing this workgroup's LDS when it exits
+    vm_wait<0>();
 }
 
 }  // namespace s16
@@ -1028,7 +1007,6 @@ hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     int64_t nc_state = keep_last ? pl.nc : pl.nc - 1;
     if (a.init && nc_state < 1) nc_state = 1;
     const bool seq = a.seq != nullptr;
-    const int cus = device_cus();
 
     auto launch_state = [&](auto hp_c, auto seq_c) -> hipError_t {
         constexpr int HP = decltype(hp_c)::value;
@@ -1036,24 +1014,21 @@ hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
         constexpr int NT = Shape<P, N, HP>::NT;
         const int64_t items = pl.b * nc_state * (h / HP);
         if (items <= 0) return hipSuccess;
-        int64_t G = (int64_t)cus * resident_per_cu<&k_state16<P, N, HP, SQ>>(NT);
-        G = G < items ? G : items;
-        return launch_timed(&k_state16<P, N, HP, SQ>, dim3((unsigned)G), dim3(NT), s, a.ev,
+        return launch_timed(&k_state16<P, N, HP, SQ>, dim3((unsigned)items), dim3(NT), s, a.ev,
                             kSlotState, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min,
                             a.dt_max, a.seq, a.init, St, Smax, Lam, Imax, pl.l, h, g, pl.Q,
-                            pl.nc, nc_state, items);
+                            (int)pl.nc, (int)nc_state);
     };
     auto launch_out = [&](auto hp_c, auto seq_c) -> hipError_t {
         constexpr int HP = decltype(hp_c)::value;
         constexpr bool SQ = decltype(seq_c)::value;
         constexpr int NT = Shape<P, N, HP>::NT;
         const int64_t items = pl.b * pl.nc * (h / HP);
-        int64_t G = (int64_t)cus * resident_per_cu<&k_out16<P, N, HP, SQ>>(NT);
-        G = G < items ? G : items;
-        return launch_timed(&k_out16<P, N, HP, SQ>, dim3((unsigned)G), dim3(NT), s, a.ev,
+        if (items <= 0) return hipSuccess;
+        return launch_timed(&k_out16<P, N, HP, SQ>, dim3((unsigned)items), dim3(NT), s, a.ev,
                             kSlotOut, x, Bm, Cm, dt, a.A, a.D, a.dt_bias, a.softplus, a.dt_min,
-                            a.dt_max, a.seq, Hb, Hs, y, pl.l, h, g, pl.Q, pl.nc,
-                            a.init != nullptr ? 1 : 0, items);
+                            a.dt_max, a.seq, Hb, Hs, y, pl.l, h, g, pl.Q, (int)pl.nc,
+                            a.init != nullptr ? 1 : 0);
     };
     typedef std::integral_constant<int, 1> One;
     typedef std::integral_constant<int, HPG> Grp;
