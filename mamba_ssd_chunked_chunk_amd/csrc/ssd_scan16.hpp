@@ -126,9 +126,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 
 // ------------------------------------------------------------ shapes ----
 // HP heads of one group per workgroup (they share the staged B and C),
-// WPH waves per head, each owning PW head_dim columns of its head.
+// WPH waves per head, each owning PW head_dim columns (CPW column tiles of
+// 16) of its head: one wave per head up to head_dim 64 (so the per-block
+// work that does not depend on the columns, the scores and the per-row
+// values, is done once per head), two for head_dim 128.
 template <int P, int N, int HP> struct Shape {
-    static constexpr int WPH = P >= 64 ? P / 32 : 1;
+    static constexpr int WPH = P >= 128 ? P / 64 : 1;
     static constexpr int PW = P / WPH;
     static constexpr int CPW = PW / 16;  // column tiles per wave
     static constexpr int W = HP * WPH, NT = 64 * W;
@@ -142,9 +145,15 @@ template <int P, int N, int HP> struct Shape {
     static constexpr int XI = XE / 8 / 64, BI = BE / 8 / 64;
     template <bool WITH_C> static constexpr int ninst() { return XI + BI * (WITH_C ? 2 : 1); }
     template <bool WITH_C> static constexpr int per_wave() { return (ninst<WITH_C>() + W - 1) / W; }
-    // y stores per lane and block (rows li and 16 + li)
-    static constexpr int NS = 2;
+    // y stores per lane and block (rows li and 16 + li; 8 columns a store)
+    static constexpr int NS = 2 * (CPW >= 2 ? CPW / 2 : 1);
+    // workgroups per compute unit the registers are budgeted for: waves
+    // holding a large state (more than 64 accumulator registers) get up to
+    // 256 registers (two waves per SIMD), others up to 168 (three)
+    static constexpr int WPS = CPW * RT > 16 ? 2 : 3;
+    static constexpr int MINB = WPS * 4 / W > 0 ? WPS * 4 / W : 1;
     static_assert(XE % 512 == 0 && BE % 512 == 0, "whole copy instructions");
+    static_assert(CPW == 1 || CPW == 2 || CPW == 4, "column tiles per wave");
 };
 
 // Raw bf16 x in LDS: row r of a head holds head_dim elements in 16-byte
@@ -198,20 +207,20 @@ __device__ __forceinline__ HL xw_split(const bf16x8 &xf, int lane, const float *
 //              32m + 8g + 7): rows ^ 32m; rows 16..31: + 16 N
 //   frag_kmaj  B^T of state-row tile 2m + h (k = the block rows 4g + r and
 //              16 + 4g + r): (kmaj ^ 32m) + 4h; rows 16..31: + 16 N
-//   frag_x     x of column tile u (k = the block rows): x + 4 u, rows
-//              16..31: + 16 P
+//   frag_x     x of column tile u (k = the block rows): (x ^ 32 (u >> 1))
+//              + 4 (u & 1), rows 16..31: + 16 P
 // (the XORs only touch bits below log2 N, and a block buffer's offset is a
 // multiple of N, so it can be added to the bases first).
 template <int P, int N, int CPW> struct FragBase {
     int rows, kmaj, x;
     __device__ __forceinline__ void init(int c0, int lane) {
-        static_assert(CPW == 1 || CPW == 2, "one or two column tiles per wave");
+
         typedef Swz<f16, N> S;
         const int g = lane >> 4, j = lane & 15;
         rows = j * N + ((g ^ S::f(j)) << 3);
         const int r = 4 * g + (j >> 2);
         kmaj = r * N + (((j & 3) ^ S::f(r)) << 3);
-        if constexpr (CPW == 2)
+        if constexpr (CPW >= 2)
             x = r * P + ((((c0 >> 3) + (j & 3)) ^ xsw<P>(r)) << 3);
         else
             x = r * P + ((((c0 >> 3) + ((j >> 1) & 1)) ^ xsw<P>(r)) << 3) + 4 * (j & 1);
@@ -232,7 +241,8 @@ template <int N> __device__ __forceinline__ bf16x8 frag_kmaj(const f16 *M, int b
     return as_bf16x8(ds_tr(M + o), ds_tr(M + o + 16 * N));
 }
 template <int P> __device__ __forceinline__ bf16x8 frag_x(const f16 *Xs, int base, int u) {
-    return as_bf16x8(ds_tr(Xs + base + 4 * u), ds_tr(Xs + base + 4 * u + 16 * P));
+    const int o = (base ^ (32 * (u >> 1))) + 4 * (u & 1);
+    return as_bf16x8(ds_tr(Xs + o), ds_tr(Xs + o + 16 * P));
 }
 
 // -------------------------------------------------- per-row values ----
@@ -242,14 +252,26 @@ template <int P> __device__ __forceinline__ bf16x8 frag_x(const f16 *Xs, int bas
 struct alignas(16) Rows {
     float lcs[T];  // cumulative log2 decay inside the block (inclusive)
     float d[T];    // processed time step (0 past the chunk's end)
-    float w[T];    // 2^(lcs_31 - lcs_j) d_j: weight in the state at the block's end
+    float w[T];    // weight of row j in the carried state (see rows_prep)
     float a2[T];   // 2^(lcs_i - lcs_15), pairs (i, i + 16) at 2 (i % 16)
     float l2[T];   // lcs_i in the same pairs
     float bw[T];   // 2^(lcs_15 - lcs_j) d_j
     int seg[T];    // packed sequences: the last row <= i of the block that starts a
                    // new document, or -1
-    float lam;     // the block's log2 decay for the state carry (-inf across a reset)
+    float lam;     // the block's log2 decay (-inf across a reset)
+    float dsh;     // deferred log2 decay D of the state entering the block
+    float mexp;    // rebasing blocks: the carried state is first scaled by 2^mexp
+    float next;    // D of the state leaving the block
+    int rebase;    // the block rebases the carried state (else it defers its decay)
 };
+// Deferred decay.  A carried state is held as H~ = 2^D H (D >= 0, uniform
+// per head), so a block whose rows leave D at most kDefer only adds its
+// rows, with weights w_j = 2^(D - lcs_j) d_j <= 2^kDefer d_j, and multiplies
+// nothing: its read-out scales row i by 2^(lcs_i - D), and the next block's
+// D grows by -lam.  A block that would take D past kDefer (or holds a reset)
+// rebases instead: H~ <- 2^(lam - D) H~ + B^T (w x) with w_j = 2^(lam - lcs_j)
+// d_j, and D = 0 after it.
+constexpr float kDefer = 32.f;
 __device__ __forceinline__ int row_pair(int r) { return 2 * (r & 15) + (r >> 4); }
 
 
@@ -300,13 +322,11 @@ __device__ __forceinline__ float softplus_fast(float z) {
 }
 
 // The block's per-row values for one head from its raw rows, written to R
-// (lanes 0..31); returns the block's log2 decay as seen by the state carry
-// (-inf when a document starts inside the block: nothing before the reset
-// reaches the block's end).
+// (lanes 0..31), for a state entering the block with deferred decay D.
 template <bool SEQ>
-__device__ __forceinline__ float rows_prep(Rows &R, const RowIn &f, float a2, float bias,
-                                           int softplus, float lo, float hi, int k, int rows,
-                                           int lane) {
+__device__ __forceinline__ void rows_prep(Rows &R, const RowIn &f, float a2, float bias,
+                                          int softplus, float lo, float hi, int k, int rows,
+                                          float D, int lane) {
     const int r = lane & 31;
     float d = 0.f;
     if (k * T + r < rows) {
@@ -324,16 +344,19 @@ __device__ __forceinline__ float rows_prep(Rows &R, const RowIn &f, float a2, fl
     }
     const float last = __shfl(a, T - 1, T);
     const float l15 = __shfl(a, 15, T);
-    float w = exp2_fast(last - a) * d;
     float lam = last;
     int seg = -1;
+    bool lazy = D - last <= kDefer;
+    float w = exp2_fast((lazy ? D : last) - a) * d;
     if constexpr (SEQ) {
         // a row whose document index differs from the previous token's
-        // starts from a zero state (token 0 starts from the initial state)
+        // starts from a zero state (token 0 starts from the initial state):
+        // the block rebases, nothing before its last reset is carried
         const bool rst = k * T + r < rows && f.cur != f.prv;
         const uint32_t m = (uint32_t)(__ballot(rst) >> (lane & 32));
         if (m) {
-            if (r < 31 - __builtin_clz(m)) w = 0.f;
+            lazy = false;
+            w = r < 31 - __builtin_clz(m) ? 0.f : exp2_fast(last - a) * d;
             lam = -INFINITY;
         }
         const uint32_t mr = m & ((2u << r) - 1u);
@@ -346,10 +369,15 @@ __device__ __forceinline__ float rows_prep(Rows &R, const RowIn &f, float a2, fl
         R.a2[row_pair(r)] = exp2_fast(a - l15);
         R.l2[row_pair(r)] = a;
         R.bw[r] = exp2_fast(l15 - a) * d;
-        R.lam = lam;
         if constexpr (SEQ) R.seg[r] = seg;
+        if (r == 0) {
+            R.lam = lam;
+            R.dsh = D;
+            R.mexp = lam - D;
+            R.next = lazy ? D - last : 0.f;
+            R.rebase = lazy ? 0 : 1;
+        }
     }
-    return lam;
 }
 
 // Power-of-two scale of an fp16 store: m (>= the largest magnitude) times
@@ -467,7 +495,7 @@ template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
 //    log2 decay (Lam); chunk-0 items also write the largest magnitude of the
 //    initial state of their heads (Imax).
 template <int P, int N, int HP, bool SEQ>
-__global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
+__global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) void k_state16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, const int32_t *__restrict__ seq, const float *__restrict__ init,
@@ -509,12 +537,14 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
     copy(lds, 0);
     vm_wait<0>();
     if (part == 0)
-        rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, lane);
+        rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, 0.f,
+                       lane);
 
     f32x4 acc[CPW * RT];
 #pragma unroll
     for (int t = 0; t < CPW * RT; ++t) acc[t] = zero4();
     float logdec = 0.f;
+    float dfin = 0.f;  // deferred decay of the state after the last block
 
     FragBase<P, N, CPW> fb;
     fb.init(c0, lane);
@@ -525,11 +555,12 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
         const int ln = opaque(lane);
         const int bx = opaque(fb.x + bo), bk = opaque(fb.kmaj + bo);
         const Neg1 nm = neg1();
-        const float lm = R.lam;
-        logdec += lm;
-        const float dec = exp2_fast(lm);
+        logdec += R.lam;
+        if (R.rebase) {
+            const float dec = exp2_fast(R.mexp);
 #pragma unroll
-        for (int t = 0; t < CPW * RT; ++t) acc[t] *= dec;
+            for (int t = 0; t < CPW * RT; ++t) acc[t] *= dec;
+        }
         const f16 *Xs = lds + L::XB + hs * T * P;
         const f16 *Bs = lds + L::BB;
         HL xw[CPW];
@@ -564,7 +595,8 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
         // the head's waves take turns at the next block's rows
         if (more && part == (k + 1) % WPH)
             rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
-                           it.rows, lane);
+                           it.rows, rows[cur][hs].next, lane);
+        dfin = rows[cur][hs].next;
     }
 
     // ---- the chunk's state: fp16 times a power of two per head
@@ -603,7 +635,10 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_state16(
         m = fmaxf(m, wmax[hs * WPH + w2]);
         mi = fmaxf(mi, wimax[hs * WPH + w2]);
     }
-    const float inv = ldexpf(1.f, 15 - scale_exp(m));
+    // the held state is 2^dfin times the chunk's state
+    const float undo = exp2_fast(-dfin);
+    m *= undo;
+    const float inv = ldexpf(1.f, 15 - scale_exp(m)) * undo;
     f16 *dst = St + (((int64_t)it.b * nc + it.c) * h + hh) * (int64_t)N * P;
 #pragma unroll
     for (int u = 0; u < CPW; ++u)
@@ -732,7 +767,7 @@ __global__ __launch_bounds__(256) void k_scan16(
 constexpr float kSplit = 60.f;
 
 template <int P, int N, int HP, bool SEQ>
-__global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
+__global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) void k_out16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const bf16 *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ D,
     const float *__restrict__ dt_bias, int softplus, float dt_min, float dt_max,
@@ -799,14 +834,15 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
         }
     }
     if (part == 0)
-        rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, lane);
+        rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, 0.f,
+                       lane);
 
     FragBase<P, N, CPW> fb;
     fb.init(c0, lane);
     // y offsets (bytes) of rows li and 16 + li of a block, from its first
-    // row: 8 consecutive columns c0 + 8 lg .. (two column tiles) or 4
-    // columns c0 + 4 lg .. (one)
-    const uint32_t yo0 = (uint32_t)(li * xs + hs * P + c0 + (CPW == 2 ? 8 : 4) * lg) * 2u;
+    // row: 8 consecutive columns c0 + 32 v + 8 lg .. (column tiles 2v,
+    // 2v + 1) or 4 columns c0 + 4 lg .. (one tile)
+    const uint32_t yo0 = (uint32_t)(li * xs + hs * P + c0 + (CPW >= 2 ? 8 : 4) * lg) * 2u;
     const uint32_t yo1 = yo0 + (uint32_t)(16 * xs) * 2u;
 
     // One block of one wave (in the buffer at element offset bo).
@@ -853,7 +889,8 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
         float colscale[2];
         pv[0][1] = zero4();
         if (lam > -kSplit) {
-            const float s15 = exp2_fast(rf.lcs[15]);
+            // the read-out scale 2^(lcs_i - D) as 2^(lcs_i - lcs_15) 2^(lcs_15 - D)
+            const float s15 = exp2_fast(rf.lcs[15] - rf.dsh);
             const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&rf.bw[4 * lg]);
             const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&rf.bw[16 + 4 * lg]);
             const f32x2 ap = *reinterpret_cast<const f32x2 *>(&rf.a2[2 * li]);
@@ -868,8 +905,8 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
             }
         } else {
             const f32x2 lp = *reinterpret_cast<const f32x2 *>(&rf.l2[2 * li]);
-            colscale[0] = exp2_fast(lp[0]);
-            colscale[1] = exp2_fast(lp[1]);
+            colscale[0] = exp2_fast(lp[0] - rf.dsh);
+            colscale[1] = exp2_fast(lp[1] - rf.dsh);
             const f32x4 lj0 = *reinterpret_cast<const f32x4 *>(&rf.lcs[4 * lg]);
             const f32x4 lj1 = *reinterpret_cast<const f32x4 *>(&rf.lcs[16 + 4 * lg]);
             const f32x4 dj0 = *reinterpret_cast<const f32x4 *>(&rf.d[4 * lg]);
@@ -926,12 +963,17 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
                 yv[u] = colscale[i2] * yh[i2][u] + yp;
             }
             const uint32_t off = i2 == 0 ? yo0 : yo1;
-            if constexpr (CPW == 2) {
-                // the two tiles interleave: 8 consecutive columns c0 + 8 lg ..
-                const bf16x4 a{(bf16)yv[0][0], (bf16)yv[0][1], (bf16)yv[0][2], (bf16)yv[0][3]};
-                const bf16x4 bq{(bf16)yv[1][0], (bf16)yv[1][1], (bf16)yv[1][2], (bf16)yv[1][3]};
-                const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, bq);
-                buf_store16(ry, off, u32x4{ua[0], ua[1], ub[0], ub[1]});
+            if constexpr (CPW >= 2) {
+                // tiles 2v, 2v + 1 interleave: 8 consecutive columns
+                // c0 + 32 v + 8 lg ..
+#pragma unroll
+                for (int v = 0; v < CPW / 2; ++v) {
+                    const f32x4 &ya = yv[2 * v], &yb2 = yv[2 * v + 1];
+                    const bf16x4 a{(bf16)ya[0], (bf16)ya[1], (bf16)ya[2], (bf16)ya[3]};
+                    const bf16x4 bq{(bf16)yb2[0], (bf16)yb2[1], (bf16)yb2[2], (bf16)yb2[3]};
+                    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, bq);
+                    buf_store16(ry, off + 64u * v, u32x4{ua[0], ua[1], ub[0], ub[1]});
+                }
             } else {
                 const bf16x4 o{(bf16)yv[0][0], (bf16)yv[0][1], (bf16)yv[0][2], (bf16)yv[0][3]};
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), ry, off, 0, 0);
@@ -940,13 +982,16 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
 
         // ---- carry the state to the next block of the chunk
         if (carry) {
-            // packed sequences: nothing carried across a reset in the block
-            const float decay = exp2_fast(rf.lam);
             HL xw[CPW];
 #pragma unroll
             for (int u = 0; u < CPW; ++u) xw[u] = xw_split(xf[u], ln, rf.w, nm);
+            // a rebasing block (packed sequences: one with a reset, which
+            // carries nothing from before it) scales the held state first
+            if (rf.rebase) {
+                const float dec = exp2_fast(rf.mexp);
 #pragma unroll
-            for (int t = 0; t < CPW * RT; ++t) accH[t] *= decay;
+                for (int t = 0; t < CPW * RT; ++t) accH[t] *= dec;
+            }
 #pragma unroll
             for (int tr = 0; tr < RT; ++tr) {
                 const bf16x8 bt = frag_kmaj<N>(Bs, bk, tr);
@@ -975,7 +1020,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), 3) void k_out16(
         // the head's waves take turns at the next block's rows
         if (more && part == (k + 1) % WPH)
             rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
-                           it.rows, lane);
+                           it.rows, rows[cur][hs].next, lane);
     }
     // no copy may still be writing this workgroup's LDS when it exits
     vm_wait<0>();
@@ -999,8 +1044,10 @@ hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     const bf16 *Cm = static_cast<const bf16 *>(a.C);
     bf16 *y = static_cast<bf16 *>(a.y);
     const int h = (int)pl.h, g = (int)pl.g;
-    constexpr int HPG = P >= 64 ? 128 / P : 4;
-    const bool grouped = HPG > 1 && group_heads(P, h / g) == HPG;
+    // four heads of a group per workgroup (two of head_dim 128) where the
+    // heads per group allow it, else one
+    constexpr int HPG = P >= 128 ? 2 : 4;
+    const bool grouped = (h / g) % HPG == 0;
     // the last chunk's own state only feeds the final state and the state
     // after the last chunk; chunk 0 also reports the initial state's size
     const bool keep_last = a.final_state != nullptr || a.states != nullptr;
