@@ -3,7 +3,8 @@
  * AMD MI355X (gfx950).
  *
  * Entry points: the chunked scan (ssd_chunk_scan, ssd_chunk_scan_ex with
- * packed documents and the state after every chunk or token), the decode
+ * packed documents and the state after every chunk or token,
+ * ssd_chunk_scan_noalloc on the library's own scratch), the decode
  * step (ssd_step), the steps just before and after the scan in a Mamba-2
  * mixer (ssd_conv1d_silu, ssd_gated_norm), the deterministic gradient pass
  * (ssd_chunk_scan_bwd), and the pieces of a sequence split into segments
@@ -30,7 +31,8 @@
  * A decode step drops the seqlen axis (section "The state between steps").
  *
  * Every pointer argument except the stream is a device pointer.  The caller
- * owns every buffer; the library allocates nothing.  Calls are asynchronous
+ * owns every buffer; the library allocates nothing (ssd_chunk_scan_noalloc
+ * uses a static device array the library holds instead of a workspace).  Calls are asynchronous
  * on the given HIP stream (NULL = the null stream) and never synchronise.
  * Arguments are validated before anything is launched: a call that returns
  * an error has launched nothing and left every output untouched.  A device
@@ -64,7 +66,9 @@ enum ssd_status {
                                  an io dtype other than SSD_F32 / SSD_BF16 */
     SSD_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the query returns */
     SSD_ERR_ALIGN = -5,       /* a pointer is not aligned as documented */
-    SSD_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+    SSD_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+    SSD_ERR_SCRATCH = -7      /* ssd_chunk_scan_noalloc: the sizes need more scratch
+                                 than SSD_SCRATCH_BYTES */
 };
 
 /*
@@ -187,6 +191,33 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim,
                                       int64_t groups, int64_t chunk);
+
+/*
+ * ssd_chunk_scan_noalloc -- ssd_chunk_scan_ex without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine); the
+ * scan's scratch is a static device array of SSD_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.
+ *
+ * Arguments, results, precision and error behaviour are those of
+ * ssd_chunk_scan_ex, except that sizes whose ssd_chunk_scan_workspace_bytes
+ * (...) exceeds SSD_SCRATCH_BYTES are rejected with SSD_ERR_SCRATCH before
+ * anything is launched (128 MiB holds, e.g., 8 x 2048 tokens of 24 heads,
+ * head_dim 64, state_dim 128, chunk 256).  All calls on one GPU share its
+ * scratch: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  The scratch's contents are
+ * never read before the call writes them.
+ */
+#define SSD_SCRATCH_BYTES (128u << 20)
+int32_t ssd_chunk_scan_noalloc(const void *x, const void *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *dt_bias,
+                               int32_t dt_softplus, float dt_min, float dt_max,
+                               const float *init_state, const int32_t *seq_idx, void *y,
+                               float *final_state, float *chunk_states, int64_t batch,
+                               int64_t seqlen, int64_t heads, int64_t head_dim,
+                               int64_t state_dim, int64_t groups, int64_t chunk,
+                               int32_t io_dtype, void *hip_stream, void *const *kernel_events);
 
 /*
  * ssd_step -- one decode step: no sequence axis, the state updated in place,

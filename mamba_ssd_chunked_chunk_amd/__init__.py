@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 from . import _lib
 from ._lib import LibraryMissing, load, status_string  # noqa: F401
 
-__all__ = ["chunk_scan", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
+__all__ = ["chunk_scan", "chunk_scan_noalloc", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
            "segment_log_decay", "combine_segments",
            "workspace_bytes", "abi_version",
            "LibraryMissing", "SsdError"]
@@ -148,6 +148,45 @@ def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,
         return y
     return (y,) + ((fin,) if return_final_state else ()) + \
         ((states,) if return_chunk_states else ())
+
+
+def chunk_scan_noalloc(x, dt, A, B, C, y, D=None, chunk_size: int = 256, dt_bias=None,
+                       dt_softplus: bool = True, dt_limit: Tuple[float, float] = (0.0, math.inf),
+                       initial_state=None, final_state=None, seq_idx=None, chunk_states=None):
+    """chunk_scan on the library's static device scratch (ssd_chunk_scan_noalloc):
+    no workspace, and nothing allocated here either -- the caller passes the
+    outputs y, and optionally final_state [b, h, n, p] and chunk_states
+    [b, ceil(l / chunk_size), h, n, p] (fp32).  Sizes whose workspace_bytes
+    exceed SSD_SCRATCH_BYTES raise SsdError (SSD_ERR_SCRATCH).  Calls that
+    overlap on one GPU race on its scratch."""
+    torch = _torch()
+    lib = load()
+    b, l, h, p = x.shape
+    g, n = B.shape[2], B.shape[3]
+    dev = x.device
+    io = x.dtype
+    _check("x", x, io)
+    _check("dt", dt, io, (b, l, h), dev)
+    _check("B", B, io, (b, l, g, n), dev)
+    _check("C", C, io, (b, l, g, n), dev)
+    _check("y", y, io, (b, l, h, p), dev)
+    _check("A", A, torch.float32, (h,), dev)
+    _check("D", D, torch.float32, (h,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (h,), dev)
+    _check("initial_state", initial_state, torch.float32, (b, h, n, p), dev)
+    _check("final_state", final_state, torch.float32, (b, h, n, p), dev)
+    _check("seq_idx", seq_idx, torch.int32, (b, l), dev)
+    nck = -(-l // int(chunk_size)) if chunk_size > 0 else 0
+    _check("chunk_states", chunk_states, torch.float32, (b, nck, h, n, p), dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_chunk_scan_noalloc(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(dt_bias),
+        int(bool(dt_softplus)), float(dt_limit[0]), float(dt_limit[1]),
+        _ptr(initial_state), _ptr(seq_idx), _ptr(y), _ptr(final_state), _ptr(chunk_states),
+        b, l, h, p, n, g, int(chunk_size), _io_code(io), stream, None)
+    if rc != 0:
+        raise SsdError("ssd_chunk_scan_noalloc", rc)
+    return y
 
 
 def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, chunk_size: int = 256, dt_bias=None,

@@ -16,12 +16,16 @@ SSD_ERR_UNSUPPORTED = -3
 SSD_ERR_WORKSPACE = -4
 SSD_ERR_ALIGN = -5
 SSD_ERR_HIP = -6
+SSD_ERR_SCRATCH = -7
+# bytes of the static device scratch of ssd_chunk_scan_noalloc
+SSD_SCRATCH_BYTES = 128 << 20
 
 # kernel_events slots of ssd_chunk_scan_ex
 EVENT_SLOTS = ("chunk_state", "state_scan", "chunk_out", "token_states")
 
 # every symbol include/ssd.h declares
-EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_workspace_bytes", "ssd_step",
+EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_noalloc",
+           "ssd_chunk_scan_workspace_bytes", "ssd_step",
            "ssd_conv1d_silu", "ssd_gated_norm", "ssd_chunk_scan_bwd",
            "ssd_segment_log_decay", "ssd_combine_segments",
            "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version")
@@ -52,6 +56,9 @@ def load() -> ctypes.CDLL:
     lib.ssd_chunk_scan_ex.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P, P, P,
                                       I64, I64, I64, I64, I64, I64, I64, I32,
                                       P, ctypes.c_size_t, P, P]
+    lib.ssd_chunk_scan_noalloc.restype = I32
+    lib.ssd_chunk_scan_noalloc.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P, P, P,
+                                           I64, I64, I64, I64, I64, I64, I64, I32, P, P]
     lib.ssd_chunk_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_workspace_bytes.argtypes = [I64] * 7
     lib.ssd_step.restype = I32

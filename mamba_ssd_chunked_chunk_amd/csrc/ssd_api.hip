@@ -93,6 +93,8 @@ const char *ssd_status_string(int32_t status) {
                                    "ssd_chunk_scan_workspace_bytes()";
     case SSD_ERR_ALIGN: return "a pointer is not aligned as documented";
     case SSD_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case SSD_ERR_SCRATCH: return "the sizes need more scratch than SSD_SCRATCH_BYTES "
+                                 "(use ssd_chunk_scan_ex with a workspace)";
     default: return "unknown status";
     }
 }

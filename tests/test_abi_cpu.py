@@ -51,7 +51,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         s = lib.ssd_status_string(code)
         assert s and s != b"unknown status"
     assert lib.ssd_status_string(12345) == b"unknown status"
@@ -215,3 +215,22 @@ def test_backward_and_segments_reject_bad_arguments(lib):
                                      None) == L.SSD_ERR_NULL
     assert lib.ssd_segment_log_decay(FAKE, FAKE, None, 1, 0.0, math.inf, None, FAKE, 2, 64, 4, 9,
                                      None) == L.SSD_ERR_UNSUPPORTED
+
+
+def test_noalloc_scratch_size_matches_header_and_rejects_beyond_it(lib):
+    """ssd_chunk_scan_noalloc rejects sizes whose workspace exceeds the
+    static scratch before any HIP call (the pointers below are never
+    dereferenced), and the binding's size is the header's."""
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+    m = re.search(r"#define\s+SSD_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.SSD_SCRATCH_BYTES
+    b, l, h, p, n, g, Q = 4, 4096, 80, 64, 128, 1, 256
+    need = lib.ssd_chunk_scan_workspace_bytes(b, l, h, p, n, g, Q)
+    assert need > L.SSD_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.ssd_chunk_scan_noalloc(fake, fake, fake, fake, fake, None, None, 1, 0.0,
+                                    math.inf, None, None, fake, None, None, b, l, h, p, n, g,
+                                    Q, L.SSD_BF16, None, None)
+    assert rc == L.SSD_ERR_SCRATCH
+    assert b"SSD_SCRATCH_BYTES" in lib.ssd_status_string(rc)
