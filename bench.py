@@ -230,6 +230,112 @@ def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4):
     return res
 
 
+# ---------------------------------------------------- profile summaries ---
+CALIB_BYTES = 256 << 20
+# kernel name patterns of the bf16 scan (the io type of every scan workload
+# but the tiny fp32 one)
+PROFILED = {"k_state16": "k_state16", "k_scan16": "k_scan16", "k_out16": "k_out16"}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError("no *%s under %s" % (suffix, d))
+
+
+def _short(name):
+    for k in PROFILED:
+        if k in name:
+            return k
+    if "neg_kernel" in name:
+        return "calib"
+    return None
+
+
+def summarize(a):
+    """profiles/ summaries from rocprofv3 csv output (see --summarize)."""
+    kind, wl = a[0], a[1]
+    if kind == "trace":
+        rows = _csv_rows(_find(a[2], "kernel_trace.csv"))
+        cmd = " ".join(a[3:])
+        per = {}
+        for r in rows:
+            k = _short(r.get("Kernel_Name", ""))
+            if k in PROFILED:
+                per.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        path = os.path.join(PROFILES, "scan_kernels_%s_kernel_trace.txt" % wl)
+        with open(path, "w") as f:
+            f.write("# rocprofv3 kernel trace of the bf16 chunked scan on the %s workload\n" % wl)
+            f.write("# command (from /tmp with TMPDIR=/tmp, repository at $R):\n#   %s\n" % cmd)
+            f.write("# every dispatch of the three kernels: the probe's warmup, plain and "
+                    "event-timed launches\n\n")
+            f.write("%-12s %6s %10s %10s %10s %10s\n" % ("kernel", "calls", "avg_us", "med_us",
+                                                        "min_us", "max_us"))
+            for k in PROFILED:
+                v = sorted(per.get(k, []))
+                if v:
+                    f.write("%-12s %6d %10.2f %10.2f %10.2f %10.2f\n" % (
+                        k, len(v), sum(v) / len(v), v[len(v) // 2], v[0], v[-1]))
+            f.write("\nsource_digest: %s\n" % source_digest())
+        print("wrote", path)
+        return
+    if kind == "traffic":
+        cmd = " ".join(a[4:])
+        vals = {}
+        for ctr, d in (("FETCH_SIZE", a[2]), ("WRITE_SIZE", a[3])):
+            for r in _csv_rows(_find(d, "counter_collection.csv")):
+                if r.get("Counter_Name") != ctr:
+                    continue
+                k = _short(r.get("Kernel_Name", ""))
+                if k:
+                    vals.setdefault((ctr, k), []).append(float(r["Counter_Value"]))
+        # the calibration kernel: its largest dispatches (CALIB_BYTES each way)
+        scale = {}
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            c = sorted(vals.get((ctr, "calib"), []))
+            big = [v for v in c if v >= 0.5 * c[-1]] if c else []
+            scale[ctr] = (CALIB_BYTES / 1024.0) / (sum(big) / len(big)) if big else None
+        for k in PROFILED:
+            fe, wr = vals.get(("FETCH_SIZE", k)), vals.get(("WRITE_SIZE", k))
+            if not fe or not wr or scale["FETCH_SIZE"] is None or scale["WRITE_SIZE"] is None:
+                continue
+            fk, wk = sum(fe) / len(fe), sum(wr) / len(wr)
+            hbm = fk * 1024 * scale["FETCH_SIZE"] + wk * 1024 * scale["WRITE_SIZE"]
+            path = os.path.join(PROFILES, "%s_%s_traffic.txt" % (k, wl))
+            with open(path, "w") as f:
+                f.write("# HBM traffic of %s on the %s workload, from two rocprofv3 counter "
+                        "runs\n" % (k, wl))
+                f.write("# commands (from /tmp with TMPDIR=/tmp, repository at $R):\n")
+                f.write("#   %s\n" % cmd.replace("COUNTER", "FETCH_SIZE"))
+                f.write("#   %s\n" % cmd.replace("COUNTER", "WRITE_SIZE"))
+                f.write("# per-dispatch means over the kernel's dispatches (KiB), each scaled "
+                        "by what the\n# same counter reads for an elementwise kernel that "
+                        "reads and writes %d MiB\n# (torch.neg) in the same run\n"
+                        % (CALIB_BYTES >> 20))
+                f.write("fetch_kib_raw_calibration: %.1f\n" % (CALIB_BYTES / 1024.0 /
+                                                           scale["FETCH_SIZE"]))
+                f.write("write_kib_raw_calibration: %.1f\n" % (CALIB_BYTES / 1024.0 /
+                                                           scale["WRITE_SIZE"]))
+                f.write("dispatches: %d\n" % len(fe))
+                f.write("fetch_kib_per_dispatch: %.1f\n" % fk)
+                f.write("write_kib_per_dispatch: %.1f\n" % wk)
+                f.write("fetch_scale: %.4f\n" % scale["FETCH_SIZE"])
+                f.write("write_scale: %.4f\n" % scale["WRITE_SIZE"])
+                f.write("hbm_bytes_per_launch: %d\n" % int(hbm))
+                f.write("source_digest: %s\n" % source_digest())
+            print("wrote", path)
+        return
+    raise SystemExit("unknown summary kind %r" % kind)
+
+
 # ------------------------------------------------------------------ main ---
 def main():
     ap = argparse.ArgumentParser()
@@ -249,8 +355,19 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-probe", default="",
-                    help="workload: run a few scans of it, for counter runs, and exit")
+                    help="workload: run a few scans of it and a 256 MiB copy (the counters' "
+                         "calibration), for profiler runs, and exit")
+    ap.add_argument("--probe-steps", type=int, default=3,
+                    help="timed scans of the probe (each run twice: plain and with events)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
+                    help="write profiles/ summaries from rocprofv3 csv output and exit: "
+                         "'trace WORKLOAD TRACE_DIR COMMAND...' or "
+                         "'traffic WORKLOAD FETCH_DIR WRITE_DIR COMMAND...'")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the scan is built and measured on a single "
@@ -267,8 +384,20 @@ def main():
 
     if args.traffic_probe:
         w = syn.WORKLOADS[args.traffic_probe]
-        time_scan(torch, ssd, w, dev, steps=3, warmup=2)
-        print(json.dumps({"traffic_probe": w.name}))
+        if w.name == "decode_2p7b":
+            w = w.replace(name="decode_2p7b_prefill")
+        r = time_scan(torch, ssd, w, dev, steps=args.probe_steps, warmup=2)
+        # calibration: a plain elementwise kernel that reads CALIB_BYTES and
+        # writes CALIB_BYTES (torch.neg; a same-type copy_ would go to the
+        # copy engine, which the counters do not see)
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": w.name,
+                          "kernels_us": {k: v["avg_us"] for k, v in r["kernels"].items()}}))
         return
 
     names = [nm for nm in args.workloads.split(",") if nm]
