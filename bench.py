@@ -487,21 +487,36 @@ def bench_states(args, torch, ssd, syn, dev):
     st_out = torch.empty((b, nc, h, n, p), dtype=torch.float32, device=dev)
     steps = max(args.steps // 2, 10)
 
-    def packed(i):
-        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
-                       dt_bias=S["bias"], out=S["y"], workspace=ws, seq_idx=seq)
+    evs = Events(torch, steps)
 
-    def states(i):
+    def plain(i, ev=None):
+        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
+                       dt_bias=S["bias"], out=S["y"], workspace=ws, kernel_events=ev)
+
+    def packed(i, ev=None):
+        ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
+                       dt_bias=S["bias"], out=S["y"], workspace=ws, seq_idx=seq,
+                       kernel_events=ev)
+
+    def states(i, ev=None):
         ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
                        dt_bias=S["bias"], out=S["y"], workspace=ws, return_chunk_states=True,
-                       chunk_states_out=st_out)
+                       chunk_states_out=st_out, kernel_events=ev)
     res = {}
-    for name, fn in (("packed", packed), ("chunk_states", states)):
+    # the plain scan on the same single input set, for a like-for-like ratio
+    for name, fn in (("plain_same_inputs", plain), ("packed", packed),
+                     ("chunk_states", states)):
         wall, _ = _time_calls(torch, fn, steps)
+        for i in range(steps):
+            fn(i, evs.handles[i])
+        torch.cuda.synchronize()
+        kern = {k: round(1e3 * evs.slot_ms(j, steps), 2) for j, k in enumerate(SLOTS)}
         res[name] = {"value": round(b * l / (wall * 1e-3), 1), "unit": "tokens/s",
-                     "ms_per_step": round(wall, 4)}
-        log("%s: %.4f ms/step" % (name, wall))
+                     "ms_per_step": round(wall, 4), "kernels_us": kern}
+        log("%s: %.4f ms/step %s" % (name, wall, json.dumps(kern)))
     res["packed"]["documents_per_step"] = int(seq[:, -1].sum()) + b
+    res["packed"]["over_plain"] = round(res["packed"]["ms_per_step"] /
+                                        res["plain_same_inputs"]["ms_per_step"], 4)
     x1, dt1, B1, C1 = S["x"][:1], S["dt"][:1], S["B"][:1], S["C"][:1]
     y1 = torch.empty((1, l, h, p), dtype=torch.bfloat16, device=dev)
     tok = torch.empty((1, l, h, n, p), dtype=torch.float32, device=dev)
