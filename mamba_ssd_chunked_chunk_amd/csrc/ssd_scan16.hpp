@@ -667,14 +667,14 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
 //    bound, so the scale needs no exchange); 2^(E_c - 15) goes to Hs.  The
 //    state after the last chunk is the final state ([state_dim][head_dim],
 //    fp32).  One thread per 4 consecutive state elements, as ScanTile in
-//    ssd_scan.hpp lays them out; chunk states are loaded 8 chunks ahead.
-template <int N, bool ROWS>
+//    ssd_scan.hpp lays them out; chunk states are loaded 8 to 16 chunks ahead.
+template <int N, bool ROWS, bool DEEP>
 __global__ __launch_bounds__(256) void k_scan16(
     const f16 *__restrict__ St, const float *__restrict__ Smax, const float *__restrict__ Lam,
     const float *__restrict__ Imax, const float *__restrict__ init, f16 *__restrict__ Hb,
     float *__restrict__ Hs, float *__restrict__ final_state, int64_t bh, int h, int64_t nc,
     int n, int p, float *__restrict__ states) {
-    constexpr int G8 = 8;
+    constexpr int GA = 8;
     __shared__ __attribute__((aligned(16))) float lds[4 * 256];
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t np4 = (int64_t)n * p / 4;
@@ -710,18 +710,26 @@ __global__ __launch_bounds__(256) void k_scan16(
     float *hsc = Hs + pair * nc;
     const int64_t ns = (final_state || states) ? nc : nc - 1;
     const int64_t klast = ns > 0 ? ns - 1 : 0;
-    for (int64_t k0 = 0; k0 < nc; k0 += G8) {
-        f16x4 Sh[G8];
-        float Lk[G8], Mk[G8];
+    // Chunk states in batches of GA; with DEEP (long sequences) two batches
+    // in flight: the next batch is requested before the current one is
+    // applied.
+    struct Batch {
+        f16x4 S[GA];
+        float L[GA], M[GA];
+    };
+    auto fetch = [&](Batch &bt, int64_t k0) {
 #pragma unroll
-        for (int u = 0; u < G8; ++u) {
+        for (int u = 0; u < GA; ++u) {
+            // past the last chunk the pass applies, the last one is read again
             const int64_t k = k0 + u < klast ? k0 + u : klast;
-            Sh[u] = S16[k * cstride];
-            Lk[u] = L[k];
-            Mk[u] = Sm[k];
+            bt.S[u] = S16[k * cstride];
+            bt.L[u] = L[k];
+            bt.M[u] = Sm[k];
         }
+    };
+    auto apply = [&](const Batch &bt, int64_t k0) {
 #pragma unroll
-        for (int u = 0; u < G8; ++u) {
+        for (int u = 0; u < GA; ++u) {
             const int64_t c = k0 + u;
             // chunk 0's boundary state is stored only for a given initial
             // state (the chunk output takes zeros otherwise)
@@ -732,16 +740,34 @@ __global__ __launch_bounds__(256) void k_scan16(
                 if (lead) hsc[c] = ldexpf(1.f, ex - 15);
             }
             if (c < ns) {
-                const float sc = ldexpf(1.f, scale_exp(Mk[u]) - 15);
-                const f32x4 S = f32x4{(float)Sh[u][0], (float)Sh[u][1], (float)Sh[u][2],
-                                      (float)Sh[u][3]} * sc;
-                const float dec = exp2_fast(Lk[u]);
+                const float sc = ldexpf(1.f, scale_exp(bt.M[u]) - 15);
+                const f32x4 S = f32x4{(float)bt.S[u][0], (float)bt.S[u][1], (float)bt.S[u][2],
+                                      (float)bt.S[u][3]} * sc;
+                const float dec = exp2_fast(bt.L[u]);
                 H = dec * H + S;
-                M = dec * M + Mk[u];
+                M = dec * M + bt.M[u];
             }
             if (ROWS && states && c < nc)
                 store_state_rows(lds, H, st, live,
                                  states + ((b * nc + c) * h + hh) * (int64_t)n * p, row0, col0, p);
+        }
+    };
+    if constexpr (DEEP) {
+        Batch b0, b1;
+        fetch(b0, 0);
+        for (int64_t k0 = 0; k0 < nc; k0 += 2 * GA) {
+            fetch(b1, k0 + GA);
+            apply(b0, k0);
+            if (k0 + GA >= nc) break;
+            fetch(b0, k0 + 2 * GA);
+            apply(b1, k0 + GA);
+        }
+    } else {
+        // few chunks: one batch at a time, fewer registers, more waves
+        for (int64_t k0 = 0; k0 < nc; k0 += GA) {
+            Batch b0;
+            fetch(b0, k0);
+            apply(b0, k0);
         }
     }
     if (ROWS && final_state)
@@ -1089,14 +1115,19 @@ hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     const int64_t np4 = (int64_t)N * P / 4;
     const int64_t tot = pl.b * pl.h * np4;
     const unsigned scan_blocks = (unsigned)((tot + kThreads - 1) / kThreads);
+    // two batches of chunk states in flight only where there are many chunks
+    const bool deep = pl.nc >= 64;
+    auto launch_scan = [&](auto rows_c, auto deep_c) -> hipError_t {
+        constexpr bool RW = decltype(rows_c)::value, DP = decltype(deep_c)::value;
+        return launch_timed(&k_scan16<N, RW, DP>, dim3(scan_blocks), dim3(kThreads), s, a.ev,
+                            kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs,
+                            RW ? a.final_state : (float *)nullptr, pl.b * pl.h, h, pl.nc, N, P,
+                            RW ? a.states : (float *)nullptr);
+    };
     if (keep_last)
-        e = launch_timed(&k_scan16<N, true>, dim3(scan_blocks), dim3(kThreads), s, a.ev,
-                         kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs, a.final_state,
-                         pl.b * pl.h, h, pl.nc, N, P, a.states);
+        e = deep ? launch_scan(Yes{}, Yes{}) : launch_scan(Yes{}, No{});
     else
-        e = launch_timed(&k_scan16<N, false>, dim3(scan_blocks), dim3(kThreads), s, a.ev,
-                         kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs, (float *)nullptr,
-                         pl.b * pl.h, h, pl.nc, N, P, (float *)nullptr);
+        e = deep ? launch_scan(No{}, Yes{}) : launch_scan(No{}, No{});
     if (e != hipSuccess) return e;
 
     return grouped ? (seq ? launch_out(Grp{}, Yes{}) : launch_out(Grp{}, No{}))
