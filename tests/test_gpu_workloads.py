@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import ssd_synth as syn
-from gpu_util import (PAIR_AXES, STATE_AXES, Y_AXES, check_close, dev_tensor, gpu_inputs, log,
+from gpu_util import (WORST, PAIR_AXES, STATE_AXES, Y_AXES, check_close, dev_tensor, gpu_inputs, log,
                       oracle_kw, run_scan, sample_pairs, to_f64, torch_mod)
 
 pytestmark = pytest.mark.gpu
@@ -38,6 +38,7 @@ SAMPLES = {"tiny_fp32": None, "mamba2_130m": 24, "mamba2_2p7b": 16, "grouped_lon
 @pytest.mark.parametrize("name", list(SAMPLES))
 def test_workload_parity(orc, name):
     w = syn.WORKLOADS[name]
+    WORST.clear()
     log("generating", name)
     inp = syn.make_inputs(w)
     log("gpu scan", name, w)
@@ -56,6 +57,8 @@ def test_workload_parity(orc, name):
         s = check_close(yg, yo, w.io, "y", PAIR_AXES)
         check_close(fg, fo, w.io, "final_state", PAIR_AXES)
     log(name, "y max_abs %.3g max_rel %.3g normwise %.3g" % s)
+    log(name, "worst err/(|o|+rms) per floor:",
+        {"%s/%s" % k: "%.2e" % v for k, v in WORST.items()})
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
