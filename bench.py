@@ -49,10 +49,17 @@ def log(*a):
 
 
 def source_digest() -> str:
+    """Digest of the scan kernels' code: comments and blank lines do not
+    count, so a comment edit does not retire the counter summaries."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.split("\n") if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,7 +15,9 @@
 //           + 2^lcs_i C_i^T H + D x_i                           (read-out)
 //     H  <- 2^lam H + B^T (w x)                                 (carry)
 // Every exponent is <= 0 when A <= 0, and the j > i half of the scores is
-// removed by a select, so no inf * 0 reaches a result.
+// removed by a select, so no inf * 0 reaches a result.  The carried state
+// is held with its decay deferred (see kDefer), so most blocks only add
+// their rows.
 //
 // Matrix-core operands.  The products run on v_mfma_f32_16x16x32_bf16 with
 // fp32 accumulation.  The inputs x, B and C are bf16 and enter the products
@@ -25,6 +27,9 @@
 // hi = bf16(v) and lo = bf16(v - hi), and multiplied as two products: 16
 // significant bits and fp32's exponent range, so any finite bf16 input is
 // handled.
+//
+// Work items: (batch, chunk, HP heads of one group), one workgroup each,
+// one wave per head up to head_dim 64 (two for head_dim 128).
 //
 // Launch sequence on one stream:
 //   1. k_state16  every chunk's own state from zero (all chunks in
@@ -485,11 +490,11 @@ template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
 
 // ----------------------------------------------------------------------------
 // 1. Chunk states: one workgroup per item; its chunk from a zero state,
-//        S <- 2^lam S + B^T (w x)   per block,
+//        S <- 2^lam S + B^T (w x)   per block (decay deferred: S~ = 2^D S),
 //    each wave holding its head_dim columns of its head's state (all
-//    state_dim rows) in MFMA accumulators.  The first wave of every head
-//    computes that head's per-row values of the next block while the
-//    current one is multiplied.  At the end the state is stored transposed
+//    state_dim rows) in MFMA accumulators.  A wave of every head computes
+//    that head's per-row values of the next block while the current one is
+//    multiplied.  At the end the state is stored transposed
 //    ([head_dim][state_dim]) as fp16 times 2^(15 - e), e the exponent of the
 //    head's largest magnitude m (written as Smax), with the chunk's total
 //    log2 decay (Lam); chunk-0 items also write the largest magnitude of the
@@ -781,9 +786,11 @@ __global__ __launch_bounds__(256) void k_scan16(
 //    and walks the chunk's blocks; per block:
 //      G^T = B C^T on the 3 causal 16 x 16 tiles, and
 //      P_ij = G_ij 2^(lcs_i - lcs_j) d_j (j <= i) in registers;
-//      y^T = 2^lcs_i (H^T C^T) + x^T (P + D I)^T (the skip term on the
-//            scores' diagonal), stored straight from the accumulators;
-//      H <- 2^lcs_last H + B^T (w x)  (except after the last block).
+//      y^T = 2^(lcs_i - D) (H~^T C^T) + x^T (P + D I)^T (the skip term on
+//            the scores' diagonal; H~ = 2^D H the held state), stored
+//            straight from the accumulators;
+//      the carry H~ += B^T (w x), after a rebase where the block needs one
+//      (except after the last block).
 //    The scores and the read-out share the C fragments.  The decay factor
 //    of P is taken as a_i b_j with a_i = 2^(lcs_i - lcs_15) and
 //    b_j = 2^(lcs_15 - lcs_j) d_j when the block's total log2 decay is above
