@@ -84,19 +84,46 @@ __device__ __forceinline__ Neg1 neg1() {
 // hi = bf16(v) (nearest); v - hi is exact in fp32 and is formed with one
 // bf16 dot product per value (hi times -1 in one half and 0 in the other,
 // plus v), then rounded to bf16 as lo.
+//
+// The residuals use the dot product form whose accumulator is a separate
+// operand (the builtin selects the form that overwrites its accumulator,
+// which costs a register copy per value while v stays live, as the carried
+// state does).  That form is written here in one assembly statement, so
+// the wait states the compiler inserts for its own instructions are kept by
+// hand: a dot product's result is read by another vector instruction only
+// three or more instructions later (all eight products come before the
+// four conversions), and the statement ends with two wait states so that a
+// matrix instruction may read lo right after it.  hi is converted outside,
+// so the compiler orders that first read of v (possibly a matrix result).
 __device__ __forceinline__ HL split8(const float (&v)[8], const Neg1 &m) {
     HL o;
+    bf16x2 h[4];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-        const bf16x2 h = __builtin_convertvector((f32x2{v[e], v[e + 1]}), bf16x2);
-        const float r0 = __builtin_amdgcn_fdot2_f32_bf16(h, m.lo, v[e], false);
-        const float r1 = __builtin_amdgcn_fdot2_f32_bf16(h, m.hi, v[e + 1], false);
-        const bf16x2 q = __builtin_convertvector((f32x2{r0, r1}), bf16x2);
-        o.hi[e] = h[0];
-        o.hi[e + 1] = h[1];
-        o.lo[e] = q[0];
-        o.lo[e + 1] = q[1];
+    for (int e = 0; e < 4; ++e) {
+        h[e] = __builtin_convertvector((f32x2{v[2 * e], v[2 * e + 1]}), bf16x2);
+        o.hi[2 * e] = h[e][0];
+        o.hi[2 * e + 1] = h[e][1];
     }
+    uint32_t l0, l1, l2, l3;
+    float t0, t1, t2, t3, t4, t5, t6, t7;
+    asm("v_dot2_f32_bf16 %4, %12, %16, %18\n\t"
+        "v_dot2_f32_bf16 %5, %12, %17, %19\n\t"
+        "v_dot2_f32_bf16 %6, %13, %16, %20\n\t"
+        "v_dot2_f32_bf16 %7, %13, %17, %21\n\t"
+        "v_dot2_f32_bf16 %8, %14, %16, %22\n\t"
+        "v_dot2_f32_bf16 %9, %14, %17, %23\n\t"
+        "v_dot2_f32_bf16 %10, %15, %16, %24\n\t"
+        "v_dot2_f32_bf16 %11, %15, %17, %25\n\t"
+        "v_cvt_pk_bf16_f32 %0, %4, %5\n\t"
+        "v_cvt_pk_bf16_f32 %1, %6, %7\n\t"
+        "v_cvt_pk_bf16_f32 %2, %8, %9\n\t"
+        "v_cvt_pk_bf16_f32 %3, %10, %11\n\t"
+        "s_nop 1"
+        : "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3), "=&v"(t0), "=&v"(t1), "=&v"(t2),
+          "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+        : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(m.lo), "v"(m.hi), "v"(v[0]),
+          "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+    o.lo = __builtin_bit_cast(bf16x8, u32x4{l0, l1, l2, l3});
     return o;
 }
 // Two accumulator tiles (contraction blocks 0..15 and 16..31 of a 32-block)
