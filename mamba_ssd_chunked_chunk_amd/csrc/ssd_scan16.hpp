@@ -699,14 +699,16 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
 //    bound, so the scale needs no exchange); 2^(E_c - 15) goes to Hs.  The
 //    state after the last chunk is the final state ([state_dim][head_dim],
 //    fp32).  One thread per 4 consecutive state elements, as ScanTile in
-//    ssd_scan.hpp lays them out; chunk states are loaded 8 to 16 chunks ahead.
-template <int N, bool ROWS, bool DEEP>
+//    ssd_scan.hpp lays them out; chunk states are loaded GA (8 where there
+//    are more than 4 chunks) to 2 GA (DEEP) chunks ahead.  A (batch, head)
+//    holds a whole number of waves (n p / 4 is a multiple of 64 for every
+//    supported size), so its per-chunk decays and maxima are scalar loads.
+template <int N, bool ROWS, bool DEEP, int GA>
 __global__ __launch_bounds__(256) void k_scan16(
     const f16 *__restrict__ St, const float *__restrict__ Smax, const float *__restrict__ Lam,
     const float *__restrict__ Imax, const float *__restrict__ init, f16 *__restrict__ Hb,
     float *__restrict__ Hs, float *__restrict__ final_state, int64_t bh, int h, int64_t nc,
     int n, int p, float *__restrict__ states) {
-    constexpr int GA = 8;
     __shared__ __attribute__((aligned(16))) float lds[4 * 256];
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t np4 = (int64_t)n * p / 4;
@@ -722,6 +724,8 @@ __global__ __launch_bounds__(256) void k_scan16(
     const int64_t pair = tile / tpp, tip = tile % tpp;
     const int row0 = (int)(tip % (n / st.R)) * st.R, col0 = (int)(tip / (n / st.R)) * st.Cc;
     const int64_t b = pair / h, hh = pair % h;
+    // the wave's (batch, head), as a wave-uniform value
+    const int64_t wpair = __builtin_amdgcn_readfirstlane((int)pair);
     const int64_t n0 = row0 + (loc % (st.R / 4)) * 4, pc = col0 + loc / (st.R / 4);
     const int64_t e4 = (pc * n + n0) / 4;
     // the (batch, head)'s first thread writes the boundary states' scales
@@ -737,8 +741,8 @@ __global__ __launch_bounds__(256) void k_scan16(
     const int64_t cstride = (int64_t)h * np4;
     const f16x4 *S16 = reinterpret_cast<const f16x4 *>(St) + (b * nc * h + hh) * np4 + e4;
     f16x4 *dst = reinterpret_cast<f16x4 *>(Hb) + (b * nc * h + hh) * np4 + e4;
-    const float *L = Lam + pair * nc;
-    const float *Sm = Smax + pair * nc;
+    const float *L = Lam + wpair * nc;
+    const float *Sm = Smax + wpair * nc;
     float *hsc = Hs + pair * nc;
     const int64_t ns = (final_state || states) ? nc : nc - 1;
     const int64_t klast = ns > 0 ? ns - 1 : 0;
@@ -1089,9 +1093,40 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
 }  // namespace s16
 
 // ----------------------------------------------------------------------------
+// The interval, in caller chunks, between the states the three passes hand
+// to each other.  The chunk-state pass and the chunk output walk a chunk in
+// 32-row blocks with a running state, so a chunk's length costs no extra
+// arithmetic: it sets only how many states are stored, scanned and read
+// back (each once) and how many work items the two parallel passes have.
+// Where the caller asks for no state after every chunk and four or more
+// workgroups per compute unit remain, 4 (else 2) consecutive chunks of the
+// caller are computed as one, which divides that state traffic by as much.
+// It is the same sum over the same blocks, with fewer states rounded to
+// their stored type on the way.  hp: heads per workgroup.
+inline int state_interval(const ScanPlan &pl, const ScanArgs &a, int hp) {
+    if (a.states != nullptr || pl.Q % 32 != 0) return 1;
+    const int64_t want = 4 * (int64_t)device_cus();
+    for (int m = 4; m > 1; m /= 2) {
+        const int64_t nc = (pl.l + m * pl.Q - 1) / (m * pl.Q);
+        if (pl.b * nc * (pl.h / hp) >= want) return m;
+    }
+    return 1;
+}
+
+// ----------------------------------------------------------------------------
 template <int P, int N>
-hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
+hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
     using namespace s16;
+    constexpr int HPG = P >= 128 ? 2 : 4;
+    const bool grouped = (plan.h / plan.g) % HPG == 0;
+    // the plan the kernels run on: its chunks may join several of the
+    // caller's (fewer stored states; the workspace map stays the caller's)
+    ScanPlan pl = plan;
+    const int m = state_interval(plan, a, grouped ? HPG : 1);
+    if (m > 1) {
+        pl.Q = plan.Q * m;
+        pl.nc = (plan.l + pl.Q - 1) / pl.Q;
+    }
     f16 *Hb = reinterpret_cast<f16 *>(a.ws + pl.off_hb);
     f16 *St = reinterpret_cast<f16 *>(a.ws + pl.off_st);
     float *Lam = reinterpret_cast<float *>(a.ws + pl.off_lam);
@@ -1104,10 +1139,6 @@ hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     const bf16 *Cm = static_cast<const bf16 *>(a.C);
     bf16 *y = static_cast<bf16 *>(a.y);
     const int h = (int)pl.h, g = (int)pl.g;
-    // four heads of a group per workgroup (two of head_dim 128) where the
-    // heads per group allow it, else one
-    constexpr int HPG = P >= 128 ? 2 : 4;
-    const bool grouped = (h / g) % HPG == 0;
     // the last chunk's own state only feeds the final state and the state
     // after the last chunk; chunk 0 also reports the initial state's size
     const bool keep_last = a.final_state != nullptr || a.states != nullptr;
@@ -1149,19 +1180,25 @@ hipError_t launch_scan16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     const int64_t np4 = (int64_t)N * P / 4;
     const int64_t tot = pl.b * pl.h * np4;
     const unsigned scan_blocks = (unsigned)((tot + kThreads - 1) / kThreads);
-    // two batches of chunk states in flight only where there are many chunks
-    const bool deep = pl.nc >= 64;
-    auto launch_scan = [&](auto rows_c, auto deep_c) -> hipError_t {
+    // chunk states requested 8 ahead, two batches in flight where there
+    // are many chunks, smaller batches for 4 chunks or fewer
+    auto launch_scan = [&](auto rows_c, auto deep_c, auto ga_c) -> hipError_t {
         constexpr bool RW = decltype(rows_c)::value, DP = decltype(deep_c)::value;
-        return launch_timed(&k_scan16<N, RW, DP>, dim3(scan_blocks), dim3(kThreads), s, a.ev,
-                            kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs,
+        constexpr int GA = decltype(ga_c)::value;
+        return launch_timed(&k_scan16<N, RW, DP, GA>, dim3(scan_blocks), dim3(kThreads), s,
+                            a.ev, kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs,
                             RW ? a.final_state : (float *)nullptr, pl.b * pl.h, h, pl.nc, N, P,
                             RW ? a.states : (float *)nullptr);
     };
-    if (keep_last)
-        e = deep ? launch_scan(Yes{}, Yes{}) : launch_scan(Yes{}, No{});
-    else
-        e = deep ? launch_scan(No{}, Yes{}) : launch_scan(No{}, No{});
+    auto launch_rows = [&](auto rows_c) -> hipError_t {
+        typedef std::integral_constant<int, 8> G8;
+        typedef std::integral_constant<int, 4> G4;
+        if (pl.nc >= 64) return launch_scan(rows_c, Yes{}, G8{});
+        if (pl.nc > 4) return launch_scan(rows_c, No{}, G8{});
+        if (pl.nc > 1) return launch_scan(rows_c, No{}, G4{});
+        return launch_scan(rows_c, No{}, One{});
+    };
+    e = keep_last ? launch_rows(Yes{}) : launch_rows(No{});
     if (e != hipSuccess) return e;
 
     return grouped ? (seq ? launch_out(Grp{}, Yes{}) : launch_out(Grp{}, No{}))

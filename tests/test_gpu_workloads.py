@@ -141,6 +141,34 @@ def test_forward_then_steps_equals_long_forward(orc, io):
     check_close(to_f64(st), fo, io, "state", STATE_AXES)
 
 
+@pytest.mark.parametrize("joined", [2, 4])
+def test_joined_chunks_parity(orc, joined):
+    """Grids large enough that the bf16 scan computes 2 or 4 of the caller's
+    256-token chunks as one (fewer stored states): batch sized from the
+    device's compute units so the grid lands on that case; sampled
+    (batch, head) pairs against the oracle, with an initial and a final
+    state for the 4-chunk case."""
+    torch = torch_mod()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    l, h, g, chunk = 2048, 16, 2, 256
+    # workgroups of 4 heads: batch * (chunks / joined) * 4 reaches 4 per CU
+    b = 4 * cus // ((l // chunk // joined) * (h // 4))
+    w = syn.Workload("joined%d" % joined, b, l, h, 16, 32, g, chunk,
+                     init_std=0.1 if joined == 4 else 0.0, seed=40 + joined)
+    WORST.clear()
+    inp = syn.make_inputs(w)
+    log("gpu scan", w)
+    y, fin = run_scan(inp, chunk, final=True)
+    pairs = sample_pairs(b, h, 12, seed=joined)
+    yo, fo = orc.scan(**oracle_kw(inp), pairs=pairs)
+    yg = np.stack([to_f64(y[pb, :, ph, :]) for pb, ph in pairs])
+    fg = np.stack([to_f64(fin[pb, ph]) for pb, ph in pairs])
+    check_close(yg, yo, w.io, "y", PAIR_AXES)
+    check_close(fg, fo, w.io, "final_state", PAIR_AXES)
+    log(w.name, "worst err/(|o|+rms) per floor:",
+        {"%s/%s" % k: "%.2e" % v for k, v in WORST.items()})
+
+
 def test_decode_workload(orc):
     """The decode workload at full size: prefill (256 x 1024 tokens, 80 heads),
     then 128 steps at batch 256; sampled pairs against the oracle."""
