@@ -78,12 +78,14 @@ def bytes_scan_min(b, l, h, p, n, g, Q, s, init=False, final=False):
     return th * (2 * p * s + 2 * n * s * g / h + s) + 4 * n * p * b * h * (int(init) + int(final))
 
 
-def bytes_kernel(name, b, l, h, p, n, g, Q, s, init=False, final=False):
+def bytes_kernel(name, b, l, h, p, n, g, Q, s, init=False, final=False, nst=None):
     """Algorithmic bytes of one launch: every operand of the kernel's step
     moved once, in the type the kernel keeps it.  bf16 io: chunk states and
     boundary states are fp16 (with one fp32 scale or maximum per (batch,
-    chunk, head)); fp32 io: fp32.  B and C count once per group."""
-    nc = -(-l // Q)
+    chunk, head)); fp32 io: fp32.  B and C count once per group.  nst: the
+    chunks per sequence whose states the call stores (the library's
+    ssd_chunk_scan_state_chunks; default ceil(l / Q))."""
+    nc = -(-l // Q) if nst is None else nst
     th = b * l * h
     x = th * p * s                      # x (or y)
     BC = b * l * g * n * s              # B or C
@@ -210,17 +212,19 @@ def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4):
     torch.cuda.synchronize()
     ms_ev = (time.perf_counter() - t1) * 1e3 / steps
     init = w.init_std > 0
+    nst = ssd.state_chunks(b, l, h, p, n, g, Q, io=w.io)
     kern = {}
     for k, name in enumerate(SLOTS):
         us = 1e3 * evs.slot_ms(k, steps)
-        alg = bytes_kernel(name, b, l, h, p, n, g, Q, s, init=init, final=final)
+        alg = bytes_kernel(name, b, l, h, p, n, g, Q, s, init=init, final=final, nst=nst)
         kern[name] = {"avg_us": round(us, 2), "alg_bytes": alg,
                       "GBs": round(alg / (us * 1e-6) / 1e9, 1),
                       "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     balg = bytes_scan_alg(b, l, h, p, n, g, Q, s, init=init, final=final)
     bmin = bytes_scan_min(b, l, h, p, n, g, Q, s, init=init, final=final)
     res = {"workload": w.name, "batch": b, "seqlen": l, "heads": h, "head_dim": p,
-           "state_dim": n, "groups": g, "chunk": Q, "io": w.io, "init_state": init,
+           "state_dim": n, "groups": g, "chunk": Q, "stored_state_chunks": nst,
+           "io": w.io, "init_state": init,
            "final_state": final, "input_sets": nsets,
            "ms_per_step": round(ms, 4), "ms_per_step_with_events": round(ms_ev, 4),
            "tokens_per_s": round(b * l / (ms * 1e-3), 1),

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 /* io dtype of x, dt, B, C and y */
 enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
@@ -191,6 +191,29 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
 size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                       int64_t head_dim, int64_t state_dim,
                                       int64_t groups, int64_t chunk);
+
+/*
+ * Number of chunks per sequence whose boundary states one ssd_chunk_scan or
+ * ssd_chunk_scan_ex call with these sizes computes, stores and scans on the
+ * current HIP device: the caller's chunks (ceil(seqlen / chunk), or the
+ * coarser computed chunks of a chunk shorter than 32 tokens), except that
+ * the bf16 scan computes runs of 2 or 4 of the caller's chunks as one chunk
+ * when it asks for no state after every chunk, the chunk is a multiple of
+ * 32 tokens and the two parallel passes still have at least four work items
+ * per compute unit of the device.  Each computed chunk is the same sum over
+ * the same 32-row blocks (kongchang "Mamba2" page, chunk-scan entry: the
+ * chunk length is a blocking of the one recurrence), so only the number of
+ * stored states changes.  The workspace's state arrays are then filled for
+ * that many chunks (a prefix of the layout ssd_chunk_scan_workspace_bytes
+ * sizes for the caller's chunks).
+ *   with_chunk_states  nonzero if the call passes chunk_states
+ * Returns the count (>= 0), or SSD_ERR_SHAPE / SSD_ERR_UNSUPPORTED for sizes
+ * or an io dtype the scan rejects.  Queries the device's compute units
+ * (once per device); allocates nothing.
+ */
+int64_t ssd_chunk_scan_state_chunks(int64_t batch, int64_t seqlen, int64_t heads,
+                                    int64_t head_dim, int64_t state_dim, int64_t groups,
+                                    int64_t chunk, int32_t io_dtype, int32_t with_chunk_states);
 
 /*
  * ssd_chunk_scan_noalloc -- ssd_chunk_scan_ex without a workspace argument,

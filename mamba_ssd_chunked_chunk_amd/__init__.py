@@ -24,7 +24,7 @@ from ._lib import LibraryMissing, load, status_string  # noqa: F401
 
 __all__ = ["chunk_scan", "chunk_scan_noalloc", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
            "segment_log_decay", "combine_segments",
-           "workspace_bytes", "abi_version",
+           "workspace_bytes", "state_chunks", "abi_version",
            "LibraryMissing", "SsdError"]
 
 
@@ -72,6 +72,18 @@ def abi_version() -> int:
 def workspace_bytes(batch, seqlen, heads, head_dim, state_dim, groups, chunk) -> int:
     return int(load().ssd_chunk_scan_workspace_bytes(batch, seqlen, heads, head_dim,
                                                      state_dim, groups, chunk))
+
+
+def state_chunks(batch, seqlen, heads, head_dim, state_dim, groups, chunk, io="bf16",
+                 with_chunk_states=False) -> int:
+    """Chunks per sequence whose boundary states a chunk_scan call with these
+    sizes stores on the current device (ssd_chunk_scan_state_chunks)."""
+    code = {"f32": 0, "bf16": 1}[io]
+    v = int(load().ssd_chunk_scan_state_chunks(batch, seqlen, heads, head_dim, state_dim,
+                                                 groups, chunk, code, int(bool(with_chunk_states))))
+    if v < 0:
+        raise SsdError("ssd_chunk_scan_state_chunks", v)
+    return v
 
 
 def chunk_scan(x, dt, A, B, C, D=None, chunk_size: int = 256, dt_bias=None,

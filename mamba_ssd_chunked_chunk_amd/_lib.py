@@ -25,7 +25,7 @@ EVENT_SLOTS = ("chunk_state", "state_scan", "chunk_out", "token_states")
 
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_noalloc",
-           "ssd_chunk_scan_workspace_bytes", "ssd_step",
+           "ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_state_chunks", "ssd_step",
            "ssd_conv1d_silu", "ssd_gated_norm", "ssd_chunk_scan_bwd",
            "ssd_segment_log_decay", "ssd_combine_segments",
            "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version")
@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
                                            I64, I64, I64, I64, I64, I64, I64, I32, P, P]
     lib.ssd_chunk_scan_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_workspace_bytes.argtypes = [I64] * 7
+    lib.ssd_chunk_scan_state_chunks.restype = I64
+    lib.ssd_chunk_scan_state_chunks.argtypes = [I64] * 7 + [I32, I32]
     lib.ssd_step.restype = I32
     lib.ssd_step.argtypes = [P, P, P, P, P, P, P, P, I32, F, F, P,
                              I64, I64, I64, I64, I64, I32, P]

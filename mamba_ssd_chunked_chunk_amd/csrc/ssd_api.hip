@@ -107,6 +107,22 @@ size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t hea
     return pl.total;
 }
 
+int64_t ssd_chunk_scan_state_chunks(int64_t batch, int64_t seqlen, int64_t heads,
+                                    int64_t head_dim, int64_t state_dim, int64_t groups,
+                                    int64_t chunk, int32_t io_dtype, int32_t with_chunk_states) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    ScanPlan pl;
+    if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io_dtype))
+        return SSD_ERR_SHAPE;
+    if (!supported_dims(head_dim, state_dim)) return SSD_ERR_UNSUPPORTED;
+    if (io_dtype == SSD_F32 || seqlen == 0) return pl.nc;
+    // the caller's per-chunk states come from chunks of the caller's length
+    // (or from the computed ones, stepped token by token)
+    const bool per_chunk = with_chunk_states != 0;
+    const int m = state_interval(pl, per_chunk, bf16_item_heads(head_dim, heads, groups));
+    return (pl.l + m * pl.Q - 1) / (m * pl.Q);
+}
+
 int32_t ssd_chunk_scan(const void *x, const void *dt, const float *A, const void *B,
                        const void *C, const float *D, const float *dt_bias,
                        int32_t dt_softplus, float dt_min, float dt_max,

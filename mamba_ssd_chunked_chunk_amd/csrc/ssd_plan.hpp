@@ -100,6 +100,36 @@ inline bool make_plan(ScanPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     return true;
 }
 
+// Heads per work item of the bf16 chunk-state and chunk-output kernels:
+// four heads of a group (two at head_dim 128) where the heads per group
+// allow it, else one.
+inline int bf16_item_heads(int64_t p, int64_t h, int64_t g) {
+    const int hp = p >= 128 ? 2 : 4;
+    return (h / g) % hp == 0 ? hp : 1;
+}
+
+int device_cus();
+
+// The interval, in caller chunks, between the states the three bf16 passes
+// hand to each other.  The chunk-state pass and the chunk output walk a
+// chunk in 32-row blocks with a running state, so a chunk's length costs no
+// extra arithmetic: it sets only how many states are stored, scanned and
+// read back (each once) and how many work items the two parallel passes
+// have.  Where the caller asks for no state after every chunk and four or
+// more workgroups per compute unit remain, 4 (else 2) consecutive chunks of
+// the caller are computed as one, which divides that state traffic by as
+// much.  It is the same sum over the same blocks, with fewer states rounded
+// to their stored type on the way.  hp: heads per work item.
+inline int state_interval(const ScanPlan &pl, bool per_chunk_states, int hp) {
+    if (per_chunk_states || pl.Q % 32 != 0) return 1;
+    const int64_t want = 4 * (int64_t)device_cus();
+    for (int m = 4; m > 1; m /= 2) {
+        const int64_t nc = (pl.l + m * pl.Q - 1) / (m * pl.Q);
+        if (pl.b * nc * (pl.h / hp) >= want) return m;
+    }
+    return 1;
+}
+
 struct ScanArgs {
     const void *x, *dt, *B, *C;
     const float *A, *D, *dt_bias;

@@ -1093,36 +1093,15 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
 }  // namespace s16
 
 // ----------------------------------------------------------------------------
-// The interval, in caller chunks, between the states the three passes hand
-// to each other.  The chunk-state pass and the chunk output walk a chunk in
-// 32-row blocks with a running state, so a chunk's length costs no extra
-// arithmetic: it sets only how many states are stored, scanned and read
-// back (each once) and how many work items the two parallel passes have.
-// Where the caller asks for no state after every chunk and four or more
-// workgroups per compute unit remain, 4 (else 2) consecutive chunks of the
-// caller are computed as one, which divides that state traffic by as much.
-// It is the same sum over the same blocks, with fewer states rounded to
-// their stored type on the way.  hp: heads per workgroup.
-inline int state_interval(const ScanPlan &pl, const ScanArgs &a, int hp) {
-    if (a.states != nullptr || pl.Q % 32 != 0) return 1;
-    const int64_t want = 4 * (int64_t)device_cus();
-    for (int m = 4; m > 1; m /= 2) {
-        const int64_t nc = (pl.l + m * pl.Q - 1) / (m * pl.Q);
-        if (pl.b * nc * (pl.h / hp) >= want) return m;
-    }
-    return 1;
-}
-
-// ----------------------------------------------------------------------------
 template <int P, int N>
 hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s) {
     using namespace s16;
     constexpr int HPG = P >= 128 ? 2 : 4;
-    const bool grouped = (plan.h / plan.g) % HPG == 0;
+    const bool grouped = bf16_item_heads(P, plan.h, plan.g) == HPG;
     // the plan the kernels run on: its chunks may join several of the
     // caller's (fewer stored states; the workspace map stays the caller's)
     ScanPlan pl = plan;
-    const int m = state_interval(plan, a, grouped ? HPG : 1);
+    const int m = state_interval(plan, a.states != nullptr, grouped ? HPG : 1);
     if (m > 1) {
         pl.Q = plan.Q * m;
         pl.nc = (plan.l + pl.Q - 1) / pl.Q;

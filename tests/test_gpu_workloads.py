@@ -155,6 +155,11 @@ def test_joined_chunks_parity(orc, joined):
     b = 4 * cus // ((l // chunk // joined) * (h // 4))
     w = syn.Workload("joined%d" % joined, b, l, h, 16, 32, g, chunk,
                      init_std=0.1 if joined == 4 else 0.0, seed=40 + joined)
+    import mamba_ssd_chunked_chunk_amd as ssd
+    assert ssd.state_chunks(b, l, h, 16, 32, g, chunk, io="bf16") == l // chunk // joined
+    assert ssd.state_chunks(b, l, h, 16, 32, g, chunk, io="bf16",
+                            with_chunk_states=True) == l // chunk
+    assert ssd.state_chunks(b, l, h, 16, 32, g, chunk, io="f32") == l // chunk
     WORST.clear()
     inp = syn.make_inputs(w)
     log("gpu scan", w)
