@@ -593,7 +593,8 @@ def bench_backward(args, torch, ssd, syn, dev):
     gen.manual_seed(w.seed + 98)
     dy = torch.randn((b, l, h, p), generator=gen, device=dev).bfloat16()
     dfin = torch.randn((b, h, n, p), generator=gen, device=dev)
-    wsb = int(ssd._lib.load().ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, Q))
+    wsb = int(ssd._lib.load().ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, Q,
+                                                                 1 if w.io == "bf16" else 0))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
     def run(i):

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 /* io dtype of x, dt, B, C and y */
 enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
@@ -352,12 +352,15 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
  *                   256-byte aligned
  *
  * Supported: head_dim and state_dim in {32, 64, 128} (the transposed scans
- * take head_dim as their state size).  batch and seqlen >= 1.  All
- * arithmetic fp32 (the scans use the fp32 path whatever the io dtype), the
- * running sums behind ddt, dA, d dt_bias and dD in fp64.  16-byte
- * alignment for x, B, C, dy, dx, dB, dC and the states, element alignment
- * for the rest; SSD_ERR_ALIGN otherwise.  Several launches: three fp32
- * chunk scans and the pass's own kernels.
+ * take head_dim as their state size).  batch and seqlen >= 1.  The three
+ * chunk scans run on the forward's kernels of the io dtype: fp32 io on the
+ * fp32 path; bf16 io on the bf16 path (bf16 inputs exact, every derived
+ * operand as two bf16 terms, fp32 accumulation and fp32 scan outputs), the
+ * adjoint scans on reversed copies in the workspace.  The running sums
+ * behind ddt, dA, d dt_bias and dD are fp64.  16-byte alignment for x, B,
+ * C, dy, dx, dB, dC and the states, element alignment for the rest;
+ * SSD_ERR_ALIGN otherwise.  Several launches: three chunk scans and the
+ * pass's own kernels.
  */
 int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const void *B,
                            const void *C, const float *D, const float *dt_bias,
@@ -369,10 +372,11 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
                            int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
                            size_t workspace_bytes, void *hip_stream);
 
-/* Bytes of workspace ssd_chunk_scan_bwd needs (0 for invalid sizes). */
+/* Bytes of workspace ssd_chunk_scan_bwd needs for these sizes and io dtype (0 for
+ * invalid sizes or an unknown io dtype). */
 size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                           int64_t head_dim, int64_t state_dim, int64_t groups,
-                                          int64_t chunk);
+                                          int64_t chunk, int32_t io_dtype);
 
 /*
  * Sequence segments (one per GPU for contexts beyond one GPU).  The state

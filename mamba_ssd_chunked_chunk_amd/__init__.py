@@ -238,7 +238,8 @@ def chunk_scan_bwd(x, dt, A, B, C, dy, D=None, chunk_size: int = 256, dt_bias=No
         out["d_dt_bias"] = torch.empty((h,), dtype=torch.float32, device=dev)
     if initial_state is not None:
         out["d_init"] = torch.empty((b, h, n, p), dtype=torch.float32, device=dev)
-    wsb = int(lib.ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, int(chunk_size)))
+    wsb = int(lib.ssd_chunk_scan_bwd_workspace_bytes(b, l, h, p, n, g, int(chunk_size),
+                                                     _io_code(io)))
     ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8,
                                                              device=dev)
     _check("workspace", ws, torch.uint8, None, dev)

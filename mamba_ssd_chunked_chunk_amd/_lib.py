@@ -77,7 +77,7 @@ def load() -> ctypes.CDLL:
                                        I64, I64, I64, I64, I64, I64, I64, I32,
                                        P, ctypes.c_size_t, P]
     lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [I64] * 7
+    lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [I64] * 7 + [I32]
     lib.ssd_segment_log_decay.restype = I32
     lib.ssd_segment_log_decay.argtypes = [P, P, P, I32, F, F, P, P, I64, I64, I64, I32, P]
     lib.ssd_combine_segments.restype = I32

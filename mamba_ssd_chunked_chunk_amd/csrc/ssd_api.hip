@@ -66,6 +66,9 @@ __global__ void k_fill_state(float *__restrict__ dst, const float *__restrict__ 
 hipError_t scan_f32(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
     return dispatch_scan<float>(pl, a, s);
 }
+hipError_t scan_bf16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s) {
+    return dispatch_scan<bf16>(pl, a, s);
+}
 
 static bool supported_dims(int64_t p, int64_t n) {
     return (p == 16 || p == 32 || p == 64 || p == 128) && (n == 32 || n == 64 || n == 128);

@@ -64,6 +64,35 @@ bool make_bwd_plan(BwdPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, int64
     return true;
 }
 
+// Workspace of the bf16 gradient pass: reversed bf16 copies of the inputs
+// the two adjoint scans read, the scans' fp32 outputs and the shared tail.
+struct BwdPlan16 {
+    ScanPlan s1, s2;
+    size_t dyR, xR, CR, BR, dtR, seqR, y1, y2, y3, du, dw, sc, part, term, fin1, finT, initT,
+        dfT, ws, total;
+    int nparts;  // waves per head of the transposed scans (their row-dot parts)
+};
+
+bool make_bwd_plan16(BwdPlan16 &P, int64_t b, int64_t l, int64_t h, int64_t p, int64_t n,
+                     int64_t g, int64_t Q) {
+    if (!make_plan(P.s1, b, l, h, p, n, g, Q, 1)) return false;
+    if (!make_plan(P.s2, b, l, h, n, p, h, Q, 1)) return false;
+    const int64_t thp = b * l * h * p, tgn = b * l * g * n, thn = b * l * h * n;
+    const int64_t th = b * l * h, st = b * h * n * p * 4;
+    size_t o = 0;
+    auto take = [&](size_t &off, int64_t bytes) { off = o; o += align256(bytes); };
+    take(P.dyR, thp * 2); take(P.xR, thp * 2); take(P.CR, tgn * 2); take(P.BR, tgn * 2);
+    take(P.dtR, th * 2); take(P.seqR, b * l * 4);
+    P.nparts = n >= 128 ? (int)(n / 64) : 1;
+    take(P.y1, thp * 2); take(P.y2, thn * 2); take(P.y3, thn * 2);
+    take(P.du, th * P.nparts * 4); take(P.dw, th * P.nparts * 4);
+    take(P.sc, th * 16); take(P.part, b * h * 3 * 8); take(P.term, b * h * 8);
+    take(P.fin1, st); take(P.finT, st); take(P.initT, st); take(P.dfT, st);
+    take(P.ws, (int64_t)(P.s1.total > P.s2.total ? P.s1.total : P.s2.total));
+    P.total = o;
+    return true;
+}
+
 struct BwdBufs {
     float *dyR, *xR, *xF, *dyF, *CR, *BR, *Bh, *CRh, *dtF, *lw, *la, *y1, *y2, *y3, *sc;
     int32_t *seqR;
@@ -114,7 +143,55 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
     if (seq && tid == 0) w.seqR[rt] = seq[bt];
 }
 
-// [pairs][n][p] -> [pairs][p][n]
+// The two bf16 values of a 32-bit word as fp32 (exact), and two fp32
+// values rounded to bf16 (nearest even) as one word.
+__device__ __forceinline__ float bf16_bits_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_bits_hi(uint32_t w) {
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16 ha = (bf16)a, hb = (bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// bf16 io: reversed copies (row t' = l - 1 - t) of dy, x, C and B, the
+// next token's time step at every reversed row (the adjoint's decay), and
+// the reversed document index; one workgroup per token, 16-byte copies.
+__global__ __launch_bounds__(256) void k_bwd_prep16(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const bf16 *__restrict__ Bm,
+    const bf16 *__restrict__ Cm, const bf16 *__restrict__ dy, const int32_t *__restrict__ seq,
+    bf16 *__restrict__ dyR, bf16 *__restrict__ xR, bf16 *__restrict__ CR,
+    bf16 *__restrict__ BR, bf16 *__restrict__ dtR, int32_t *__restrict__ seqR, int64_t l, int h,
+    int g, int p, int n) {
+    const int64_t bt = blockIdx.x, b = bt / l, t = bt % l;
+    const int64_t rt = b * l + (l - 1 - t);
+    const int tid = threadIdx.x;
+    const int hp8 = h * p / 8, gn8 = g * n / 8;
+    const uint4 *dys = reinterpret_cast<const uint4 *>(dy + bt * h * p);
+    const uint4 *xs = reinterpret_cast<const uint4 *>(x + bt * h * p);
+    uint4 *dyd = reinterpret_cast<uint4 *>(dyR + rt * h * p);
+    uint4 *xd = reinterpret_cast<uint4 *>(xR + rt * h * p);
+    for (int i = tid; i < hp8; i += 256) {
+        dyd[i] = dys[i];
+        xd[i] = xs[i];
+    }
+    const uint4 *cs = reinterpret_cast<const uint4 *>(Cm + bt * g * n);
+    const uint4 *bs = reinterpret_cast<const uint4 *>(Bm + bt * g * n);
+    uint4 *cd = reinterpret_cast<uint4 *>(CR + rt * g * n);
+    uint4 *bd = reinterpret_cast<uint4 *>(BR + rt * g * n);
+    for (int i = tid; i < gn8; i += 256) {
+        cd[i] = cs[i];
+        bd[i] = bs[i];
+    }
+    // the reversed row of token t carries token t + 1's step (none for the
+    // last token, whose reversed row is the sequence's first: no decay)
+    for (int i = tid; i < h; i += 256)
+        dtR[rt * h + i] = t + 1 < l ? dt[(bt + 1) * h + i] : (bf16)0.f;
+    if (seq && tid == 0) seqR[rt] = seq[bt];
+}
+
+// [pairs][n][p] -> [pairs][p][n], element by element (the fp32 pass)
 __global__ void k_transpose_np(const float *__restrict__ src, float *__restrict__ dst,
                                int64_t pairs, int n, int p) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -122,6 +199,24 @@ __global__ void k_transpose_np(const float *__restrict__ src, float *__restrict_
     if (i >= pairs * np) return;
     const int64_t pr = i / np, r = i % np, k = r / p, j = r % p;
     dst[pr * np + j * n + k] = src[i];
+}
+
+// The same through 32 x 32 tiles in LDS, reads and writes along rows: one
+// workgroup (32 x 8 threads) per tile of one pair; n and p are multiples of
+// 32.
+__global__ __launch_bounds__(256) void k_transpose_tiles(const float *__restrict__ src,
+                                                         float *__restrict__ dst, int n, int p) {
+    __shared__ float tile[32][33];
+    const int64_t pr = blockIdx.z;
+    const int k0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const float *s0 = src + pr * (int64_t)n * p;
+    float *d0 = dst + pr * (int64_t)n * p;
+#pragma unroll
+    for (int r = ty; r < 32; r += 8) tile[r][tx] = s0[(int64_t)(k0 + r) * p + j0 + tx];
+    __syncthreads();
+#pragma unroll
+    for (int r = ty; r < 32; r += 8) d0[(int64_t)(j0 + r) * n + k0 + tx] = tile[tx][r];
 }
 
 // Per token and head (16 lanes, 4 consecutive elements each): dx, and the
@@ -172,6 +267,112 @@ __global__ __launch_bounds__(256) void k_bwd_tok(
     }
 }
 
+// The bf16 pass's per-token step, one workgroup per token: per head (16
+// lanes, 4 consecutive elements each) dx = D dy + d yb, and the scalars
+// u - v, yb . x, dy . x and d for the running sums, with u = C . (h dy) and
+// yb . x = B . (g x) summed from the transposed scans' row dots (fp32, one
+// part per wave); then dB and dC, the group's heads summed in a fixed order
+// from the bf16 read-outs.  The heads' d are kept in LDS for the second
+// step (up to kTokHeads heads; beyond, taken from the time steps again).
+constexpr int kTokHeads = 1024;
+
+__global__ __launch_bounds__(256) void k_bwd_tokg(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const bf16 *__restrict__ dy,
+    const float *__restrict__ D, const float *__restrict__ dt_bias, int softplus, float dt_min,
+    float dt_max, const bf16 *__restrict__ yb1, const bf16 *__restrict__ y2,
+    const bf16 *__restrict__ y3, const float *__restrict__ du, const float *__restrict__ dw,
+    int nparts, float *__restrict__ sc_out, bf16 *__restrict__ dx, bf16 *__restrict__ dB,
+    bf16 *__restrict__ dC, int64_t l, int h, int g, int p, int n) {
+    __shared__ float dsh[kTokHeads];
+    const int64_t bt = blockIdx.x, b = bt / l, t = bt % l;
+    const int64_t rt = b * l + (l - 1 - t);
+    const int tid = threadIdx.x;
+    // p / 8 lanes per head, 8 elements each (16-byte rows); the lane groups
+    // are whole and aligned in every round (256 threads)
+    const int lph = p / 8, sl = tid & (lph - 1);
+    for (int task = tid; task < h * lph; task += 256) {
+        const int hh = task / lph;
+        const float d = time_step(to_f32(dt[bt * h + hh]), dt_bias ? dt_bias[hh] : 0.f,
+                                  softplus, dt_min, dt_max);
+        const float Dh = D ? D[hh] : 0.f;
+        const int64_t at = (bt * h + hh) * p + 8 * sl;
+        const u32x4 yq = *reinterpret_cast<const u32x4 *>(yb1 + (rt * h + hh) * p + 8 * sl);
+        const u32x4 xq = *reinterpret_cast<const u32x4 *>(x + at);
+        const u32x4 dq = *reinterpret_cast<const u32x4 *>(dy + at);
+        float dsum = 0.f;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float d0 = bf16_bits_lo(dq[e]), d1 = bf16_bits_hi(dq[e]);
+            dsum += d0 * bf16_bits_lo(xq[e]) + d1 * bf16_bits_hi(xq[e]);
+            const float o0 = Dh * d0 + d * bf16_bits_lo(yq[e]);
+            const float o1 = Dh * d1 + d * bf16_bits_hi(yq[e]);
+            o[e] = pack_bf16x2(o0, o1);
+        }
+        *reinterpret_cast<u32x4 *>(dx + at) = o;
+        for (int off = lph >> 1; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
+        if (sl == 0) {
+            float usum = 0.f, wsum = 0.f;
+            for (int q = 0; q < nparts; ++q) {
+                usum += du[(bt * h + hh) * nparts + q];
+                wsum += dw[(rt * h + hh) * nparts + q];
+            }
+            float *o = sc_out + ((b * h + hh) * l + t) * 4;
+            *reinterpret_cast<f32x4 *>(o) = f32x4{usum - d * wsum, wsum, dsum, d};
+            if (hh < kTokHeads) dsh[hh] = d;
+        }
+    }
+    __syncthreads();
+    // dB, dC: 16 head sets (set j: heads j, j + 16, .. of the group, in
+    // order) x n / 8 lanes of 8 consecutive elements; the sets' partial
+    // sums are added in set order through LDS
+    __shared__ f32x4 pb[16][16][2], pc[16][16][2];
+    const int hpg = h / g, kl = tid & 15, js = tid >> 4, nk = n / 8;
+    for (int gi = 0; gi < g; ++gi) {
+        f32x4 sb0 = zero4(), sb1 = zero4(), sc0 = zero4(), sc1 = zero4();
+        if (kl < nk) {
+            for (int q = js; q < hpg; q += 16) {
+                const int hh = gi * hpg + q;
+                const float d = hh < kTokHeads
+                                    ? dsh[hh]
+                                    : time_step(to_f32(dt[bt * h + hh]),
+                                                dt_bias ? dt_bias[hh] : 0.f, softplus, dt_min,
+                                                dt_max);
+                const u32x4 bq = *reinterpret_cast<const u32x4 *>(y3 + (rt * h + hh) * n + 8 * kl);
+                const u32x4 cq = *reinterpret_cast<const u32x4 *>(y2 + (bt * h + hh) * n + 8 * kl);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    sb0[2 * e] += d * bf16_bits_lo(bq[e]);
+                    sb0[2 * e + 1] += d * bf16_bits_hi(bq[e]);
+                    sb1[2 * e] += d * bf16_bits_lo(bq[2 + e]);
+                    sb1[2 * e + 1] += d * bf16_bits_hi(bq[2 + e]);
+                    sc0[2 * e] += bf16_bits_lo(cq[e]);
+                    sc0[2 * e + 1] += bf16_bits_hi(cq[e]);
+                    sc1[2 * e] += bf16_bits_lo(cq[2 + e]);
+                    sc1[2 * e + 1] += bf16_bits_hi(cq[2 + e]);
+                }
+            }
+        }
+        pb[js][kl][0] = sb0;
+        pb[js][kl][1] = sb1;
+        pc[js][kl][0] = sc0;
+        pc[js][kl][1] = sc1;
+        __syncthreads();
+        if (js < 2 && kl < nk) {
+            // thread (js, kl) finishes half js of lane kl's 8 elements
+            f32x4 tb = zero4(), tc = zero4();
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                tb += pb[j][kl][js];
+                tc += pc[j][kl][js];
+            }
+            st4(dB + (bt * g + gi) * n + 8 * kl + 4 * js, tb);
+            st4(dC + (bt * g + gi) * n + 8 * kl + 4 * js, tc);
+        }
+        __syncthreads();
+    }
+}
+
 // <d_final, h_l> per (batch, head), h_l^T from the transposed forward scan.
 __global__ __launch_bounds__(256) void k_bwd_term(const float *__restrict__ dfin,
                                                   const float *__restrict__ finT,
@@ -207,10 +408,29 @@ template <typename IO>
 __global__ __launch_bounds__(kCumThreads) void k_bwd_cum(
     const IO *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ dt_bias,
     int softplus, float dt_min, float dt_max, const int32_t *__restrict__ seq, int has_init,
-    BwdBufs w, IO *__restrict__ ddt, int64_t l, int h) {
+    BwdBufs w, IO *__restrict__ ddt, int64_t l, int h, const float *__restrict__ tdf = nullptr,
+    const float *__restrict__ tfin = nullptr, int64_t np = 0) {
     __shared__ double seg_val[kCumThreads], red[3][kCumThreads];
     __shared__ int seg_cut[kCumThreads];
     const int64_t pr = blockIdx.x;
+    // with tdf: the final-state term <d_final, h_l> of this (batch, head)
+    // from both in the same element order, summed here in fixed order
+    double term = 0.0;
+    if (tdf) {
+        double s = 0.0;
+        for (int64_t i = threadIdx.x; i < np; i += kCumThreads)
+            s += (double)tdf[pr * np + i] * (double)tfin[pr * np + i];
+        red[0][threadIdx.x] = s;
+        __syncthreads();
+        for (int off = kCumThreads / 2; off > 0; off >>= 1) {
+            if ((int)threadIdx.x < off) red[0][threadIdx.x] += red[0][threadIdx.x + off];
+            __syncthreads();
+        }
+        term = red[0][0];
+        __syncthreads();
+    } else if (w.term) {
+        term = w.term[pr];
+    }
     const int64_t b = pr / h;
     const int hh = (int)(pr % h), tid = threadIdx.x;
     const float Ah = A[hh], bias = dt_bias ? dt_bias[hh] : 0.f;
@@ -235,7 +455,7 @@ __global__ __launch_bounds__(kCumThreads) void k_bwd_cum(
     __syncthreads();
     if (tid == 0) {
         // the sum entering each segment from the right, stored in seg_val
-        double carry = w.term ? w.term[pr] : 0.0;
+        double carry = term;
         for (int k = kCumThreads - 1; k >= 0; --k) {
             const double v = seg_val[k];
             const int c = seg_cut[k];
@@ -258,7 +478,7 @@ __global__ __launch_bounds__(kCumThreads) void k_bwd_cum(
         const float z = to_f32(dt[(b * l + t) * h + hh]) + bias;
         const float spv = softplus ? (z > 20.f ? z : log1pf(expf(z))) : z;
         const bool pass = spv >= dt_min && spv <= dt_max;
-        const double dsp = softplus ? 1.0 / (1.0 + exp(-(double)z)) : 1.0;
+        const double dsp = softplus ? (double)(1.f / (1.f + expf(-z))) : 1.0;
         const double g = pass ? dd * dsp : 0.0;
         ddt[(b * l + t) * h + hh] = (IO)(float)g;
         sA += (double)v[3] * da;
@@ -329,6 +549,111 @@ __global__ void k_bwd_init(const float *__restrict__ fin1, const float *__restri
 
 bool al16(const void *q) { return ((uintptr_t)q & 15) == 0; }
 
+// The gradient pass for bf16 io: the three scans on the bf16 kernels (bf16
+// operands exact, derived operands as two bf16 terms, fp32 accumulation and
+// fp32 outputs), the adjoint ones on reversed copies with unit weights and
+// the next token's decay, the transposed ones reading the group's B or C
+// rows for every head (x slot = head / heads per group) instead of
+// broadcast copies; then the same per-token, running-sum and group-sum
+// kernels as the fp32 pass.
+int32_t bwd_bf16(const bf16 *x, const bf16 *dt, const float *A, const bf16 *B, const bf16 *C,
+                 const float *D, const float *dt_bias, int32_t dt_softplus, float dt_min,
+                 float dt_max, const float *init_state, const int32_t *seq_idx, const bf16 *dy,
+                 const float *d_final, bf16 *dx, bf16 *ddt, float *dA, bf16 *dB, bf16 *dC,
+                 float *dD, float *d_dt_bias, float *d_init, int64_t b, int64_t l, int64_t h,
+                 int64_t p, int64_t n, int64_t g, int64_t chunk, void *workspace,
+                 size_t workspace_bytes, hipStream_t s) {
+    BwdPlan16 P;
+    if (!make_bwd_plan16(P, b, l, h, p, n, g, chunk)) return SSD_ERR_SHAPE;
+    const int64_t lim32 = (int64_t)1 << 31;
+    if (P.s1.lp * 4 >= lim32 || P.s2.lp * 4 >= lim32) return SSD_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < P.total) return SSD_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    bf16 *dyR = reinterpret_cast<bf16 *>(ws + P.dyR), *xR = reinterpret_cast<bf16 *>(ws + P.xR);
+    bf16 *CR = reinterpret_cast<bf16 *>(ws + P.CR), *BR = reinterpret_cast<bf16 *>(ws + P.BR);
+    bf16 *dtR = reinterpret_cast<bf16 *>(ws + P.dtR);
+    int32_t *seqR = reinterpret_cast<int32_t *>(ws + P.seqR);
+    BwdBufs w{};
+    w.sc = reinterpret_cast<float *>(ws + P.sc);
+    w.part = reinterpret_cast<double *>(ws + P.part);
+    w.term = d_final ? reinterpret_cast<double *>(ws + P.term) : nullptr;
+    w.fin1 = reinterpret_cast<float *>(ws + P.fin1);
+    w.finT = reinterpret_cast<float *>(ws + P.finT);
+    w.initT = reinterpret_cast<float *>(ws + P.initT);
+    w.dfT = reinterpret_cast<float *>(ws + P.dfT);
+    char *scan_ws = ws + P.ws;
+    const int64_t bl = b * l, pairs = b * h, np = n * p;
+    const unsigned eblk = (unsigned)((pairs * np + 255) / 256);
+    const int sp = dt_softplus ? 1 : 0;
+    hipError_t e = hipSuccess;
+    auto ok = [&]() { return (e = hipGetLastError()) == hipSuccess; };
+
+    hipLaunchKernelGGL(k_bwd_prep16, dim3((unsigned)bl), dim3(256), 0, s, x, dt, B, C, dy,
+                       seq_idx, dyR, xR, CR, BR, dtR, seqR, l, (int)h, (int)g, (int)p, (int)n);
+    const dim3 tgrid((unsigned)(p / 32), (unsigned)(n / 32), (unsigned)pairs);
+    if (init_state)
+        hipLaunchKernelGGL(k_transpose_tiles, tgrid, dim3(256), 0, s, init_state, w.initT,
+                           (int)n, (int)p);
+    if (d_final)
+        hipLaunchKernelGGL(k_transpose_tiles, tgrid, dim3(256), 0, s, d_final, w.dfT, (int)n,
+                           (int)p);
+    if (!ok()) return SSD_ERR_HIP;
+
+    // 1. the adjoint, reversed: read-out yb_t = g_t^T B_t, final state g_0
+    bf16 *y1 = reinterpret_cast<bf16 *>(ws + P.y1), *y2 = reinterpret_cast<bf16 *>(ws + P.y2);
+    bf16 *y3 = reinterpret_cast<bf16 *>(ws + P.y3);
+    float *du = reinterpret_cast<float *>(ws + P.du), *dw = reinterpret_cast<float *>(ws + P.dw);
+    // the two adjoint scans share their chunks (scan 3 reads scan 1's states)
+    const int m = state_interval(P.s1, false, bf16_item_heads(p, h, g));
+    ScanArgs a1{dyR, dtR, CR, BR, A, nullptr, dt_bias, sp, dt_min, dt_max, d_final, y1,
+                d_init ? w.fin1 : nullptr, scan_ws, seq_idx ? seqR : nullptr, nullptr};
+    a1.adj = 1;
+    a1.interval = m;
+    if ((e = scan_bf16(P.s1, a1, s)) != hipSuccess) return SSD_ERR_HIP;
+    // 3. the adjoint transposed, reversed (x slot: the head's group row of
+    //    C): its boundary states are scan 1's, read transposed; read-out
+    //    g_t x_t and its dot with B_t (yb_t . x_t)
+    ScanArgs a3{CR, dtR, dyR, xR, A, nullptr, dt_bias, sp, dt_min, dt_max, d_final, y3,
+                nullptr, scan_ws, seq_idx ? seqR : nullptr, nullptr};
+    a3.xrow = g * n;
+    a3.xdiv = (int)(h / g);
+    a3.adj = 1;
+    a3.dotv = BR;
+    a3.dotrow = g * n;
+    a3.dotdiv = (int)(h / g);
+    a3.dotout = dw;
+    a3.interval = m;
+    a3.hb_in = scan_ws + P.s1.off_hb;
+    a3.hs_in = reinterpret_cast<const float *>(scan_ws + P.s1.off_hs);
+    a3.hbt = 1;
+    if ((e = scan_bf16(P.s2, a3, s)) != hipSuccess) return SSD_ERR_HIP;
+    // 2. the forward transposed (x slot: the head's group row of B): read-out
+    //    h_t dy_t, its dot with C_t (u), final state h_l^T
+    ScanArgs a2{B, dt, x, dy, A, nullptr, dt_bias, sp, dt_min, dt_max,
+                init_state ? w.initT : nullptr, y2, d_final ? w.finT : nullptr, scan_ws,
+                seq_idx, nullptr};
+    a2.xrow = g * n;
+    a2.xdiv = (int)(h / g);
+    a2.dotv = C;
+    a2.dotrow = g * n;
+    a2.dotdiv = (int)(h / g);
+    a2.dotout = du;
+    if ((e = scan_bf16(P.s2, a2, s)) != hipSuccess) return SSD_ERR_HIP;
+
+    hipLaunchKernelGGL(k_bwd_tokg, dim3((unsigned)bl), dim3(256), 0, s, x, dt, dy, D, dt_bias,
+                       sp, dt_min, dt_max, y1, y2, y3, du, dw, P.nparts, w.sc, dx, dB, dC, l,
+                       (int)h, (int)g, (int)p, (int)n);
+    hipLaunchKernelGGL((k_bwd_cum<bf16>), dim3((unsigned)pairs), dim3(kCumThreads), 0, s, dt, A,
+                       dt_bias, sp, dt_min, dt_max, seq_idx, init_state ? 1 : 0, w, ddt, l,
+                       (int)h, d_final ? w.dfT : nullptr, d_final ? w.finT : nullptr, np);
+    hipLaunchKernelGGL(k_bwd_sum, dim3((unsigned)((h + 63) / 64)), dim3(64), 0, s, w.part, dA,
+                       d_dt_bias, dD, b, (int)h);
+    if (d_init)
+        hipLaunchKernelGGL(k_bwd_init, dim3(eblk), dim3(256), 0, s, w.fin1, w.sc, A, d_init,
+                           pairs, (int)h, l, np);
+    return ok() ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // namespace
 
 }  // namespace ssd
@@ -339,7 +664,14 @@ extern "C" {
 
 size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads,
                                           int64_t head_dim, int64_t state_dim, int64_t groups,
-                                          int64_t chunk) {
+                                          int64_t chunk, int32_t io_dtype) {
+    if (io_dtype == SSD_BF16) {
+        BwdPlan16 P;
+        if (!make_bwd_plan16(P, batch, seqlen, heads, head_dim, state_dim, groups, chunk))
+            return 0;
+        return P.total;
+    }
+    if (io_dtype != SSD_F32) return 0;
     BwdPlan P;
     if (!make_bwd_plan(P, batch, seqlen, heads, head_dim, state_dim, groups, chunk)) return 0;
     return P.total;
@@ -375,6 +707,15 @@ int32_t ssd_chunk_scan_bwd(const void *x, const void *dt, const float *A, const 
         ((uintptr_t)A & 3) || ((uintptr_t)D & 3) || ((uintptr_t)dt_bias & 3) ||
         ((uintptr_t)dA & 3) || ((uintptr_t)dD & 3) || ((uintptr_t)d_dt_bias & 3))
         return SSD_ERR_ALIGN;
+    if (io_dtype == SSD_BF16)
+        return bwd_bf16(static_cast<const bf16 *>(x), static_cast<const bf16 *>(dt), A,
+                        static_cast<const bf16 *>(B), static_cast<const bf16 *>(C), D, dt_bias,
+                        dt_softplus, dt_min, dt_max, init_state, seq_idx,
+                        static_cast<const bf16 *>(dy), d_final, static_cast<bf16 *>(dx),
+                        static_cast<bf16 *>(ddt), dA, static_cast<bf16 *>(dB),
+                        static_cast<bf16 *>(dC), dD, d_dt_bias, d_init, batch, seqlen, heads,
+                        head_dim, state_dim, groups, chunk, workspace, workspace_bytes,
+                        static_cast<hipStream_t>(hip_stream));
     BwdPlan P;
     if (!make_bwd_plan(P, batch, seqlen, heads, head_dim, state_dim, groups, chunk))
         return SSD_ERR_SHAPE;

@@ -144,6 +144,38 @@ struct ScanArgs {
     // fp32 io only, or NULL: every token's weight and log2 decay [b, l, h],
     // given in place of the time step (dt, A, dt_bias and the limits unused)
     const float *lw = nullptr, *la = nullptr;
+    // bf16 io only (the gradient pass's scans; defaults give the forward):
+    //   xrow  row stride of x in elements (0: heads * head_dim);
+    //   xdiv  heads per x slot: head hh reads x slot hh / xdiv (a group's
+    //         row of a [b, l, groups, width] tensor for xdiv = heads/groups);
+    //   adj   every row's weight is 1 instead of its time step, and the
+    //         sequence's first row takes no decay (the adjoint recurrence
+    //         g_t = alpha_{t+1} g_{t+1} + C_t dy_t^T, run on reversed rows
+    //         whose time steps are the next token's);
+    //   dotv  NULL, or (one head per workgroup only) a [b, l, slots, P]
+    //         tensor in the io type, row stride dotrow elements, head hh
+    //         reading slot hh / dotdiv: the chunk output then also writes
+    //         every output row's dot with its row, from the fp32 values
+    //         before rounding, to dotout [b, l, heads, waves per head] (one
+    //         part per wave's columns)
+    int64_t xrow = 0;
+    int xdiv = 1;
+    int adj = 0;
+    const void *dotv = nullptr;
+    int64_t dotrow = 0;
+    int dotdiv = 1;
+    float *dotout = nullptr;
+    //   interval  caller chunks per computed chunk (0: state_interval's
+    //             choice)
+    //   hb_in     NULL, or the boundary states (scaled fp16) and their
+    //   hs_in     scales of an earlier call with the same chunks: only the
+    //             chunk output runs, reading them; hbt: they hold the
+    //             transposed states ([state_dim][head_dim] order of this
+    //             call's state)
+    int interval = 0;
+    const void *hb_in = nullptr;
+    const float *hs_in = nullptr;
+    int hbt = 0;
     // NULL, or 2 * kEventSlots hipEvent_t owned by the caller: the start and
     // end of the call's launch in each slot (kernel execution only), see
     // launch_timed
@@ -201,6 +233,8 @@ hipError_t launch_token_states(const ScanPlan &pl, const ScanArgs &a, const floa
 
 // The fp32 scan dispatched over the compiled (head_dim, state_dim) set.
 hipError_t scan_f32(const ScanPlan &pl, const ScanArgs &a, hipStream_t s);
+// the bf16 scan kernels (ScanArgs' xrow / xdiv / adj / dot modes)
+hipError_t scan_bf16(const ScanPlan &pl, const ScanArgs &a, hipStream_t s);
 
 // Launchers, one per (io, head_dim, state_dim) instantiation.
 template <typename IO, int P, int N>

@@ -358,7 +358,7 @@ __device__ __forceinline__ float softplus_fast(float z) {
 template <bool SEQ>
 __device__ __forceinline__ void rows_prep(Rows &R, const RowIn &f, float a2, float bias,
                                           int softplus, float lo, float hi, int k, int rows,
-                                          float D, int lane) {
+                                          float D, int lane, int adj = 0, bool first = false) {
     const int r = lane & 31;
     float d = 0.f;
     if (k * T + r < rows) {
@@ -368,6 +368,12 @@ __device__ __forceinline__ void rows_prep(Rows &R, const RowIn &f, float a2, flo
         d = d > hi ? hi : d;
     }
     float a = a2 * d;
+    // adjoint rows: d sets the decay only, the weight is 1 (0 past the end),
+    // and the sequence's first row takes no decay
+    if (adj) {
+        d = k * T + r < rows ? 1.f : 0.f;
+        if (first && k == 0 && r == 0) a = 0.f;
+    }
     // inclusive prefix sum over the block's 32 rows (each 32-lane half)
 #pragma unroll
     for (int off = 1; off < T; off <<= 1) {
@@ -420,6 +426,21 @@ __device__ __forceinline__ int scale_exp(float m) {
     if (m >= 0x1p-100f) frexpf(m, &ex);  // m = f 2^ex, f in [0.5, 1)
     return ex;
 }
+
+// How a call reads x and weighs its rows (ScanArgs): x row stride
+// (elements) and heads per x slot; adj: unit row weights (adjoint scans).
+struct Roles {
+    int64_t xrow;
+    int xdiv;
+    int adj;
+    // the chunk output's row dots (ScanArgs::dotv): source, its row stride,
+    // heads per source slot, output
+    const bf16 *dotv;
+    int64_t dotrow;
+    int dotdiv;
+    float *dotout;
+    int hbt;  // boundary states stored transposed (row-major [N][P])
+};
 
 // --------------------------------------------------- work items ----
 // Item = (batch, chunk, HP consecutive heads of one group), heads fastest;
@@ -532,7 +553,8 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, const int32_t *__restrict__ seq, const float *__restrict__ init,
     f16 *__restrict__ St, float *__restrict__ Smax, float *__restrict__ Lam,
-    float *__restrict__ Imax, int64_t l, int h, int g, int64_t Q, int nc, int nc_items) {
+    float *__restrict__ Imax, int64_t l, int h, int g, int64_t Q, int nc, int nc_items,
+    Roles md) {
     typedef Shape<P, N, HP> K;
     typedef Buf<P, N, HP> L;
     constexpr int CPW = K::CPW, RT = K::RT, WPH = K::WPH;
@@ -543,11 +565,11 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int hs = wave / WPH, part = wave % WPH, c0 = part * K::PW;
-    const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N;
+    const int64_t xs = md.xrow, bs = (int64_t)g * N;
     const Item it = decode_item(xcd_item(blockIdx.x, gridDim.x), nc_items, h / HP, h, g, l, Q,
                                 HP);
     const int hh = it.hh0 + hs;
-    const bf16 *xb = x + ((it.b * l + it.t0) * h + it.hh0) * P;
+    const bf16 *xb = x + (it.b * l + it.t0) * xs + (int64_t)(it.hh0 / md.xdiv) * P;
     const bf16 *bb = Bm + ((it.b * l + it.t0) * g + it.gi) * N;
     const bf16 *dtb = dt + (it.b * l + it.t0) * h + hh;
     const int32_t *sq = SEQ ? seq + it.b * l : nullptr;
@@ -570,7 +592,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     vm_wait<0>();
     if (part == 0)
         rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, 0.f,
-                       lane);
+                       lane, md.adj, it.t0 == 0);
 
     f32x4 acc[CPW * RT];
 #pragma unroll
@@ -627,7 +649,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         // the head's waves take turns at the next block's rows
         if (more && part == (k + 1) % WPH)
             rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
-                           it.rows, rows[cur][hs].next, lane);
+                           it.rows, rows[cur][hs].next, lane, md.adj, it.t0 == 0);
         dfin = rows[cur][hs].next;
     }
 
@@ -830,13 +852,13 @@ __global__ __launch_bounds__(256) void k_scan16(
 //    that head's per-row values of the next block.
 constexpr float kSplit = 60.f;
 
-template <int P, int N, int HP, bool SEQ>
+template <int P, int N, int HP, bool SEQ, bool DOT>
 __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) void k_out16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const bf16 *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ D,
     const float *__restrict__ dt_bias, int softplus, float dt_min, float dt_max,
     const int32_t *__restrict__ seq, const f16 *__restrict__ Hb, const float *__restrict__ Hs,
-    bf16 *__restrict__ y, int64_t l, int h, int g, int64_t Q, int nc, int has_init) {
+    bf16 *__restrict__ y, int64_t l, int h, int g, int64_t Q, int nc, int has_init, Roles md) {
     typedef Shape<P, N, HP> K;
     typedef Buf<P, N, HP> L;
     constexpr int CPW = K::CPW, RT = K::RT, WPH = K::WPH, NB = K::NB, NS = K::NS;
@@ -847,10 +869,10 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int lg = lane >> 4, li = lane & 15;
     const int hs = wave / WPH, part = wave % WPH, c0 = part * K::PW;
-    const int64_t xs = (int64_t)h * P, bs = (int64_t)g * N;
+    const int64_t xs = md.xrow, bs = (int64_t)g * N, ys = (int64_t)h * P;
     const Item it = decode_item(xcd_item(blockIdx.x, gridDim.x), nc, h / HP, h, g, l, Q, HP);
     const int hh = it.hh0 + hs;
-    const bf16 *xb = x + ((it.b * l + it.t0) * h + it.hh0) * P;
+    const bf16 *xb = x + (it.b * l + it.t0) * xs + (int64_t)(it.hh0 / md.xdiv) * P;
     bf16 *yb = y + ((it.b * l + it.t0) * h + it.hh0) * P;
     const int64_t bo = ((it.b * l + it.t0) * g + it.gi) * N;
     const bf16 *bb = Bm + bo, *cb = Cm + bo;
@@ -881,14 +903,33 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         const Rsrc rh = make_rsrc(Hb + (((int64_t)it.b * nc + it.c) * h + hh) * (int64_t)N * P,
                                   have ? (int64_t)N * P * 2 : 0);
         u32x2 raw[CPW * RT];
+        if (md.hbt) {
+            // four consecutive state rows of one column, P elements apart
 #pragma unroll
-        for (int u = 0; u < CPW; ++u)
+            for (int u = 0; u < CPW; ++u)
 #pragma unroll
-            for (int tr = 0; tr < RT; ++tr)
-                raw[u * RT + tr] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                               rh, (uint32_t)((c0 + col_of<CPW>(u, li)) * N + state_row(tr, lg)) * 2u,
-                               0, 0));
+                for (int tr = 0; tr < RT; ++tr) {
+                    const uint32_t o =
+                        (uint32_t)(state_row(tr, lg) * P + c0 + col_of<CPW>(u, li)) * 2u;
+                    uint32_t q[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        q[e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                            rh, o + (uint32_t)(e * P * 2), 0, 0);
+                    raw[u * RT + tr] = u32x2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+                }
+        } else {
+#pragma unroll
+            for (int u = 0; u < CPW; ++u)
+#pragma unroll
+                for (int tr = 0; tr < RT; ++tr)
+                    raw[u * RT + tr] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                   rh,
+                                   (uint32_t)((c0 + col_of<CPW>(u, li)) * N + state_row(tr, lg)) *
+                                       2u,
+                                   0, 0));
+        }
         const float sc = have ? Hs[((int64_t)it.b * h + hh) * nc + it.c] : 0.f;
         vm_wait<0>();
 #pragma unroll
@@ -899,15 +940,28 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     }
     if (part == 0)
         rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, 0.f,
-                       lane);
+                       lane, md.adj, it.t0 == 0);
 
     FragBase<P, N, CPW> fb;
     fb.init(c0, lane);
     // y offsets (bytes) of rows li and 16 + li of a block, from its first
     // row: 8 consecutive columns c0 + 32 v + 8 lg .. (column tiles 2v,
     // 2v + 1) or 4 columns c0 + 4 lg .. (one tile)
-    const uint32_t yo0 = (uint32_t)(li * xs + hs * P + c0 + (CPW >= 2 ? 8 : 4) * lg) * 2u;
-    const uint32_t yo1 = yo0 + (uint32_t)(16 * xs) * 2u;
+    const uint32_t yo0 = (uint32_t)(li * ys + hs * P + c0 + (CPW >= 2 ? 8 : 4) * lg) * 2u;
+    const uint32_t yo1 = yo0 + (uint32_t)(16 * ys) * 2u;
+    // DOT: every output row dotted with the matching row of md.dotv over the
+    // wave's columns (the head's slot of a [b, l, slots, P] tensor), from the
+    // fp32 accumulators: the block's y values are kept (ykeep) and its dot
+    // rows loaded (dvv) before the next block's copies are issued, and the
+    // dots are formed after the block's wait, so that no wait for them
+    // holds up those copies.  Output [b, l, heads, WPH] fp32.
+    constexpr int DV = CPW >= 2 ? CPW / 2 : 1;
+    f32x4 ykeep[DOT ? 2 : 1][DOT ? CPW : 1];
+    u32x4 dvv[DOT ? 2 : 1][DOT ? DV : 1];
+    const bf16 *dbase = nullptr;
+    if constexpr (DOT)
+        dbase = md.dotv + (it.b * l + it.t0) * md.dotrow +
+                (int64_t)((it.hh0 + hs) / md.dotdiv) * P + c0;
 
     // One block of one wave (in the buffer at element offset bo).
     auto compute = [&](int bo, const Rows &rf, int kb, bool carry) {
@@ -1011,8 +1065,8 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         const int r0 = kb * T;
         int valid = it.rows - r0;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const Rsrc ry = make_rsrc(yb + (valid > 0 ? (int64_t)r0 : 0) * xs,
-                                  (int64_t)valid * xs * 2);
+        const Rsrc ry = make_rsrc(yb + (valid > 0 ? (int64_t)r0 : 0) * ys,
+                                  (int64_t)valid * ys * 2);
         bf16x8 xf[CPW];
 #pragma unroll
         for (int u = 0; u < CPW; ++u) xf[u] = frag_x<P>(Xs, bx, u);
@@ -1025,6 +1079,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
                 f32x4 yp = mma(xf[u], pf.hi, zero4());
                 yp = mma(xf[u], pf.lo, yp);
                 yv[u] = colscale[i2] * yh[i2][u] + yp;
+                if constexpr (DOT) ykeep[i2][u] = yv[u];
             }
             const uint32_t off = i2 == 0 ? yo0 : yo1;
             if constexpr (CPW >= 2) {
@@ -1075,16 +1130,71 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         const int cur = k & 1;
         lds_barrier();
         const bool more = k + 1 < it.nblk;
+        int dvalid = 0;
+        if constexpr (DOT) {
+            dvalid = it.rows - k * T;
+            dvalid = dvalid > T ? T : dvalid;
+            const Rsrc rd = make_rsrc(dbase + (int64_t)k * T * md.dotrow,
+                                      (int64_t)dvalid * md.dotrow * 2);
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+                for (int v = 0; v < DV; ++v) {
+                    const uint32_t o =
+                        (uint32_t)((16 * i2 + li) * md.dotrow + 32 * v + (CPW >= 2 ? 8 : 4) * lg) *
+                        2u;
+                    if constexpr (CPW >= 2) {
+                        dvv[i2][v] = __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, 0));
+                    } else {
+                        const u32x2 q = __builtin_bit_cast(
+                            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rd, o, 0, 0));
+                        dvv[i2][v] = u32x4{q[0], q[1], 0u, 0u};
+                    }
+                }
+        }
         RowIn rn;
         rows_load<SEQ>(rn, dtb, sq, it.t0, l, h, it.rows, k + 1, lane);
         if (more) copy(lds + (cur ^ 1) * L::SIZE_BC, k + 1);
         issue_fence();
         compute(cur * L::SIZE_BC, rows[cur][hs], k, more);
         vm_wait<NS>();
+        if constexpr (DOT) {
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                float sd = 0.f;
+#pragma unroll
+                for (int v = 0; v < DV; ++v) {
+                    const u32x4 q = dvv[i2][v];
+                    if constexpr (CPW >= 2) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            sd += ykeep[i2][2 * v][2 * e] * bf16_lo(q[e]);
+                            sd += ykeep[i2][2 * v][2 * e + 1] * bf16_hi(q[e]);
+                            sd += ykeep[i2][2 * v + 1][2 * e] * bf16_lo(q[2 + e]);
+                            sd += ykeep[i2][2 * v + 1][2 * e + 1] * bf16_hi(q[2 + e]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            sd += ykeep[i2][0][2 * e] * bf16_lo(q[e]);
+                            sd += ykeep[i2][0][2 * e + 1] * bf16_hi(q[e]);
+                        }
+                    }
+                }
+                // the row's four lane groups hold its other columns
+                sd += __shfl_xor(sd, 16, 64);
+                sd += __shfl_xor(sd, 32, 64);
+                const int row = 16 * i2 + li;
+                if (lg == 0 && row < dvalid)
+                    md.dotout[((it.b * l + it.t0 + (int64_t)k * T + row) * h + hh) * WPH + part] =
+                        sd;
+            }
+        }
         // the head's waves take turns at the next block's rows
         if (more && part == (k + 1) % WPH)
             rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
-                           it.rows, rows[cur][hs].next, lane);
+                           it.rows, rows[cur][hs].next, lane, md.adj, it.t0 == 0);
     }
     // no copy may still be writing this workgroup's LDS when it exits
     vm_wait<0>();
@@ -1101,23 +1211,29 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
     // the plan the kernels run on: its chunks may join several of the
     // caller's (fewer stored states; the workspace map stays the caller's)
     ScanPlan pl = plan;
-    const int m = state_interval(plan, a.states != nullptr, grouped ? HPG : 1);
+    const int m =
+        a.interval > 0 ? a.interval : state_interval(plan, a.states != nullptr, grouped ? HPG : 1);
     if (m > 1) {
         pl.Q = plan.Q * m;
         pl.nc = (plan.l + pl.Q - 1) / pl.Q;
     }
-    f16 *Hb = reinterpret_cast<f16 *>(a.ws + pl.off_hb);
+    f16 *Hb = a.hb_in ? const_cast<f16 *>(static_cast<const f16 *>(a.hb_in))
+                      : reinterpret_cast<f16 *>(a.ws + pl.off_hb);
     f16 *St = reinterpret_cast<f16 *>(a.ws + pl.off_st);
     float *Lam = reinterpret_cast<float *>(a.ws + pl.off_lam);
     float *Smax = reinterpret_cast<float *>(a.ws + pl.off_scl);
-    float *Hs = reinterpret_cast<float *>(a.ws + pl.off_hs);
+    float *Hs = a.hs_in ? const_cast<float *>(a.hs_in) : reinterpret_cast<float *>(a.ws + pl.off_hs);
     float *Imax = reinterpret_cast<float *>(a.ws + pl.off_imx);
     const bf16 *x = static_cast<const bf16 *>(a.x);
     const bf16 *dt = static_cast<const bf16 *>(a.dt);
     const bf16 *Bm = static_cast<const bf16 *>(a.B);
     const bf16 *Cm = static_cast<const bf16 *>(a.C);
-    bf16 *y = static_cast<bf16 *>(a.y);
     const int h = (int)pl.h, g = (int)pl.g;
+    const Roles md{a.xrow ? a.xrow : (int64_t)h * P, a.xdiv, a.adj,
+                   static_cast<const bf16 *>(a.dotv), a.dotrow, a.dotdiv, a.dotout, a.hbt};
+    // row dots only on workgroups of one head (the gradient pass's
+    // transposed scans)
+    if (a.dotout && grouped) return hipErrorInvalidValue;
     // the last chunk's own state only feeds the final state and the state
     // after the last chunk; chunk 0 also reports the initial state's size
     const bool keep_last = a.final_state != nullptr || a.states != nullptr;
@@ -1134,7 +1250,7 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
         return launch_timed(&k_state16<P, N, HP, SQ>, dim3((unsigned)items), dim3(NT), s, a.ev,
                             kSlotState, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min,
                             a.dt_max, a.seq, a.init, St, Smax, Lam, Imax, pl.l, h, g, pl.Q,
-                            (int)pl.nc, (int)nc_state);
+                            (int)pl.nc, (int)nc_state, md);
     };
     auto launch_out = [&](auto hp_c, auto seq_c) -> hipError_t {
         constexpr int HP = decltype(hp_c)::value;
@@ -1142,43 +1258,54 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
         constexpr int NT = Shape<P, N, HP>::NT;
         const int64_t items = pl.b * pl.nc * (h / HP);
         if (items <= 0) return hipSuccess;
-        return launch_timed(&k_out16<P, N, HP, SQ>, dim3((unsigned)items), dim3(NT), s, a.ev,
-                            kSlotOut, x, Bm, Cm, dt, a.A, a.D, a.dt_bias, a.softplus, a.dt_min,
-                            a.dt_max, a.seq, Hb, Hs, y, pl.l, h, g, pl.Q, (int)pl.nc,
-                            a.init != nullptr ? 1 : 0);
+        if constexpr (HP == 1) {
+            if (a.dotout)
+                return launch_timed(&k_out16<P, N, 1, SQ, true>, dim3((unsigned)items),
+                                    dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
+                                    a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
+                                    static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
+                                    a.init != nullptr ? 1 : 0, md);
+        }
+        return launch_timed(&k_out16<P, N, HP, SQ, false>, dim3((unsigned)items), dim3(NT), s,
+                            a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D, a.dt_bias, a.softplus,
+                            a.dt_min, a.dt_max, a.seq, Hb, Hs, static_cast<bf16 *>(a.y), pl.l,
+                            h, g, pl.Q, (int)pl.nc, a.init != nullptr ? 1 : 0, md);
     };
     typedef std::integral_constant<int, 1> One;
     typedef std::integral_constant<int, HPG> Grp;
     typedef std::true_type Yes;
     typedef std::false_type No;
 
-    hipError_t e = grouped ? (seq ? launch_state(Grp{}, Yes{}) : launch_state(Grp{}, No{}))
-                           : (seq ? launch_state(One{}, Yes{}) : launch_state(One{}, No{}));
-    if (e != hipSuccess) return e;
+    // boundary states given (hb_in): the chunk output alone
+    if (!a.hb_in) {
+        hipError_t e = grouped ? (seq ? launch_state(Grp{}, Yes{}) : launch_state(Grp{}, No{}))
+                               : (seq ? launch_state(One{}, Yes{}) : launch_state(One{}, No{}));
+        if (e != hipSuccess) return e;
 
-    const int64_t np4 = (int64_t)N * P / 4;
-    const int64_t tot = pl.b * pl.h * np4;
-    const unsigned scan_blocks = (unsigned)((tot + kThreads - 1) / kThreads);
-    // chunk states requested 8 ahead, two batches in flight where there
-    // are many chunks, smaller batches for 4 chunks or fewer
-    auto launch_scan = [&](auto rows_c, auto deep_c, auto ga_c) -> hipError_t {
-        constexpr bool RW = decltype(rows_c)::value, DP = decltype(deep_c)::value;
-        constexpr int GA = decltype(ga_c)::value;
-        return launch_timed(&k_scan16<N, RW, DP, GA>, dim3(scan_blocks), dim3(kThreads), s,
-                            a.ev, kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs,
-                            RW ? a.final_state : (float *)nullptr, pl.b * pl.h, h, pl.nc, N, P,
-                            RW ? a.states : (float *)nullptr);
-    };
-    auto launch_rows = [&](auto rows_c) -> hipError_t {
-        typedef std::integral_constant<int, 8> G8;
-        typedef std::integral_constant<int, 4> G4;
-        if (pl.nc >= 64) return launch_scan(rows_c, Yes{}, G8{});
-        if (pl.nc > 4) return launch_scan(rows_c, No{}, G8{});
-        if (pl.nc > 1) return launch_scan(rows_c, No{}, G4{});
-        return launch_scan(rows_c, No{}, One{});
-    };
-    e = keep_last ? launch_rows(Yes{}) : launch_rows(No{});
-    if (e != hipSuccess) return e;
+        const int64_t np4 = (int64_t)N * P / 4;
+        const int64_t tot = pl.b * pl.h * np4;
+        const unsigned scan_blocks = (unsigned)((tot + kThreads - 1) / kThreads);
+        // chunk states requested 8 ahead, two batches in flight where there
+        // are many chunks, smaller batches for 4 chunks or fewer
+        auto launch_scan = [&](auto rows_c, auto deep_c, auto ga_c) -> hipError_t {
+            constexpr bool RW = decltype(rows_c)::value, DP = decltype(deep_c)::value;
+            constexpr int GA = decltype(ga_c)::value;
+            return launch_timed(&k_scan16<N, RW, DP, GA>, dim3(scan_blocks), dim3(kThreads), s,
+                                a.ev, kSlotScan, St, Smax, Lam, Imax, a.init, Hb, Hs,
+                                RW ? a.final_state : (float *)nullptr, pl.b * pl.h, h, pl.nc, N, P,
+                                RW ? a.states : (float *)nullptr);
+        };
+        auto launch_rows = [&](auto rows_c) -> hipError_t {
+            typedef std::integral_constant<int, 8> G8;
+            typedef std::integral_constant<int, 4> G4;
+            if (pl.nc >= 64) return launch_scan(rows_c, Yes{}, G8{});
+            if (pl.nc > 4) return launch_scan(rows_c, No{}, G8{});
+            if (pl.nc > 1) return launch_scan(rows_c, No{}, G4{});
+            return launch_scan(rows_c, No{}, One{});
+        };
+        e = keep_last ? launch_rows(Yes{}) : launch_rows(No{});
+        if (e != hipSuccess) return e;
+    }
 
     return grouped ? (seq ? launch_out(Grp{}, Yes{}) : launch_out(Grp{}, No{}))
                    : (seq ? launch_out(One{}, Yes{}) : launch_out(One{}, No{}));

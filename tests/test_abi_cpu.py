@@ -205,8 +205,10 @@ def test_backward_and_segments_reject_bad_arguments(lib):
     assert bwd(dy=None) == L.SSD_ERR_NULL
     assert bwd(dx=FAKE + 8) == L.SSD_ERR_ALIGN
     assert bwd(wsb=1024) == L.SSD_ERR_WORKSPACE
-    assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 1, 64) > 0
-    assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 3, 64) == 0
+    for io in (L.SSD_F32, L.SSD_BF16):
+        assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 1, 64, io) > 0
+        assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 3, 64, io) == 0
+    assert lib.ssd_chunk_scan_bwd_workspace_bytes(2, 64, 4, 64, 128, 1, 64, 7) == 0
     assert lib.ssd_combine_segments(FAKE, FAKE, None, None, None, None, 0, 2, 4, 64, 64,
                                     None) == L.SSD_ERR_SHAPE
     assert lib.ssd_combine_segments(None, FAKE, None, None, None, None, 2, 2, 4, 64, 64,
