@@ -73,10 +73,26 @@ struct BwdPlan16 {
     int nparts;  // waves per head of the transposed scans (their row-dot parts)
 };
 
+// The parts of a scan plan's workspace the bf16 kernels use (scaled fp16
+// boundary and chunk states, per-chunk decays, maxima and scales), packed
+// from offset 0; the fp32 path's per-row arrays and fp32-sized states are
+// left out.
+void compact_bf16(ScanPlan &pl) {
+    const int64_t sts = pl.b * pl.nc * pl.h * pl.n * pl.p * 2, per = pl.b * pl.h * pl.nc * 4;
+    size_t o = 0;
+    auto take = [&](size_t &off, int64_t bytes) { off = o; o += align256(bytes); };
+    take(pl.off_hb, sts); take(pl.off_st, sts); take(pl.off_lam, per); take(pl.off_scl, per);
+    take(pl.off_hs, per); take(pl.off_imx, pl.b * pl.h * 4);
+    pl.off_lcs = pl.off_dtp = pl.off_wgt = pl.off_sgr = pl.off_img = pl.off_hc = o;
+    pl.total = o;
+}
+
 bool make_bwd_plan16(BwdPlan16 &P, int64_t b, int64_t l, int64_t h, int64_t p, int64_t n,
                      int64_t g, int64_t Q) {
     if (!make_plan(P.s1, b, l, h, p, n, g, Q, 1)) return false;
     if (!make_plan(P.s2, b, l, h, n, p, h, Q, 1)) return false;
+    compact_bf16(P.s1);
+    compact_bf16(P.s2);
     const int64_t thp = b * l * h * p, tgn = b * l * g * n, thn = b * l * h * n;
     const int64_t th = b * l * h, st = b * h * n * p * 4;
     size_t o = 0;
