@@ -355,8 +355,10 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
  * take head_dim as their state size).  batch and seqlen >= 1.  The three
  * chunk scans run on the forward's kernels of the io dtype: fp32 io on the
  * fp32 path; bf16 io on the bf16 path (bf16 inputs exact, every derived
- * operand as two bf16 terms, fp32 accumulation and fp32 scan outputs), the
- * adjoint scans on reversed copies in the workspace.  The running sums
+ * operand as two bf16 terms, fp32 accumulation; the adjoint scans read the
+ * inputs in reversed row order, the transposed scans read each head's
+ * group row of B or C, and the sums that need fp32 are taken from the
+ * scans' fp32 values before rounding).  The running sums
  * behind ddt, dA, d dt_bias and dD are fp64.  16-byte alignment for x, B,
  * C, dy, dx, dB, dC and the states, element alignment for the rest;
  * SSD_ERR_ALIGN otherwise.  Several launches: three chunk scans and the

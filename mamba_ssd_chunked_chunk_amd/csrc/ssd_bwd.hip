@@ -68,8 +68,7 @@ bool make_bwd_plan(BwdPlan &P, int64_t b, int64_t l, int64_t h, int64_t p, int64
 // the two adjoint scans read, the scans' fp32 outputs and the shared tail.
 struct BwdPlan16 {
     ScanPlan s1, s2;
-    size_t dyR, xR, CR, BR, dtR, seqR, y1, y2, y3, du, dw, sc, part, term, fin1, finT, initT,
-        dfT, ws, total;
+    size_t y1, y2, y3, du, dw, sc, part, term, fin1, finT, initT, dfT, ws, total;
     int nparts;  // waves per head of the transposed scans (their row-dot parts)
 };
 
@@ -93,12 +92,10 @@ bool make_bwd_plan16(BwdPlan16 &P, int64_t b, int64_t l, int64_t h, int64_t p, i
     if (!make_plan(P.s2, b, l, h, n, p, h, Q, 1)) return false;
     compact_bf16(P.s1);
     compact_bf16(P.s2);
-    const int64_t thp = b * l * h * p, tgn = b * l * g * n, thn = b * l * h * n;
+    const int64_t thp = b * l * h * p, thn = b * l * h * n;
     const int64_t th = b * l * h, st = b * h * n * p * 4;
     size_t o = 0;
     auto take = [&](size_t &off, int64_t bytes) { off = o; o += align256(bytes); };
-    take(P.dyR, thp * 2); take(P.xR, thp * 2); take(P.CR, tgn * 2); take(P.BR, tgn * 2);
-    take(P.dtR, th * 2); take(P.seqR, b * l * 4);
     P.nparts = n >= 128 ? (int)(n / 64) : 1;
     take(P.y1, thp * 2); take(P.y2, thn * 2); take(P.y3, thn * 2);
     take(P.du, th * P.nparts * 4); take(P.dw, th * P.nparts * 4);
@@ -169,42 +166,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     const bf16 ha = (bf16)a, hb = (bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
            ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-// bf16 io: reversed copies (row t' = l - 1 - t) of dy, x, C and B, the
-// next token's time step at every reversed row (the adjoint's decay), and
-// the reversed document index; one workgroup per token, 16-byte copies.
-__global__ __launch_bounds__(256) void k_bwd_prep16(
-    const bf16 *__restrict__ x, const bf16 *__restrict__ dt, const bf16 *__restrict__ Bm,
-    const bf16 *__restrict__ Cm, const bf16 *__restrict__ dy, const int32_t *__restrict__ seq,
-    bf16 *__restrict__ dyR, bf16 *__restrict__ xR, bf16 *__restrict__ CR,
-    bf16 *__restrict__ BR, bf16 *__restrict__ dtR, int32_t *__restrict__ seqR, int64_t l, int h,
-    int g, int p, int n) {
-    const int64_t bt = blockIdx.x, b = bt / l, t = bt % l;
-    const int64_t rt = b * l + (l - 1 - t);
-    const int tid = threadIdx.x;
-    const int hp8 = h * p / 8, gn8 = g * n / 8;
-    const uint4 *dys = reinterpret_cast<const uint4 *>(dy + bt * h * p);
-    const uint4 *xs = reinterpret_cast<const uint4 *>(x + bt * h * p);
-    uint4 *dyd = reinterpret_cast<uint4 *>(dyR + rt * h * p);
-    uint4 *xd = reinterpret_cast<uint4 *>(xR + rt * h * p);
-    for (int i = tid; i < hp8; i += 256) {
-        dyd[i] = dys[i];
-        xd[i] = xs[i];
-    }
-    const uint4 *cs = reinterpret_cast<const uint4 *>(Cm + bt * g * n);
-    const uint4 *bs = reinterpret_cast<const uint4 *>(Bm + bt * g * n);
-    uint4 *cd = reinterpret_cast<uint4 *>(CR + rt * g * n);
-    uint4 *bd = reinterpret_cast<uint4 *>(BR + rt * g * n);
-    for (int i = tid; i < gn8; i += 256) {
-        cd[i] = cs[i];
-        bd[i] = bs[i];
-    }
-    // the reversed row of token t carries token t + 1's step (none for the
-    // last token, whose reversed row is the sequence's first: no decay)
-    for (int i = tid; i < h; i += 256)
-        dtR[rt * h + i] = t + 1 < l ? dt[(bt + 1) * h + i] : (bf16)0.f;
-    if (seq && tid == 0) seqR[rt] = seq[bt];
 }
 
 // [pairs][n][p] -> [pairs][p][n], element by element (the fp32 pass)
@@ -301,7 +262,6 @@ __global__ __launch_bounds__(256) void k_bwd_tokg(
     bf16 *__restrict__ dC, int64_t l, int h, int g, int p, int n) {
     __shared__ float dsh[kTokHeads];
     const int64_t bt = blockIdx.x, b = bt / l, t = bt % l;
-    const int64_t rt = b * l + (l - 1 - t);
     const int tid = threadIdx.x;
     // p / 8 lanes per head, 8 elements each (16-byte rows); the lane groups
     // are whole and aligned in every round (256 threads)
@@ -312,7 +272,7 @@ __global__ __launch_bounds__(256) void k_bwd_tokg(
                                   softplus, dt_min, dt_max);
         const float Dh = D ? D[hh] : 0.f;
         const int64_t at = (bt * h + hh) * p + 8 * sl;
-        const u32x4 yq = *reinterpret_cast<const u32x4 *>(yb1 + (rt * h + hh) * p + 8 * sl);
+        const u32x4 yq = *reinterpret_cast<const u32x4 *>(yb1 + at);
         const u32x4 xq = *reinterpret_cast<const u32x4 *>(x + at);
         const u32x4 dq = *reinterpret_cast<const u32x4 *>(dy + at);
         float dsum = 0.f;
@@ -331,7 +291,7 @@ __global__ __launch_bounds__(256) void k_bwd_tokg(
             float usum = 0.f, wsum = 0.f;
             for (int q = 0; q < nparts; ++q) {
                 usum += du[(bt * h + hh) * nparts + q];
-                wsum += dw[(rt * h + hh) * nparts + q];
+                wsum += dw[(bt * h + hh) * nparts + q];
             }
             float *o = sc_out + ((b * h + hh) * l + t) * 4;
             *reinterpret_cast<f32x4 *>(o) = f32x4{usum - d * wsum, wsum, dsum, d};
@@ -354,7 +314,7 @@ __global__ __launch_bounds__(256) void k_bwd_tokg(
                                     : time_step(to_f32(dt[bt * h + hh]),
                                                 dt_bias ? dt_bias[hh] : 0.f, softplus, dt_min,
                                                 dt_max);
-                const u32x4 bq = *reinterpret_cast<const u32x4 *>(y3 + (rt * h + hh) * n + 8 * kl);
+                const u32x4 bq = *reinterpret_cast<const u32x4 *>(y3 + (bt * h + hh) * n + 8 * kl);
                 const u32x4 cq = *reinterpret_cast<const u32x4 *>(y2 + (bt * h + hh) * n + 8 * kl);
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
@@ -585,10 +545,6 @@ int32_t bwd_bf16(const bf16 *x, const bf16 *dt, const float *A, const bf16 *B, c
     if (P.s1.lp * 4 >= lim32 || P.s2.lp * 4 >= lim32) return SSD_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < P.total) return SSD_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
-    bf16 *dyR = reinterpret_cast<bf16 *>(ws + P.dyR), *xR = reinterpret_cast<bf16 *>(ws + P.xR);
-    bf16 *CR = reinterpret_cast<bf16 *>(ws + P.CR), *BR = reinterpret_cast<bf16 *>(ws + P.BR);
-    bf16 *dtR = reinterpret_cast<bf16 *>(ws + P.dtR);
-    int32_t *seqR = reinterpret_cast<int32_t *>(ws + P.seqR);
     BwdBufs w{};
     w.sc = reinterpret_cast<float *>(ws + P.sc);
     w.part = reinterpret_cast<double *>(ws + P.part);
@@ -604,8 +560,6 @@ int32_t bwd_bf16(const bf16 *x, const bf16 *dt, const float *A, const bf16 *B, c
     hipError_t e = hipSuccess;
     auto ok = [&]() { return (e = hipGetLastError()) == hipSuccess; };
 
-    hipLaunchKernelGGL(k_bwd_prep16, dim3((unsigned)bl), dim3(256), 0, s, x, dt, B, C, dy,
-                       seq_idx, dyR, xR, CR, BR, dtR, seqR, l, (int)h, (int)g, (int)p, (int)n);
     const dim3 tgrid((unsigned)(p / 32), (unsigned)(n / 32), (unsigned)pairs);
     if (init_state)
         hipLaunchKernelGGL(k_transpose_tiles, tgrid, dim3(256), 0, s, init_state, w.initT,
@@ -621,20 +575,24 @@ int32_t bwd_bf16(const bf16 *x, const bf16 *dt, const float *A, const bf16 *B, c
     float *du = reinterpret_cast<float *>(ws + P.du), *dw = reinterpret_cast<float *>(ws + P.dw);
     // the two adjoint scans share their chunks (scan 3 reads scan 1's states)
     const int m = state_interval(P.s1, false, bf16_item_heads(p, h, g));
-    ScanArgs a1{dyR, dtR, CR, BR, A, nullptr, dt_bias, sp, dt_min, dt_max, d_final, y1,
-                d_init ? w.fin1 : nullptr, scan_ws, seq_idx ? seqR : nullptr, nullptr};
+    ScanArgs a1{dy, dt, C, B, A, nullptr, dt_bias, sp, dt_min, dt_max, d_final, y1,
+                d_init ? w.fin1 : nullptr, scan_ws, seq_idx, nullptr};
     a1.adj = 1;
+    a1.rev = 1;
+    a1.dshift = 1;
     a1.interval = m;
     if ((e = scan_bf16(P.s1, a1, s)) != hipSuccess) return SSD_ERR_HIP;
     // 3. the adjoint transposed, reversed (x slot: the head's group row of
     //    C): its boundary states are scan 1's, read transposed; read-out
     //    g_t x_t and its dot with B_t (yb_t . x_t)
-    ScanArgs a3{CR, dtR, dyR, xR, A, nullptr, dt_bias, sp, dt_min, dt_max, d_final, y3,
-                nullptr, scan_ws, seq_idx ? seqR : nullptr, nullptr};
+    ScanArgs a3{C, dt, dy, x, A, nullptr, dt_bias, sp, dt_min, dt_max, d_final, y3, nullptr,
+                scan_ws, seq_idx, nullptr};
     a3.xrow = g * n;
     a3.xdiv = (int)(h / g);
     a3.adj = 1;
-    a3.dotv = BR;
+    a3.rev = 1;
+    a3.dshift = 1;
+    a3.dotv = B;
     a3.dotrow = g * n;
     a3.dotdiv = (int)(h / g);
     a3.dotout = dw;

@@ -172,6 +172,11 @@ struct ScanArgs {
     //             chunk output runs, reading them; hbt: they hold the
     //             transposed states ([state_dim][head_dim] order of this
     //             call's state)
+    //   rev       the call's row t is the tensors' row l - 1 - t (x, B, C,
+    //             dt (row l - 1 - t + dshift, past the end: zero), seq and
+    //             the outputs y and dotout): a recurrence run backwards in
+    //             time without reversed copies
+    int rev = 0, dshift = 0;
     int interval = 0;
     const void *hb_in = nullptr;
     const float *hs_in = nullptr;

@@ -317,27 +317,30 @@ struct RowIn {
 };
 
 // Loads block k's raw rows of one head (one vector memory operation per
-// lane, three with packed sequences).  dt0: the chunk's first row of the
-// head's time steps (rows h apart); seq: the sequence's document indices;
-// t0: the chunk's first token; rows: valid rows of the chunk.  Rows past the
-// chunk's end read as zero.
+// lane, three with packed sequences).  dts: the head's time steps of the
+// whole sequence (rows h apart); seq: the sequence's document indices; t0:
+// the chunk's first token.  Rows past the sequence read as zero (rows past
+// the chunk are read but not used).  rev: row t is the tensors' row
+// l - 1 - t (its time step row l - 1 - t + dshift); the token before it is
+// the tensors' next one.
 template <bool SEQ>
-__device__ __forceinline__ void rows_load(RowIn &f, const bf16 *dt0, const int32_t *seq,
-                                          int64_t t0, int64_t l, int h, int rows, int k,
-                                          int lane) {
+__device__ __forceinline__ void rows_load(RowIn &f, const bf16 *dts, const int32_t *seq,
+                                          int64_t t0, int64_t l, int h, int k, int lane, int rev,
+                                          int dshift) {
     const int r = lane & 31;
-    int valid = rows - k * T;
-    valid = valid < 0 ? 0 : (valid > T ? T : valid);
-    const Rsrc rd = make_rsrc(dt0 + (int64_t)(valid > 0 ? k * T : 0) * h, (int64_t)valid * h * 2);
-    f.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (uint32_t)(r * h * 2), 0, 0);
+    const int64_t t = t0 + (int64_t)k * T + r;
+    // source rows outside [0, l) give offsets past the range (unsigned)
+    const int64_t src = rev ? l - 1 - t + dshift : t;
+    const Rsrc rd = make_rsrc(dts, l * h * 2);
+    f.dt = __builtin_amdgcn_raw_buffer_load_b16(rd, (uint32_t)(src * h * 2), 0, 0);
     if constexpr (SEQ) {
-        // the token before the chunk's first (t0 - 1) is read for every
-        // chunk but the sequence's first, whose row 0 compares with itself
-        const int64_t t = t0 + (int64_t)k * T + r;
+        // the token before the chunk's first is read for every chunk but
+        // the sequence's first, whose row 0 compares with itself
         const Rsrc rq = make_rsrc(seq, l * 4);
-        f.cur = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)(t * 4), 0, 0);
-        f.prv = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)((t > 0 ? t - 1 : 0) * 4),
-                                                          0, 0);
+        const int64_t sc = rev ? l - 1 - t : t;
+        const int64_t sp = t > 0 ? (rev ? l - t : t - 1) : sc;
+        f.cur = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)(sc * 4), 0, 0);
+        f.prv = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (uint32_t)(sp * 4), 0, 0);
     }
 }
 
@@ -440,6 +443,10 @@ struct Roles {
     int dotdiv;
     float *dotout;
     int hbt;  // boundary states stored transposed (row-major [N][P])
+    // rows in reversed order: row t of the call is row l - 1 - t of the
+    // tensors (and its time step row l - 1 - t + dshift, past the end
+    // reading as zero)
+    int rev, dshift;
 };
 
 // --------------------------------------------------- work items ----
@@ -492,7 +499,10 @@ template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
     static constexpr bool STATIC = K::XI % K::W == 0 && K::BI % K::W == 0;
     __device__ static __forceinline__ int klass(int j, int q) { return STATIC ? j * K::W : q; }
     uint32_t off[NJ];
-    __device__ __forceinline__ void init(int64_t xs, int64_t bs, int wave, int lane) {
+    // rev: the block's rows are read in reversed order, row r of the block
+    // from source row valid - 1 - r (offsets relative to the last valid row;
+    // rows past it fall outside the range)
+    __device__ __forceinline__ void init(int64_t xs, int64_t bs, int wave, int lane, int rev) {
         constexpr int CH = P / 8, CB = N / 8;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -500,35 +510,41 @@ template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
             if (qc < K::XI) {
                 const int s = q * 64 + lane;
                 const int hs = s / (T * CH), rem = s % (T * CH), r = rem / CH, kk = rem % CH;
-                off[j] = (uint32_t)(r * xs + hs * P + ((kk ^ xsw<P>(r)) << 3)) * 2u;
+                const int64_t rs = rev ? -(int64_t)r * xs : (int64_t)r * xs;
+                off[j] = (uint32_t)(rs + hs * P + ((kk ^ xsw<P>(r)) << 3)) * 2u;
             } else if (qc < K::XI + K::BI * (WITH_C ? 2 : 1)) {
                 const int qb = q - K::XI;
                 const int s = (qb % K::BI) * 64 + lane;
                 const int r = s / CB, kk = s % CB;
-                off[j] = (uint32_t)(r * bs + ((kk ^ Swz<f16, N>::f(r)) << 3)) * 2u;
+                const int64_t rs = rev ? -(int64_t)r * bs : (int64_t)r * bs;
+                off[j] = (uint32_t)(rs + ((kk ^ Swz<f16, N>::f(r)) << 3)) * 2u;
             } else {
                 off[j] = 0u;
             }
         }
     }
-    // Copies block rows r0.. (valid rows) of x (from xrow0, the WG's first
-    // head), B and C (from their row r0) into LDS buffer buf.
+    // Copies a block's valid rows of x (from the WG's first head), B and C
+    // into LDS buffer buf.  x, B, C: the block's first source row (rev: its
+    // lowest, the last valid row of the block).
     __device__ __forceinline__ void copy(f16 *buf, f16 *spare, const bf16 *x, const bf16 *B,
                                          const bf16 *C, int64_t xs, int64_t bs, int valid,
-                                         int wave) const {
+                                         int wave, int rev) const {
         typedef Buf<P, N, HP> L;
         const RsrcW rx = make_rsrc_w(x, (int64_t)valid * xs * 2);
         const RsrcW rb = make_rsrc_w(B, (int64_t)valid * bs * 2);
         const RsrcW rc = make_rsrc_w(WITH_C ? C : B, WITH_C ? (int64_t)valid * bs * 2 : 0);
+        const int vm = valid > 0 ? valid - 1 : 0;
+        const uint32_t ax = rev ? (uint32_t)(vm * xs * 2) : 0u;
+        const uint32_t ab = rev ? (uint32_t)(vm * bs * 2) : 0u;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int q = wave + j * K::W, qc = klass(j, q);
             if (qc < K::XI) {
-                lds_dma16(rx, (lds_void *)(buf + L::XB + q * 512), off[j]);
+                lds_dma16(rx, (lds_void *)(buf + L::XB + q * 512), off[j] + ax);
             } else if (qc < K::XI + K::BI) {
-                lds_dma16(rb, (lds_void *)(buf + L::BB + (q - K::XI) * 512), off[j]);
+                lds_dma16(rb, (lds_void *)(buf + L::BB + (q - K::XI) * 512), off[j] + ab);
             } else if (WITH_C && qc < K::XI + 2 * K::BI) {
-                lds_dma16(rc, (lds_void *)(buf + L::CB + (q - K::XI - K::BI) * 512), off[j]);
+                lds_dma16(rc, (lds_void *)(buf + L::CB + (q - K::XI - K::BI) * 512), off[j] + ab);
             } else {
                 lds_dma16(rc, (lds_void *)spare, 0u);
             }
@@ -569,25 +585,28 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     const Item it = decode_item(xcd_item(blockIdx.x, gridDim.x), nc_items, h / HP, h, g, l, Q,
                                 HP);
     const int hh = it.hh0 + hs;
-    const bf16 *xb = x + (it.b * l + it.t0) * xs + (int64_t)(it.hh0 / md.xdiv) * P;
-    const bf16 *bb = Bm + ((it.b * l + it.t0) * g + it.gi) * N;
-    const bf16 *dtb = dt + (it.b * l + it.t0) * h + hh;
+    // the sequence's rows of x (the WG's first head's slot), B and dt
+    const bf16 *xq = x + it.b * l * xs + (int64_t)(it.hh0 / md.xdiv) * P;
+    const bf16 *bq = Bm + (it.b * l * g + it.gi) * N;
+    const bf16 *dts = dt + it.b * l * h + hh;
     const int32_t *sq = SEQ ? seq + it.b * l : nullptr;
     const float a2 = A[hh] * kLog2e;
     const float bias = dt_bias ? dt_bias[hh] : 0.f;
 
     CopyPlan<P, N, HP, false> cp;
-    cp.init(xs, bs, wave, lane);
+    cp.init(xs, bs, wave, lane, md.rev);
     auto copy = [&](f16 *buf, int k) {
         int valid = it.rows - k * T;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const int64_t r0 = valid > 0 ? (int64_t)k * T : 0;
-        cp.copy(buf, spare, xb + r0 * xs, bb + r0 * bs, nullptr, xs, bs, valid, wave);
+        // the block's lowest source row
+        const int64_t sr =
+            valid > 0 ? (md.rev ? l - it.t0 - (int64_t)k * T - valid : it.t0 + (int64_t)k * T) : 0;
+        cp.copy(buf, spare, xq + sr * xs, bq + sr * bs, nullptr, xs, bs, valid, wave, md.rev);
     };
 
     // the chunk's first block
     RowIn ri;
-    rows_load<SEQ>(ri, dtb, sq, it.t0, l, h, it.rows, 0, lane);
+    rows_load<SEQ>(ri, dts, sq, it.t0, l, h, 0, lane, md.rev, md.dshift);
     copy(lds, 0);
     vm_wait<0>();
     if (part == 0)
@@ -641,7 +660,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         // every wave loads the rows (past the chunk's end they read as
         // zero), so that the loaded registers need no merge before use
         RowIn rn;
-        rows_load<SEQ>(rn, dtb, sq, it.t0, l, h, it.rows, k + 1, lane);
+        rows_load<SEQ>(rn, dts, sq, it.t0, l, h, k + 1, lane, md.rev, md.dshift);
         if (more) copy(lds + (cur ^ 1) * L::SIZE_B, k + 1);
         issue_fence();
         compute(cur * L::SIZE_B, rows[cur][hs]);
@@ -872,30 +891,37 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     const int64_t xs = md.xrow, bs = (int64_t)g * N, ys = (int64_t)h * P;
     const Item it = decode_item(xcd_item(blockIdx.x, gridDim.x), nc, h / HP, h, g, l, Q, HP);
     const int hh = it.hh0 + hs;
-    const bf16 *xb = x + (it.b * l + it.t0) * xs + (int64_t)(it.hh0 / md.xdiv) * P;
-    bf16 *yb = y + ((it.b * l + it.t0) * h + it.hh0) * P;
-    const int64_t bo = ((it.b * l + it.t0) * g + it.gi) * N;
-    const bf16 *bb = Bm + bo, *cb = Cm + bo;
-    const bf16 *dtb = dt + (it.b * l + it.t0) * h + hh;
+    // the sequence's rows of x (the WG's first head's slot), y, B, C, dt
+    const bf16 *xq = x + it.b * l * xs + (int64_t)(it.hh0 / md.xdiv) * P;
+    bf16 *yq = y + it.b * l * ys + (int64_t)it.hh0 * P;
+    const int64_t bo = (it.b * l * g + it.gi) * N;
+    const bf16 *bq = Bm + bo, *cq = Cm + bo;
+    const bf16 *dts = dt + it.b * l * h + hh;
     const int32_t *sq = SEQ ? seq + it.b * l : nullptr;
     const float a2 = A[hh] * kLog2e;
     const float bias = dt_bias ? dt_bias[hh] : 0.f;
     const float Dh = D ? D[hh] : 0.f;
+    // block k's lowest source row (rev: its last valid row)
+    auto src_row = [&](int k, int valid) -> int64_t {
+        return valid > 0 ? (md.rev ? l - it.t0 - (int64_t)k * T - valid : it.t0 + (int64_t)k * T)
+                         : 0;
+    };
 
     CopyPlan<P, N, HP, true> cp;
-    cp.init(xs, bs, wave, lane);
+    cp.init(xs, bs, wave, lane, md.rev);
     auto copy = [&](f16 *buf, int k) {
         int valid = it.rows - k * T;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const int64_t r0 = valid > 0 ? (int64_t)k * T : 0;
-        cp.copy(buf, spare, xb + r0 * xs, bb + r0 * bs, cb + r0 * bs, xs, bs, valid, wave);
+        const int64_t sr = src_row(k, valid);
+        cp.copy(buf, spare, xq + sr * xs, bq + sr * bs, cq + sr * bs, xs, bs, valid, wave,
+                md.rev);
     };
 
     // the chunk's first block and the wave's columns of the boundary state
     // (fp16 times the chunk's scale; zero for chunk 0 without an initial
     // state)
     RowIn ri;
-    rows_load<SEQ>(ri, dtb, sq, it.t0, l, h, it.rows, 0, lane);
+    rows_load<SEQ>(ri, dts, sq, it.t0, l, h, 0, lane, md.rev, md.dshift);
     copy(lds, 0);
     f32x4 accH[CPW * RT];
     {
@@ -947,8 +973,11 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     // y offsets (bytes) of rows li and 16 + li of a block, from its first
     // row: 8 consecutive columns c0 + 32 v + 8 lg .. (column tiles 2v,
     // 2v + 1) or 4 columns c0 + 4 lg .. (one tile)
-    const uint32_t yo0 = (uint32_t)(li * ys + hs * P + c0 + (CPW >= 2 ? 8 : 4) * lg) * 2u;
-    const uint32_t yo1 = yo0 + (uint32_t)(16 * ys) * 2u;
+    // y rows li and 16 + li of a block (rev: offsets relative to the
+    // block's last valid row, completed per block)
+    const uint32_t yc = (uint32_t)(hs * P + c0 + (CPW >= 2 ? 8 : 4) * lg) * 2u;
+    const uint32_t yo0 = md.rev ? yc - (uint32_t)(li * ys) * 2u : yc + (uint32_t)(li * ys) * 2u;
+    const uint32_t y16 = (uint32_t)(16 * ys) * 2u;
     // DOT: every output row dotted with the matching row of md.dotv over the
     // wave's columns (the head's slot of a [b, l, slots, P] tensor), from the
     // fp32 accumulators: the block's y values are kept (ykeep) and its dot
@@ -960,8 +989,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     u32x4 dvv[DOT ? 2 : 1][DOT ? DV : 1];
     const bf16 *dbase = nullptr;
     if constexpr (DOT)
-        dbase = md.dotv + (it.b * l + it.t0) * md.dotrow +
-                (int64_t)((it.hh0 + hs) / md.dotdiv) * P + c0;
+        dbase = md.dotv + it.b * l * md.dotrow + (int64_t)((it.hh0 + hs) / md.dotdiv) * P + c0;
 
     // One block of one wave (in the buffer at element offset bo).
     auto compute = [&](int bo, const Rows &rf, int kb, bool carry) {
@@ -1065,8 +1093,8 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         const int r0 = kb * T;
         int valid = it.rows - r0;
         valid = valid < 0 ? 0 : (valid > T ? T : valid);
-        const Rsrc ry = make_rsrc(yb + (valid > 0 ? (int64_t)r0 : 0) * ys,
-                                  (int64_t)valid * ys * 2);
+        const Rsrc ry = make_rsrc(yq + src_row(kb, valid) * ys, (int64_t)valid * ys * 2);
+        const uint32_t ya = md.rev ? yo0 + (uint32_t)((valid > 0 ? valid - 1 : 0) * ys) * 2u : yo0;
         bf16x8 xf[CPW];
 #pragma unroll
         for (int u = 0; u < CPW; ++u) xf[u] = frag_x<P>(Xs, bx, u);
@@ -1081,7 +1109,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
                 yv[u] = colscale[i2] * yh[i2][u] + yp;
                 if constexpr (DOT) ykeep[i2][u] = yv[u];
             }
-            const uint32_t off = i2 == 0 ? yo0 : yo1;
+            const uint32_t off = i2 == 0 ? ya : (md.rev ? ya - y16 : ya + y16);
             if constexpr (CPW >= 2) {
                 // tiles 2v, 2v + 1 interleave: 8 consecutive columns
                 // c0 + 32 v + 8 lg ..
@@ -1134,15 +1162,15 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
         if constexpr (DOT) {
             dvalid = it.rows - k * T;
             dvalid = dvalid > T ? T : dvalid;
-            const Rsrc rd = make_rsrc(dbase + (int64_t)k * T * md.dotrow,
+            const Rsrc rd = make_rsrc(dbase + src_row(k, dvalid) * md.dotrow,
                                       (int64_t)dvalid * md.dotrow * 2);
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
                 for (int v = 0; v < DV; ++v) {
+                    const int64_t dr = md.rev ? dvalid - 1 - (16 * i2 + li) : 16 * i2 + li;
                     const uint32_t o =
-                        (uint32_t)((16 * i2 + li) * md.dotrow + 32 * v + (CPW >= 2 ? 8 : 4) * lg) *
-                        2u;
+                        (uint32_t)(dr * md.dotrow + 32 * v + (CPW >= 2 ? 8 : 4) * lg) * 2u;
                     if constexpr (CPW >= 2) {
                         dvv[i2][v] = __builtin_bit_cast(
                             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, 0));
@@ -1154,7 +1182,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
                 }
         }
         RowIn rn;
-        rows_load<SEQ>(rn, dtb, sq, it.t0, l, h, it.rows, k + 1, lane);
+        rows_load<SEQ>(rn, dts, sq, it.t0, l, h, k + 1, lane, md.rev, md.dshift);
         if (more) copy(lds + (cur ^ 1) * L::SIZE_BC, k + 1);
         issue_fence();
         compute(cur * L::SIZE_BC, rows[cur][hs], k, more);
@@ -1186,9 +1214,9 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
                 sd += __shfl_xor(sd, 16, 64);
                 sd += __shfl_xor(sd, 32, 64);
                 const int row = 16 * i2 + li;
+                const int64_t t = it.t0 + (int64_t)k * T + row;
                 if (lg == 0 && row < dvalid)
-                    md.dotout[((it.b * l + it.t0 + (int64_t)k * T + row) * h + hh) * WPH + part] =
-                        sd;
+                    md.dotout[((it.b * l + (md.rev ? l - 1 - t : t)) * h + hh) * WPH + part] = sd;
             }
         }
         // the head's waves take turns at the next block's rows
@@ -1230,7 +1258,8 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
     const bf16 *Cm = static_cast<const bf16 *>(a.C);
     const int h = (int)pl.h, g = (int)pl.g;
     const Roles md{a.xrow ? a.xrow : (int64_t)h * P, a.xdiv, a.adj,
-                   static_cast<const bf16 *>(a.dotv), a.dotrow, a.dotdiv, a.dotout, a.hbt};
+                   static_cast<const bf16 *>(a.dotv), a.dotrow, a.dotdiv, a.dotout, a.hbt,
+                   a.rev, a.dshift};
     // row dots only on workgroups of one head (the gradient pass's
     // transposed scans)
     if (a.dotout && grouped) return hipErrorInvalidValue;
