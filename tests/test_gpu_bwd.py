@@ -131,3 +131,30 @@ def test_gradients_edge_shapes(case, io):
     seq = _seq(b, l, cuts) if any(cuts) else None
     gpu = _run(inp, cot, Q, seq=seq, d_final=dfin)
     _compare(gpu, _oracle(inp, cot, seq=seq, d_final=dfin), io)
+
+
+def test_gradients_joined_chunks():
+    """A grid large enough that the bf16 pass stores its states every 2
+    (adjoint scans, whose transposed one reads the other's states) and 4
+    (transposed forward scan) of the caller's chunks: batch sized from the
+    device's compute units; two batch rows (every head, so the group sums of
+    dB and dC are whole) against the oracle run on those rows."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    l, h, p, n, g, Q = 2048, 16, 32, 64, 2, 256
+    b = 4 * cus // ((l // Q // 2) * (h // 4))
+    assert ssd.state_chunks(b, l, h, p, n, g, Q, io="bf16") == l // Q // 2
+    inp = syn.random_case(5600, b, l, h, p, n, g, io="bf16", init_std=0.2)
+    cot = syn.cotangent_case(5601, b, l, h, p, n, io="bf16")
+    gpu = _run(inp, cot, Q)
+    rows = [0, b - 1]
+    sub = dict(inp)
+    for k in ("x", "dt", "B", "C", "init_state"):
+        sub[k] = inp[k][rows]
+    csub = dict(dy=cot["dy"][rows], d_final=cot["d_final"][rows], io=cot["io"])
+    ref = _oracle(sub, csub)
+    for k in ("dx", "ddt", "dB", "dC", "d_init"):
+        v = gpu[k][rows]
+        s = check_close(to_f64(v), ref[k], "bf16", k, AXES[k])
+        log("joined %s max_abs %.3g max_rel %.3g" % (k, s[0], s[1]))
