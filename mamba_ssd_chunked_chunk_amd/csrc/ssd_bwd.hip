@@ -597,9 +597,14 @@ int32_t bwd_bf16(const bf16 *x, const bf16 *dt, const float *A, const bf16 *B, c
     a3.dotdiv = (int)(h / g);
     a3.dotout = dw;
     a3.interval = m;
-    a3.hb_in = scan_ws + P.s1.off_hb;
-    a3.hs_in = reinterpret_cast<const float *>(scan_ws + P.s1.off_hs);
-    a3.hbt = 1;
+    if ((P.s1.l + m * P.s1.Q - 1) / (m * P.s1.Q) > 1) {
+        a3.hb_in = scan_ws + P.s1.off_hb;
+        a3.hs_in = reinterpret_cast<const float *>(scan_ws + P.s1.off_hs);
+        a3.hbt = 1;
+    } else {
+        // one chunk: scan 1 stored no states; scan 3 starts from d_final^T
+        a3.init = d_final ? w.dfT : nullptr;
+    }
     if ((e = scan_bf16(P.s2, a3, s)) != hipSuccess) return SSD_ERR_HIP;
     // 2. the forward transposed (x slot: the head's group row of B): read-out
     //    h_t dy_t, its dot with C_t (u), final state h_l^T

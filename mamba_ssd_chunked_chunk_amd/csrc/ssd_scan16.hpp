@@ -447,6 +447,11 @@ struct Roles {
     // tensors (and its time step row l - 1 - t + dshift, past the end
     // reading as zero)
     int rev, dshift;
+    // a call whose sequences are one computed chunk: the chunk output seeds
+    // its state from init32 (fp32 [b, h, N, P], or zero) and writes the
+    // state after its last row to final32 (or not), with no stored states
+    const float *init32;
+    float *final32;
 };
 
 // --------------------------------------------------- work items ----
@@ -871,7 +876,7 @@ __global__ __launch_bounds__(256) void k_scan16(
 //    that head's per-row values of the next block.
 constexpr float kSplit = 60.f;
 
-template <int P, int N, int HP, bool SEQ, bool DOT>
+template <int P, int N, int HP, bool SEQ, bool DOT, bool ONE>
 __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) void k_out16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const bf16 *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ D,
@@ -924,7 +929,26 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     rows_load<SEQ>(ri, dts, sq, it.t0, l, h, 0, lane, md.rev, md.dshift);
     copy(lds, 0);
     f32x4 accH[CPW * RT];
-    {
+    if constexpr (ONE) {
+        // one chunk: the initial state itself (four rows of a column), or zero
+        const Rsrc ri32 = make_rsrc(md.init32 ? md.init32 + (it.b * h + hh) * (int64_t)N * P
+                                              : nullptr,
+                                    md.init32 ? (int64_t)N * P * 4 : 0);
+        // per-lane offset of (row 8 lg, column c0 + col_of(u, li)); the row
+        // tr, e part is a uniform offset
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+            const uint32_t vo = (uint32_t)(8 * lg * P + c0 + col_of<CPW>(u, li)) * 4u;
+#pragma unroll
+            for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    accH[u * RT + tr][e] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(
+                                   ri32, vo, (state_row(tr, 0) + e) * P * 4, 0));
+        }
+        vm_wait<0>();
+    } else {
         const bool have = it.c > 0 || has_init;
         const Rsrc rh = make_rsrc(Hb + (((int64_t)it.b * nc + it.c) * h + hh) * (int64_t)N * P,
                                   have ? (int64_t)N * P * 2 : 0);
@@ -964,6 +988,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
             accH[t] = f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]} * sc;
         }
     }
+    // one chunk: every block carries, the last one into the final state
     if (part == 0)
         rows_prep<SEQ>(rows[0][hs], ri, a2, bias, softplus, dt_min, dt_max, 0, it.rows, 0.f,
                        lane, md.adj, it.t0 == 0);
@@ -1224,6 +1249,52 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
             rows_prep<SEQ>(rows[cur ^ 1][hs], rn, a2, bias, softplus, dt_min, dt_max, k + 1,
                            it.rows, rows[cur][hs].next, lane, md.adj, it.t0 == 0);
     }
+    if (ONE && md.final32 != nullptr && it.nblk > 0) {
+        // the last block's carry (after the loop, so that the loop is the
+        // multi-chunk kernel's): its x fragments read again, from its buffer
+        const int bo = ((it.nblk - 1) & 1) * L::SIZE_BC;
+        const Rows &rf = rows[(it.nblk - 1) & 1][hs];
+        {
+            const int ln = opaque(lane);
+            const int bx = opaque(fb.x + bo), bk = opaque(fb.kmaj + bo);
+            const Neg1 nm = neg1();
+            const f16 *Bs = lds + L::BB;
+            const f16 *Xs = lds + L::XB + hs * T * P;
+            HL xw[CPW];
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) xw[u] = xw_split(frag_x<P>(Xs, bx, u), ln, rf.w, nm);
+            if (rf.rebase) {
+                const float dec = exp2_fast(rf.mexp);
+#pragma unroll
+                for (int t = 0; t < CPW * RT; ++t) accH[t] *= dec;
+            }
+#pragma unroll
+            for (int tr = 0; tr < RT; ++tr) {
+                const bf16x8 bt = frag_kmaj<N>(Bs, bk, tr);
+#pragma unroll
+                for (int u = 0; u < CPW; ++u) {
+                    accH[u * RT + tr] = mma(bt, xw[u].hi, accH[u * RT + tr]);
+                    accH[u * RT + tr] = mma(bt, xw[u].lo, accH[u * RT + tr]);
+                }
+            }
+        }
+        // the held state is 2^next times the state after the last row
+        const float undo = exp2_fast(-rf.next);
+        const Rsrc rfin = make_rsrc(md.final32 + (it.b * h + hh) * (int64_t)N * P,
+                                    (int64_t)N * P * 4);
+        const int ln = opaque(lane), gq = ln >> 4, lq = ln & 15;
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+            const uint32_t vo = (uint32_t)(8 * gq * P + c0 + col_of<CPW>(u, lq)) * 4u;
+#pragma unroll
+            for (int tr = 0; tr < RT; ++tr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(uint32_t, accH[u * RT + tr][e] * undo), rfin, vo,
+                        (state_row(tr, 0) + e) * P * 4, 0);
+        }
+    }
     // no copy may still be writing this workgroup's LDS when it exits
     vm_wait<0>();
 }
@@ -1257,9 +1328,12 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
     const bf16 *Bm = static_cast<const bf16 *>(a.B);
     const bf16 *Cm = static_cast<const bf16 *>(a.C);
     const int h = (int)pl.h, g = (int)pl.g;
+    // sequences of one computed chunk (no per-chunk states asked): the chunk
+    // output alone, from the initial state to the final one
+    const bool one = pl.nc == 1 && a.states == nullptr && a.hb_in == nullptr;
     const Roles md{a.xrow ? a.xrow : (int64_t)h * P, a.xdiv, a.adj,
                    static_cast<const bf16 *>(a.dotv), a.dotrow, a.dotdiv, a.dotout, a.hbt,
-                   a.rev, a.dshift};
+                   a.rev, a.dshift, one ? a.init : nullptr, one ? a.final_state : nullptr};
     // row dots only on workgroups of one head (the gradient pass's
     // transposed scans)
     if (a.dotout && grouped) return hipErrorInvalidValue;
@@ -1288,25 +1362,37 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
         const int64_t items = pl.b * pl.nc * (h / HP);
         if (items <= 0) return hipSuccess;
         if constexpr (HP == 1) {
+            if (a.dotout && one)
+                return launch_timed(&k_out16<P, N, 1, SQ, true, true>, dim3((unsigned)items),
+                                    dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
+                                    a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
+                                    static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
+                                    0, md);
             if (a.dotout)
-                return launch_timed(&k_out16<P, N, 1, SQ, true>, dim3((unsigned)items),
+                return launch_timed(&k_out16<P, N, 1, SQ, true, false>, dim3((unsigned)items),
                                     dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
                                     a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
                                     static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
                                     a.init != nullptr ? 1 : 0, md);
         }
-        return launch_timed(&k_out16<P, N, HP, SQ, false>, dim3((unsigned)items), dim3(NT), s,
-                            a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D, a.dt_bias, a.softplus,
-                            a.dt_min, a.dt_max, a.seq, Hb, Hs, static_cast<bf16 *>(a.y), pl.l,
-                            h, g, pl.Q, (int)pl.nc, a.init != nullptr ? 1 : 0, md);
+        if (one)
+            return launch_timed(&k_out16<P, N, HP, SQ, false, true>, dim3((unsigned)items),
+                                dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
+                                a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
+                                static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc, 0, md);
+        return launch_timed(&k_out16<P, N, HP, SQ, false, false>, dim3((unsigned)items),
+                            dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D, a.dt_bias,
+                            a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
+                            static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
+                            a.init != nullptr ? 1 : 0, md);
     };
     typedef std::integral_constant<int, 1> One;
     typedef std::integral_constant<int, HPG> Grp;
     typedef std::true_type Yes;
     typedef std::false_type No;
 
-    // boundary states given (hb_in): the chunk output alone
-    if (!a.hb_in) {
+    // boundary states given (hb_in), or one chunk: the chunk output alone
+    if (!a.hb_in && !one) {
         hipError_t e = grouped ? (seq ? launch_state(Grp{}, Yes{}) : launch_state(Grp{}, No{}))
                                : (seq ? launch_state(One{}, Yes{}) : launch_state(One{}, No{}));
         if (e != hipSuccess) return e;
