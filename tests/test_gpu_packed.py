@@ -58,6 +58,27 @@ def _pid(c):
     return "b%d_l%d_h%d_p%d_n%d_g%d_Q%d" % c[:7]
 
 
+# sequences of one chunk without per-chunk states: the bf16 scan runs its
+# chunk output alone (initial state in, final state out)
+ONE_CHUNK = [
+    (2, 200, 8, 64, 128, 2, 256, 0.3, [(3, 50, 51, 199), ()]),
+    (1, 256, 4, 128, 64, 1, 256, 0.2, [(128, 129)]),
+    (3, 70, 4, 32, 32, 4, 128, 0.0, [(1,), (), (33, 69)]),
+]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ONE_CHUNK, ids=_pid)
+def test_packed_one_chunk(orc, case, io):
+    b, l, h, p, n, g, Q, init, cuts = case
+    inp = syn.random_case(3100 + sum(case[:7]), b, l, h, p, n, g, io=io, init_std=init)
+    seq = _seq(b, l, cuts) if any(cuts) else None
+    y, fin = _run(inp, Q, seq=seq)
+    yo, fo = orc.scan(**oracle_kw(inp), seq_idx=seq)
+    check_close(to_f64(y), yo, io, "y", Y_AXES)
+    check_close(to_f64(fin), fo, io, "final_state", STATE_AXES)
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("case", PACKED, ids=_pid)
 def test_packed_sequences_parity(orc, case, io):
