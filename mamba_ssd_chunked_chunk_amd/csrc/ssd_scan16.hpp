@@ -161,9 +161,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 // WPH waves per head, each owning PW head_dim columns (CPW column tiles of
 // 16) of its head: one wave per head up to head_dim 64 (so the per-block
 // work that does not depend on the columns, the scores and the per-row
-// values, is done once per head), two for head_dim 128.
-template <int P, int N, int HP> struct Shape {
-    static constexpr int WPH = P >= 128 ? P / 64 : 1;
+// values, is done once per head), two for head_dim 128; WH > 0 sets WPH
+// (the split layouts of head_dim 64, two waves of 32 columns).
+template <int P, int N, int HP, int WH = 0> struct Shape {
+    static constexpr int WPH = WH > 0 ? WH : (P >= 128 ? P / 64 : 1);
     static constexpr int PW = P / WPH;
     static constexpr int CPW = PW / 16;  // column tiles per wave
     static constexpr int W = HP * WPH, NT = 64 * W;
@@ -483,8 +484,8 @@ __device__ __forceinline__ Item decode_item(int64_t item, int nc, int hpg, int h
 // from a bank-aligned position so that reads of B and C at the same
 // in-matrix offset (which the compiler pairs into one instruction) fall in
 // different banks.
-template <int P, int N, int HP> struct Buf {
-    typedef Shape<P, N, HP> K;
+template <int P, int N, int HP, int WH = 0> struct Buf {
+    typedef Shape<P, N, HP, WH> K;
     static constexpr int XB = 0, BB = K::XE + 64, CB = BB + K::BE + 64;
     // buffer sizes a multiple of N elements (see FragBase)
     static constexpr int SIZE_B = (BB + K::BE + N - 1) / N * N;
@@ -495,8 +496,8 @@ template <int P, int N, int HP> struct Buf {
 // one wave: instruction j of the wave is wave instruction q = wave + j W of
 // the block; x first (XI instructions), then B (BI), then C (BI, WITH_C).
 // Each lane fetches the 16-byte source chunk its swizzled LDS slot holds.
-template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
-    typedef Shape<P, N, HP> K;
+template <int P, int N, int HP, bool WITH_C, int WH = 0> struct CopyPlan {
+    typedef Shape<P, N, HP, WH> K;
     static constexpr int NJ = K::template per_wave<WITH_C>();
     // When the x and B blocks are whole multiples of W instructions, all W
     // instructions j W .. j W + W - 1 copy the same matrix, so which one a
@@ -534,7 +535,7 @@ template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
     __device__ __forceinline__ void copy(f16 *buf, f16 *spare, const bf16 *x, const bf16 *B,
                                          const bf16 *C, int64_t xs, int64_t bs, int valid,
                                          int wave, int rev) const {
-        typedef Buf<P, N, HP> L;
+        typedef Buf<P, N, HP, WH> L;
         const RsrcW rx = make_rsrc_w(x, (int64_t)valid * xs * 2);
         const RsrcW rb = make_rsrc_w(B, (int64_t)valid * bs * 2);
         const RsrcW rc = make_rsrc_w(WITH_C ? C : B, WITH_C ? (int64_t)valid * bs * 2 : 0);
@@ -568,19 +569,19 @@ template <int P, int N, int HP, bool WITH_C> struct CopyPlan {
 //    head's largest magnitude m (written as Smax), with the chunk's total
 //    log2 decay (Lam); chunk-0 items also write the largest magnitude of the
 //    initial state of their heads (Imax).
-template <int P, int N, int HP, bool SEQ>
-__global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) void k_state16(
+template <int P, int N, int HP, bool SEQ, int WH>
+__global__ __launch_bounds__((Shape<P, N, HP, WH>::NT), (Shape<P, N, HP, WH>::MINB)) void k_state16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ dt,
     const float *__restrict__ A, const float *__restrict__ dt_bias, int softplus, float dt_min,
     float dt_max, const int32_t *__restrict__ seq, const float *__restrict__ init,
     f16 *__restrict__ St, float *__restrict__ Smax, float *__restrict__ Lam,
     float *__restrict__ Imax, int64_t l, int h, int g, int64_t Q, int nc, int nc_items,
     Roles md) {
-    typedef Shape<P, N, HP> K;
-    typedef Buf<P, N, HP> L;
+    typedef Shape<P, N, HP, WH> K;
+    typedef Buf<P, N, HP, WH> L;
     constexpr int CPW = K::CPW, RT = K::RT, WPH = K::WPH;
     __shared__ __attribute__((aligned(16))) f16 lds[2 * L::SIZE_B];
-    __shared__ __attribute__((aligned(16))) f16 spare[CopyPlan<P, N, HP, false>::STATIC ? 8 : 512];
+    __shared__ __attribute__((aligned(16))) f16 spare[CopyPlan<P, N, HP, false, WH>::STATIC ? 8 : 512];
     __shared__ Rows rows[2][HP];
     __shared__ float wmax[K::W], wimax[K::W];
 
@@ -598,7 +599,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
     const float a2 = A[hh] * kLog2e;
     const float bias = dt_bias ? dt_bias[hh] : 0.f;
 
-    CopyPlan<P, N, HP, false> cp;
+    CopyPlan<P, N, HP, false, WH> cp;
     cp.init(xs, bs, wave, lane, md.rev);
     auto copy = [&](f16 *buf, int k) {
         int valid = it.rows - k * T;
@@ -876,18 +877,18 @@ __global__ __launch_bounds__(256) void k_scan16(
 //    that head's per-row values of the next block.
 constexpr float kSplit = 60.f;
 
-template <int P, int N, int HP, bool SEQ, bool DOT, bool ONE>
-__global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) void k_out16(
+template <int P, int N, int HP, bool SEQ, bool DOT, bool ONE, int WH>
+__global__ __launch_bounds__((Shape<P, N, HP, WH>::NT), (Shape<P, N, HP, WH>::MINB)) void k_out16(
     const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const bf16 *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ D,
     const float *__restrict__ dt_bias, int softplus, float dt_min, float dt_max,
     const int32_t *__restrict__ seq, const f16 *__restrict__ Hb, const float *__restrict__ Hs,
     bf16 *__restrict__ y, int64_t l, int h, int g, int64_t Q, int nc, int has_init, Roles md) {
-    typedef Shape<P, N, HP> K;
-    typedef Buf<P, N, HP> L;
+    typedef Shape<P, N, HP, WH> K;
+    typedef Buf<P, N, HP, WH> L;
     constexpr int CPW = K::CPW, RT = K::RT, WPH = K::WPH, NB = K::NB, NS = K::NS;
     __shared__ __attribute__((aligned(16))) f16 lds[2 * L::SIZE_BC];
-    __shared__ __attribute__((aligned(16))) f16 spare[CopyPlan<P, N, HP, true>::STATIC ? 8 : 512];
+    __shared__ __attribute__((aligned(16))) f16 spare[CopyPlan<P, N, HP, true, WH>::STATIC ? 8 : 512];
     __shared__ Rows rows[2][HP];
 
     const int wave = wave_id(), lane = threadIdx.x & 63;
@@ -912,7 +913,7 @@ __global__ __launch_bounds__((Shape<P, N, HP>::NT), (Shape<P, N, HP>::MINB)) voi
                          : 0;
     };
 
-    CopyPlan<P, N, HP, true> cp;
+    CopyPlan<P, N, HP, true, WH> cp;
     cp.init(xs, bs, wave, lane, md.rev);
     auto copy = [&](f16 *buf, int k) {
         int valid = it.rows - k * T;
@@ -1343,58 +1344,89 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
     int64_t nc_state = keep_last ? pl.nc : pl.nc - 1;
     if (a.init && nc_state < 1) nc_state = 1;
     const bool seq = a.seq != nullptr;
+    // Workgroup layout: 0 one head, 1 a group's HPG heads (one wave per head
+    // up to head_dim 64), 2 HPG / 2 heads, 3 one head, both with two waves per
+    // head_dim 64 head (32 columns each).  A wave of a split head holds half
+    // the state (64 accumulator registers, three waves per SIMD) and repeats
+    // the head's scores and per-row values.  Grouped calls split where the
+    // split grid fits the chip at once (three workgroups per compute unit):
+    // there the grouped grid would leave compute units with one workgroup
+    // beside others with two.  Calls that are not grouped always split: one
+    // head of one wave holds the B and C blocks for itself, and LDS then
+    // allows only three such waves per compute unit.  The row dots of the
+    // gradient pass's transposed scans keep one wave per head.
+    int lay = grouped ? 1 : 0;
+    if (P == 64 && !a.dotout) {
+        if (!grouped)
+            lay = (h / g) % 2 == 0 ? 2 : 3;
+        else if (2 * pl.b * pl.nc * (h / HPG) <= 3 * (int64_t)device_cus())
+            lay = 2;
+    }
 
-    auto launch_state = [&](auto hp_c, auto seq_c) -> hipError_t {
-        constexpr int HP = decltype(hp_c)::value;
+    typedef std::integral_constant<int, 1> One;
+    typedef std::integral_constant<int, HPG> Grp;
+    typedef std::true_type Yes;
+    typedef std::false_type No;
+
+    auto launch_state = [&](auto hp_c, auto wh_c, auto seq_c) -> hipError_t {
+        constexpr int HP = decltype(hp_c)::value, WH = decltype(wh_c)::value;
         constexpr bool SQ = decltype(seq_c)::value;
-        constexpr int NT = Shape<P, N, HP>::NT;
+        constexpr int NT = Shape<P, N, HP, WH>::NT;
         const int64_t items = pl.b * nc_state * (h / HP);
         if (items <= 0) return hipSuccess;
-        return launch_timed(&k_state16<P, N, HP, SQ>, dim3((unsigned)items), dim3(NT), s, a.ev,
-                            kSlotState, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min,
+        return launch_timed(&k_state16<P, N, HP, SQ, WH>, dim3((unsigned)items), dim3(NT), s,
+                            a.ev, kSlotState, x, Bm, dt, a.A, a.dt_bias, a.softplus, a.dt_min,
                             a.dt_max, a.seq, a.init, St, Smax, Lam, Imax, pl.l, h, g, pl.Q,
                             (int)pl.nc, (int)nc_state, md);
     };
-    auto launch_out = [&](auto hp_c, auto seq_c) -> hipError_t {
-        constexpr int HP = decltype(hp_c)::value;
+    auto launch_out = [&](auto hp_c, auto wh_c, auto seq_c) -> hipError_t {
+        constexpr int HP = decltype(hp_c)::value, WH = decltype(wh_c)::value;
         constexpr bool SQ = decltype(seq_c)::value;
-        constexpr int NT = Shape<P, N, HP>::NT;
+        constexpr int NT = Shape<P, N, HP, WH>::NT;
         const int64_t items = pl.b * pl.nc * (h / HP);
         if (items <= 0) return hipSuccess;
-        if constexpr (HP == 1) {
+        if constexpr (HP == 1 && WH == 0) {
             if (a.dotout && one)
-                return launch_timed(&k_out16<P, N, 1, SQ, true, true>, dim3((unsigned)items),
+                return launch_timed(&k_out16<P, N, 1, SQ, true, true, 0>, dim3((unsigned)items),
                                     dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
                                     a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
                                     static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
                                     0, md);
             if (a.dotout)
-                return launch_timed(&k_out16<P, N, 1, SQ, true, false>, dim3((unsigned)items),
+                return launch_timed(&k_out16<P, N, 1, SQ, true, false, 0>, dim3((unsigned)items),
                                     dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
                                     a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
                                     static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
                                     a.init != nullptr ? 1 : 0, md);
         }
         if (one)
-            return launch_timed(&k_out16<P, N, HP, SQ, false, true>, dim3((unsigned)items),
+            return launch_timed(&k_out16<P, N, HP, SQ, false, true, WH>, dim3((unsigned)items),
                                 dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D,
                                 a.dt_bias, a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
                                 static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc, 0, md);
-        return launch_timed(&k_out16<P, N, HP, SQ, false, false>, dim3((unsigned)items),
+        return launch_timed(&k_out16<P, N, HP, SQ, false, false, WH>, dim3((unsigned)items),
                             dim3(NT), s, a.ev, kSlotOut, x, Bm, Cm, dt, a.A, a.D, a.dt_bias,
                             a.softplus, a.dt_min, a.dt_max, a.seq, Hb, Hs,
                             static_cast<bf16 *>(a.y), pl.l, h, g, pl.Q, (int)pl.nc,
                             a.init != nullptr ? 1 : 0, md);
     };
-    typedef std::integral_constant<int, 1> One;
-    typedef std::integral_constant<int, HPG> Grp;
-    typedef std::true_type Yes;
-    typedef std::false_type No;
+    // runs a launcher in the call's layout: one head per workgroup, a group's
+    // HPG heads, or (split) half as many heads with two waves per head
+    auto dispatch = [&](auto launch) -> hipError_t {
+        typedef std::integral_constant<int, 0> W0;
+        if constexpr (P == 64) {
+            typedef std::integral_constant<int, HPG / 2> Half;
+            typedef std::integral_constant<int, 2> W2;
+            if (lay == 2) return seq ? launch(Half{}, W2{}, Yes{}) : launch(Half{}, W2{}, No{});
+            if (lay == 3) return seq ? launch(One{}, W2{}, Yes{}) : launch(One{}, W2{}, No{});
+        }
+        if (lay == 1) return seq ? launch(Grp{}, W0{}, Yes{}) : launch(Grp{}, W0{}, No{});
+        return seq ? launch(One{}, W0{}, Yes{}) : launch(One{}, W0{}, No{});
+    };
 
     // boundary states given (hb_in), or one chunk: the chunk output alone
     if (!a.hb_in && !one) {
-        hipError_t e = grouped ? (seq ? launch_state(Grp{}, Yes{}) : launch_state(Grp{}, No{}))
-                               : (seq ? launch_state(One{}, Yes{}) : launch_state(One{}, No{}));
+        hipError_t e = dispatch(launch_state);
         if (e != hipSuccess) return e;
 
         const int64_t np4 = (int64_t)N * P / 4;
@@ -1422,8 +1454,7 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
 
-    return grouped ? (seq ? launch_out(Grp{}, Yes{}) : launch_out(Grp{}, No{}))
-                   : (seq ? launch_out(One{}, Yes{}) : launch_out(One{}, No{}));
+    return dispatch(launch_out);
 }
 
 }  // namespace ssd
