@@ -115,15 +115,19 @@ int device_cus();
 // chunk in 32-row blocks with a running state, so a chunk's length costs no
 // extra arithmetic: it sets only how many states are stored, scanned and
 // read back (each once) and how many work items the two parallel passes
-// have.  Where the caller asks for no state after every chunk and four or
-// more workgroups per compute unit remain, 4 (else 2) consecutive chunks of
-// the caller are computed as one, which divides that state traffic by as
-// much.  It is the same sum over the same blocks, with fewer states rounded
-// to their stored type on the way.  hp: heads per work item.
+// have.  Where the caller asks for no state after every chunk, the largest
+// of 8, 4 and 2 consecutive chunks of the caller is computed as one that
+// still leaves two or more workgroups per compute unit (the grid then fills
+// the chip at least once at two resident workgroups each), which divides
+// the state traffic by as much; no longer join where a shorter one already
+// covers the whole sequence.  It is the same sum over the same blocks, with
+// fewer states rounded to their stored type on the way.  hp: heads per work
+// item.
 inline int state_interval(const ScanPlan &pl, bool per_chunk_states, int hp) {
     if (per_chunk_states || pl.Q % 32 != 0) return 1;
-    const int64_t want = 4 * (int64_t)device_cus();
-    for (int m = 4; m > 1; m /= 2) {
+    const int64_t want = 2 * (int64_t)device_cus();
+    for (int m = 8; m > 1; m /= 2) {
+        if ((pl.l + (m / 2) * pl.Q - 1) / ((m / 2) * pl.Q) == 1) continue;
         const int64_t nc = (pl.l + m * pl.Q - 1) / (m * pl.Q);
         if (pl.b * nc * (pl.h / hp) >= want) return m;
     }

@@ -134,16 +134,18 @@ def test_gradients_edge_shapes(case, io):
 
 
 def test_gradients_joined_chunks():
-    """A grid large enough that the bf16 pass stores its states every 2
-    (adjoint scans, whose transposed one reads the other's states) and 4
-    (transposed forward scan) of the caller's chunks: batch sized from the
-    device's compute units; two batch rows (every head, so the group sums of
-    dB and dC are whole) against the oracle run on those rows."""
+    """A grid large enough that the bf16 pass stores its states every 2 of
+    the caller's chunks in the adjoint scans (whose transposed one reads the
+    other's states) and computes the transposed forward scan (one head per
+    workgroup, four times the items) as one chunk per sequence: batch sized
+    from the device's compute units; two batch rows (every head, so the
+    group sums of dB and dC are whole) against the oracle run on those
+    rows."""
     import mamba_ssd_chunked_chunk_amd as ssd
     torch = torch_mod()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     l, h, p, n, g, Q = 2048, 16, 32, 64, 2, 256
-    b = 4 * cus // ((l // Q // 2) * (h // 4))
+    b = 3 * cus // ((l // Q // 2) * (h // 4))
     assert ssd.state_chunks(b, l, h, p, n, g, Q, io="bf16") == l // Q // 2
     inp = syn.random_case(5600, b, l, h, p, n, g, io="bf16", init_std=0.2)
     cot = syn.cotangent_case(5601, b, l, h, p, n, io="bf16")

@@ -141,18 +141,19 @@ def test_forward_then_steps_equals_long_forward(orc, io):
     check_close(to_f64(st), fo, io, "state", STATE_AXES)
 
 
-@pytest.mark.parametrize("joined", [2, 4])
+@pytest.mark.parametrize("joined", [2, 4, 8])
 def test_joined_chunks_parity(orc, joined):
-    """Grids large enough that the bf16 scan computes 2 or 4 of the caller's
-    256-token chunks as one (fewer stored states): batch sized from the
-    device's compute units so the grid lands on that case; sampled
+    """Grids large enough that the bf16 scan computes 2, 4 or 8 of the
+    caller's 256-token chunks as one (fewer stored states): batch sized from
+    the device's compute units so the grid lands on that case; sampled
     (batch, head) pairs against the oracle, with an initial and a final
     state for the 4-chunk case."""
     torch = torch_mod()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    l, h, g, chunk = 2048, 16, 2, 256
-    # workgroups of 4 heads: batch * (chunks / joined) * 4 reaches 4 per CU
-    b = 4 * cus // ((l // chunk // joined) * (h // 4))
+    l, h, g, chunk = (4096 if joined == 8 else 2048), 16, 2, 256
+    # workgroups of 4 heads: batch * (chunks / joined) * 4 = 3 per CU, so
+    # joining twice as many would leave fewer than 2 per CU
+    b = 3 * cus // ((l // chunk // joined) * (h // 4))
     w = syn.Workload("joined%d" % joined, b, l, h, 16, 32, g, chunk,
                      init_std=0.1 if joined == 4 else 0.0, seed=40 + joined)
     import mamba_ssd_chunked_chunk_amd as ssd
