@@ -39,21 +39,26 @@ SLOTS = ("chunk_state", "state_scan", "chunk_out")
 HEADLINE = "grouped_long"
 SCAN_WORKLOADS = ("tiny_fp32", "mamba2_130m", "mamba2_2p7b", "grouped_long", "decode_2p7b")
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("mamba_ssd_chunked_chunk_amd/csrc/ssd_scan16.hpp",
-                  "mamba_ssd_chunked_chunk_amd/csrc/ssd_device.hpp",
-                  "mamba_ssd_chunked_chunk_amd/csrc/ssd_plan.hpp")
+_CSRC = "mamba_ssd_chunked_chunk_amd/csrc/"
+# the sources of each profiled kernel (its counter summaries are retired
+# when they change)
+KERNEL_SOURCES = {
+    "scan": tuple(_CSRC + f for f in ("ssd_scan16.hpp", "ssd_device.hpp", "ssd_plan.hpp")),
+    "k_step": tuple(_CSRC + f for f in ("ssd_step.hpp", "ssd_device.hpp", "ssd_plan.hpp")),
+}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """Digest of the scan kernels' code: comments and blank lines do not
-    count, so a comment edit does not retire the counter summaries."""
+def source_digest(kernel: str = "scan") -> str:
+    """Digest of a kernel's code (the bf16 scan kernels: "scan"): comments
+    and blank lines do not count, so a comment edit does not retire the
+    counter summaries."""
     import re
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES["k_step" if kernel == "k_step" else "scan"]:
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -125,7 +130,7 @@ def measured_traffic(kernel: str, workload: str):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     try:
-        if kv.get("source_digest") != source_digest():
+        if kv.get("source_digest") != source_digest(kernel):
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
@@ -256,7 +261,8 @@ def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4):
 CALIB_BYTES = 256 << 20
 # kernel name patterns of the bf16 scan (the io type of every scan workload
 # but the tiny fp32 one)
-PROFILED = {"k_state16": "k_state16", "k_scan16": "k_scan16", "k_out16": "k_out16"}
+PROFILED = {"k_state16": "k_state16", "k_scan16": "k_scan16", "k_out16": "k_out16",
+            "k_step": "k_step"}
 
 
 def _csv_rows(path):
@@ -297,8 +303,9 @@ def summarize(a):
         with open(path, "w") as f:
             f.write("# rocprofv3 kernel trace of the bf16 chunked scan on the %s workload\n" % wl)
             f.write("# command (from /tmp with TMPDIR=/tmp, repository at $R):\n#   %s\n" % cmd)
-            f.write("# every dispatch of the three kernels: the probe's warmup, plain and "
-                    "event-timed launches\n\n")
+            f.write("# every dispatch of the kernels: the probe's warmup, plain and "
+                    "event-timed launches (decode: then the steps after the prefill, "
+                    "as many again)\n\n")
             f.write("%-12s %6s %10s %10s %10s %10s\n" % ("kernel", "calls", "avg_us", "med_us",
                                                         "min_us", "max_us"))
             for k in PROFILED:
@@ -307,6 +314,8 @@ def summarize(a):
                     f.write("%-12s %6d %10.2f %10.2f %10.2f %10.2f\n" % (
                         k, len(v), sum(v) / len(v), v[len(v) // 2], v[0], v[-1]))
             f.write("\nsource_digest: %s\n" % source_digest())
+            if per.get("k_step"):
+                f.write("k_step_source_digest: %s\n" % source_digest("k_step"))
         print("wrote", path)
         return
     if kind == "traffic":
@@ -352,7 +361,7 @@ def summarize(a):
                 f.write("fetch_scale: %.4f\n" % scale["FETCH_SIZE"])
                 f.write("write_scale: %.4f\n" % scale["WRITE_SIZE"])
                 f.write("hbm_bytes_per_launch: %d\n" % int(hbm))
-                f.write("source_digest: %s\n" % source_digest())
+                f.write("source_digest: %s\n" % source_digest(k))
             print("wrote", path)
         return
     raise SystemExit("unknown summary kind %r" % kind)
@@ -409,6 +418,9 @@ def main():
         if w.name == "decode_2p7b":
             w = w.replace(name="decode_2p7b_prefill")
         r = time_scan(torch, ssd, w, dev, steps=args.probe_steps, warmup=2)
+        if w.name == "decode_2p7b_prefill":
+            # the decode step after the prefill (the k_step counters)
+            bench_decode(argparse.Namespace(decode_steps=args.probe_steps), torch, ssd, syn, dev)
         # calibration: a plain elementwise kernel that reads CALIB_BYTES and
         # writes CALIB_BYTES (torch.neg; a same-type copy_ would go to the
         # copy engine, which the counters do not see)
