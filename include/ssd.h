@@ -197,10 +197,12 @@ size_t ssd_chunk_scan_workspace_bytes(int64_t batch, int64_t seqlen, int64_t hea
  * ssd_chunk_scan_ex call with these sizes computes, stores and scans on the
  * current HIP device: the caller's chunks (ceil(seqlen / chunk), or the
  * coarser computed chunks of a chunk shorter than 32 tokens), except that
- * the bf16 scan computes runs of 2 or 4 of the caller's chunks as one chunk
- * when it asks for no state after every chunk, the chunk is a multiple of
- * 32 tokens and the two parallel passes still have at least four work items
- * per compute unit of the device.  Each computed chunk is the same sum over
+ * the bf16 scan computes runs of 8, 4 or 2 of the caller's chunks as one
+ * chunk when it asks for no state after every chunk and the chunk is a
+ * multiple of 32 tokens: the longest run after which the two parallel
+ * passes still have at least two workgroups per compute unit of the device
+ * (none longer than a shorter run that already covers the whole sequence).
+ * Each computed chunk is the same sum over
  * the same 32-row blocks (kongchang "Mamba2" page, chunk-scan entry: the
  * chunk length is a blocking of the one recurrence), so only the number of
  * stored states changes.  The workspace's state arrays are then filled for

@@ -29,7 +29,7 @@ SMALL = [
     (1, 1000, 2, 64, 64, 2, 64, 0.0),     # 16 chunks through the state scan
     (1, 1500, 4, 64, 128, 1, 512, 0.1),   # long chunks: 16 row blocks carried per chunk
     (2, 1400, 2, 64, 128, 1, 700, 0.2),   # chunk of 700 rows, ragged blocks
-    (1, 200, 3, 64, 128, 1, 64, 0.1),     # odd group size: one head per workgroup
+    (1, 200, 3, 64, 128, 1, 64, 0.1),     # odd group size: one head (two waves) per workgroup
     (2, 130, 8, 32, 128, 2, 64, 0.1),     # head_dim 32, four heads per workgroup
 ]
 
