@@ -602,7 +602,74 @@ def bench_neighbors(args, torch, ssd, syn, dev):
                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    res["mixer"] = bench_mixer(args, torch, ssd, syn, dev)
     res["config"] = {"workload": "mamba2_130m mixer", "conv_width": K, "norm_groups": 1}
+    return res
+
+
+def bench_mixer(args, torch, ssd, syn, dev, sets=4):
+    """The whole mixer between the projections at the 130m shape (8 x 2048
+    tokens, bf16, conv width 4 over 1792 channels, one RMS norm over 1536):
+    one ssd_mixer_forward call against the three entry points called in a
+    row on the same inputs, both cycling through `sets` independently drawn
+    input sets (xbc, dt, z: 110 MB a set) so that inputs are not served
+    from the 256 MB Infinity Cache."""
+    w = syn.WORKLOADS["mamba2_130m"]
+    b, l, h, p, n, g, Q, K = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, \
+        w.chunk, 4
+    ch = h * p + 2 * g * n
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(901)
+    S = []
+    for _ in range(sets):
+        S.append(dict(xbc=torch.randn(b, l, ch, generator=gen, device=dev).bfloat16(),
+                      z=torch.randn(b, l, h * p, generator=gen, device=dev).bfloat16(),
+                      dt=torch.randn(b, l, h, generator=gen, device=dev).bfloat16()))
+    wt = (torch.rand(ch, K, generator=gen, device=dev) * 2 - 1) / math.sqrt(K)
+    cb = (torch.rand(ch, generator=gen, device=dev) * 2 - 1) / math.sqrt(K)
+    A = -torch.exp(torch.rand(h, generator=gen, device=dev) * math.log(16))
+    dtb = torch.log(torch.expm1(torch.exp(
+        torch.rand(h, generator=gen, device=dev) * (math.log(0.1) - math.log(1e-3)) +
+        math.log(1e-3))))
+    D = torch.ones(h, device=dev)
+    nw = 1 + 0.1 * torch.randn(h * p, generator=gen, device=dev)
+    out = torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ssd.mixer_workspace_bytes(b, l, h, p, n, g, Q), dtype=torch.uint8,
+                     device=dev)
+    xs = (torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev),
+          torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev),
+          torch.empty((b, l, g, n), dtype=torch.bfloat16, device=dev))
+    y = torch.empty((b, l, h, p), dtype=torch.bfloat16, device=dev)
+    sws = torch.empty(ssd.workspace_bytes(b, l, h, p, n, g, Q), dtype=torch.uint8, device=dev)
+
+    def one(i):
+        s = S[i % sets]
+        ssd.mixer_forward(s["xbc"], s["dt"], A, wt, h, p, n, g, z=s["z"], conv_bias=cb, D=D,
+                          dt_bias=dtb, norm_weight=nw, chunk_size=Q, out=out, workspace=ws)
+
+    def chain(i):
+        s = S[i % sets]
+        x, B, C = ssd.conv1d_silu(s["xbc"], wt, h, p, n, g, bias=cb, out=xs)
+        ssd.chunk_scan(x, s["dt"], A, B, C, D, chunk_size=Q, dt_bias=dtb, out=y, workspace=sws)
+        ssd.gated_norm(y.reshape(b * l, h * p), s["z"].reshape(b * l, h * p), nw,
+                       out=out.reshape(b * l, h * p))
+    steps = max(args.steps // 2, 10)
+    res = {}
+    for name, fn in (("one_call", one), ("separate_calls", chain)):
+        wall, ev = _time_calls(torch, fn, steps)
+        res[name] = {"ms_per_call": round(ev, 4), "wall_ms_per_call": round(wall, 4),
+                     "value": round(b * l / (ev * 1e-3), 1), "unit": "tokens/s"}
+        log("mixer %s: %.4f ms" % (name, ev))
+    # bytes a mixer must move: xbc, dt and z read, out written (bf16), the
+    # conv taps and the per-head and norm parameters (the scan's state
+    # round trip and the x/B/C and y intermediates are the design's, not
+    # the method's)
+    alg = (b * l * (ch + h + 2 * h * p)) * 2 + ch * (K + 1) * 4 + 3 * h * 4 + h * p * 4
+    ms = res["one_call"]["ms_per_call"]
+    res["alg_bytes"] = alg
+    res["frac_of_hbm_roof"] = round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    res["one_call_over_separate"] = round(ms / res["separate_calls"]["ms_per_call"], 4)
+    res["input_sets"] = sets
     return res
 
 

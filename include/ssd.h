@@ -6,7 +6,8 @@
  * packed documents and the state after every chunk or token,
  * ssd_chunk_scan_noalloc on the library's own scratch), the decode
  * step (ssd_step), the steps just before and after the scan in a Mamba-2
- * mixer (ssd_conv1d_silu, ssd_gated_norm), the deterministic gradient pass
+ * mixer (ssd_conv1d_silu, ssd_gated_norm, and both with the scan in one call:
+ * ssd_mixer_forward), the deterministic gradient pass
  * (ssd_chunk_scan_bwd), and the pieces of a sequence split into segments
  * (ssd_segment_log_decay, ssd_combine_segments); plus workspace queries
  * and status strings.
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 /* io dtype of x, dt, B, C and y */
 enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 };
@@ -324,6 +325,56 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
 int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *out,
                        int64_t rows, int64_t dim, int64_t group_size, float eps,
                        int32_t normalize, int32_t io_dtype, void *hip_stream);
+
+/*
+ * ssd_mixer_forward -- the Mamba-2 mixer between its two projections in one
+ * call: the split of the projection channels, the causal conv1d + SiLU, the
+ * chunk scan and the gated RMS norm.  The transformers issue page on a
+ * Mamba-2 layer's paths names a training path that runs the split, the conv
+ * and the scan as one fused operation against an inference path of separate
+ * calls; the nnterp guide ("Mamba-2" page) reads y before the gated norm and
+ * the output projection.  The result is, bit for bit, that of
+ *
+ *   ssd_conv1d_silu(xbc, ... apply_silu = 1) -> x, B, C
+ *   ssd_chunk_scan_ex(x, dt, A, B, C, D, dt_bias, ..., seq_idx) -> y
+ *   ssd_gated_norm(y, z, norm_weight, out, b*l, h*p, norm_group, eps, normalize)
+ *
+ * with x, B and C held in the workspace and y written into `out` (the norm
+ * then runs in place).  No pass is skipped except the norm when z is NULL
+ * and normalize is 0 (out = y).
+ *
+ *   xbc, conv_weight, conv_bias, conv_width, conv_init, conv_final
+ *                 as for ssd_conv1d_silu (conv_init/conv_final may be NULL)
+ *   dt, A, D, dt_bias, dt_softplus, dt_min, dt_max, init_state,
+ *   final_state, seq_idx
+ *                 as for ssd_chunk_scan_ex (seq_idx also masks the conv)
+ *   z             [b, l, h*p] io dtype gate or NULL; 16-byte aligned
+ *   norm_weight, norm_group, eps, normalize
+ *                 as for ssd_gated_norm (norm_group > 0 always)
+ *   out           [b, l, h, p] io dtype output; 16-byte aligned; must not
+ *                 overlap any input
+ *   workspace     at least ssd_mixer_workspace_bytes(...) bytes, 256-byte
+ *                 aligned: the scan's workspace, then x, B and C
+ *
+ * Every argument of the three passes is checked before the first launch:
+ * an error return has launched nothing (SSD_ERR_HIP aside, which a launch
+ * reports after the passes before it were queued).
+ */
+int32_t ssd_mixer_forward(const void *xbc, const void *z, const void *dt,
+                          const float *conv_weight, const float *conv_bias, int64_t conv_width,
+                          const float *conv_init, float *conv_final, const float *A,
+                          const float *D, const float *dt_bias, int32_t dt_softplus,
+                          float dt_min, float dt_max, const float *init_state,
+                          float *final_state, const int32_t *seq_idx, const float *norm_weight,
+                          int64_t norm_group, float eps, int32_t normalize, void *out,
+                          int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
+                          int64_t state_dim, int64_t groups, int64_t chunk, int32_t io_dtype,
+                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of workspace ssd_mixer_forward needs (0: invalid or overflowing sizes). */
+size_t ssd_mixer_workspace_bytes(int64_t batch, int64_t seqlen, int64_t heads, int64_t head_dim,
+                                 int64_t state_dim, int64_t groups, int64_t chunk,
+                                 int32_t io_dtype);
 
 /*
  * ssd_chunk_scan_bwd -- gradients of ssd_chunk_scan_ex's y and final state,

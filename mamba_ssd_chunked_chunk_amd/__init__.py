@@ -23,6 +23,7 @@ from . import _lib
 from ._lib import LibraryMissing, load, status_string  # noqa: F401
 
 __all__ = ["chunk_scan", "chunk_scan_noalloc", "chunk_scan_bwd", "step", "conv1d_silu", "gated_norm",
+           "mixer_forward", "mixer_workspace_bytes",
            "segment_log_decay", "combine_segments",
            "workspace_bytes", "state_chunks", "abi_version",
            "LibraryMissing", "SsdError"]
@@ -405,3 +406,77 @@ def gated_norm(y, z=None, weight=None, group_size: Optional[int] = None, eps: fl
     if rc != 0:
         raise SsdError("ssd_gated_norm", rc)
     return o
+
+
+def mixer_workspace_bytes(batch, seqlen, heads, head_dim, state_dim, groups, chunk,
+                          io="bf16") -> int:
+    """Workspace bytes of one mixer_forward call (ssd_mixer_workspace_bytes)."""
+    code = _lib.SSD_BF16 if io == "bf16" else _lib.SSD_F32
+    return int(load().ssd_mixer_workspace_bytes(batch, seqlen, heads, head_dim, state_dim,
+                                                groups, chunk, code))
+
+
+def mixer_forward(xbc, dt, A, conv_weight, heads, head_dim, state_dim, groups, z=None,
+                  conv_bias=None, conv_init=None, D=None, dt_bias=None,
+                  dt_softplus: bool = True, dt_limit: Tuple[float, float] = (0.0, math.inf),
+                  initial_state=None, seq_idx=None, norm_weight=None,
+                  norm_group: Optional[int] = None, eps: float = 1e-5, normalize: bool = True,
+                  chunk_size: int = 256, return_final_state: bool = False,
+                  return_conv_state: bool = False, out=None, workspace=None):
+    """The mixer between its projections in one call (ssd_mixer_forward):
+    conv1d + SiLU + split of xbc [b, l, h*p + 2*g*n], the chunk scan, and
+    the silu(z)-gated RMS norm over groups of norm_group channels (default:
+    all h*p).  Returns out [b, l, h, p], followed by the final state and/or
+    the final conv state [b, width-1, ch] when asked for."""
+    torch = _torch()
+    lib = load()
+    if xbc.dim() != 3:
+        raise ValueError("xbc must be [batch, seqlen, channels]")
+    b, l, ch = xbc.shape
+    dev = xbc.device
+    if dev.type != "cuda":
+        raise ValueError("xbc must be a GPU tensor")
+    io = xbc.dtype
+    code = _io_code(io)
+    h, p, n, g = int(heads), int(head_dim), int(state_dim), int(groups)
+    if ch != h * p + 2 * g * n:
+        raise ValueError("xbc has %d channels, expected heads*head_dim + 2*groups*state_dim = %d"
+                         % (ch, h * p + 2 * g * n))
+    K = int(conv_weight.shape[1]) if conv_weight.dim() == 2 else -1
+    _check("xbc", xbc, io)
+    _check("dt", dt, io, (b, l, h), dev)
+    _check("z", z, io, (b, l, h * p), dev)
+    _check("conv_weight", conv_weight, torch.float32, (ch, K), dev)
+    _check("conv_bias", conv_bias, torch.float32, (ch,), dev)
+    _check("conv_init", conv_init, torch.float32, (b, K - 1, ch), dev)
+    _check("A", A, torch.float32, (h,), dev)
+    _check("D", D, torch.float32, (h,), dev)
+    _check("dt_bias", dt_bias, torch.float32, (h,), dev)
+    _check("initial_state", initial_state, torch.float32, (b, h, n, p), dev)
+    _check("seq_idx", seq_idx, torch.int32, (b, l), dev)
+    _check("norm_weight", norm_weight, torch.float32, (h * p,), dev)
+    y = torch.empty((b, l, h, p), dtype=io, device=dev) if out is None else out
+    _check("out", y, io, (b, l, h, p), dev)
+    fin = torch.empty((b, h, n, p), dtype=torch.float32, device=dev) \
+        if return_final_state else None
+    cfin = torch.empty((b, K - 1, ch), dtype=torch.float32, device=dev) \
+        if return_conv_state else None
+    wsb = int(lib.ssd_mixer_workspace_bytes(b, l, h, p, n, g, int(chunk_size), code))
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _check("workspace", ws, torch.uint8, None, dev)
+    G = h * p if norm_group is None else int(norm_group)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.ssd_mixer_forward(
+        _ptr(xbc), _ptr(z), _ptr(dt), _ptr(conv_weight), _ptr(conv_bias), K, _ptr(conv_init),
+        _ptr(cfin), _ptr(A), _ptr(D), _ptr(dt_bias), int(bool(dt_softplus)),
+        float(dt_limit[0]), float(dt_limit[1]), _ptr(initial_state), _ptr(fin), _ptr(seq_idx),
+        _ptr(norm_weight), G, float(eps), int(bool(normalize)), _ptr(y), b, l, h, p, n, g,
+        int(chunk_size), code, _ptr(ws), ws.numel() * ws.element_size(), stream)
+    if rc != 0:
+        raise SsdError("ssd_mixer_forward", rc)
+    if not return_final_state and not return_conv_state:
+        return y
+    return (y,) + ((fin,) if return_final_state else ()) + \
+        ((cfin,) if return_conv_state else ())

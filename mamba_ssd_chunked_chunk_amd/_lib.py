@@ -26,7 +26,8 @@ EVENT_SLOTS = ("chunk_state", "state_scan", "chunk_out", "token_states")
 # every symbol include/ssd.h declares
 EXPORTS = ("ssd_chunk_scan", "ssd_chunk_scan_ex", "ssd_chunk_scan_noalloc",
            "ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan_state_chunks", "ssd_step",
-           "ssd_conv1d_silu", "ssd_gated_norm", "ssd_chunk_scan_bwd",
+           "ssd_conv1d_silu", "ssd_gated_norm", "ssd_mixer_forward",
+           "ssd_mixer_workspace_bytes", "ssd_chunk_scan_bwd",
            "ssd_segment_log_decay", "ssd_combine_segments",
            "ssd_chunk_scan_bwd_workspace_bytes", "ssd_status_string", "ssd_abi_version")
 
@@ -71,6 +72,12 @@ def load() -> ctypes.CDLL:
                                     I64, I32, I32, P]
     lib.ssd_gated_norm.restype = I32
     lib.ssd_gated_norm.argtypes = [P, P, P, P, I64, I64, I64, F, I32, I32, P]
+    lib.ssd_mixer_forward.restype = I32
+    lib.ssd_mixer_forward.argtypes = [P, P, P, P, P, I64, P, P, P, P, P, I32, F, F, P, P, P, P,
+                                      I64, F, I32, P, I64, I64, I64, I64, I64, I64, I64, I32,
+                                      P, ctypes.c_size_t, P]
+    lib.ssd_mixer_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_mixer_workspace_bytes.argtypes = [I64] * 7 + [I32]
     lib.ssd_chunk_scan_bwd.restype = I32
     lib.ssd_chunk_scan_bwd.argtypes = [P, P, P, P, P, P, P, I32, F, F, P, P, P, P,
                                        P, P, P, P, P, P, P, P,

@@ -78,6 +78,57 @@ static bool mul_ok(int64_t a, int64_t b, int64_t lim) { return a == 0 || b <= li
 
 }  // namespace ssd
 
+namespace ssd {
+
+// Every argument check of ssd_chunk_scan_ex, in its order (SSD_OK: the
+// call launches); the mixer runs it before its first launch.
+int32_t scan_status(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                    const float *D, const float *dt_bias, const float *init_state,
+                    const int32_t *seq_idx, const void *y, const float *final_state,
+                    const float *chunk_states, int64_t batch, int64_t seqlen, int64_t heads,
+                    int64_t head_dim, int64_t state_dim, int64_t groups, int64_t chunk,
+                    int32_t io_dtype, const void *workspace, size_t workspace_bytes) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
+        groups <= 0 || chunk <= 0 || heads % groups != 0)
+        return SSD_ERR_SHAPE;
+    if (!supported_dims(head_dim, state_dim)) return SSD_ERR_UNSUPPORTED;
+    const int64_t lim = (int64_t)1 << 62;
+    if (!mul_ok(batch, seqlen, lim) || !mul_ok(batch * seqlen, heads, lim) ||
+        !mul_ok(batch * seqlen * heads, 128 * 128, lim))
+        return SSD_ERR_UNSUPPORTED;
+    const bool work = batch > 0 && seqlen > 0;
+    if (!A) return SSD_ERR_NULL;
+    if (work && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL;
+    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) ||
+        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256) ||
+        !aligned(seq_idx, 4) || !aligned(chunk_states, 16))
+        return SSD_ERR_ALIGN;
+    if (!work) return SSD_OK;
+    ScanPlan pl;
+    if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io_dtype))
+        return SSD_ERR_SHAPE;
+    // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
+    const int64_t gmax = ((int64_t)1 << 31) - 1;
+    if (pl.b * pl.nc * pl.h * 8 > gmax || pl.b * pl.h * pl.n * pl.p / 4 / 256 + 1 > gmax)
+        return SSD_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
+    // one (batch, head)
+    const int64_t lim32 = ((int64_t)1 << 31);
+    if (64 * heads * head_dim * 4 >= lim32 || 64 * groups * state_dim * 4 >= lim32 ||
+        pl.lp * 4 >= lim32)
+        return SSD_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < ssd_chunk_scan_workspace_bytes(
+                                            batch, seqlen, heads, head_dim, state_dim, groups,
+                                            chunk))
+        return SSD_ERR_WORKSPACE;
+    return SSD_OK;
+}
+
+}  // namespace ssd
+
 using namespace ssd;
 
 extern "C" {
@@ -147,24 +198,12 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
                           int64_t seqlen, int64_t heads, int64_t head_dim, int64_t state_dim,
                           int64_t groups, int64_t chunk, int32_t io_dtype, void *workspace,
                           size_t workspace_bytes, void *hip_stream, void *const *kernel_events) {
-    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
-    if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
-        groups <= 0 || chunk <= 0 || heads % groups != 0)
-        return SSD_ERR_SHAPE;
-    if (!supported_dims(head_dim, state_dim)) return SSD_ERR_UNSUPPORTED;
-    const int64_t lim = (int64_t)1 << 62;
-    if (!mul_ok(batch, seqlen, lim) || !mul_ok(batch * seqlen, heads, lim) ||
-        !mul_ok(batch * seqlen * heads, 128 * 128, lim))
-        return SSD_ERR_UNSUPPORTED;
+    const int32_t st = scan_status(x, dt, A, B, C, D, dt_bias, init_state, seq_idx, y,
+                                   final_state, chunk_states, batch, seqlen, heads, head_dim,
+                                   state_dim, groups, chunk, io_dtype, workspace,
+                                   workspace_bytes);
+    if (st != SSD_OK) return st;
     const bool work = batch > 0 && seqlen > 0;
-    if (!A) return SSD_ERR_NULL;
-    if (work && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL;
-    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
-    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
-        !aligned(dt, es) || !aligned(A, 4) || !aligned(D, 4) || !aligned(dt_bias, 4) ||
-        !aligned(init_state, 16) || !aligned(final_state, 16) || !aligned(workspace, 256) ||
-        !aligned(seq_idx, 4) || !aligned(chunk_states, 16))
-        return SSD_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
     if (!work) {
@@ -178,22 +217,7 @@ int32_t ssd_chunk_scan_ex(const void *x, const void *dt, const float *A, const v
     }
 
     ScanPlan pl;
-    if (!make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io_dtype))
-        return SSD_ERR_SHAPE;
-    // grid limits: one-dimensional grids of at most 2^31 - 1 workgroups
-    const int64_t gmax = ((int64_t)1 << 31) - 1;
-    if (pl.b * pl.nc * pl.h * 8 > gmax || pl.b * pl.h * pl.n * pl.p / 4 / 256 + 1 > gmax)
-        return SSD_ERR_UNSUPPORTED;
-    // 32-bit buffer offsets: 64 rows of x, B, C or y, and the padded rows of
-    // one (batch, head)
-    const int64_t lim32 = ((int64_t)1 << 31);
-    if (64 * heads * head_dim * 4 >= lim32 || 64 * groups * state_dim * 4 >= lim32 ||
-        pl.lp * 4 >= lim32)
-        return SSD_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < ssd_chunk_scan_workspace_bytes(
-                                            batch, seqlen, heads, head_dim, state_dim, groups,
-                                            chunk))
-        return SSD_ERR_WORKSPACE;
+    make_plan(pl, batch, seqlen, heads, head_dim, state_dim, groups, chunk, io_dtype);
 
     ScanArgs a{x, dt, B, C, A, D, dt_bias, dt_softplus ? 1 : 0, dt_min, dt_max,
                init_state, y, final_state, static_cast<char *>(workspace), seq_idx,

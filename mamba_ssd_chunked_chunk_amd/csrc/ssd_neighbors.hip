@@ -231,6 +231,54 @@ __global__ void k_copy_or_zero(float *__restrict__ dst, const float *__restrict_
 
 }  // namespace
 
+// Every argument check of ssd_conv1d_silu, in its order (SSD_OK: the call
+// launches, or has nothing to launch); the mixer runs it before its first
+// launch.
+int32_t conv_status(const void *xbc, const float *weight, const float *bias,
+                    const float *conv_init, const int32_t *seq_idx, const void *x, const void *B,
+                    const void *C, const float *conv_final, int64_t batch, int64_t seqlen,
+                    int64_t heads, int64_t head_dim, int64_t state_dim, int64_t groups,
+                    int64_t width, int32_t io_dtype) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
+        groups <= 0 || width < 1)
+        return SSD_ERR_SHAPE;
+    if (width > 4 || head_dim % 4 != 0 || state_dim % 4 != 0) return SSD_ERR_UNSUPPORTED;
+    const int64_t hp = heads * head_dim, gn = groups * state_dim, ch = hp + 2 * gn;
+    if (ch > ((int64_t)1 << 24) || batch > 65535 || seqlen > ((int64_t)1 << 36))
+        return SSD_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0) {
+        if (conv_final && batch > 0 && width > 1 &&
+            (!aligned16(conv_final) || !aligned16(conv_init)))
+            return SSD_ERR_ALIGN;
+        return SSD_OK;
+    }
+    if (!xbc || !weight || !x || !B || !C) return SSD_ERR_NULL;
+    if (!aligned16(xbc) || !aligned16(x) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(bias) || !aligned16(conv_init) || !aligned16(conv_final) ||
+        ((uintptr_t)weight & 3) || ((uintptr_t)seq_idx & 3))
+        return SSD_ERR_ALIGN;
+    const int64_t runs = (seqlen + kConvRun - 1) / kConvRun;
+    if (runs > 65535) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+// Every argument check of ssd_gated_norm, in its order.
+int32_t norm_status(const void *y, const void *z, const float *weight, const void *out,
+                    int64_t rows, int64_t dim, int64_t group_size, float eps, int32_t io_dtype) {
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (rows < 0 || dim <= 0 || group_size <= 0 || dim % group_size != 0 || !(eps >= 0.f))
+        return SSD_ERR_SHAPE;
+    if (group_size % 4 != 0 || dim > ((int64_t)1 << 30)) return SSD_ERR_UNSUPPORTED;
+    if (rows == 0) return SSD_OK;
+    if (!y || !out) return SSD_ERR_NULL;
+    if (!aligned16(y) || !aligned16(z) || !aligned16(out) || !aligned16(weight))
+        return SSD_ERR_ALIGN;
+    const int64_t blocks = (rows * (dim / group_size) + 3) / 4;
+    if (blocks > ((int64_t)1 << 31) - 1) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
 }  // namespace ssd
 
 using namespace ssd;
@@ -242,19 +290,15 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
                         void *C, float *conv_final, int64_t batch, int64_t seqlen,
                         int64_t heads, int64_t head_dim, int64_t state_dim, int64_t groups,
                         int64_t width, int32_t apply_silu, int32_t io_dtype, void *hip_stream) {
-    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
-    if (batch < 0 || seqlen < 0 || heads <= 0 || head_dim <= 0 || state_dim <= 0 ||
-        groups <= 0 || width < 1)
-        return SSD_ERR_SHAPE;
-    if (width > 4 || head_dim % 4 != 0 || state_dim % 4 != 0) return SSD_ERR_UNSUPPORTED;
+    const int32_t st = conv_status(xbc, weight, bias, conv_init, seq_idx, x, B, C, conv_final,
+                                   batch, seqlen, heads, head_dim, state_dim, groups, width,
+                                   io_dtype);
+    if (st != SSD_OK) return st;
     const int64_t hp = heads * head_dim, gn = groups * state_dim, ch = hp + 2 * gn;
-    if (ch > ((int64_t)1 << 24) || batch > 65535 || seqlen > ((int64_t)1 << 36))
-        return SSD_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     if (batch == 0 || seqlen == 0) {
         // nothing to convolve: the window after the sequence is conv_init
         if (conv_final && batch > 0 && width > 1) {
-            if (!aligned16(conv_final) || !aligned16(conv_init)) return SSD_ERR_ALIGN;
             const int64_t cnt = batch * (width - 1) * ch;
             hipLaunchKernelGGL(k_copy_or_zero, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0,
                                s, conv_final, conv_init, cnt);
@@ -262,13 +306,7 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
         }
         return SSD_OK;
     }
-    if (!xbc || !weight || !x || !B || !C) return SSD_ERR_NULL;
-    if (!aligned16(xbc) || !aligned16(x) || !aligned16(B) || !aligned16(C) ||
-        !aligned16(bias) || !aligned16(conv_init) || !aligned16(conv_final) ||
-        ((uintptr_t)weight & 3) || ((uintptr_t)seq_idx & 3))
-        return SSD_ERR_ALIGN;
     const int64_t runs = (seqlen + kConvRun - 1) / kConvRun;
-    if (runs > 65535) return SSD_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((ch / 4 + kConvThreads - 1) / kConvThreads), (unsigned)runs,
                     (unsigned)batch);
 #define SSD_CONV(IO, KK)                                                                       \
@@ -302,14 +340,9 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
 int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *out,
                        int64_t rows, int64_t dim, int64_t group_size, float eps,
                        int32_t normalize, int32_t io_dtype, void *hip_stream) {
-    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
-    if (rows < 0 || dim <= 0 || group_size <= 0 || dim % group_size != 0 || !(eps >= 0.f))
-        return SSD_ERR_SHAPE;
-    if (group_size % 4 != 0 || dim > ((int64_t)1 << 30)) return SSD_ERR_UNSUPPORTED;
+    const int32_t st = norm_status(y, z, weight, out, rows, dim, group_size, eps, io_dtype);
+    if (st != SSD_OK) return st;
     if (rows == 0) return SSD_OK;
-    if (!y || !out) return SSD_ERR_NULL;
-    if (!aligned16(y) || !aligned16(z) || !aligned16(out) || !aligned16(weight))
-        return SSD_ERR_ALIGN;
     const int64_t waves = rows * (dim / group_size);
     const int64_t blocks = (waves + 3) / 4;
     if (blocks > ((int64_t)1 << 31) - 1) return SSD_ERR_UNSUPPORTED;

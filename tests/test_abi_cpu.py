@@ -236,3 +236,40 @@ def test_noalloc_scratch_size_matches_header_and_rejects_beyond_it(lib):
                                     Q, L.SSD_BF16, None, None)
     assert rc == L.SSD_ERR_SCRATCH
     assert b"SSD_SCRATCH_BYTES" in lib.ssd_status_string(rc)
+
+
+def test_mixer_checks_every_pass_before_launching(lib):
+    """ssd_mixer_forward returns the status of whichever of its three passes
+    rejects an argument, before its first launch (on this machine a launch
+    would report SSD_ERR_HIP instead)."""
+    from mamba_ssd_chunked_chunk_amd import _lib as L
+    b, l, h, p, n, g, Q = 2, 64, 4, 64, 64, 1, 64
+    wsb = lib.ssd_mixer_workspace_bytes(b, l, h, p, n, g, Q, 1)
+    assert wsb > lib.ssd_chunk_scan_workspace_bytes(b, l, h, p, n, g, Q) + b * l * h * p * 2
+    assert lib.ssd_mixer_workspace_bytes(b, l, h, p, n, g, 0, 1) == 0
+    assert lib.ssd_mixer_workspace_bytes(b, l, h, p, n, g, Q, 7) == 0
+
+    def mix(**over):
+        kw = dict(xbc=FAKE, z=None, dt=FAKE, K=4, G=h * p, eps=1e-5, out=FAKE, b=b, l=l, p=p,
+                  io=1, ws=FAKE, wsb=wsb, init=None, seq=None)
+        kw.update(over)
+        return lib.ssd_mixer_forward(kw["xbc"], kw["z"], kw["dt"], FAKE, None, kw["K"], None,
+                                     None, FAKE, None, None, 1, 0.0, math.inf, kw["init"], None,
+                                     kw["seq"], None, kw["G"], kw["eps"], 1, kw["out"], kw["b"],
+                                     kw["l"], h, kw["p"], n, g, Q, kw["io"], kw["ws"], kw["wsb"],
+                                     None)
+    assert mix(wsb=wsb - 1) == L.SSD_ERR_WORKSPACE
+    assert mix(ws=None) == L.SSD_ERR_WORKSPACE
+    assert mix(ws=FAKE + 16) == L.SSD_ERR_ALIGN
+    assert mix(K=5) == L.SSD_ERR_UNSUPPORTED           # the conv's check
+    assert mix(xbc=FAKE + 4) == L.SSD_ERR_ALIGN        # the conv's check
+    assert mix(dt=FAKE + 1) == L.SSD_ERR_ALIGN         # the scan's check
+    assert mix(init=FAKE + 8) == L.SSD_ERR_ALIGN       # the scan's check
+    assert mix(seq=FAKE + 2) == L.SSD_ERR_ALIGN
+    assert mix(G=24) == L.SSD_ERR_SHAPE                # the norm's check
+    assert mix(eps=-1.0) == L.SSD_ERR_SHAPE            # the norm's check
+    assert mix(z=FAKE + 2) == L.SSD_ERR_ALIGN          # the norm's check
+    assert mix(out=None) == L.SSD_ERR_NULL
+    assert mix(io=4) == L.SSD_ERR_UNSUPPORTED
+    assert mix(p=18) == L.SSD_ERR_UNSUPPORTED
+    assert mix(b=0, wsb=lib.ssd_mixer_workspace_bytes(0, l, h, p, n, g, Q, 1)) == L.SSD_OK
