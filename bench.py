@@ -183,10 +183,11 @@ class Events:
         return tot / calls
 
 
-def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4):
-    """W warmup + K timed ssd_chunk_scan calls over cycled input sets; then
-    the same K calls again with kernel events.  Returns the step time and the
-    average duration of every kernel."""
+def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4, prewarm_s=0.0):
+    """`prewarm_s` seconds of untimed calls, then W warmup + K timed
+    ssd_chunk_scan calls over cycled input sets; then the same K calls again
+    with kernel events.  Returns the step time and the average duration of
+    every kernel."""
     b, l, h, p, n, g, Q = w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups, w.chunk
     s = 4 if w.io == "f32" else 2
     per_set = b * l * h * p * s * 2 + 2 * b * l * g * n * s
@@ -201,6 +202,11 @@ def time_scan(torch, ssd, w, dev, steps, warmup, max_sets=4):
         ssd.chunk_scan(S["x"], S["dt"], S["A"], S["B"], S["C"], S["D"], chunk_size=Q,
                        dt_bias=S["bias"], initial_state=S["init"], return_final_state=final,
                        final_out=fin, out=S["y"], workspace=ws, kernel_events=ev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < prewarm_s:
+        for i in range(8):
+            run(i)
+        torch.cuda.synchronize()
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
@@ -384,6 +390,11 @@ def main():
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the gradient-pass measurement")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prewarm-s", type=float, default=0.3,
+                    help="seconds of untimed scan calls on each workload before its W warmup "
+                         "steps: a sudden sustained load drives the GPU's power management "
+                         "through a transient of ~40 steps (grouped_long per-step times 0.62, "
+                         "then up to 0.83, settling at 0.60 ms)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-probe", default="",
                     help="workload: run a few scans of it and a 256 MiB copy (the counters' "
@@ -395,6 +406,8 @@ def main():
                          "'trace WORKLOAD TRACE_DIR COMMAND...' or "
                          "'traffic WORKLOAD FETCH_DIR WRITE_DIR COMMAND...'")
     args = ap.parse_args()
+    global PREWARM_S
+    PREWARM_S = args.prewarm_s
 
     if args.summarize:
         summarize(args.summarize)
@@ -442,7 +455,8 @@ def main():
         w = syn.WORKLOADS[nm]
         if nm == "decode_2p7b":
             w = w.replace(name="decode_2p7b_prefill")
-        results[w.name] = time_scan(torch, ssd, w, dev, args.steps, args.warmup)
+        results[w.name] = time_scan(torch, ssd, w, dev, args.steps, args.warmup,
+                                    prewarm_s=args.prewarm_s)
     head = results[HEADLINE]
     wh = syn.WORKLOADS[HEADLINE]
     dom = max(SLOTS, key=lambda k: head["kernels"][k]["avg_us"])
@@ -471,7 +485,8 @@ def main():
 
     out = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "steps": args.steps, "warmup": args.warmup, "prewarm_s": args.prewarm_s,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) x/B/C/dt, A=-exp(U[0,ln16]), "
                 "dt_bias=softplus^-1(loguniform[1e-3,0.1]), D=1, zero initial state)",
@@ -490,9 +505,23 @@ def main():
 
 
 # --------------------------------------------------------------- extras ----
+# seconds of untimed calls before each measurement's warmup (--prewarm-s)
+PREWARM_S = 0.0
+
+
+def _prewarm(torch, fn):
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PREWARM_S:
+        for i in range(8):
+            fn(i)
+        torch.cuda.synchronize()
+
+
 def _time_calls(torch, fn, calls, warm=3):
     """Average ms of fn(i) over `calls` calls, each bracketed by events on
-    the current stream (one kernel per call)."""
+    the current stream (one kernel per call), after PREWARM_S seconds and
+    `warm` calls of untimed calls."""
+    _prewarm(torch, fn)
     for i in range(warm):
         fn(i)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -723,6 +752,8 @@ def bench_decode(args, torch, ssd, syn, dev):
         return torch.randn(*shape, generator=gen, device=dev).bfloat16()
     xs, dts, Bs, Cs = rnd(K, b, h, p), rnd(K, b, h), rnd(K, b, g, n), rnd(K, b, g, n)
     y = torch.empty((b, h, p), dtype=torch.bfloat16, device=dev)
+    _prewarm(torch, lambda k: ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias,
+                                       out=y))
     for k in range(3):
         ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
     torch.cuda.synchronize()

@@ -15,6 +15,8 @@
 // accesses, a wave covering 256 consecutive channels of one token).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "../../include/ssd.h"
 #include "ssd_device.hpp"
 #include "ssd_plan.hpp"
@@ -32,14 +34,19 @@ __device__ __forceinline__ float silu_f(float v) {
 }
 
 // ----------------------------------------------------------------- conv1d --
-// One thread: 4 consecutive channels over kConvRun consecutive tokens.  All
-// the run's rows and the width - 1 rows before it are requested before any
-// arithmetic (bf16 rows stay packed in registers until used), then the
-// outputs are formed and stored.  With a document index, a tap whose source
-// token lies in another document than the output token reads zero; rows
-// before token 0 come from conv_init and belong to token 0's document.
-constexpr int kConvRun = 8;
+// One thread: V consecutive channels (16 bytes of io: 8 bf16 or 4 fp32, or
+// 4 bf16 where the x, B, C widths are not multiples of 8) over kConvRun
+// consecutive tokens.  Threads of a wave take consecutive channel groups of
+// one run, so every row load and store of a wave is one contiguous 1 KiB.
+// All the run's rows and the width - 1 rows before it are requested before
+// any arithmetic (bf16 rows stay packed in registers until used), then the
+// outputs are formed and stored.  With a document index, a tap whose
+// source token lies in another document than the output token reads zero;
+// rows before token 0 come from conv_init and belong to token 0's document.
 constexpr int kConvThreads = 256;
+// tokens per thread: 16, or 8 for 8-channel threads (their 16-token runs
+// need 184 registers, two waves per SIMD)
+template <int V> constexpr int conv_run() { return V == 8 ? 8 : 16; }
 
 // 4 io elements as loaded (bf16 stays packed in registers until used)
 template <typename IO> struct Raw4;
@@ -49,40 +56,52 @@ __device__ __forceinline__ f32x4 widen4(const f32x4 &v) { return v; }
 __device__ __forceinline__ f32x4 widen4(const bf16x4 &v) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
+__device__ __forceinline__ void narrow4(f32x4 &o, const f32x4 &v) { o = v; }
+__device__ __forceinline__ void narrow4(bf16x4 &o, const f32x4 &v) {
+    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+}
+// V io elements of one row, moved as one access
+template <typename IO, int V> struct alignas(V * sizeof(IO)) RowV {
+    typename Raw4<IO>::type q[V / 4];
+};
 
-template <typename IO, int K, bool SEQ>
+template <typename IO, int K, bool SEQ, int V>
 __global__ __launch_bounds__(kConvThreads) void k_conv1d_silu(
     const IO *__restrict__ xbc, const float *__restrict__ w, const float *__restrict__ bias,
     const float *__restrict__ init, const int32_t *__restrict__ seq, IO *__restrict__ xo,
     IO *__restrict__ Bo, IO *__restrict__ Co, float *__restrict__ fin, int64_t l, int ch, int hp,
     int gn, int apply_silu) {
-    typedef typename Raw4<IO>::type R4;
-    const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * 4;
-    if (c0 >= ch) return;
-    const int64_t b = blockIdx.z;
-    const int64_t t0 = (int64_t)blockIdx.y * kConvRun;
+    typedef RowV<IO, V> R;
+    constexpr int NQ = V / 4, kConvRun = conv_run<V>();
+    const int ncg = ch / V;
+    const int64_t idx = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
+    const int64_t run = idx / ncg;
+    const int c0 = (int)(idx - run * ncg) * V;
+    const int64_t t0 = run * kConvRun;
+    if (t0 >= l) return;
+    const int64_t b = blockIdx.y;
     const IO *src = xbc + b * l * ch + c0;
     const int32_t *sq = SEQ ? seq + b * l : nullptr;
 
     // the run's tokens t0 .. t0 + kConvRun - 1 (raw), then the K - 1 before
-    // them (fp32: they may come from conv_init), all requested before use
+    // them, all requested before any of them is used: every load reads a
+    // clamped, valid row (rows past the end feed no stored output, rows
+    // before token 0 are replaced below), so no branch merges a loaded value
+    // and the loads stay in flight together
     constexpr int H = K - 1;
-    R4 row[kConvRun];
+    R row[kConvRun];
 #pragma unroll
     for (int i = 0; i < kConvRun; ++i) {
         const int64_t t = t0 + i;
-        if (t < l) row[i] = *reinterpret_cast<const R4 *>(src + t * ch);
-        else row[i] = R4{};
+        row[i] = *reinterpret_cast<const R *>(src + (t < l ? t : l - 1) * ch);
     }
-    f32x4 halo[H > 0 ? H : 1];
+    f32x4 halo[H > 0 ? H : 1][NQ];
 #pragma unroll
     for (int j = 0; j < H; ++j) {
         const int64_t s = t0 - H + j;
-        if (s >= 0)
-            halo[j] = widen4(*reinterpret_cast<const R4 *>(src + s * ch));
-        else
-            halo[j] = init ? *reinterpret_cast<const f32x4 *>(init + (b * H + H + s) * ch + c0)
-                           : zero4();
+        const R r = *reinterpret_cast<const R *>(src + (s < 0 ? 0 : s) * ch);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) halo[j][q] = widen4(r.q[q]);
     }
     int doc[SEQ ? kConvRun + H : 1];
     if constexpr (SEQ) {
@@ -92,14 +111,32 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_silu(
             doc[j] = sq[s < 0 ? 0 : (s < l ? s : l - 1)];
         }
     }
-    f32x4 wk[K];
+    f32x4 wk[K][NQ];
 #pragma unroll
     for (int k = 0; k < K; ++k)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wk[k][e] = w[(int64_t)(c0 + e) * K + k];
-    const f32x4 bv = bias ? *reinterpret_cast<const f32x4 *>(bias + c0) : zero4();
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wk[k][q][e] = w[(int64_t)(c0 + 4 * q + e) * K + k];
+    f32x4 bv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        bv[q] = bias ? *reinterpret_cast<const f32x4 *>(bias + c0 + 4 * q) : zero4();
+    // the first run: the rows before token 0 come from conv_init (or zero)
+    if (t0 < H) {
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            const int64_t s = t0 - H + j;
+            if (s < 0)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    halo[j][q] = init ? *reinterpret_cast<const f32x4 *>(
+                                            init + (b * H + H + s) * ch + c0 + 4 * q)
+                                      : zero4();
+        }
+    }
 
-    // destination: x, B or C (channel groups of 4 never straddle them)
+    // destination: x, B or C (channel groups of V never straddle them)
     IO *dst;
     int64_t ds;
     if (c0 < hp) {
@@ -112,20 +149,25 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_silu(
         dst = Co + b * l * gn + (c0 - hp - gn);
         ds = gn;
     }
-    // input j of the window (0 .. kConvRun + H - 1): halo, then the run
-    auto in = [&](int j) { return j < H ? halo[j] : widen4(row[j - H]); };
+    // part q of input j of the window (0 .. kConvRun + H - 1): halo, then the run
+    auto in = [&](int j, int q) { return j < H ? halo[j][q] : widen4(row[j - H].q[q]); };
 #pragma unroll
     for (int i = 0; i < kConvRun; ++i) {
         const int64_t t = t0 + i;
         if (t < l) {
-            f32x4 acc = bv + wk[K - 1] * in(i + H);
+            R o;
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k)
-                if (!SEQ || doc[i + k] == doc[i + H]) acc += wk[k] * in(i + k);
-            if (apply_silu)
+            for (int q = 0; q < NQ; ++q) {
+                f32x4 acc = bv[q] + wk[K - 1][q] * in(i + H, q);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = silu_f(acc[e]);
-            st4(dst + t * ds, acc);
+                for (int k = 0; k < K - 1; ++k)
+                    if (!SEQ || doc[i + k] == doc[i + H]) acc += wk[k][q] * in(i + k, q);
+                if (apply_silu)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = silu_f(acc[e]);
+                narrow4(o.q[q], acc);
+            }
+            *reinterpret_cast<R *>(dst + t * ds) = o;
         }
     }
     // the last width - 1 inputs (rows of earlier documents zero), written by
@@ -134,25 +176,30 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_silu(
         const int jl = (int)(l - 1 - t0) + H;  // window index of token l - 1
 #pragma unroll
         for (int j = 0; j < H; ++j) {
-            const int q = jl - H + 1 + j;  // window index of token l - H + j
-            f32x4 v = zero4();
+            const int qi = jl - H + 1 + j;  // window index of token l - H + j
 #pragma unroll
-            for (int r = 0; r < kConvRun + H; ++r)
-                if (r == q && (!SEQ || doc[r] == doc[jl])) v = in(r);
-            *reinterpret_cast<f32x4 *>(fin + (b * H + j) * ch + c0) = v;
+            for (int q = 0; q < NQ; ++q) {
+                f32x4 v = zero4();
+#pragma unroll
+                for (int r = 0; r < kConvRun + H; ++r)
+                    if (r == qi && (!SEQ || doc[r] == doc[jl])) v = in(r, q);
+                *reinterpret_cast<f32x4 *>(fin + (b * H + j) * ch + c0 + 4 * q) = v;
+            }
         }
     }
 }
 
 // ------------------------------------------------------------- gated norm --
-// One wave per (row, channel group).  Groups of up to 256 * kNormVec
-// channels are held in registers: every lane requests its y and z vectors at
-// once, the sum of squares of v = y * silu(z) is reduced across the wave,
-// and v / sqrt(mean(v^2) + eps) * weight is written.  Larger groups take
-// two passes over memory (the second from the cache).  y and out may be the
-// same buffer: each lane writes only elements it has already read.
-constexpr int kNormVec = 8;
-
+// One wave per (row, channel group); 4 consecutive channels per lane, a
+// wave covering 256 channels per step.  Groups of up to 256 * NV channels
+// (NV <= 8) are held in registers: every lane requests all its y, z and
+// weight vectors at once (clamped, valid addresses; lanes past the group's
+// end are masked after the loads, so no branch merges a loaded value and
+// the loads stay in flight together), the sum of squares of
+// v = y * silu(z) is reduced across the wave, and v / sqrt(mean(v^2) + eps)
+// * weight is written.  Larger groups take two passes over memory (the
+// second from the cache).  y and out may be the same buffer: each lane
+// writes only elements its wave has already read.
 template <typename IO>
 __device__ __forceinline__ f32x4 gated4(const IO *y, const IO *z, int64_t at) {
     f32x4 v = ld4(y + at);
@@ -170,6 +217,55 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// GATE: z given; NORM: normalize; WT: a weight (with NORM)
+template <typename IO, bool GATE, bool NORM, bool WT, int NV>
+__global__ __launch_bounds__(256) void k_gated_norm_reg(const IO *y, const IO *__restrict__ z,
+                                                        const float *__restrict__ w, IO *out,
+                                                        int64_t rows, int dim, int G,
+                                                        float eps) {
+    typedef typename Raw4<IO>::type R4;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int ng = dim / G;
+    const int64_t r = item / ng;
+    if (r >= rows) return;
+    const int c0 = (int)(item % ng) * G;
+    const int64_t base = r * dim + c0;
+    R4 ry[NV], rz[GATE ? NV : 1];
+    f32x4 wv[WT ? NV : 1];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int i = lane * 4 + 256 * k;
+        const int ii = i < G ? i : 0;
+        ry[k] = *reinterpret_cast<const R4 *>(y + base + ii);
+        if constexpr (GATE) rz[k] = *reinterpret_cast<const R4 *>(z + base + ii);
+        if constexpr (WT) wv[k] = *reinterpret_cast<const f32x4 *>(w + c0 + ii);
+    }
+    // keep every load above this point (the scheduler would otherwise sink
+    // the weight loads to their use after the reduction, each then waited
+    // for on its own)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 v[NV];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        v[k] = widen4(ry[k]);
+        if constexpr (GATE) {
+            const f32x4 zv = widen4(rz[k]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[k][e] *= silu_f(zv[e]);
+        }
+        if (lane * 4 + 256 * k >= G) v[k] = zero4();
+        ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+    }
+    const float scale = NORM ? 1.f / sqrtf(wave_sum(ss) / (float)G + eps) : 1.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int i = lane * 4 + 256 * k;
+        if (i < G) st4(out + base + i, WT ? v[k] * scale * wv[k] : v[k] * scale);
+    }
+}
+
 template <typename IO>
 __global__ __launch_bounds__(256) void k_gated_norm(const IO *y, const IO *__restrict__ z,
                                                     const float *__restrict__ w, IO *out,
@@ -182,29 +278,6 @@ __global__ __launch_bounds__(256) void k_gated_norm(const IO *y, const IO *__res
     if (r >= rows) return;
     const int c0 = (int)(item % ng) * G;
     const int64_t base = r * dim + c0;
-    if (G <= 256 * kNormVec) {
-        f32x4 v[kNormVec];
-        float ss = 0.f;
-#pragma unroll
-        for (int k = 0; k < kNormVec; ++k) {
-            const int i = lane * 4 + 256 * k;
-            v[k] = i < G ? gated4(y, z, base + i) : zero4();
-        }
-#pragma unroll
-        for (int k = 0; k < kNormVec; ++k)
-            ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
-        const float scale = normalize ? 1.f / sqrtf(wave_sum(ss) / (float)G + eps) : 1.f;
-#pragma unroll
-        for (int k = 0; k < kNormVec; ++k) {
-            const int i = lane * 4 + 256 * k;
-            if (i < G) {
-                f32x4 o = v[k] * scale;
-                if (normalize && w) o *= *reinterpret_cast<const f32x4 *>(w + c0 + i);
-                st4(out + base + i, o);
-            }
-        }
-        return;
-    }
     float scale = 1.f;
     if (normalize) {
         float ss = 0.f;
@@ -219,6 +292,44 @@ __global__ __launch_bounds__(256) void k_gated_norm(const IO *y, const IO *__res
         if (normalize && w) o *= *reinterpret_cast<const f32x4 *>(w + c0 + i);
         st4(out + base + i, o);
     }
+}
+
+// Launches the norm: the register-resident kernel for groups of up to 2048
+// channels (NV = 1, 2, 4, 6 or 8 steps of 256), else the two-pass one.
+template <typename IO>
+hipError_t launch_gated_norm(const IO *y, const IO *z, const float *w, IO *out, int64_t rows,
+                             int dim, int G, float eps, bool normalize, dim3 grid,
+                             hipStream_t s) {
+    const int steps = (G + 255) / 256;
+    const bool gate = z != nullptr, wt = normalize && w != nullptr;
+    auto go = [&](auto nv_c, auto gate_c, auto norm_c, auto wt_c) {
+        constexpr int NV = decltype(nv_c)::value;
+        hipLaunchKernelGGL((k_gated_norm_reg<IO, decltype(gate_c)::value,
+                                             decltype(norm_c)::value, decltype(wt_c)::value, NV>),
+                           grid, dim3(256), 0, s, y, z, w, out, rows, dim, G, eps);
+    };
+    auto pick = [&](auto nv_c) {
+        typedef std::true_type T;
+        typedef std::false_type F;
+        if (gate) {
+            if (!normalize) go(nv_c, T{}, F{}, F{});
+            else if (wt) go(nv_c, T{}, T{}, T{});
+            else go(nv_c, T{}, T{}, F{});
+        } else {
+            if (!normalize) go(nv_c, F{}, F{}, F{});
+            else if (wt) go(nv_c, F{}, T{}, T{});
+            else go(nv_c, F{}, T{}, F{});
+        }
+    };
+    if (steps <= 1) pick(std::integral_constant<int, 1>{});
+    else if (steps <= 2) pick(std::integral_constant<int, 2>{});
+    else if (steps <= 4) pick(std::integral_constant<int, 4>{});
+    else if (steps <= 6) pick(std::integral_constant<int, 6>{});
+    else if (steps <= 8) pick(std::integral_constant<int, 8>{});
+    else
+        hipLaunchKernelGGL((k_gated_norm<IO>), grid, dim3(256), 0, s, y, z, w, out, rows, dim, G,
+                           eps, normalize ? 1 : 0);
+    return hipGetLastError();
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
@@ -258,8 +369,7 @@ int32_t conv_status(const void *xbc, const float *weight, const float *bias,
         !aligned16(bias) || !aligned16(conv_init) || !aligned16(conv_final) ||
         ((uintptr_t)weight & 3) || ((uintptr_t)seq_idx & 3))
         return SSD_ERR_ALIGN;
-    const int64_t runs = (seqlen + kConvRun - 1) / kConvRun;
-    if (runs > 65535) return SSD_ERR_UNSUPPORTED;
+    if (seqlen > ((int64_t)1 << 19)) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 
@@ -306,31 +416,40 @@ int32_t ssd_conv1d_silu(const void *xbc, const float *weight, const float *bias,
         }
         return SSD_OK;
     }
-    const int64_t runs = (seqlen + kConvRun - 1) / kConvRun;
-    const dim3 grid((unsigned)((ch / 4 + kConvThreads - 1) / kConvThreads), (unsigned)runs,
+    // 16-byte rows per thread: 8 bf16 channels where x, B and C split at
+    // multiples of 8, else 4
+    const bool v8 = io_dtype == SSD_BF16 && hp % 8 == 0 && gn % 8 == 0;
+    const int V = v8 ? 8 : 4;
+    const int64_t run = v8 ? conv_run<8>() : conv_run<4>();
+    const int64_t runs = (seqlen + run - 1) / run;
+    const dim3 grid((unsigned)((ch / V * runs + kConvThreads - 1) / kConvThreads),
                     (unsigned)batch);
-#define SSD_CONV(IO, KK)                                                                       \
+#define SSD_CONV(IO, KK, VV)                                                                   \
     if (seq_idx)                                                                               \
-        hipLaunchKernelGGL((k_conv1d_silu<IO, KK, true>), grid, dim3(kConvThreads), 0, s,      \
+        hipLaunchKernelGGL((k_conv1d_silu<IO, KK, true, VV>), grid, dim3(kConvThreads), 0, s,  \
                            static_cast<const IO *>(xbc), weight, bias, conv_init, seq_idx,     \
                            static_cast<IO *>(x), static_cast<IO *>(B), static_cast<IO *>(C),   \
                            conv_final, seqlen, (int)ch, (int)hp, (int)gn, apply_silu ? 1 : 0); \
     else                                                                                       \
-        hipLaunchKernelGGL((k_conv1d_silu<IO, KK, false>), grid, dim3(kConvThreads), 0, s,     \
+        hipLaunchKernelGGL((k_conv1d_silu<IO, KK, false, VV>), grid, dim3(kConvThreads), 0, s, \
                            static_cast<const IO *>(xbc), weight, bias, conv_init, nullptr,     \
                            static_cast<IO *>(x), static_cast<IO *>(B), static_cast<IO *>(C),   \
                            conv_final, seqlen, (int)ch, (int)hp, (int)gn, apply_silu ? 1 : 0)
-#define SSD_CONV_W(IO)                                                                         \
+#define SSD_CONV_W(IO, VV)                                                                     \
     switch (width) {                                                                           \
-    case 1: SSD_CONV(IO, 1); break;                                                            \
-    case 2: SSD_CONV(IO, 2); break;                                                            \
-    case 3: SSD_CONV(IO, 3); break;                                                            \
-    default: SSD_CONV(IO, 4); break;                                                           \
+    case 1: SSD_CONV(IO, 1, VV); break;                                                        \
+    case 2: SSD_CONV(IO, 2, VV); break;                                                        \
+    case 3: SSD_CONV(IO, 3, VV); break;                                                        \
+    default: SSD_CONV(IO, 4, VV); break;                                                       \
     }
     if (io_dtype == SSD_BF16) {
-        SSD_CONV_W(bf16)
+        if (v8) {
+            SSD_CONV_W(bf16, 8)
+        } else {
+            SSD_CONV_W(bf16, 4)
+        }
     } else {
-        SSD_CONV_W(float)
+        SSD_CONV_W(float, 4)
     }
 #undef SSD_CONV_W
 #undef SSD_CONV
@@ -347,17 +466,17 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
     const int64_t blocks = (waves + 3) / 4;
     if (blocks > ((int64_t)1 << 31) - 1) return SSD_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    if (io_dtype == SSD_BF16)
-        hipLaunchKernelGGL((k_gated_norm<bf16>), dim3((unsigned)blocks), dim3(256), 0, s,
-                           static_cast<const bf16 *>(y), static_cast<const bf16 *>(z), weight,
-                           static_cast<bf16 *>(out), rows, (int)dim, (int)group_size, eps,
-                           normalize ? 1 : 0);
-    else
-        hipLaunchKernelGGL((k_gated_norm<float>), dim3((unsigned)blocks), dim3(256), 0, s,
-                           static_cast<const float *>(y), static_cast<const float *>(z), weight,
-                           static_cast<float *>(out), rows, (int)dim, (int)group_size, eps,
-                           normalize ? 1 : 0);
-    return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    const dim3 grid((unsigned)blocks);
+    const hipError_t e =
+        io_dtype == SSD_BF16
+            ? launch_gated_norm<bf16>(static_cast<const bf16 *>(y), static_cast<const bf16 *>(z),
+                                      weight, static_cast<bf16 *>(out), rows, (int)dim,
+                                      (int)group_size, eps, normalize != 0, grid, s)
+            : launch_gated_norm<float>(static_cast<const float *>(y),
+                                       static_cast<const float *>(z), weight,
+                                       static_cast<float *>(out), rows, (int)dim,
+                                       (int)group_size, eps, normalize != 0, grid, s);
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
 }  // extern "C"

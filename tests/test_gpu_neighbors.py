@@ -53,6 +53,8 @@ CONV = [
     (1, 2, 2, 16, 32, 2, 4),       # fewer tokens than the window
     (2, 100, 3, 128, 64, 1, 2),
     (1, 64, 2, 16, 32, 1, 1),      # no history
+    (2, 45, 3, 12, 36, 1, 4),      # bf16 x, B widths not multiples of 8: 4-channel threads
+    (1, 300, 2, 64, 64, 1, 4),     # many runs, the last one ragged
 ]
 
 
@@ -126,7 +128,12 @@ def _norm(case, z=True, weight=True, normalize=True, G=None, inplace=False):
 
 
 # (rows, dim, group_size)
-NORM = [(7, 1536, 1536), (5, 64, 16), (3, 4096, 512), (2, 8, 4), (33, 1536, 192)]
+NORM = [(7, 1536, 1536), (5, 64, 16), (3, 4096, 512), (2, 8, 4), (33, 1536, 192),
+        (3, 3072, 1024),   # 4 steps of 256 channels in registers
+        (2, 2048, 2048),   # 8 steps
+        (4, 1400, 700),    # 3 steps, held as 4 with the last masked
+        (3, 5008, 1252),   # 5 steps, held as 6
+        (2, 6144, 3072)]   # beyond registers: two passes
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -144,6 +151,8 @@ def test_norm_parity(case, io):
 def test_norm_in_place(io):
     c = syn.norm_case(4600, 9, 512, io=io)
     _norm(c, G=128, inplace=True)
+    c = syn.norm_case(4601, 5, 1400, io=io)
+    _norm(c, G=700, inplace=True)
 
 
 def test_norm_bench_shape():
