@@ -45,6 +45,8 @@ _CSRC = "mamba_ssd_chunked_chunk_amd/csrc/"
 KERNEL_SOURCES = {
     "scan": tuple(_CSRC + f for f in ("ssd_scan16.hpp", "ssd_device.hpp", "ssd_plan.hpp")),
     "k_step": tuple(_CSRC + f for f in ("ssd_step.hpp", "ssd_device.hpp", "ssd_plan.hpp")),
+    "neighbors": tuple(_CSRC + f for f in ("ssd_neighbors.hip", "ssd_mixer.hip",
+                                           "ssd_device.hpp")),
 }
 
 
@@ -58,7 +60,7 @@ def source_digest(kernel: str = "scan") -> str:
     counter summaries."""
     import re
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES["k_step" if kernel == "k_step" else "scan"]:
+    for rel in KERNEL_SOURCES[kernel if kernel in KERNEL_SOURCES else "scan"]:
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -370,6 +372,39 @@ def summarize(a):
                 f.write("source_digest: %s\n" % source_digest(k))
             print("wrote", path)
         return
+    if kind == "mixer":
+        # every kernel of a --mixer-probe run: the conv, the scan's three
+        # kernels and the norm, as one ssd_mixer_forward call launches them
+        rows = _csv_rows(_find(a[2], "kernel_trace.csv"))
+        cmd = " ".join(a[3:])
+        names = ("k_conv1d_silu", "k_state16", "k_scan16", "k_out16", "k_gated_norm")
+        per = {}
+        for r in rows:
+            nm = r.get("Kernel_Name", "")
+            k = next((x for x in names if x in nm), None)
+            if k:
+                per.setdefault(k, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        path = os.path.join(PROFILES, "mixer_%s_kernel_trace.txt" % wl)
+        with open(path, "w") as f:
+            f.write("# rocprofv3 kernel trace of ssd_mixer_forward (conv1d + SiLU, chunk scan, "
+                    "gated norm) at the %s mixer shape\n" % wl)
+            f.write("# command (from /tmp with TMPDIR=/tmp, repository at $R):\n#   %s\n" % cmd)
+            f.write("# every dispatch of the probe's calls (warm-up and timed)\n\n")
+            f.write("%-14s %6s %10s %10s %10s %10s\n" % ("kernel", "calls", "avg_us", "med_us",
+                                                        "min_us", "max_us"))
+            tot = 0.0
+            for k in names:
+                v = sorted(per.get(k, []))
+                if v:
+                    tot += sum(v) / len(v)
+                    f.write("%-14s %6d %10.2f %10.2f %10.2f %10.2f\n" % (
+                        k, len(v), sum(v) / len(v), v[len(v) // 2], v[0], v[-1]))
+            f.write("\nsum of kernel averages: %.2f us\n" % tot)
+            f.write("neighbors_source_digest: %s\n" % source_digest("neighbors"))
+            f.write("source_digest: %s\n" % source_digest())
+        print("wrote", path)
+        return
     raise SystemExit("unknown summary kind %r" % kind)
 
 
@@ -399,6 +434,9 @@ def main():
     ap.add_argument("--traffic-probe", default="",
                     help="workload: run a few scans of it and a 256 MiB copy (the counters' "
                          "calibration), for profiler runs, and exit")
+    ap.add_argument("--mixer-probe", action="store_true",
+                    help="run the 130m-shape mixer (ssd_mixer_forward) 2 x --probe-steps "
+                         "times after its warm-up, for profiler runs, and exit")
     ap.add_argument("--probe-steps", type=int, default=3,
                     help="timed scans of the probe (each run twice: plain and with events)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG", default=None,
@@ -425,6 +463,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+
+    if args.mixer_probe:
+        r = bench_mixer(argparse.Namespace(steps=2 * args.probe_steps), torch, ssd, syn, dev,
+                        only_one_call=True)
+        print(json.dumps({"mixer_probe": r}))
+        return
 
     if args.traffic_probe:
         w = syn.WORKLOADS[args.traffic_probe]
@@ -636,7 +680,7 @@ def bench_neighbors(args, torch, ssd, syn, dev):
     return res
 
 
-def bench_mixer(args, torch, ssd, syn, dev, sets=4):
+def bench_mixer(args, torch, ssd, syn, dev, sets=4, only_one_call=False):
     """The whole mixer between the projections at the 130m shape (8 x 2048
     tokens, bf16, conv width 4 over 1792 channels, one RMS norm over 1536):
     one ssd_mixer_forward call against the three entry points called in a
@@ -684,7 +728,8 @@ def bench_mixer(args, torch, ssd, syn, dev, sets=4):
                        out=out.reshape(b * l, h * p))
     steps = max(args.steps // 2, 10)
     res = {}
-    for name, fn in (("one_call", one), ("separate_calls", chain)):
+    for name, fn in (("one_call", one),) + (() if only_one_call else
+                                             (("separate_calls", chain),)):
         wall, ev = _time_calls(torch, fn, steps)
         res[name] = {"ms_per_call": round(ev, 4), "wall_ms_per_call": round(wall, 4),
                      "value": round(b * l / (ev * 1e-3), 1), "unit": "tokens/s"}
@@ -697,7 +742,8 @@ def bench_mixer(args, torch, ssd, syn, dev, sets=4):
     ms = res["one_call"]["ms_per_call"]
     res["alg_bytes"] = alg
     res["frac_of_hbm_roof"] = round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-    res["one_call_over_separate"] = round(ms / res["separate_calls"]["ms_per_call"], 4)
+    if not only_one_call:
+        res["one_call_over_separate"] = round(ms / res["separate_calls"]["ms_per_call"], 4)
     res["input_sets"] = sets
     return res
 
