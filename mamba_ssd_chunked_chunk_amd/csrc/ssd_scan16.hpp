@@ -357,6 +357,13 @@ __device__ __forceinline__ float softplus_fast(float z) {
     return 0.69314718055994531f * __builtin_amdgcn_logf(1.f + t);
 }
 
+// v moved across lanes by the DPP control CTRL in the rows of ROWMASK;
+// lanes whose source is outside the row, and rows outside the mask, get 0.
+template <int CTRL, int ROWMASK> __device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROWMASK, 0xf, false));
+}
+
 // The block's per-row values for one head from its raw rows, written to R
 // (lanes 0..31), for a state entering the block with deferred decay D.
 template <bool SEQ>
@@ -378,14 +385,19 @@ __device__ __forceinline__ void rows_prep(Rows &R, const RowIn &f, float a2, flo
         d = k * T + r < rows ? 1.f : 0.f;
         if (first && k == 0 && r == 0) a = 0.f;
     }
-    // inclusive prefix sum over the block's 32 rows (each 32-lane half)
-#pragma unroll
-    for (int off = 1; off < T; off <<= 1) {
-        const float v = __shfl_up(a, off, T);
-        if (r >= off) a += v;
-    }
-    const float last = __shfl(a, T - 1, T);
-    const float l15 = __shfl(a, 15, T);
+    // inclusive prefix sum over the block's 32 rows (each 32-lane half holds
+    // the same rows): shifts by 1, 2, 4 and 8 lanes inside each 16-lane row
+    // (sources outside the row add zero), then rows 1 and 3 add the last
+    // lane of the row before them; all cross-lane moves are DPP, no LDS
+    a += dpp_f<0x111, 0xf>(a);  // row_shr:1
+    a += dpp_f<0x112, 0xf>(a);  // row_shr:2
+    a += dpp_f<0x114, 0xf>(a);  // row_shr:4
+    a += dpp_f<0x118, 0xf>(a);  // row_shr:8
+    a += dpp_f<0x142, 0xa>(a);  // row_bcast:15 into rows 1 and 3
+    const float last = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), T - 1));
+    const float l15 = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), 15));
     float lam = last;
     int seg = -1;
     bool lazy = D - last <= kDefer;
