@@ -296,6 +296,12 @@ def _short(name):
     return None
 
 
+def syn_workload(name):
+    sys.path.insert(0, ROOT)
+    import ssd_synth as syn
+    return syn.WORKLOADS[name]
+
+
 def summarize(a):
     """profiles/ summaries from rocprofv3 csv output (see --summarize)."""
     kind, wl = a[0], a[1]
@@ -371,6 +377,42 @@ def summarize(a):
                 f.write("hbm_bytes_per_launch: %d\n" % int(hbm))
                 f.write("source_digest: %s\n" % source_digest(k))
             print("wrote", path)
+        return
+    if kind == "sq":
+        # SQ counters of the scan kernels: per-dispatch means of every
+        # counter in the comma-separated counter-run directories; the
+        # commands that made them separated by ' ;; '
+        dirs = a[2].split(",")
+        cmds = " ".join(a[3:]).split(" ;; ")
+        vals = {}
+        for d in dirs:
+            for r in _csv_rows(_find(d, "counter_collection.csv")):
+                k = _short(r.get("Kernel_Name", ""))
+                if k in ("k_state16", "k_scan16", "k_out16"):
+                    vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+        path = os.path.join(PROFILES, "scan_kernels_%s_sq_counters.txt" % wl)
+        w = syn_workload(wl)
+        with open(path, "w") as f:
+            f.write("# SQ counters of the bf16 scan kernels on the %s workload (batch %d, seqlen "
+                    "%d,\n# %d heads, head_dim %d, state_dim %d, %d groups, chunk %d), "
+                    "per-dispatch means over the\n# probe's dispatches; %d counter runs (from "
+                    "/tmp with TMPDIR=/tmp, repository at $R):\n"
+                    % (wl, w.batch, w.seqlen, w.heads, w.head_dim, w.state_dim, w.groups,
+                       w.chunk, len(cmds)))
+            for c in cmds:
+                f.write("#   %s\n" % c.strip())
+            f.write("\n")
+            for k in ("k_state16", "k_scan16", "k_out16"):
+                if k not in vals:
+                    continue
+                f.write("%s\n" % k)
+                for ctr in sorted(vals[k]):
+                    v = vals[k][ctr]
+                    f.write("  %-30s %18.1f\n" % (ctr, sum(v) / len(v)))
+                f.write("\n")
+            f.write("source_digest: %s\n" % source_digest())
+        print("wrote", path)
         return
     if kind == "mixer":
         # every kernel of a --mixer-probe run: the conv, the scan's three
@@ -471,6 +513,8 @@ def main():
         return
 
     if args.traffic_probe:
+        # a fixed number of dispatches for the profilers: no time-based pre-warm
+        PREWARM_S = 0.0
         w = syn.WORKLOADS[args.traffic_probe]
         if w.name == "decode_2p7b":
             w = w.replace(name="decode_2p7b_prefill")
@@ -798,8 +842,8 @@ def bench_decode(args, torch, ssd, syn, dev):
         return torch.randn(*shape, generator=gen, device=dev).bfloat16()
     xs, dts, Bs, Cs = rnd(K, b, h, p), rnd(K, b, h), rnd(K, b, g, n), rnd(K, b, g, n)
     y = torch.empty((b, h, p), dtype=torch.bfloat16, device=dev)
-    _prewarm(torch, lambda k: ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias,
-                                       out=y))
+    _prewarm(torch, lambda k: ssd.step(st, xs[k % K], dts[k % K], A, Bs[k % K], Cs[k % K], D,
+                                       dt_bias=bias, out=y))
     for k in range(3):
         ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
     torch.cuda.synchronize()
@@ -808,8 +852,8 @@ def bench_decode(args, torch, ssd, syn, dev):
         ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, dt_bias=bias, out=y)
     torch.cuda.synchronize()
     rate = K / (time.perf_counter() - t0)
-    _, ms = _time_calls(torch, lambda k: ssd.step(st, xs[k], dts[k], A, Bs[k], Cs[k], D,
-                                                  dt_bias=bias, out=y), K, warm=0)
+    _, ms = _time_calls(torch, lambda k: ssd.step(st, xs[k % K], dts[k % K], A, Bs[k % K],
+                                                  Cs[k % K], D, dt_bias=bias, out=y), K, warm=0)
     alg = bytes_step(b, h, p, n, g, 2)
     achieved = alg / (ms * 1e-3) / 1e9
     log("decode: %.1f steps/s, kernel %.2f us, %.0f GB/s" % (rate, ms * 1e3, achieved))
