@@ -20,15 +20,18 @@
 // are finished with cross-lane shuffles; alpha and d are wave-uniform.
 #pragma once
 
+#include <type_traits>
+
 #include "ssd_device.hpp"
 #include "ssd_plan.hpp"
 
 namespace ssd {
 
-// The M consecutive io values at p (p and M * sizeof(IO) 16-byte multiples
-// where R16, else element by element) as loaded.
-template <typename IO, int M> struct Run {
-    static constexpr bool R16 = (M * sizeof(IO)) % 16 == 0;
+// The M consecutive io values at p as loaded: 16 bytes at a time where VEC
+// (p 16-byte aligned) and M * sizeof(IO) is a multiple of 16, else element
+// by element.
+template <typename IO, int M, bool VEC> struct Run {
+    static constexpr bool R16 = VEC && (M * sizeof(IO)) % 16 == 0;
     static constexpr int NV = R16 ? M * sizeof(IO) / 16 : 1;
     u32x4 v[NV];
     IO e[R16 ? 1 : M];
@@ -51,7 +54,8 @@ template <typename IO, int M> struct Run {
     }
 };
 
-template <typename IO, int P, int N>
+// VB: B and C 16-byte aligned (their runs then load 16 bytes at a time)
+template <typename IO, int P, int N, bool VB>
 __global__ __launch_bounds__(256) void k_step(
     float *__restrict__ state, const IO *__restrict__ x, const IO *__restrict__ dt,
     const float *__restrict__ A, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
@@ -80,7 +84,7 @@ __global__ __launch_bounds__(256) void k_step(
         sv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (int64_t)k * P));
     const IO dtr = dt[pair];
     const f32x4 xv = ld4(x + pair * P + q * 4);
-    Run<IO, ITER> Br, Cr;
+    Run<IO, ITER, VB> Br, Cr;
     Br.load(Bm + (b * g + gi) * N + r0);
     Cr.load(Cm + (b * g + gi) * N + r0);
     const float Ah = A[hh];
@@ -120,11 +124,16 @@ template <typename IO, int P, int N>
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     const int64_t pairs = a.b * a.h;
     const unsigned nblk = (unsigned)((pairs + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((k_step<IO, P, N>), dim3(nblk), dim3(256), 0, s, a.state,
-                       static_cast<const IO *>(a.x), static_cast<const IO *>(a.dt), a.A,
-                       static_cast<const IO *>(a.B), static_cast<const IO *>(a.C), a.D, a.dt_bias,
-                       a.softplus, a.dt_min, a.dt_max, static_cast<IO *>(a.y), pairs, (int)a.h,
-                       (int)a.g);
+    const bool vb = ((uintptr_t)a.B & 15) == 0 && ((uintptr_t)a.C & 15) == 0;
+    auto go = [&](auto vb_c) {
+        hipLaunchKernelGGL((k_step<IO, P, N, decltype(vb_c)::value>), dim3(nblk), dim3(256), 0,
+                           s, a.state, static_cast<const IO *>(a.x),
+                           static_cast<const IO *>(a.dt), a.A, static_cast<const IO *>(a.B),
+                           static_cast<const IO *>(a.C), a.D, a.dt_bias, a.softplus, a.dt_min,
+                           a.dt_max, static_cast<IO *>(a.y), pairs, (int)a.h, (int)a.g);
+    };
+    if (vb) go(std::true_type{});
+    else go(std::false_type{});
     return hipGetLastError();
 }
 

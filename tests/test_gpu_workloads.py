@@ -97,6 +97,54 @@ def test_step_shapes(orc, p, n):
     check_close(to_f64(st), so, "f32", "state", STATE_AXES)
 
 
+@pytest.mark.parametrize("p,n", [(16, 32), (32, 64), (64, 32), (64, 128), (128, 128)])
+def test_step_shapes_bf16(orc, p, n):
+    """bf16 io at every run length of state rows per lane (2 to 64 rows:
+    B and C read element by element or 16 bytes at a time, one to four
+    batches of rows in flight)."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, h, g = 3, 6, 2
+    inp = syn.random_case(40 + p + n, b, 1, h, p, n, g, io="bf16")
+    st0 = np.random.default_rng(5).standard_normal((b, h, n, p)).astype(np.float32)
+    st = dev_tensor(st0)
+    y = ssd.step(st, dev_tensor(inp["x"][:, 0]), dev_tensor(inp["dt"][:, 0]),
+                 dev_tensor(inp["A"]), dev_tensor(inp["B"][:, 0]), dev_tensor(inp["C"][:, 0]),
+                 dev_tensor(inp["D"]), dt_bias=dev_tensor(inp["dt_bias"]))
+    torch.cuda.synchronize()
+    yo, so = orc.step(st0, inp["x"][:, 0], inp["dt"][:, 0], inp["A"], inp["B"][:, 0],
+                      inp["C"][:, 0], inp["D"], inp["dt_bias"], io="bf16")
+    check_close(to_f64(y), yo, "bf16", "y", (2,))
+    check_close(to_f64(st), so, "f32", "state", STATE_AXES)
+
+
+def test_step_unaligned_B_C_equals_aligned():
+    """B and C only 2-byte aligned (views one element into their storage):
+    the element-by-element path gives the bits of the 16-byte one."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, h, p, n, g = 4, 8, 64, 128, 2
+    inp = syn.random_case(77, b, 1, h, p, n, g, io="bf16")
+    st0 = np.random.default_rng(6).standard_normal((b, h, n, p)).astype(np.float32)
+    B0, C0 = dev_tensor(inp["B"][:, 0]), dev_tensor(inp["C"][:, 0])
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 != 0 and v.is_contiguous()
+        return v
+    args = (dev_tensor(inp["x"][:, 0]), dev_tensor(inp["dt"][:, 0]), dev_tensor(inp["A"]))
+    st1, st2 = dev_tensor(st0), dev_tensor(st0)
+    y1 = ssd.step(st1, *args, B0, C0, dev_tensor(inp["D"]), dt_bias=dev_tensor(inp["dt_bias"]))
+    y2 = ssd.step(st2, *args, shifted(B0), shifted(C0), dev_tensor(inp["D"]),
+                  dt_bias=dev_tensor(inp["dt_bias"]))
+    torch.cuda.synchronize()
+    assert B0.data_ptr() % 16 == 0
+    assert torch.equal(y1, y2)
+    assert torch.equal(st1, st2)
+
+
 def test_step_zero_time_step_leaves_state_equal():
     """dt = 0 is the exact skip (nnterp, "betas and decays are one argument"):
     exp(0) = 1 and no write, so the state is value-equal afterwards."""
