@@ -352,7 +352,7 @@ int32_t ssd_gated_norm(const void *y, const void *z, const float *weight, void *
  *   norm_weight, norm_group, eps, normalize
  *                 as for ssd_gated_norm (norm_group > 0 always)
  *   out           [b, l, h, p] io dtype output; 16-byte aligned; must not
- *                 overlap any input
+ *                 overlap any input or the workspace
  *   workspace     at least ssd_mixer_workspace_bytes(...) bytes, 256-byte
  *                 aligned: the scan's workspace, then x, B and C
  *
