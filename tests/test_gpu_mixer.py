@@ -164,3 +164,51 @@ def test_mixer_with_no_tokens_passes_the_states_through():
     assert out.shape == (b, 0, h, p)
     assert torch.equal(fin, init)
     assert torch.equal(cfin, cinit)
+
+
+def test_mixer_graph_capture_replays_match_eager():
+    """One ssd_mixer_forward call (conv, scan and norm: kernel launches only,
+    nothing allocated or cleared by the library) captured in a HIP graph and
+    replayed several times with eager work in between: every replay equals
+    the eager call bit for bit."""
+    import mamba_ssd_chunked_chunk_amd as ssd
+    torch = torch_mod()
+    b, l, h, p, n, g, K, Q = 2, 700, 8, 64, 128, 2, 4, 256
+    case = _case(7500, b, l, h, p, n, g, K, "bf16", docs=True, init_std=0.1)
+    c, sc = case["c"], case["sc"]
+    T = {k: dev_tensor(v) for k, v in (("xbc", c["xbc"]), ("w", c["weight"]), ("cb", c["bias"]),
+                                       ("ci", c["conv_init"]), ("dt", sc["dt"]), ("A", sc["A"]),
+                                       ("D", sc["D"]), ("bias", sc["dt_bias"]),
+                                       ("init", sc["init_state"]), ("z", case["z"]),
+                                       ("nw", case["nw"]))}
+    seq = _dev_int(case["seq"])
+    out = torch.empty((b, l, h, p), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ssd.mixer_workspace_bytes(b, l, h, p, n, g, Q), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        ssd.mixer_forward(T["xbc"], T["dt"], T["A"], T["w"], h, p, n, g, z=T["z"],
+                          conv_bias=T["cb"], conv_init=T["ci"], D=T["D"], dt_bias=T["bias"],
+                          initial_state=T["init"], seq_idx=seq, norm_weight=T["nw"],
+                          norm_group=256, chunk_size=Q, out=out, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                      # warm the path on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for k in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), k
+        call()                      # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), k
