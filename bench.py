@@ -302,6 +302,25 @@ def syn_workload(name):
     return syn.WORKLOADS[name]
 
 
+def _kernel_label(name):
+    """k_name<template ints> from a mangled or demangled kernel name."""
+    import re
+    m = re.search(r"(k_[a-z0-9_]+)", name)
+    if not m:
+        return name[:40]
+    k = m.group(1)
+    rest = name[m.end():]
+    if name.startswith("_Z"):
+        t = re.match(r"I((?:L[a-z]+\d+E|DF16b|[a-z])+)E", rest)
+        if t:
+            args = re.findall(r"L[a-z]+(\d+)E|(DF16b)|([fd])", t.group(1))
+            vals = [a or ("bf16" if b else ("f32" if c == "f" else c)) for a, b, c in args]
+            return "%s<%s>" % (k, ",".join(vals))
+        return k
+    t = re.match(r"<([^>]*)>", rest)
+    return "%s<%s>" % (k, t.group(1).replace(" ", "")) if t else k
+
+
 def summarize(a):
     """profiles/ summaries from rocprofv3 csv output (see --summarize)."""
     kind, wl = a[0], a[1]
@@ -411,6 +430,46 @@ def summarize(a):
                     v = vals[k][ctr]
                     f.write("  %-30s %18.1f\n" % (ctr, sum(v) / len(v)))
                 f.write("\n")
+            f.write("source_digest: %s\n" % source_digest())
+        print("wrote", path)
+        return
+    if kind == "bwd":
+        # the gradient calls of a run (each from its first kernel,
+        # k_transpose_tiles, to its last, k_bwd_sum): every kernel's
+        # dispatches inside them, grouped by kernel and template arguments
+        rows = _csv_rows(_find(a[2], "kernel_trace.csv"))
+        cmd = " ".join(a[3:])
+        ev = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                      r.get("Kernel_Name", "")) for r in rows))
+        calls, cur = [], None
+        for t0, t1, nm in ev:
+            if "k_transpose_tiles" in nm:
+                cur = []
+            if cur is not None:
+                cur.append((t0, t1, nm))
+                if "k_bwd_sum" in nm:
+                    calls.append(cur)
+                    cur = None
+        per, spans, ktot = {}, [], []
+        for c in calls:
+            spans.append((c[-1][1] - c[0][0]) / 1e3)
+            ktot.append(sum(t1 - t0 for t0, t1, _ in c) / 1e3)
+            for t0, t1, nm in c:
+                per.setdefault(_kernel_label(nm), []).append((t1 - t0) / 1e3)
+        path = os.path.join(PROFILES, "gradient_pass_%s_kernel_trace.txt" % wl)
+        with open(path, "w") as f:
+            f.write("# rocprofv3 kernel trace of bench.py's gradient-pass measurement, %s "
+                    "workload (bf16 io,\n# final-state cotangent)\n" % wl)
+            f.write("# command (from /tmp with TMPDIR=/tmp, repository at $R):\n#   %s\n" % cmd)
+            f.write("# every gradient call in the run (%d), from its first kernel "
+                    "(k_transpose_tiles) to its last (k_bwd_sum)\n\n" % len(calls))
+            f.write("%-58s %6s %10s %10s\n" % ("kernel", "calls", "avg_us", "total_us"))
+            for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+                f.write("%-58s %6d %10.2f %10.1f\n" % (k, len(v), sum(v) / len(v), sum(v)))
+            if calls:
+                f.write("\nkernel time per call: %.1f us; first dispatch to last end per call: "
+                        "median %.1f us\n" % (sum(ktot) / len(ktot),
+                                              sorted(spans)[len(spans) // 2]))
             f.write("source_digest: %s\n" % source_digest())
         print("wrote", path)
         return
