@@ -433,6 +433,34 @@ def summarize(a):
             f.write("source_digest: %s\n" % source_digest())
         print("wrote", path)
         return
+    if kind == "bench":
+        # every scan kernel of a bench.py run of one workload (its pre-warm,
+        # warm-up, timed and event-timed calls)
+        rows = _csv_rows(_find(a[2], "kernel_trace.csv"))
+        cmd = " ".join(a[3:])
+        per = {}
+        for r in rows:
+            k = _short(r.get("Kernel_Name", ""))
+            if k in ("k_state16", "k_scan16", "k_out16"):
+                per.setdefault(k, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        path = os.path.join(PROFILES, "bench_%s_kernel_trace.txt" % wl)
+        with open(path, "w") as f:
+            f.write("# rocprofv3 kernel trace of the bench's own measurement of the %s "
+                    "workload\n" % wl)
+            f.write("# command (from /tmp with TMPDIR=/tmp, repository at $R):\n#   %s\n" % cmd)
+            f.write("# every dispatch of the scan kernels in the run: pre-warm, warm-up, "
+                    "timed and event-timed calls\n\n")
+            f.write("%-12s %6s %10s %10s %10s %10s\n" % ("kernel", "calls", "avg_us", "med_us",
+                                                        "min_us", "max_us"))
+            for k in ("k_state16", "k_scan16", "k_out16"):
+                v = sorted(per.get(k, []))
+                if v:
+                    f.write("%-12s %6d %10.2f %10.2f %10.2f %10.2f\n" % (
+                        k, len(v), sum(v) / len(v), v[len(v) // 2], v[0], v[-1]))
+            f.write("\nsource_digest: %s\n" % source_digest())
+        print("wrote", path)
+        return
     if kind == "bwd":
         # the gradient calls of a run (each from its first kernel,
         # k_transpose_tiles, to its last, k_bwd_sum): every kernel's
