@@ -173,7 +173,7 @@ int64_t ssd_chunk_scan_state_chunks(int64_t batch, int64_t seqlen, int64_t heads
     // the caller's per-chunk states come from chunks of the caller's length
     // (or from the computed ones, stepped token by token)
     const bool per_chunk = with_chunk_states != 0;
-    const int m = state_interval(pl, per_chunk, bf16_item_heads(head_dim, heads, groups));
+    const int m = bf16_state_interval(pl, per_chunk, head_dim, true);
     return (pl.l + m * pl.Q - 1) / (m * pl.Q);
 }
 

@@ -134,6 +134,29 @@ inline int state_interval(const ScanPlan &pl, bool per_chunk_states, int hp) {
     return 1;
 }
 
+// The state interval the bf16 scan runs a call at.  Head_dim 64 with a
+// group's heads in fours (the four-head workgroups) may instead take the
+// split layout's own interval (two heads of two waves per workgroup, three
+// workgroups per compute unit): where the split items at that interval fit
+// the chip in one round while the four-head grid at its interval does not
+// (mamba2_2p7b: 640 split items of 4 joined chunks against 640 four-head
+// items of 2 in 1.25 rounds; 0.247 -> 0.235 ms on one box).  may_split:
+// not for the gradient pass's row-dot scans nor given boundary states.
+inline int bf16_state_interval(const ScanPlan &pl, bool per_chunk_states, int64_t p,
+                               bool may_split) {
+    const int hpg = bf16_item_heads(p, pl.h, pl.g);
+    int m = state_interval(pl, per_chunk_states, hpg);
+    if (p == 64 && hpg == 4 && may_split) {
+        const int ms = state_interval(pl, per_chunk_states, 2);
+        const int64_t cap = 3 * (int64_t)device_cus();
+        auto split_items = [&](int mm) {
+            return 2 * pl.b * ((pl.l + pl.Q * mm - 1) / (pl.Q * mm)) * (pl.h / 4);
+        };
+        if (ms > m && split_items(ms) <= cap && split_items(m) > cap) m = ms;
+    }
+    return m;
+}
+
 struct ScanArgs {
     const void *x, *dt, *B, *C;
     const float *A, *D, *dt_bias;

@@ -1323,8 +1323,9 @@ hipError_t launch_scan16(const ScanPlan &plan, const ScanArgs &a, hipStream_t s)
     // the plan the kernels run on: its chunks may join several of the
     // caller's (fewer stored states; the workspace map stays the caller's)
     ScanPlan pl = plan;
-    const int m =
-        a.interval > 0 ? a.interval : state_interval(plan, a.states != nullptr, grouped ? HPG : 1);
+    const int m = a.interval > 0 ? a.interval
+                                 : bf16_state_interval(plan, a.states != nullptr, P,
+                                                       !a.dotout && !a.hb_in);
     if (m > 1) {
         pl.Q = plan.Q * m;
         pl.nc = (plan.l + pl.Q - 1) / pl.Q;
